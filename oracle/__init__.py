@@ -1,0 +1,137 @@
+"""Test infrastructure only: ctypes wrapper of the plain CPU oracle (oracle.c).
+
+Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
+leg use this package.  It shares no code with the GPU library: it has its own
+C source, built by the host compiler with OpenMP into ``liboracle.so`` next to
+this file.
+
+Every function takes *logical* NumPy matrices (any memory order) and returns
+NumPy arrays.  Real inputs are computed in float64 and complex inputs in
+complex128, whatever their storage precision (a float32 input is widened
+exactly first).
+
+JAXMg paper, "Software design": potrs solves A x = b for symmetric
+(Hermitian) positive-definite A through a Cholesky factorization, and the
+same factorization optionally gives log det(A).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc and OpenMP into liboracle.so."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB):
+                build(force=True)
+            lib = ctypes.CDLL(_LIB)
+            i64, vp = ctypes.c_int64, ctypes.c_void_p
+            lib.oracle_num_threads.restype = ctypes.c_int
+            for suf in ("d", "z"):
+                f = getattr(lib, "oracle_potrf_" + suf)
+                f.argtypes, f.restype = [i64, vp, vp], ctypes.c_int
+                f = getattr(lib, "oracle_potrs_" + suf)
+                f.argtypes, f.restype = [i64, i64, vp, vp], None
+                f = getattr(lib, "oracle_logdet_" + suf)
+                f.argtypes, f.restype = [i64, vp], ctypes.c_double
+            _lib = lib
+    return _lib
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle runs on."""
+    return int(_load().oracle_num_threads())
+
+
+def _wide(x) -> np.ndarray:
+    x = np.asarray(x)
+    dt = np.complex128 if np.iscomplexobj(x) else np.float64
+    return np.ascontiguousarray(x, dtype=dt)
+
+
+def _p(x: np.ndarray):
+    return x.ctypes.data_as(ctypes.c_void_p)
+
+
+def potrf(a):
+    """Cholesky factor of the lower triangle of ``a``: returns (L, info).
+
+    L is lower triangular with a positive real diagonal and zeros above it.
+    info = 0 on success, else j + 1 for the first column j whose pivot is not
+    positive (then L holds the columns finished before j and zeros after)."""
+    a = _wide(a)
+    n = a.shape[0]
+    if a.shape != (n, n):
+        raise ValueError("a must be square")
+    l = np.zeros_like(a)
+    if n == 0:
+        return l, 0
+    f = _load().oracle_potrf_z if np.iscomplexobj(a) else _load().oracle_potrf_d
+    info = f(n, _p(a), _p(l))
+    return l, int(info)
+
+
+def potrs(l, b):
+    """Solve (L L^H) X = B given the factor L: L Y = B, then L^H X = Y."""
+    l = _wide(l)
+    n = l.shape[0]
+    b = np.asarray(b)
+    vec = b.ndim == 1
+    b2 = b.reshape(n, 1) if vec else b
+    cplx = np.iscomplexobj(l) or np.iscomplexobj(b2)
+    dt = np.complex128 if cplx else np.float64
+    l = np.ascontiguousarray(l, dtype=dt)
+    # right-hand-side columns one after another: the transpose, row-major
+    bt = np.ascontiguousarray(b2.T, dtype=dt)
+    nrhs = bt.shape[0]
+    if n > 0 and nrhs > 0:
+        f = _load().oracle_potrs_z if cplx else _load().oracle_potrs_d
+        f(n, nrhs, _p(l), _p(bt))
+    x = bt.T.copy()
+    return x.reshape(b.shape) if vec else x
+
+
+def logdet(l) -> float:
+    """log det(A) = 2 * sum_i log L_ii from the Cholesky factor L of A."""
+    l = _wide(l)
+    n = l.shape[0]
+    if n == 0:
+        return 0.0
+    f = _load().oracle_logdet_z if np.iscomplexobj(l) else _load().oracle_logdet_d
+    return float(f(n, _p(l)))
+
+
+def solve(a, b, want_logdet: bool = False):
+    """potrf, then potrs (and log det).  Returns (X, info) or (X, logdet, info);
+    X and logdet are NaN when info != 0."""
+    l, info = potrf(a)
+    b = np.asarray(b)
+    if info != 0:
+        x = np.full(b.shape, np.nan, dtype=np.result_type(b.dtype, np.asarray(a).dtype, np.float64))
+        return (x, float("nan"), info) if want_logdet else (x, info)
+    x = potrs(l, b)
+    if want_logdet:
+        return x, logdet(l), info
+    return x, info
