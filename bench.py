@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark: potrf + logdet + potrs throughput on one MI355X.
+
+One step = the whole solve path on one synthetic input: Cholesky
+factorization of A (in place), log det from the factor, and the blocked
+forward/back substitution of B (in place).  Inputs are generated once, with
+a pristine copy kept in HBM; before every step A and B are restored from it
+by a device-to-device copy that is outside the step's timed events.
+
+Default workload: fp64 SPD solve, N = 32768, N_RHS = 128, T_A = 512,
+A = G G^T / N + 0.05 I (G iid N(0,1), seeded), B iid N(0,1).
+
+TFLOP/s = (N^3/3 + 2 N^2 N_RHS) / step time (x4 for complex: real-equivalent).
+
+Printed: one JSON line with the metric, the roofline of the dominant kernel
+(the trailing update A22 -= L21 L21^H, timed live with HIP events around each
+launch on its stream) and the CPU oracle timed on a bounded sample of the same
+workload (its leading principal block).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK = {  # MI355X published dense peaks, TFLOP/s
+    "f64": 78.6,
+    "c128": 78.6,
+    "f32": 157.3,
+    "c64": 157.3,
+}
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=3)
+    p.add_argument("--warmup", type=int, default=1)
+    p.add_argument("--config", type=int, default=5, help="workload 1..5 (default 5: fp64 N=32768)")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-check", action="store_true", help="skip the backward-error check of the last step")
+    return p.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    ws = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or ws != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "requested_gpus": args.gpus}), flush=True)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import cholesky_spd_solve_amd as spd
+    import spdgen
+
+    spd.load()
+    cfg = dict(spdgen.CONFIGS[args.config])
+    dt, n, nrhs, T = cfg["dtype"], cfg["n"], cfg["nrhs"], cfg["T_A"]
+    cplx = dt in ("c64", "c128")
+    fmul = 4.0 if cplx else 1.0
+    flops_potrf = fmul * n**3 / 3.0
+    flops_potrs = fmul * 2.0 * n * n * nrhs
+    flops = flops_potrf + flops_potrs
+
+    t0 = time.time()
+    log(f"[bench] generating config {args.config}: {dt} N={n} N_RHS={nrhs} T_A={T} seed={args.seed}")
+    A0, B0, _ = spdgen.make_config(args.config, args.seed, device="cuda")
+    torch.cuda.synchronize()
+    log(f"[bench] inputs ready in {time.time() - t0:.1f} s")
+    A = spdgen.to_colmajor(A0)
+    B = spdgen.to_colmajor(B0)
+    work = spd.workspace(A.dtype, n, nrhs, T)
+    info = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ldbuf = torch.zeros(1, dtype=torch.float64, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def restore():
+        A.copy_(A0)
+        B.copy_(B0)
+
+    def step(ev):
+        ev[0].record(stream)
+        spd.potrf(A, T, info=info, work=work)
+        ev[1].record(stream)
+        if cfg["logdet"]:
+            spd.logdet(A, info, out=ldbuf)
+        ev[2].record(stream)
+        spd.potrs(A, B, T, info=info, work=work)
+        ev[3].record(stream)
+
+    def events():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+    for w in range(args.warmup):
+        restore()
+        step(events())
+        torch.cuda.synchronize()
+        log(f"[bench] warmup {w + 1}/{args.warmup} done")
+
+    # timed region: K steps; restores happen between steps, outside the events
+    spd.profile_enable(1 << spd.PROF_SYRK)
+    spd.profile_read(spd.PROF_SYRK)
+    evs = []
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for k in range(args.steps):
+        restore()
+        ev = events()
+        step(ev)
+        evs.append(ev)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    spd.profile_enable(0)
+    syrk_ms, syrk_launches, syrk_flops = spd.profile_read(spd.PROF_SYRK)
+
+    step_ms = [e[0].elapsed_time(e[3]) for e in evs]
+    potrf_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    logdet_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    potrs_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    ms = float(np.mean(step_ms))
+    status = int(info.item())
+    log(f"[bench] steps: {', '.join(f'{x:.2f}' for x in step_ms)} ms; info={status}")
+
+    check = None
+    if not args.no_check:
+        # normwise backward error of the last step's X, residual in double on the GPU
+        wd = torch.complex128 if cplx else torch.float64
+        Aw, Xw, Bw = A0.to(wd), B.to(wd), B0.to(wd)
+        r = Bw - Aw @ Xw
+        eta = (r.abs().amax(dim=0) / (Aw.abs().sum(dim=1).max() * Xw.abs().amax(dim=0) + Bw.abs().amax(dim=0))).max()
+        eps = 2.0**-52 if dt in ("f64", "c128") else 2.0**-23
+        check = {"backward_error": float(eta.item()), "bound_64_n_eps": 64 * n * eps,
+                 "ok": bool(eta.item() <= 64 * n * eps and status == 0)}
+        del Aw, Xw, Bw, r
+        log(f"[bench] backward error {check['backward_error']:.3e} (bound {check['bound_64_n_eps']:.3e})")
+
+    value = flops / (ms * 1e-3) / 1e12
+    potrf_tf = flops_potrf / (float(np.mean(potrf_ms)) * 1e-3) / 1e12
+    syrk_avg_ms = syrk_ms / max(syrk_launches, 1)
+    syrk_achieved = (syrk_flops / syrk_launches) / (syrk_avg_ms * 1e-3) / 1e12 if syrk_launches else None
+    peak = PEAK[dt]
+    roofline = {
+        "kernel": "gemm_kernel (trailing update A22 -= L21 L21^H, lower tiles)",
+        "bound": "mfma",
+        "achieved": syrk_achieved,
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": (syrk_achieved / peak) if syrk_achieved else None,
+        "traffic": None,
+        "launches": syrk_launches,
+        "avg_launch_ms": syrk_avg_ms,
+        "flops_per_launch": syrk_flops / max(syrk_launches, 1),
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(A0, B0, n, nrhs, fmul, args.cpu_seconds)
+
+    out = {
+        "metric": "potrf+potrs TFLOP/s and % of MFMA peak, fp64 N=32768, 1 MI355X",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic",
+        "config": {"workload": f"{dt} SPD solve N={n} N_RHS={nrhs} T_A={T}, A = G G^H/N + {cfg['delta']} I, "
+                               f"seed {args.seed}", "n": n, "n_rhs": nrhs, "T_A": T, "logdet": cfg["logdet"]},
+        "pct_of_peak": 100.0 * value / peak,
+        "potrf_tflops": potrf_tf,
+        "potrf_pct_of_peak": 100.0 * potrf_tf / peak,
+        "phase_ms": {"potrf": float(np.mean(potrf_ms)), "logdet": float(np.mean(logdet_ms)),
+                     "potrs": float(np.mean(potrs_ms))},
+        "wall_ms_per_step_incl_restore": 1e3 * wall / args.steps,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "check": check,
+    }
+    print(json.dumps(out), flush=True)
+    return 0 if (check is None or check["ok"]) else 1
+
+
+def cpu_baseline(A0, B0, n, nrhs, fmul, target_s):
+    """The CPU oracle, as it stands, on the leading principal block of the same
+    matrix (and the matching rows of B): a bounded sample sized for about
+    ``target_s`` seconds, scaled to TFLOP/s with the same flop formula."""
+    import numpy as np
+
+    import oracle
+
+    def run(m):
+        a = A0[:m, :m].cpu().numpy()
+        b = B0[:m, :].cpu().numpy()
+        t = time.perf_counter()
+        l, info = oracle.potrf(a)
+        oracle.potrs(l, b)
+        oracle.logdet(l)
+        return time.perf_counter() - t, info
+
+    m0 = min(n, 1024)
+    t0, _ = run(m0)
+    m = int(m0 * (target_s / max(t0, 1e-3)) ** (1.0 / 3.0))
+    m = max(256, min(n, (m // 256) * 256))
+    log(f"[bench] cpu oracle: {m0} took {t0:.2f} s; sample size {m}")
+    t, info = run(m)
+    fl = fmul * (m**3 / 3.0 + 2.0 * m * m * nrhs)
+    return {"value": fl / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"leading {m} x {m} principal block of the same A with the first {m} rows of all "
+                      f"{nrhs} right-hand sides (potrf + potrs + logdet), {t:.2f} s",
+            "seconds": t}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,710 @@
+// Host side of the gfx950 dense SPD/HPD solver: argument checking, workspace
+// layout and the launch sequences of the blocked Cholesky factorization,
+// blocked substitution and log-determinant (declared in include/spd.h).
+//
+// Right-looking blocked Cholesky with tile size T (JAXMg paper, "Software
+// design": potrs = potrf + potrs with a user tile size T_A), for k = 0, 1, ...:
+//   1. factor the diagonal tile  A_kk = L_kk L_kk^H  and form inv(L_kk)
+//   2. panel solve               L_ik = A_ik L_kk^-H  (i > k), as A_ik inv(L_kk)^H
+//   3. trailing update           A_ij -= L_ik L_jk^H  (k < j <= i, lower part)
+// Step 1 is itself blocked by LEAF = 64 columns: each leaf is factored and
+// inverted inside LDS by one workgroup, the rows below it inside the tile are
+// solved against the leaf inverse and the rest of the tile is updated; the
+// leaf inverses are then merged pairwise (inv([A 0; B C]) has lower-left
+// block -inv(C) B inv(A)) until inv(L_kk) is complete.
+//
+// The solve L L^H X = B walks the same tiles: Y_k = inv(L_kk) (B_k - ...)
+// forwards, then X_k = inv(L_kk)^H (Y_k - ...) backwards, with every
+// inv(L_kk) built up front by the same leaf + merge kernels.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "spd.h"
+#include "spd_gemm.hpp"
+#include "spd_kernels.hpp"
+
+namespace spd {
+
+static thread_local std::string g_last_error;
+
+static int hip_fail(hipError_t e, const char *where)
+{
+    g_last_error = std::string(where) + ": " + hipGetErrorString(e);
+    return SPD_ERR_HIP;
+}
+
+#define SPD_CHECK_LAUNCH(where)                          \
+    do {                                                 \
+        hipError_t e_ = hipGetLastError();               \
+        if (e_ != hipSuccess)                            \
+            return hip_fail(e_, where);                  \
+    } while (0)
+
+// ------------------------------------------------------------ profiling ---
+
+struct ProfRec {
+    int cls;
+    hipEvent_t a, b;
+    double flops;
+};
+static std::mutex g_prof_mu;
+static int g_prof_mask = 0;
+static std::vector<ProfRec> g_prof;
+
+struct ProfScope {
+    bool on = false;
+    ProfRec r{};
+    hipStream_t s{};
+    ProfScope(int cls, double flops, hipStream_t stream)
+    {
+        std::lock_guard<std::mutex> g(g_prof_mu);
+        if (!(g_prof_mask & (1 << cls)))
+            return;
+        on = true;
+        s = stream;
+        r.cls = cls;
+        r.flops = flops;
+        (void)hipEventCreate(&r.a);
+        (void)hipEventCreate(&r.b);
+        (void)hipEventRecord(r.a, s);
+    }
+    ~ProfScope()
+    {
+        if (!on)
+            return;
+        (void)hipEventRecord(r.b, s);
+        std::lock_guard<std::mutex> g(g_prof_mu);
+        g_prof.push_back(r);
+    }
+};
+
+enum { PROF_SYRK = 0, PROF_PANEL = 1, PROF_DIAG = 2, PROF_SOLVE = 3 };
+
+// ------------------------------------------------------------- helpers ----
+
+static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+static inline int64_t align_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+
+enum Lay { NT, NN, TN };
+
+struct Gemm {
+    const void *A = nullptr, *B = nullptr;
+    void *C = nullptr;
+    int64_t lda = 1, ldb = 1, ldc = 1;
+    int64_t sA_out = 0, sA_in = 0, sB_out = 0, sB_in = 0, sC_out = 0, sC_in = 0;
+    int nb_inner = 1, batch = 1;
+    int64_t m = 0, n = 0, k = 0;
+    bool tri = false;
+    int kmode = KM_NONE;
+    bool neg = false;
+    bool beta = false;
+    const int *info = nullptr;
+    bool small = false;    // prefer the small tile shape
+    bool inplace = false;  // C aliases A: one workgroup must own whole rows (n <= BN)
+};
+
+template <typename R, bool CPLX, int BM, int BN, int KB, int WM, int WN>
+static int launch_gemm_cfg(Lay lay, const Gemm &g, hipStream_t s)
+{
+    GemmArgs a;
+    a.A = g.A;
+    a.B = g.B;
+    a.C = g.C;
+    a.lda = g.lda;
+    a.ldb = g.ldb;
+    a.ldc = g.ldc;
+    a.sA_out = g.sA_out;
+    a.sA_in = g.sA_in;
+    a.sB_out = g.sB_out;
+    a.sB_in = g.sB_in;
+    a.sC_out = g.sC_out;
+    a.sC_in = g.sC_in;
+    a.nb_inner = g.nb_inner;
+    a.m = (int)g.m;
+    a.n = (int)g.n;
+    a.k = (int)g.k;
+    a.tiles_m = (int)cdiv(g.m, BM);
+    a.tiles_n = (int)cdiv(g.n, BN);
+    a.ntiles = g.tri ? a.tiles_m * (a.tiles_m + 1) / 2 : a.tiles_m * a.tiles_n;
+    a.tri = g.tri ? 1 : 0;
+    a.kmode = g.kmode;
+    a.neg = g.neg ? 1 : 0;
+    a.beta = g.beta ? 1 : 0;
+    a.info = g.info;
+    dim3 grid(a.ntiles, 1, g.batch), block(64 * WM * WN);
+    switch (lay) {
+    case NT: gemm_kernel<R, CPLX, BM, BN, KB, WM, WN, false, true><<<grid, block, 0, s>>>(a); break;
+    case NN: gemm_kernel<R, CPLX, BM, BN, KB, WM, WN, false, false><<<grid, block, 0, s>>>(a); break;
+    case TN: gemm_kernel<R, CPLX, BM, BN, KB, WM, WN, true, false><<<grid, block, 0, s>>>(a); break;
+    }
+    SPD_CHECK_LAUNCH("gemm_kernel");
+    return 0;
+}
+
+template <typename R, bool CPLX>
+static int gemm(Lay lay, const Gemm &g, hipStream_t s)
+{
+    if (g.m <= 0 || g.n <= 0 || g.batch <= 0)
+        return 0;
+    if (g.k <= 0 && g.beta)
+        return 0;
+    if (g.inplace) {
+        // C aliases A: a workgroup reads rows [i0, i0 + BM) of A for every k and
+        // writes the same rows of C only after its last read, so it must cover
+        // all n columns itself.
+        if (g.n > 64 || g.A != g.C) {
+            g_last_error = "in-place product needs n <= 64 and C == A";
+            return SPD_ERR_HIP;
+        }
+        return launch_gemm_cfg<R, CPLX, 64, 64, 16, 2, 2>(lay, g, s);
+    }
+    if constexpr (!CPLX) {
+        const int64_t tiles128 = g.tri ? cdiv(g.m, 128) * (cdiv(g.m, 128) + 1) / 2
+                                       : cdiv(g.m, 128) * cdiv(g.n, 128);
+        if (!g.small && tiles128 * g.batch >= 512)
+            return launch_gemm_cfg<R, CPLX, 128, 128, 16, 2, 2>(lay, g, s);
+        return launch_gemm_cfg<R, CPLX, 64, 64, 16, 2, 2>(lay, g, s);
+    } else {
+        const int64_t tiles64 = g.tri ? cdiv(g.m, 64) * (cdiv(g.m, 64) + 1) / 2 : cdiv(g.m, 64) * cdiv(g.n, 64);
+        if (!g.small && tiles64 * g.batch >= 512)
+            return launch_gemm_cfg<R, CPLX, 64, 64, 16, 2, 2>(lay, g, s);
+        return launch_gemm_cfg<R, CPLX, 32, 32, 16, 2, 2>(lay, g, s);
+    }
+}
+
+template <typename E>
+static int copy2d(E *dst, int64_t ldd, const E *src, int64_t lds, int64_t m, int64_t n, const int *info,
+                  hipStream_t s)
+{
+    if (m <= 0 || n <= 0)
+        return 0;
+    const int64_t blocks = std::min<int64_t>(cdiv(m * n, 256), 4096);
+    copy2d_kernel<E><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(dst, ldd, src, lds, m, n, info);
+    SPD_CHECK_LAUNCH("copy2d_kernel");
+    return 0;
+}
+
+template <typename E>
+static int zero2d(E *dst, int64_t ldd, int64_t m, int64_t n, hipStream_t s)
+{
+    if (m <= 0 || n <= 0)
+        return 0;
+    const int64_t blocks = std::min<int64_t>(cdiv(m * n, 256), 8192);
+    zero2d_kernel<E><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(dst, ldd, m, n);
+    SPD_CHECK_LAUNCH("zero2d_kernel");
+    return 0;
+}
+
+#define SPD_TRY(x)              \
+    do {                        \
+        int r_ = (x);           \
+        if (r_ != 0)            \
+            return r_;          \
+    } while (0)
+
+// Workspace layout, in elements of the working type (each region 256-byte
+// aligned):  INV  nt * T * T   inverted diagonal tiles (tile t at t*T*T, ld T)
+//            W    n * T        panel L21 (potrf) / merge temporaries (both)
+//            TMP  max(T*T, T*n_rhs)   one block row of the right-hand side
+struct Layout {
+    int64_t T, nt, inv, w, tmp, total;  // offsets / sizes in elements
+};
+
+static Layout make_layout(int64_t n, int64_t n_rhs, int64_t T_A, int64_t esize)
+{
+    Layout L;
+    L.T = std::max<int64_t>(1, std::min(T_A, n));
+    L.nt = cdiv(n, L.T);
+    const int64_t al = 256 / esize;
+    L.inv = 0;
+    L.w = align_up(L.nt * L.T * L.T, al);
+    L.tmp = L.w + align_up(n * L.T, al);
+    L.total = L.tmp + align_up(std::max(L.T * L.T, L.T * std::max<int64_t>(n_rhs, 1)), al);
+    return L;
+}
+
+template <typename R, bool CPLX>
+struct Solver {
+    typedef typename Elem<R, CPLX>::type E;
+    static constexpr double FMUL = CPLX ? 4.0 : 1.0;  // real flops per real-type flop
+
+    static int leaves(E *A, int64_t lda, int64_t n, int64_t T, E *Inv, int64_t ldi, int64_t sInv,
+                      int64_t ntiles, bool factor, int *info, int64_t col0, hipStream_t s)
+    {
+        LeafArgs p;
+        p.A = A;
+        p.lda = lda;
+        p.Inv = Inv;
+        p.ldi = ldi;
+        p.sInv = sInv;
+        p.n = (int)n;
+        p.T = (int)T;
+        p.lpt = (int)cdiv(T, LEAF);
+        p.factor = factor ? 1 : 0;
+        p.info = info;
+        p.col0 = (int)col0;
+        const int64_t grid = ntiles * p.lpt;
+        if (grid <= 0)
+            return 0;
+        leaf_kernel<R, CPLX><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p);
+        SPD_CHECK_LAUNCH("leaf_kernel");
+        return 0;
+    }
+
+    // Complete inv(L_tt) from its inverted leaves for `ntiles` tiles of size tk
+    // whose diagonal blocks start at D (stride sD between tiles, leading
+    // dimension lda) and whose inverses start at Inv (stride sInv, ld ldi).
+    // Level h merges blocks [2ph, (2p+1)h) and [(2p+1)h, (2p+2)h):
+    //   X21 = -inv(C) (L21 inv(A)).   Tmp holds the L21 inv(A) products.
+    static int merge_inverses(const E *D, int64_t lda, int64_t sD, E *Inv, int64_t ldi, int64_t sInv,
+                              int64_t ntiles, int64_t tk, E *Tmp, const int *info, hipStream_t s)
+    {
+        for (int64_t h = LEAF; h < tk; h *= 2) {
+            const int64_t nblk = cdiv(tk, h), pairs = nblk / 2;
+            if (pairs == 0)
+                break;
+            const bool ragged = (2 * pairs * h) > tk;
+            const int64_t pf = pairs - (ragged ? 1 : 0);
+            if (pf > 0) {
+                Gemm g1;  // T1 = L21 inv(A)      (h x h) * (h x h)
+                g1.A = D + h;
+                g1.lda = lda;
+                g1.sA_out = sD;
+                g1.sA_in = 2 * h * (1 + lda);
+                g1.B = Inv;
+                g1.ldb = ldi;
+                g1.sB_out = sInv;
+                g1.sB_in = 2 * h * (1 + ldi);
+                g1.C = Tmp;
+                g1.ldc = h;
+                g1.sC_out = pf * h * h;
+                g1.sC_in = h * h;
+                g1.nb_inner = (int)pf;
+                g1.batch = (int)(pf * ntiles);
+                g1.m = h;
+                g1.n = h;
+                g1.k = h;
+                g1.kmode = KM_BEG_BY_J;
+                g1.info = info;
+                SPD_TRY((gemm<R, CPLX>(NN, g1, s)));
+                Gemm g2;  // X21 = -inv(C) T1
+                g2.A = Inv + h * (1 + ldi);
+                g2.lda = ldi;
+                g2.sA_out = sInv;
+                g2.sA_in = 2 * h * (1 + ldi);
+                g2.B = Tmp;
+                g2.ldb = h;
+                g2.sB_out = pf * h * h;
+                g2.sB_in = h * h;
+                g2.C = Inv + h;
+                g2.ldc = ldi;
+                g2.sC_out = sInv;
+                g2.sC_in = 2 * h * (1 + ldi);
+                g2.nb_inner = (int)pf;
+                g2.batch = (int)(pf * ntiles);
+                g2.m = h;
+                g2.n = h;
+                g2.k = h;
+                g2.kmode = KM_END_BY_I;
+                g2.neg = true;
+                g2.info = info;
+                SPD_TRY((gemm<R, CPLX>(NN, g2, s)));
+            }
+            if (ragged) {
+                const int64_t p = pairs - 1, a0 = 2 * p * h, c0 = a0 + h, hc = tk - c0;
+                Gemm g1;
+                g1.A = D + c0 + a0 * lda;
+                g1.lda = lda;
+                g1.sA_out = sD;
+                g1.B = Inv + a0 * (1 + ldi);
+                g1.ldb = ldi;
+                g1.sB_out = sInv;
+                g1.C = Tmp;
+                g1.ldc = hc;
+                g1.sC_out = hc * h;
+                g1.batch = (int)ntiles;
+                g1.m = hc;
+                g1.n = h;
+                g1.k = h;
+                g1.kmode = KM_BEG_BY_J;
+                g1.info = info;
+                SPD_TRY((gemm<R, CPLX>(NN, g1, s)));
+                Gemm g2;
+                g2.A = Inv + c0 * (1 + ldi);
+                g2.lda = ldi;
+                g2.sA_out = sInv;
+                g2.B = Tmp;
+                g2.ldb = hc;
+                g2.sB_out = hc * h;
+                g2.C = Inv + c0 + a0 * ldi;
+                g2.ldc = ldi;
+                g2.sC_out = sInv;
+                g2.batch = (int)ntiles;
+                g2.m = hc;
+                g2.n = h;
+                g2.k = hc;
+                g2.kmode = KM_END_BY_I;
+                g2.neg = true;
+                g2.info = info;
+                SPD_TRY((gemm<R, CPLX>(NN, g2, s)));
+            }
+        }
+        return 0;
+    }
+
+    static int potrf(int64_t n, E *A, int64_t lda, int64_t T_A, int *info, void *work, hipStream_t s)
+    {
+        set_int_kernel<<<1, 1, 0, s>>>(info, 0);
+        SPD_CHECK_LAUNCH("set_int_kernel");
+        if (n == 0)
+            return 0;
+        const Layout L = make_layout(n, 0, T_A, sizeof(E));
+        const int64_t T = L.T;
+        E *Inv = (E *)work + L.inv;  // inverse of the current diagonal tile, ld T
+        E *W = (E *)work + L.w;
+        SPD_TRY(zero2d<E>(Inv, T, T, T, s));
+        for (int64_t c0 = 0; c0 < n; c0 += T) {
+            const int64_t tk = std::min(T, n - c0);
+            E *D = A + c0 + c0 * lda;
+            {
+                ProfScope ps(PROF_DIAG, FMUL * 2.0 * (double)tk * tk * tk / 3.0, s);
+                // ---- 1. diagonal tile, leaf by leaf
+                for (int64_t b0 = 0; b0 < tk; b0 += LEAF) {
+                    const int64_t lb = std::min<int64_t>(LEAF, tk - b0);
+                    E *Db = D + b0 + b0 * lda;
+                    SPD_TRY(leaves(Db, lda, lb, lb, Inv + b0 * (1 + T), T, 0, 1, true, info, c0 + b0, s));
+                    const int64_t r = tk - b0 - lb;
+                    if (r <= 0)
+                        continue;
+                    E *P = Db + lb;  // r x lb below the leaf
+                    Gemm g;          // P <- P inv(Lb)^H, in place (one tile column)
+                    g.A = P;
+                    g.lda = lda;
+                    g.B = Inv + b0 * (1 + T);
+                    g.ldb = T;
+                    g.C = P;
+                    g.ldc = lda;
+                    g.m = r;
+                    g.n = lb;
+                    g.k = lb;
+                    g.kmode = KM_END_BY_J;
+                    g.info = info;
+                    g.inplace = true;
+                    SPD_TRY((gemm<R, CPLX>(NT, g, s)));
+                    Gemm u;  // rest of the tile: lower part of D22 -= P P^H
+                    u.A = P;
+                    u.lda = lda;
+                    u.B = P;
+                    u.ldb = lda;
+                    u.C = P + lb * lda;
+                    u.ldc = lda;
+                    u.m = r;
+                    u.n = r;
+                    u.k = lb;
+                    u.tri = true;
+                    u.neg = true;
+                    u.beta = true;
+                    u.info = info;
+                    SPD_TRY((gemm<R, CPLX>(NT, u, s)));
+                }
+                SPD_TRY(merge_inverses(D, lda, 0, Inv, T, 0, 1, tk, W, info, s));
+            }
+            const int64_t m = n - c0 - tk;
+            if (m <= 0)
+                break;
+            E *P = D + tk;  // m x tk panel
+            {
+                // ---- 2. panel: W = P inv(L_kk)^H, then P = W
+                ProfScope ps(PROF_PANEL, FMUL * (double)m * tk * tk, s);
+                Gemm g;
+                g.A = P;
+                g.lda = lda;
+                g.B = Inv;
+                g.ldb = T;
+                g.C = W;
+                g.ldc = m;
+                g.m = m;
+                g.n = tk;
+                g.k = tk;
+                g.kmode = KM_END_BY_J;
+                g.info = info;
+                SPD_TRY((gemm<R, CPLX>(NT, g, s)));
+                SPD_TRY(copy2d<E>(P, lda, W, m, m, tk, info, s));
+            }
+            {
+                // ---- 3. trailing update: lower part of A22 -= W W^H
+                ProfScope ps(PROF_SYRK, FMUL * (double)m * (double)(m + 1) * (double)tk, s);
+                Gemm u;
+                u.A = W;
+                u.lda = m;
+                u.B = W;
+                u.ldb = m;
+                u.C = P + tk * lda;
+                u.ldc = lda;
+                u.m = m;
+                u.n = m;
+                u.k = tk;
+                u.tri = true;
+                u.neg = true;
+                u.beta = true;
+                u.info = info;
+                SPD_TRY((gemm<R, CPLX>(NT, u, s)));
+            }
+        }
+        return 0;
+    }
+
+    static int potrs(int64_t n, int64_t nrhs, const E *A, int64_t lda, E *B, int64_t ldb, int64_t T_A,
+                     const int *info, void *work, hipStream_t s)
+    {
+        if (n == 0 || nrhs == 0)
+            return 0;
+        const Layout L = make_layout(n, nrhs, T_A, sizeof(E));
+        const int64_t T = L.T, nt = L.nt;
+        E *Inv = (E *)work + L.inv;
+        E *W = (E *)work + L.w;
+        E *Tmp = (E *)work + L.tmp;  // T x nrhs, ld T
+        {
+            ProfScope ps(PROF_SOLVE, FMUL * 2.0 * (double)n * n * nrhs, s);
+            // inverses of every diagonal tile
+            SPD_TRY(zero2d<E>(Inv, T, T, nt * T, s));
+            SPD_TRY(leaves(const_cast<E *>(A), lda, n, T, Inv, T, T * T, nt, false, const_cast<int *>(info), 0, s));
+            const int64_t nfull = (n % T == 0) ? nt : nt - 1;
+            if (nfull > 0)
+                SPD_TRY(merge_inverses(A, lda, T * (1 + lda), Inv, T, T * T, nfull, T, W, info, s));
+            if (nfull < nt) {
+                const int64_t c0 = nfull * T;
+                SPD_TRY(merge_inverses(A + c0 + c0 * lda, lda, 0, Inv + nfull * T * T, T, 0, 1, n - c0, W, info,
+                                       s));
+            }
+            // forward: L Y = B
+            for (int64_t k = 0; k < nt; ++k) {
+                const int64_t c0 = k * T, tk = std::min(T, n - c0), m = n - c0 - tk;
+                Gemm g;  // Tmp = inv(L_kk) B_k
+                g.A = Inv + k * T * T;
+                g.lda = T;
+                g.B = B + c0;
+                g.ldb = ldb;
+                g.C = Tmp;
+                g.ldc = T;
+                g.m = tk;
+                g.n = nrhs;
+                g.k = tk;
+                g.kmode = KM_END_BY_I;
+                g.info = info;
+                SPD_TRY((gemm<R, CPLX>(NN, g, s)));
+                SPD_TRY(copy2d<E>(B + c0, ldb, Tmp, T, tk, nrhs, info, s));
+                if (m > 0) {
+                    Gemm u;  // B_below -= L_panel Y_k
+                    u.A = A + (c0 + tk) + c0 * lda;
+                    u.lda = lda;
+                    u.B = Tmp;
+                    u.ldb = T;
+                    u.C = B + c0 + tk;
+                    u.ldc = ldb;
+                    u.m = m;
+                    u.n = nrhs;
+                    u.k = tk;
+                    u.neg = true;
+                    u.beta = true;
+                    u.info = info;
+                    SPD_TRY((gemm<R, CPLX>(NN, u, s)));
+                }
+            }
+            // backward: L^H X = Y
+            for (int64_t k = nt - 1; k >= 0; --k) {
+                const int64_t c0 = k * T, tk = std::min(T, n - c0);
+                Gemm g;  // Tmp = inv(L_kk)^H Y_k
+                g.A = Inv + k * T * T;
+                g.lda = T;
+                g.B = B + c0;
+                g.ldb = ldb;
+                g.C = Tmp;
+                g.ldc = T;
+                g.m = tk;
+                g.n = nrhs;
+                g.k = tk;
+                g.kmode = KM_BEG_BY_I;
+                g.info = info;
+                SPD_TRY((gemm<R, CPLX>(TN, g, s)));
+                SPD_TRY(copy2d<E>(B + c0, ldb, Tmp, T, tk, nrhs, info, s));
+                if (c0 > 0) {
+                    Gemm u;  // Y_top -= L_k,0:k^H X_k
+                    u.A = A + c0;
+                    u.lda = lda;
+                    u.B = Tmp;
+                    u.ldb = T;
+                    u.C = B;
+                    u.ldc = ldb;
+                    u.m = c0;
+                    u.n = nrhs;
+                    u.k = tk;
+                    u.neg = true;
+                    u.beta = true;
+                    u.info = info;
+                    SPD_TRY((gemm<R, CPLX>(TN, u, s)));
+                }
+            }
+        }
+        {
+            const int64_t blocks = std::min<int64_t>(cdiv(n * nrhs, 256), 4096);
+            nan_fill_kernel<R, CPLX><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(B, ldb, n, nrhs, info);
+            SPD_CHECK_LAUNCH("nan_fill_kernel");
+        }
+        return 0;
+    }
+
+    static int logdet(int64_t n, const E *A, int64_t lda, const int *info, double *out, hipStream_t s)
+    {
+        logdet_kernel<R, CPLX><<<1, 1024, 0, s>>>(A, lda, n, info, out);
+        SPD_CHECK_LAUNCH("logdet_kernel");
+        return 0;
+    }
+};
+
+static int64_t elem_size(int dt)
+{
+    switch (dt) {
+    case SPD_R32: return 4;
+    case SPD_R64: return 8;
+    case SPD_C64: return 8;
+    case SPD_C128: return 16;
+    default: return 0;
+    }
+}
+
+}  // namespace spd
+
+using namespace spd;
+
+extern "C" {
+
+size_t spd_workspace_size(spd_dtype_t dt, int64_t n, int64_t n_rhs, int64_t T_A)
+{
+    const int64_t es = elem_size(dt);
+    if (es == 0 || n < 0 || n_rhs < 0 || T_A < 1 || n == 0)
+        return 0;
+    return (size_t)(make_layout(n, n_rhs, T_A, es).total * es);
+}
+
+int spd_potrf(spd_dtype_t dt, int64_t n, void *dA, int64_t lda, int64_t T_A, int32_t *d_info, void *d_work,
+              size_t work_bytes, void *stream)
+{
+    if (elem_size(dt) == 0) return -1;
+    if (n < 0 || n > INT32_MAX) return -2;
+    if (dA == nullptr && n > 0) return -3;
+    if (lda < std::max<int64_t>(1, n)) return -4;
+    if (T_A < 1) return -5;
+    if (d_info == nullptr) return -6;
+    const size_t need = spd_workspace_size(dt, n, 0, T_A);
+    if (d_work == nullptr && need > 0) return -7;
+    if (work_bytes < need) return -8;
+    hipStream_t s = (hipStream_t)stream;
+    switch (dt) {
+    case SPD_R32: return Solver<float, false>::potrf(n, (float *)dA, lda, T_A, d_info, d_work, s);
+    case SPD_R64: return Solver<double, false>::potrf(n, (double *)dA, lda, T_A, d_info, d_work, s);
+    case SPD_C64:
+        return Solver<float, true>::potrf(n, (Elem<float, true>::type *)dA, lda, T_A, d_info, d_work, s);
+    case SPD_C128:
+        return Solver<double, true>::potrf(n, (Elem<double, true>::type *)dA, lda, T_A, d_info, d_work, s);
+    }
+    return -1;
+}
+
+int spd_potrs(spd_dtype_t dt, int64_t n, int64_t n_rhs, const void *dA, int64_t lda, void *dB, int64_t ldb,
+              int64_t T_A, const int32_t *d_info, void *d_work, size_t work_bytes, void *stream)
+{
+    if (elem_size(dt) == 0) return -1;
+    if (n < 0 || n > INT32_MAX) return -2;
+    if (n_rhs < 0 || n_rhs > INT32_MAX) return -3;
+    if (dA == nullptr && n > 0) return -4;
+    if (lda < std::max<int64_t>(1, n)) return -5;
+    if (dB == nullptr && n > 0 && n_rhs > 0) return -6;
+    if (ldb < std::max<int64_t>(1, n)) return -7;
+    if (T_A < 1) return -8;
+    const size_t need = spd_workspace_size(dt, n, n_rhs, T_A);
+    if (d_work == nullptr && need > 0) return -10;
+    if (work_bytes < need) return -11;
+    hipStream_t s = (hipStream_t)stream;
+    switch (dt) {
+    case SPD_R32:
+        return Solver<float, false>::potrs(n, n_rhs, (const float *)dA, lda, (float *)dB, ldb, T_A, d_info, d_work, s);
+    case SPD_R64:
+        return Solver<double, false>::potrs(n, n_rhs, (const double *)dA, lda, (double *)dB, ldb, T_A, d_info,
+                                            d_work, s);
+    case SPD_C64:
+        return Solver<float, true>::potrs(n, n_rhs, (const Elem<float, true>::type *)dA, lda,
+                                          (Elem<float, true>::type *)dB, ldb, T_A, d_info, d_work, s);
+    case SPD_C128:
+        return Solver<double, true>::potrs(n, n_rhs, (const Elem<double, true>::type *)dA, lda,
+                                           (Elem<double, true>::type *)dB, ldb, T_A, d_info, d_work, s);
+    }
+    return -1;
+}
+
+int spd_logdet(spd_dtype_t dt, int64_t n, const void *dA, int64_t lda, const int32_t *d_info, double *d_logdet,
+               void *stream)
+{
+    if (elem_size(dt) == 0) return -1;
+    if (n < 0) return -2;
+    if (dA == nullptr && n > 0) return -3;
+    if (lda < std::max<int64_t>(1, n)) return -4;
+    if (d_logdet == nullptr) return -6;
+    hipStream_t s = (hipStream_t)stream;
+    switch (dt) {
+    case SPD_R32: return Solver<float, false>::logdet(n, (const float *)dA, lda, d_info, d_logdet, s);
+    case SPD_R64: return Solver<double, false>::logdet(n, (const double *)dA, lda, d_info, d_logdet, s);
+    case SPD_C64:
+        return Solver<float, true>::logdet(n, (const Elem<float, true>::type *)dA, lda, d_info, d_logdet, s);
+    case SPD_C128:
+        return Solver<double, true>::logdet(n, (const Elem<double, true>::type *)dA, lda, d_info, d_logdet, s);
+    }
+    return -1;
+}
+
+const char *spd_last_error(void) { return g_last_error.c_str(); }
+
+int spd_profile_enable(int mask)
+{
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    g_prof_mask = mask;
+    return 0;
+}
+
+int spd_profile_read(int kernel_class, double *ms, int64_t *launches, double *flops)
+{
+    if (kernel_class < 0 || kernel_class > 3)
+        return -1;
+    std::vector<ProfRec> mine;
+    {
+        std::lock_guard<std::mutex> g(g_prof_mu);
+        std::vector<ProfRec> rest;
+        for (auto &r : g_prof)
+            (r.cls == kernel_class ? mine : rest).push_back(r);
+        g_prof.swap(rest);
+    }
+    double tot = 0.0, fl = 0.0;
+    int rc = 0;
+    for (auto &r : mine) {
+        float t = 0.f;
+        hipError_t e = hipEventSynchronize(r.b);
+        if (e == hipSuccess)
+            e = hipEventElapsedTime(&t, r.a, r.b);
+        if (e != hipSuccess && rc == 0)
+            rc = hip_fail(e, "spd_profile_read");
+        tot += t;
+        fl += r.flops;
+        (void)hipEventDestroy(r.a);
+        (void)hipEventDestroy(r.b);
+    }
+    if (ms) *ms = tot;
+    if (launches) *launches = (int64_t)mine.size();
+    if (flops) *flops = fl;
+    return rc;
+}
+
+}  // extern "C"

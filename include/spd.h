@@ -1,0 +1,127 @@
+/*
+ * spd.h - C ABI of the MI355X (gfx950) dense symmetric / Hermitian
+ * positive-definite solver: blocked Cholesky factorization (potrf), the
+ * triangular solves that use it (potrs) and the log-determinant (logdet).
+ *
+ * The operation (JAXMg paper, "Software design", the potrs routine): solve
+ * A X = B for an N x N symmetric (Hermitian) positive-definite A and an
+ * N x N_RHS right-hand side B through the Cholesky factorization A = L L^H,
+ * and optionally return log det(A) from the same factor.  The tile size T_A
+ * is the caller's throughput / memory knob (same paper, "Software design" and
+ * Figure 4); here it is the outer panel width of the right-looking blocked
+ * factorization and the block size of the blocked triangular solves.
+ * Supported element types: float32, float64, complex64, complex128 (same
+ * paper, "Software design": all four dtypes).
+ *
+ * Conventions shared by every entry point
+ *   - Matrices are column-major: element (i, j) of A is at A[i + j*lda].
+ *     Complex elements are (real, imaginary) pairs, as C99 / std::complex.
+ *   - Only the lower triangle of A (i >= j) is read or written; the strict
+ *     upper triangle and the rows [n, lda) of every column are never touched.
+ *     For complex A only the real part of the diagonal is read.
+ *   - Buffers are transformed in place: potrf overwrites the lower triangle of
+ *     A with L (real positive diagonal); potrs overwrites B with X.
+ *   - All pointers named d_* or dA/dB are device pointers owned by the caller.
+ *     The library allocates no device memory and keeps no state between calls
+ *     (except while profiling is switched on, see spd_profile_*).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     the calls return without waiting for it.  Numerical status is reported on
+ *     the device through d_info, so no host synchronisation happens inside.
+ *   - Return value: 0 when the work was enqueued; -i when the i-th argument is
+ *     invalid (nothing is enqueued); SPD_ERR_HIP when the HIP runtime reported
+ *     an error while enqueueing (spd_last_error() describes it).
+ *   - Calls on one stream run in order; calls that share a workspace must not
+ *     run concurrently.
+ */
+#ifndef SPD_H
+#define SPD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SPD_R32 = 0,  /* float                */
+    SPD_R64 = 1,  /* double               */
+    SPD_C64 = 2,  /* complex float        */
+    SPD_C128 = 3  /* complex double       */
+} spd_dtype_t;
+
+#define SPD_ERR_HIP 1
+
+/* Bytes of device workspace that spd_potrf and spd_potrs need for these
+ * sizes (one workspace serves both).  Returns 0 for invalid arguments
+ * (n < 0, n_rhs < 0, T_A < 1, unknown dtype) and for n == 0. */
+size_t spd_workspace_size(spd_dtype_t dt, int64_t n, int64_t n_rhs, int64_t T_A);
+
+/* Cholesky factorization A = L L^H (JAXMg paper, "Software design": the
+ * factorization step of potrs).
+ *   dt        element type
+ *   n         order of A, n >= 0
+ *   dA        device, n x n column-major, leading dimension lda; on exit the
+ *             lower triangle holds L (diagonal real, > 0)
+ *   lda       >= max(1, n)
+ *   T_A       tile size >= 1 (values > n mean one tile); n need not be a
+ *             multiple of T_A
+ *   d_info    device int32, written by the call: 0 on success, or j > 0 when
+ *             the leading minor of order j is not positive definite (the pivot
+ *             of column j-1 is <= 0 or NaN); then the factorization stopped
+ *             there and the contents of the lower triangle from column j-1 on
+ *             are unspecified
+ *   d_work    device workspace of work_bytes >= spd_workspace_size(dt, n, 0, T_A)
+ *             bytes (may be NULL when that size is 0)
+ *   stream    hipStream_t
+ * Argument numbers for the -i return: dt=1 n=2 dA=3 lda=4 T_A=5 d_info=6
+ * d_work=7 work_bytes=8. */
+int spd_potrf(spd_dtype_t dt, int64_t n, void *dA, int64_t lda, int64_t T_A,
+              int32_t *d_info, void *d_work, size_t work_bytes, void *stream);
+
+/* Solve A X = B from the factor of spd_potrf: L Y = B, then L^H X = Y
+ * (JAXMg paper, "Software design": potrs; B is N x N_RHS).
+ *   dA, lda   the factor L as left by spd_potrf (lower triangle read only)
+ *   dB, ldb   device, n x n_rhs column-major, ldb >= max(1, n); overwritten by X
+ *   T_A       block size of the blocked substitution (any value >= 1)
+ *   d_info    the d_info written by spd_potrf (may be NULL: treated as 0);
+ *             if it is non-zero every entry of X is set to NaN
+ *   d_work    workspace of >= spd_workspace_size(dt, n, n_rhs, T_A) bytes
+ * Argument numbers: dt=1 n=2 n_rhs=3 dA=4 lda=5 dB=6 ldb=7 T_A=8 d_info=9
+ * d_work=10 work_bytes=11. */
+int spd_potrs(spd_dtype_t dt, int64_t n, int64_t n_rhs, const void *dA, int64_t lda,
+              void *dB, int64_t ldb, int64_t T_A, const int32_t *d_info,
+              void *d_work, size_t work_bytes, void *stream);
+
+/* log det(A) = 2 * sum_i log(Re L_ii) from the factor L of spd_potrf (JAXMg
+ * paper, "Software design": the same factorization can return log det(A);
+ * "Cholesky solve (potrs)": the log-determinant term of the Gaussian-process
+ * marginal likelihood).  Accumulated in double for every dtype by a fixed
+ * reduction tree, so repeated calls give identical bits.
+ *   dA, lda    the factor L
+ *   d_info     the d_info of spd_potrf (may be NULL); non-zero gives NaN
+ *   d_logdet   device double, written by the call (0 for n == 0)
+ * Argument numbers: dt=1 n=2 dA=3 lda=4 d_info=5 d_logdet=6. */
+int spd_logdet(spd_dtype_t dt, int64_t n, const void *dA, int64_t lda,
+               const int32_t *d_info, double *d_logdet, void *stream);
+
+/* Text of the last HIP error seen by this library in the calling thread. */
+const char *spd_last_error(void);
+
+/* Kernel timing for measurement harnesses.  While enabled (mask != 0), every
+ * launch of the selected kernel classes is bracketed by HIP events recorded
+ * on its stream; spd_profile_read synchronises on those events and returns,
+ * for one class, the summed kernel time in milliseconds, the number of
+ * launches and their algorithmic flop count (real-equivalent flops: a complex
+ * multiply-add counts 8), then forgets that class's events.
+ * Classes: bit 0 = trailing update (A22 -= L21 L21^H), bit 1 = panel solve,
+ * bit 2 = diagonal-tile factorization and inversion, bit 3 = substitution.
+ * Returns 0, or -1 for an unknown class, SPD_ERR_HIP on a HIP error. */
+int spd_profile_enable(int mask);
+int spd_profile_read(int kernel_class, double *ms, int64_t *launches, double *flops);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPD_H */

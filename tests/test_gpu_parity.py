@@ -1,0 +1,328 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Small and medium sizes are compared element by element with the oracle run on
+the very same input bytes.  The three large workloads (fp32 N=16384,
+complex128 N=8192, fp64 N=32768) are too big for the unblocked oracle, so there
+the oracle computes sampled outputs (the leading 2*T_A columns of L and the
+same columns of sampled rows, which depend only on the leading principal
+block plus those rows) and the rest is checked through properties that hold
+at any size: the normwise backward error of X, the factorization residual at
+sampled entries, and log det recomputed from the factor's diagonal.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import spdgen
+from helpers import (EPS, L_TOL, LOGDET_TOL, TORCH, X_TOL, backward_error, logdet_rel, rel_err_cols, wide)
+
+pytestmark = pytest.mark.gpu
+
+
+def cm_copy(t: torch.Tensor, ld: int | None = None, pad_value=0.0) -> torch.Tensor:
+    """Column-major copy of a logical matrix (on the same device)."""
+    return spdgen.to_colmajor(t, ld, pad_value)
+
+
+def bits(t: torch.Tensor) -> torch.Tensor:
+    t = torch.view_as_real(t) if t.is_complex() else t
+    return t.contiguous().view(torch.int64 if t.dtype == torch.float64 else torch.int32)
+
+
+def gpu_solve(spd, A, B, T_A, want_logdet=True):
+    """potrf -> logdet -> potrs in place on A and B; returns (info, logdet)."""
+    n = A.shape[0]
+    nrhs = B.shape[1]
+    work = spd.workspace(A.dtype, n, nrhs, T_A)
+    info = spd.potrf(A, T_A, work=work)
+    ld = spd.logdet(A, info) if want_logdet else None
+    spd.potrs(A, B, T_A, info=info, work=work)
+    torch.cuda.synchronize()
+    return int(info.item()), (float(ld.item()) if ld is not None else None)
+
+
+def check_against_oracle(spd, dt, n, nrhs, T_A, seed=0, delta=0.5, A=None, B=None):
+    if A is None:
+        A = spdgen.make_A(n, dt, delta, seed, device="cuda")
+    if B is None:
+        B = spdgen.make_B(n, nrhs, dt, seed, device="cuda")
+    A_np = wide(A)  # the exact input bytes, widened for the oracle
+    B_np = wide(B)
+    L = cm_copy(A)
+    X = cm_copy(B)
+    info, ld = gpu_solve(spd, L, X, T_A)
+    assert info == 0
+    Lo, info_o = oracle.potrf(A_np)
+    assert info_o == 0
+    Xo = oracle.potrs(Lo, B_np)
+    ldo = oracle.logdet(Lo)
+
+    Lg = np.tril(wide(L))
+    err_L = np.abs(Lg - Lo).max() / np.abs(Lo).max()
+    err_x = rel_err_cols(X, Xo)
+    eta = backward_error(A, X, B)
+    err_ld = logdet_rel(ld, ldo)
+    tol_ld = LOGDET_TOL if dt in ("f64", "c128") else 1e-4
+    msg = f"{dt} n={n} nrhs={nrhs} T_A={T_A}: L {err_L:.2e} x {err_x:.2e} eta {eta:.2e} logdet {err_ld:.2e}"
+    print(msg)
+    assert err_L <= L_TOL[dt], msg
+    assert err_x <= X_TOL[dt], msg
+    assert eta <= 64 * n * EPS[dt], msg
+    assert err_ld <= tol_ld, msg
+    return L, X, ld
+
+
+SMALL_CASES = [
+    ("f64", 1, 1, 64), ("f64", 2, 3, 1), ("f64", 63, 2, 16), ("f64", 64, 1, 64), ("f64", 65, 5, 64),
+    ("f64", 127, 4, 32), ("f64", 130, 7, 100), ("f64", 300, 16, 128), ("f64", 777, 3, 1000),
+    ("f64", 1000, 33, 256), ("f64", 1500, 8, 512), ("f64", 2100, 130, 192),
+    ("f32", 65, 2, 64), ("f32", 300, 16, 128), ("f32", 1000, 33, 256), ("f32", 1500, 64, 512),
+    ("c128", 1, 1, 8), ("c128", 65, 3, 64), ("c128", 300, 16, 100), ("c128", 1000, 32, 256),
+    ("c64", 130, 4, 64), ("c64", 700, 8, 256),
+]
+
+
+@pytest.mark.parametrize("dt,n,nrhs,T_A", SMALL_CASES)
+def test_parity_sweep(gpu, dt, n, nrhs, T_A):
+    check_against_oracle(gpu, dt, n, nrhs, T_A, seed=n % 7)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_config1_full(gpu, seed):
+    """fp64 N=256, N_RHS=1, T_A=64, A = G G^T/N + I: element-by-element."""
+    A, B, c = spdgen.make_config(1, seed, device="cuda")
+    check_against_oracle(gpu, c["dtype"], c["n"], c["nrhs"], c["T_A"], A=A, B=B)
+
+
+def test_config2_full(gpu):
+    """fp64 N=4096, N_RHS=16, T_A=256, delta=0.1: element-by-element."""
+    A, B, c = spdgen.make_config(2, 0, device="cuda")
+    check_against_oracle(gpu, c["dtype"], c["n"], c["nrhs"], c["T_A"], A=A, B=B)
+
+
+# ----------------------------------------------------- large workloads ---
+
+def sampled_parity(spd, k: int, seed: int = 0):
+    A, B, c = spdgen.make_config(k, seed, device="cuda")
+    dt, n, nrhs, T = c["dtype"], c["n"], c["nrhs"], c["T_A"]
+    L = cm_copy(A)
+    X = cm_copy(B)
+    info, ld = gpu_solve(spd, L, X, T, want_logdet=True)
+    assert info == 0
+
+    # (1) sampled outputs the oracle computes exactly: columns [0, K) of L on
+    # the rows [0, K) and on sampled rows R.  Cholesky of the principal block
+    # on S = [0, K) + R has these entries (its first K columns only involve
+    # A[S, :K] and earlier columns).
+    K = min(n, 2 * T)
+    rng = np.random.default_rng(1000 + k)
+    tail = np.arange(max(K, n - 5), n)
+    R = np.unique(np.concatenate([rng.choice(np.arange(K, n), 96, replace=False), tail]))
+    S = np.concatenate([np.arange(K), R])
+    St = torch.from_numpy(S).cuda()
+    A_sub = wide(A[St][:, St])
+    Lo, info_o = oracle.potrf(A_sub)
+    assert info_o == 0
+    Lg_sub = wide(L[St][:, :K])
+    Lg_sub = np.where(np.arange(len(S))[:, None] >= np.arange(K)[None, :], Lg_sub, 0)
+    err_L = np.abs(Lg_sub - Lo[:, :K]).max() / np.abs(Lo[:, :K]).max()
+    assert err_L <= L_TOL[dt], err_L
+    d = wide(torch.diagonal(L)).real
+    pre = 2.0 * np.sum(np.log(d[:K]))
+    pre_o = oracle.logdet(Lo[:K, :K])
+    tol_ld = LOGDET_TOL if dt in ("f64", "c128") else 1e-4
+    assert logdet_rel(pre, pre_o) <= tol_ld
+
+    # (2) log det: the device reduction against the factor's own diagonal
+    full = 2.0 * math.fsum(np.log(d))
+    assert logdet_rel(ld, full) <= 1e-13
+
+    # (3) normwise backward error of X (residual in double on the GPU)
+    eta = backward_error(A, X, B)
+    assert eta <= 64 * n * EPS[dt], eta
+
+    # (4) factorization residual at sampled entries (i >= j):
+    #     |A_ij - sum_k L_ik conj(L_jk)| <= 64 n eps sum_k |L_ik||L_jk|
+    ii = rng.integers(0, n, 200)
+    jj = (rng.random(200) * (ii + 1)).astype(np.int64)
+    Lr_i = wide(L[torch.from_numpy(ii).cuda()])
+    Lr_j = wide(L[torch.from_numpy(jj).cuda()])
+    Aw = wide(A[torch.from_numpy(ii).cuda(), torch.from_numpy(jj).cuda()])
+    worst = 0.0
+    for t in range(len(ii)):
+        i, j = ii[t], jj[t]
+        li, lj = Lr_i[t, : j + 1], Lr_j[t, : j + 1]
+        r = abs(Aw[t] - np.sum(li * np.conj(lj)))
+        bound = 64 * n * EPS[dt] * np.sum(np.abs(li) * np.abs(lj))
+        worst = max(worst, r / bound)
+    assert worst <= 1.0, worst
+
+    # (5) independent library cross-check (torch / rocSOLVER Cholesky)
+    Ld = torch.linalg.cholesky(A)
+    Xr = torch.cholesky_solve(B, Ld)
+    err_x = rel_err_cols(X, Xr)
+    assert err_x <= X_TOL[dt], err_x
+    ldr = 2.0 * float(torch.log(torch.diagonal(Ld).real.double()).sum().item())
+    assert logdet_rel(ld, ldr) <= tol_ld
+    print(f"config {k}: L[:, :{K}] {err_L:.2e} eta {eta:.2e} residual/bound {worst:.2e} "
+          f"x vs library {err_x:.2e} logdet {ld:.10g}")
+
+
+def test_config3_sampled(gpu):
+    sampled_parity(gpu, 3)
+
+
+def test_config4_sampled(gpu):
+    sampled_parity(gpu, 4)
+
+
+def test_config5_sampled(gpu):
+    sampled_parity(gpu, 5)
+
+
+# ------------------------------------------------------- invariants -------
+
+def test_pages_benchmark_input(gpu):
+    """A = diag(1..N), b = ones (the JAXMg paper's potrs benchmark input):
+    x_i = 1/i, log det = ln N!."""
+    for n, T in ((256, 64), (2048, 512), (1000, 96)):
+        A, B = spdgen.diag_benchmark(n, 2, "f64", device="cuda")
+        info, ld = gpu_solve(gpu, A, B, T)
+        assert info == 0
+        xe = 1.0 / np.arange(1, n + 1)
+        np.testing.assert_allclose(wide(B)[:, 0], xe, rtol=4 * EPS["f64"], atol=0)
+        np.testing.assert_allclose(wide(B)[:, 1], xe, rtol=4 * EPS["f64"], atol=0)
+        assert logdet_rel(ld, math.lgamma(n + 1)) <= 1e-13
+
+
+@pytest.mark.parametrize("dt", ["f64", "c128", "f32"])
+def test_deterministic(gpu, dt):
+    n, nrhs, T = 700, 9, 128
+    A = spdgen.make_A(n, dt, 0.3, 5, device="cuda")
+    B = spdgen.make_B(n, nrhs, dt, 5, device="cuda")
+    outs = []
+    for _ in range(2):
+        L, X = cm_copy(A), cm_copy(B)
+        info, ld = gpu_solve(gpu, L, X, T)
+        assert info == 0
+        outs.append((torch.tril(L).clone(), X.clone(), ld))
+    assert torch.equal(outs[0][0], outs[1][0])
+    assert torch.equal(outs[0][1], outs[1][1])
+    assert outs[0][2] == outs[1][2]
+
+
+def test_power_of_two_scaling(gpu):
+    """A -> 4A must give exactly L -> 2L and X -> X/4 (every operation scales
+    by a power of two)."""
+    n, nrhs, T = 600, 5, 128
+    A = spdgen.make_A(n, "f64", 0.2, 8, device="cuda")
+    B = spdgen.make_B(n, nrhs, "f64", 8, device="cuda")
+    L1, X1 = cm_copy(A), cm_copy(B)
+    gpu_solve(gpu, L1, X1, T)
+    L4, X4 = cm_copy(A * 4.0), cm_copy(B)
+    gpu_solve(gpu, L4, X4, T)
+    assert torch.equal(torch.tril(L4), 2.0 * torch.tril(L1))
+    assert torch.equal(X4, X1 / 4.0)
+
+
+@pytest.mark.parametrize("dt", ["f64", "c128"])
+def test_upper_triangle_and_padding_untouched(gpu, dt):
+    """NaN in the strict upper triangle and in the lda/ldb padding must be
+    ignored and left exactly as it was."""
+    n, nrhs, T = 333, 6, 64
+    A = spdgen.make_A(n, dt, 0.5, 3, device="cuda")
+    B = spdgen.make_B(n, nrhs, dt, 3, device="cuda")
+    lda, ldb = n + 5, n + 3
+    Lp = cm_copy(A, lda, pad_value=float("nan"))
+    iu = torch.triu_indices(n, n, 1, device="cuda")
+    Lp[iu[0], iu[1]] = float("nan")
+    Xp = cm_copy(B, ldb, pad_value=float("nan"))
+    base_A = Lp.as_strided((lda * n,), (1,)).clone()
+    base_B = Xp.as_strided((ldb * nrhs,), (1,)).clone()
+    info, ld = gpu_solve(gpu, Lp, Xp, T)
+    assert info == 0
+    Lc, Xc = cm_copy(A), cm_copy(B)
+    info2, ld2 = gpu_solve(gpu, Lc, Xc, T)
+    assert torch.equal(torch.tril(Lp), torch.tril(Lc))
+    assert torch.equal(Xp, Xc)
+    assert ld == ld2
+    after_A = Lp.as_strided((lda * n,), (1,))
+    after_B = Xp.as_strided((ldb * nrhs,), (1,))
+    # the upper triangle and padding keep their exact bits (NaN)
+    colA = torch.arange(n, device="cuda").repeat_interleave(lda)
+    rowA = torch.arange(lda, device="cuda").repeat(n)
+    untouched = (rowA < colA) | (rowA >= n)
+    assert torch.equal(bits(after_A[untouched]), bits(base_A[untouched]))
+    rowB = torch.arange(ldb, device="cuda").repeat(nrhs)
+    assert torch.equal(bits(after_B[rowB >= n]), bits(base_B[rowB >= n]))
+
+
+@pytest.mark.parametrize("j", [0, 5, 64, 100, 299])
+def test_info_negative_pivot(gpu, j):
+    n, T = 300, 64
+    A = spdgen.make_A(n, "f64", 0.5, 4, device="cuda")
+    A[j, j] = -1.0
+    _, info_o = oracle.potrf(wide(A))
+    L, X = cm_copy(A), cm_copy(spdgen.make_B(n, 2, "f64", 4, device="cuda"))
+    info, ld = gpu_solve(gpu, L, X, T)
+    assert info == info_o == j + 1
+    assert math.isnan(ld)
+    assert torch.isnan(X).all()
+
+
+def test_info_nan_and_zero(gpu):
+    n = 100
+    A = spdgen.make_A(n, "c128", 0.5, 4, device="cuda")
+    A[0, 0] = float("nan")
+    L, X = cm_copy(A), cm_copy(spdgen.make_B(n, 1, "c128", 4, device="cuda"))
+    info, ld = gpu_solve(gpu, L, X, 32)
+    assert info == 1 and math.isnan(ld)
+    Z = spdgen.to_colmajor(torch.zeros(n, n, dtype=torch.float64, device="cuda"))
+    X = spdgen.to_colmajor(torch.ones(n, 1, dtype=torch.float64, device="cuda"))
+    info, ld = gpu_solve(gpu, Z, X, 32)
+    assert info == 1 and math.isnan(ld) and torch.isnan(X).all()
+    with pytest.raises(gpu.LinAlgError):
+        gpu.solve(spdgen.to_colmajor(torch.zeros(4, 4, dtype=torch.float64, device="cuda")),
+                  spdgen.to_colmajor(torch.ones(4, 1, dtype=torch.float64, device="cuda")), 2)
+
+
+def test_empty(gpu):
+    A = torch.empty((0, 0), dtype=torch.float64, device="cuda")
+    info = gpu.potrf(A, 16)
+    ld = gpu.logdet(A, info)
+    torch.cuda.synchronize()
+    assert int(info.item()) == 0 and float(ld.item()) == 0.0
+
+
+def test_rhs_chunks_bitwise(gpu):
+    """Each column of X depends only on its own column of B."""
+    n, nrhs, T = 520, 40, 128
+    A = spdgen.make_A(n, "f64", 0.5, 9, device="cuda")
+    B = spdgen.make_B(n, nrhs, "f64", 9, device="cuda")
+    L = cm_copy(A)
+    work = gpu.workspace(L.dtype, n, nrhs, T)
+    info = gpu.potrf(L, T, work=work)
+    Xall = cm_copy(B)
+    gpu.potrs(L, Xall, T, info=info, work=work)
+    parts = []
+    for c0 in range(0, nrhs, 7):
+        Xc = cm_copy(B[:, c0:c0 + 7])
+        gpu.potrs(L, Xc, T, info=info, work=work)
+        parts.append(Xc)
+    torch.cuda.synchronize()
+    assert torch.equal(Xall, torch.cat(parts, dim=1))
+
+
+def test_binding_rejects_bad_arguments(gpu):
+    A = spdgen.make_A(8, "f64", 0.5, 0, device="cuda")
+    with pytest.raises(ValueError):
+        gpu.potrf(A[:, :7], 4)  # not square
+    with pytest.raises(ValueError, match="argument 5"):
+        gpu.potrf(A, 0)  # T_A < 1
+    with pytest.raises(ValueError):
+        gpu.potrf(torch.empty(8, 8, device="cuda", dtype=torch.float64), 4)  # row-major storage
