@@ -23,7 +23,8 @@
 // loads for slice s+1 are in flight while slice s feeds the matrix cores.
 // The MFMA's A-source is fed from opB and its B-source from opA, so that a
 // lane's four accumulator registers hold four C columns of one row and each
-// 16-lane group reads/writes one contiguous 16-element column segment of C.
+// 16-lane group reads/writes one contiguous 16-element column segment of C
+// (which four columns depends on the instruction, see acc_row).
 //
 // Complex types keep real and imaginary parts in separate LDS planes and use
 // four real MFMAs per complex multiply-add.
@@ -49,6 +50,14 @@ __device__ __forceinline__ fx4 mfma16(float a, float b, fx4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
+
+// Row of the 16x16 MFMA result held by accumulator register q of a lane in
+// lane group g = lane / 16 (the column is lane % 16).  The fp32 instruction
+// gives each lane group four consecutive rows; the fp64 one interleaves the
+// groups (measured on gfx950 with a known-input probe).
+template <typename R> __device__ __forceinline__ int acc_row(int g, int q);
+template <> __device__ __forceinline__ int acc_row<float>(int g, int q) { return 4 * g + q; }
+template <> __device__ __forceinline__ int acc_row<double>(int g, int q) { return 4 * q + g; }
 
 // k-range restriction for triangular operands whose zero triangle is stored
 // explicitly (the inverted diagonal blocks): skip slices that are all zero.
@@ -196,7 +205,7 @@ gemm_kernel(const GemmArgs p)
             for (int fj = 0; fj < FN; ++fj) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int j = j0 + jb + fj * 16 + lk * 4 + q;
+                    const int j = j0 + jb + fj * 16 + acc_row<R>(lk, q);
                     if (i < m && j < n) {
                         R re, im = 0;
                         Elem<R, CPLX>::load(C + i + (int64_t)j * p.ldc, re, im);
@@ -322,7 +331,7 @@ gemm_kernel(const GemmArgs p)
         for (int fj = 0; fj < FN; ++fj) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int j = j0 + jb + fj * 16 + lk * 4 + q;
+                const int j = j0 + jb + fj * 16 + acc_row<R>(lk, q);
                 if (i < m && j < n && (!p.tri || i >= j))
                     Elem<R, CPLX>::store(C + i + (int64_t)j * p.ldc, acc[0][fi][fj][q],
                                          CPLX ? acc[NP - 1][fi][fj][q] : R(0));
