@@ -157,7 +157,7 @@ def main():
     syrk_achieved = (syrk_flops / syrk_launches) / (syrk_avg_ms * 1e-3) / 1e12 if syrk_launches else None
     peak = PEAK[dt]
     roofline = {
-        "kernel": "gemm_kernel (trailing update A22 -= L21 L21^H, lower tiles)",
+        "kernel": "syrk_kernel (trailing update A22 -= L21 L21^H, lower tiles)",
         "bound": "mfma",
         "achieved": syrk_achieved,
         "peak": peak,

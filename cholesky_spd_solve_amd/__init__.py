@@ -32,7 +32,8 @@ DTYPE_CODE = {
     torch.complex128: SPD_C128,
 }
 SYMBOLS = ("spd_workspace_size", "spd_potrf", "spd_potrs", "spd_logdet", "spd_last_error",
-           "spd_profile_enable", "spd_profile_read")
+           "spd_profile_enable", "spd_profile_read", "spd_debug_validate")
+SPD_ERR_HIP, SPD_ERR_CHECK = 1, 2
 PROF_SYRK, PROF_PANEL, PROF_DIAG, PROF_SOLVE = 0, 1, 2, 3
 
 _lock = threading.Lock()
@@ -79,6 +80,8 @@ def load():
             lib.spd_profile_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double),
                                              ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]
             lib.spd_profile_read.restype = i32
+            lib.spd_debug_validate.argtypes = [i32]
+            lib.spd_debug_validate.restype = i32
             _lib = lib
     return _lib
 
@@ -89,7 +92,8 @@ def _check(rc: int, what: str):
     if rc < 0:
         raise ValueError(f"{what}: argument {-rc} is invalid")
     msg = load().spd_last_error().decode(errors="replace")
-    raise SpdError(f"{what}: HIP error: {msg}")
+    kind = "launch validation failed" if rc == SPD_ERR_CHECK else "HIP error"
+    raise SpdError(f"{what}: {kind}: {msg}")
 
 
 def _code(t: torch.Tensor) -> int:
@@ -198,6 +202,12 @@ def solve(A: torch.Tensor, B: torch.Tensor, T_A: int, want_logdet: bool = False,
     if want_logdet:
         return B, float(ld.item())
     return B
+
+
+def debug_validate(mode: int) -> None:
+    """Launch validation: 0 off, 1 replay every launch's addresses on the host
+    before enqueueing it, 2 replay only (dry run, no GPU work)."""
+    _check(load().spd_debug_validate(int(mode)), "spd_debug_validate")
 
 
 def profile_enable(mask: int) -> None:

@@ -26,6 +26,8 @@
 #include "spd.h"
 #include "spd_gemm.hpp"
 #include "spd_kernels.hpp"
+#include "spd_syrk.hpp"
+#include "spd_check.hpp"
 
 namespace spd {
 
@@ -36,6 +38,29 @@ static int hip_fail(hipError_t e, const char *where)
     g_last_error = std::string(where) + ": " + hipGetErrorString(e);
     return SPD_ERR_HIP;
 }
+
+// Launch validation (spd_debug_validate): 0 off, 1 replay each launch on the
+// host before enqueueing it, 2 replay only (no GPU work, no HIP calls).
+static int g_validate = 0;
+static thread_local Checker g_chk;
+
+static int check_fail()
+{
+    g_last_error = "launch validation: " + g_chk.err;
+    return SPD_ERR_CHECK;
+}
+
+// Replays a launch on the host when validation is on; returns 0 to go on,
+// -1 to skip the launch (dry run), or an error code.
+#define SPD_VALIDATE(check_expr)             \
+    do {                                     \
+        if (g_validate) {                    \
+            if (!(check_expr))               \
+                return check_fail();         \
+            if (g_validate == 2)             \
+                return 0;                    \
+        }                                    \
+    } while (0)
 
 #define SPD_CHECK_LAUNCH(where)                          \
     do {                                                 \
@@ -62,7 +87,7 @@ struct ProfScope {
     ProfScope(int cls, double flops, hipStream_t stream)
     {
         std::lock_guard<std::mutex> g(g_prof_mu);
-        if (!(g_prof_mask & (1 << cls)))
+        if (!(g_prof_mask & (1 << cls)) || g_validate == 2)
             return;
         on = true;
         s = stream;
@@ -107,6 +132,15 @@ struct Gemm {
     bool inplace = false;  // C aliases A: one workgroup must own whole rows (n <= BN)
 };
 
+template <typename R, bool CPLX, int BM, int BN, int KB, int WM, int WN, bool AT, bool BT>
+static int launch_gemm_kernel(dim3 grid, dim3 block, const GemmArgs &a, hipStream_t s)
+{
+    SPD_VALIDATE((check_gemm<R, CPLX, BM, BN, KB, WM, WN, AT, BT>(a, grid, g_chk)));
+    gemm_kernel<R, CPLX, BM, BN, KB, WM, WN, AT, BT><<<grid, block, 0, s>>>(a);
+    SPD_CHECK_LAUNCH("gemm_kernel");
+    return 0;
+}
+
 template <typename R, bool CPLX, int BM, int BN, int KB, int WM, int WN>
 static int launch_gemm_cfg(Lay lay, const Gemm &g, hipStream_t s)
 {
@@ -137,12 +171,11 @@ static int launch_gemm_cfg(Lay lay, const Gemm &g, hipStream_t s)
     a.info = g.info;
     dim3 grid(a.ntiles, 1, g.batch), block(64 * WM * WN);
     switch (lay) {
-    case NT: gemm_kernel<R, CPLX, BM, BN, KB, WM, WN, false, true><<<grid, block, 0, s>>>(a); break;
-    case NN: gemm_kernel<R, CPLX, BM, BN, KB, WM, WN, false, false><<<grid, block, 0, s>>>(a); break;
-    case TN: gemm_kernel<R, CPLX, BM, BN, KB, WM, WN, true, false><<<grid, block, 0, s>>>(a); break;
+    case NT: return launch_gemm_kernel<R, CPLX, BM, BN, KB, WM, WN, false, true>(grid, block, a, s);
+    case NN: return launch_gemm_kernel<R, CPLX, BM, BN, KB, WM, WN, false, false>(grid, block, a, s);
+    case TN: return launch_gemm_kernel<R, CPLX, BM, BN, KB, WM, WN, true, false>(grid, block, a, s);
     }
-    SPD_CHECK_LAUNCH("gemm_kernel");
-    return 0;
+    return SPD_ERR_HIP;
 }
 
 template <typename R, bool CPLX>
@@ -182,6 +215,7 @@ static int copy2d(E *dst, int64_t ldd, const E *src, int64_t lds, int64_t m, int
 {
     if (m <= 0 || n <= 0)
         return 0;
+    SPD_VALIDATE(check_2d<E>("copy2d_kernel", dst, ldd, src, lds, m, n, info, g_chk));
     const int64_t blocks = std::min<int64_t>(cdiv(m * n, 256), 4096);
     copy2d_kernel<E><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(dst, ldd, src, lds, m, n, info);
     SPD_CHECK_LAUNCH("copy2d_kernel");
@@ -193,9 +227,18 @@ static int zero2d(E *dst, int64_t ldd, int64_t m, int64_t n, hipStream_t s)
 {
     if (m <= 0 || n <= 0)
         return 0;
+    SPD_VALIDATE(check_2d<E>("zero2d_kernel", dst, ldd, (const E *)nullptr, 0, m, n, nullptr, g_chk));
     const int64_t blocks = std::min<int64_t>(cdiv(m * n, 256), 8192);
     zero2d_kernel<E><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(dst, ldd, m, n);
     SPD_CHECK_LAUNCH("zero2d_kernel");
+    return 0;
+}
+
+static int set_info(int *info, hipStream_t s)
+{
+    SPD_VALIDATE(g_chk.access(info, 4, true, "set_int_kernel", 0, 0));
+    set_int_kernel<<<1, 1, 0, s>>>(info, 0);
+    SPD_CHECK_LAUNCH("set_int_kernel");
     return 0;
 }
 
@@ -214,6 +257,12 @@ struct Layout {
     int64_t T, nt, inv, w, tmp, total;  // offsets / sizes in elements
 };
 
+// The trailing-update panel W is stored with its leading dimension rounded up
+// to SYRK_LDW rows and its width to SYRK_KP columns, the padding zeroed, so the
+// trailing-update kernel reads whole tiles and slices only.
+constexpr int64_t SYRK_LDW = 128;  // multiple of every trailing-update tile size
+constexpr int64_t SYRK_KP = 32;    // multiple of every trailing-update slice depth
+
 static Layout make_layout(int64_t n, int64_t n_rhs, int64_t T_A, int64_t esize)
 {
     Layout L;
@@ -222,7 +271,7 @@ static Layout make_layout(int64_t n, int64_t n_rhs, int64_t T_A, int64_t esize)
     const int64_t al = 256 / esize;
     L.inv = 0;
     L.w = align_up(L.nt * L.T * L.T, al);
-    L.tmp = L.w + align_up(n * L.T, al);
+    L.tmp = L.w + align_up(align_up(n, SYRK_LDW) * align_up(L.T, SYRK_KP), al);
     L.total = L.tmp + align_up(std::max(L.T * L.T, L.T * std::max<int64_t>(n_rhs, 1)), al);
     return L;
 }
@@ -250,6 +299,7 @@ struct Solver {
         const int64_t grid = ntiles * p.lpt;
         if (grid <= 0)
             return 0;
+        SPD_VALIDATE((check_leaf<R, CPLX>(p, (unsigned)grid, g_chk)));
         leaf_kernel<R, CPLX><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p);
         SPD_CHECK_LAUNCH("leaf_kernel");
         return 0;
@@ -356,10 +406,43 @@ struct Solver {
         return 0;
     }
 
+    // Lower triangle of C (m x m, ldc) -= W W^H with W as laid out above.
+    template <int BM, int KB, int WM, int WN>
+    static int syrk_cfg(int64_t m, const E *W, int64_t ldw, int64_t kp, E *C, int64_t ldc, const int *info,
+                        hipStream_t s)
+    {
+        static_assert(SYRK_LDW % BM == 0 && SYRK_KP % KB == 0, "panel padding too small for the tile");
+        SyrkArgs a;
+        a.W = W;
+        a.ldw = ldw;
+        a.C = C;
+        a.ldc = ldc;
+        a.m = (int)m;
+        a.kp = (int)kp;
+        a.tiles = (int)cdiv(m, BM);
+        a.ntiles = a.tiles * (a.tiles + 1) / 2;
+        a.info = info;
+        const dim3 grid((unsigned)a.ntiles), block(64 * WM * WN);
+        SPD_VALIDATE((check_syrk<R, CPLX, BM, KB, WM, WN>(a, grid, g_chk)));
+        syrk_kernel<R, CPLX, BM, KB, WM, WN><<<grid, block, 0, s>>>(a);
+        SPD_CHECK_LAUNCH("syrk_kernel");
+        return 0;
+    }
+
+    static int syrk(int64_t m, const E *W, int64_t ldw, int64_t kp, E *C, int64_t ldc, const int *info,
+                    hipStream_t s)
+    {
+        if (m <= 0)
+            return 0;
+        if constexpr (CPLX)
+            return syrk_cfg<64, 16, 2, 2>(m, W, ldw, kp, C, ldc, info, s);
+        else
+            return syrk_cfg<128, 16, 2, 2>(m, W, ldw, kp, C, ldc, info, s);
+    }
+
     static int potrf(int64_t n, E *A, int64_t lda, int64_t T_A, int *info, void *work, hipStream_t s)
     {
-        set_int_kernel<<<1, 1, 0, s>>>(info, 0);
-        SPD_CHECK_LAUNCH("set_int_kernel");
+        SPD_TRY(set_info(info, s));
         if (n == 0)
             return 0;
         const Layout L = make_layout(n, 0, T_A, sizeof(E));
@@ -417,6 +500,8 @@ struct Solver {
             if (m <= 0)
                 break;
             E *P = D + tk;  // m x tk panel
+            // W: m x tk panel with leading dimension ldw, zero-padded to ldw x kp
+            const int64_t ldw = align_up(m, SYRK_LDW), kp = align_up(tk, SYRK_KP);
             {
                 // ---- 2. panel: W = P inv(L_kk)^H, then P = W
                 ProfScope ps(PROF_PANEL, FMUL * (double)m * tk * tk, s);
@@ -426,33 +511,21 @@ struct Solver {
                 g.B = Inv;
                 g.ldb = T;
                 g.C = W;
-                g.ldc = m;
+                g.ldc = ldw;
                 g.m = m;
                 g.n = tk;
                 g.k = tk;
                 g.kmode = KM_END_BY_J;
                 g.info = info;
                 SPD_TRY((gemm<R, CPLX>(NT, g, s)));
-                SPD_TRY(copy2d<E>(P, lda, W, m, m, tk, info, s));
+                SPD_TRY(zero2d<E>(W + m, ldw, ldw - m, kp, s));
+                SPD_TRY(zero2d<E>(W + tk * ldw, ldw, m, kp - tk, s));
+                SPD_TRY(copy2d<E>(P, lda, W, ldw, m, tk, info, s));
             }
             {
                 // ---- 3. trailing update: lower part of A22 -= W W^H
                 ProfScope ps(PROF_SYRK, FMUL * (double)m * (double)(m + 1) * (double)tk, s);
-                Gemm u;
-                u.A = W;
-                u.lda = m;
-                u.B = W;
-                u.ldb = m;
-                u.C = P + tk * lda;
-                u.ldc = lda;
-                u.m = m;
-                u.n = m;
-                u.k = tk;
-                u.tri = true;
-                u.neg = true;
-                u.beta = true;
-                u.info = info;
-                SPD_TRY((gemm<R, CPLX>(NT, u, s)));
+                SPD_TRY(syrk(m, W, ldw, kp, P + tk * lda, lda, info, s));
             }
         }
         return 0;
@@ -550,16 +623,22 @@ struct Solver {
                 }
             }
         }
-        {
-            const int64_t blocks = std::min<int64_t>(cdiv(n * nrhs, 256), 4096);
-            nan_fill_kernel<R, CPLX><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(B, ldb, n, nrhs, info);
-            SPD_CHECK_LAUNCH("nan_fill_kernel");
-        }
+        return nan_fill(n, nrhs, B, ldb, info, s);
+    }
+
+    static int nan_fill(int64_t n, int64_t nrhs, E *B, int64_t ldb, const int *info, hipStream_t s)
+    {
+        SPD_VALIDATE(check_2d<E>("nan_fill_kernel", B, ldb, (const E *)nullptr, 0, n, nrhs, info, g_chk));
+        const int64_t blocks = std::min<int64_t>(cdiv(n * nrhs, 256), 4096);
+        nan_fill_kernel<R, CPLX><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(B, ldb, n, nrhs, info);
+        SPD_CHECK_LAUNCH("nan_fill_kernel");
         return 0;
     }
 
     static int logdet(int64_t n, const E *A, int64_t lda, const int *info, double *out, hipStream_t s)
     {
+        SPD_VALIDATE(check_2d<E>("logdet_kernel", (E *)nullptr, 0, A, lda + 1, 1, n, info, g_chk) &&
+                     g_chk.access(out, sizeof(double), true, "logdet_kernel", 0, 0));
         logdet_kernel<R, CPLX><<<1, 1024, 0, s>>>(A, lda, n, info, out);
         SPD_CHECK_LAUNCH("logdet_kernel");
         return 0;
@@ -575,6 +654,15 @@ static int64_t elem_size(int dt)
     case SPD_C128: return 16;
     default: return 0;
     }
+}
+
+// Bytes spanned by an m x n column-major matrix with leading dimension ld
+// (the last column needs only m rows).
+static size_t matrix_bytes(int dt, int64_t m, int64_t n, int64_t ld)
+{
+    if (m <= 0 || n <= 0)
+        return 0;
+    return (size_t)(((n - 1) * ld + m) * elem_size(dt));
 }
 
 }  // namespace spd
@@ -603,6 +691,12 @@ int spd_potrf(spd_dtype_t dt, int64_t n, void *dA, int64_t lda, int64_t T_A, int
     const size_t need = spd_workspace_size(dt, n, 0, T_A);
     if (d_work == nullptr && need > 0) return -7;
     if (work_bytes < need) return -8;
+    if (g_validate) {
+        g_chk.begin();
+        g_chk.add(dA, matrix_bytes(dt, n, n, lda), true, "A");
+        g_chk.add(d_info, 4, true, "info");
+        g_chk.add(d_work, work_bytes, true, "workspace");
+    }
     hipStream_t s = (hipStream_t)stream;
     switch (dt) {
     case SPD_R32: return Solver<float, false>::potrf(n, (float *)dA, lda, T_A, d_info, d_work, s);
@@ -629,6 +723,13 @@ int spd_potrs(spd_dtype_t dt, int64_t n, int64_t n_rhs, const void *dA, int64_t 
     const size_t need = spd_workspace_size(dt, n, n_rhs, T_A);
     if (d_work == nullptr && need > 0) return -10;
     if (work_bytes < need) return -11;
+    if (g_validate) {
+        g_chk.begin();
+        g_chk.add(dA, matrix_bytes(dt, n, n, lda), false, "L");
+        g_chk.add(dB, matrix_bytes(dt, n, n_rhs, ldb), true, "B");
+        g_chk.add(d_info, 4, false, "info");
+        g_chk.add(d_work, work_bytes, true, "workspace");
+    }
     hipStream_t s = (hipStream_t)stream;
     switch (dt) {
     case SPD_R32:
@@ -654,6 +755,12 @@ int spd_logdet(spd_dtype_t dt, int64_t n, const void *dA, int64_t lda, const int
     if (dA == nullptr && n > 0) return -3;
     if (lda < std::max<int64_t>(1, n)) return -4;
     if (d_logdet == nullptr) return -6;
+    if (g_validate) {
+        g_chk.begin();
+        g_chk.add(dA, matrix_bytes(dt, n, n, lda), false, "L");
+        g_chk.add(d_info, 4, false, "info");
+        g_chk.add(d_logdet, sizeof(double), true, "logdet");
+    }
     hipStream_t s = (hipStream_t)stream;
     switch (dt) {
     case SPD_R32: return Solver<float, false>::logdet(n, (const float *)dA, lda, d_info, d_logdet, s);
@@ -667,6 +774,14 @@ int spd_logdet(spd_dtype_t dt, int64_t n, const void *dA, int64_t lda, const int
 }
 
 const char *spd_last_error(void) { return g_last_error.c_str(); }
+
+int spd_debug_validate(int mode)
+{
+    if (mode < 0 || mode > 2)
+        return -1;
+    g_validate = mode;
+    return 0;
+}
 
 int spd_profile_enable(int mask)
 {

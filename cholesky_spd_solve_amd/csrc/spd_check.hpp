@@ -1,0 +1,260 @@
+// Host-side launch validator of the dense SPD/HPD solver.
+//
+// When switched on (spd_debug_validate), every kernel launch is first replayed
+// on the host: each workgroup and thread of the launch computes, with the same
+// index arithmetic the kernel itself uses (tile enumeration, k ranges, the
+// loaders' thread-to-element maps, leaf_geom, acc_row), the addresses it would
+// read or write, and each access must lie inside one of the buffers the caller
+// passed to the entry point (the matrix, the right-hand side, the workspace,
+// info, the log-determinant); a write must also be to a buffer the entry point
+// may modify.  The first violation stops the call with SPD_ERR_CHECK and a
+// message naming the kernel, the workgroup, the thread and the address.
+//
+// Mode 2 ("dry run") validates without touching the GPU at all, so the whole
+// launch sequence of any problem shape can be checked on a machine without a
+// GPU.  The replay is exhaustive (every thread of every workgroup), so it is
+// meant for small and medium shapes.
+#pragma once
+
+#include <stdint.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "spd_gemm.hpp"
+#include "spd_kernels.hpp"
+#include "spd_syrk.hpp"
+
+namespace spd {
+
+struct Region {
+    uintptr_t lo, hi;
+    bool writable;
+    const char *name;
+};
+
+struct Checker {
+    std::vector<Region> regions;
+    std::string err;
+
+    void begin()
+    {
+        regions.clear();
+        err.clear();
+    }
+    void add(const void *p, size_t bytes, bool writable, const char *name)
+    {
+        if (p != nullptr && bytes > 0)
+            regions.push_back({(uintptr_t)p, (uintptr_t)p + bytes, writable, name});
+    }
+    bool access(const void *p, size_t bytes, bool write, const char *kernel, long wg, long th)
+    {
+        const uintptr_t a = (uintptr_t)p, b = a + bytes;
+        for (const Region &r : regions) {
+            if (a >= r.lo && b <= r.hi) {
+                if (write && !r.writable)
+                    break;
+                return true;
+            }
+        }
+        char buf[256];
+        snprintf(buf, sizeof buf, "%s: workgroup %ld thread %ld %s %zu bytes at %p outside every %s buffer",
+                 kernel, wg, th, write ? "writes" : "reads", bytes, p, write ? "writable" : "");
+        err = buf;
+        return false;
+    }
+};
+
+// Replay of gemm_kernel (spd_gemm.hpp): element-wise bounds-checked operand
+// loads of the k slices [kbeg, kend), the C prologue (beta) and the epilogue.
+template <typename R, bool CPLX, int BM, int BN, int KB, int WM, int WN, bool AT, bool BT>
+static bool check_gemm(const GemmArgs &p, dim3 grid, Checker &c)
+{
+    typedef typename Elem<R, CPLX>::type E;
+    constexpr int NT = 64 * WM * WN;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 16, FN = TN / 16;
+    constexpr int LA = BM * KB / NT, LB = BN * KB / NT;
+    const char *kn = "gemm_kernel";
+    if (p.info != nullptr && !c.access(p.info, 4, false, kn, 0, 0))
+        return false;
+    for (unsigned z = 0; z < grid.z; ++z) {
+        const int zo = (int)z / p.nb_inner, zi = (int)z - zo * p.nb_inner;
+        const E *A = (const E *)p.A + zo * p.sA_out + zi * p.sA_in;
+        const E *B = (const E *)p.B + zo * p.sB_out + zi * p.sB_in;
+        E *C = (E *)p.C + zo * p.sC_out + zi * p.sC_in;
+        for (unsigned b = 0; b < grid.x; ++b) {
+            const long wg = (long)z * grid.x + b;
+            int I, J;
+            const int t = xcd_remap((int)b, p.ntiles);
+            if (p.tri) {
+                tri_index(t, I, J);
+            } else {
+                I = t % p.tiles_m;
+                J = t / p.tiles_m;
+            }
+            const int i0 = I * BM, j0 = J * BN, m = p.m, n = p.n;
+            int kbeg = 0, kend = p.k;
+            switch (p.kmode) {
+            case KM_END_BY_J: kend = std::min(kend, j0 + BN); break;
+            case KM_BEG_BY_J: kbeg = j0; break;
+            case KM_END_BY_I: kend = std::min(kend, i0 + BM); break;
+            case KM_BEG_BY_I: kbeg = i0; break;
+            default: break;
+            }
+            kbeg = (kbeg / KB) * KB;
+            for (int tid = 0; tid < NT; ++tid) {
+                const int lane = tid & 63, wave = tid >> 6;
+                const int wm = wave % WM, wn = wave / WM;
+                const int li = lane & 15, lk = lane >> 4;
+                const int ib = wm * TM, jb = wn * TN;
+                for (int k0 = kbeg; k0 < kend; k0 += KB) {
+                    for (int q = 0; q < LA; ++q) {
+                        const int e = tid + NT * q;
+                        const int i = AT ? e / KB : e % BM, kk = AT ? e % KB : e / BM;
+                        const int gi = i0 + i, gk = k0 + kk;
+                        if (gi < m && gk < kend) {
+                            const E *src = AT ? (A + gk + (int64_t)gi * p.lda) : (A + gi + (int64_t)gk * p.lda);
+                            if (!c.access(src, sizeof(E), false, kn, wg, tid))
+                                return false;
+                        }
+                    }
+                    for (int q = 0; q < LB; ++q) {
+                        const int e = tid + NT * q;
+                        const int j = BT ? e % BN : e / KB, kk = BT ? e / BN : e % KB;
+                        const int gj = j0 + j, gk = k0 + kk;
+                        if (gj < n && gk < kend) {
+                            const E *src = BT ? (B + gj + (int64_t)gk * p.ldb) : (B + gk + (int64_t)gj * p.ldb);
+                            if (!c.access(src, sizeof(E), false, kn, wg, tid))
+                                return false;
+                        }
+                    }
+                }
+                for (int fi = 0; fi < FM; ++fi)
+                    for (int fj = 0; fj < FN; ++fj)
+                        for (int q = 0; q < 4; ++q) {
+                            const int i = i0 + ib + fi * 16 + li, j = j0 + jb + fj * 16 + acc_row<R>(lk, q);
+                            if (p.beta && i < m && j < n &&
+                                !c.access(C + i + (int64_t)j * p.ldc, sizeof(E), false, kn, wg, tid))
+                                return false;
+                            if (i < m && j < n && (!p.tri || i >= j) &&
+                                !c.access(C + i + (int64_t)j * p.ldc, sizeof(E), true, kn, wg, tid))
+                                return false;
+                        }
+            }
+        }
+    }
+    return true;
+}
+
+// Replay of syrk_kernel (spd_syrk.hpp): whole-tile vector loads of both row
+// blocks of W for every slice, and the epilogue's read-modify-write of C.
+template <typename R, bool CPLX, int BM, int KB, int WM, int WN>
+static bool check_syrk(const SyrkArgs &p, dim3 grid, Checker &c)
+{
+    typedef typename Elem<R, CPLX>::type E;
+    constexpr int NT = 64 * WM * WN;
+    constexpr int TM = BM / WM, TN = BM / WN;
+    constexpr int FM = TM / 16, FN = TN / 16;
+    typedef SyrkLoad<R, CPLX, BM, KB, NT> LD;
+    const char *kn = "syrk_kernel";
+    if (p.info != nullptr && !c.access(p.info, 4, false, kn, 0, 0))
+        return false;
+    if (p.ldw % BM != 0 || p.kp % KB != 0 || p.kp <= 0) {
+        c.err = "syrk_kernel: panel layout is not whole tiles and slices";
+        return false;
+    }
+    for (unsigned b = 0; b < grid.x; ++b) {
+        int I, J;
+        tri_index(xcd_remap((int)b, p.ntiles), I, J);
+        const int i0 = I * BM, j0 = J * BM;
+        if (I >= p.tiles || J > I) {
+            c.err = "syrk_kernel: workgroup maps outside the lower tiles";
+            return false;
+        }
+        const E *W = (const E *)p.W;
+        for (int tid = 0; tid < NT; ++tid) {
+            for (int k0 = 0; k0 < p.kp; k0 += KB)
+                for (int q = 0; q < LD::L; ++q) {
+                    int r, k;
+                    LD::coords(tid, q, r, k);
+                    const uint32_t off = (uint32_t)(r + (int64_t)k * p.ldw);
+                    if (r + LD::V > BM || k >= KB) {
+                        c.err = "syrk_kernel: load outside its tile slice";
+                        return false;
+                    }
+                    if (!c.access(W + i0 + (int64_t)k0 * p.ldw + off, LD::V * sizeof(E), false, kn, b, tid) ||
+                        !c.access(W + j0 + (int64_t)k0 * p.ldw + off, LD::V * sizeof(E), false, kn, b, tid))
+                        return false;
+                }
+            const int lane = tid & 63, wave = tid >> 6;
+            const int wm = wave % WM, wn = wave / WM;
+            const int li = lane & 15, lk = lane >> 4;
+            const int ib = wm * TM, jb = wn * TN;
+            const bool whole = (I != J) && (i0 + BM <= p.m);
+            E *Ct = (E *)p.C + i0 + (int64_t)j0 * p.ldc;
+            for (int fi = 0; fi < FM; ++fi)
+                for (int fj = 0; fj < FN; ++fj)
+                    for (int q = 0; q < 4; ++q) {
+                        const int i = ib + fi * 16 + li, j = jb + fj * 16 + acc_row<R>(lk, q);
+                        if (whole || (i0 + i < p.m && i0 + i >= j0 + j)) {
+                            E *dst = Ct + (uint32_t)(i + (int64_t)j * p.ldc);
+                            if (!c.access(dst, sizeof(E), false, kn, b, tid) ||
+                                !c.access(dst, sizeof(E), true, kn, b, tid))
+                                return false;
+                        }
+                    }
+        }
+    }
+    return true;
+}
+
+template <typename R, bool CPLX>
+static bool check_leaf(const LeafArgs &p, unsigned grid, Checker &c)
+{
+    typedef typename Elem<R, CPLX>::type E;
+    const char *kn = "leaf_kernel";
+    if (p.info != nullptr && !c.access(p.info, 4, p.factor != 0, kn, 0, 0))
+        return false;
+    for (unsigned g = 0; g < grid; ++g) {
+        int64_t c0, ioff;
+        int lb;
+        if (!leaf_geom(p, (int)g, c0, lb, ioff))
+            continue;
+        const E *A = (const E *)p.A + c0 + c0 * p.lda;
+        const E *Inv = (const E *)p.Inv + ioff;
+        for (int col = 0; col < lb; ++col)
+            for (int r = 0; r < lb; ++r) {
+                if (r >= col) {
+                    if (!c.access(A + r + (int64_t)col * p.lda, sizeof(E), false, kn, g, 0))
+                        return false;
+                    if (p.factor && !c.access(A + r + (int64_t)col * p.lda, sizeof(E), true, kn, g, 0))
+                        return false;
+                }
+                if (!c.access(Inv + r + (int64_t)col * p.ldi, sizeof(E), true, kn, g, 0))
+                    return false;
+            }
+    }
+    return true;
+}
+
+// dst(0:m, 0:n) written, src(0:m, 0:n) read (either may be null)
+template <typename E>
+static bool check_2d(const char *kn, E *dst, int64_t ldd, const E *src, int64_t lds, int64_t m, int64_t n,
+                     const int *info, Checker &c)
+{
+    if (info != nullptr && !c.access(info, 4, false, kn, 0, 0))
+        return false;
+    for (int64_t j = 0; j < n; ++j)
+        for (int64_t i = 0; i < m; ++i) {
+            if (dst != nullptr && !c.access(dst + i + j * ldd, sizeof(E), true, kn, 0, 0))
+                return false;
+            if (src != nullptr && !c.access(src + i + j * lds, sizeof(E), false, kn, 0, 0))
+                return false;
+        }
+    return true;
+}
+
+}  // namespace spd

@@ -55,9 +55,9 @@ __device__ __forceinline__ fx4 mfma16(float a, float b, fx4 c)
 // lane group g = lane / 16 (the column is lane % 16).  The fp32 instruction
 // gives each lane group four consecutive rows; the fp64 one interleaves the
 // groups (measured on gfx950 with a known-input probe).
-template <typename R> __device__ __forceinline__ int acc_row(int g, int q);
-template <> __device__ __forceinline__ int acc_row<float>(int g, int q) { return 4 * g + q; }
-template <> __device__ __forceinline__ int acc_row<double>(int g, int q) { return 4 * q + g; }
+template <typename R> __host__ __device__ inline int acc_row(int g, int q);
+template <> __host__ __device__ inline int acc_row<float>(int g, int q) { return 4 * g + q; }
+template <> __host__ __device__ inline int acc_row<double>(int g, int q) { return 4 * q + g; }
 
 // k-range restriction for triangular operands whose zero triangle is stored
 // explicitly (the inverted diagonal blocks): skip slices that are all zero.

@@ -27,6 +27,24 @@ struct LeafArgs {
     int col0;       // global column of A[0, 0] (for info)
 };
 
+// Leaf handled by workgroup g: its first global column c0 (relative to the
+// matrix base), its order lb and the element offset of its inverse from Inv.
+// False when the workgroup has no leaf (ragged last tile).
+__host__ __device__ inline bool leaf_geom(const LeafArgs &p, int g, int64_t &c0, int &lb, int64_t &ioff)
+{
+    const int t = g / p.lpt, b = g - t * p.lpt;
+    const int64_t tc = (int64_t)t * p.T;
+    if (tc >= p.n)
+        return false;
+    const int tk = (int)((p.T < p.n - tc) ? p.T : p.n - tc);
+    if (b * LEAF >= tk)
+        return false;
+    lb = (LEAF < tk - b * LEAF) ? LEAF : tk - b * LEAF;
+    c0 = tc + (int64_t)b * LEAF;
+    ioff = (int64_t)t * p.sInv + (int64_t)b * LEAF * (1 + p.ldi);
+    return true;
+}
+
 // One workgroup per leaf.  Leaf g lies in tile t = g / lpt at leaf slot
 // b = g % lpt: columns c = t*T + b*LEAF ... of the matrix.
 //
@@ -51,18 +69,12 @@ __global__ void __launch_bounds__(256) leaf_kernel(const LeafArgs p)
 
     if (p.info != nullptr && *p.info != 0)
         return;
-    const int g = blockIdx.x;
-    const int t = g / p.lpt, b = g - t * p.lpt;
-    const int64_t tc = (int64_t)t * p.T;
-    if (tc >= p.n)
+    int64_t c0, ioff;
+    int lb;
+    if (!leaf_geom(p, (int)blockIdx.x, c0, lb, ioff))
         return;
-    const int tk = (int)min<int64_t>(p.T, p.n - tc);
-    if (b * LEAF >= tk)
-        return;
-    const int lb = min(LEAF, tk - b * LEAF);
-    const int64_t c0 = tc + (int64_t)b * LEAF;
     E *A = (E *)p.A + c0 + c0 * p.lda;
-    E *Inv = (E *)p.Inv + (int64_t)t * p.sInv + (int64_t)b * LEAF * (1 + p.ldi);
+    E *Inv = (E *)p.Inv + ioff;
     const int tid = threadIdx.x;
 
     for (int e = tid; e < lb * lb; e += 256) {

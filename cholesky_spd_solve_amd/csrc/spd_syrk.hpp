@@ -1,0 +1,251 @@
+// Trailing update of the right-looking blocked Cholesky factorization on the
+// gfx950 matrix cores (JAXMg paper, "Software design": the potrf step of
+// potrs; this is the symmetric rank-T_A update that carries almost all of its
+// flops):
+//
+//     C(i, j) -= sum_k W(i, k) * conj(W(j, k))      for 0 <= j <= i < m
+//
+// W is the freshly solved panel L21 (m x T_A), staged in the workspace with a
+// layout this kernel can read without any bounds logic:
+//   - leading dimension ldw is a multiple of the tile size BM, and rows
+//     [m, ldw) are zero, so every row block of W is whole;
+//   - the number of columns kp is a multiple of the slice depth KB, and columns
+//     beyond the panel width are zero.
+// Only C needs bounds: the tiles on the diagonal and those that cross row m.
+//
+// A workgroup owns one BM x BM tile (I, J), I >= J, of the lower triangle of
+// C, split over WM x WN wave64s; each wave holds (BM/WM) x (BM/WN) of C as
+// 16x16 accumulator blocks of v_mfma_*_16x16x4.  W is consumed KB columns at
+// a time: the next slice is loaded from HBM into registers (16-byte vector
+// loads, 32-bit offsets from a uniform tile origin) while the current slice is
+// read from LDS by the matrix cores; one barrier per slice.  C is read and
+// written once, in the epilogue, one 16-row block at a time.
+//
+// Complex types keep real and imaginary parts in separate LDS planes and use
+// four real MFMAs per complex multiply-add.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "spd_gemm.hpp"
+
+namespace spd {
+
+struct SyrkArgs {
+    const void *W;  // panel, column-major, leading dimension ldw (see above)
+    int64_t ldw;
+    void *C;        // trailing matrix, column-major, leading dimension ldc
+    int64_t ldc;
+    int m;          // order of C
+    int kp;         // columns of W (a multiple of KB)
+    int tiles;      // tile rows = ceil(m / BM)
+    int ntiles;     // lower tiles = tiles * (tiles + 1) / 2
+    const int *info;  // if non-null and *info != 0 the kernel does nothing
+};
+
+// Elements per 16-byte vector load and the loader's thread -> element map,
+// shared with the host-side launch validator.
+template <typename R, bool CPLX, int BM, int KB, int NT>
+struct SyrkLoad {
+    typedef typename Elem<R, CPLX>::type E;
+    static constexpr int V = (int)(16 / sizeof(E));  // elements per vector
+    static constexpr int NCH = BM / V;               // vectors per column of a tile
+    static constexpr int L = BM * KB / (V * NT);     // vector loads per thread per operand
+    static_assert(BM % V == 0 && (BM * KB) % (V * NT) == 0, "tile does not divide into vector loads");
+
+    // row r (first of V) and column k of load q of thread tid, within a tile slice
+    __host__ __device__ static inline void coords(int tid, int q, int &r, int &k)
+    {
+        const int e = tid + NT * q;
+        r = (e % NCH) * V;
+        k = e / NCH;
+    }
+};
+
+template <typename R, bool CPLX, int BM, int KB, int WM, int WN>
+__global__ void __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)))
+syrk_kernel(const SyrkArgs p)
+{
+    typedef typename Elem<R, CPLX>::type E;
+    typedef typename AccT<R>::type V4;
+    typedef SyrkLoad<R, CPLX, BM, KB, 64 * WM * WN> LD;
+    constexpr int NT = 64 * WM * WN;
+    constexpr int TM = BM / WM, TN = BM / WN;
+    constexpr int FM = TM / 16, FN = TN / 16;
+    constexpr int NP = CPLX ? 2 : 1;
+    constexpr int V = LD::V, L = LD::L;
+    static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
+    static_assert(KB % 4 == 0, "KB must be a multiple of 4");
+
+    __shared__ R As[2][NP][KB][BM];  // As[.][.][k][r] = W(i0 + r, k0 + k)
+    __shared__ R Bs[2][NP][KB][BM];  // Bs[.][.][k][r] = conj(W(j0 + r, k0 + k))
+
+    if (p.info != nullptr && *p.info != 0)
+        return;
+
+    int I, J;
+    tri_index(xcd_remap((int)blockIdx.x, p.ntiles), I, J);
+    const int i0 = I * BM, j0 = J * BM;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave % WM, wn = wave / WM;
+    const int li = lane & 15, lk = lane >> 4;
+    const int ib = wm * TM, jb = wn * TN;
+
+    // per-thread element offsets inside a slice (identical for both operands)
+    uint32_t off[L];
+    int rr[L], kk[L];
+#pragma unroll
+    for (int q = 0; q < L; ++q) {
+        LD::coords(tid, q, rr[q], kk[q]);
+        off[q] = (uint32_t)(rr[q] + (int64_t)kk[q] * p.ldw);
+    }
+
+    const E *__restrict__ wa = (const E *)p.W + i0;  // slice origin of the row block of C
+    const E *__restrict__ wb = (const E *)p.W + j0;  // slice origin of the column block
+    const int64_t step = (int64_t)KB * p.ldw;
+
+    R ra[L][V][NP], rb[L][V][NP];
+    auto load = [&](const E *__restrict__ oa, const E *__restrict__ ob) {
+#pragma unroll
+        for (int q = 0; q < L; ++q) {
+            if constexpr (CPLX && V == 1) {
+                Elem<R, true>::load(oa + off[q], ra[q][0][0], ra[q][0][NP - 1]);
+                Elem<R, true>::load(ob + off[q], rb[q][0][0], rb[q][0][NP - 1]);
+            } else if constexpr (CPLX) {
+                // two complex elements in one 16-byte vector
+                typedef R vt __attribute__((ext_vector_type(4)));
+                const vt x = *(const vt *)(oa + off[q]);
+                const vt y = *(const vt *)(ob + off[q]);
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    ra[q][v][0] = x[2 * v];
+                    ra[q][v][NP - 1] = x[2 * v + 1];
+                    rb[q][v][0] = y[2 * v];
+                    rb[q][v][NP - 1] = y[2 * v + 1];
+                }
+            } else {
+                typedef R vt __attribute__((ext_vector_type(V)));
+                const vt x = *(const vt *)(oa + off[q]);
+                const vt y = *(const vt *)(ob + off[q]);
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    ra[q][v][0] = x[v];
+                    rb[q][v][0] = y[v];
+                }
+            }
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < L; ++q)
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                As[buf][0][kk[q]][rr[q] + v] = ra[q][v][0];
+                Bs[buf][0][kk[q]][rr[q] + v] = rb[q][v][0];
+                if constexpr (CPLX) {
+                    As[buf][1][kk[q]][rr[q] + v] = ra[q][v][1];
+                    Bs[buf][1][kk[q]][rr[q] + v] = -rb[q][v][1];  // conj(W(j, k))
+                }
+            }
+    };
+
+    V4 acc[NP][FM][FN];
+#pragma unroll
+    for (int c = 0; c < NP; ++c)
+#pragma unroll
+        for (int fi = 0; fi < FM; ++fi)
+#pragma unroll
+            for (int fj = 0; fj < FN; ++fj)
+                acc[c][fi][fj] = V4{0, 0, 0, 0};
+
+    load(wa, wb);
+    store(0);
+    __syncthreads();
+    int cur = 0;
+    for (int k0 = 0; k0 < p.kp; k0 += KB) {
+        const bool more = k0 + KB < p.kp;
+        if (more) {
+            wa += step;
+            wb += step;
+            load(wa, wb);
+        }
+#pragma unroll
+        for (int s = 0; s < KB / 4; ++s) {
+            const int kr = s * 4 + lk;
+            R a[NP][FM], b[NP][FN];
+#pragma unroll
+            for (int c = 0; c < NP; ++c) {
+#pragma unroll
+                for (int fi = 0; fi < FM; ++fi)
+                    a[c][fi] = As[cur][c][kr][ib + fi * 16 + li];
+#pragma unroll
+                for (int fj = 0; fj < FN; ++fj)
+                    b[c][fj] = Bs[cur][c][kr][jb + fj * 16 + li];
+            }
+#pragma unroll
+            for (int fi = 0; fi < FM; ++fi)
+#pragma unroll
+                for (int fj = 0; fj < FN; ++fj) {
+                    if constexpr (!CPLX) {
+                        acc[0][fi][fj] = mfma16(b[0][fj], a[0][fi], acc[0][fi][fj]);
+                    } else {
+                        // re += br*ar - bi*ai ; im += bi*ar + br*ai
+                        acc[0][fi][fj] = mfma16(b[0][fj], a[0][fi], acc[0][fi][fj]);
+                        acc[0][fi][fj] = mfma16(-b[1][fj], a[1][fi], acc[0][fi][fj]);
+                        acc[1][fi][fj] = mfma16(b[1][fj], a[0][fi], acc[1][fi][fj]);
+                        acc[1][fi][fj] = mfma16(b[0][fj], a[1][fi], acc[1][fi][fj]);
+                    }
+                }
+        }
+        if (more)
+            store(cur ^ 1);
+        __syncthreads();
+        cur ^= 1;
+    }
+
+    // ---- epilogue: C -= acc, one 16-row block at a time
+    E *__restrict__ Ct = (E *)p.C + i0 + (int64_t)j0 * p.ldc;
+    const bool whole = (I != J) && (i0 + BM <= p.m);  // every element of the tile is updated
+#pragma unroll
+    for (int fi = 0; fi < FM; ++fi) {
+        const int i = ib + fi * 16 + li;
+        R cr[FN][4], ci[FN][4];
+        if (whole) {
+#pragma unroll
+            for (int fj = 0; fj < FN; ++fj)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int j = jb + fj * 16 + acc_row<R>(lk, q);
+                    ci[fj][q] = 0;
+                    Elem<R, CPLX>::load(Ct + (uint32_t)(i + (int64_t)j * p.ldc), cr[fj][q], ci[fj][q]);
+                }
+#pragma unroll
+            for (int fj = 0; fj < FN; ++fj)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int j = jb + fj * 16 + acc_row<R>(lk, q);
+                    Elem<R, CPLX>::store(Ct + (uint32_t)(i + (int64_t)j * p.ldc), cr[fj][q] - acc[0][fi][fj][q],
+                                         CPLX ? ci[fj][q] - acc[NP - 1][fi][fj][q] : R(0));
+                }
+        } else {
+#pragma unroll
+            for (int fj = 0; fj < FN; ++fj)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int j = jb + fj * 16 + acc_row<R>(lk, q);
+                    if (i0 + i < p.m && i0 + i >= j0 + j) {
+                        E *dst = Ct + (uint32_t)(i + (int64_t)j * p.ldc);
+                        R xr, xi = 0;
+                        Elem<R, CPLX>::load(dst, xr, xi);
+                        Elem<R, CPLX>::store(dst, xr - acc[0][fi][fj][q],
+                                             CPLX ? xi - acc[NP - 1][fi][fj][q] : R(0));
+                    }
+                }
+        }
+    }
+}
+
+}  // namespace spd

@@ -29,7 +29,8 @@
  *     the device through d_info, so no host synchronisation happens inside.
  *   - Return value: 0 when the work was enqueued; -i when the i-th argument is
  *     invalid (nothing is enqueued); SPD_ERR_HIP when the HIP runtime reported
- *     an error while enqueueing (spd_last_error() describes it).
+ *     an error while enqueueing, SPD_ERR_CHECK when launch validation (see
+ *     spd_debug_validate) rejected a launch (spd_last_error() describes it).
  *   - Calls on one stream run in order; calls that share a workspace must not
  *     run concurrently.
  */
@@ -51,6 +52,7 @@ typedef enum {
 } spd_dtype_t;
 
 #define SPD_ERR_HIP 1
+#define SPD_ERR_CHECK 2
 
 /* Bytes of device workspace that spd_potrf and spd_potrs need for these
  * sizes (one workspace serves both).  Returns 0 for invalid arguments
@@ -105,8 +107,25 @@ int spd_potrs(spd_dtype_t dt, int64_t n, int64_t n_rhs, const void *dA, int64_t 
 int spd_logdet(spd_dtype_t dt, int64_t n, const void *dA, int64_t lda,
                const int32_t *d_info, double *d_logdet, void *stream);
 
-/* Text of the last HIP error seen by this library in the calling thread. */
+/* Text of the last error (HIP or launch validation) seen by this library in
+ * the calling thread. */
 const char *spd_last_error(void);
+
+/* Launch validation, a debugging aid for callers and tests.
+ *   mode 0  off (default)
+ *   mode 1  before each kernel is enqueued, replay on the host every address
+ *           each of its threads would read or write, and require each to lie
+ *           inside the buffers passed to the entry point (the matrix, B, the
+ *           workspace, info, logdet; writes only to buffers that call may
+ *           modify); a violation returns SPD_ERR_CHECK without enqueueing it
+ *   mode 2  the same replay with nothing enqueued and no HIP call made at all
+ *           ("dry run"): pointers are never dereferenced, so any addresses
+ *           may be passed, and the launch sequence of any shape can be
+ *           checked on a machine without a GPU
+ * The replay visits every thread of every workgroup, so its host cost grows
+ * with the problem's work; it is meant for small and medium shapes.  The
+ * setting is process-wide.  Returns 0, or -1 for an unknown mode. */
+int spd_debug_validate(int mode);
 
 /* Kernel timing for measurement harnesses.  While enabled (mask != 0), every
  * launch of the selected kernel classes is bracketed by HIP events recorded
