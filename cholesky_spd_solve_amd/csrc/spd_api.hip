@@ -19,6 +19,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdlib>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -242,6 +243,13 @@ static int set_info(int *info, hipStream_t s)
     return 0;
 }
 
+#define SPD_TRY_HIP(x, where)            \
+    do {                                  \
+        hipError_t e_ = (x);              \
+        if (e_ != hipSuccess)             \
+            return hip_fail(e_, where);   \
+    } while (0)
+
 #define SPD_TRY(x)              \
     do {                        \
         int r_ = (x);           \
@@ -251,10 +259,11 @@ static int set_info(int *info, hipStream_t s)
 
 // Workspace layout, in elements of the working type (each region 256-byte
 // aligned):  INV  nt * T * T   inverted diagonal tiles (tile t at t*T*T, ld T)
-//            W    n * T        panel L21 (potrf) / merge temporaries (both)
+//            W    2 x (n rounded up to 128) x (T rounded up to 32): the panels
+//                 L21 of two consecutive steps (potrf) / merge temporaries (both)
 //            TMP  max(T*T, T*n_rhs)   one block row of the right-hand side
 struct Layout {
-    int64_t T, nt, inv, w, tmp, total;  // offsets / sizes in elements
+    int64_t T, nt, inv, w, wsz, tmp, total;  // offsets / sizes in elements
 };
 
 // The trailing-update panel W is stored with its leading dimension rounded up
@@ -271,10 +280,86 @@ static Layout make_layout(int64_t n, int64_t n_rhs, int64_t T_A, int64_t esize)
     const int64_t al = 256 / esize;
     L.inv = 0;
     L.w = align_up(L.nt * L.T * L.T, al);
-    L.tmp = L.w + align_up(align_up(n, SYRK_LDW) * align_up(L.T, SYRK_KP), al);
+    L.wsz = align_up(align_up(n, SYRK_LDW) * align_up(L.T, SYRK_KP), al);
+    L.tmp = L.w + 2 * L.wsz;  // two panel buffers: step k's and step k+1's
     L.total = L.tmp + align_up(std::max(L.T * L.T, L.T * std::max<int64_t>(n_rhs, 1)), al);
     return L;
 }
+
+// The lookahead schedule is on unless the environment sets SPD_LOOKAHEAD=0
+// (the sequential schedule does the same work without overlap; it is there
+// to measure each kernel on its own).
+static bool lookahead_enabled()
+{
+    static const bool on = [] {
+        const char *v = getenv("SPD_LOOKAHEAD");
+        return !(v != nullptr && v[0] == '0');
+    }();
+    return on;
+}
+
+// The auxiliary stream and events of the lookahead schedule: one set per
+// host thread and device, created on first use and kept until the process
+// ends.  Default priority, non-blocking with respect to the null stream.  In a
+// dry run (no HIP calls) both schedules run on the caller's stream.
+struct AuxStreams {
+    hipStream_t look = nullptr;
+    hipEvent_t ev_fork = nullptr, ev_panel = nullptr, ev_rest = nullptr;
+};
+
+struct Lookahead {
+    hipStream_t look = nullptr;
+    hipEvent_t ev_fork = nullptr, ev_panel = nullptr, ev_rest = nullptr;
+
+    int begin(hipStream_t s)
+    {
+        if (g_validate == 2) {
+            look = s;
+            return 0;
+        }
+        static thread_local std::vector<std::pair<int, AuxStreams>> per_device;
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess)
+            return hip_fail(e, "hipGetDevice");
+        AuxStreams *x = nullptr;
+        for (auto &pd : per_device)
+            if (pd.first == dev)
+                x = &pd.second;
+        if (x == nullptr) {
+            AuxStreams n;
+            if ((e = hipStreamCreateWithFlags(&n.look, hipStreamNonBlocking)) != hipSuccess)
+                return hip_fail(e, "hipStreamCreateWithFlags");
+            for (hipEvent_t *ev : {&n.ev_fork, &n.ev_panel, &n.ev_rest})
+                if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess)
+                    return hip_fail(e, "hipEventCreateWithFlags");
+            per_device.emplace_back(dev, n);
+            x = &per_device.back().second;
+        }
+        look = x->look;
+        ev_fork = x->ev_fork;
+        ev_panel = x->ev_panel;
+        ev_rest = x->ev_rest;
+        // the auxiliary stream starts after everything already queued on s
+        SPD_TRY_HIP(hipEventRecord(ev_fork, s), "hipEventRecord");
+        SPD_TRY_HIP(hipStreamWaitEvent(look, ev_fork, 0), "hipStreamWaitEvent");
+        return 0;
+    }
+    int record(hipEvent_t ev, hipStream_t st)
+    {
+        if (g_validate == 2)
+            return 0;
+        SPD_TRY_HIP(hipEventRecord(ev, st), "hipEventRecord");
+        return 0;
+    }
+    int wait(hipStream_t st, hipEvent_t ev)
+    {
+        if (g_validate == 2)
+            return 0;
+        SPD_TRY_HIP(hipStreamWaitEvent(st, ev, 0), "hipStreamWaitEvent");
+        return 0;
+    }
+};
 
 template <typename R, bool CPLX>
 struct Solver {
@@ -406,10 +491,13 @@ struct Solver {
         return 0;
     }
 
-    // Lower triangle of C (m x m, ldc) -= W W^H with W as laid out above.
+    static constexpr int64_t syrk_bm() { return CPLX ? 64 : 128; }
+
+    // Lower triangle of C (m x m, ldc) -= W W^H with W as laid out above; with
+    // jt_end > 0 only the first jt_end tile columns (jt_end * BM columns of C).
     template <int BM, int KB, int WM, int WN>
-    static int syrk_cfg(int64_t m, const E *W, int64_t ldw, int64_t kp, E *C, int64_t ldc, const int *info,
-                        hipStream_t s)
+    static int syrk_cfg(int64_t m, const E *W, int64_t ldw, int64_t kp, E *C, int64_t ldc, int jt_end,
+                        const int *info, hipStream_t s)
     {
         static_assert(SYRK_LDW % BM == 0 && SYRK_KP % KB == 0, "panel padding too small for the tile");
         SyrkArgs a;
@@ -420,7 +508,14 @@ struct Solver {
         a.m = (int)m;
         a.kp = (int)kp;
         a.tiles = (int)cdiv(m, BM);
-        a.ntiles = a.tiles * (a.tiles + 1) / 2;
+        a.jt_end = (jt_end > 0 && jt_end < a.tiles) ? jt_end : 0;
+        if (a.jt_end > 0) {
+            a.ntiles = 0;
+            for (int J = 0; J < a.jt_end; ++J)
+                a.ntiles += a.tiles - J;
+        } else {
+            a.ntiles = a.tiles * (a.tiles + 1) / 2;
+        }
         a.info = info;
         const dim3 grid((unsigned)a.ntiles), block(64 * WM * WN);
         SPD_VALIDATE((check_syrk<R, CPLX, BM, KB, WM, WN>(a, grid, g_chk)));
@@ -429,105 +524,149 @@ struct Solver {
         return 0;
     }
 
-    static int syrk(int64_t m, const E *W, int64_t ldw, int64_t kp, E *C, int64_t ldc, const int *info,
-                    hipStream_t s)
+    // kw: the panel's true width (kp is it rounded up), for the flop count
+    static int syrk(int64_t m, const E *W, int64_t ldw, int64_t kp, int64_t kw, E *C, int64_t ldc, int jt_end,
+                    const int *info, hipStream_t s)
     {
         if (m <= 0)
             return 0;
+        const int64_t w = jt_end > 0 ? std::min<int64_t>(m, jt_end * syrk_bm()) : m;  // columns of C updated
+        ProfScope ps(PROF_SYRK, FMUL * (double)w * (2.0 * m - w + 1.0) * (double)kw, s);
         if constexpr (CPLX)
-            return syrk_cfg<64, 16, 2, 2>(m, W, ldw, kp, C, ldc, info, s);
+            return syrk_cfg<64, 16, 2, 2>(m, W, ldw, kp, C, ldc, jt_end, info, s);
         else
-            return syrk_cfg<128, 16, 2, 2>(m, W, ldw, kp, C, ldc, info, s);
+            return syrk_cfg<128, 16, 2, 4>(m, W, ldw, kp, C, ldc, jt_end, info, s);
     }
 
+    // Diagonal tile at (c0, c0) of order tk = min(T, n - c0): factor it in
+    // place and build inv(L_kk) in Inv (ld T); then, if rows remain below it,
+    // solve the panel into Wk with the zero-padded layout the trailing update
+    // reads (leading dimension m rounded up to SYRK_LDW, width tk rounded up to
+    // SYRK_KP) and copy it back into A.  All on stream s.
+    static int diag_panel(int64_t n, E *A, int64_t lda, int64_t T, int64_t c0, E *Inv, E *Wk, int *info,
+                          hipStream_t s)
+    {
+        const int64_t tk = std::min(T, n - c0);
+        E *D = A + c0 + c0 * lda;
+        {
+            ProfScope ps(PROF_DIAG, FMUL * 2.0 * (double)tk * tk * tk / 3.0, s);
+            for (int64_t b0 = 0; b0 < tk; b0 += LEAF) {
+                const int64_t lb = std::min<int64_t>(LEAF, tk - b0);
+                E *Db = D + b0 + b0 * lda;
+                SPD_TRY(leaves(Db, lda, lb, lb, Inv + b0 * (1 + T), T, 0, 1, true, info, c0 + b0, s));
+                const int64_t r = tk - b0 - lb;
+                if (r <= 0)
+                    continue;
+                E *P = Db + lb;  // r x lb below the leaf
+                Gemm g;          // P <- P inv(Lb)^H, in place (one tile column)
+                g.A = P;
+                g.lda = lda;
+                g.B = Inv + b0 * (1 + T);
+                g.ldb = T;
+                g.C = P;
+                g.ldc = lda;
+                g.m = r;
+                g.n = lb;
+                g.k = lb;
+                g.kmode = KM_END_BY_J;
+                g.info = info;
+                g.inplace = true;
+                SPD_TRY((gemm<R, CPLX>(NT, g, s)));
+                Gemm u;  // rest of the tile: lower part of D22 -= P P^H
+                u.A = P;
+                u.lda = lda;
+                u.B = P;
+                u.ldb = lda;
+                u.C = P + lb * lda;
+                u.ldc = lda;
+                u.m = r;
+                u.n = r;
+                u.k = lb;
+                u.tri = true;
+                u.neg = true;
+                u.beta = true;
+                u.info = info;
+                SPD_TRY((gemm<R, CPLX>(NT, u, s)));
+            }
+            SPD_TRY(merge_inverses(D, lda, 0, Inv, T, 0, 1, tk, Wk, info, s));
+        }
+        const int64_t m = n - c0 - tk;
+        if (m <= 0)
+            return 0;
+        E *P = D + tk;  // m x tk panel
+        const int64_t ldw = align_up(m, SYRK_LDW), kp = align_up(tk, SYRK_KP);
+        ProfScope ps(PROF_PANEL, FMUL * (double)m * tk * tk, s);
+        Gemm g;  // Wk = P inv(L_kk)^H
+        g.A = P;
+        g.lda = lda;
+        g.B = Inv;
+        g.ldb = T;
+        g.C = Wk;
+        g.ldc = ldw;
+        g.m = m;
+        g.n = tk;
+        g.k = tk;
+        g.kmode = KM_END_BY_J;
+        g.info = info;
+        SPD_TRY((gemm<R, CPLX>(NT, g, s)));
+        SPD_TRY(zero2d<E>(Wk + m, ldw, ldw - m, kp, s));
+        SPD_TRY(zero2d<E>(Wk + tk * ldw, ldw, m, kp - tk, s));
+        SPD_TRY(copy2d<E>(P, lda, Wk, ldw, m, tk, info, s));
+        return 0;
+    }
+
+    // Right-looking blocked Cholesky.  Without lookahead, step k is: diagonal
+    // tile and panel k, then the whole trailing update with panel k.  With
+    // lookahead (T a multiple of the trailing-update tile, three or more
+    // tiles), an auxiliary stream runs ahead by one step: it applies panel k to
+    // the next tile column only, factors diagonal tile k+1 and solves panel k+1
+    // (into the other panel buffer), while the caller's stream applies panel k
+    // to the rest of the trailing matrix.  Events order the two streams:
+    // panel k is ready before stream s uses it, and the update of step k-1 has
+    // finished before the auxiliary stream touches tile column k+1.
     static int potrf(int64_t n, E *A, int64_t lda, int64_t T_A, int *info, void *work, hipStream_t s)
     {
         SPD_TRY(set_info(info, s));
         if (n == 0)
             return 0;
         const Layout L = make_layout(n, 0, T_A, sizeof(E));
-        const int64_t T = L.T;
+        const int64_t T = L.T, nt = L.nt;
         E *Inv = (E *)work + L.inv;  // inverse of the current diagonal tile, ld T
-        E *W = (E *)work + L.w;
+        E *Wb[2] = {(E *)work + L.w, (E *)work + L.w + L.wsz};
         SPD_TRY(zero2d<E>(Inv, T, T, T, s));
-        for (int64_t c0 = 0; c0 < n; c0 += T) {
-            const int64_t tk = std::min(T, n - c0);
-            E *D = A + c0 + c0 * lda;
-            {
-                ProfScope ps(PROF_DIAG, FMUL * 2.0 * (double)tk * tk * tk / 3.0, s);
-                // ---- 1. diagonal tile, leaf by leaf
-                for (int64_t b0 = 0; b0 < tk; b0 += LEAF) {
-                    const int64_t lb = std::min<int64_t>(LEAF, tk - b0);
-                    E *Db = D + b0 + b0 * lda;
-                    SPD_TRY(leaves(Db, lda, lb, lb, Inv + b0 * (1 + T), T, 0, 1, true, info, c0 + b0, s));
-                    const int64_t r = tk - b0 - lb;
-                    if (r <= 0)
-                        continue;
-                    E *P = Db + lb;  // r x lb below the leaf
-                    Gemm g;          // P <- P inv(Lb)^H, in place (one tile column)
-                    g.A = P;
-                    g.lda = lda;
-                    g.B = Inv + b0 * (1 + T);
-                    g.ldb = T;
-                    g.C = P;
-                    g.ldc = lda;
-                    g.m = r;
-                    g.n = lb;
-                    g.k = lb;
-                    g.kmode = KM_END_BY_J;
-                    g.info = info;
-                    g.inplace = true;
-                    SPD_TRY((gemm<R, CPLX>(NT, g, s)));
-                    Gemm u;  // rest of the tile: lower part of D22 -= P P^H
-                    u.A = P;
-                    u.lda = lda;
-                    u.B = P;
-                    u.ldb = lda;
-                    u.C = P + lb * lda;
-                    u.ldc = lda;
-                    u.m = r;
-                    u.n = r;
-                    u.k = lb;
-                    u.tri = true;
-                    u.neg = true;
-                    u.beta = true;
-                    u.info = info;
-                    SPD_TRY((gemm<R, CPLX>(NT, u, s)));
-                }
-                SPD_TRY(merge_inverses(D, lda, 0, Inv, T, 0, 1, tk, W, info, s));
+        const bool lookahead = lookahead_enabled() && (T % syrk_bm() == 0) && nt >= 3;
+        if (!lookahead) {
+            for (int64_t c0 = 0; c0 < n; c0 += T) {
+                const int64_t tk = std::min(T, n - c0), m = n - c0 - tk;
+                SPD_TRY(diag_panel(n, A, lda, T, c0, Inv, Wb[0], info, s));
+                if (m > 0)
+                    SPD_TRY(syrk(m, Wb[0], align_up(m, SYRK_LDW), align_up(tk, SYRK_KP), tk,
+                                 A + (c0 + tk) * (1 + lda), lda, 0, info, s));
             }
-            const int64_t m = n - c0 - tk;
-            if (m <= 0)
-                break;
-            E *P = D + tk;  // m x tk panel
-            // W: m x tk panel with leading dimension ldw, zero-padded to ldw x kp
-            const int64_t ldw = align_up(m, SYRK_LDW), kp = align_up(tk, SYRK_KP);
-            {
-                // ---- 2. panel: W = P inv(L_kk)^H, then P = W
-                ProfScope ps(PROF_PANEL, FMUL * (double)m * tk * tk, s);
-                Gemm g;
-                g.A = P;
-                g.lda = lda;
-                g.B = Inv;
-                g.ldb = T;
-                g.C = W;
-                g.ldc = ldw;
-                g.m = m;
-                g.n = tk;
-                g.k = tk;
-                g.kmode = KM_END_BY_J;
-                g.info = info;
-                SPD_TRY((gemm<R, CPLX>(NT, g, s)));
-                SPD_TRY(zero2d<E>(W + m, ldw, ldw - m, kp, s));
-                SPD_TRY(zero2d<E>(W + tk * ldw, ldw, m, kp - tk, s));
-                SPD_TRY(copy2d<E>(P, lda, W, ldw, m, tk, info, s));
-            }
-            {
-                // ---- 3. trailing update: lower part of A22 -= W W^H
-                ProfScope ps(PROF_SYRK, FMUL * (double)m * (double)(m + 1) * (double)tk, s);
-                SPD_TRY(syrk(m, W, ldw, kp, P + tk * lda, lda, info, s));
-            }
+            return 0;
         }
+        Lookahead la;
+        SPD_TRY(la.begin(s));
+        hipStream_t sl = la.look;
+        SPD_TRY(diag_panel(n, A, lda, T, 0, Inv, Wb[0], info, sl));
+        SPD_TRY(la.record(la.ev_panel, sl));
+        const int jt = (int)(T / syrk_bm()), kp = (int)align_up(T, SYRK_KP);
+        for (int64_t k = 0; k + 1 < nt; ++k) {
+            const int64_t c0 = k * T, m = n - c0 - T, ldw = align_up(m, SYRK_LDW);
+            E *Wk = Wb[k % 2];
+            SPD_TRY(la.wait(s, la.ev_panel));  // panel k
+            if (k > 0)
+                SPD_TRY(la.wait(sl, la.ev_rest));  // update of step k-1 done
+            // tile column k+1 of the trailing matrix, then diagonal tile and panel k+1
+            SPD_TRY(syrk(m, Wk, ldw, kp, T, A + (c0 + T) * (1 + lda), lda, jt, info, sl));
+            SPD_TRY(diag_panel(n, A, lda, T, c0 + T, Inv, Wb[(k + 1) % 2], info, sl));
+            SPD_TRY(la.record(la.ev_panel, sl));
+            // the rest of the trailing matrix, beyond tile column k+1
+            if (m > T)
+                SPD_TRY(syrk(m - T, Wk + T, ldw, kp, T, A + (c0 + 2 * T) * (1 + lda), lda, 0, info, s));
+            SPD_TRY(la.record(la.ev_rest, s));
+        }
+        SPD_TRY(la.wait(s, la.ev_panel));  // join: last diagonal tile
         return 0;
     }
 

@@ -168,9 +168,9 @@ static bool check_syrk(const SyrkArgs &p, dim3 grid, Checker &c)
     }
     for (unsigned b = 0; b < grid.x; ++b) {
         int I, J;
-        tri_index(xcd_remap((int)b, p.ntiles), I, J);
+        syrk_tile(p, (int)b, I, J);
         const int i0 = I * BM, j0 = J * BM;
-        if (I >= p.tiles || J > I) {
+        if (I >= p.tiles || J > I || (p.jt_end > 0 && J >= p.jt_end)) {
             c.err = "syrk_kernel: workgroup maps outside the lower tiles";
             return false;
         }

@@ -197,6 +197,10 @@ gemm_kernel(const GemmArgs p)
 #pragma unroll
             for (int fj = 0; fj < FN; ++fj)
                 acc[c][fi][fj] = V4{0, 0, 0, 0};
+    // The product is always accumulated with a plus sign; C - AB is formed as
+    // -((-C) + AB), which rounds exactly like C + (-A)B (negation commutes with
+    // rounding), so the operands reach the matrix cores as loaded.
+    const R sg = p.neg ? R(-1) : R(1);
     if (p.beta) {
 #pragma unroll
         for (int fi = 0; fi < FM; ++fi) {
@@ -209,9 +213,9 @@ gemm_kernel(const GemmArgs p)
                     if (i < m && j < n) {
                         R re, im = 0;
                         Elem<R, CPLX>::load(C + i + (int64_t)j * p.ldc, re, im);
-                        acc[0][fi][fj][q] = re;
+                        acc[0][fi][fj][q] = sg * re;
                         if constexpr (CPLX)
-                            acc[NP - 1][fi][fj][q] = im;
+                            acc[NP - 1][fi][fj][q] = sg * im;
                     }
                 }
             }
@@ -220,7 +224,6 @@ gemm_kernel(const GemmArgs p)
 
     // ---- global -> register staging
     R ra[NP][LA], rb[NP][LB];
-    const R sgnA = p.neg ? R(-1) : R(1);
     auto load_tiles = [&](int k0) {
 #pragma unroll
         for (int q = 0; q < LA; ++q) {
@@ -235,8 +238,8 @@ gemm_kernel(const GemmArgs p)
                 Elem<R, CPLX>::load(src, re, im);
                 if (AT) im = -im;
             }
-            ra[0][q] = sgnA * re;
-            if constexpr (CPLX) ra[NP - 1][q] = sgnA * im;
+            ra[0][q] = re;
+            if constexpr (CPLX) ra[NP - 1][q] = im;
         }
 #pragma unroll
         for (int q = 0; q < LB; ++q) {
@@ -333,8 +336,8 @@ gemm_kernel(const GemmArgs p)
             for (int q = 0; q < 4; ++q) {
                 const int j = j0 + jb + fj * 16 + acc_row<R>(lk, q);
                 if (i < m && j < n && (!p.tri || i >= j))
-                    Elem<R, CPLX>::store(C + i + (int64_t)j * p.ldc, acc[0][fi][fj][q],
-                                         CPLX ? acc[NP - 1][fi][fj][q] : R(0));
+                    Elem<R, CPLX>::store(C + i + (int64_t)j * p.ldc, sg * acc[0][fi][fj][q],
+                                         CPLX ? sg * acc[NP - 1][fi][fj][q] : R(0));
             }
         }
     }

@@ -45,8 +45,8 @@ __host__ __device__ inline bool leaf_geom(const LeafArgs &p, int g, int64_t &c0,
     return true;
 }
 
-// One workgroup per leaf.  Leaf g lies in tile t = g / lpt at leaf slot
-// b = g % lpt: columns c = t*T + b*LEAF ... of the matrix.
+// One workgroup per leaf.  Leaf w lies in tile t = w / lpt at leaf slot
+// b = w % lpt: columns c = t*T + b*LEAF ... of the matrix.
 //
 // factor = 1: right-looking unblocked Cholesky of the leaf's lower triangle in
 // LDS (pivot from the real part of the diagonal; a pivot that is not > 0,
@@ -57,12 +57,18 @@ __host__ __device__ inline bool leaf_geom(const LeafArgs &p, int g, int64_t &c0,
 // being final once column j of L is, and then removed from the rows below.
 //
 // factor = 0: the leaf already holds L; only inv(L) is produced.
+//
+// Thread (r, g) = (tid % 64, tid / 64) owns row r of the leaf and of its
+// inverse, columns g, g + 4, g + 8, ...: every column step is a few LDS
+// read-modify-writes per thread with no index division, and the values of
+// column j a wave needs are the same for all its lanes (LDS broadcasts).
 template <typename R, bool CPLX>
 __global__ void __launch_bounds__(256) leaf_kernel(const LeafArgs p)
 {
     typedef typename Elem<R, CPLX>::type E;
     constexpr int NP = CPLX ? 2 : 1;
     constexpr int LD = LEAF + 1;
+    constexpr int G = 4;           // column phases (waves)
     __shared__ R S[NP][LEAF][LD];  // S[.][c][r] = L(r, c)
     __shared__ R X[NP][LEAF][LD];  // X[.][c][r] = inv(L)(r, c)
     __shared__ R dg[LEAF];
@@ -76,11 +82,11 @@ __global__ void __launch_bounds__(256) leaf_kernel(const LeafArgs p)
     E *A = (E *)p.A + c0 + c0 * p.lda;
     E *Inv = (E *)p.Inv + ioff;
     const int tid = threadIdx.x;
+    const int r = tid & (LEAF - 1), g = tid / LEAF;
 
-    for (int e = tid; e < lb * lb; e += 256) {
-        const int r = e % lb, c = e / lb;
+    for (int c = g; c < lb; c += G) {
         R re = 0, im = 0;
-        if (r >= c)
+        if (r < lb && r >= c)
             Elem<R, CPLX>::load(A + r + (int64_t)c * p.lda, re, im);
         if (r == c)
             im = 0;
@@ -105,44 +111,39 @@ __global__ void __launch_bounds__(256) leaf_kernel(const LeafArgs p)
             ljj = S[0][j][j];
         }
         const R rinv = R(1) / ljj;
-        // column j of L below the diagonal, and row j of inv(L)
-        for (int e = tid; e < lb; e += 256) {
-            if (p.factor && e > j) {
-                S[0][j][e] *= rinv;
-                if constexpr (CPLX) S[NP - 1][j][e] *= rinv;
-            }
-            if (e <= j) {
-                X[0][e][j] *= rinv;
-                if constexpr (CPLX) X[NP - 1][e][j] *= rinv;
-            }
+        // column j of L below the diagonal (phase 0), row j of inv(L) (phase 1)
+        if (g == 0 && p.factor && r > j && r < lb) {
+            S[0][j][r] *= rinv;
+            if constexpr (CPLX) S[NP - 1][j][r] *= rinv;
+        }
+        if (g == 1 && r <= j) {
+            X[0][r][j] *= rinv;
+            if constexpr (CPLX) X[NP - 1][r][j] *= rinv;
         }
         if (p.factor && tid == 0)
             dg[j] = ljj;
         __syncthreads();
-        const int w = lb - j - 1;
-        if (w > 0) {
+        if (r > j && r < lb) {
+            const R ar = S[0][j][r];
+            const R ai = CPLX ? S[NP - 1][j][r] : R(0);
             if (p.factor) {
                 // trailing lower triangle: S(r, c) -= L(r, j) conj(L(c, j)), j < c <= r
-                for (int e = tid; e < w * w; e += 256) {
-                    const int r = j + 1 + e % w, c = j + 1 + e / w;
-                    if (r >= c) {
-                        const R ar = S[0][j][r], br = S[0][j][c];
-                        if constexpr (CPLX) {
-                            const R ai = S[1][j][r], bi = S[1][j][c];
-                            S[0][c][r] -= ar * br + ai * bi;
-                            S[1][c][r] -= ai * br - ar * bi;
-                        } else {
-                            S[0][c][r] -= ar * br;
-                        }
+                for (int c = j + 1 + g; c <= r; c += G) {
+                    const R br = S[0][j][c];
+                    if constexpr (CPLX) {
+                        const R bi = S[1][j][c];
+                        S[0][c][r] -= ar * br + ai * bi;
+                        S[1][c][r] -= ai * br - ar * bi;
+                    } else {
+                        S[0][c][r] -= ar * br;
                     }
                 }
             }
             // rows below j of inv(L): X(r, c) -= L(r, j) X(j, c), c <= j < r
-            for (int e = tid; e < w * (j + 1); e += 256) {
-                const int r = j + 1 + e % w, c = e / w;
-                const R ar = S[0][j][r], xr = X[0][c][j];
+            for (int c = g; c <= j; c += G) {
+                const R xr = X[0][c][j];
                 if constexpr (CPLX) {
-                    const R ai = S[1][j][r], xi = X[1][c][j];
+                    const R xi = X[1][c][j];
                     X[0][c][r] -= ar * xr - ai * xi;
                     X[1][c][r] -= ar * xi + ai * xr;
                 } else {
@@ -153,8 +154,9 @@ __global__ void __launch_bounds__(256) leaf_kernel(const LeafArgs p)
         __syncthreads();
     }
 
-    for (int e = tid; e < lb * lb; e += 256) {
-        const int r = e % lb, c = e / lb;
+    for (int c = g; c < lb; c += G) {
+        if (r >= lb)
+            continue;
         if (p.factor && r >= c) {
             if (r == c)
                 Elem<R, CPLX>::store(A + r + (int64_t)c * p.lda, dg[c], R(0));

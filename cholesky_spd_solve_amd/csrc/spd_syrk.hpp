@@ -14,7 +14,8 @@
 // Only C needs bounds: the tiles on the diagonal and those that cross row m.
 //
 // A workgroup owns one BM x BM tile (I, J), I >= J, of the lower triangle of
-// C, split over WM x WN wave64s; each wave holds (BM/WM) x (BM/WN) of C as
+// C (of all of it, or of its first jt_end tile columns only), split over
+// WM x WN wave64s; each wave holds (BM/WM) x (BM/WN) of C as
 // 16x16 accumulator blocks of v_mfma_*_16x16x4.  W is consumed KB columns at
 // a time: the next slice is loaded from HBM into registers (16-byte vector
 // loads, 32-bit offsets from a uniform tile origin) while the current slice is
@@ -40,9 +41,29 @@ struct SyrkArgs {
     int m;          // order of C
     int kp;         // columns of W (a multiple of KB)
     int tiles;      // tile rows = ceil(m / BM)
-    int ntiles;     // lower tiles = tiles * (tiles + 1) / 2
+    int jt_end;     // 0: every lower tile; > 0: only tile columns J < jt_end
+    int ntiles;     // number of tiles updated (workgroups)
     const int *info;  // if non-null and *info != 0 the kernel does nothing
 };
+
+// Tile (I, J) of workgroup b: the whole lower triangle in row order, or, with
+// jt_end > 0, the first jt_end tile columns in column order (column J holds
+// tiles I = J .. tiles - 1).  Workgroup ids are first remapped so consecutive
+// tiles share an XCD.  Shared with the host-side launch validator.
+__host__ __device__ inline void syrk_tile(const SyrkArgs &p, int b, int &I, int &J)
+{
+    int t = xcd_remap(b, p.ntiles);
+    if (p.jt_end <= 0) {
+        tri_index(t, I, J);
+        return;
+    }
+    J = 0;
+    while (J + 1 < p.jt_end && t >= p.tiles - J) {
+        t -= p.tiles - J;
+        ++J;
+    }
+    I = J + t;
+}
 
 // Elements per 16-byte vector load and the loader's thread -> element map,
 // shared with the host-side launch validator.
@@ -85,7 +106,7 @@ syrk_kernel(const SyrkArgs p)
         return;
 
     int I, J;
-    tri_index(xcd_remap((int)blockIdx.x, p.ntiles), I, J);
+    syrk_tile(p, (int)blockIdx.x, I, J);
     const int i0 = I * BM, j0 = J * BM;
 
     const int tid = threadIdx.x;

@@ -53,11 +53,16 @@ def test_workspace_size(lib):
     assert f(1, 10, -1, 64) == 0
     assert f(1, 10, 1, 0) == 0
     assert f(9, 10, 1, 4) == 0
-    # INV nt*T*T + W n*T + TMP max(T*T, T*nrhs), each rounded up to 256 bytes
+    # INV nt*T*T + two panels of (n rounded up to 128) x (T rounded up to 32)
+    # + TMP max(T*T, T*nrhs), each rounded up to 256 bytes
     n, nrhs, T = 32768, 128, 512
-    el = (n // T) * T * T + n * T + T * T
+    el = (n // T) * T * T + 2 * n * T + T * T
     assert f(1, n, nrhs, T) == el * 8
     assert f(3, n, nrhs, T) == el * 16
+    n, nrhs, T = 1000, 7, 100
+    up = lambda a, b: -(-a // b) * b
+    el = up(10 * 100 * 100, 32) + 2 * up(1024 * 128, 32) + up(100 * 100, 32)
+    assert f(1, n, nrhs, T) == el * 8
     # T_A > n is clamped to n
     assert f(1, 100, 1, 1000) == f(1, 100, 1, 100)
 
