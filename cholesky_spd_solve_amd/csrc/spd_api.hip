@@ -385,7 +385,10 @@ struct Solver {
         if (grid <= 0)
             return 0;
         SPD_VALIDATE((check_leaf<R, CPLX>(p, (unsigned)grid, g_chk)));
-        leaf_kernel<R, CPLX><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p);
+        if constexpr (CPLX)
+            leaf_kernel<R, CPLX><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p);
+        else
+            leaf16_kernel<R><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p);
         SPD_CHECK_LAUNCH("leaf_kernel");
         return 0;
     }

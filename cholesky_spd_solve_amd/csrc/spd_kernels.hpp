@@ -170,6 +170,235 @@ __global__ void __launch_bounds__(256) leaf_kernel(const LeafArgs p)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Blocked leaf for real types: the same result as leaf_kernel (L and inv(L)
+// of a LEAF x LEAF diagonal block) with 16 x 16 sub-blocks.
+//
+//   for b = 0..3:  factor and invert the diagonal block (b, b)        (one wave)
+//                  L(i, b) = A(i, b) inv(L(b, b))^T         i > b      (MFMA)
+//                  A(i, j) -= L(i, b) L(j, b)^T        b < j <= i      (MFMA)
+//   inv(L)(i, b) = -inv(L(i, i)) sum_{b<=k<i} L(i, k) inv(L)(k, b)    (MFMA,
+//                  by increasing i - b)
+//
+// The 16 x 16 diagonal blocks are done in registers by one wave: lane (r, q)
+// holds row r, columns 4q..4q+3 of the block and of its inverse; the pivot is
+// read with v_readlane and column j reaches the other lanes with shuffles.
+// Every 16 x 16 x 16 product is four v_mfma_*_16x16x4 with operands read from
+// LDS.  Padding beyond lb is the identity.
+
+// Value of x in lane `lane` of the wave (lane wave-uniform).
+__device__ __forceinline__ double lane_value(double x, int lane)
+{
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ float lane_value(float x, int lane)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
+// Value of x in lane src (per-lane source), through the LDS crossbar.
+__device__ __forceinline__ double lane_shuffle(double x, int src)
+{
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const int lo = __builtin_amdgcn_ds_bpermute(src << 2, (int)(uint32_t)u);
+    const int hi = __builtin_amdgcn_ds_bpermute(src << 2, (int)(uint32_t)(u >> 32));
+    return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+__device__ __forceinline__ float lane_shuffle(float x, int src)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, x)));
+}
+
+// acc += A B for 16 x 16 blocks in LDS: A(r, k) = pa[k * ak + r * ar],
+// B(k, c) = pb[k * bk + c * bc].  Lane (li, lk) = (lane % 16, lane / 16) ends
+// with C(li, acc_row(lk, q)) in acc[q].
+template <typename R>
+__device__ __forceinline__ typename AccT<R>::type mma16(const R *pa, int ak, int ar, const R *pb, int bk, int bc,
+                                                        typename AccT<R>::type acc)
+{
+    const int lane = threadIdx.x & 63, li = lane & 15, lk = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int k = 4 * s + lk;
+        const R a = pa[k * ak + li * ar];
+        const R b = pb[k * bk + li * bc];
+        acc = mfma16(b, a, acc);
+    }
+    return acc;
+}
+
+constexpr int LB16 = 16;         // sub-block order
+constexpr int LDL = LEAF + 1;    // LDS row length of the leaf arrays
+
+// Factor (factor = 1) and invert, or only invert, the 16 x 16 diagonal block
+// at (o, o) of S (S[c][r] = element (r, c)); L goes back to S, inv to X.  One
+// wave.  A pivot that is not > 0 records info (columns < lb only), sets
+// *failed and is replaced by 1.
+template <typename R>
+__device__ void diag16(R (*S)[LDL], R (*X)[LDL], int o, int factor, int lb, int gcol, int *info, int *failed)
+{
+    const int lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+    R v[4], w[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int c = 4 * q + t;
+        v[t] = (r >= c) ? S[o + c][o + r] : R(0);
+        w[t] = (r == c) ? R(1) : R(0);
+    }
+#pragma unroll
+    for (int j = 0; j < LB16; ++j) {
+        const int qo = j >> 2, t = j & 3;
+        const R d = lane_value(v[t], qo * 16 + j);
+        R ljj = d;
+        if (factor) {
+            if (!(d > R(0))) {
+                if (lane == 0 && o + j < lb) {
+                    atomicCAS(info, 0, gcol + o + j + 1);
+                    *failed = 1;
+                }
+                ljj = R(1);
+            } else {
+                ljj = sqrt(d);
+            }
+        }
+        const R rinv = R(1) / ljj;
+        if (factor && q == qo)
+            v[t] = (r > j) ? v[t] * rinv : ((r == j) ? ljj : v[t]);
+        const R lrj = lane_shuffle(v[t], qo * 16 + r);  // L(r, j)
+        if (factor) {
+#pragma unroll
+            for (int t2 = 0; t2 < 4; ++t2) {
+                const int c = 4 * q + t2;
+                const R lcj = lane_shuffle(v[t], qo * 16 + c);  // L(c, j)
+                if (c > j && r >= c)
+                    v[t2] -= lrj * lcj;
+            }
+        }
+#pragma unroll
+        for (int t2 = 0; t2 < 4; ++t2) {
+            const int c = 4 * q + t2;
+            const R xjc = lane_shuffle(w[t2], q * 16 + j) * rinv;  // final X(j, c)
+            if (c <= j)
+                w[t2] = (r == j) ? xjc : ((r > j) ? w[t2] - lrj * xjc : w[t2]);
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int c = 4 * q + t;
+        if (factor)
+            S[o + c][o + r] = (r >= c) ? v[t] : R(0);
+        X[o + c][o + r] = (r >= c) ? w[t] : R(0);
+    }
+}
+
+template <typename R>
+__global__ void __launch_bounds__(256) leaf16_kernel(const LeafArgs p)
+{
+    typedef typename AccT<R>::type V4;
+    constexpr int NB = LEAF / LB16;  // 4 sub-blocks
+    __shared__ R S[LEAF][LDL];       // S[c][r] = L(r, c)
+    __shared__ R X[LEAF][LDL];       // X[c][r] = inv(L)(r, c)
+    __shared__ R Tm[4][LB16][LB16 + 1];  // per-wave 16 x 16 scratch
+    __shared__ int failed;
+
+    if (p.info != nullptr && *p.info != 0)
+        return;
+    int64_t c0, ioff;
+    int lb;
+    if (!leaf_geom(p, (int)blockIdx.x, c0, lb, ioff))
+        return;
+    R *A = (R *)p.A + c0 + c0 * p.lda;
+    R *Inv = (R *)p.Inv + ioff;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int li = lane & 15, lk = lane >> 4;
+    const int r = tid & (LEAF - 1), g = tid / LEAF;
+
+    for (int c = g; c < LEAF; c += 4) {
+        R v = (r == c) ? R(1) : R(0);
+        if (r < lb && c < lb && r >= c)
+            v = A[r + (int64_t)c * p.lda];
+        S[c][r] = v;
+        X[c][r] = R(0);
+    }
+    if (tid == 0)
+        failed = 0;
+    __syncthreads();
+
+    // store the 16 x 16 accumulator block (lane layout of mma16) at (ro, co)
+    // of M, scaled by sg; lower part only when low
+    auto put = [&](R (*M)[LDL], int ro, int co, const V4 &acc, R sg, bool low) {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+            const int rr = li, cc = acc_row<R>(lk, qq);
+            if (!low || rr >= cc)
+                M[co + cc][ro + rr] = sg * acc[qq];
+        }
+    };
+
+    for (int b = 0; b < NB; ++b) {
+        const int o = b * LB16;
+        if (wave == 0)
+            diag16<R>(S, X, o, p.factor, lb, p.col0 + (int)c0, p.info, &failed);
+        __syncthreads();
+        if (p.factor) {
+            // L(i, b) = A(i, b) inv(L(b, b))^T, one block per wave
+            const int i = b + 1 + wave;
+            if (i < NB) {
+                V4 acc = {0, 0, 0, 0};
+                acc = mma16<R>(&S[o][i * LB16], LDL, 1, &X[o][o], LDL, 1, acc);
+                put(S, i * LB16, o, acc, R(1), false);
+            }
+            __syncthreads();
+            // A(i, j) -= L(i, b) L(j, b)^T, b < j <= i
+            for (int t = wave; t < (NB - 1 - b) * (NB - b) / 2; t += 4) {
+                int ti, tj;
+                tri_index(t, ti, tj);
+                const int i2 = b + 1 + ti, j2 = b + 1 + tj;
+                V4 acc = {0, 0, 0, 0};
+                acc = mma16<R>(&S[o][i2 * LB16], LDL, 1, &S[o][j2 * LB16], LDL, 1, acc);
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    const int rr = li, cc = acc_row<R>(lk, qq);
+                    if (i2 != j2 || rr >= cc)
+                        S[j2 * LB16 + cc][i2 * LB16 + rr] -= acc[qq];
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    // inverse off-diagonal blocks, by distance d = i - b
+    for (int d = 1; d < NB; ++d) {
+        const int b = wave, i = b + d;
+        if (i < NB) {
+            V4 acc = {0, 0, 0, 0};
+            for (int k = b; k < i; ++k)  // T = sum_k L(i, k) X(k, b)
+                acc = mma16<R>(&S[k * LB16][i * LB16], LDL, 1, &X[b * LB16][k * LB16], 1, LDL, acc);
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq)
+                Tm[wave][acc_row<R>(lk, qq)][li] = acc[qq];  // Tm[c][r] = T(r, c)
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's LDS stores done before reading them back
+            __builtin_amdgcn_wave_barrier();
+            V4 acc2 = {0, 0, 0, 0};  // X(i, b) = -inv(L(i, i)) T
+            acc2 = mma16<R>(&X[i * LB16][i * LB16], LDL, 1, &Tm[wave][0][0], 1, LB16 + 1, acc2);
+            put(X, i * LB16, b * LB16, acc2, R(-1), false);
+        }
+        __syncthreads();
+    }
+
+    if (failed)
+        return;
+    for (int c = g; c < lb; c += 4) {
+        if (r >= lb)
+            continue;
+        if (p.factor && r >= c)
+            A[r + (int64_t)c * p.lda] = S[c][r];
+        Inv[r + (int64_t)c * p.ldi] = (r >= c) ? X[c][r] : R(0);
+    }
+}
+
 // log det A = 2 * sum_i log(Re L_ii), accumulated in double.  One workgroup;
 // thread t owns the diagonal entries i = t, t + 1024, ... and the partial sums
 // are combined by a fixed binary tree, so the result is the same bits on every
