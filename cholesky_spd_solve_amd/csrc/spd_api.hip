@@ -197,11 +197,16 @@ static int gemm(Lay lay, const Gemm &g, hipStream_t s)
         return launch_gemm_cfg<R, CPLX, 64, 64, 16, 2, 2>(lay, g, s);
     }
     if constexpr (!CPLX) {
+        // large products: 128x128 tiles; small ones: 64x64, or 32x32 when even
+        // 64x64 tiles would leave most CUs idle (latency-bound chains)
         const int64_t tiles128 = g.tri ? cdiv(g.m, 128) * (cdiv(g.m, 128) + 1) / 2
                                        : cdiv(g.m, 128) * cdiv(g.n, 128);
+        const int64_t tiles64 = g.tri ? cdiv(g.m, 64) * (cdiv(g.m, 64) + 1) / 2 : cdiv(g.m, 64) * cdiv(g.n, 64);
         if (!g.small && tiles128 * g.batch >= 512)
             return launch_gemm_cfg<R, CPLX, 128, 128, 16, 2, 2>(lay, g, s);
-        return launch_gemm_cfg<R, CPLX, 64, 64, 16, 2, 2>(lay, g, s);
+        if (tiles64 * g.batch >= 128)
+            return launch_gemm_cfg<R, CPLX, 64, 64, 16, 2, 2>(lay, g, s);
+        return launch_gemm_cfg<R, CPLX, 32, 32, 16, 2, 2>(lay, g, s);
     } else {
         const int64_t tiles64 = g.tri ? cdiv(g.m, 64) * (cdiv(g.m, 64) + 1) / 2 : cdiv(g.m, 64) * cdiv(g.n, 64);
         if (!g.small && tiles64 * g.batch >= 512)
@@ -611,6 +616,7 @@ struct Solver {
         g.k = tk;
         g.kmode = KM_END_BY_J;
         g.info = info;
+        g.small = true;  // lean tiles: this product shares the GPU with the trailing update
         SPD_TRY((gemm<R, CPLX>(NT, g, s)));
         SPD_TRY(zero2d<E>(Wk + m, ldw, ldw - m, kp, s));
         SPD_TRY(zero2d<E>(Wk + tk * ldw, ldw, m, kp - tk, s));

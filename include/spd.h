@@ -22,11 +22,19 @@
  *   - Buffers are transformed in place: potrf overwrites the lower triangle of
  *     A with L (real positive diagonal); potrs overwrites B with X.
  *   - All pointers named d_* or dA/dB are device pointers owned by the caller.
- *     The library allocates no device memory and keeps no state between calls
- *     (except while profiling is switched on, see spd_profile_*).
+ *     The library allocates no device memory.  Its only state between calls is
+ *     what spd_profile_* keeps while profiling is on and, for the lookahead
+ *     schedule of spd_potrf, one auxiliary HIP stream (default priority,
+ *     non-blocking) and three events per host thread and device, created on
+ *     first use and kept until the process ends.  Calls from one host thread
+ *     must not overlap on one device (they share that stream).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
- *     the calls return without waiting for it.  Numerical status is reported on
- *     the device through d_info, so no host synchronisation happens inside.
+ *     the calls return without waiting for it.  spd_potrf may also run part of
+ *     the factorization on its auxiliary stream, ordered with `stream` by
+ *     events: it starts after the work already on `stream` and everything it
+ *     enqueues is complete before any work enqueued on `stream` afterwards.
+ *     Numerical status is reported on the device through d_info, so no host
+ *     synchronisation happens inside.
  *   - Return value: 0 when the work was enqueued; -i when the i-th argument is
  *     invalid (nothing is enqueued); SPD_ERR_HIP when the HIP runtime reported
  *     an error while enqueueing, SPD_ERR_CHECK when launch validation (see
