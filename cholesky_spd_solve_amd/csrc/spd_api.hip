@@ -540,10 +540,16 @@ struct Solver {
             return 0;
         const int64_t w = jt_end > 0 ? std::min<int64_t>(m, jt_end * syrk_bm()) : m;  // columns of C updated
         ProfScope ps(PROF_SYRK, FMUL * (double)w * (2.0 * m - w + 1.0) * (double)kw, s);
+        // slice depth: 16 for the large early steps, 8 below (more
+        // workgroups in flight per byte of LDS; measured better for m < ~24k)
         if constexpr (CPLX)
             return syrk_cfg<64, 16, 2, 2>(m, W, ldw, kp, C, ldc, jt_end, info, s);
-        else
+        else if constexpr (sizeof(R) == 4)  // a 16-deep slice is one 16-byte load per thread
             return syrk_cfg<128, 16, 2, 4>(m, W, ldw, kp, C, ldc, jt_end, info, s);
+        else if (m >= 24576)
+            return syrk_cfg<128, 16, 2, 4>(m, W, ldw, kp, C, ldc, jt_end, info, s);
+        else
+            return syrk_cfg<128, 8, 2, 4>(m, W, ldw, kp, C, ldc, jt_end, info, s);
     }
 
     // Diagonal tile at (c0, c0) of order tk = min(T, n - c0): factor it in

@@ -19,7 +19,9 @@
 // 16x16 accumulator blocks of v_mfma_*_16x16x4.  W is consumed KB columns at
 // a time: the next slice is loaded from HBM into registers (16-byte vector
 // loads, 32-bit offsets from a uniform tile origin) while the current slice is
-// read from LDS by the matrix cores; one barrier per slice.  C is read and
+// read from LDS by the matrix cores; one barrier per slice.  Within a slice the
+// operands of the next k-step are read from LDS ahead of the current one's
+// matrix-core instructions.  C is read and
 // written once, in the epilogue, one 16-row block at a time.
 //
 // Complex types keep real and imaginary parts in separate LDS planes and use
@@ -193,10 +195,11 @@ syrk_kernel(const SyrkArgs p)
             wb += step;
             load(wa, wb);
         }
-#pragma unroll
-        for (int s = 0; s < KB / 4; ++s) {
-            const int kr = s * 4 + lk;
-            R a[NP][FM], b[NP][FN];
+        // Operand fragments are double-buffered in registers: those of k-step
+        // s+1 are read from LDS before the matrix-core instructions of k-step s
+        // are issued, so the LDS latency hides behind them.
+        R fa[2][NP][FM], fb[2][NP][FN];
+        auto frag = [&](int kr, R (&a)[NP][FM], R (&b)[NP][FN]) {
 #pragma unroll
             for (int c = 0; c < NP; ++c) {
 #pragma unroll
@@ -206,6 +209,14 @@ syrk_kernel(const SyrkArgs p)
                 for (int fj = 0; fj < FN; ++fj)
                     b[c][fj] = Bs[cur][c][kr][jb + fj * 16 + li];
             }
+        };
+        frag(lk, fa[0], fb[0]);
+#pragma unroll
+        for (int s = 0; s < KB / 4; ++s) {
+            if (s + 1 < KB / 4)
+                frag((s + 1) * 4 + lk, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+            const R(&a)[NP][FM] = fa[s & 1];
+            const R(&b)[NP][FN] = fb[s & 1];
 #pragma unroll
             for (int fi = 0; fi < FM; ++fi)
 #pragma unroll
