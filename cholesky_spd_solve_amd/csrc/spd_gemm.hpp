@@ -152,9 +152,6 @@ gemm_kernel(const GemmArgs p)
     __shared__ R As[2][NP][KB][PA];
     __shared__ R Bs[2][NP][KB][PB];
 
-    if (p.info != nullptr && *p.info != 0)
-        return;
-
     // ---- tile coordinates
     int I, J;
     const int t = xcd_remap((int)blockIdx.x, p.ntiles);
@@ -281,8 +278,13 @@ gemm_kernel(const GemmArgs p)
         }
     };
 
-    if (kbeg < kend) {
+    // the status word is read once the first loads are in flight; the operand
+    // buffers are valid whatever it holds, and nothing is written before it
+    if (kbeg < kend)
         load_tiles(kbeg);
+    if (p.info != nullptr && *p.info != 0)
+        return;
+    if (kbeg < kend) {
         store_tiles(0);
         __syncthreads();
         int cur = 0;

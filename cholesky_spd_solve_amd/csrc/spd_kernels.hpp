@@ -73,8 +73,6 @@ __global__ void __launch_bounds__(256) leaf_kernel(const LeafArgs p)
     __shared__ R X[NP][LEAF][LD];  // X[.][c][r] = inv(L)(r, c)
     __shared__ R dg[LEAF];
 
-    if (p.info != nullptr && *p.info != 0)
-        return;
     int64_t c0, ioff;
     int lb;
     if (!leaf_geom(p, (int)blockIdx.x, c0, lb, ioff))
@@ -84,16 +82,29 @@ __global__ void __launch_bounds__(256) leaf_kernel(const LeafArgs p)
     const int tid = threadIdx.x;
     const int r = tid & (LEAF - 1), g = tid / LEAF;
 
-    for (int c = g; c < lb; c += G) {
-        R re = 0, im = 0;
-        if (r < lb && r >= c)
-            Elem<R, CPLX>::load(A + r + (int64_t)c * p.lda, re, im);
+    // all loads in flight together, the status word alongside them
+    R vr[LEAF / G], vi[LEAF / G];
+#pragma unroll
+    for (int k = 0; k < LEAF / G; ++k) {
+        const int c = g + G * k;
+        vr[k] = 0;
+        vi[k] = 0;
+        if (r < lb && c < lb && r >= c)
+            Elem<R, CPLX>::load(A + r + (int64_t)c * p.lda, vr[k], vi[k]);
         if (r == c)
-            im = 0;
-        S[0][c][r] = re;
-        if constexpr (CPLX) S[NP - 1][c][r] = im;
-        X[0][c][r] = (r == c) ? R(1) : R(0);
-        if constexpr (CPLX) X[NP - 1][c][r] = 0;
+            vi[k] = 0;
+    }
+    if (p.info != nullptr && *p.info != 0)
+        return;
+#pragma unroll
+    for (int k = 0; k < LEAF / G; ++k) {
+        const int c = g + G * k;
+        if (c < lb) {
+            S[0][c][r] = vr[k];
+            if constexpr (CPLX) S[NP - 1][c][r] = vi[k];
+            X[0][c][r] = (r == c) ? R(1) : R(0);
+            if constexpr (CPLX) X[NP - 1][c][r] = 0;
+        }
     }
     __syncthreads();
 
@@ -180,11 +191,12 @@ __global__ void __launch_bounds__(256) leaf_kernel(const LeafArgs p)
 //   inv(L)(i, b) = -inv(L(i, i)) sum_{b<=k<i} L(i, k) inv(L)(k, b)    (MFMA,
 //                  by increasing i - b)
 //
-// The 16 x 16 diagonal blocks are done in registers by one wave: lane (r, q)
-// holds row r, columns 4q..4q+3 of the block and of its inverse; the pivot is
-// read with v_readlane and column j reaches the other lanes with shuffles.
-// Every 16 x 16 x 16 product is four v_mfma_*_16x16x4 with operands read from
-// LDS.  Padding beyond lb is the identity.
+// The 16 x 16 diagonal blocks are done in registers by one wave with no LDS
+// traffic inside the column sweep: lane c holds column c of the symmetric
+// block (which is also row c) and column c of the inverse; the entries L(r, j)
+// reach the other lanes through DPP row broadcasts.  Every
+// 16 x 16 x 16 product is four v_mfma_*_16x16x4 with operands read from LDS.
+// Padding beyond lb is the identity.
 
 // Value of x in lane `lane` of the wave (lane wave-uniform).
 __device__ __forceinline__ double lane_value(double x, int lane)
@@ -198,19 +210,19 @@ __device__ __forceinline__ float lane_value(float x, int lane)
 {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
 }
-// Value of x in lane src (per-lane source), through the LDS crossbar.
-__device__ __forceinline__ double lane_shuffle(double x, int src)
+// Value of x in lane N of this lane's row of 16 lanes (DPP row_newbcast:N).
+template <int N>
+__device__ __forceinline__ double row_value(double x)
 {
-    const uint64_t u = __builtin_bit_cast(uint64_t, x);
-    const int lo = __builtin_amdgcn_ds_bpermute(src << 2, (int)(uint32_t)u);
-    const int hi = __builtin_amdgcn_ds_bpermute(src << 2, (int)(uint32_t)(u >> 32));
-    return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+    const long long b = __builtin_amdgcn_mov_dpp(__builtin_bit_cast(long long, x), 0x150 + N, 0xf, 0xf, true);
+    return __builtin_bit_cast(double, b);
 }
-__device__ __forceinline__ float lane_shuffle(float x, int src)
+template <int N>
+__device__ __forceinline__ float row_value(float x)
 {
-    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, x)));
+    const int b = __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + N, 0xf, 0xf, true);
+    return __builtin_bit_cast(float, b);
 }
-
 // acc += A B for 16 x 16 blocks in LDS: A(r, k) = pa[k * ak + r * ar],
 // B(k, c) = pb[k * bk + c * bc].  Lane (li, lk) = (lane % 16, lane / 16) ends
 // with C(li, acc_row(lk, q)) in acc[q].
@@ -232,69 +244,126 @@ __device__ __forceinline__ typename AccT<R>::type mma16(const R *pa, int ak, int
 constexpr int LB16 = 16;         // sub-block order
 constexpr int LDL = LEAF + 1;    // LDS row length of the leaf arrays
 
-// Factor (factor = 1) and invert, or only invert, the 16 x 16 diagonal block
-// at (o, o) of S (S[c][r] = element (r, c)); L goes back to S, inv to X.  One
-// wave.  A pivot that is not > 0 records info (columns < lb only), sets
-// *failed and is replaced by 1.
-template <typename R>
-__device__ void diag16(R (*S)[LDL], R (*X)[LDL], int o, int factor, int lb, int gcol, int *info, int *failed)
+// 1/sqrt(d) for finite d > 0 (and sqrt(d) in sq), without branches.  With
+// d = f 2^e (f in [1/2, 1)) and k = floor(e / 2), m = d 4^-k lies in [1/2, 2):
+// the hardware reciprocal square root estimate of m is refined by coupled
+// Newton steps on g -> sqrt(m) and h -> 1/(2 sqrt(m)) (each step squares the
+// relative error), and the powers of two are put back exactly.  The result is
+// within a few units in the last place.
+__device__ __forceinline__ double rsqrt_refined(double d, double &sq)
 {
-    const int lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
-    R v[4], w[4];
+    const int k = __builtin_amdgcn_frexp_exp(d) >> 1;
+    const double m = __builtin_amdgcn_ldexp(d, -2 * k);
+    const double y = __builtin_amdgcn_rsq(m);
+    double g = m * y, h = 0.5 * y;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int c = 4 * q + t;
-        v[t] = (r >= c) ? S[o + c][o + r] : R(0);
-        w[t] = (r == c) ? R(1) : R(0);
+    for (int it = 0; it < 2; ++it) {
+        const double r = fma(-g, h, 0.5);
+        g = fma(g, r, g);
+        h = fma(h, r, h);
     }
-#pragma unroll
-    for (int j = 0; j < LB16; ++j) {
-        const int qo = j >> 2, t = j & 3;
-        const R d = lane_value(v[t], qo * 16 + j);
-        R ljj = d;
-        if (factor) {
-            if (!(d > R(0))) {
-                if (lane == 0 && o + j < lb) {
-                    atomicCAS(info, 0, gcol + o + j + 1);
-                    *failed = 1;
-                }
-                ljj = R(1);
-            } else {
-                ljj = sqrt(d);
-            }
-        }
-        const R rinv = R(1) / ljj;
-        if (factor && q == qo)
-            v[t] = (r > j) ? v[t] * rinv : ((r == j) ? ljj : v[t]);
-        const R lrj = lane_shuffle(v[t], qo * 16 + r);  // L(r, j)
-        if (factor) {
-#pragma unroll
-            for (int t2 = 0; t2 < 4; ++t2) {
-                const int c = 4 * q + t2;
-                const R lcj = lane_shuffle(v[t], qo * 16 + c);  // L(c, j)
-                if (c > j && r >= c)
-                    v[t2] -= lrj * lcj;
-            }
-        }
-#pragma unroll
-        for (int t2 = 0; t2 < 4; ++t2) {
-            const int c = 4 * q + t2;
-            const R xjc = lane_shuffle(w[t2], q * 16 + j) * rinv;  // final X(j, c)
-            if (c <= j)
-                w[t2] = (r == j) ? xjc : ((r > j) ? w[t2] - lrj * xjc : w[t2]);
-        }
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int c = 4 * q + t;
-        if (factor)
-            S[o + c][o + r] = (r >= c) ? v[t] : R(0);
-        X[o + c][o + r] = (r >= c) ? w[t] : R(0);
+    sq = __builtin_amdgcn_ldexp(g, k);
+    return __builtin_amdgcn_ldexp(h + h, -k);
+}
+__device__ __forceinline__ float rsqrt_refined(float d, float &sq)
+{
+    const int k = __builtin_amdgcn_frexp_expf(d) >> 1;
+    const float m = __builtin_amdgcn_ldexpf(d, -2 * k);
+    const float y = __builtin_amdgcn_rsqf(m);
+    float g = m * y, h = 0.5f * y;
+    const float r = fmaf(-g, h, 0.5f);
+    g = fmaf(g, r, g);
+    h = fmaf(h, r, h);
+    sq = __builtin_amdgcn_ldexpf(g, k);
+    return __builtin_amdgcn_ldexpf(h + h, -k);
+}
+
+// Row updates of column J of the sweep below: A(r, c) -= L(r, J) L(c, J) and
+// x(r) -= L(r, J) x(J) for r = R0 .. 15.
+template <typename R, bool FACTOR, int J, int R0>
+__device__ __forceinline__ void diag16_rows(R *a, R *x)
+{
+    if constexpr (R0 < LB16) {
+        const R lrj = row_value<R0>(a[J]);  // L(R0, J), from lane R0
+        if constexpr (FACTOR)
+            a[R0] -= lrj * a[J];
+        x[R0] -= lrj * x[J];
+        diag16_rows<R, FACTOR, J, R0 + 1>(a, x);
     }
 }
 
+// Column J of the sweep below, then the columns after it.  A pivot that is
+// not > 0 (NaN included) is replaced by 1 and the first such column kept in
+// bad; every lane sees the same pivot, so nothing diverges.
+template <typename R, bool FACTOR, int J>
+__device__ __forceinline__ void diag16_step(R *a, R *x, int c, int &bad)
+{
+    if constexpr (J < LB16) {
+        R d = row_value<J>(a[J]);
+        R s;
+        if constexpr (FACTOR) {
+            const bool ok = d > R(0);
+            bad = (!ok && bad < 0) ? J : bad;
+            d = ok ? d : R(1);
+            R ljj;
+            s = rsqrt_refined(d, ljj);
+            a[J] = (c == J) ? ljj : a[J] * s;
+        } else {
+            s = R(1) / d;
+        }
+        x[J] *= s;
+        diag16_rows<R, FACTOR, J, J + 1>(a, x);
+        // Pin the column's results here: left alone, the compiler moves the
+        // updates of x past the later columns and keeps all of their
+        // broadcasts live at once.
+#pragma unroll
+        for (int r = J; r < LB16; ++r)
+            asm volatile("" : "+v"(a[r]), "+v"(x[r]));
+        diag16_step<R, FACTOR, J + 1>(a, x, c, bad);
+    }
+}
+
+// Factor (FACTOR) and invert, or only invert, the 16 x 16 diagonal block at
+// (o, o) of S (S[c][r] = element (r, c), lower triangle); L goes back to S
+// (zeros above the diagonal), inv(L) to X.  One wave; lanes 16..63 repeat
+// the work of lanes 0..15 and store nothing.  A pivot that is not > 0 records
+// info (columns < lb only), sets *failed and is replaced by 1.
+//
+// Lane c keeps a[r] = A(r, c) = A(c, r) for all r.  Step j: the pivot is lane
+// j's a[j]; every lane scales its a[j] by 1/L(j, j), which leaves L(c, j) in
+// lane c; then A(r, c) -= L(r, j) L(c, j) for r > j with L(r, j) read from
+// lane r.  The inverse is the forward substitution L x = e_c in lane c, which
+// needs the same L(r, j) at the same step.
+template <typename R, bool FACTOR>
+__device__ void diag16(R (*S)[LDL], R (*X)[LDL], int o, int lb, int gcol, int *info, int *failed)
+{
+    const int lane = threadIdx.x & 63, c = lane & 15;
+    R a[LB16], x[LB16];
+#pragma unroll
+    for (int r = 0; r < LB16; ++r) {
+        a[r] = (r >= c) ? S[o + c][o + r] : S[o + r][o + c];
+        x[r] = (r == c) ? R(1) : R(0);
+    }
+    int bad = -1;
+    diag16_step<R, FACTOR, 0>(a, x, c, bad);
+    if (FACTOR && bad >= 0 && lane == 0 && o + bad < lb) {
+        atomicCAS(info, 0, gcol + o + bad + 1);
+        *failed = 1;
+    }
+    if (lane < LB16) {
+#pragma unroll
+        for (int r = 0; r < LB16; ++r) {
+            if constexpr (FACTOR)
+                S[o + r][o + c] = (r <= c) ? a[r] : R(0);  // row c of L
+            X[o + c][o + r] = (r >= c) ? x[r] : R(0);      // column c of inv(L)
+        }
+    }
+}
+
+// At most 256 registers per lane, so that a leaf fits in the registers one
+// finishing trailing-update workgroup gives back.
 template <typename R>
-__global__ void __launch_bounds__(256) leaf16_kernel(const LeafArgs p)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) leaf16_kernel(const LeafArgs p)
 {
     typedef typename AccT<R>::type V4;
     constexpr int NB = LEAF / LB16;  // 4 sub-blocks
@@ -303,8 +372,6 @@ __global__ void __launch_bounds__(256) leaf16_kernel(const LeafArgs p)
     __shared__ R Tm[4][LB16][LB16 + 1];  // per-wave 16 x 16 scratch
     __shared__ int failed;
 
-    if (p.info != nullptr && *p.info != 0)
-        return;
     int64_t c0, ioff;
     int lb;
     if (!leaf_geom(p, (int)blockIdx.x, c0, lb, ioff))
@@ -315,12 +382,22 @@ __global__ void __launch_bounds__(256) leaf16_kernel(const LeafArgs p)
     const int li = lane & 15, lk = lane >> 4;
     const int r = tid & (LEAF - 1), g = tid / LEAF;
 
-    for (int c = g; c < LEAF; c += 4) {
-        R v = (r == c) ? R(1) : R(0);
+    // all loads of the leaf are in flight together (one memory round trip),
+    // and the status word is read alongside them
+    R v[LEAF / 4];
+#pragma unroll
+    for (int k = 0; k < LEAF / 4; ++k) {
+        const int c = g + 4 * k;
+        v[k] = (r == c) ? R(1) : R(0);
         if (r < lb && c < lb && r >= c)
-            v = A[r + (int64_t)c * p.lda];
-        S[c][r] = v;
-        X[c][r] = R(0);
+            v[k] = A[r + (int64_t)c * p.lda];
+    }
+    if (p.info != nullptr && *p.info != 0)
+        return;
+#pragma unroll
+    for (int k = 0; k < LEAF / 4; ++k) {
+        S[g + 4 * k][r] = v[k];
+        X[g + 4 * k][r] = R(0);
     }
     if (tid == 0)
         failed = 0;
@@ -339,8 +416,12 @@ __global__ void __launch_bounds__(256) leaf16_kernel(const LeafArgs p)
 
     for (int b = 0; b < NB; ++b) {
         const int o = b * LB16;
-        if (wave == 0)
-            diag16<R>(S, X, o, p.factor, lb, p.col0 + (int)c0, p.info, &failed);
+        if (wave == 0) {
+            if (p.factor)
+                diag16<R, true>(S, X, o, lb, p.col0 + (int)c0, p.info, &failed);
+            else
+                diag16<R, false>(S, X, o, lb, p.col0 + (int)c0, p.info, &failed);
+        }
         __syncthreads();
         if (p.factor) {
             // L(i, b) = A(i, b) inv(L(b, b))^T, one block per wave

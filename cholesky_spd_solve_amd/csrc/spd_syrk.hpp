@@ -104,9 +104,6 @@ syrk_kernel(const SyrkArgs p)
     __shared__ R As[2][NP][KB][BM];  // As[.][.][k][r] = W(i0 + r, k0 + k)
     __shared__ R Bs[2][NP][KB][BM];  // Bs[.][.][k][r] = conj(W(j0 + r, k0 + k))
 
-    if (p.info != nullptr && *p.info != 0)
-        return;
-
     int I, J;
     syrk_tile(p, (int)blockIdx.x, I, J);
     const int i0 = I * BM, j0 = J * BM;
@@ -185,6 +182,10 @@ syrk_kernel(const SyrkArgs p)
                 acc[c][fi][fj] = V4{0, 0, 0, 0};
 
     load(wa, wb);
+    // status word read alongside the first slice (the panel is valid whatever
+    // it holds; nothing is written before it)
+    if (p.info != nullptr && *p.info != 0)
+        return;
     store(0);
     __syncthreads();
     int cur = 0;
