@@ -278,48 +278,74 @@ __device__ __forceinline__ float rsqrt_refined(float d, float &sq)
     return __builtin_amdgcn_ldexpf(h + h, -k);
 }
 
-// Row updates of column J of the sweep below: A(r, c) -= L(r, J) L(c, J) and
-// x(r) -= L(r, J) x(J) for r = R0 .. 15.
-template <typename R, bool FACTOR, int J, int R0>
-__device__ __forceinline__ void diag16_rows(R *a, R *x)
+// b[r] = L(r, J) for r = R0 .. 15, each from lane r's a[J].
+template <typename R, int J, int R0>
+__device__ __forceinline__ void diag16_bcast(const R *a, R *b)
 {
     if constexpr (R0 < LB16) {
-        const R lrj = row_value<R0>(a[J]);  // L(R0, J), from lane R0
-        if constexpr (FACTOR)
-            a[R0] -= lrj * a[J];
-        x[R0] -= lrj * x[J];
-        diag16_rows<R, FACTOR, J, R0 + 1>(a, x);
+        b[R0] = row_value<R0>(a[J]);
+        diag16_bcast<R, J, R0 + 1>(a, b);
     }
 }
 
-// Column J of the sweep below, then the columns after it.  A pivot that is
-// not > 0 (NaN included) is replaced by 1 and the first such column kept in
-// bad; every lane sees the same pivot, so nothing diverges.
+// Scale of pivot column J: s = 1/L(J, J) and ljj = L(J, J) from the pivot
+// lane J's a[J].  A pivot that is not > 0 (NaN included) is replaced by 1 and
+// the first such column kept in bad; every lane sees the same pivot, so
+// nothing diverges.
 template <typename R, bool FACTOR, int J>
-__device__ __forceinline__ void diag16_step(R *a, R *x, int c, int &bad)
+__device__ __forceinline__ void diag16_pivot(const R *a, R &s, R &ljj, int &bad)
+{
+    R d = row_value<J>(a[J]);
+    if constexpr (FACTOR) {
+        const bool ok = d > R(0);
+        bad = (!ok && bad < 0) ? J : bad;
+        d = ok ? d : R(1);
+        s = rsqrt_refined(d, ljj);
+    } else {
+        ljj = d;
+        s = R(1) / d;
+    }
+}
+
+// Column J of the sweep below (its pivot scale s, ljj already known), then
+// the columns after it.  The next pivot is computed right after row J + 1 is
+// updated, ahead of the other rows, so its dependent chain overlaps them.
+template <typename R, bool FACTOR, int J>
+__device__ __forceinline__ void diag16_step(R *a, R *x, int c, R s, R ljj, int &bad)
 {
     if constexpr (J < LB16) {
-        R d = row_value<J>(a[J]);
-        R s;
-        if constexpr (FACTOR) {
-            const bool ok = d > R(0);
-            bad = (!ok && bad < 0) ? J : bad;
-            d = ok ? d : R(1);
-            R ljj;
-            s = rsqrt_refined(d, ljj);
+        if constexpr (FACTOR)
             a[J] = (c == J) ? ljj : a[J] * s;
-        } else {
-            s = R(1) / d;
-        }
         x[J] *= s;
-        diag16_rows<R, FACTOR, J, J + 1>(a, x);
-        // Pin the column's results here: left alone, the compiler moves the
-        // updates of x past the later columns and keeps all of their
-        // broadcasts live at once.
+        R s1 = R(0), l1 = R(0);
+        if constexpr (J + 1 < LB16) {
+            const R lrj = row_value<J + 1>(a[J]);  // L(J + 1, J)
+            if constexpr (FACTOR)
+                a[J + 1] -= lrj * a[J];
+            x[J + 1] -= lrj * x[J];
+            diag16_pivot<R, FACTOR, J + 1>(a, s1, l1, bad);
+        }
+        // The broadcasts of the column all go out first (into registers of
+        // their own, pinned so the compiler cannot fold them back onto one),
+        // so no update waits on the broadcast just before it.
+        R b[LB16];
+        diag16_bcast<R, J, J + 2>(a, b);
 #pragma unroll
-        for (int r = J; r < LB16; ++r)
+        for (int r = J + 2; r < LB16; ++r)
+            asm volatile("" : "+v"(b[r]));
+#pragma unroll
+        for (int r = J + 2; r < LB16; ++r) {
+            if constexpr (FACTOR)
+                a[r] -= b[r] * a[J];
+            x[r] -= b[r] * x[J];
+        }
+        // Pin the column's results for the rows past the next pivot here:
+        // left alone, the compiler moves the updates of x past the later
+        // columns and keeps all of their broadcasts live at once.
+#pragma unroll
+        for (int r = J + 2; r < LB16; ++r)
             asm volatile("" : "+v"(a[r]), "+v"(x[r]));
-        diag16_step<R, FACTOR, J + 1>(a, x, c, bad);
+        diag16_step<R, FACTOR, J + 1>(a, x, c, s1, l1, bad);
     }
 }
 
@@ -345,7 +371,9 @@ __device__ void diag16(R (*S)[LDL], R (*X)[LDL], int o, int lb, int gcol, int *i
         x[r] = (r == c) ? R(1) : R(0);
     }
     int bad = -1;
-    diag16_step<R, FACTOR, 0>(a, x, c, bad);
+    R s0, l0;
+    diag16_pivot<R, FACTOR, 0>(a, s0, l0, bad);
+    diag16_step<R, FACTOR, 0>(a, x, c, s0, l0, bad);
     if (FACTOR && bad >= 0 && lane == 0 && o + bad < lb) {
         atomicCAS(info, 0, gcol + o + bad + 1);
         *failed = 1;
@@ -471,12 +499,21 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) l
 
     if (failed)
         return;
-    for (int c = g; c < lb; c += 4) {
-        if (r >= lb)
-            continue;
-        if (p.factor && r >= c)
-            A[r + (int64_t)c * p.lda] = S[c][r];
-        Inv[r + (int64_t)c * p.ldi] = (r >= c) ? X[c][r] : R(0);
+    // every LDS read first, then the global stores back to back
+    R sv[LEAF / 4], xv[LEAF / 4];
+#pragma unroll
+    for (int k = 0; k < LEAF / 4; ++k) {
+        sv[k] = S[g + 4 * k][r];
+        xv[k] = X[g + 4 * k][r];
+    }
+#pragma unroll
+    for (int k = 0; k < LEAF / 4; ++k) {
+        const int c = g + 4 * k;
+        if (r < lb && c < lb) {
+            if (p.factor && r >= c)
+                A[r + (int64_t)c * p.lda] = sv[k];
+            Inv[r + (int64_t)c * p.ldi] = (r >= c) ? xv[k] : R(0);
+        }
     }
 }
 
