@@ -27,6 +27,7 @@
 #include "spd.h"
 #include "spd_gemm.hpp"
 #include "spd_kernels.hpp"
+#include "spd_rect.hpp"
 #include "spd_syrk.hpp"
 #include "spd_check.hpp"
 
@@ -268,7 +269,7 @@ static int set_info(int *info, hipStream_t s)
 //                 L21 of two consecutive steps (potrf) / merge temporaries (both)
 //            TMP  max(T*T, T*n_rhs)   one block row of the right-hand side
 struct Layout {
-    int64_t T, nt, inv, w, wsz, tmp, total;  // offsets / sizes in elements
+    int64_t T, nt, inv, w, wsz, tmp, q, ldq, kq, qsz, gf, gb, part, total;  // offsets / sizes in elements
 };
 
 // The trailing-update panel W is stored with its leading dimension rounded up
@@ -276,6 +277,13 @@ struct Layout {
 // trailing-update kernel reads whole tiles and slices only.
 constexpr int64_t SYRK_LDW = 128;  // multiple of every trailing-update tile size
 constexpr int64_t SYRK_KP = 32;    // multiple of every trailing-update slice depth
+// The substitutions' block update reads the solved block transposed from a
+// buffer with RECT_LDQ-aligned rows and RECT_KB-aligned columns, zero padded.
+constexpr int64_t RECT_LDQ = 128;  // multiple of every block-update tile width
+constexpr int64_t RECT_KB = 32;    // multiple of every block-update slice depth
+// The chain product of the substitutions is split into this many partial
+// products (two operand pairs, each split along its depth).
+constexpr int64_t CHAIN_SPLITS = 8;
 
 static Layout make_layout(int64_t n, int64_t n_rhs, int64_t T_A, int64_t esize)
 {
@@ -287,7 +295,22 @@ static Layout make_layout(int64_t n, int64_t n_rhs, int64_t T_A, int64_t esize)
     L.w = align_up(L.nt * L.T * L.T, al);
     L.wsz = align_up(align_up(n, SYRK_LDW) * align_up(L.T, SYRK_KP), al);
     L.tmp = L.w + 2 * L.wsz;  // two panel buffers: step k's and step k+1's
-    L.total = L.tmp + align_up(std::max(L.T * L.T, L.T * std::max<int64_t>(n_rhs, 1)), al);
+    L.q = L.tmp + align_up(std::max(L.T * L.T, L.T * std::max<int64_t>(n_rhs, 1)), al);
+    L.ldq = align_up(n_rhs, RECT_LDQ);
+    L.kq = align_up(L.T, RECT_KB);
+    L.qsz = L.ldq * L.kq;  // two buffers, adjacent
+    if (n_rhs > 0) {
+        // the substitutions' chain products: -inv(L_k+1,k+1) L_k+1,k and
+        // -L_k,k-1 inv(L_k-1,k-1) per block, and the partial sums of the
+        // split products
+        L.gf = L.q + align_up(2 * L.qsz, al);
+        L.gb = L.gf + align_up(L.nt * L.T * L.T, al);
+        L.part = L.gb + align_up(L.nt * L.T * L.T, al);
+        L.total = L.part + align_up(CHAIN_SPLITS * L.T * n_rhs, al);
+    } else {
+        L.gf = L.gb = L.part = L.q;
+        L.total = L.q;
+    }
     return L;
 }
 
@@ -552,6 +575,88 @@ struct Solver {
             return syrk_cfg<128, 8, 2, 4>(m, W, ldw, kp, C, ldc, jt_end, info, s);
     }
 
+    template <int BM, int BN, int KB, int WM, int WN, bool PT, bool VEC>
+    static int rect_cfg(const E *P, int64_t ldp, const E *Q, int64_t ldq, E *C, int64_t ldc, int64_t m,
+                        int64_t n, int64_t kp, int64_t kvalid, const int *info, hipStream_t s)
+    {
+        static_assert(RECT_LDQ % BN == 0 && RECT_KB % KB == 0, "operand buffer padding too small for the tile");
+        RectArgs a;
+        a.P = P;
+        a.ldp = ldp;
+        a.Q = Q;
+        a.ldq = ldq;
+        a.C = C;
+        a.ldc = ldc;
+        a.m = (int)m;
+        a.n = (int)n;
+        a.kp = (int)kp;
+        a.kvalid = (int)kvalid;
+        a.tiles_m = (int)cdiv(m, BM);
+        a.ntiles = a.tiles_m * (int)cdiv(n, BN);
+        a.info = info;
+        const dim3 grid((unsigned)a.ntiles), block(64 * WM * WN);
+        SPD_VALIDATE((check_rect<R, BM, BN, KB, WM, WN, PT, VEC>(a, grid, g_chk)));
+        rect_kernel<R, BM, BN, KB, WM, WN, PT, VEC><<<grid, block, 0, s>>>(a);
+        SPD_CHECK_LAUNCH("rect_kernel");
+        return 0;
+    }
+
+    // C(m x n) -= P Q^T for the substitutions (see spd_rect.hpp); Q is the
+    // solved block transposed into the ldq x kp operand buffer.
+    template <bool PT>
+    static int rect(const E *P, int64_t ldp, const E *Q, int64_t ldq, E *C, int64_t ldc, int64_t m, int64_t n,
+                    int64_t kp, int64_t kvalid, bool vec, const int *info, hipStream_t s)
+    {
+        if (m <= 0 || n <= 0)
+            return 0;
+        if constexpr (CPLX) {
+            g_last_error = "block update kernel is for real types";
+            return SPD_ERR_HIP;
+        } else {
+            // tile rows by update height: 64 while that still gives about two
+            // workgroups per CU, else 32 (one workgroup's 512-deep product is
+            // a fixed latency, so more, smaller tiles finish sooner)
+            constexpr int KBL = sizeof(R) == 8 ? 16 : 32;  // slice depth of the 64-row tiles
+            const bool big = m >= 16384;
+            if (n > 64) {
+                if (big)
+                    return vec ? rect_cfg<64, 128, KBL, 2, 4, PT, true>(P, ldp, Q, ldq, C, ldc, m, n, kp, kvalid, info, s)
+                               : rect_cfg<64, 128, KBL, 2, 4, PT, false>(P, ldp, Q, ldq, C, ldc, m, n, kp, kvalid, info, s);
+                return vec ? rect_cfg<32, 128, 32, 1, 4, PT, true>(P, ldp, Q, ldq, C, ldc, m, n, kp, kvalid, info, s)
+                           : rect_cfg<32, 128, 32, 1, 4, PT, false>(P, ldp, Q, ldq, C, ldc, m, n, kp, kvalid, info, s);
+            }
+            if (big)
+                return vec ? rect_cfg<64, 64, KBL, 2, 2, PT, true>(P, ldp, Q, ldq, C, ldc, m, n, kp, kvalid, info, s)
+                           : rect_cfg<64, 64, KBL, 2, 2, PT, false>(P, ldp, Q, ldq, C, ldc, m, n, kp, kvalid, info, s);
+            return vec ? rect_cfg<32, 64, 32, 1, 2, PT, true>(P, ldp, Q, ldq, C, ldc, m, n, kp, kvalid, info, s)
+                       : rect_cfg<32, 64, 32, 1, 2, PT, false>(P, ldp, Q, ldq, C, ldc, m, n, kp, kvalid, info, s);
+        }
+    }
+
+    // The block update kernel addresses P with 32-bit offsets inside a tile
+    // (64 columns of A must span fewer than 2^31 elements).  It reads P with
+    // 16-byte vectors when A is 16-byte aligned and the leading dimension and
+    // the block offsets (multiples of T) keep every vector aligned; otherwise
+    // element by element, with the same arithmetic.
+    static bool rect_usable(int64_t lda) { return !CPLX && lda < (INT64_C(1) << 24); }
+    static bool rect_vec(const E *A, int64_t lda, int64_t T)
+    {
+        const int64_t V = 16 / (int64_t)sizeof(E);
+        return ((uintptr_t)A % 16 == 0) && (lda % V == 0) && (T % V == 0);
+    }
+
+    static int copy_t(E *dst, int64_t ldd, E *qt, int64_t ldq, const E *src, int64_t lds, int64_t m, int64_t n,
+                      int64_t kp, const int *info, hipStream_t s)
+    {
+        if (kp <= 0 || n <= 0)
+            return 0;
+        SPD_VALIDATE((check_copy_t<E>(dst, ldd, qt, ldq, src, lds, m, n, kp, info, g_chk)));
+        const int64_t blocks = std::min<int64_t>(cdiv(kp * n, 256), 4096);
+        copy_t_kernel<E><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(dst, ldd, qt, ldq, src, lds, m, n, kp, info);
+        SPD_CHECK_LAUNCH("copy_t_kernel");
+        return 0;
+    }
+
     // Diagonal tile at (c0, c0) of order tk = min(T, n - c0): factor it in
     // place and build inv(L_kk) in Inv (ld T); then, if rows remain below it,
     // solve the panel into Wk with the zero-padded layout the trailing update
@@ -685,99 +790,290 @@ struct Solver {
         return 0;
     }
 
+    // Y_k (or X_k) = inv(L_kk) B_k (TRANS: inv(L_kk)^H B_k) into Tmp (ld T)
+    static int apply_inv(const E *Inv, int64_t k, int64_t T, E *B, int64_t ldb, int64_t c0, int64_t tk, int64_t nrhs,
+                         E *Tmp, bool trans, const int *info, hipStream_t s)
+    {
+        Gemm g;
+        g.A = Inv + k * T * T;
+        g.lda = T;
+        g.B = B + c0;
+        g.ldb = ldb;
+        g.C = Tmp;
+        g.ldc = T;
+        g.m = tk;
+        g.n = nrhs;
+        g.k = tk;
+        g.kmode = trans ? KM_BEG_BY_I : KM_END_BY_I;
+        g.info = info;
+        return trans ? gemm<R, CPLX>(TN, g, s) : gemm<R, CPLX>(NN, g, s);
+    }
+
+    // inverses of every diagonal tile, for the block substitutions
+    static int all_inverses(int64_t n, const E *A, int64_t lda, int64_t T, int64_t nt, E *Inv, E *W, const int *info,
+                            hipStream_t s)
+    {
+        SPD_TRY(zero2d<E>(Inv, T, T, nt * T, s));
+        SPD_TRY(leaves(const_cast<E *>(A), lda, n, T, Inv, T, T * T, nt, false, const_cast<int *>(info), 0, s));
+        const int64_t nfull = (n % T == 0) ? nt : nt - 1;
+        if (nfull > 0)
+            SPD_TRY(merge_inverses(A, lda, T * (1 + lda), Inv, T, T * T, nfull, T, W, info, s));
+        if (nfull < nt) {
+            const int64_t c0 = nfull * T;
+            SPD_TRY(merge_inverses(A + c0 + c0 * lda, lda, 0, Inv + nfull * T * T, T, 0, 1, n - c0, W, info, s));
+        }
+        return 0;
+    }
+
     static int potrs(int64_t n, int64_t nrhs, const E *A, int64_t lda, E *B, int64_t ldb, int64_t T_A,
                      const int *info, void *work, hipStream_t s)
     {
         if (n == 0 || nrhs == 0)
             return 0;
         const Layout L = make_layout(n, nrhs, T_A, sizeof(E));
-        const int64_t T = L.T, nt = L.nt;
-        E *Inv = (E *)work + L.inv;
-        E *W = (E *)work + L.w;
-        E *Tmp = (E *)work + L.tmp;  // T x nrhs, ld T
         {
             ProfScope ps(PROF_SOLVE, FMUL * 2.0 * (double)n * n * nrhs, s);
-            // inverses of every diagonal tile
-            SPD_TRY(zero2d<E>(Inv, T, T, nt * T, s));
-            SPD_TRY(leaves(const_cast<E *>(A), lda, n, T, Inv, T, T * T, nt, false, const_cast<int *>(info), 0, s));
-            const int64_t nfull = (n % T == 0) ? nt : nt - 1;
-            if (nfull > 0)
-                SPD_TRY(merge_inverses(A, lda, T * (1 + lda), Inv, T, T * T, nfull, T, W, info, s));
-            if (nfull < nt) {
-                const int64_t c0 = nfull * T;
-                SPD_TRY(merge_inverses(A + c0 + c0 * lda, lda, 0, Inv + nfull * T * T, T, 0, 1, n - c0, W, info,
-                                       s));
-            }
-            // forward: L Y = B
-            for (int64_t k = 0; k < nt; ++k) {
-                const int64_t c0 = k * T, tk = std::min(T, n - c0), m = n - c0 - tk;
-                Gemm g;  // Tmp = inv(L_kk) B_k
-                g.A = Inv + k * T * T;
-                g.lda = T;
-                g.B = B + c0;
-                g.ldb = ldb;
-                g.C = Tmp;
-                g.ldc = T;
-                g.m = tk;
-                g.n = nrhs;
-                g.k = tk;
-                g.kmode = KM_END_BY_I;
-                g.info = info;
-                SPD_TRY((gemm<R, CPLX>(NN, g, s)));
-                SPD_TRY(copy2d<E>(B + c0, ldb, Tmp, T, tk, nrhs, info, s));
-                if (m > 0) {
-                    Gemm u;  // B_below -= L_panel Y_k
-                    u.A = A + (c0 + tk) + c0 * lda;
-                    u.lda = lda;
-                    u.B = Tmp;
-                    u.ldb = T;
-                    u.C = B + c0 + tk;
-                    u.ldc = ldb;
-                    u.m = m;
-                    u.n = nrhs;
-                    u.k = tk;
-                    u.neg = true;
-                    u.beta = true;
-                    u.info = info;
-                    SPD_TRY((gemm<R, CPLX>(NN, u, s)));
-                }
-            }
-            // backward: L^H X = Y
-            for (int64_t k = nt - 1; k >= 0; --k) {
-                const int64_t c0 = k * T, tk = std::min(T, n - c0);
-                Gemm g;  // Tmp = inv(L_kk)^H Y_k
-                g.A = Inv + k * T * T;
-                g.lda = T;
-                g.B = B + c0;
-                g.ldb = ldb;
-                g.C = Tmp;
-                g.ldc = T;
-                g.m = tk;
-                g.n = nrhs;
-                g.k = tk;
-                g.kmode = KM_BEG_BY_I;
-                g.info = info;
-                SPD_TRY((gemm<R, CPLX>(TN, g, s)));
-                SPD_TRY(copy2d<E>(B + c0, ldb, Tmp, T, tk, nrhs, info, s));
-                if (c0 > 0) {
-                    Gemm u;  // Y_top -= L_k,0:k^H X_k
-                    u.A = A + c0;
-                    u.lda = lda;
-                    u.B = Tmp;
-                    u.ldb = T;
-                    u.C = B;
-                    u.ldc = ldb;
-                    u.m = c0;
-                    u.n = nrhs;
-                    u.k = tk;
-                    u.neg = true;
-                    u.beta = true;
-                    u.info = info;
-                    SPD_TRY((gemm<R, CPLX>(TN, u, s)));
-                }
-            }
+            if (rect_usable(lda))
+                SPD_TRY(potrs_blocks(n, nrhs, A, lda, B, ldb, L, info, work, s));
+            else
+                SPD_TRY(potrs_general(n, nrhs, A, lda, B, ldb, L, info, work, s));
         }
         return nan_fill(n, nrhs, B, ldb, info, s);
+    }
+
+    // Block substitutions on the general product kernel (complex types, and
+    // leading dimensions beyond the block-update kernel's 32-bit offsets).
+    static int potrs_general(int64_t n, int64_t nrhs, const E *A, int64_t lda, E *B, int64_t ldb, const Layout &L,
+                             const int *info, void *work, hipStream_t s)
+    {
+        const int64_t T = L.T, nt = L.nt;
+        E *Inv = (E *)work + L.inv;
+        E *Tmp = (E *)work + L.tmp;  // T x nrhs, ld T
+        SPD_TRY(all_inverses(n, A, lda, T, nt, Inv, (E *)work + L.w, info, s));
+        // forward: L Y = B
+        for (int64_t k = 0; k < nt; ++k) {
+            const int64_t c0 = k * T, tk = std::min(T, n - c0), m = n - c0 - tk;
+            SPD_TRY(apply_inv(Inv, k, T, B, ldb, c0, tk, nrhs, Tmp, false, info, s));
+            SPD_TRY(copy2d<E>(B + c0, ldb, Tmp, T, tk, nrhs, info, s));
+            if (m > 0) {
+                Gemm u;  // B_below -= L_panel Y_k
+                u.A = A + (c0 + tk) + c0 * lda;
+                u.lda = lda;
+                u.B = Tmp;
+                u.ldb = T;
+                u.C = B + c0 + tk;
+                u.ldc = ldb;
+                u.m = m;
+                u.n = nrhs;
+                u.k = tk;
+                u.neg = true;
+                u.beta = true;
+                u.info = info;
+                SPD_TRY((gemm<R, CPLX>(NN, u, s)));
+            }
+        }
+        // backward: L^H X = Y
+        for (int64_t k = nt - 1; k >= 0; --k) {
+            const int64_t c0 = k * T, tk = std::min(T, n - c0);
+            SPD_TRY(apply_inv(Inv, k, T, B, ldb, c0, tk, nrhs, Tmp, true, info, s));
+            SPD_TRY(copy2d<E>(B + c0, ldb, Tmp, T, tk, nrhs, info, s));
+            if (c0 > 0) {
+                Gemm u;  // Y_top -= L_k,0:k^H X_k
+                u.A = A + c0;
+                u.lda = lda;
+                u.B = Tmp;
+                u.ldb = T;
+                u.C = B;
+                u.ldc = ldb;
+                u.m = c0;
+                u.n = nrhs;
+                u.k = tk;
+                u.neg = true;
+                u.beta = true;
+                u.info = info;
+                SPD_TRY((gemm<R, CPLX>(TN, u, s)));
+            }
+        }
+        return 0;
+    }
+
+    // Block substitutions on the block-update kernel (real types), one block
+    // ahead on the auxiliary stream when there are at least three blocks:
+    //
+    //   chain (auxiliary stream): update the next block's rows with the block
+    //     just solved, solve the next block (inverse product), write it back
+    //     into B and, transposed, into one of two operand buffers;
+    //   caller's stream: update every row beyond the next block with the block
+    //     just solved.
+    //
+    // Events: the caller's stream waits for the operand buffer of block k
+    // before its update; the chain waits for the caller's update of step k-1
+    // before it touches the next block's rows (which that update wrote) and
+    // before it overwrites the operand buffer that update read.  The back
+    // substitution runs the same way from the last block up.
+    static int potrs_blocks(int64_t n, int64_t nrhs, const E *A, int64_t lda, E *B, int64_t ldb, const Layout &L,
+                            const int *info, void *work, hipStream_t s)
+    {
+        const int64_t T = L.T, nt = L.nt;
+        E *Inv = (E *)work + L.inv;
+        E *Tmp = (E *)work + L.tmp;
+        E *Qb[2] = {(E *)work + L.q, (E *)work + L.q + L.qsz};
+        E *GF = (E *)work + L.gf, *GB = (E *)work + L.gb, *Part = (E *)work + L.part;
+        const bool vec = rect_vec(A, lda, T);
+        SPD_TRY(all_inverses(n, A, lda, T, nt, Inv, (E *)work + L.w, info, s));
+        SPD_TRY(zero2d<E>(Qb[0], L.ldq, L.ldq, 2 * L.kq, s));  // both buffers (adjacent, same ld)
+        const int64_t nfull = n / T;  // whole blocks
+        // split chain: depth split of each operand pair, sh parts of ks
+        const int64_t sh = (T % 4 == 0 && T >= 64) ? 4 : (T % 2 == 0 && T >= 32) ? 2 : 1, ks = T / sh;
+        const bool split = nfull >= 2;
+        if (split) {
+            // GF_k = -inv(L_k+1,k+1) L_k+1,k for whole blocks k+1 (k = 0 .. nfull-2)
+            Gemm g;
+            g.A = Inv + T * T;
+            g.lda = T;
+            g.sA_out = T * T;
+            g.B = A + T;
+            g.ldb = lda;
+            g.sB_out = T * (1 + lda);
+            g.C = GF;
+            g.ldc = T;
+            g.sC_out = T * T;
+            g.batch = (int)(nfull - 1);
+            g.m = g.n = g.k = T;
+            g.kmode = KM_END_BY_I;
+            g.neg = true;
+            g.info = info;
+            SPD_TRY((gemm<R, CPLX>(NN, g, s)));
+            // GB_k = -L_k,k-1 inv(L_k-1,k-1) for whole blocks k (k = 1 .. nfull-1)
+            Gemm h;
+            h.A = A + T;
+            h.lda = lda;
+            h.sA_out = T * (1 + lda);
+            h.B = Inv;
+            h.ldb = T;
+            h.sB_out = T * T;
+            h.C = GB + T * T;
+            h.ldc = T;
+            h.sC_out = T * T;
+            h.batch = (int)(nfull - 1);
+            h.m = h.n = h.k = T;
+            h.kmode = KM_BEG_BY_J;
+            h.neg = true;
+            h.info = info;
+            SPD_TRY((gemm<R, CPLX>(NN, h, s)));
+        }
+        // Next block (index kn, rows [cn, cn + T)) in one split product:
+        //   forward:  Y_kn = GF_k Y_k + inv(L_kn,kn) B_kn          (kn = k + 1)
+        //   backward: X_kn = inv(L_kn,kn)^T B_kn + GB_k^T X_k      (kn = k - 1)
+        // as 2*sh partial products of depth ks, then their fixed-order sum,
+        // written back into B and, transposed, into operand buffer q.
+        auto chain = [&](int64_t k, int64_t kn, bool back, int q, hipStream_t st) -> int {
+            const int64_t c0 = k * T, cn = kn * T;
+            Gemm g;
+            const E *A0 = back ? Inv + kn * T * T : GF + k * T * T;  // pairs with B rows c0 (fwd) / cn (bwd)
+            const E *A1 = back ? GB + k * T * T : Inv + kn * T * T;
+            g.A = A0;
+            g.lda = T;
+            g.sA_out = (int64_t)(A1 - A0);
+            g.sA_in = back ? ks : ks * T;
+            g.B = B + std::min(c0, cn);
+            g.ldb = ldb;
+            g.sB_out = T;
+            g.sB_in = ks;
+            g.C = Part;
+            g.ldc = T;
+            g.sC_out = sh * T * nrhs;
+            g.sC_in = T * nrhs;
+            g.nb_inner = (int)sh;
+            g.batch = (int)(2 * sh);
+            g.m = T;
+            g.n = nrhs;
+            g.k = ks;
+            g.small = true;
+            g.info = info;
+            SPD_TRY((back ? gemm<R, CPLX>(TN, g, st) : gemm<R, CPLX>(NN, g, st)));
+            if constexpr (CPLX) {
+                g_last_error = "split substitution chain is for real types";
+                return SPD_ERR_HIP;
+            } else {
+                const int64_t kp = align_up(T, RECT_KB);
+                SPD_VALIDATE((check_reduce_copy_t<E>(B + cn, ldb, Qb[q], L.ldq, Part, T, T * nrhs, (int)(2 * sh), T,
+                                                      nrhs, kp, info, g_chk)));
+                const int64_t blocks = std::min<int64_t>(cdiv(kp * nrhs, 256), 4096);
+                reduce_copy_t_kernel<E><<<dim3((unsigned)blocks), dim3(256), 0, st>>>(
+                    B + cn, ldb, Qb[q], L.ldq, Part, T, T * nrhs, (int)(2 * sh), T, nrhs, kp, info);
+                SPD_CHECK_LAUNCH("reduce_copy_t_kernel");
+                return 0;
+            }
+        };
+        const bool ahead = lookahead_enabled() && nt >= 3;
+        Lookahead la;
+        hipStream_t sl = s;
+        if (ahead) {
+            SPD_TRY(la.begin(s));
+            sl = la.look;
+        }
+        auto rec = [&](hipEvent_t ev, hipStream_t st) { return ahead ? la.record(ev, st) : 0; };
+        auto wait = [&](hipStream_t st, hipEvent_t ev) { return ahead ? la.wait(st, ev) : 0; };
+        int qi = 0;  // operand buffer of the block being applied
+        // solve block k (inverse product), write it back and transpose it into Qb[q]
+        auto solve_block = [&](int64_t k, bool trans, int q, hipStream_t st) -> int {
+            const int64_t c0 = k * T, tk = std::min(T, n - c0);
+            SPD_TRY(apply_inv(Inv, k, T, B, ldb, c0, tk, nrhs, Tmp, trans, info, st));
+            return copy_t(B + c0, ldb, Qb[q], L.ldq, Tmp, T, tk, nrhs, align_up(tk, RECT_KB), info, st);
+        };
+        // ---- forward: L Y = B
+        SPD_TRY(solve_block(0, false, qi, sl));
+        SPD_TRY(rec(la.ev_panel, sl));
+        for (int64_t k = 0; k < nt; ++k) {
+            const int64_t c0 = k * T, tk = std::min(T, n - c0), r0 = c0 + tk, m = n - r0;
+            const int64_t kp = align_up(tk, RECT_KB);
+            SPD_TRY(wait(s, la.ev_panel));  // Y_k in Qb[qi]
+            if (m <= 0)
+                break;
+            const int64_t t1 = std::min(T, m);  // rows of block k+1
+            if (k > 0)
+                SPD_TRY(wait(sl, la.ev_rest));  // step k-1's update wrote block k+1 and read Qb[qi^1]
+            if (split && k + 1 < nfull) {
+                SPD_TRY(chain(k, k + 1, false, qi ^ 1, sl));
+            } else {
+                SPD_TRY(rect<false>(A + r0 + c0 * lda, lda, Qb[qi], L.ldq, B + r0, ldb, t1, nrhs, kp, tk, vec, info,
+                                    sl));
+                SPD_TRY(solve_block(k + 1, false, qi ^ 1, sl));
+            }
+            SPD_TRY(rec(la.ev_panel, sl));
+            if (m > t1)
+                SPD_TRY(rect<false>(A + (r0 + t1) + c0 * lda, lda, Qb[qi], L.ldq, B + r0 + t1, ldb, m - t1, nrhs, kp,
+                                    tk, vec, info, s));
+            SPD_TRY(rec(la.ev_rest, s));
+            qi ^= 1;
+        }
+        // ---- backward: L^H X = Y, from the last block up
+        SPD_TRY(wait(sl, la.ev_rest));  // every forward update is done
+        qi ^= 1;
+        SPD_TRY(solve_block(nt - 1, true, qi, sl));
+        SPD_TRY(rec(la.ev_panel, sl));
+        for (int64_t k = nt - 1; k >= 0; --k) {
+            const int64_t c0 = k * T, tk = std::min(T, n - c0), kp = align_up(tk, RECT_KB);
+            SPD_TRY(wait(s, la.ev_panel));  // X_k in Qb[qi]
+            if (k == 0)
+                break;
+            const int64_t cp = c0 - T;  // block k-1 is rows [cp, c0)
+            SPD_TRY(wait(sl, la.ev_rest));
+            if (split && k < nfull) {
+                SPD_TRY(chain(k, k - 1, true, qi ^ 1, sl));
+            } else {
+                SPD_TRY(rect<true>(A + c0 + cp * lda, lda, Qb[qi], L.ldq, B + cp, ldb, T, nrhs, kp, tk, vec, info,
+                                   sl));
+                SPD_TRY(solve_block(k - 1, true, qi ^ 1, sl));
+            }
+            SPD_TRY(rec(la.ev_panel, sl));
+            if (cp > 0)
+                SPD_TRY(rect<true>(A + c0, lda, Qb[qi], L.ldq, B, ldb, cp, nrhs, kp, tk, vec, info, s));
+            SPD_TRY(rec(la.ev_rest, s));
+            qi ^= 1;
+        }
+        return 0;
     }
 
     static int nan_fill(int64_t n, int64_t nrhs, E *B, int64_t ldb, const int *info, hipStream_t s)

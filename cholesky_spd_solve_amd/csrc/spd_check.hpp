@@ -25,6 +25,7 @@
 
 #include "spd_gemm.hpp"
 #include "spd_kernels.hpp"
+#include "spd_rect.hpp"
 #include "spd_syrk.hpp"
 
 namespace spd {
@@ -211,6 +212,89 @@ static bool check_syrk(const SyrkArgs &p, dim3 grid, Checker &c)
     return true;
 }
 
+// Replay of rect_kernel (spd_rect.hpp): the P loads (whole vectors on the
+// fast path, element by element with the row and column masks otherwise), the
+// unmasked Q vectors, and the epilogue's read-modify-write of C.
+template <typename R, int BM, int BN, int KB, int WM, int WN, bool PT, bool VEC>
+static bool check_rect(const RectArgs &p, dim3 grid, Checker &c)
+{
+    constexpr int NT = 64 * WM * WN;
+    typedef RectLoad<R, BM, BN, KB, NT, PT> LD;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 16, FN = TN / 16;
+    constexpr int V = LD::V;
+    const char *kn = "rect_kernel";
+    if (p.info != nullptr && !c.access(p.info, 4, false, kn, 0, 0))
+        return false;
+    if (p.ldq % BN != 0 || p.kp % KB != 0 || p.kp <= 0 || p.kvalid > p.kp || (int64_t)p.tiles_m * BM < p.m ||
+        (int64_t)p.ntiles != (int64_t)p.tiles_m * ((p.n + BN - 1) / BN)) {
+        c.err = "rect_kernel: operand layout is not whole tiles and slices";
+        return false;
+    }
+    for (unsigned b = 0; b < grid.x; ++b) {
+        const int t = xcd_remap((int)b, p.ntiles);
+        const int I = t % p.tiles_m, J = t / p.tiles_m;
+        const int i0 = I * BM, j0 = J * BN;
+        if ((int64_t)j0 >= p.ldq) {
+            c.err = "rect_kernel: workgroup maps past the operand buffer";
+            return false;
+        }
+        const bool prows = i0 + BM <= p.m;
+        const R *P = (const R *)p.P + (PT ? (int64_t)i0 * p.ldp : (int64_t)i0);
+        const R *Q = (const R *)p.Q + j0;
+        for (int tid = 0; tid < NT; ++tid) {
+            for (int k0 = 0; k0 < p.kp; k0 += KB) {
+                const R *pa = P + (PT ? (int64_t)k0 : (int64_t)k0 * p.ldp);
+                const R *qb = Q + (int64_t)k0 * p.ldq;
+                const bool fast = prows && k0 + KB <= p.kvalid;
+                for (int q = 0; q < LD::LP; ++q) {
+                    int r, k;
+                    LD::p_coords(tid, q, r, k);
+                    const int64_t off = PT ? (k + (int64_t)r * p.ldp) : (r + (int64_t)k * p.ldp);
+                    if (fast) {
+                        if (VEC && ((uintptr_t)(pa + off)) % 16 != 0) {
+                            c.err = "rect_kernel: unaligned vector load of P";
+                            return false;
+                        }
+                        if (!c.access(pa + off, 16, false, kn, b, tid))
+                            return false;
+                    } else {
+                        for (int v = 0; v < V; ++v) {
+                            const int i = i0 + r + (PT ? 0 : v), kk = k0 + k + (PT ? v : 0);
+                            if (i < p.m && kk < p.kvalid && !c.access(pa + off + v, sizeof(R), false, kn, b, tid))
+                                return false;
+                        }
+                    }
+                }
+                for (int q = 0; q < LD::LQ; ++q) {
+                    int r, k;
+                    LD::q_coords(tid, q, r, k);
+                    if (!c.access(qb + r + (int64_t)k * p.ldq, 16, false, kn, b, tid))
+                        return false;
+                }
+            }
+            const int lane = tid & 63, wave = tid >> 6;
+            const int wm = wave % WM, wn = wave / WM;
+            const int li = lane & 15, lk = lane >> 4;
+            const int ib = wm * TM, jb = wn * TN;
+            const bool whole = prows && (j0 + BN <= p.n);
+            R *Ct = (R *)p.C + i0 + (int64_t)j0 * p.ldc;
+            for (int fi = 0; fi < FM; ++fi)
+                for (int fj = 0; fj < FN; ++fj)
+                    for (int q = 0; q < 4; ++q) {
+                        const int i = ib + fi * 16 + li, j = jb + fj * 16 + acc_row<R>(lk, q);
+                        if (whole || (i0 + i < p.m && j0 + j < p.n)) {
+                            R *dst = Ct + i + (int64_t)j * p.ldc;
+                            if (!c.access(dst, sizeof(R), false, kn, b, tid) ||
+                                !c.access(dst, sizeof(R), true, kn, b, tid))
+                                return false;
+                        }
+                    }
+        }
+    }
+    return true;
+}
+
 template <typename R, bool CPLX>
 static bool check_leaf(const LeafArgs &p, unsigned grid, Checker &c)
 {
@@ -254,6 +338,38 @@ static bool check_2d(const char *kn, E *dst, int64_t ldd, const E *src, int64_t 
             if (src != nullptr && !c.access(src + i + j * lds, sizeof(E), false, kn, 0, 0))
                 return false;
         }
+    return true;
+}
+
+// copy_t_kernel: dst(0:m, 0:n) and src(0:m, 0:n) as check_2d, and qt(j, i)
+// for i < kp, j < n
+template <typename E>
+static bool check_copy_t(E *dst, int64_t ldd, E *qt, int64_t ldq, const E *src, int64_t lds, int64_t m,
+                         int64_t n, int64_t kp, const int *info, Checker &c)
+{
+    const char *kn = "copy_t_kernel";
+    if (!check_2d<E>(kn, dst, ldd, src, lds, m, n, info, c))
+        return false;
+    for (int64_t i = 0; i < kp; ++i)
+        for (int64_t j = 0; j < n; ++j)
+            if (!c.access(qt + j + i * ldq, sizeof(E), true, kn, 0, 0))
+                return false;
+    return true;
+}
+
+// reduce_copy_t_kernel: S partial blocks read, dst and qt as copy_t
+template <typename E>
+static bool check_reduce_copy_t(E *dst, int64_t ldd, E *qt, int64_t ldq, const E *part, int64_t ldp, int64_t sp,
+                                int S, int64_t m, int64_t n, int64_t kp, const int *info, Checker &c)
+{
+    const char *kn = "reduce_copy_t_kernel";
+    for (int z = 0; z < S; ++z)
+        if (!check_2d<E>(kn, z == 0 ? dst : nullptr, ldd, part + z * sp, ldp, m, n, info, c))
+            return false;
+    for (int64_t i = 0; i < kp; ++i)
+        for (int64_t j = 0; j < n; ++j)
+            if (!c.access(qt + j + i * ldq, sizeof(E), true, kn, 0, 0))
+                return false;
     return true;
 }
 
