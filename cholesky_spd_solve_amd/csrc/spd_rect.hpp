@@ -23,6 +23,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "spd_gemm.hpp"
 
 namespace spd {
@@ -79,7 +81,9 @@ struct RectLoad {
 // VEC: P may be read with 16-byte vectors (the host checked the alignment);
 // otherwise the same elements are read one by one.  The arithmetic is the
 // same either way, so results do not depend on the leading dimension.
-template <typename R, int BM, int BN, int KB, int WM, int WN, bool PT, bool VEC>
+// DEPTH: slices of P and Q in flight from memory (1: the next one; 2: the
+// next two, in two register sets, for more bytes in flight per CU).
+template <typename R, int BM, int BN, int KB, int WM, int WN, bool PT, bool VEC, int DEPTH = 1>
 __global__ void __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)))
 rect_kernel(const RectArgs p)
 {
@@ -126,8 +130,9 @@ rect_kernel(const RectArgs p)
     const int64_t qstep = (int64_t)KB * p.ldq;
     const bool prows = i0 + BM <= p.m;  // every row of the P block exists
 
-    R ra[LP][V], rb[LQ][V];
-    auto load = [&](const R *__restrict__ oa, const R *__restrict__ ob, int k0) {
+    static_assert(DEPTH == 1 || DEPTH == 2, "one or two slices in flight");
+    R rga[DEPTH][LP][V], rgb[DEPTH][LQ][V];
+    auto load = [&](R (&ra)[LP][V], R (&rb)[LQ][V], const R *__restrict__ oa, const R *__restrict__ ob, int k0) {
         if (prows && k0 + KB <= p.kvalid) {
 #pragma unroll
             for (int q = 0; q < LP; ++q) {
@@ -159,7 +164,7 @@ rect_kernel(const RectArgs p)
                 rb[q][v] = y[v];
         }
     };
-    auto store = [&](int buf) {
+    auto store = [&](const R (&ra)[LP][V], const R (&rb)[LQ][V], int buf) {
 #pragma unroll
         for (int q = 0; q < LP; ++q)
 #pragma unroll
@@ -183,29 +188,36 @@ rect_kernel(const RectArgs p)
         for (int fj = 0; fj < FN; ++fj)
             acc[fi][fj] = V4{0, 0, 0, 0};
 
-    load(pa, qb, 0);
+    const int nsl = p.kp / KB;
+    load(rga[0], rgb[0], pa, qb, 0);
+    if (DEPTH == 2 && nsl > 1)
+        load(rga[DEPTH - 1], rgb[DEPTH - 1], pa + pstep, qb + qstep, KB);
     // status word read alongside the first slice (the operands are valid
     // whatever it holds; nothing is written before it)
     if (p.info != nullptr && *p.info != 0)
         return;
-    store(0);
+    store(rga[0], rgb[0], 0);
     __syncthreads();
-    int cur = 0;
-    for (int k0 = 0; k0 < p.kp; k0 += KB) {
-        const bool more = k0 + KB < p.kp;
-        if (more) {
-            pa += pstep;
-            qb += qstep;
-            load(pa, qb, k0 + KB);
+    // Slice sl is read from LDS buffer sl % 2.  With DEPTH 2 the registers of
+    // set sl % 2 are refilled with slice sl + 2 while slice sl is multiplied,
+    // and set (sl + 1) % 2 (slice sl + 1, loaded one slice earlier) goes to LDS
+    // after it; with DEPTH 1 slice sl + 1 is loaded and stored within it.
+    auto body = [&](int sl, auto par) {
+        constexpr int P = decltype(par)::value;  // sl % 2
+        if (DEPTH == 2) {
+            if (sl + 2 < nsl)
+                load(rga[P % DEPTH], rgb[P % DEPTH], pa + (sl + 2) * pstep, qb + (sl + 2) * qstep, (sl + 2) * KB);
+        } else if (sl + 1 < nsl) {
+            load(rga[0], rgb[0], pa + (sl + 1) * pstep, qb + (sl + 1) * qstep, (sl + 1) * KB);
         }
         R fa[2][FM], fb[2][FN];
         auto frag = [&](int kr, R (&a)[FM], R (&b)[FN]) {
 #pragma unroll
             for (int fi = 0; fi < FM; ++fi)
-                a[fi] = As[cur][kr][ib + fi * 16 + li];
+                a[fi] = As[P][kr][ib + fi * 16 + li];
 #pragma unroll
             for (int fj = 0; fj < FN; ++fj)
-                b[fj] = Bs[cur][kr][jb + fj * 16 + li];
+                b[fj] = Bs[P][kr][jb + fj * 16 + li];
         };
         frag(lk, fa[0], fb[0]);
 #pragma unroll
@@ -218,10 +230,14 @@ rect_kernel(const RectArgs p)
                 for (int fj = 0; fj < FN; ++fj)
                     acc[fi][fj] = mfma16(fb[s & 1][fj], fa[s & 1][fi], acc[fi][fj]);
         }
-        if (more)
-            store(cur ^ 1);
+        if (sl + 1 < nsl)
+            store(rga[(P + 1) % DEPTH], rgb[(P + 1) % DEPTH], P ^ 1);
         __syncthreads();
-        cur ^= 1;
+    };
+    for (int sl = 0; sl < nsl; sl += 2) {
+        body(sl, std::integral_constant<int, 0>());
+        if (sl + 1 < nsl)
+            body(sl + 1, std::integral_constant<int, 1>());
     }
 
     // epilogue: C -= acc, one 16-row block at a time
