@@ -31,8 +31,8 @@ DTYPE_CODE = {
     torch.complex64: SPD_C64,
     torch.complex128: SPD_C128,
 }
-SYMBOLS = ("spd_workspace_size", "spd_potrf", "spd_potrs", "spd_logdet", "spd_last_error",
-           "spd_profile_enable", "spd_profile_read", "spd_debug_validate")
+SYMBOLS = ("spd_workspace_size", "spd_potrf", "spd_potrs", "spd_forward_solve", "spd_gp_loglik", "spd_logdet",
+           "spd_last_error", "spd_profile_enable", "spd_profile_read", "spd_debug_validate")
 SPD_ERR_HIP, SPD_ERR_CHECK = 1, 2
 PROF_SYRK, PROF_PANEL, PROF_DIAG, PROF_SOLVE = 0, 1, 2, 3
 
@@ -71,6 +71,10 @@ def load():
             lib.spd_potrf.restype = i32
             lib.spd_potrs.argtypes = [i32, i64, i64, vp, i64, vp, i64, i64, vp, vp, sz, vp]
             lib.spd_potrs.restype = i32
+            lib.spd_forward_solve.argtypes = [i32, i64, i64, vp, i64, vp, i64, i64, vp, vp, sz, vp]
+            lib.spd_forward_solve.restype = i32
+            lib.spd_gp_loglik.argtypes = [i32, i64, i64, vp, i64, vp, i64, i64, vp, vp, vp, sz, vp]
+            lib.spd_gp_loglik.restype = i32
             lib.spd_logdet.argtypes = [i32, i64, vp, i64, vp, vp, vp]
             lib.spd_logdet.restype = i32
             lib.spd_last_error.argtypes = []
@@ -171,6 +175,45 @@ def potrs(L: torch.Tensor, B: torch.Tensor, T_A: int, info: torch.Tensor | None 
                           work.numel(), ctypes.c_void_p(_stream(stream)))
     _check(rc, "spd_potrs")
     return B
+
+
+def forward_solve(L: torch.Tensor, B: torch.Tensor, T_A: int, info: torch.Tensor | None = None,
+                  work: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Overwrite B with L^-1 B (forward substitution only); returns B."""
+    lda = _colmajor(L, "L")
+    ldb = _colmajor(B, "B")
+    n, nrhs = B.shape
+    if L.shape != (n, n):
+        raise ValueError("L must be n x n with n = B.shape[0]")
+    if B.dtype != L.dtype:
+        raise TypeError("L and B must have the same dtype")
+    if work is None:
+        work = workspace(L.dtype, n, nrhs, T_A, L.device)
+    rc = load().spd_forward_solve(_code(L), n, nrhs, _ptr(L), lda, _ptr(B), ldb, int(T_A), _ptr(info), _ptr(work),
+                                  work.numel(), ctypes.c_void_p(_stream(stream)))
+    _check(rc, "spd_forward_solve")
+    return B
+
+
+def gp_loglik(L: torch.Tensor, R: torch.Tensor, T_A: int, info: torch.Tensor | None = None,
+              work: torch.Tensor | None = None, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Gaussian-process marginal log-likelihood of each residual column of R
+    (R is overwritten by L^-1 R) into a device float64 tensor of R.shape[1]."""
+    lda = _colmajor(L, "L")
+    ldr = _colmajor(R, "R")
+    n, nrhs = R.shape
+    if L.shape != (n, n):
+        raise ValueError("L must be n x n with n = R.shape[0]")
+    if R.dtype != L.dtype:
+        raise TypeError("L and R must have the same dtype")
+    if work is None:
+        work = workspace(L.dtype, n, nrhs, T_A, L.device)
+    if out is None:
+        out = torch.empty(nrhs, dtype=torch.float64, device=L.device)
+    rc = load().spd_gp_loglik(_code(L), n, nrhs, _ptr(L), lda, _ptr(R), ldr, int(T_A), _ptr(info), _ptr(out),
+                              _ptr(work), work.numel(), ctypes.c_void_p(_stream(stream)))
+    _check(rc, "spd_gp_loglik")
+    return out
 
 
 def logdet(L: torch.Tensor, info: torch.Tensor | None = None, out: torch.Tensor | None = None,

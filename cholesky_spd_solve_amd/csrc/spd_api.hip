@@ -825,26 +825,46 @@ struct Solver {
         return 0;
     }
 
+    // backward = false: the forward substitution L Y = B only
     static int potrs(int64_t n, int64_t nrhs, const E *A, int64_t lda, E *B, int64_t ldb, int64_t T_A,
-                     const int *info, void *work, hipStream_t s)
+                     const int *info, void *work, hipStream_t s, bool backward = true)
     {
         if (n == 0 || nrhs == 0)
             return 0;
         const Layout L = make_layout(n, nrhs, T_A, sizeof(E));
         {
-            ProfScope ps(PROF_SOLVE, FMUL * 2.0 * (double)n * n * nrhs, s);
+            ProfScope ps(PROF_SOLVE, FMUL * (backward ? 2.0 : 1.0) * (double)n * n * nrhs, s);
             if (rect_usable(lda))
-                SPD_TRY(potrs_blocks(n, nrhs, A, lda, B, ldb, L, info, work, s));
+                SPD_TRY(potrs_blocks(n, nrhs, A, lda, B, ldb, L, info, work, s, backward));
             else
-                SPD_TRY(potrs_general(n, nrhs, A, lda, B, ldb, L, info, work, s));
+                SPD_TRY(potrs_general(n, nrhs, A, lda, B, ldb, L, info, work, s, backward));
         }
         return nan_fill(n, nrhs, B, ldb, info, s);
+    }
+
+    // Gaussian-process marginal log-likelihood of the residual columns of R
+    // (real types): R <- L^-1 R, then the per-column reduction.
+    static int gp_loglik(int64_t n, int64_t nrhs, const E *A, int64_t lda, E *Rm, int64_t ldr, int64_t T_A,
+                         const int *info, double *out, void *work, hipStream_t s)
+    {
+        if (nrhs == 0)
+            return 0;
+        SPD_TRY(potrs(n, nrhs, A, lda, Rm, ldr, T_A, info, work, s, false));
+        if constexpr (CPLX) {
+            g_last_error = "the likelihood is defined for real types";
+            return SPD_ERR_HIP;
+        } else {
+            SPD_VALIDATE((check_gp_loglik<R>(Rm, ldr, A, lda, n, nrhs, info, out, g_chk)));
+            gp_loglik_kernel<R><<<dim3((unsigned)nrhs), dim3(256), 0, s>>>(Rm, ldr, A, lda, n, info, out);
+            SPD_CHECK_LAUNCH("gp_loglik_kernel");
+            return 0;
+        }
     }
 
     // Block substitutions on the general product kernel (complex types, and
     // leading dimensions beyond the block-update kernel's 32-bit offsets).
     static int potrs_general(int64_t n, int64_t nrhs, const E *A, int64_t lda, E *B, int64_t ldb, const Layout &L,
-                             const int *info, void *work, hipStream_t s)
+                             const int *info, void *work, hipStream_t s, bool backward)
     {
         const int64_t T = L.T, nt = L.nt;
         E *Inv = (E *)work + L.inv;
@@ -872,6 +892,8 @@ struct Solver {
                 SPD_TRY((gemm<R, CPLX>(NN, u, s)));
             }
         }
+        if (!backward)
+            return 0;
         // backward: L^H X = Y
         for (int64_t k = nt - 1; k >= 0; --k) {
             const int64_t c0 = k * T, tk = std::min(T, n - c0);
@@ -912,7 +934,7 @@ struct Solver {
     // before it overwrites the operand buffer that update read.  The back
     // substitution runs the same way from the last block up.
     static int potrs_blocks(int64_t n, int64_t nrhs, const E *A, int64_t lda, E *B, int64_t ldb, const Layout &L,
-                            const int *info, void *work, hipStream_t s)
+                            const int *info, void *work, hipStream_t s, bool backward)
     {
         const int64_t T = L.T, nt = L.nt;
         E *Inv = (E *)work + L.inv;
@@ -944,6 +966,8 @@ struct Solver {
             g.neg = true;
             g.info = info;
             SPD_TRY((gemm<R, CPLX>(NN, g, s)));
+        }
+        if (split && backward) {
             // GB_k = -L_k,k-1 inv(L_k-1,k-1) for whole blocks k (k = 1 .. nfull-1)
             Gemm h;
             h.A = A + T;
@@ -1048,6 +1072,8 @@ struct Solver {
             SPD_TRY(rec(la.ev_rest, s));
             qi ^= 1;
         }
+        if (!backward)
+            return 0;
         // ---- backward: L^H X = Y, from the last block up
         SPD_TRY(wait(sl, la.ev_rest));  // every forward update is done
         qi ^= 1;
@@ -1195,6 +1221,76 @@ int spd_potrs(spd_dtype_t dt, int64_t n, int64_t n_rhs, const void *dA, int64_t 
                                            (Elem<double, true>::type *)dB, ldb, T_A, d_info, d_work, s);
     }
     return -1;
+}
+
+int spd_forward_solve(spd_dtype_t dt, int64_t n, int64_t n_rhs, const void *dA, int64_t lda, void *dB, int64_t ldb,
+                      int64_t T_A, const int32_t *d_info, void *d_work, size_t work_bytes, void *stream)
+{
+    if (elem_size(dt) == 0) return -1;
+    if (n < 0 || n > INT32_MAX) return -2;
+    if (n_rhs < 0 || n_rhs > INT32_MAX) return -3;
+    if (dA == nullptr && n > 0) return -4;
+    if (lda < std::max<int64_t>(1, n)) return -5;
+    if (dB == nullptr && n > 0 && n_rhs > 0) return -6;
+    if (ldb < std::max<int64_t>(1, n)) return -7;
+    if (T_A < 1) return -8;
+    const size_t need = spd_workspace_size(dt, n, n_rhs, T_A);
+    if (d_work == nullptr && need > 0) return -10;
+    if (work_bytes < need) return -11;
+    if (g_validate) {
+        g_chk.begin();
+        g_chk.add(dA, matrix_bytes(dt, n, n, lda), false, "L");
+        g_chk.add(dB, matrix_bytes(dt, n, n_rhs, ldb), true, "B");
+        g_chk.add(d_info, 4, false, "info");
+        g_chk.add(d_work, work_bytes, true, "workspace");
+    }
+    hipStream_t s = (hipStream_t)stream;
+    switch (dt) {
+    case SPD_R32:
+        return Solver<float, false>::potrs(n, n_rhs, (const float *)dA, lda, (float *)dB, ldb, T_A, d_info, d_work, s,
+                                           false);
+    case SPD_R64:
+        return Solver<double, false>::potrs(n, n_rhs, (const double *)dA, lda, (double *)dB, ldb, T_A, d_info,
+                                            d_work, s, false);
+    case SPD_C64:
+        return Solver<float, true>::potrs(n, n_rhs, (const Elem<float, true>::type *)dA, lda,
+                                          (Elem<float, true>::type *)dB, ldb, T_A, d_info, d_work, s, false);
+    case SPD_C128:
+        return Solver<double, true>::potrs(n, n_rhs, (const Elem<double, true>::type *)dA, lda,
+                                           (Elem<double, true>::type *)dB, ldb, T_A, d_info, d_work, s, false);
+    }
+    return -1;
+}
+
+int spd_gp_loglik(spd_dtype_t dt, int64_t n, int64_t n_rhs, const void *dA, int64_t lda, void *dR, int64_t ldr,
+                  int64_t T_A, const int32_t *d_info, double *d_out, void *d_work, size_t work_bytes, void *stream)
+{
+    if (dt != SPD_R32 && dt != SPD_R64) return -1;
+    if (n < 0 || n > INT32_MAX) return -2;
+    if (n_rhs < 0 || n_rhs > INT32_MAX) return -3;
+    if (dA == nullptr && n > 0) return -4;
+    if (lda < std::max<int64_t>(1, n)) return -5;
+    if (dR == nullptr && n > 0 && n_rhs > 0) return -6;
+    if (ldr < std::max<int64_t>(1, n)) return -7;
+    if (T_A < 1) return -8;
+    if (d_out == nullptr && n_rhs > 0) return -10;
+    const size_t need = spd_workspace_size(dt, n, n_rhs, T_A);
+    if (d_work == nullptr && need > 0) return -11;
+    if (work_bytes < need) return -12;
+    if (g_validate) {
+        g_chk.begin();
+        g_chk.add(dA, matrix_bytes(dt, n, n, lda), false, "L");
+        g_chk.add(dR, matrix_bytes(dt, n, n_rhs, ldr), true, "R");
+        g_chk.add(d_info, 4, false, "info");
+        g_chk.add(d_out, (size_t)n_rhs * sizeof(double), true, "out");
+        g_chk.add(d_work, work_bytes, true, "workspace");
+    }
+    hipStream_t s = (hipStream_t)stream;
+    if (dt == SPD_R32)
+        return Solver<float, false>::gp_loglik(n, n_rhs, (const float *)dA, lda, (float *)dR, ldr, T_A, d_info, d_out,
+                                               d_work, s);
+    return Solver<double, false>::gp_loglik(n, n_rhs, (const double *)dA, lda, (double *)dR, ldr, T_A, d_info, d_out,
+                                            d_work, s);
 }
 
 int spd_logdet(spd_dtype_t dt, int64_t n, const void *dA, int64_t lda, const int32_t *d_info, double *d_logdet,

@@ -373,4 +373,21 @@ static bool check_reduce_copy_t(E *dst, int64_t ldd, E *qt, int64_t ldq, const E
     return true;
 }
 
+// gp_loglik_kernel: Y(0:n, 0:nrhs) and the diagonal of L read, out written
+template <typename R>
+static bool check_gp_loglik(const R *Y, int64_t ldy, const R *L, int64_t lda, int64_t n, int64_t nrhs,
+                            const int *info, double *out, Checker &c)
+{
+    const char *kn = "gp_loglik_kernel";
+    if (!check_2d<R>(kn, nullptr, 0, Y, ldy, n, nrhs, info, c))
+        return false;
+    for (int64_t i = 0; i < n; ++i)
+        if (!c.access(L + i * (1 + lda), sizeof(R), false, kn, 0, 0))
+            return false;
+    for (int64_t j = 0; j < nrhs; ++j)
+        if (!c.access(out + j, sizeof(double), true, kn, j, 0))
+            return false;
+    return true;
+}
+
 }  // namespace spd

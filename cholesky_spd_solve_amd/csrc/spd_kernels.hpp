@@ -546,6 +546,42 @@ __global__ void __launch_bounds__(1024) logdet_kernel(const void *Lv, int64_t ld
         *out = (info != nullptr && *info != 0) ? __longlong_as_double(0x7ff8000000000000LL) : 2.0 * red[0];
 }
 
+// Gaussian-process marginal log-likelihood per right-hand-side column (JAXMg
+// paper, "Research Impact Statement", "Cholesky solve (potrs)"): with Y = L^-1 R
+// already in place of R,
+//     out[j] = -1/2 |Y(:, j)|^2 - sum_i log L_ii - (n/2) log(2 pi)
+// (the middle term is 1/2 log det A).  One workgroup per column; both sums are
+// accumulated in double by a fixed reduction tree, so the result is the same
+// bits on every run.  NaN if the factorization reported a failure.
+template <typename R>
+__global__ void __launch_bounds__(256) gp_loglik_kernel(const R *Y, int64_t ldy, const R *L, int64_t lda, int64_t n,
+                                                        const int *info, double *out)
+{
+    __shared__ double red[2][256];
+    const int tid = threadIdx.x, j = blockIdx.x;
+    double ss = 0.0, ld = 0.0;
+    for (int64_t i = tid; i < n; i += 256) {
+        const double y = (double)Y[i + (int64_t)j * ldy];
+        ss += y * y;
+        ld += log((double)L[i * (1 + lda)]);
+    }
+    red[0][tid] = ss;
+    red[1][tid] = ld;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (tid < w) {
+            red[0][tid] += red[0][tid + w];
+            red[1][tid] += red[1][tid + w];
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        const double two_pi = 6.283185307179586476925286766559;
+        out[j] = (info != nullptr && *info != 0) ? __longlong_as_double(0x7ff8000000000000LL)
+                                                 : -0.5 * red[0][0] - red[1][0] - 0.5 * (double)n * log(two_pi);
+    }
+}
+
 __global__ void set_int_kernel(int *p, int v) { *p = v; }
 
 // dst(0:m, 0:n) = src(0:m, 0:n)

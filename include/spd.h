@@ -1,7 +1,9 @@
 /*
  * spd.h - C ABI of the MI355X (gfx950) dense symmetric / Hermitian
  * positive-definite solver: blocked Cholesky factorization (potrf), the
- * triangular solves that use it (potrs) and the log-determinant (logdet).
+ * triangular solves that use it (potrs, and the forward substitution alone),
+ * the log-determinant (logdet) and the Gaussian-process marginal
+ * log-likelihood built from them.
  *
  * The operation (JAXMg paper, "Software design", the potrs routine): solve
  * A X = B for an N x N symmetric (Hermitian) positive-definite A and an
@@ -102,6 +104,36 @@ int spd_potrf(spd_dtype_t dt, int64_t n, void *dA, int64_t lda, int64_t T_A,
 int spd_potrs(spd_dtype_t dt, int64_t n, int64_t n_rhs, const void *dA, int64_t lda,
               void *dB, int64_t ldb, int64_t T_A, const int32_t *d_info,
               void *d_work, size_t work_bytes, void *stream);
+
+/* Forward substitution only: overwrite B with Y = L^-1 B, from the factor of
+ * spd_potrf (JAXMg paper, "Software design": the first of potrs' two
+ * triangular solves; "Research Impact Statement", "Cholesky solve (potrs)":
+ * the quadratic term of the Gaussian-process likelihood is |L^-1 r|^2).
+ * Arguments, layout, workspace and the NaN-on-failure rule are those of
+ * spd_potrs (same argument numbers); only L Y = B is solved. */
+int spd_forward_solve(spd_dtype_t dt, int64_t n, int64_t n_rhs, const void *dA, int64_t lda,
+                      void *dB, int64_t ldb, int64_t T_A, const int32_t *d_info,
+                      void *d_work, size_t work_bytes, void *stream);
+
+/* Gaussian-process marginal log-likelihood (JAXMg paper, "Research Impact
+ * Statement", "Cholesky solve (potrs)"): for A = K + Sigma factored by
+ * spd_potrf and each residual column r_j = y_j - m_j of R,
+ *     out[j] = -1/2 r_j^T A^-1 r_j - 1/2 log det A - (n/2) log(2 pi),
+ * computed as -1/2 |L^-1 r_j|^2 - sum_i log L_ii - (n/2) log(2 pi).
+ * Real types only (dt = SPD_R32 or SPD_R64; the formula is the real Gaussian
+ * density).
+ *   dA, lda   the factor L (lower triangle read only)
+ *   dR, ldr   device, n x n_rhs column-major residuals; overwritten by L^-1 R
+ *   d_info    the d_info of spd_potrf (may be NULL); non-zero gives NaN in
+ *             every out[j] and in R
+ *   d_out     device double[n_rhs], written; each value is summed in double by
+ *             a fixed reduction tree, so repeated calls give identical bits
+ *   d_work    workspace of >= spd_workspace_size(dt, n, n_rhs, T_A) bytes
+ * Argument numbers: dt=1 n=2 n_rhs=3 dA=4 lda=5 dR=6 ldr=7 T_A=8 d_info=9
+ * d_out=10 d_work=11 work_bytes=12. */
+int spd_gp_loglik(spd_dtype_t dt, int64_t n, int64_t n_rhs, const void *dA, int64_t lda,
+                  void *dR, int64_t ldr, int64_t T_A, const int32_t *d_info, double *d_out,
+                  void *d_work, size_t work_bytes, void *stream);
 
 /* log det(A) = 2 * sum_i log(Re L_ii) from the factor L of spd_potrf (JAXMg
  * paper, "Software design": the same factorization can return log det(A);

@@ -56,6 +56,8 @@ def _load():
                 f.argtypes, f.restype = [i64, i64, vp, vp], None
                 f = getattr(lib, "oracle_logdet_" + suf)
                 f.argtypes, f.restype = [i64, vp], ctypes.c_double
+                f = getattr(lib, "oracle_fwd_" + suf)
+                f.argtypes, f.restype = [i64, i64, vp, vp], None
             _lib = lib
     return _lib
 
@@ -104,13 +106,57 @@ def potrs(l, b):
     dt = np.complex128 if cplx else np.float64
     l = np.ascontiguousarray(l, dtype=dt)
     # right-hand-side columns one after another: the transpose, row-major
-    bt = np.ascontiguousarray(b2.T, dtype=dt)
+    bt = np.array(b2.T, dtype=dt, order="C", copy=True)  # never the caller's memory
     nrhs = bt.shape[0]
     if n > 0 and nrhs > 0:
         f = _load().oracle_potrs_z if cplx else _load().oracle_potrs_d
         f(n, nrhs, _p(l), _p(bt))
     x = bt.T.copy()
     return x.reshape(b.shape) if vec else x
+
+
+def forward_solve(l, b):
+    """Y with L Y = B (forward substitution only) given the factor L."""
+    l = _wide(l)
+    n = l.shape[0]
+    b = np.asarray(b)
+    vec = b.ndim == 1
+    b2 = b.reshape(n, 1) if vec else b
+    cplx = np.iscomplexobj(l) or np.iscomplexobj(b2)
+    dt = np.complex128 if cplx else np.float64
+    l = np.ascontiguousarray(l, dtype=dt)
+    bt = np.array(b2.T, dtype=dt, order="C", copy=True)  # never the caller's memory
+    if n > 0 and bt.shape[0] > 0:
+        f = _load().oracle_fwd_z if cplx else _load().oracle_fwd_d
+        f(n, bt.shape[0], _p(l), _p(bt))
+    y = bt.T.copy()
+    return y.reshape(b.shape) if vec else y
+
+
+def gp_loglik(a, r):
+    """Gaussian-process marginal log-likelihood per column r_j of R (JAXMg
+    paper, "Research Impact Statement", "Cholesky solve (potrs)"): with
+    r = y - m the residual and A = K + Sigma,
+
+        log L = -1/2 r^T A^{-1} r - 1/2 log det A - (N/2) log(2 pi),
+
+    written out directly: x = A^{-1} r by the oracle's solve, the quadratic
+    term as the dot product r . x, log det A from the factor.  Real A only.
+    Returns (values, info); values are NaN when info != 0."""
+    a = np.asarray(a)
+    if np.iscomplexobj(a):
+        raise ValueError("the likelihood is defined for real A")
+    r = np.asarray(r, dtype=np.float64)
+    vec = r.ndim == 1
+    r2 = r.reshape(-1, 1) if vec else r
+    n = r2.shape[0]
+    x, ld, info = solve(a, r2, want_logdet=True)
+    if info != 0:
+        out = np.full(r2.shape[1], np.nan)
+    else:
+        quad = np.einsum("ij,ij->j", r2, x)
+        out = -0.5 * quad - 0.5 * ld - 0.5 * n * np.log(2.0 * np.pi)
+    return (out[0] if vec else out), info
 
 
 def logdet(l) -> float:

@@ -8,7 +8,9 @@
  * symmetric (Hermitian) positive-definite A, the Cholesky factor A = L L^H
  * with L lower triangular and a positive real diagonal, the solution of
  * A X = B by L Y = B then L^H X = Y, and, from the same factor,
- * log det A = 2 * sum_i log L_ii.
+ * log det A = 2 * sum_i log L_ii.  The forward substitution L Y = B alone is
+ * also exported (the Gaussian-process likelihood of the same paper, "Cholesky
+ * solve (potrs)", uses it).
  *
  * The factorization is the textbook unblocked column-by-column (Crout /
  * left-looking) form of the definition L L^H = A:
@@ -88,6 +90,22 @@ void oracle_potrs_d(int64_t n, int64_t nrhs, const double *l, double *b)
     }
 }
 
+/* Forward substitution only: L y = b, row by row; b is overwritten by y. */
+void oracle_fwd_d(int64_t n, int64_t nrhs, const double *l, double *b)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t c = 0; c < nrhs; ++c) {
+        double *y = b + c * n;
+        for (int64_t i = 0; i < n; ++i) {
+            const double *li = l + i * n;
+            double s = y[i];
+            for (int64_t k = 0; k < i; ++k)
+                s -= li[k] * y[k];
+            y[i] = s / li[i];
+        }
+    }
+}
+
 double oracle_logdet_d(int64_t n, const double *l)
 {
     double s = 0.0;
@@ -144,6 +162,23 @@ void oracle_potrs_z(int64_t n, int64_t nrhs, const double complex *l, double com
             y[i] = xi;
             for (int64_t k = 0; k < i; ++k)
                 y[k] -= conj(li[k]) * xi;
+        }
+    }
+}
+
+/* Forward substitution only: L y = b; b is overwritten by y. */
+void oracle_fwd_z(int64_t n, int64_t nrhs, const double complex *l, double complex *b)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t c = 0; c < nrhs; ++c) {
+        double complex *y = b + c * n;
+        for (int64_t i = 0; i < n; ++i) {
+            const double complex *li = l + i * n;
+            double complex s = y[i];
+            for (int64_t k = 0; k < i; ++k)
+                s -= li[k] * y[k];
+            const double d = creal(li[i]);
+            y[i] = CMPLX(creal(s) / d, cimag(s) / d);
         }
     }
 }

@@ -73,6 +73,24 @@ def test_dry_run_padded_and_unaligned(lib, dt, n, nrhs, T):
     dry_solve(lib, CODE[dt], n, nrhs, T, lda=n + 2, ldb=n + 2, shift=1)
 
 
+@pytest.mark.parametrize("dt,n,nrhs,T", [s for s in SHAPES if s[0] in ("f64", "f32")])
+def test_dry_run_forward_solve_and_gp_loglik(lib, dt, n, nrhs, T):
+    code, es = CODE[dt], ES[CODE[dt]]
+    vp = ctypes.c_void_p
+    A, B, info, out, work = BASE, 2 * BASE, 3 * BASE, 3 * BASE + 4096, 4 * BASE
+    wbytes = lib.spd_workspace_size(code, n, nrhs, T)
+    assert lib.spd_forward_solve(code, n, nrhs, vp(A), n, vp(B), n, T, vp(info), vp(work), wbytes, None) == 0, \
+        lib.spd_last_error()
+    assert lib.spd_gp_loglik(code, n, nrhs, vp(A), n, vp(B), n, T, vp(info), vp(out), vp(work), wbytes, None) == 0, \
+        lib.spd_last_error()
+
+
+def test_dry_run_real_general_path(lib):
+    """A leading dimension past the block-update kernel's 32-bit offsets sends
+    real types down the general substitution path; it must stay in bounds."""
+    dry_solve(lib, 1, 65, 3, 32, lda=(1 << 24) + 8)
+
+
 def test_dry_run_detects_a_short_workspace(lib):
     """The validator itself: a workspace one byte too small for the kernels
     (but passed as large enough) must be caught."""

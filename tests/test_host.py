@@ -95,6 +95,17 @@ def test_argument_validation_returns_before_gpu_work(lib):
     ld = lib.spd_logdet
     assert ld(1, 4, dummy, 2, info, dummy, None) == -4
     assert ld(1, 4, dummy, 4, info, None, None) == -6
+    fw = lib.spd_forward_solve
+    assert fw(7, 4, 2, dummy, 4, dummy, 4, 2, info, dummy, 1 << 20, None) == -1
+    assert fw(1, 4, 2, dummy, 4, dummy, 3, 2, info, dummy, 1 << 20, None) == -7
+    assert fw(1, 4, 2, dummy, 4, dummy, 4, 2, info, dummy, 8, None) == -11
+    gp = lib.spd_gp_loglik
+    out = vp(0x3000)
+    assert gp(3, 4, 2, dummy, 4, dummy, 4, 2, info, out, dummy, 1 << 20, None) == -1  # complex
+    assert gp(2, 4, 2, dummy, 4, dummy, 4, 2, info, out, dummy, 1 << 20, None) == -1
+    assert gp(1, 4, 2, dummy, 3, dummy, 4, 2, info, out, dummy, 1 << 20, None) == -5
+    assert gp(1, 4, 2, dummy, 4, dummy, 4, 2, info, None, dummy, 1 << 20, None) == -10
+    assert gp(1, 4, 2, dummy, 4, dummy, 4, 2, info, out, dummy, 8, None) == -12
 
 
 def test_profile_class_validation(lib):

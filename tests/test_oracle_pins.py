@@ -362,3 +362,76 @@ def test_info_matches_leading_minors(j0):
     first_bad = next(k for k, m in enumerate(minors, start=1) if m <= 0)
     _, info = oracle.potrf(A.astype(np.float64))
     assert info == first_bad == j0 + 1
+
+
+# ------------------------------------------- forward solve, GP likelihood ---
+# JAXMg paper, "Research Impact Statement", "Cholesky solve (potrs)": the
+# Gaussian-process marginal log-likelihood -1/2 r^T A^-1 r - 1/2 log det A -
+# (N/2) log 2 pi, r = y - m.
+
+@pytest.mark.parametrize("n,seed", [(1, 0), (7, 1), (50, 2), (200, 3)])
+def test_gp_loglik_matches_scipy_multivariate_normal(n, seed):
+    """scipy's multivariate normal log-density (computed through an eigen-
+    decomposition of the covariance) is the same quantity."""
+    import scipy.stats
+    rng = np.random.default_rng(seed)
+    G = rng.standard_normal((n, n))
+    A = G @ G.T / n + 0.3 * np.eye(n)
+    m = rng.standard_normal(n)
+    ys = rng.standard_normal((n, 3))
+    v, info = oracle.gp_loglik(A, ys - m[:, None])
+    assert info == 0
+    ref = scipy.stats.multivariate_normal(mean=m, cov=A).logpdf(ys.T)
+    np.testing.assert_allclose(v, np.atleast_1d(ref), rtol=1e-11, atol=1e-11)
+
+
+def test_gp_loglik_diagonal_closed_form():
+    rng = np.random.default_rng(4)
+    n = 300
+    d = 0.1 + rng.random(n)
+    r = rng.standard_normal((n, 2))
+    v, info = oracle.gp_loglik(np.diag(d), r)
+    ref = -0.5 * (r ** 2 / d[:, None]).sum(0) - 0.5 * np.log(d).sum() - 0.5 * n * np.log(2 * np.pi)
+    np.testing.assert_allclose(v, ref, rtol=1e-13)
+
+
+def test_gp_loglik_one_point():
+    """N = 1: -r^2 / (2 a) - log(a) / 2 - log(2 pi) / 2 exactly."""
+    v, info = oracle.gp_loglik(np.array([[4.0]]), np.array([2.0]))
+    assert info == 0 and abs(v - (-0.5 - 0.5 * np.log(4.0) - 0.5 * np.log(2 * np.pi))) < 1e-15
+
+
+def test_gp_loglik_not_positive_definite():
+    A = np.array([[1.0, 2.0], [2.0, 1.0]])
+    v, info = oracle.gp_loglik(A, np.ones((2, 2)))
+    assert info == 2 and np.isnan(v).all()
+
+
+@pytest.mark.parametrize("cplx", [False, True])
+def test_forward_solve_exact_integers(cplx):
+    """Unit lower-triangular integer L and integer y: b = L y is exact, so the
+    substitution must return y bit for bit."""
+    rng = np.random.default_rng(12)
+    n = 30
+    L = int_lower(n, rng, cplx, diag_max=1).astype(np.complex128 if cplx else np.float64)
+    y = rng.integers(-4, 5, size=(n, 2)).astype(np.float64)
+    if cplx:
+        y = y + 1j * rng.integers(-4, 5, size=(n, 2))
+    b = L @ y
+    np.testing.assert_array_equal(oracle.forward_solve(L, b), y)
+
+
+def test_forward_solve_matches_scipy_and_keeps_input():
+    import scipy.linalg
+    rng = np.random.default_rng(13)
+    n = 80
+    A = random_spd(n, 3, False, delta=0.2)
+    L, info = oracle.potrf(A)
+    for b in (rng.standard_normal((n, 1)), rng.standard_normal(n), rng.standard_normal((n, 4))):
+        b0 = b.copy()
+        y = oracle.forward_solve(L, b)
+        assert np.array_equal(b, b0)  # the caller's array is never written
+        ref = scipy.linalg.solve_triangular(L, b, lower=True)
+        np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+        x = oracle.potrs(L, b)
+        assert np.array_equal(b, b0)
