@@ -12,6 +12,11 @@ A = G G^T / N + 0.05 I (G iid N(0,1), seeded), B iid N(0,1).
 
 TFLOP/s = (N^3/3 + 2 N^2 N_RHS) / step time (x4 for complex: real-equivalent).
 
+With --workload gp a step is instead the factorization plus the Gaussian-
+process marginal log-likelihood of the N_RHS columns of B taken as residuals
+(forward substitution and a per-column reduction);
+TFLOP/s = (N^3/3 + N^2 N_RHS) / step time.
+
 Printed: one JSON line with the metric, the roofline of the dominant kernel
 (the trailing update A22 -= L21 L21^H, timed live with HIP events around each
 launch on its stream) and the CPU oracle timed on a bounded sample of the same
@@ -49,6 +54,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-check", action="store_true", help="skip the backward-error check of the last step")
+    p.add_argument("--workload", choices=("solve", "gp"), default="solve",
+                   help="solve (default): potrf + logdet + potrs; gp: potrf + the Gaussian-process marginal "
+                        "log-likelihood of the N_RHS residual columns (forward substitution + reduction)")
     return p.parse_args()
 
 
@@ -75,8 +83,12 @@ def main():
     dt, n, nrhs, T = cfg["dtype"], cfg["n"], cfg["nrhs"], cfg["T_A"]
     cplx = dt in ("c64", "c128")
     fmul = 4.0 if cplx else 1.0
+    gp = args.workload == "gp"
+    if gp and cplx:
+        print(json.dumps({"error": "the Gaussian-process likelihood is defined for real types"}), flush=True)
+        return 2
     flops_potrf = fmul * n**3 / 3.0
-    flops_potrs = fmul * 2.0 * n * n * nrhs
+    flops_potrs = fmul * (1.0 if gp else 2.0) * n * n * nrhs  # gp: forward substitution only
     flops = flops_potrf + flops_potrs
 
     t0 = time.time()
@@ -89,6 +101,7 @@ def main():
     work = spd.workspace(A.dtype, n, nrhs, T)
     info = torch.zeros(1, dtype=torch.int32, device="cuda")
     ldbuf = torch.zeros(1, dtype=torch.float64, device="cuda")
+    gpout = torch.zeros(nrhs, dtype=torch.float64, device="cuda")
     stream = torch.cuda.current_stream()
 
     def restore():
@@ -99,10 +112,13 @@ def main():
         ev[0].record(stream)
         spd.potrf(A, T, info=info, work=work)
         ev[1].record(stream)
-        if cfg["logdet"]:
+        if cfg["logdet"] and not gp:
             spd.logdet(A, info, out=ldbuf)
         ev[2].record(stream)
-        spd.potrs(A, B, T, info=info, work=work)
+        if gp:
+            spd.gp_loglik(A, B, T, info=info, work=work, out=gpout)
+        else:
+            spd.potrs(A, B, T, info=info, work=work)
         ev[3].record(stream)
 
     def events():
@@ -139,7 +155,22 @@ def main():
     log(f"[bench] steps: {', '.join(f'{x:.2f}' for x in step_ms)} ms; info={status}")
 
     check = None
-    if not args.no_check:
+    if not args.no_check and gp:
+        # normwise backward error of the forward substitution L Y = R, with the
+        # computed factor, in double on the GPU
+        Lw = torch.tril(A).to(torch.float64)
+        Yw, Rw = B.to(torch.float64), B0.to(torch.float64)
+        r = Rw - Lw @ Yw
+        eta = (r.abs().amax(dim=0) / (Lw.abs().sum(dim=1).max() * Yw.abs().amax(dim=0) + Rw.abs().amax(dim=0))).max()
+        eps = 2.0**-52 if dt == "f64" else 2.0**-23
+        finite = bool(torch.isfinite(gpout).all().item())
+        check = {"forward_backward_error": float(eta.item()), "bound_64_n_eps": 64 * n * eps,
+                 "loglik_first": float(gpout[0].item()), "ok": bool(eta.item() <= 64 * n * eps and status == 0
+                                                                   and finite)}
+        del Lw, Yw, Rw, r
+        log(f"[bench] forward-substitution backward error {check['forward_backward_error']:.3e} "
+            f"(bound {check['bound_64_n_eps']:.3e}); loglik[0] = {check['loglik_first']:.6f}")
+    elif not args.no_check:
         # normwise backward error of the last step's X, residual in double on the GPU
         wd = torch.complex128 if cplx else torch.float64
         Aw, Xw, Bw = A0.to(wd), B.to(wd), B0.to(wd)
@@ -171,10 +202,15 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(A0, B0, n, nrhs, fmul, args.cpu_seconds)
+        cpu = cpu_baseline(A0, B0, n, nrhs, fmul, args.cpu_seconds, gp)
 
+    metric = ("GP marginal log-likelihood (potrf + forward substitution) TFLOP/s, fp64 N=32768, 1 MI355X" if gp
+              else "potrf+potrs TFLOP/s and % of MFMA peak, fp64 N=32768, 1 MI355X")
+    workload = (f"{dt} Gaussian-process log-likelihood N={n}, {nrhs} residual columns, T_A={T}, "
+                f"A = G G^H/N + {cfg['delta']} I, seed {args.seed}" if gp else
+                f"{dt} SPD solve N={n} N_RHS={nrhs} T_A={T}, A = G G^H/N + {cfg['delta']} I, seed {args.seed}")
     out = {
-        "metric": "potrf+potrs TFLOP/s and % of MFMA peak, fp64 N=32768, 1 MI355X",
+        "metric": metric,
         "value": value,
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -186,13 +222,13 @@ def main():
         "vs_baseline": None,
         "dtype": dt,
         "data": "synthetic",
-        "config": {"workload": f"{dt} SPD solve N={n} N_RHS={nrhs} T_A={T}, A = G G^H/N + {cfg['delta']} I, "
-                               f"seed {args.seed}", "n": n, "n_rhs": nrhs, "T_A": T, "logdet": cfg["logdet"]},
+        "config": {"workload": workload, "n": n, "n_rhs": nrhs, "T_A": T, "logdet": cfg["logdet"] or gp},
         "pct_of_peak": 100.0 * value / peak,
         "potrf_tflops": potrf_tf,
         "potrf_pct_of_peak": 100.0 * potrf_tf / peak,
-        "phase_ms": {"potrf": float(np.mean(potrf_ms)), "logdet": float(np.mean(logdet_ms)),
-                     "potrs": float(np.mean(potrs_ms))},
+        "phase_ms": ({"potrf": float(np.mean(potrf_ms)), "gp_loglik": float(np.mean(potrs_ms))} if gp else
+                     {"potrf": float(np.mean(potrf_ms)), "logdet": float(np.mean(logdet_ms)),
+                      "potrs": float(np.mean(potrs_ms))}),
         "wall_ms_per_step_incl_restore": 1e3 * wall / args.steps,
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -202,10 +238,12 @@ def main():
     return 0 if (check is None or check["ok"]) else 1
 
 
-def cpu_baseline(A0, B0, n, nrhs, fmul, target_s):
+def cpu_baseline(A0, B0, n, nrhs, fmul, target_s, gp=False):
     """The CPU oracle, as it stands, on the leading principal block of the same
     matrix (and the matching rows of B): a bounded sample sized for about
-    ``target_s`` seconds, scaled to TFLOP/s with the same flop formula."""
+    ``target_s`` seconds, scaled to TFLOP/s with the same flop formula.  For
+    the likelihood workload the oracle's own definition (a full solve and
+    log det) is what runs."""
     import numpy as np
 
     import oracle
@@ -214,6 +252,9 @@ def cpu_baseline(A0, B0, n, nrhs, fmul, target_s):
         a = A0[:m, :m].cpu().numpy()
         b = B0[:m, :].cpu().numpy()
         t = time.perf_counter()
+        if gp:
+            _, info = oracle.gp_loglik(a, b)
+            return time.perf_counter() - t, info
         l, info = oracle.potrf(a)
         oracle.potrs(l, b)
         oracle.logdet(l)
@@ -225,10 +266,11 @@ def cpu_baseline(A0, B0, n, nrhs, fmul, target_s):
     m = max(256, min(n, (m // 256) * 256))
     log(f"[bench] cpu oracle: {m0} took {t0:.2f} s; sample size {m}")
     t, info = run(m)
-    fl = fmul * (m**3 / 3.0 + 2.0 * m * m * nrhs)
+    fl = fmul * (m**3 / 3.0 + (1.0 if gp else 2.0) * m * m * nrhs)
+    what = "Gaussian-process log-likelihood by its definition" if gp else "potrf + potrs + logdet"
     return {"value": fl / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"leading {m} x {m} principal block of the same A with the first {m} rows of all "
-                      f"{nrhs} right-hand sides (potrf + potrs + logdet), {t:.2f} s",
+                      f"{nrhs} right-hand sides ({what}), {t:.2f} s",
             "seconds": t}
 
 
