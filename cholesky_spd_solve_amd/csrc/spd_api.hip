@@ -555,24 +555,37 @@ struct Solver {
         return 0;
     }
 
-    // kw: the panel's true width (kp is it rounded up), for the flop count
-    static int syrk(int64_t m, const E *W, int64_t ldw, int64_t kp, int64_t kw, E *C, int64_t ldc, int jt_end,
+    // kw: the panel's true width (kp is it rounded up), for the flop count;
+    // cols > 0: only the first cols columns of C (a multiple of 128)
+    static int syrk(int64_t m, const E *W, int64_t ldw, int64_t kp, int64_t kw, E *C, int64_t ldc, int64_t cols,
                     const int *info, hipStream_t s)
     {
         if (m <= 0)
             return 0;
-        const int64_t w = jt_end > 0 ? std::min<int64_t>(m, jt_end * syrk_bm()) : m;  // columns of C updated
+        const int64_t w = cols > 0 ? std::min<int64_t>(m, cols) : m;  // columns of C updated
         ProfScope ps(PROF_SYRK, FMUL * (double)w * (2.0 * m - w + 1.0) * (double)kw, s);
-        // slice depth: 16 for the large early steps, 8 below (more
-        // workgroups in flight per byte of LDS; measured better for m < ~24k)
-        if constexpr (CPLX)
-            return syrk_cfg<64, 16, 2, 2>(m, W, ldw, kp, C, ldc, jt_end, info, s);
-        else if constexpr (sizeof(R) == 4)  // a 16-deep slice is one 16-byte load per thread
-            return syrk_cfg<128, 16, 2, 4>(m, W, ldw, kp, C, ldc, jt_end, info, s);
-        else if (m >= 24576)
-            return syrk_cfg<128, 16, 2, 4>(m, W, ldw, kp, C, ldc, jt_end, info, s);
-        else
-            return syrk_cfg<128, 8, 2, 4>(m, W, ldw, kp, C, ldc, jt_end, info, s);
+        auto jt = [&](int64_t bm) { return cols > 0 ? (int)(cols / bm) : 0; };
+        if constexpr (CPLX) {
+            return syrk_cfg<64, 16, 2, 2>(m, W, ldw, kp, C, ldc, jt(64), info, s);
+        } else {
+            // Launches with fewer 128-row tiles than two per CU take 64-row
+            // tiles: one 128 x 128 x T tile is a fixed ~55 us of a CU's
+            // matrix-core time, so a small update finishes sooner on four times
+            // as many workgroups with a quarter of the work each.
+            const int64_t t128 = cdiv(m, 128);
+            const int64_t n128 = cols > 0 ? std::min<int64_t>(cols / 128, t128) * t128 : t128 * (t128 + 1) / 2;
+            if (n128 < 512)
+                return syrk_cfg<64, 16, 2, 2>(m, W, ldw, kp, C, ldc, jt(64), info, s);
+            if constexpr (sizeof(R) == 4) {  // a 16-deep slice is one 16-byte load per thread
+                return syrk_cfg<128, 16, 2, 4>(m, W, ldw, kp, C, ldc, jt(128), info, s);
+            } else {
+                // slice depth: 16 for the large early steps, 8 below (more
+                // workgroups in flight per byte of LDS; measured better for m < ~24k)
+                if (m >= 24576)
+                    return syrk_cfg<128, 16, 2, 4>(m, W, ldw, kp, C, ldc, jt(128), info, s);
+                return syrk_cfg<128, 8, 2, 4>(m, W, ldw, kp, C, ldc, jt(128), info, s);
+            }
+        }
     }
 
     template <int BM, int BN, int KB, int WM, int WN, bool PT, bool VEC>
@@ -770,7 +783,7 @@ struct Solver {
         hipStream_t sl = la.look;
         SPD_TRY(diag_panel(n, A, lda, T, 0, Inv, Wb[0], info, sl));
         SPD_TRY(la.record(la.ev_panel, sl));
-        const int jt = (int)(T / syrk_bm()), kp = (int)align_up(T, SYRK_KP);
+        const int kp = (int)align_up(T, SYRK_KP);
         for (int64_t k = 0; k + 1 < nt; ++k) {
             const int64_t c0 = k * T, m = n - c0 - T, ldw = align_up(m, SYRK_LDW);
             E *Wk = Wb[k % 2];
@@ -778,7 +791,7 @@ struct Solver {
             if (k > 0)
                 SPD_TRY(la.wait(sl, la.ev_rest));  // update of step k-1 done
             // tile column k+1 of the trailing matrix, then diagonal tile and panel k+1
-            SPD_TRY(syrk(m, Wk, ldw, kp, T, A + (c0 + T) * (1 + lda), lda, jt, info, sl));
+            SPD_TRY(syrk(m, Wk, ldw, kp, T, A + (c0 + T) * (1 + lda), lda, T, info, sl));
             SPD_TRY(diag_panel(n, A, lda, T, c0 + T, Inv, Wb[(k + 1) % 2], info, sl));
             SPD_TRY(la.record(la.ev_panel, sl));
             // the rest of the trailing matrix, beyond tile column k+1
