@@ -588,7 +588,7 @@ struct Solver {
         }
     }
 
-    template <int BM, int BN, int KB, int WM, int WN, bool PT, bool VEC>
+    template <int BM, int BN, int KB, int WM, int WN, bool PT, bool VEC, bool STORE = false>
     static int rect_cfg(const E *P, int64_t ldp, const E *Q, int64_t ldq, E *C, int64_t ldc, int64_t m,
                         int64_t n, int64_t kp, int64_t kvalid, const int *info, hipStream_t s)
     {
@@ -608,8 +608,8 @@ struct Solver {
         a.ntiles = a.tiles_m * (int)cdiv(n, BN);
         a.info = info;
         const dim3 grid((unsigned)a.ntiles), block(64 * WM * WN);
-        SPD_VALIDATE((check_rect<R, BM, BN, KB, WM, WN, PT, VEC>(a, grid, g_chk)));
-        rect_kernel<R, BM, BN, KB, WM, WN, PT, VEC><<<grid, block, 0, s>>>(a);
+        SPD_VALIDATE((check_rect<R, BM, BN, KB, WM, WN, PT, VEC, STORE>(a, grid, g_chk)));
+        rect_kernel<R, BM, BN, KB, WM, WN, PT, VEC, 1, STORE><<<grid, block, 0, s>>>(a);
         SPD_CHECK_LAUNCH("rect_kernel");
         return 0;
     }
@@ -728,20 +728,43 @@ struct Solver {
         E *P = D + tk;  // m x tk panel
         const int64_t ldw = align_up(m, SYRK_LDW), kp = align_up(tk, SYRK_KP);
         ProfScope ps(PROF_PANEL, FMUL * (double)m * tk * tk, s);
-        Gemm g;  // Wk = P inv(L_kk)^H
-        g.A = P;
-        g.lda = lda;
-        g.B = Inv;
-        g.ldb = T;
-        g.C = Wk;
-        g.ldc = ldw;
-        g.m = m;
-        g.n = tk;
-        g.k = tk;
-        g.kmode = KM_END_BY_J;
-        g.info = info;
-        g.small = true;  // lean tiles: this product shares the GPU with the trailing update
-        SPD_TRY((gemm<R, CPLX>(NT, g, s)));
+        bool done = false;
+        if constexpr (!CPLX) {
+            if (T % RECT_LDQ == 0 && tk == T && rect_usable(lda)) {
+                // Wk = P inv(L_kk)^T on the block-update kernel (C = P Q^T with
+                // Q = inv(L_kk), ld T): more, shorter workgroups than the general
+                // product, which matters in the late steps where this product is
+                // on the critical path
+                const bool vec = rect_vec(A, lda, T);
+                if (m >= 16384)
+                    SPD_TRY((vec ? rect_cfg<64, 128, (sizeof(R) == 8 ? 16 : 32), 2, 4, false, true, true>(
+                                       P, lda, Inv, T, Wk, ldw, m, tk, tk, tk, info, s)
+                                 : rect_cfg<64, 128, (sizeof(R) == 8 ? 16 : 32), 2, 4, false, false, true>(
+                                       P, lda, Inv, T, Wk, ldw, m, tk, tk, tk, info, s)));
+                else
+                    SPD_TRY((vec ? rect_cfg<32, 128, 32, 1, 4, false, true, true>(P, lda, Inv, T, Wk, ldw, m, tk, tk, tk,
+                                                                                 info, s)
+                                 : rect_cfg<32, 128, 32, 1, 4, false, false, true>(P, lda, Inv, T, Wk, ldw, m, tk, tk,
+                                                                                  tk, info, s)));
+                done = true;
+            }
+        }
+        if (!done) {
+            Gemm g;  // Wk = P inv(L_kk)^H
+            g.A = P;
+            g.lda = lda;
+            g.B = Inv;
+            g.ldb = T;
+            g.C = Wk;
+            g.ldc = ldw;
+            g.m = m;
+            g.n = tk;
+            g.k = tk;
+            g.kmode = KM_END_BY_J;
+            g.info = info;
+            g.small = true;  // lean tiles: this product shares the GPU with the trailing update
+            SPD_TRY((gemm<R, CPLX>(NT, g, s)));
+        }
         SPD_TRY(zero2d<E>(Wk + m, ldw, ldw - m, kp, s));
         SPD_TRY(zero2d<E>(Wk + tk * ldw, ldw, m, kp - tk, s));
         SPD_TRY(copy2d<E>(P, lda, Wk, ldw, m, tk, info, s));

@@ -215,7 +215,7 @@ static bool check_syrk(const SyrkArgs &p, dim3 grid, Checker &c)
 // Replay of rect_kernel (spd_rect.hpp): the P loads (whole vectors on the
 // fast path, element by element with the row and column masks otherwise), the
 // unmasked Q vectors, and the epilogue's read-modify-write of C.
-template <typename R, int BM, int BN, int KB, int WM, int WN, bool PT, bool VEC>
+template <typename R, int BM, int BN, int KB, int WM, int WN, bool PT, bool VEC, bool STORE = false>
 static bool check_rect(const RectArgs &p, dim3 grid, Checker &c)
 {
     constexpr int NT = 64 * WM * WN;
@@ -285,7 +285,7 @@ static bool check_rect(const RectArgs &p, dim3 grid, Checker &c)
                         const int i = ib + fi * 16 + li, j = jb + fj * 16 + acc_row<R>(lk, q);
                         if (whole || (i0 + i < p.m && j0 + j < p.n)) {
                             R *dst = Ct + i + (int64_t)j * p.ldc;
-                            if (!c.access(dst, sizeof(R), false, kn, b, tid) ||
+                            if ((!STORE && !c.access(dst, sizeof(R), false, kn, b, tid)) ||
                                 !c.access(dst, sizeof(R), true, kn, b, tid))
                                 return false;
                         }

@@ -83,7 +83,8 @@ struct RectLoad {
 // same either way, so results do not depend on the leading dimension.
 // DEPTH: slices of P and Q in flight from memory (1: the next one; 2: the
 // next two, in two register sets, for more bytes in flight per CU).
-template <typename R, int BM, int BN, int KB, int WM, int WN, bool PT, bool VEC, int DEPTH = 1>
+// STORE: C = P Q^T (C is not read) instead of C -= P Q^T.
+template <typename R, int BM, int BN, int KB, int WM, int WN, bool PT, bool VEC, int DEPTH = 1, bool STORE = false>
 __global__ void __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)))
 rect_kernel(const RectArgs p)
 {
@@ -240,9 +241,22 @@ rect_kernel(const RectArgs p)
             body(sl + 1, std::integral_constant<int, 1>());
     }
 
-    // epilogue: C -= acc, one 16-row block at a time
+    // epilogue: C -= acc (or C = acc), one 16-row block at a time
     R *__restrict__ Ct = (R *)p.C + i0 + (int64_t)j0 * p.ldc;
     const bool whole = prows && (j0 + BN <= p.n);
+    if constexpr (STORE) {
+#pragma unroll
+        for (int fi = 0; fi < FM; ++fi)
+#pragma unroll
+            for (int fj = 0; fj < FN; ++fj)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int i = ib + fi * 16 + li, j = jb + fj * 16 + acc_row<R>(lk, q);
+                    if (whole || (i0 + i < p.m && j0 + j < p.n))
+                        Ct[i + (int64_t)j * p.ldc] = acc[fi][fj][q];
+                }
+        return;
+    }
 #pragma unroll
     for (int fi = 0; fi < FM; ++fi) {
         const int i = ib + fi * 16 + li;
