@@ -269,7 +269,7 @@ static int set_info(int *info, hipStream_t s)
 //                 L21 of two consecutive steps (potrf) / merge temporaries (both)
 //            TMP  max(T*T, T*n_rhs)   one block row of the right-hand side
 struct Layout {
-    int64_t T, nt, inv, w, wsz, tmp, q, ldq, kq, qsz, gf, gb, part, total;  // offsets / sizes in elements
+    int64_t T, nt, inv, w, wsz, tmp, ctr, q, ldq, kq, qsz, gf, gb, part, total;  // offsets / sizes in elements
 };
 
 // The trailing-update panel W is stored with its leading dimension rounded up
@@ -295,7 +295,9 @@ static Layout make_layout(int64_t n, int64_t n_rhs, int64_t T_A, int64_t esize)
     L.w = align_up(L.nt * L.T * L.T, al);
     L.wsz = align_up(align_up(n, SYRK_LDW) * align_up(L.T, SYRK_KP), al);
     L.tmp = L.w + 2 * L.wsz;  // two panel buffers: step k's and step k+1's
-    L.q = L.tmp + align_up(std::max(L.T * L.T, L.T * std::max<int64_t>(n_rhs, 1)), al);
+    // ctr: the fused leaf + panel launch's workgroup counter (one int)
+    L.ctr = L.tmp + align_up(std::max(L.T * L.T, L.T * std::max<int64_t>(n_rhs, 1)), al);
+    L.q = L.ctr + al;
     L.ldq = align_up(n_rhs, RECT_LDQ);
     L.kq = align_up(L.T, RECT_KB);
     L.qsz = L.ldq * L.kq;  // two buffers, adjacent
@@ -412,6 +414,8 @@ struct Solver {
         const int64_t grid = ntiles * p.lpt;
         if (grid <= 0)
             return 0;
+        p.prows = 0;
+        p.ctr = nullptr;
         SPD_VALIDATE((check_leaf<R, CPLX>(p, (unsigned)grid, g_chk)));
         if constexpr (CPLX)
             leaf_kernel<R, CPLX><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p);
@@ -419,6 +423,37 @@ struct Solver {
             leaf16_kernel<R><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p);
         SPD_CHECK_LAUNCH("leaf_kernel");
         return 0;
+    }
+
+    // Real types: factor and invert the lb x lb leaf at D and solve the prows
+    // rows below it, P <- P inv(L_leaf)^T in place, in one launch.
+    static int leaf_panel(E *D, int64_t lda, int64_t lb, int64_t prows, E *Inv, int64_t ldi, int *info, int *ctr,
+                          int64_t col0, hipStream_t s)
+    {
+        if constexpr (CPLX) {
+            g_last_error = "fused leaf and panel launch is for real types";
+            return SPD_ERR_HIP;
+        } else {
+            LeafArgs p;
+            p.A = D;
+            p.lda = lda;
+            p.Inv = Inv;
+            p.ldi = ldi;
+            p.sInv = 0;
+            p.n = (int)lb;
+            p.T = (int)lb;
+            p.lpt = 1;
+            p.factor = 1;
+            p.info = info;
+            p.col0 = (int)col0;
+            p.prows = (int)prows;
+            p.ctr = ctr;
+            const int64_t grid = 1 + cdiv(prows, LEAF);
+            SPD_VALIDATE((check_leaf<R, CPLX>(p, (unsigned)grid, g_chk, true)));
+            leaf16_kernel<R, true><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p);
+            SPD_CHECK_LAUNCH("leaf16_kernel (leaf + panel)");
+            return 0;
+        }
     }
 
     // Complete inv(L_tt) from its inverted leaves for `ntiles` tiles of size tk
@@ -676,7 +711,7 @@ struct Solver {
     // reads (leading dimension m rounded up to SYRK_LDW, width tk rounded up to
     // SYRK_KP) and copy it back into A.  All on stream s.
     static int diag_panel(int64_t n, E *A, int64_t lda, int64_t T, int64_t c0, E *Inv, E *Wk, int *info,
-                          hipStream_t s)
+                          int *ctr, hipStream_t s)
     {
         const int64_t tk = std::min(T, n - c0);
         E *D = A + c0 + c0 * lda;
@@ -685,25 +720,33 @@ struct Solver {
             for (int64_t b0 = 0; b0 < tk; b0 += LEAF) {
                 const int64_t lb = std::min<int64_t>(LEAF, tk - b0);
                 E *Db = D + b0 + b0 * lda;
-                SPD_TRY(leaves(Db, lda, lb, lb, Inv + b0 * (1 + T), T, 0, 1, true, info, c0 + b0, s));
                 const int64_t r = tk - b0 - lb;
-                if (r <= 0)
-                    continue;
                 E *P = Db + lb;  // r x lb below the leaf
-                Gemm g;          // P <- P inv(Lb)^H, in place (one tile column)
-                g.A = P;
-                g.lda = lda;
-                g.B = Inv + b0 * (1 + T);
-                g.ldb = T;
-                g.C = P;
-                g.ldc = lda;
-                g.m = r;
-                g.n = lb;
-                g.k = lb;
-                g.kmode = KM_END_BY_J;
-                g.info = info;
-                g.inplace = true;
-                SPD_TRY((gemm<R, CPLX>(NT, g, s)));
+                if constexpr (!CPLX) {
+                    // the leaf and P <- P inv(Lb)^T in one launch
+                    SPD_TRY(leaf_panel(Db, lda, lb, std::max<int64_t>(r, 0), Inv + b0 * (1 + T), T, info, ctr, c0 + b0,
+                                       s));
+                    if (r <= 0)
+                        continue;
+                } else {
+                    SPD_TRY(leaves(Db, lda, lb, lb, Inv + b0 * (1 + T), T, 0, 1, true, info, c0 + b0, s));
+                    if (r <= 0)
+                        continue;
+                    Gemm g;  // P <- P inv(Lb)^H, in place (one tile column)
+                    g.A = P;
+                    g.lda = lda;
+                    g.B = Inv + b0 * (1 + T);
+                    g.ldb = T;
+                    g.C = P;
+                    g.ldc = lda;
+                    g.m = r;
+                    g.n = lb;
+                    g.k = lb;
+                    g.kmode = KM_END_BY_J;
+                    g.info = info;
+                    g.inplace = true;
+                    SPD_TRY((gemm<R, CPLX>(NT, g, s)));
+                }
                 Gemm u;  // rest of the tile: lower part of D22 -= P P^H
                 u.A = P;
                 u.lda = lda;
@@ -788,13 +831,16 @@ struct Solver {
         const Layout L = make_layout(n, 0, T_A, sizeof(E));
         const int64_t T = L.T, nt = L.nt;
         E *Inv = (E *)work + L.inv;  // inverse of the current diagonal tile, ld T
+        int *ctr = (int *)((E *)work + L.ctr);
+        if constexpr (!CPLX)
+            SPD_TRY(set_info(ctr, s));
         E *Wb[2] = {(E *)work + L.w, (E *)work + L.w + L.wsz};
         SPD_TRY(zero2d<E>(Inv, T, T, T, s));
         const bool lookahead = lookahead_enabled() && (T % syrk_bm() == 0) && nt >= 3;
         if (!lookahead) {
             for (int64_t c0 = 0; c0 < n; c0 += T) {
                 const int64_t tk = std::min(T, n - c0), m = n - c0 - tk;
-                SPD_TRY(diag_panel(n, A, lda, T, c0, Inv, Wb[0], info, s));
+                SPD_TRY(diag_panel(n, A, lda, T, c0, Inv, Wb[0], info, ctr, s));
                 if (m > 0)
                     SPD_TRY(syrk(m, Wb[0], align_up(m, SYRK_LDW), align_up(tk, SYRK_KP), tk,
                                  A + (c0 + tk) * (1 + lda), lda, 0, info, s));
@@ -804,7 +850,7 @@ struct Solver {
         Lookahead la;
         SPD_TRY(la.begin(s));
         hipStream_t sl = la.look;
-        SPD_TRY(diag_panel(n, A, lda, T, 0, Inv, Wb[0], info, sl));
+        SPD_TRY(diag_panel(n, A, lda, T, 0, Inv, Wb[0], info, ctr, sl));
         SPD_TRY(la.record(la.ev_panel, sl));
         const int kp = (int)align_up(T, SYRK_KP);
         for (int64_t k = 0; k + 1 < nt; ++k) {
@@ -815,7 +861,7 @@ struct Solver {
                 SPD_TRY(la.wait(sl, la.ev_rest));  // update of step k-1 done
             // tile column k+1 of the trailing matrix, then diagonal tile and panel k+1
             SPD_TRY(syrk(m, Wk, ldw, kp, T, A + (c0 + T) * (1 + lda), lda, T, info, sl));
-            SPD_TRY(diag_panel(n, A, lda, T, c0 + T, Inv, Wb[(k + 1) % 2], info, sl));
+            SPD_TRY(diag_panel(n, A, lda, T, c0 + T, Inv, Wb[(k + 1) % 2], info, ctr, sl));
             SPD_TRY(la.record(la.ev_panel, sl));
             // the rest of the trailing matrix, beyond tile column k+1
             if (m > T)

@@ -295,31 +295,49 @@ static bool check_rect(const RectArgs &p, dim3 grid, Checker &c)
     return true;
 }
 
+// panel: the leaf + panel launch (leaf16_kernel<R, true>): every workgroup
+// factors the one leaf; workgroup 0 writes it and its inverse, workgroup
+// w >= 1 reads and writes rows [64(w-1), 64w) of the p.prows panel rows.
 template <typename R, bool CPLX>
-static bool check_leaf(const LeafArgs &p, unsigned grid, Checker &c)
+static bool check_leaf(const LeafArgs &p, unsigned grid, Checker &c, bool panel = false)
 {
     typedef typename Elem<R, CPLX>::type E;
-    const char *kn = "leaf_kernel";
+    const char *kn = panel ? "leaf16_kernel (leaf + panel)" : "leaf_kernel";
     if (p.info != nullptr && !c.access(p.info, 4, p.factor != 0, kn, 0, 0))
         return false;
+    if (panel && (p.ctr == nullptr || !c.access(p.ctr, 4, true, kn, 0, 0))) {
+        if (c.err.empty())
+            c.err = "leaf16_kernel (leaf + panel): no workgroup counter";
+        return false;
+    }
     for (unsigned g = 0; g < grid; ++g) {
         int64_t c0, ioff;
         int lb;
-        if (!leaf_geom(p, (int)g, c0, lb, ioff))
+        if (!leaf_geom(p, panel ? 0 : (int)g, c0, lb, ioff))
             continue;
         const E *A = (const E *)p.A + c0 + c0 * p.lda;
         const E *Inv = (const E *)p.Inv + ioff;
+        const bool writes_leaf = true;  // with panel, whichever workgroup finishes last
         for (int col = 0; col < lb; ++col)
             for (int r = 0; r < lb; ++r) {
                 if (r >= col) {
                     if (!c.access(A + r + (int64_t)col * p.lda, sizeof(E), false, kn, g, 0))
                         return false;
-                    if (p.factor && !c.access(A + r + (int64_t)col * p.lda, sizeof(E), true, kn, g, 0))
+                    if (writes_leaf && p.factor && !c.access(A + r + (int64_t)col * p.lda, sizeof(E), true, kn, g, 0))
                         return false;
                 }
-                if (!c.access(Inv + r + (int64_t)col * p.ldi, sizeof(E), true, kn, g, 0))
+                if (writes_leaf && !c.access(Inv + r + (int64_t)col * p.ldi, sizeof(E), true, kn, g, 0))
                     return false;
             }
+        if (panel && g > 0) {
+            const E *Pb = A + lb + (int64_t)(g - 1) * LEAF;
+            const int prow = std::min<int>(LEAF, p.prows - (int)(g - 1) * LEAF);
+            for (int col = 0; col < lb; ++col)
+                for (int r = 0; r < prow; ++r)
+                    if (!c.access(Pb + r + (int64_t)col * p.lda, sizeof(E), false, kn, g, 0) ||
+                        !c.access(Pb + r + (int64_t)col * p.lda, sizeof(E), true, kn, g, 0))
+                        return false;
+        }
     }
     return true;
 }

@@ -25,6 +25,8 @@ struct LeafArgs {
     int factor;     // 1: factor the leaf and invert it; 0: L is given, invert only
     int *info;      // factor mode: set to (col0 + first failing column + 1)
     int col0;       // global column of A[0, 0] (for info)
+    int prows;      // leaf + panel launch only: rows of the panel below the leaf
+    int *ctr;       // leaf + panel launch only: workgroup counter, 0 between launches
 };
 
 // Leaf handled by workgroup g: its first global column c0 (relative to the
@@ -375,7 +377,8 @@ __device__ void diag16(R (*S)[LDL], R (*X)[LDL], int o, int lb, int gcol, int *i
     diag16_pivot<R, FACTOR, 0>(a, s0, l0, bad);
     diag16_step<R, FACTOR, 0>(a, x, c, s0, l0, bad);
     if (FACTOR && bad >= 0 && lane == 0 && o + bad < lb) {
-        atomicCAS(info, 0, gcol + o + bad + 1);
+        if (info != nullptr)
+            atomicCAS(info, 0, gcol + o + bad + 1);
         *failed = 1;
     }
     if (lane < LB16) {
@@ -390,7 +393,17 @@ __device__ void diag16(R (*S)[LDL], R (*X)[LDL], int o, int lb, int gcol, int *i
 
 // At most 256 registers per lane, so that a leaf fits in the registers one
 // finishing trailing-update workgroup gives back.
-template <typename R>
+//
+// PANEL: one launch factors a single leaf and solves the panel below it,
+// L(i, leaf) = A(i, leaf) inv(L_leaf)^T for the p.prows rows that follow the
+// leaf.  Every workgroup factors and inverts the leaf in its own LDS (the same
+// bits); workgroup w >= 1 also multiplies rows [64(w-1), 64w) of the panel by
+// inv(L_leaf)^T in place.  L may only replace A's leaf once no workgroup still
+// has to read it, so each workgroup counts itself out on p.ctr when done and
+// the last one stores L and inv(L) and resets the counter (no workgroup waits
+// for another).  Only workgroup 0 records info.  The panel rows are loaded
+// together with the leaf.
+template <typename R, bool PANEL = false>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) leaf16_kernel(const LeafArgs p)
 {
     typedef typename AccT<R>::type V4;
@@ -402,23 +415,32 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) l
 
     int64_t c0, ioff;
     int lb;
-    if (!leaf_geom(p, (int)blockIdx.x, c0, lb, ioff))
+    const int w = PANEL ? (int)blockIdx.x : 0;  // panel block of this workgroup (0: none)
+    if (!leaf_geom(p, PANEL ? 0 : (int)blockIdx.x, c0, lb, ioff))
         return;
     R *A = (R *)p.A + c0 + c0 * p.lda;
     R *Inv = (R *)p.Inv + ioff;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int li = lane & 15, lk = lane >> 4;
     const int r = tid & (LEAF - 1), g = tid / LEAF;
+    int *const info = (w == 0) ? p.info : nullptr;
+    R *const Pb = A + lb + (int64_t)(w - 1) * LEAF;  // panel block w: rows lb + 64(w-1) + r
+    const int prow = p.prows - (w - 1) * LEAF;       // its rows that exist
 
-    // all loads of the leaf are in flight together (one memory round trip),
-    // and the status word is read alongside them
-    R v[LEAF / 4];
+    // all loads of the leaf (and of the panel block) are in flight together
+    // (one memory round trip), and the status word is read alongside them
+    R v[LEAF / 4], pv[PANEL ? LEAF / 4 : 1];
 #pragma unroll
     for (int k = 0; k < LEAF / 4; ++k) {
         const int c = g + 4 * k;
         v[k] = (r == c) ? R(1) : R(0);
         if (r < lb && c < lb && r >= c)
             v[k] = A[r + (int64_t)c * p.lda];
+        if constexpr (PANEL) {
+            pv[k] = R(0);
+            if (w > 0 && r < prow && c < lb)
+                pv[k] = Pb[r + (int64_t)c * p.lda];
+        }
     }
     if (p.info != nullptr && *p.info != 0)
         return;
@@ -446,9 +468,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) l
         const int o = b * LB16;
         if (wave == 0) {
             if (p.factor)
-                diag16<R, true>(S, X, o, lb, p.col0 + (int)c0, p.info, &failed);
+                diag16<R, true>(S, X, o, lb, p.col0 + (int)c0, info, &failed);
             else
-                diag16<R, false>(S, X, o, lb, p.col0 + (int)c0, p.info, &failed);
+                diag16<R, false>(S, X, o, lb, p.col0 + (int)c0, info, &failed);
         }
         __syncthreads();
         if (p.factor) {
@@ -499,12 +521,48 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) l
 
     if (failed)
         return;
-    // every LDS read first, then the global stores back to back
+    // L and inv(L) into registers first (every LDS read, then the global
+    // stores back to back; and the panel block may take S's place)
     R sv[LEAF / 4], xv[LEAF / 4];
 #pragma unroll
     for (int k = 0; k < LEAF / 4; ++k) {
         sv[k] = S[g + 4 * k][r];
         xv[k] = X[g + 4 * k][r];
+    }
+    if constexpr (PANEL) {
+        if (w > 0) {
+            // panel block B (rows of this workgroup) into S, then
+            // P = B inv(L)^T: wave v owns the 16-row block v, P(v, j) =
+            // sum_{k <= j} B(v, k) inv(L)(j, k) over 16 x 16 blocks
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < LEAF / 4; ++k)
+                S[g + 4 * k][r] = pv[k];
+            __syncthreads();
+#pragma unroll
+            for (int bj = 0; bj < NB; ++bj) {
+                V4 acc = {0, 0, 0, 0};
+                for (int bk = 0; bk <= bj; ++bk)
+                    acc = mma16<R>(&S[bk * LB16][wave * LB16], LDL, 1, &X[bk * LB16][bj * LB16], LDL, 1, acc);
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    const int rr = wave * LB16 + li, cc = bj * LB16 + acc_row<R>(lk, qq);
+                    if (rr < prow && cc < lb)
+                        Pb[rr + (int64_t)cc * p.lda] = acc[qq];
+                }
+            }
+        }
+        // count out; the last workgroup stores the leaf
+        __shared__ int last;
+        __syncthreads();
+        if (tid == 0) {
+            last = atomicAdd(p.ctr, 1) == (int)gridDim.x - 1;
+            if (last)
+                atomicExch(p.ctr, 0);
+        }
+        __syncthreads();
+        if (!last)
+            return;
     }
 #pragma unroll
     for (int k = 0; k < LEAF / 4; ++k) {
