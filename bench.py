@@ -42,6 +42,12 @@ PEAK = {  # MI355X published dense peaks, TFLOP/s
     "c64": 157.3,
 }
 HBM_PEAK_GBS = 8000.0
+# HBM bytes per trailing-update launch at the default workload (fp64 N=32768,
+# T_A=512), from FETCH_SIZE and WRITE_SIZE counter passes scaled by a plain
+# copy's reading (profiles/counters_syrk_f64_n32768_t512.md).  Valid for the
+# trailing-update kernels as they were when the counters were taken; set to
+# None when they change.
+SYRK_TRAFFIC_BYTES = {("f64", 32768, 512): 4.359e9}
 
 
 def parse():
@@ -194,7 +200,7 @@ def main():
         "peak": peak,
         "unit": "TFLOP/s",
         "frac": (syrk_achieved / peak) if syrk_achieved else None,
-        "traffic": None,
+        "traffic": SYRK_TRAFFIC_BYTES.get((dt, n, T)) if not gp else None,
         "launches": syrk_launches,
         "avg_launch_ms": syrk_avg_ms,
         "flops_per_launch": syrk_flops / max(syrk_launches, 1),
