@@ -47,7 +47,7 @@ HBM_PEAK_GBS = 8000.0
 # copy's reading (profiles/counters_syrk_f64_n32768_t512.md).  Valid for the
 # trailing-update kernels as they were when the counters were taken; set to
 # None when they change.
-SYRK_TRAFFIC_BYTES = {("f64", 32768, 512): 4.359e9}
+SYRK_TRAFFIC_BYTES = {("f64", 32768, 512): 4.398e9}
 
 
 def parse():
@@ -60,6 +60,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-check", action="store_true", help="skip the backward-error check of the last step")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only copy 1 GiB device to device (twice), for scaling HBM byte counters")
     p.add_argument("--workload", choices=("solve", "gp"), default="solve",
                    help="solve (default): potrf + logdet + potrs; gp: potrf + the Gaussian-process marginal "
                         "log-likelihood of the N_RHS residual columns (forward substitution + reduction)")
@@ -80,6 +82,22 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        # a plain copy of known size: 1 GiB read and 1 GiB written per copy
+        nbytes = 1 << 30
+        src = torch.ones(nbytes // 8, dtype=torch.float64, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        print(json.dumps({"copy_bytes": nbytes, "ms": ms, "read_plus_write_GBs": 2 * nbytes / ms / 1e6}), flush=True)
+        return 0
 
     import cholesky_spd_solve_amd as spd
     import spdgen
