@@ -17,6 +17,14 @@ process marginal log-likelihood of the N_RHS columns of B taken as residuals
 (forward substitution and a per-column reduction);
 TFLOP/s = (N^3/3 + N^2 N_RHS) / step time.
 
+With --workload sygst a step is the factorization B = L L^H (B the
+config's SPD matrix) plus the reduction of the generalized eigenproblem
+A v = w B v (--itype 1; 2 and 3 for A B v = w v, B A v = w v) to standard
+form, A symmetric indefinite (G + G^T)/sqrt(2N); TFLOP/s = (N^3/3 + N^3) /
+step time, N^3 being the reduction's conventional flop count; the roofline is
+that of the substitutions' block-update kernel (itype 1) or of the two
+triangular products (itypes 2, 3).
+
 Printed: one JSON line with the metric, the roofline of the dominant kernel
 (the trailing update A22 -= L21 L21^H, timed live with HIP events around each
 launch on its stream) and the CPU oracle timed on a bounded sample of the same
@@ -62,9 +70,11 @@ def parse():
     p.add_argument("--no-check", action="store_true", help="skip the backward-error check of the last step")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only copy 1 GiB device to device (twice), for scaling HBM byte counters")
-    p.add_argument("--workload", choices=("solve", "gp"), default="solve",
+    p.add_argument("--workload", choices=("solve", "gp", "sygst"), default="solve",
                    help="solve (default): potrf + logdet + potrs; gp: potrf + the Gaussian-process marginal "
-                        "log-likelihood of the N_RHS residual columns (forward substitution + reduction)")
+                        "log-likelihood of the N_RHS residual columns (forward substitution + reduction); "
+                        "sygst: potrf of B + reduction of the generalized eigenproblem (A, B) to standard form")
+    p.add_argument("--itype", type=int, choices=(1, 2, 3), default=1, help="problem type of --workload sygst")
     return p.parse_args()
 
 
@@ -111,6 +121,8 @@ def main():
     if gp and cplx:
         print(json.dumps({"error": "the Gaussian-process likelihood is defined for real types"}), flush=True)
         return 2
+    if args.workload == "sygst":
+        return bench_sygst(args, cfg)
     flops_potrf = fmul * n**3 / 3.0
     flops_potrs = fmul * (1.0 if gp else 2.0) * n * n * nrhs  # gp: forward substitution only
     flops = flops_potrf + flops_potrs
@@ -260,6 +272,146 @@ def main():
     }
     print(json.dumps(out), flush=True)
     return 0 if (check is None or check["ok"]) else 1
+
+
+def bench_sygst(args, cfg):
+    """potrf of B, then the reduction of (A, B) to standard form."""
+    import numpy as np
+    import torch
+
+    import cholesky_spd_solve_amd as spd
+    import spdgen
+
+    dt, n, T, itype = cfg["dtype"], cfg["n"], cfg["T_A"], args.itype
+    cplx = dt in ("c64", "c128")
+    fmul = 4.0 if cplx else 1.0
+    flops_potrf = fmul * n**3 / 3.0
+    flops_gst = fmul * float(n) ** 3
+    t0 = time.time()
+    log(f"[bench] generating sygst itype {itype}: {dt} N={n} T_A={T} seed={args.seed}")
+    B0 = spdgen.make_A(n, dt, cfg["delta"], args.seed, device="cuda")
+    H0 = spdgen.make_herm(n, dt, args.seed + 1, device="cuda")
+    torch.cuda.synchronize()
+    log(f"[bench] inputs ready in {time.time() - t0:.1f} s")
+    Lb = spdgen.to_colmajor(B0)
+    H = spdgen.to_colmajor(H0)
+    work = spd.workspace(Lb.dtype, n, 0, T)
+    gbytes = spd.sygst_workspace_size(H.dtype, itype, n, T)
+    gwork = torch.empty(max(gbytes, 1), dtype=torch.uint8, device="cuda")
+    info = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def restore():
+        Lb.copy_(B0)
+        H.copy_(H0)
+
+    def step(ev):
+        ev[0].record(stream)
+        spd.potrf(Lb, T, info=info, work=work)
+        ev[1].record(stream)
+        spd.sygst(itype, H, Lb, T, info=info, work=gwork)
+        ev[2].record(stream)
+
+    def events():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+
+    for w in range(args.warmup):
+        restore()
+        step(events())
+        torch.cuda.synchronize()
+        log(f"[bench] warmup {w + 1}/{args.warmup} done")
+    cls = spd.PROF_UPDATE if (itype == 1 and not cplx) else spd.PROF_SOLVE
+    spd.profile_enable(1 << cls)
+    spd.profile_read(cls)
+    evs = []
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        restore()
+        ev = events()
+        step(ev)
+        evs.append(ev)
+    torch.cuda.synchronize()
+    spd.profile_enable(0)
+    k_ms, k_launches, k_flops = spd.profile_read(cls)
+    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
+    potrf_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    gst_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    ms = float(np.mean(step_ms))
+    status = int(info.item())
+    log(f"[bench] steps: {', '.join(f'{x:.2f}' for x in step_ms)} ms; info={status}")
+
+    check = None
+    if not args.no_check:
+        # L C L^H = A (itype 1) or C = L^H A L (itypes 2, 3), in double on the GPU
+        wd = torch.complex128 if cplx else torch.float64
+        Lw = torch.tril(Lb).to(wd)
+        C = torch.tril(H, -1).to(wd)
+        C = C + C.mH + torch.diag_embed(torch.diagonal(H).real.to(wd))
+        Aw = H0.to(wd)
+        if itype == 1:
+            err = ((Lw @ C @ Lw.mH - Aw).abs().max() / Aw.abs().max()).item()
+        else:
+            err = ((C - Lw.mH @ Aw @ Lw).abs().max() / C.abs().max()).item()
+        eps = 2.0**-52 if dt in ("f64", "c128") else 2.0**-23
+        check = {"identity_error": float(err), "bound_64_n_eps": 64 * n * eps,
+                 "ok": bool(err <= 64 * n * eps and status == 0)}
+        del Lw, C, Aw
+        log(f"[bench] reduction identity error {err:.3e} (bound {64 * n * eps:.3e})")
+
+    peak = PEAK[dt]
+    avg = k_ms / max(k_launches, 1)
+    ach = (k_flops / k_launches) / (avg * 1e-3) / 1e12 if k_launches else None
+    roofline = {
+        "kernel": ("rect_kernel (substitution block update B_rows -= L_panel X_k)" if cls == spd.PROF_UPDATE
+                   else "gemm_kernel (triangular products P = A L, C = L^H P)"),
+        "bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
+        "frac": (ach / peak) if ach else None, "traffic": None, "launches": k_launches,
+        "avg_launch_ms": avg, "flops_per_launch": k_flops / max(k_launches, 1),
+    }
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_sygst(B0, H0, n, itype, fmul, args.cpu_seconds)
+    value = (flops_potrf + flops_gst) / (ms * 1e-3) / 1e12
+    out = {
+        "metric": f"generalized-eigenproblem reduction (potrf of B + sygst itype {itype}) TFLOP/s, 1 MI355X",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt,
+        "data": "synthetic",
+        "config": {"workload": f"{dt} reduction of A v = w B v type {itype}, N={n}, T_A={T}, "
+                               f"B = G G^H/N + {cfg['delta']} I, A = (G' + G'^H)/sqrt(2N), seed {args.seed}",
+                   "n": n, "T_A": T, "itype": itype},
+        "pct_of_peak": 100.0 * value / peak,
+        "phase_ms": {"potrf": float(np.mean(potrf_ms)), "sygst": float(np.mean(gst_ms))},
+        "sygst_tflops": flops_gst / (float(np.mean(gst_ms)) * 1e-3) / 1e12,
+        "roofline": roofline, "cpu_baseline": cpu, "check": check,
+    }
+    print(json.dumps(out), flush=True)
+    return 0 if (check is None or check["ok"]) else 1
+
+
+def cpu_baseline_sygst(B0, H0, n, itype, fmul, target_s):
+    """The CPU oracle on the leading principal blocks of B and A: potrf, then
+    the reduction by its definition; same flop formula as the GPU value."""
+    import oracle
+
+    def run(m):
+        b = B0[:m, :m].cpu().numpy()
+        a = H0[:m, :m].cpu().numpy()
+        t = time.perf_counter()
+        l, info = oracle.potrf(b)
+        oracle.sygst(itype, a, l)
+        return time.perf_counter() - t
+
+    m0 = min(n, 1024)
+    t0 = run(m0)
+    m = int(m0 * (target_s / max(t0, 1e-3)) ** (1.0 / 3.0))
+    m = max(256, min(n, (m // 256) * 256))
+    log(f"[bench] cpu oracle: {m0} took {t0:.2f} s; sample size {m}")
+    t = run(m)
+    fl = fmul * (m**3 / 3.0 + float(m) ** 3)
+    return {"value": fl / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"leading {m} x {m} principal blocks of the same B and A (potrf + reduction by its "
+                      f"definition), {t:.2f} s", "seconds": t}
 
 
 def cpu_baseline(A0, B0, n, nrhs, fmul, target_s, gp=False):

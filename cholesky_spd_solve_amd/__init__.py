@@ -32,9 +32,10 @@ DTYPE_CODE = {
     torch.complex128: SPD_C128,
 }
 SYMBOLS = ("spd_workspace_size", "spd_potrf", "spd_potrs", "spd_forward_solve", "spd_gp_loglik", "spd_logdet",
-           "spd_last_error", "spd_profile_enable", "spd_profile_read", "spd_debug_validate")
+           "spd_sygst_workspace_size", "spd_sygst", "spd_last_error", "spd_profile_enable", "spd_profile_read",
+           "spd_debug_validate")
 SPD_ERR_HIP, SPD_ERR_CHECK = 1, 2
-PROF_SYRK, PROF_PANEL, PROF_DIAG, PROF_SOLVE = 0, 1, 2, 3
+PROF_SYRK, PROF_PANEL, PROF_DIAG, PROF_SOLVE, PROF_UPDATE = 0, 1, 2, 3, 4
 
 _lock = threading.Lock()
 _lib = None
@@ -77,6 +78,10 @@ def load():
             lib.spd_gp_loglik.restype = i32
             lib.spd_logdet.argtypes = [i32, i64, vp, i64, vp, vp, vp]
             lib.spd_logdet.restype = i32
+            lib.spd_sygst_workspace_size.argtypes = [i32, i32, i64, i64]
+            lib.spd_sygst_workspace_size.restype = sz
+            lib.spd_sygst.argtypes = [i32, i32, i64, vp, i64, vp, i64, i64, vp, vp, sz, vp]
+            lib.spd_sygst.restype = i32
             lib.spd_last_error.argtypes = []
             lib.spd_last_error.restype = ctypes.c_char_p
             lib.spd_profile_enable.argtypes = [i32]
@@ -226,6 +231,32 @@ def logdet(L: torch.Tensor, info: torch.Tensor | None = None, out: torch.Tensor 
     rc = load().spd_logdet(_code(L), n, _ptr(L), lda, _ptr(info), _ptr(out), ctypes.c_void_p(_stream(stream)))
     _check(rc, "spd_logdet")
     return out
+
+
+def sygst_workspace_size(dtype: torch.dtype, itype: int, n: int, T_A: int) -> int:
+    return int(load().spd_sygst_workspace_size(DTYPE_CODE[dtype], int(itype), n, T_A))
+
+
+def sygst(itype: int, A: torch.Tensor, L: torch.Tensor, T_A: int, info: torch.Tensor | None = None,
+          work: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Reduce the generalized eigenproblem of (A, B = L L^H) to standard form
+    in place: the lower triangle of A becomes that of L^-1 A L^-H (itype 1) or
+    L^H A L (itypes 2 and 3).  ``info`` is the one potrf returned for B.
+    Returns A."""
+    lda = _colmajor(A, "A")
+    ldl = _colmajor(L, "L")
+    n = A.shape[0]
+    if A.shape != (n, n) or L.shape != (n, n):
+        raise ValueError("A and L must be n x n")
+    if A.dtype != L.dtype:
+        raise TypeError("A and L must have the same dtype")
+    if work is None:
+        nbytes = sygst_workspace_size(A.dtype, itype, n, T_A)
+        work = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=A.device)
+    rc = load().spd_sygst(_code(A), int(itype), n, _ptr(A), lda, _ptr(L), ldl, int(T_A), _ptr(info), _ptr(work),
+                          work.numel(), ctypes.c_void_p(_stream(stream)))
+    _check(rc, "spd_sygst")
+    return A
 
 
 def solve(A: torch.Tensor, B: torch.Tensor, T_A: int, want_logdet: bool = False, check: bool = True):

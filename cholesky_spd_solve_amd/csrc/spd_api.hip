@@ -89,7 +89,7 @@ struct ProfScope {
     ProfScope(int cls, double flops, hipStream_t stream)
     {
         std::lock_guard<std::mutex> g(g_prof_mu);
-        if (!(g_prof_mask & (1 << cls)) || g_validate == 2)
+        if (cls < 0 || !(g_prof_mask & (1 << cls)) || g_validate == 2)
             return;
         on = true;
         s = stream;
@@ -109,7 +109,7 @@ struct ProfScope {
     }
 };
 
-enum { PROF_SYRK = 0, PROF_PANEL = 1, PROF_DIAG = 2, PROF_SOLVE = 3 };
+enum { PROF_SYRK = 0, PROF_PANEL = 1, PROF_DIAG = 2, PROF_SOLVE = 3, PROF_UPDATE = 4 };
 
 // ------------------------------------------------------------- helpers ----
 
@@ -314,6 +314,26 @@ static Layout make_layout(int64_t n, int64_t n_rhs, int64_t T_A, int64_t esize)
         L.total = L.q;
     }
     return L;
+}
+
+// Workspace of the generalized-eigenproblem reduction, in elements (each
+// region 256-byte aligned): M (n x n, ld n) holds the full Hermitian A and then
+// the result; itype 1 puts the substitution workspace for n right-hand sides
+// after it, itypes 2 and 3 two more n x n matrices: X = L with zeros above its
+// diagonal and P = M X.
+struct GstLayout {
+    int64_t m, x, p, solve, total;
+};
+
+static GstLayout make_gst_layout(int itype, int64_t n, int64_t T_A, int64_t esize)
+{
+    GstLayout G;
+    const int64_t sq = align_up(n * n, 256 / esize);
+    G.m = 0;
+    G.x = G.solve = sq;
+    G.p = 2 * sq;
+    G.total = itype == 1 ? sq + make_layout(n, n, T_A, esize).total : 3 * sq;
+    return G;
 }
 
 // The lookahead schedule is on unless the environment sets SPD_LOOKAHEAD=0
@@ -644,6 +664,7 @@ struct Solver {
         a.info = info;
         const dim3 grid((unsigned)a.ntiles), block(64 * WM * WN);
         SPD_VALIDATE((check_rect<R, BM, BN, KB, WM, WN, PT, VEC, STORE>(a, grid, g_chk)));
+        ProfScope ps(STORE ? -1 : PROF_UPDATE, 2.0 * (double)m * n * kvalid, s);  // STORE: potrf's panel
         rect_kernel<R, BM, BN, KB, WM, WN, PT, VEC, 1, STORE><<<grid, block, 0, s>>>(a);
         SPD_CHECK_LAUNCH("rect_kernel");
         return 0;
@@ -941,6 +962,72 @@ struct Solver {
             SPD_CHECK_LAUNCH("gp_loglik_kernel");
             return 0;
         }
+    }
+
+    // Reduction of the Hermitian-definite generalized eigenproblem to standard
+    // form from B = L L^H (L from potrf, lower triangle read only):
+    //   itype 1 (A v = w B v):             C = inv(L) A inv(L)^H
+    //   itype 2, 3 (A B v = w v, B A v = w v): C = L^H A L
+    // A's lower triangle is read and overwritten by C's.  itype 1 runs two
+    // forward substitutions with n right-hand sides around one conjugate
+    // transpose (inv(L) A is the conjugate transpose of A inv(L)^H, A being
+    // Hermitian); itypes 2 and 3 run two triangular products.
+    static int gst(int itype, int64_t n, E *A, int64_t lda, const E *Lb, int64_t ldl, int64_t T_A, const int *info,
+                   void *work, hipStream_t s)
+    {
+        if (n == 0)
+            return 0;
+        const GstLayout G = make_gst_layout(itype, n, T_A, sizeof(E));
+        E *M = (E *)work + G.m;
+        const int64_t blocks = std::min<int64_t>(cdiv(n * n, 256), 8192);
+        SPD_VALIDATE(check_expand<E>("herm_full_kernel", A, lda, M, n, n, true, g_chk));
+        herm_full_kernel<R, CPLX><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(A, lda, M, n, n);
+        SPD_CHECK_LAUNCH("herm_full_kernel");
+        if (itype == 1) {
+            void *pw = (E *)work + G.solve;
+            SPD_TRY(potrs(n, n, Lb, ldl, M, n, T_A, info, pw, s, false));  // inv(L) A
+            const int64_t tt = cdiv(n, 32), pairs = tt * (tt + 1) / 2;
+            SPD_VALIDATE(check_conj_transpose<E>(M, n, n, (unsigned)pairs, info, g_chk));
+            conj_transpose_kernel<R, CPLX><<<dim3((unsigned)pairs), dim3(256), 0, s>>>(M, n, n, info);
+            SPD_CHECK_LAUNCH("conj_transpose_kernel");                    // A inv(L)^H
+            SPD_TRY(potrs(n, n, Lb, ldl, M, n, T_A, info, pw, s, false));  // inv(L) A inv(L)^H
+        } else {
+            E *X = (E *)work + G.x, *P = (E *)work + G.p;
+            SPD_VALIDATE(check_expand<E>("tril_kernel", Lb, ldl, X, n, n, false, g_chk));
+            tril_kernel<R, CPLX><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(Lb, ldl, X, n, n);
+            SPD_CHECK_LAUNCH("tril_kernel");
+            Gemm g;  // P = M X; X(k, j) = 0 for k < j
+            g.A = M;
+            g.lda = n;
+            g.B = X;
+            g.ldb = n;
+            g.C = P;
+            g.ldc = n;
+            g.m = g.n = g.k = n;
+            g.kmode = KM_BEG_BY_J;
+            g.info = info;
+            {
+                ProfScope ps(PROF_SOLVE, FMUL * (double)n * n * n, s);  // n^2 (n - j) / 2 multiply-adds
+                SPD_TRY((gemm<R, CPLX>(NN, g, s)));
+            }
+            Gemm h;  // lower triangle of M = X^H P; X^H(i, k) = 0 for k < i
+            h.A = X;
+            h.lda = n;
+            h.B = P;
+            h.ldb = n;
+            h.C = M;
+            h.ldc = n;
+            h.m = h.n = h.k = n;
+            h.kmode = KM_BEG_BY_I;
+            h.tri = true;
+            h.info = info;
+            ProfScope ps(PROF_SOLVE, FMUL * (double)n * n * n / 3.0, s);  // sum over i >= j of (n - i)
+            SPD_TRY((gemm<R, CPLX>(TN, h, s)));
+        }
+        SPD_VALIDATE(check_copy_lower<E>(A, lda, M, n, n, info, g_chk));
+        copy_lower_kernel<R, CPLX><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(A, lda, M, n, n, info);
+        SPD_CHECK_LAUNCH("copy_lower_kernel");
+        return 0;
     }
 
     // Block substitutions on the general product kernel (complex types, and
@@ -1375,6 +1462,52 @@ int spd_gp_loglik(spd_dtype_t dt, int64_t n, int64_t n_rhs, const void *dA, int6
                                             d_work, s);
 }
 
+size_t spd_sygst_workspace_size(spd_dtype_t dt, int itype, int64_t n, int64_t T_A)
+{
+    const int64_t es = elem_size(dt);
+    if (es == 0 || itype < 1 || itype > 3 || n <= 0 || T_A < 1)
+        return 0;
+    return (size_t)(make_gst_layout(itype, n, T_A, es).total * es);
+}
+
+int spd_sygst(spd_dtype_t dt, int itype, int64_t n, void *dA, int64_t lda, const void *dL, int64_t ldl, int64_t T_A,
+              const int32_t *d_info, void *d_work, size_t work_bytes, void *stream)
+{
+    if (elem_size(dt) == 0) return -1;
+    if (itype < 1 || itype > 3) return -2;
+    if (n < 0 || n > (1 << 20)) return -3;  // keeps the transpose grid below 2^31 workgroups
+    if (dA == nullptr && n > 0) return -4;
+    if (lda < std::max<int64_t>(1, n)) return -5;
+    if (dL == nullptr && n > 0) return -6;
+    if (ldl < std::max<int64_t>(1, n)) return -7;
+    if (T_A < 1) return -8;
+    const size_t need = spd_sygst_workspace_size(dt, itype, n, T_A);
+    if (d_work == nullptr && need > 0) return -10;
+    if (work_bytes < need) return -11;
+    if (g_validate) {
+        g_chk.begin();
+        g_chk.add(dA, matrix_bytes(dt, n, n, lda), true, "A");
+        g_chk.add(dL, matrix_bytes(dt, n, n, ldl), false, "L");
+        g_chk.add(d_info, 4, false, "info");
+        g_chk.add(d_work, work_bytes, true, "workspace");
+    }
+    hipStream_t s = (hipStream_t)stream;
+    switch (dt) {
+    case SPD_R32:
+        return Solver<float, false>::gst(itype, n, (float *)dA, lda, (const float *)dL, ldl, T_A, d_info, d_work, s);
+    case SPD_R64:
+        return Solver<double, false>::gst(itype, n, (double *)dA, lda, (const double *)dL, ldl, T_A, d_info, d_work,
+                                          s);
+    case SPD_C64:
+        return Solver<float, true>::gst(itype, n, (Elem<float, true>::type *)dA, lda,
+                                        (const Elem<float, true>::type *)dL, ldl, T_A, d_info, d_work, s);
+    case SPD_C128:
+        return Solver<double, true>::gst(itype, n, (Elem<double, true>::type *)dA, lda,
+                                         (const Elem<double, true>::type *)dL, ldl, T_A, d_info, d_work, s);
+    }
+    return -1;
+}
+
 int spd_logdet(spd_dtype_t dt, int64_t n, const void *dA, int64_t lda, const int32_t *d_info, double *d_logdet,
                void *stream)
 {
@@ -1420,7 +1553,7 @@ int spd_profile_enable(int mask)
 
 int spd_profile_read(int kernel_class, double *ms, int64_t *launches, double *flops)
 {
-    if (kernel_class < 0 || kernel_class > 3)
+    if (kernel_class < 0 || kernel_class > 4)
         return -1;
     std::vector<ProfRec> mine;
     {

@@ -408,4 +408,67 @@ static bool check_gp_loglik(const R *Y, int64_t ldy, const R *L, int64_t lda, in
     return true;
 }
 
+// Generalized-eigenproblem helpers: element maps of herm_full_kernel,
+// tril_kernel, copy_lower_kernel and the tile pairs of conj_transpose_kernel.
+template <typename E>
+static bool check_expand(const char *kn, const E *src, int64_t lds, E *dst, int64_t ldd, int64_t n, bool mirror,
+                         Checker &c)
+{
+    for (int64_t j = 0; j < n; ++j)
+        for (int64_t i = 0; i < n; ++i) {
+            if (i >= j && !c.access(src + i + j * lds, sizeof(E), false, kn, 0, 0))
+                return false;
+            if (mirror && i < j && !c.access(src + j + i * lds, sizeof(E), false, kn, 0, 0))
+                return false;
+            if (!c.access(dst + i + j * ldd, sizeof(E), true, kn, 0, 0))
+                return false;
+        }
+    return true;
+}
+
+template <typename E>
+static bool check_copy_lower(E *A, int64_t lda, const E *M, int64_t ldm, int64_t n, const int *info, Checker &c)
+{
+    const char *kn = "copy_lower_kernel";
+    if (info != nullptr && !c.access(info, 4, false, kn, 0, 0))
+        return false;
+    for (int64_t j = 0; j < n; ++j)
+        for (int64_t i = j; i < n; ++i)
+            if (!c.access(M + i + j * ldm, sizeof(E), false, kn, 0, 0) ||
+                !c.access(A + i + j * lda, sizeof(E), true, kn, 0, 0))
+                return false;
+    return true;
+}
+
+template <typename E>
+static bool check_conj_transpose(E *M, int64_t ldm, int64_t n, unsigned grid, const int *info, Checker &c)
+{
+    const char *kn = "conj_transpose_kernel";
+    constexpr int TB = 32;
+    if (info != nullptr && !c.access(info, 4, false, kn, 0, 0))
+        return false;
+    const int64_t tt = (n + TB - 1) / TB;
+    if ((int64_t)grid != tt * (tt + 1) / 2) {
+        c.err = "conj_transpose_kernel: grid is not the lower tile pairs";
+        return false;
+    }
+    for (unsigned b = 0; b < grid; ++b) {
+        int I, J;
+        tri_index((int)b, I, J);
+        const int64_t i0 = (int64_t)I * TB, j0 = (int64_t)J * TB;
+        for (int cc = 0; cc < TB; ++cc)
+            for (int t = 0; t < TB; ++t) {
+                if (i0 + t < n && j0 + cc < n &&
+                    (!c.access(M + (i0 + t) + (j0 + cc) * ldm, sizeof(E), false, kn, b, t) ||
+                     !c.access(M + (i0 + t) + (j0 + cc) * ldm, sizeof(E), true, kn, b, t)))
+                    return false;
+                if (j0 + t < n && i0 + cc < n &&
+                    (!c.access(M + (j0 + t) + (i0 + cc) * ldm, sizeof(E), false, kn, b, t) ||
+                     !c.access(M + (j0 + t) + (i0 + cc) * ldm, sizeof(E), true, kn, b, t)))
+                    return false;
+            }
+    }
+    return true;
+}
+
 }  // namespace spd

@@ -640,6 +640,119 @@ __global__ void __launch_bounds__(256) gp_loglik_kernel(const R *Y, int64_t ldy,
     }
 }
 
+// Reduction of the generalized eigenproblem (helpers).  M (n x n, ldm) gets
+// the full Hermitian matrix whose lower triangle is stored in A: M(i, j) =
+// A(i, j) for i >= j and conj(A(j, i)) above; only A's lower triangle is
+// read, and the imaginary part of the diagonal is taken as zero.
+template <typename R, bool CPLX>
+__global__ void __launch_bounds__(256) herm_full_kernel(const void *Av, int64_t lda, void *Mv, int64_t ldm, int64_t n)
+{
+    typedef typename Elem<R, CPLX>::type E;
+    const E *A = (const E *)Av;
+    E *M = (E *)Mv;
+    const int64_t total = n * n;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+        const int64_t i = e % n, j = e / n;
+        R re, im = 0;
+        if (i >= j) {
+            Elem<R, CPLX>::load(A + i + j * lda, re, im);
+            if (i == j)
+                im = 0;
+        } else {
+            Elem<R, CPLX>::load(A + j + i * lda, re, im);
+            im = -im;
+        }
+        Elem<R, CPLX>::store(M + i + j * ldm, re, im);
+    }
+}
+
+// M <- M^H in place for square n x n M: one workgroup per pair of 32 x 32
+// tiles (I, J), I >= J, staged through LDS so that reads and writes run down
+// columns.
+template <typename R, bool CPLX>
+__global__ void __launch_bounds__(256) conj_transpose_kernel(void *Mv, int64_t ldm, int64_t n, const int *info)
+{
+    typedef typename Elem<R, CPLX>::type E;
+    constexpr int TB = 32;
+    __shared__ R a[2][TB][TB + 1], b[2][TB][TB + 1];  // [part][col][row]
+    if (info != nullptr && *info != 0)
+        return;
+    E *M = (E *)Mv;
+    int I, J;
+    tri_index((int)blockIdx.x, I, J);
+    const int64_t i0 = (int64_t)I * TB, j0 = (int64_t)J * TB;
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
+    for (int c = ty; c < TB; c += 8) {
+        R re = 0, im = 0;
+        if (i0 + tx < n && j0 + c < n)
+            Elem<R, CPLX>::load(M + (i0 + tx) + (j0 + c) * ldm, re, im);  // tile (I, J)
+        a[0][c][tx] = re;
+        a[1][c][tx] = im;
+        re = 0;
+        im = 0;
+        if (j0 + tx < n && i0 + c < n)
+            Elem<R, CPLX>::load(M + (j0 + tx) + (i0 + c) * ldm, re, im);  // tile (J, I)
+        b[0][c][tx] = re;
+        b[1][c][tx] = im;
+    }
+    __syncthreads();
+    for (int c = ty; c < TB; c += 8) {
+        // new (I, J)(r, c) = conj(old (J, I)(c, r)); new (J, I)(r, c) = conj(old (I, J)(c, r))
+        if (i0 + tx < n && j0 + c < n)
+            Elem<R, CPLX>::store(M + (i0 + tx) + (j0 + c) * ldm, b[0][tx][c], -b[1][tx][c]);
+        if (I != J && j0 + tx < n && i0 + c < n)
+            Elem<R, CPLX>::store(M + (j0 + tx) + (i0 + c) * ldm, a[0][tx][c], -a[1][tx][c]);
+    }
+}
+
+// A(i, j) = M(i, j) for i >= j (the lower triangle only), the diagonal's
+// imaginary part set to zero (the result is Hermitian); NaN there instead when
+// info reports a failure.
+template <typename R, bool CPLX>
+__global__ void __launch_bounds__(256) copy_lower_kernel(void *Av, int64_t lda, const void *Mv, int64_t ldm,
+                                                         int64_t n, const int *info)
+{
+    typedef typename Elem<R, CPLX>::type E;
+    const bool bad = info != nullptr && *info != 0;
+    const R qnan = (R)__longlong_as_double(0x7ff8000000000000LL);
+    E *A = (E *)Av;
+    const E *M = (const E *)Mv;
+    const int64_t total = n * n;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+        const int64_t i = e % n, j = e / n;
+        if (i < j)
+            continue;
+        R re = qnan, im = qnan;
+        if (!bad) {
+            Elem<R, CPLX>::load(M + i + j * ldm, re, im);
+            if (i == j)
+                im = 0;
+        }
+        Elem<R, CPLX>::store(A + i + j * lda, re, im);
+    }
+}
+
+// X (n x n, ldx) = the lower triangle of L with zeros above it (the diagonal's
+// imaginary part taken as zero); only L's lower triangle is read.
+template <typename R, bool CPLX>
+__global__ void __launch_bounds__(256) tril_kernel(const void *Lv, int64_t ldl, void *Xv, int64_t ldx, int64_t n)
+{
+    typedef typename Elem<R, CPLX>::type E;
+    const E *L = (const E *)Lv;
+    E *X = (E *)Xv;
+    const int64_t total = n * n;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+        const int64_t i = e % n, j = e / n;
+        R re = 0, im = 0;
+        if (i >= j) {
+            Elem<R, CPLX>::load(L + i + j * ldl, re, im);
+            if (i == j)
+                im = 0;
+        }
+        Elem<R, CPLX>::store(X + i + j * ldx, re, im);
+    }
+}
+
 __global__ void set_int_kernel(int *p, int v) { *p = v; }
 
 // dst(0:m, 0:n) = src(0:m, 0:n)

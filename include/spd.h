@@ -135,6 +135,40 @@ int spd_gp_loglik(spd_dtype_t dt, int64_t n, int64_t n_rhs, const void *dA, int6
                   void *dR, int64_t ldr, int64_t T_A, const int32_t *d_info, double *d_out,
                   void *d_work, size_t work_bytes, void *stream);
 
+/* Bytes of device workspace spd_sygst needs; 0 for invalid arguments
+ * (unknown dtype or itype, n <= 0, T_A < 1).  About n^2 elements plus the
+ * substitution workspace for n right-hand sides (itype 1), or 3 n^2 elements
+ * (itypes 2 and 3). */
+size_t spd_sygst_workspace_size(spd_dtype_t dt, int itype, int64_t n, int64_t T_A);
+
+/* Reduction of a Hermitian-definite generalized eigenproblem to standard form
+ * (the Cholesky-based reduction behind the "eigh_gen(a, b, itype)" solver of
+ * the page "Differentiable Generalized Eigenvalue Decomposition", section
+ * "API Reference", whose types 1-3 are the three problems below; the
+ * eigen-solve that follows is not part of this library).  With
+ * B = L L^H factored by spd_potrf:
+ *     itype 1  (A v = w B v):                   C = L^-1 A L^-H
+ *     itype 2, 3 (A B v = w v, B A v = w v):    C = L^H A L
+ * C is Hermitian with the same eigenvalues w as the generalized problem (the
+ * eigenvectors are v = L^-H u for itype 1 and 2, v = L u for itype 3, u those
+ * of C).
+ *   itype     1, 2 or 3
+ *   dA, lda   device, n x n column-major, lda >= max(1, n); the lower triangle
+ *             of the Hermitian A is read (the diagonal's imaginary part taken
+ *             as 0) and overwritten by the lower triangle of C (with a real
+ *             diagonal); the strict upper triangle is not touched
+ *   dL, ldl   the factor of B as left by spd_potrf (lower triangle read only)
+ *   T_A       block size of the substitutions (itype 1; any value >= 1)
+ *   d_info    the d_info of spd_potrf for B (may be NULL: treated as 0); if it
+ *             is non-zero the lower triangle of A is set to NaN
+ *   d_work    workspace of >= spd_sygst_workspace_size(dt, itype, n, T_A) bytes
+ * n is limited to 2^20.
+ * Argument numbers: dt=1 itype=2 n=3 dA=4 lda=5 dL=6 ldl=7 T_A=8 d_info=9
+ * d_work=10 work_bytes=11. */
+int spd_sygst(spd_dtype_t dt, int itype, int64_t n, void *dA, int64_t lda, const void *dL,
+              int64_t ldl, int64_t T_A, const int32_t *d_info, void *d_work, size_t work_bytes,
+              void *stream);
+
 /* log det(A) = 2 * sum_i log(Re L_ii) from the factor L of spd_potrf (JAXMg
  * paper, "Software design": the same factorization can return log det(A);
  * "Cholesky solve (potrs)": the log-determinant term of the Gaussian-process
@@ -174,7 +208,10 @@ int spd_debug_validate(int mode);
  * launches and their algorithmic flop count (real-equivalent flops: a complex
  * multiply-add counts 8), then forgets that class's events.
  * Classes: bit 0 = trailing update (A22 -= L21 L21^H), bit 1 = panel solve,
- * bit 2 = diagonal-tile factorization and inversion, bit 3 = substitution.
+ * bit 2 = diagonal-tile factorization and inversion, bit 3 = substitution
+ * (each whole call) and spd_sygst's two triangular products (itypes 2 and 3,
+ * each launch), bit 4 = the substitutions' block-update kernel (real
+ * types: B_rows -= L_panel X_k, each launch).
  * Returns 0, or -1 for an unknown class, SPD_ERR_HIP on a HIP error. */
 int spd_profile_enable(int mask);
 int spd_profile_read(int kernel_class, double *ms, int64_t *launches, double *flops);

@@ -159,6 +159,35 @@ def gp_loglik(a, r):
     return (out[0] if vec else out), info
 
 
+def sygst(itype: int, a, l):
+    """Standard form of the Hermitian-definite generalized eigenproblem for
+    (A, B = L L^H), the reduction behind the page "Differentiable Generalized
+    Eigenvalue Decomposition", section "API Reference" (types 1: A v = w B v,
+    2: A B v = w v, 3: B A v = w v), written as its definition:
+
+        itype 1:    C = L^-1 A L^-H     (L^-1 by forward substitution on I)
+        itype 2, 3: C = L^H A L
+
+    Only the lower triangle of ``a`` is read (A Hermitian, the diagonal's
+    imaginary part taken as zero); ``l`` is the lower-triangular factor.
+    Returns the full n x n matrix C."""
+    if itype not in (1, 2, 3):
+        raise ValueError("itype must be 1, 2 or 3")
+    a = _wide(a)
+    n = a.shape[0]
+    cplx = np.iscomplexobj(a) or np.iscomplexobj(l)
+    dt = np.complex128 if cplx else np.float64
+    low = np.tril(a, -1).astype(dt)
+    full = low + low.conj().T + np.diag(np.real(np.diagonal(a))).astype(dt)
+    lt = np.tril(np.asarray(l, dtype=dt))
+    if n == 0:
+        return np.zeros((0, 0), dtype=dt)
+    if itype == 1:
+        linv = forward_solve(lt, np.eye(n, dtype=dt))
+        return linv @ full @ linv.conj().T
+    return lt.conj().T @ full @ lt
+
+
 def logdet(l) -> float:
     """log det(A) = 2 * sum_i log L_ii from the Cholesky factor L of A."""
     l = _wide(l)

@@ -146,6 +146,19 @@ def make_B(n: int, nrhs: int, dtype: str, seed: int = 0, ldb: int | None = None,
     return to_colmajor(b, ldb, pad_value)
 
 
+def make_herm(n: int, dtype: str, seed: int = 0, lda: int | None = None, device: str | torch.device = "cpu",
+              pad_value=0.0) -> torch.Tensor:
+    """Symmetric / Hermitian indefinite H = (G + G^H) / sqrt(2 n), exactly
+    Hermitian, column-major (the A of a generalized eigenproblem A v = w B v;
+    its spectrum fills about [-2, 2])."""
+    tdt, _, cplx = DTYPES[dtype]
+    wide = torch.complex128 if cplx else torch.float64
+    g = torch.from_numpy(gaussian(n, n, cplx, seed, 2)).to(wide).to(device)
+    h = (g + g.mH) * (1.0 / math.sqrt(2.0 * n))
+    del g
+    return to_colmajor(_mirror_lower(h).to(tdt), lda, pad_value)
+
+
 def make_config(k: int, seed: int = 0, device="cpu"):
     """(A, B, meta) for workload ``k`` (1..5)."""
     c = dict(CONFIGS[k])

@@ -104,3 +104,20 @@ def test_dry_run_detects_a_short_workspace(lib):
     assert rc == -8
     rc = lib.spd_potrf(1, n, vp(BASE), n - 1 + 1, T, vp(3 * BASE), vp(4 * BASE), need, None)
     assert rc == 0, lib.spd_last_error()
+
+
+GST_SHAPES = [("f64", 1, 8), ("f64", 65, 32), ("f64", 200, 64), ("f64", 260, 128), ("f32", 130, 64),
+              ("c128", 70, 32), ("c64", 100, 64)]
+
+
+@pytest.mark.parametrize("itype", [1, 2, 3])
+@pytest.mark.parametrize("dt,n,T", GST_SHAPES)
+def test_dry_run_sygst(lib, itype, dt, n, T):
+    code = CODE[dt]
+    vp = ctypes.c_void_p
+    A, Lb, info, work = BASE, 2 * BASE, 3 * BASE, 4 * BASE
+    wbytes = lib.spd_sygst_workspace_size(code, itype, n, T)
+    assert wbytes > 0
+    for lda, ldl in ((n, n), (n + 3, n + 5)):
+        rc = lib.spd_sygst(code, itype, n, vp(A), lda, vp(Lb), ldl, T, vp(info), vp(work), wbytes, None)
+        assert rc == 0, (rc, lib.spd_last_error())

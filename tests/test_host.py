@@ -74,6 +74,20 @@ def test_workspace_size(lib):
     assert f(1, 100, 1, 1000) == f(1, 100, 1, 100)
 
 
+def test_sygst_workspace_size(lib):
+    f = lib.spd_sygst_workspace_size
+    assert f(1, 0, 10, 4) == 0 and f(1, 4, 10, 4) == 0 and f(1, 1, 0, 4) == 0 and f(1, 1, 10, 0) == 0
+    assert f(9, 1, 10, 4) == 0
+    up = lambda a, b: -(-a // b) * b
+    for dt, es in ((1, 8), (3, 16), (0, 4)):
+        n, T = 1000, 128
+        sq = up(n * n, 256 // es) * es
+        # itypes 2 and 3: M, X = tril(L), P = M X
+        assert f(dt, 2, n, T) == f(dt, 3, n, T) == 3 * sq
+        # itype 1: M, then the substitution workspace for n right-hand sides
+        assert f(dt, 1, n, T) == sq + lib.spd_workspace_size(dt, n, n, T)
+
+
 def test_argument_validation_returns_before_gpu_work(lib):
     vp = ctypes.c_void_p
     dummy = vp(0x1000)  # never dereferenced: every call below is rejected first
@@ -106,6 +120,19 @@ def test_argument_validation_returns_before_gpu_work(lib):
     assert gp(1, 4, 2, dummy, 3, dummy, 4, 2, info, out, dummy, 1 << 20, None) == -5
     assert gp(1, 4, 2, dummy, 4, dummy, 4, 2, info, None, dummy, 1 << 20, None) == -10
     assert gp(1, 4, 2, dummy, 4, dummy, 4, 2, info, out, dummy, 8, None) == -12
+    gst = lib.spd_sygst
+    assert gst(7, 1, 4, dummy, 4, dummy, 4, 2, info, dummy, 1 << 20, None) == -1
+    assert gst(1, 0, 4, dummy, 4, dummy, 4, 2, info, dummy, 1 << 20, None) == -2
+    assert gst(1, 4, 4, dummy, 4, dummy, 4, 2, info, dummy, 1 << 20, None) == -2
+    assert gst(1, 1, -1, dummy, 4, dummy, 4, 2, info, dummy, 1 << 20, None) == -3
+    assert gst(1, 1, 4, None, 4, dummy, 4, 2, info, dummy, 1 << 20, None) == -4
+    assert gst(1, 1, 4, dummy, 3, dummy, 4, 2, info, dummy, 1 << 20, None) == -5
+    assert gst(1, 1, 4, dummy, 4, None, 4, 2, info, dummy, 1 << 20, None) == -6
+    assert gst(1, 2, 4, dummy, 4, dummy, 3, 2, info, dummy, 1 << 20, None) == -7
+    assert gst(1, 3, 4, dummy, 4, dummy, 4, 0, info, dummy, 1 << 20, None) == -8
+    assert gst(1, 1, 4, dummy, 4, dummy, 4, 2, info, None, 1 << 20, None) == -10
+    assert gst(1, 1, 4, dummy, 4, dummy, 4, 2, info, dummy, 8, None) == -11
+    assert gst(1, 1, 0, None, 1, None, 1, 2, info, None, 0, None) == 0  # n == 0: nothing to do
 
 
 def test_profile_class_validation(lib):

@@ -435,3 +435,111 @@ def test_forward_solve_matches_scipy_and_keeps_input():
         np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
         x = oracle.potrs(L, b)
         assert np.array_equal(b, b0)
+
+
+# ----------------------------------------------- generalized eigenproblem ---
+# Page "Differentiable Generalized Eigenvalue Decomposition", section "API
+# Reference": type 1 is A v = w B v, type 2 A B v = w v, type 3 B A v = w v.
+
+def _herm(n, seed, cplx):
+    """Hermitian (not definite) test matrix with a real diagonal."""
+    rng = np.random.default_rng(seed)
+    M = rng.standard_normal((n, n))
+    if cplx:
+        M = M + 1j * rng.standard_normal((n, n))
+    M = M + M.conj().T
+    return np.tril(M, -1) + np.tril(M, -1).conj().T + np.diag(np.diag(M).real)
+
+
+@pytest.mark.parametrize("itype", [1, 2, 3])
+@pytest.mark.parametrize("n,cplx", [(1, False), (5, False), (60, False), (7, True), (50, True)])
+def test_sygst_eigenvalues_match_scipy_generalized_eigh(itype, n, cplx):
+    """The standard form has the generalized problem's eigenvalues; scipy's
+    generalized eigh (LAPACK's own reduction and solver) gives them."""
+    A = _herm(n, 20 + n, cplx)
+    B = random_spd(n, 40 + n, cplx, delta=0.5)
+    L, info = oracle.potrf(B)
+    assert info == 0
+    C = oracle.sygst(itype, A, L)
+    np.testing.assert_allclose(C, C.conj().T, rtol=0, atol=1e-12 * np.abs(C).max())
+    w = np.linalg.eigvalsh(C)
+    ref = scipy.linalg.eigh(A, B, type=itype, eigvals_only=True)
+    np.testing.assert_allclose(w, ref, rtol=0, atol=1e-10 * max(1.0, np.abs(ref).max()))
+
+
+@pytest.mark.parametrize("itype", [1, 2, 3])
+@pytest.mark.parametrize("cplx", [False, True])
+def test_sygst_eigenvectors_solve_the_generalized_problem(itype, cplx):
+    """Back-transformed eigenvectors of C solve the original problem:
+    v = L^-H u for types 1 and 2, v = L u for type 3."""
+    n = 40
+    A = _herm(n, 5, cplx)
+    B = random_spd(n, 6, cplx, delta=0.3)
+    L, _ = oracle.potrf(B)
+    w, U = np.linalg.eigh(oracle.sygst(itype, A, L))
+    if itype == 3:
+        V = L @ U
+    else:
+        V = scipy.linalg.solve_triangular(L.conj().T, U, lower=False)
+    lhs = {1: A @ V, 2: A @ B @ V, 3: B @ A @ V}[itype]
+    rhs = (B @ V) * w if itype == 1 else V * w
+    np.testing.assert_allclose(lhs, rhs, rtol=0, atol=1e-9 * np.abs(lhs).max())
+
+
+@pytest.mark.parametrize("itype", [1, 2, 3])
+@pytest.mark.parametrize("cplx", [False, True])
+def test_sygst_identity_factor_returns_A(itype, cplx):
+    """B = I gives C = A exactly, and only A's lower triangle is read."""
+    n = 9
+    A = _herm(n, 8, cplx)
+    Araw = np.tril(A) + np.triu(np.full((n, n), 7.5), 1)  # upper triangle is junk
+    C = oracle.sygst(itype, Araw, np.eye(n))
+    np.testing.assert_array_equal(C, A)
+
+
+@pytest.mark.parametrize("itype", [1, 2, 3])
+def test_sygst_diagonal_factor_closed_form(itype):
+    """Diagonal L = diag(s) with powers of two: C_ij = A_ij / (s_i s_j) for
+    type 1 and A_ij s_i s_j for types 2 and 3, exactly."""
+    n = 12
+    A = _herm(n, 9, False)
+    s = 2.0 ** np.arange(-3, n - 3)
+    C = oracle.sygst(itype, A, np.diag(s))
+    ref = A / np.outer(s, s) if itype == 1 else A * np.outer(s, s)
+    np.testing.assert_array_equal(C, ref)
+
+
+def _exact_mat(a):
+    return [[Fraction(int(v)) for v in row] for row in a]
+
+
+def _exact_mul(x, y):
+    n, m, p = len(x), len(y), len(y[0])
+    return [[sum(x[i][k] * y[k][j] for k in range(m)) for j in range(p)] for i in range(n)]
+
+
+@pytest.mark.parametrize("itype", [1, 2])
+def test_sygst_exact_integer_brute_force(itype):
+    """Unit lower-triangular integer L: L^-1 is an integer matrix, so with an
+    integer A every result is a small integer; compared with exact rational
+    arithmetic (a transposed or unconjugated operand changes the values)."""
+    rng = np.random.default_rng(31)
+    n = 8
+    L = int_lower(n, rng, diag_max=1, off=2).astype(np.float64)
+    Ai = rng.integers(-5, 6, size=(n, n))
+    A = np.tril(Ai, -1) + np.tril(Ai, -1).T + np.diag(np.diag(Ai))
+    Lx, Ax = _exact_mat(L), _exact_mat(A)
+    if itype == 1:
+        # inverse of the unit lower-triangular L by exact forward substitution
+        inv = [[Fraction(int(i == j)) for j in range(n)] for i in range(n)]
+        for i in range(n):
+            for j in range(n):
+                inv[i][j] -= sum(Lx[i][k] * inv[k][j] for k in range(i))
+        invH = [list(r) for r in zip(*inv)]
+        ref = _exact_mul(_exact_mul(inv, Ax), invH)
+    else:
+        LH = [list(r) for r in zip(*Lx)]
+        ref = _exact_mul(_exact_mul(LH, Ax), Lx)
+    assert all(v.denominator == 1 and abs(v) < 2**50 for row in ref for v in row)
+    C = oracle.sygst(itype, A.astype(np.float64), L)
+    np.testing.assert_array_equal(C, np.array([[float(v) for v in row] for row in ref]))
