@@ -22,8 +22,8 @@ config's SPD matrix) plus the reduction of the generalized eigenproblem
 A v = w B v (--itype 1; 2 and 3 for A B v = w v, B A v = w v) to standard
 form, A symmetric indefinite (G + G^T)/sqrt(2N); TFLOP/s = (N^3/3 + N^3) /
 step time, N^3 being the reduction's conventional flop count; the roofline is
-that of the substitutions' block-update kernel (itype 1) or of the two
-triangular products (itypes 2, 3).
+that of the trailing-update kernel in its rank-2k form, which carries the
+bulk of the reduction's flops.
 
 Printed: one JSON line with the metric, the roofline of the dominant kernel
 (the trailing update A22 -= L21 L21^H, timed live with HIP events around each
@@ -320,7 +320,7 @@ def bench_sygst(args, cfg):
         step(events())
         torch.cuda.synchronize()
         log(f"[bench] warmup {w + 1}/{args.warmup} done")
-    cls = spd.PROF_UPDATE if (itype == 1 and not cplx) else spd.PROF_SOLVE
+    cls = spd.PROF_SYRK  # the rank-2k (and, for itypes 2 and 3, rank-n) products
     spd.profile_enable(1 << cls)
     spd.profile_read(cls)
     evs = []
@@ -362,8 +362,8 @@ def bench_sygst(args, cfg):
     avg = k_ms / max(k_launches, 1)
     ach = (k_flops / k_launches) / (avg * 1e-3) / 1e12 if k_launches else None
     roofline = {
-        "kernel": ("rect_kernel (substitution block update B_rows -= L_panel X_k)" if cls == spd.PROF_UPDATE
-                   else "gemm_kernel (triangular products P = A L, C = L^H P)"),
+        "kernel": ("syrk_kernel as rank-2k update A22 -= Z L21^H + L21 Z^H" if itype == 1 else
+                   "syrk_kernel as products Wf = Gsb L and C += Wf^H Lsb + Lsb^H Wf"),
         "bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
         "frac": (ach / peak) if ach else None, "traffic": None, "launches": k_launches,
         "avg_launch_ms": avg, "flops_per_launch": k_flops / max(k_launches, 1),

@@ -317,22 +317,63 @@ static Layout make_layout(int64_t n, int64_t n_rhs, int64_t T_A, int64_t esize)
 }
 
 // Workspace of the generalized-eigenproblem reduction, in elements (each
-// region 256-byte aligned): M (n x n, ld n) holds the full Hermitian A and then
-// the result; itype 1 puts the substitution workspace for n right-hand sides
-// after it, itypes 2 and 3 two more n x n matrices: X = L with zeros above its
-// diagonal and P = M X.
+// region 256-byte aligned).  M (n x n, ld n) holds the full Hermitian A and
+// then the result.
+//   itype 1: the substitution workspace for n right-hand sides (its INV and W
+//            regions also serve the blocked sweep), the two rank-2k operand
+//            panels P and Q (n rounded up to 128 rows, 2 x (T rounded up to
+//            32) columns), Y and V (n x T, ld n), and two T x T tiles;
+//   itypes 2, 3: three square matrices of order n rounded up to 128 (the
+//            block strictly-lower part of A, then of L^H; L^H; the stacked
+//            row panels), the lower triangles of L's diagonal blocks and
+//            their products (nt T x T tiles each), and two T x n blocks.
 struct GstLayout {
-    int64_t m, x, p, solve, total;
+    int64_t T, nt, m, solve, p, q, y, v, d, t1, g, lh, wf, ld, ldg, total;
 };
 
 static GstLayout make_gst_layout(int itype, int64_t n, int64_t T_A, int64_t esize)
 {
-    GstLayout G;
-    const int64_t sq = align_up(n * n, 256 / esize);
+    GstLayout G{};
+    const int64_t al = 256 / esize;
+    G.T = std::max<int64_t>(1, std::min(T_A, n));
+    G.nt = cdiv(n, G.T);
     G.m = 0;
-    G.x = G.solve = sq;
-    G.p = 2 * sq;
-    G.total = itype == 1 ? sq + make_layout(n, n, T_A, esize).total : 3 * sq;
+    int64_t o = align_up(n * n, al);
+    if (itype == 1) {
+        const int64_t pw = align_up(n, SYRK_LDW) * 2 * align_up(G.T, SYRK_KP);
+        G.solve = o;
+        o += align_up(make_layout(n, n, T_A, esize).total, al);
+        G.p = o;
+        o += align_up(pw, al);
+        G.q = o;
+        o += align_up(pw, al);
+        G.y = o;
+        o += align_up(n * G.T, al);
+        G.v = o;
+        o += align_up(n * G.T, al);
+        G.d = o;
+        o += align_up(G.T * G.T, al);
+        G.t1 = o;
+        o += align_up(G.T * G.T, al);
+    } else {
+        G.ldg = align_up(n, SYRK_LDW);
+        const int64_t sq = align_up(G.ldg * G.ldg, al);
+        G.g = o;
+        o += sq;
+        G.lh = o;
+        o += sq;
+        G.wf = o;
+        o += sq;
+        G.ld = o;
+        o += align_up(G.nt * G.T * G.T, al);
+        G.t1 = o;
+        o += align_up(G.nt * G.T * G.T, al);
+        G.v = o;
+        o += align_up(G.T * n, al);
+        G.y = o;  // X blocks
+        o += align_up(G.T * n, al);
+    }
+    G.total = o;
     return G;
 }
 
@@ -581,13 +622,24 @@ struct Solver {
 
     // Lower triangle of C (m x m, ldc) -= W W^H with W as laid out above; with
     // jt_end > 0 only the first jt_end tile columns (jt_end * BM columns of C).
+    // Extra operands of the rank-2k form: the column operand V (nullptr: W) and
+    // the depth range and sign (see SyrkArgs).
+    struct Syr2 {
+        const E *V = nullptr;
+        int krange = SYRK_K_ALL;
+        bool add = false;
+    };
+
     template <int BM, int KB, int WM, int WN>
     static int syrk_cfg(int64_t m, const E *W, int64_t ldw, int64_t kp, E *C, int64_t ldc, int jt_end,
-                        const int *info, hipStream_t s)
+                        const int *info, hipStream_t s, const Syr2 &x = Syr2())
     {
         static_assert(SYRK_LDW % BM == 0 && SYRK_KP % KB == 0, "panel padding too small for the tile");
         SyrkArgs a;
         a.W = W;
+        a.V = x.V != nullptr ? x.V : W;
+        a.krange = x.krange;
+        a.add = x.add ? 1 : 0;
         a.ldw = ldw;
         a.C = C;
         a.ldc = ldc;
@@ -612,16 +664,17 @@ struct Solver {
 
     // kw: the panel's true width (kp is it rounded up), for the flop count;
     // cols > 0: only the first cols columns of C (a multiple of 128)
+    // x: the rank-2k form (timed by its caller, not as the trailing update)
     static int syrk(int64_t m, const E *W, int64_t ldw, int64_t kp, int64_t kw, E *C, int64_t ldc, int64_t cols,
-                    const int *info, hipStream_t s)
+                    const int *info, hipStream_t s, const Syr2 &x = Syr2())
     {
         if (m <= 0)
             return 0;
         const int64_t w = cols > 0 ? std::min<int64_t>(m, cols) : m;  // columns of C updated
-        ProfScope ps(PROF_SYRK, FMUL * (double)w * (2.0 * m - w + 1.0) * (double)kw, s);
+        ProfScope ps(x.V == nullptr ? PROF_SYRK : -1, FMUL * (double)w * (2.0 * m - w + 1.0) * (double)kw, s);
         auto jt = [&](int64_t bm) { return cols > 0 ? (int)(cols / bm) : 0; };
         if constexpr (CPLX) {
-            return syrk_cfg<64, 16, 2, 2>(m, W, ldw, kp, C, ldc, jt(64), info, s);
+            return syrk_cfg<64, 16, 2, 2>(m, W, ldw, kp, C, ldc, jt(64), info, s, x);
         } else {
             // Launches with fewer 128-row tiles than two per CU take 64-row
             // tiles: one 128 x 128 x T tile is a fixed ~55 us of a CU's
@@ -630,15 +683,15 @@ struct Solver {
             const int64_t t128 = cdiv(m, 128);
             const int64_t n128 = cols > 0 ? std::min<int64_t>(cols / 128, t128) * t128 : t128 * (t128 + 1) / 2;
             if (n128 < 512)
-                return syrk_cfg<64, 16, 2, 2>(m, W, ldw, kp, C, ldc, jt(64), info, s);
+                return syrk_cfg<64, 16, 2, 2>(m, W, ldw, kp, C, ldc, jt(64), info, s, x);
             if constexpr (sizeof(R) == 4) {  // a 16-deep slice is one 16-byte load per thread
-                return syrk_cfg<128, 16, 2, 4>(m, W, ldw, kp, C, ldc, jt(128), info, s);
+                return syrk_cfg<128, 16, 2, 4>(m, W, ldw, kp, C, ldc, jt(128), info, s, x);
             } else {
                 // slice depth: 16 for the large early steps, 8 below (more
                 // workgroups in flight per byte of LDS; measured better for m < ~24k)
                 if (m >= 24576)
-                    return syrk_cfg<128, 16, 2, 4>(m, W, ldw, kp, C, ldc, jt(128), info, s);
-                return syrk_cfg<128, 8, 2, 4>(m, W, ldw, kp, C, ldc, jt(128), info, s);
+                    return syrk_cfg<128, 16, 2, 4>(m, W, ldw, kp, C, ldc, jt(128), info, s, x);
+                return syrk_cfg<128, 8, 2, 4>(m, W, ldw, kp, C, ldc, jt(128), info, s, x);
             }
         }
     }
@@ -968,10 +1021,9 @@ struct Solver {
     // form from B = L L^H (L from potrf, lower triangle read only):
     //   itype 1 (A v = w B v):             C = inv(L) A inv(L)^H
     //   itype 2, 3 (A B v = w v, B A v = w v): C = L^H A L
-    // A's lower triangle is read and overwritten by C's.  itype 1 runs two
-    // forward substitutions with n right-hand sides around one conjugate
-    // transpose (inv(L) A is the conjugate transpose of A inv(L)^H, A being
-    // Hermitian); itypes 2 and 3 run two triangular products.
+    // A's lower triangle is read and overwritten by C's.  Both run by T-blocks
+    // with their bulk in rank-2k products on the trailing-update kernel; the
+    // flop count is that of the unblocked definition's symmetric form, n^3.
     static int gst(int itype, int64_t n, E *A, int64_t lda, const E *Lb, int64_t ldl, int64_t T_A, const int *info,
                    void *work, hipStream_t s)
     {
@@ -979,61 +1031,252 @@ struct Solver {
             return 0;
         const GstLayout G = make_gst_layout(itype, n, T_A, sizeof(E));
         E *M = (E *)work + G.m;
+        SPD_TRY(herm_full(A, lda, M, n, n, s));
+        if (itype == 1)
+            SPD_TRY(gst1(n, M, Lb, ldl, T_A, G, info, work, s));
+        else
+            SPD_TRY(gst23(n, M, Lb, ldl, G, info, work, s));
         const int64_t blocks = std::min<int64_t>(cdiv(n * n, 256), 8192);
-        SPD_VALIDATE(check_expand<E>("herm_full_kernel", A, lda, M, n, n, true, g_chk));
-        herm_full_kernel<R, CPLX><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(A, lda, M, n, n);
-        SPD_CHECK_LAUNCH("herm_full_kernel");
-        if (itype == 1) {
-            void *pw = (E *)work + G.solve;
-            SPD_TRY(potrs(n, n, Lb, ldl, M, n, T_A, info, pw, s, false));  // inv(L) A
-            const int64_t tt = cdiv(n, 32), pairs = tt * (tt + 1) / 2;
-            SPD_VALIDATE(check_conj_transpose<E>(M, n, n, (unsigned)pairs, info, g_chk));
-            conj_transpose_kernel<R, CPLX><<<dim3((unsigned)pairs), dim3(256), 0, s>>>(M, n, n, info);
-            SPD_CHECK_LAUNCH("conj_transpose_kernel");                    // A inv(L)^H
-            SPD_TRY(potrs(n, n, Lb, ldl, M, n, T_A, info, pw, s, false));  // inv(L) A inv(L)^H
-        } else {
-            E *X = (E *)work + G.x, *P = (E *)work + G.p;
-            SPD_VALIDATE(check_expand<E>("tril_kernel", Lb, ldl, X, n, n, false, g_chk));
-            tril_kernel<R, CPLX><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(Lb, ldl, X, n, n);
-            SPD_CHECK_LAUNCH("tril_kernel");
-            Gemm g;  // P = M X; X(k, j) = 0 for k < j
-            g.A = M;
-            g.lda = n;
-            g.B = X;
-            g.ldb = n;
-            g.C = P;
-            g.ldc = n;
-            g.m = g.n = g.k = n;
-            g.kmode = KM_BEG_BY_J;
-            g.info = info;
-            {
-                ProfScope ps(PROF_SOLVE, FMUL * (double)n * n * n, s);  // n^2 (n - j) / 2 multiply-adds
-                SPD_TRY((gemm<R, CPLX>(NN, g, s)));
-            }
-            Gemm h;  // lower triangle of M = X^H P; X^H(i, k) = 0 for k < i
-            h.A = X;
-            h.lda = n;
-            h.B = P;
-            h.ldb = n;
-            h.C = M;
-            h.ldc = n;
-            h.m = h.n = h.k = n;
-            h.kmode = KM_BEG_BY_I;
-            h.tri = true;
-            h.info = info;
-            ProfScope ps(PROF_SOLVE, FMUL * (double)n * n * n / 3.0, s);  // sum over i >= j of (n - i)
-            SPD_TRY((gemm<R, CPLX>(TN, h, s)));
-        }
         SPD_VALIDATE(check_copy_lower<E>(A, lda, M, n, n, info, g_chk));
         copy_lower_kernel<R, CPLX><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(A, lda, M, n, n, info);
         SPD_CHECK_LAUNCH("copy_lower_kernel");
         return 0;
     }
 
-    // Block substitutions on the general product kernel (complex types, and
-    // leading dimensions beyond the block-update kernel's 32-bit offsets).
+    // D (n x n, ldd) = the full Hermitian matrix whose lower triangle is in S
+    static int herm_full(const E *S, int64_t lds, E *D, int64_t ldd, int64_t n, hipStream_t s)
+    {
+        const int64_t blocks = std::min<int64_t>(cdiv(n * n, 256), 8192);
+        SPD_VALIDATE(check_expand<E>("herm_full_kernel", S, lds, D, ldd, n, true, g_chk));
+        herm_full_kernel<R, CPLX><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(S, lds, D, ldd, n);
+        SPD_CHECK_LAUNCH("herm_full_kernel");
+        return 0;
+    }
+
+    // Type 1, right-looking by T-blocks.  With the leading block split off and
+    // W11 = inv(L11):
+    //   C11 = W11 A11 W11^H,  Y = A21 W11^H,  Z = Y - L21 C11 / 2,
+    //   A22 <- A22 - Z L21^H - L21 Z^H       (then reduced the same way),
+    //   C21 = inv(L22) (Y - L21 C11).
+    // Y - L21 C11 is kept in place of A21; the solves by the trailing factors
+    // L22 of every step are one forward substitution at the end, of the block
+    // strictly-lower part (block row r non-zero in columns [0, rT) only).
+    static int gst1(int64_t n, E *M, const E *Lb, int64_t ldl, int64_t T_A, const GstLayout &G, const int *info,
+                    void *work, hipStream_t s)
+    {
+        const Layout SL = make_layout(n, n, T_A, sizeof(E));
+        const int64_t T = SL.T, nt = SL.nt, kh = align_up(T, SYRK_KP);
+        E *sw = (E *)work + G.solve;
+        E *Inv = sw + SL.inv;
+        E *P = (E *)work + G.p, *Q = (E *)work + G.q, *Y = (E *)work + G.y, *V = (E *)work + G.v;
+        E *D = (E *)work + G.d, *T1 = (E *)work + G.t1;
+        SPD_TRY(all_inverses(n, Lb, ldl, T, nt, Inv, sw + SL.w, info, s));
+        for (int64_t k = 0; k < nt; ++k) {
+            const int64_t c0 = k * T, tk = std::min(T, n - c0), r0 = c0 + tk, m = n - r0;
+            E *Mkk = M + c0 + c0 * n;
+            const E *Wk = Inv + k * T * T;
+            SPD_TRY(herm_full(Mkk, n, D, T, tk, s));  // its lower triangle is current
+            Gemm g1;  // T1 = W11 A11
+            g1.A = Wk;
+            g1.lda = T;
+            g1.B = D;
+            g1.ldb = T;
+            g1.C = T1;
+            g1.ldc = T;
+            g1.m = g1.n = g1.k = tk;
+            g1.kmode = KM_END_BY_I;
+            g1.info = info;
+            g1.small = true;
+            SPD_TRY((gemm<R, CPLX>(NN, g1, s)));
+            Gemm g2;  // C11 = T1 W11^H, the whole tile
+            g2.A = T1;
+            g2.lda = T;
+            g2.B = Wk;
+            g2.ldb = T;
+            g2.C = Mkk;
+            g2.ldc = n;
+            g2.m = g2.n = g2.k = tk;
+            g2.kmode = KM_END_BY_J;
+            g2.info = info;
+            g2.small = true;
+            SPD_TRY((gemm<R, CPLX>(NT, g2, s)));
+            if (m <= 0)
+                break;
+            Gemm g3;  // Y = A21 W11^H
+            g3.A = M + r0 + c0 * n;
+            g3.lda = n;
+            g3.B = Wk;
+            g3.ldb = T;
+            g3.C = Y;
+            g3.ldc = n;
+            g3.m = m;
+            g3.n = g3.k = tk;
+            g3.kmode = KM_END_BY_J;
+            g3.info = info;
+            SPD_TRY((gemm<R, CPLX>(NT, g3, s)));
+            Gemm g4;  // V = L21 C11
+            g4.A = Lb + r0 + c0 * ldl;
+            g4.lda = ldl;
+            g4.B = Mkk;
+            g4.ldb = n;
+            g4.C = V;
+            g4.ldc = n;
+            g4.m = m;
+            g4.n = g4.k = tk;
+            g4.info = info;
+            SPD_TRY((gemm<R, CPLX>(NN, g4, s)));
+            const int64_t ldw = align_up(m, SYRK_LDW);
+            SPD_VALIDATE(check_gst_pack<E>(Y, n, V, n, Lb + r0 + c0 * ldl, ldl, P, Q, ldw, M + r0 + c0 * n, n, m, tk,
+                                           kh, g_chk));
+            const int64_t pb = std::min<int64_t>(cdiv(ldw * kh, 256), 8192);
+            gst_pack_kernel<R, CPLX><<<dim3((unsigned)pb), dim3(256), 0, s>>>(Y, n, V, n, Lb + r0 + c0 * ldl, ldl, P, Q,
+                                                                              ldw, M + r0 + c0 * n, n, m, tk, kh);
+            SPD_CHECK_LAUNCH("gst_pack_kernel");
+            ProfScope ps(PROF_SYRK, FMUL * 2.0 * (double)m * (m + 1) * tk, s);
+            Syr2 x;  // A22 -= P Q^H = Z L21^H + L21 Z^H
+            x.V = Q;
+            SPD_TRY(syrk(m, P, ldw, 2 * kh, 2 * tk, M + r0 + r0 * n, n, 0, info, s, x));
+        }
+        // C21 blocks: the forward substitution of the block strictly-lower part
+        if (rect_usable(ldl))
+            return potrs_blocks(n, n, Lb, ldl, M, n, SL, info, sw, s, false, true);
+        return potrs_general(n, n, Lb, ldl, M, n, SL, info, sw, s, false, true);
+    }
+
+    // Types 2 and 3 (C = L^H A L) by T-blocks, with no sequential sweep.  For
+    // block row k (p = kT columns before it) let a21 = A(k, 0:p),
+    // l21 = L(k, 0:p), a22 = A_kk, l22 = L_kk and
+    //   w_k = a21 L(0:p, 0:p) + a22 l21 / 2.
+    // Then C(k, 0:p) receives l22^H (w_k + a22 l21 / 2), C_kk receives
+    // l22^H a22 l22, and the leading p x p block receives w_k^H l21 + l21^H w_k.
+    // Summed over k the last terms are Wf^H Lsb + Lsb^H Wf, with Wf the w_k
+    // stacked as block rows (block strictly lower) and Lsb the block
+    // strictly-lower part of L; the first terms of all w_k are the one product
+    // Gsb L, Gsb the block strictly-lower part of A.
+    static int gst23(int64_t n, E *M, const E *Lb, int64_t ldl, const GstLayout &G, const int *info, void *work,
+                     hipStream_t s)
+    {
+        const int64_t T = G.T, nt = G.nt, ldg = G.ldg, nfull = n / T;
+        E *Gb = (E *)work + G.g, *LH = (E *)work + G.lh, *Wf = (E *)work + G.wf;
+        E *Ld = (E *)work + G.ld, *T1 = (E *)work + G.t1, *Vb = (E *)work + G.v, *Xb = (E *)work + G.y;
+        const int64_t sqb = std::min<int64_t>(cdiv(ldg * ldg, 256), 8192);
+        SPD_VALIDATE(check_gst_diag_tril<E>(Lb, ldl, Ld, n, T, nt, g_chk));
+        gst_diag_tril_kernel<R, CPLX><<<dim3((unsigned)std::min<int64_t>(cdiv(nt * T * T, 256), 8192)), dim3(256), 0,
+                                        s>>>(Lb, ldl, Ld, n, T, nt);
+        SPD_CHECK_LAUNCH("gst_diag_tril_kernel");
+        SPD_VALIDATE(check_gst_blocklower<E>(M, n, Gb, ldg, n, T, g_chk));
+        gst_blocklower_kernel<R, CPLX><<<dim3((unsigned)sqb), dim3(256), 0, s>>>(M, n, Gb, ldg, n, T);
+        SPD_CHECK_LAUNCH("gst_blocklower_kernel");
+        SPD_VALIDATE(check_gst_lh<E>(Lb, ldl, LH, ldg, n, g_chk));
+        gst_lh_kernel<R, CPLX><<<dim3((unsigned)sqb), dim3(256), 0, s>>>(Lb, ldl, LH, ldg, n, T, 0);
+        SPD_CHECK_LAUNCH("gst_lh_kernel");
+        SPD_TRY(zero2d<E>(Wf, ldg, ldg, ldg, s));
+        {
+            // Wf = Gsb L = Gsb (L^H)^H; row i of Gsb is zero from its block's
+            // first column on and column j of L above j, so the depth of tile
+            // (I, J) is [j0, i0 + BM)
+            ProfScope ps(PROF_SYRK, FMUL * (double)n * n * n / 3.0, s);
+            Syr2 x;
+            x.V = LH;
+            x.krange = SYRK_K_BAND;
+            x.add = true;
+            SPD_TRY(syrk(n, Gb, ldg, ldg, n, Wf, ldg, 0, info, s, x));
+        }
+        // block rows k >= 1: V = a22 l21, w_k += V/2, X = w_k + V/2, C(k, 0:p) = l22^H X
+        for (int64_t k = 1; k < nt; ++k) {
+            const int64_t c0 = k * T, tk = std::min(T, n - c0);
+            Gemm g;
+            g.A = M + c0 + c0 * n;
+            g.lda = n;
+            g.B = Lb + c0;
+            g.ldb = ldl;
+            g.C = Vb;
+            g.ldc = T;
+            g.m = tk;
+            g.n = c0;
+            g.k = tk;
+            g.info = info;
+            SPD_TRY((gemm<R, CPLX>(NN, g, s)));
+            SPD_VALIDATE(check_gst_half<E>(Wf + c0, ldg, Vb, Xb, T, tk, c0, g_chk));
+            gst_half_kernel<R, CPLX><<<dim3((unsigned)std::min<int64_t>(cdiv(tk * c0, 256), 8192)), dim3(256), 0, s>>>(
+                Wf + c0, ldg, Vb, Xb, T, tk, c0);
+            SPD_CHECK_LAUNCH("gst_half_kernel");
+            Gemm h;
+            h.A = Ld + k * T * T;
+            h.lda = T;
+            h.B = Xb;
+            h.ldb = T;
+            h.C = M + c0;
+            h.ldc = n;
+            h.m = tk;
+            h.n = c0;
+            h.k = tk;
+            h.kmode = KM_BEG_BY_I;
+            h.info = info;
+            SPD_TRY((gemm<R, CPLX>(TN, h, s)));
+        }
+        // diagonal blocks: C_kk = l22^H (a22 l22), whole blocks batched, then the ragged one
+        auto diag = [&](int64_t k0, int64_t cnt, int64_t tk) -> int {
+            const int64_t c0 = k0 * T;
+            Gemm g;
+            g.A = M + c0 + c0 * n;
+            g.lda = n;
+            g.sA_out = T * (1 + n);
+            g.B = Ld + k0 * T * T;
+            g.ldb = T;
+            g.sB_out = T * T;
+            g.C = T1;
+            g.ldc = T;
+            g.sC_out = T * T;
+            g.batch = (int)cnt;
+            g.m = g.n = g.k = tk;
+            g.kmode = KM_BEG_BY_J;
+            g.info = info;
+            SPD_TRY((gemm<R, CPLX>(NN, g, s)));
+            Gemm h;
+            h.A = Ld + k0 * T * T;
+            h.lda = T;
+            h.sA_out = T * T;
+            h.B = T1;
+            h.ldb = T;
+            h.sB_out = T * T;
+            h.C = M + c0 + c0 * n;
+            h.ldc = n;
+            h.sC_out = T * (1 + n);
+            h.batch = (int)cnt;
+            h.m = h.n = h.k = tk;
+            h.kmode = KM_BEG_BY_I;
+            h.info = info;
+            return gemm<R, CPLX>(TN, h, s);
+        };
+        if (nfull > 0)
+            SPD_TRY(diag(0, nfull, T));
+        if (nfull < nt)
+            SPD_TRY(diag(nfull, 1, n - nfull * T));
+        // Wf^H in place (the padding stays zero), then Lsb^H into the Gsb buffer
+        const int64_t tt = cdiv(n, 32), pairs = tt * (tt + 1) / 2;
+        SPD_VALIDATE(check_conj_transpose<E>(Wf, ldg, n, (unsigned)pairs, info, g_chk));
+        conj_transpose_kernel<R, CPLX><<<dim3((unsigned)pairs), dim3(256), 0, s>>>(Wf, ldg, n, info);
+        SPD_CHECK_LAUNCH("conj_transpose_kernel");
+        SPD_VALIDATE(check_gst_lh<E>(Lb, ldl, Gb, ldg, n, g_chk));
+        gst_lh_kernel<R, CPLX><<<dim3((unsigned)sqb), dim3(256), 0, s>>>(Lb, ldl, Gb, ldg, n, T, 1);
+        SPD_CHECK_LAUNCH("gst_lh_kernel");
+        // lower triangle of C += Wf^H Lsb + Lsb^H Wf; row a of either operand
+        // is zero before a's next block, so tile row I needs depth [i0, n)
+        ProfScope ps(PROF_SYRK, FMUL * 2.0 * (double)n * n * n / 3.0, s);
+        Syr2 x1, x2;
+        x1.V = Gb;
+        x1.krange = x2.krange = SYRK_K_ROW;
+        x1.add = x2.add = true;
+        x2.V = Wf;
+        SPD_TRY(syrk(n, Wf, ldg, ldg, n, M, n, 0, info, s, x1));
+        return syrk(n, Gb, ldg, ldg, n, M, n, 0, info, s, x2);
+    }
+
+    // prefix (forward only): block row r of B has non-zero columns [0, r T)
+    // only and the rest of it is left alone (see potrs_blocks).
     static int potrs_general(int64_t n, int64_t nrhs, const E *A, int64_t lda, E *B, int64_t ldb, const Layout &L,
-                             const int *info, void *work, hipStream_t s, bool backward)
+                             const int *info, void *work, hipStream_t s, bool backward, bool prefix = false)
     {
         const int64_t T = L.T, nt = L.nt;
         E *Inv = (E *)work + L.inv;
@@ -1042,8 +1285,11 @@ struct Solver {
         // forward: L Y = B
         for (int64_t k = 0; k < nt; ++k) {
             const int64_t c0 = k * T, tk = std::min(T, n - c0), m = n - c0 - tk;
-            SPD_TRY(apply_inv(Inv, k, T, B, ldb, c0, tk, nrhs, Tmp, false, info, s));
-            SPD_TRY(copy2d<E>(B + c0, ldb, Tmp, T, tk, nrhs, info, s));
+            const int64_t nc = prefix ? std::min(nrhs, c0) : nrhs;  // columns of block row k
+            if (nc <= 0)
+                continue;
+            SPD_TRY(apply_inv(Inv, k, T, B, ldb, c0, tk, nc, Tmp, false, info, s));
+            SPD_TRY(copy2d<E>(B + c0, ldb, Tmp, T, tk, nc, info, s));
             if (m > 0) {
                 Gemm u;  // B_below -= L_panel Y_k
                 u.A = A + (c0 + tk) + c0 * lda;
@@ -1053,7 +1299,7 @@ struct Solver {
                 u.C = B + c0 + tk;
                 u.ldc = ldb;
                 u.m = m;
-                u.n = nrhs;
+                u.n = nc;
                 u.k = tk;
                 u.neg = true;
                 u.beta = true;
@@ -1102,9 +1348,18 @@ struct Solver {
     // before it touches the next block's rows (which that update wrote) and
     // before it overwrites the operand buffer that update read.  The back
     // substitution runs the same way from the last block up.
+    //
+    // prefix (forward only; the second substitution of the type-1 reduction):
+    // block row r of B is non-zero in columns [0, r T) only and its other
+    // columns (the diagonal block and the rest) are left alone; step k then
+    // updates and solves only the columns block k's solution can reach.
     static int potrs_blocks(int64_t n, int64_t nrhs, const E *A, int64_t lda, E *B, int64_t ldb, const Layout &L,
-                            const int *info, void *work, hipStream_t s, bool backward)
+                            const int *info, void *work, hipStream_t s, bool backward, bool prefix = false)
     {
+        if (prefix && backward) {
+            g_last_error = "column-prefix substitution is forward only";
+            return SPD_ERR_HIP;
+        }
         const int64_t T = L.T, nt = L.nt;
         E *Inv = (E *)work + L.inv;
         E *Tmp = (E *)work + L.tmp;
@@ -1116,7 +1371,8 @@ struct Solver {
         const int64_t nfull = n / T;  // whole blocks
         // split chain: depth split of each operand pair, sh parts of ks
         const int64_t sh = (T % 4 == 0 && T >= 64) ? 4 : (T % 2 == 0 && T >= 32) ? 2 : 1, ks = T / sh;
-        const bool split = nfull >= 2;
+        const bool split = nfull >= 2 && !prefix;
+        auto cols = [&](int64_t r) { return prefix ? std::min(nrhs, r * T) : nrhs; };  // columns of block row r
         if (split) {
             // GF_k = -inv(L_k+1,k+1) L_k+1,k for whole blocks k+1 (k = 0 .. nfull-2)
             Gemm g;
@@ -1211,9 +1467,9 @@ struct Solver {
         int qi = 0;  // operand buffer of the block being applied
         // solve block k (inverse product), write it back and transpose it into Qb[q]
         auto solve_block = [&](int64_t k, bool trans, int q, hipStream_t st) -> int {
-            const int64_t c0 = k * T, tk = std::min(T, n - c0);
-            SPD_TRY(apply_inv(Inv, k, T, B, ldb, c0, tk, nrhs, Tmp, trans, info, st));
-            return copy_t(B + c0, ldb, Qb[q], L.ldq, Tmp, T, tk, nrhs, align_up(tk, RECT_KB), info, st);
+            const int64_t c0 = k * T, tk = std::min(T, n - c0), nc = cols(k);
+            SPD_TRY(apply_inv(Inv, k, T, B, ldb, c0, tk, nc, Tmp, trans, info, st));
+            return copy_t(B + c0, ldb, Qb[q], L.ldq, Tmp, T, tk, nc, align_up(tk, RECT_KB), info, st);
         };
         // ---- forward: L Y = B
         SPD_TRY(solve_block(0, false, qi, sl));
@@ -1230,14 +1486,14 @@ struct Solver {
             if (split && k + 1 < nfull) {
                 SPD_TRY(chain(k, k + 1, false, qi ^ 1, sl));
             } else {
-                SPD_TRY(rect<false>(A + r0 + c0 * lda, lda, Qb[qi], L.ldq, B + r0, ldb, t1, nrhs, kp, tk, vec, info,
-                                    sl));
+                SPD_TRY(rect<false>(A + r0 + c0 * lda, lda, Qb[qi], L.ldq, B + r0, ldb, t1, cols(k), kp, tk, vec,
+                                    info, sl));
                 SPD_TRY(solve_block(k + 1, false, qi ^ 1, sl));
             }
             SPD_TRY(rec(la.ev_panel, sl));
             if (m > t1)
-                SPD_TRY(rect<false>(A + (r0 + t1) + c0 * lda, lda, Qb[qi], L.ldq, B + r0 + t1, ldb, m - t1, nrhs, kp,
-                                    tk, vec, info, s));
+                SPD_TRY(rect<false>(A + (r0 + t1) + c0 * lda, lda, Qb[qi], L.ldq, B + r0 + t1, ldb, m - t1, cols(k),
+                                    kp, tk, vec, info, s));
             SPD_TRY(rec(la.ev_rest, s));
             qi ^= 1;
         }

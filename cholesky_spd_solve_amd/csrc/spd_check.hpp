@@ -176,8 +176,15 @@ static bool check_syrk(const SyrkArgs &p, dim3 grid, Checker &c)
             return false;
         }
         const E *W = (const E *)p.W;
+        const E *Vc = (const E *)p.V;
+        int kb, ke;
+        syrk_krange<BM>(p, i0, j0, kb, ke);
+        if (kb < 0 || ke > p.kp || kb >= ke || kb % KB != 0 || ke % KB != 0) {
+            c.err = "syrk_kernel: depth range outside the panel or not whole slices";
+            return false;
+        }
         for (int tid = 0; tid < NT; ++tid) {
-            for (int k0 = 0; k0 < p.kp; k0 += KB)
+            for (int k0 = kb; k0 < ke; k0 += KB)
                 for (int q = 0; q < LD::L; ++q) {
                     int r, k;
                     LD::coords(tid, q, r, k);
@@ -187,7 +194,7 @@ static bool check_syrk(const SyrkArgs &p, dim3 grid, Checker &c)
                         return false;
                     }
                     if (!c.access(W + i0 + (int64_t)k0 * p.ldw + off, LD::V * sizeof(E), false, kn, b, tid) ||
-                        !c.access(W + j0 + (int64_t)k0 * p.ldw + off, LD::V * sizeof(E), false, kn, b, tid))
+                        !c.access(Vc + j0 + (int64_t)k0 * p.ldw + off, LD::V * sizeof(E), false, kn, b, tid))
                         return false;
                 }
             const int lane = tid & 63, wave = tid >> 6;
@@ -469,6 +476,89 @@ static bool check_conj_transpose(E *M, int64_t ldm, int64_t n, unsigned grid, co
             }
     }
     return true;
+}
+
+// Element maps of the blocked-reduction helpers: every element a thread of
+// these grid-stride kernels touches, in each buffer.
+template <typename E>
+static bool check_region(const char *kn, const E *base, int64_t ld, int64_t rows, int64_t cols, bool write,
+                         Checker &c)
+{
+    for (int64_t j = 0; j < cols; ++j)
+        for (int64_t i = 0; i < rows; ++i)
+            if (!c.access(base + i + j * ld, sizeof(E), write, kn, 0, 0))
+                return false;
+    return true;
+}
+
+template <typename E>
+static bool check_gst_pack(const E *Y, int64_t ldy, const E *V, int64_t ldv, const E *L, int64_t ldl, E *P, E *Q,
+                           int64_t ldw, E *X, int64_t ldx, int64_t m, int64_t tk, int64_t kh, Checker &c)
+{
+    const char *kn = "gst_pack_kernel";
+    if (m > ldw || tk > kh) {
+        c.err = "gst_pack_kernel: panel larger than its buffer";
+        return false;
+    }
+    return check_region(kn, Y, ldy, m, tk, false, c) && check_region(kn, V, ldv, m, tk, false, c) &&
+           check_region(kn, L, ldl, m, tk, false, c) && check_region(kn, X, ldx, m, tk, true, c) &&
+           check_region(kn, P, ldw, ldw, 2 * kh, true, c) && check_region(kn, Q, ldw, ldw, 2 * kh, true, c);
+}
+
+template <typename E>
+static bool check_gst_blocklower(const E *A, int64_t lda, E *G, int64_t ldg, int64_t n, int64_t T, Checker &c)
+{
+    const char *kn = "gst_blocklower_kernel";
+    if (!check_region(kn, G, ldg, ldg, ldg, true, c))
+        return false;
+    for (int64_t j = 0; j < n; ++j)
+        for (int64_t i = (j / T + 1) * T; i < n; ++i)
+            if (!c.access(A + i + j * lda, sizeof(E), false, kn, 0, 0))
+                return false;
+    return true;
+}
+
+template <typename E>
+static bool check_lower_read(const char *kn, const E *L, int64_t ldl, int64_t n, Checker &c)
+{
+    for (int64_t j = 0; j < n; ++j)
+        for (int64_t i = j; i < n; ++i)
+            if (!c.access(L + i + j * ldl, sizeof(E), false, kn, 0, 0))
+                return false;
+    return true;
+}
+
+template <typename E>
+static bool check_gst_lh(const E *L, int64_t ldl, E *X, int64_t ldx, int64_t n, Checker &c)
+{
+    const char *kn = "gst_lh_kernel";
+    if (ldx < n) {
+        c.err = "gst_lh_kernel: leading dimension below n";
+        return false;
+    }
+    return check_region(kn, X, ldx, ldx, ldx, true, c) && check_lower_read(kn, L, ldl, n, c);
+}
+
+template <typename E>
+static bool check_gst_diag_tril(const E *L, int64_t ldl, E *D, int64_t n, int64_t T, int64_t nt, Checker &c)
+{
+    const char *kn = "gst_diag_tril_kernel";
+    if (!check_region(kn, D, T * T, T * T, nt, true, c))
+        return false;
+    for (int64_t t = 0; t < nt; ++t)
+        for (int64_t j = 0; j < T; ++j)
+            for (int64_t i = j; i < T && t * T + i < n; ++i)
+                if (!c.access(L + (t * T + i) + (t * T + j) * ldl, sizeof(E), false, kn, 0, 0))
+                    return false;
+    return true;
+}
+
+template <typename E>
+static bool check_gst_half(E *W, int64_t ldw, const E *V, E *X, int64_t ldv, int64_t rows, int64_t p, Checker &c)
+{
+    const char *kn = "gst_half_kernel";
+    return check_region(kn, W, ldw, rows, p, false, c) && check_region(kn, W, ldw, rows, p, true, c) &&
+           check_region(kn, V, ldv, rows, p, false, c) && check_region(kn, X, ldv, rows, p, true, c);
 }
 
 }  // namespace spd

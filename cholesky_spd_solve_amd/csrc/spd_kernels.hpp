@@ -753,6 +753,129 @@ __global__ void __launch_bounds__(256) tril_kernel(const void *Lv, int64_t ldl, 
     }
 }
 
+// ---- blocked reduction of the generalized eigenproblem (helpers) ----
+
+// One step of the type-1 reduction, after Y = A21 inv(L11)^H and V = L21 C11
+// (m x tk each): Z = Y - V/2 goes into P[:, 0:tk) and Q[:, kh:kh+tk), L21 into
+// P[:, kh:kh+tk) and Q[:, 0:tk), and X = Y - V back into the matrix (the block
+// column under the diagonal block).  P and Q (ldw x 2 kh) are written whole,
+// zero outside those columns and below row m, so that the rank-2k update
+// C -= P Q^H = Z L21^H + L21 Z^H reads them without bounds.
+template <typename R, bool CPLX>
+__global__ void __launch_bounds__(256) gst_pack_kernel(const void *Yv, int64_t ldy, const void *Vv, int64_t ldv,
+                                                       const void *Lv, int64_t ldl, void *Pv, void *Qv, int64_t ldw,
+                                                       void *Xv, int64_t ldx, int64_t m, int64_t tk, int64_t kh)
+{
+    typedef typename Elem<R, CPLX>::type E;
+    const E *Y = (const E *)Yv, *V = (const E *)Vv, *L = (const E *)Lv;
+    E *P = (E *)Pv, *Q = (E *)Qv, *X = (E *)Xv;
+    const int64_t total = ldw * kh;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+        const int64_t i = e % ldw, k = e / ldw;
+        R zr = 0, zi = 0, lr = 0, li = 0;
+        if (i < m && k < tk) {
+            R yr, yi = 0, vr, vi = 0;
+            Elem<R, CPLX>::load(Y + i + k * ldy, yr, yi);
+            Elem<R, CPLX>::load(V + i + k * ldv, vr, vi);
+            Elem<R, CPLX>::load(L + i + k * ldl, lr, li);
+            zr = yr - R(0.5) * vr;
+            zi = yi - R(0.5) * vi;
+            Elem<R, CPLX>::store(X + i + k * ldx, yr - vr, yi - vi);
+        }
+        Elem<R, CPLX>::store(P + i + k * ldw, zr, zi);
+        Elem<R, CPLX>::store(P + i + (kh + k) * ldw, lr, li);
+        Elem<R, CPLX>::store(Q + i + k * ldw, lr, li);
+        Elem<R, CPLX>::store(Q + i + (kh + k) * ldw, zr, zi);
+    }
+}
+
+// G (ldg x ldg, zero padded) = the strictly block-lower part of the Hermitian
+// matrix whose lower triangle is stored in A: G(i, j) = A(i, j) when row i lies
+// in a later T-block than column j, else 0.
+template <typename R, bool CPLX>
+__global__ void __launch_bounds__(256) gst_blocklower_kernel(const void *Av, int64_t lda, void *Gv, int64_t ldg,
+                                                             int64_t n, int64_t T)
+{
+    typedef typename Elem<R, CPLX>::type E;
+    const E *A = (const E *)Av;
+    E *G = (E *)Gv;
+    const int64_t total = ldg * ldg;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+        const int64_t i = e % ldg, j = e / ldg;
+        R re = 0, im = 0;
+        if (i < n && j < n && i / T > j / T)
+            Elem<R, CPLX>::load(A + i + j * lda, re, im);
+        Elem<R, CPLX>::store(G + i + j * ldg, re, im);
+    }
+}
+
+// X (ldx x ldx, zero padded) = L^H restricted to the entries (i, j) with
+// j >= i (strict = 0: the whole upper triangle of L^H) or with column j in a
+// later T-block than row i (strict = 1); L's lower triangle is read, the
+// diagonal's imaginary part taken as zero.
+template <typename R, bool CPLX>
+__global__ void __launch_bounds__(256) gst_lh_kernel(const void *Lv, int64_t ldl, void *Xv, int64_t ldx, int64_t n,
+                                                     int64_t T, int strict)
+{
+    typedef typename Elem<R, CPLX>::type E;
+    const E *L = (const E *)Lv;
+    E *X = (E *)Xv;
+    const int64_t total = ldx * ldx;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+        const int64_t i = e % ldx, j = e / ldx;
+        R re = 0, im = 0;
+        if (i < n && j < n && (strict ? j / T > i / T : j >= i)) {
+            Elem<R, CPLX>::load(L + j + i * ldl, re, im);
+            im = (i == j) ? R(0) : -im;
+        }
+        Elem<R, CPLX>::store(X + i + j * ldx, re, im);
+    }
+}
+
+// Ld: the lower triangles of L's T x T diagonal blocks, zeros above (tile t
+// at t*T*T, ld T; the ragged last block zero padded), the diagonal's
+// imaginary part zero.
+template <typename R, bool CPLX>
+__global__ void __launch_bounds__(256) gst_diag_tril_kernel(const void *Lv, int64_t ldl, void *Dv, int64_t n,
+                                                            int64_t T, int64_t nt)
+{
+    typedef typename Elem<R, CPLX>::type E;
+    const E *L = (const E *)Lv;
+    E *D = (E *)Dv;
+    const int64_t total = nt * T * T;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+        const int64_t t = e / (T * T), r = e % (T * T), i = r % T, j = r / T, c0 = t * T;
+        R re = 0, im = 0;
+        if (i >= j && c0 + i < n) {
+            Elem<R, CPLX>::load(L + (c0 + i) + (c0 + j) * ldl, re, im);
+            if (i == j)
+                im = 0;
+        }
+        Elem<R, CPLX>::store(D + e, re, im);
+    }
+}
+
+// For a rows x p block: W += V/2, then X = W + V/2 (V and X with ld ldv).
+template <typename R, bool CPLX>
+__global__ void __launch_bounds__(256) gst_half_kernel(void *Wv, int64_t ldw, const void *Vv, void *Xv, int64_t ldv,
+                                                       int64_t rows, int64_t p)
+{
+    typedef typename Elem<R, CPLX>::type E;
+    E *W = (E *)Wv, *X = (E *)Xv;
+    const E *V = (const E *)Vv;
+    const int64_t total = rows * p;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+        const int64_t i = e % rows, j = e / rows;
+        R wr, wi = 0, vr, vi = 0;
+        Elem<R, CPLX>::load(W + i + j * ldw, wr, wi);
+        Elem<R, CPLX>::load(V + i + j * ldv, vr, vi);
+        wr += R(0.5) * vr;
+        wi += R(0.5) * vi;
+        Elem<R, CPLX>::store(W + i + j * ldw, wr, wi);
+        Elem<R, CPLX>::store(X + i + j * ldv, wr + R(0.5) * vr, wi + R(0.5) * vi);
+    }
+}
+
 __global__ void set_int_kernel(int *p, int v) { *p = v; }
 
 // dst(0:m, 0:n) = src(0:m, 0:n)

@@ -5,6 +5,11 @@
 //
 //     C(i, j) -= sum_k W(i, k) * conj(W(j, k))      for 0 <= j <= i < m
 //
+// The same kernel computes C -/+= W V^H over the lower tiles for two
+// different operands laid out alike (the rank-2k updates of the
+// generalized-eigenproblem reduction), optionally with a per-tile depth range
+// where the operands are known to be zero outside it.
+//
 // W is the freshly solved panel L21 (m x T_A), staged in the workspace with a
 // layout this kernel can read without any bounds logic:
 //   - leading dimension ldw is a multiple of the tile size BM, and rows
@@ -37,6 +42,7 @@ namespace spd {
 
 struct SyrkArgs {
     const void *W;  // panel, column-major, leading dimension ldw (see above)
+    const void *V;  // column operand, same layout (V == W: the symmetric update)
     int64_t ldw;
     void *C;        // trailing matrix, column-major, leading dimension ldc
     int64_t ldc;
@@ -45,8 +51,31 @@ struct SyrkArgs {
     int tiles;      // tile rows = ceil(m / BM)
     int jt_end;     // 0: every lower tile; > 0: only tile columns J < jt_end
     int ntiles;     // number of tiles updated (workgroups)
+    int krange;     // depth range of tile (I, J): SYRK_K_ALL [0, kp), SYRK_K_ROW [i0, kp),
+                    // SYRK_K_BAND [j0, i0 + BM) (the operands are zero outside it)
+    int add;        // 1: C += W V^H instead of C -= W V^H
     const int *info;  // if non-null and *info != 0 the kernel does nothing
 };
+
+enum { SYRK_K_ALL = 0, SYRK_K_ROW = 1, SYRK_K_BAND = 2 };
+
+__device__ inline double fma_r(double a, double b, double c) { return __builtin_fma(a, b, c); }
+__device__ inline float fma_r(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
+
+// Depth range [kb, ke) of the tile at rows i0, columns j0 (multiples of BM,
+// hence of the slice depth); shared with the host-side launch validator.
+template <int BM>
+__host__ __device__ inline void syrk_krange(const SyrkArgs &p, int i0, int j0, int &kb, int &ke)
+{
+    kb = 0;
+    ke = p.kp;
+    if (p.krange == SYRK_K_ROW) {
+        kb = i0;
+    } else if (p.krange == SYRK_K_BAND) {
+        kb = j0;
+        ke = i0 + BM < p.kp ? i0 + BM : p.kp;
+    }
+}
 
 // Tile (I, J) of workgroup b: the whole lower triangle in row order, or, with
 // jt_end > 0, the first jt_end tile columns in column order (column J holds
@@ -123,8 +152,10 @@ syrk_kernel(const SyrkArgs p)
         off[q] = (uint32_t)(rr[q] + (int64_t)kk[q] * p.ldw);
     }
 
-    const E *__restrict__ wa = (const E *)p.W + i0;  // slice origin of the row block of C
-    const E *__restrict__ wb = (const E *)p.W + j0;  // slice origin of the column block
+    int kb, ke;
+    syrk_krange<BM>(p, i0, j0, kb, ke);
+    const E *__restrict__ wa = (const E *)p.W + i0 + (int64_t)kb * p.ldw;  // slice origin, row block of C
+    const E *__restrict__ wb = (const E *)p.V + j0 + (int64_t)kb * p.ldw;  // slice origin, column block
     const int64_t step = (int64_t)KB * p.ldw;
 
     R ra[L][V][NP], rb[L][V][NP];
@@ -189,8 +220,8 @@ syrk_kernel(const SyrkArgs p)
     store(0);
     __syncthreads();
     int cur = 0;
-    for (int k0 = 0; k0 < p.kp; k0 += KB) {
-        const bool more = k0 + KB < p.kp;
+    for (int k0 = kb; k0 < ke; k0 += KB) {
+        const bool more = k0 + KB < ke;
         if (more) {
             wa += step;
             wb += step;
@@ -239,7 +270,9 @@ syrk_kernel(const SyrkArgs p)
         cur ^= 1;
     }
 
-    // ---- epilogue: C -= acc, one 16-row block at a time
+    // ---- epilogue: C -= acc (C += acc when p.add), one 16-row block at a time;
+    // fma(-1, acc, c) rounds exactly as c - acc
+    const R sg = p.add ? R(1) : R(-1);
     E *__restrict__ Ct = (E *)p.C + i0 + (int64_t)j0 * p.ldc;
     const bool whole = (I != J) && (i0 + BM <= p.m);  // every element of the tile is updated
 #pragma unroll
@@ -260,8 +293,9 @@ syrk_kernel(const SyrkArgs p)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int j = jb + fj * 16 + acc_row<R>(lk, q);
-                    Elem<R, CPLX>::store(Ct + (uint32_t)(i + (int64_t)j * p.ldc), cr[fj][q] - acc[0][fi][fj][q],
-                                         CPLX ? ci[fj][q] - acc[NP - 1][fi][fj][q] : R(0));
+                    Elem<R, CPLX>::store(Ct + (uint32_t)(i + (int64_t)j * p.ldc),
+                                         fma_r(sg, acc[0][fi][fj][q], cr[fj][q]),
+                                         CPLX ? fma_r(sg, acc[NP - 1][fi][fj][q], ci[fj][q]) : R(0));
                 }
         } else {
 #pragma unroll
@@ -273,8 +307,8 @@ syrk_kernel(const SyrkArgs p)
                         E *dst = Ct + (uint32_t)(i + (int64_t)j * p.ldc);
                         R xr, xi = 0;
                         Elem<R, CPLX>::load(dst, xr, xi);
-                        Elem<R, CPLX>::store(dst, xr - acc[0][fi][fj][q],
-                                             CPLX ? xi - acc[NP - 1][fi][fj][q] : R(0));
+                        Elem<R, CPLX>::store(dst, fma_r(sg, acc[0][fi][fj][q], xr),
+                                             CPLX ? fma_r(sg, acc[NP - 1][fi][fj][q], xi) : R(0));
                     }
                 }
         }

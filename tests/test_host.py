@@ -81,11 +81,20 @@ def test_sygst_workspace_size(lib):
     up = lambda a, b: -(-a // b) * b
     for dt, es in ((1, 8), (3, 16), (0, 4)):
         n, T = 1000, 128
-        sq = up(n * n, 256 // es) * es
-        # itypes 2 and 3: M, X = tril(L), P = M X
-        assert f(dt, 2, n, T) == f(dt, 3, n, T) == 3 * sq
-        # itype 1: M, then the substitution workspace for n right-hand sides
-        assert f(dt, 1, n, T) == sq + lib.spd_workspace_size(dt, n, n, T)
+        al = 256 // es
+        sq = up(n * n, al)
+        # itype 1: M, the substitution workspace for n right-hand sides, the
+        # rank-2k panels P and Q ((n up to 128) x 2 (T up to 32)), Y and V
+        # (n x T), two T x T tiles
+        solve = lib.spd_workspace_size(dt, n, n, T) // es
+        pw = up(up(n, 128) * 2 * up(T, 32), al)
+        assert f(dt, 1, n, T) == (sq + up(solve, al) + 2 * pw + 2 * up(n * T, al) + 2 * up(T * T, al)) * es
+        # itypes 2 and 3: M, three squares of order n up to 128, two sets of
+        # nt T x T tiles, two T x n blocks
+        nt = -(-n // T)
+        sq128 = up(up(n, 128) ** 2, al)
+        ref = (sq + 3 * sq128 + 2 * up(nt * T * T, al) + 2 * up(T * n, al)) * es
+        assert f(dt, 2, n, T) == f(dt, 3, n, T) == ref
 
 
 def test_argument_validation_returns_before_gpu_work(lib):
