@@ -323,12 +323,12 @@ static Layout make_layout(int64_t n, int64_t n_rhs, int64_t T_A, int64_t esize)
 //            regions also serve the blocked sweep), the two rank-2k operand
 //            panels P and Q (n rounded up to 128 rows, 2 x (T rounded up to
 //            32) columns), Y and V (n x T, ld n), and two T x T tiles;
-//   itypes 2, 3: three square matrices of order n rounded up to 128 (the
-//            block strictly-lower part of A, then of L^H; L^H; the stacked
-//            row panels), the lower triangles of L's diagonal blocks and
-//            their products (nt T x T tiles each), and two T x n blocks.
+//   itypes 2, 3: two square matrices of order n rounded up to 128 (L^H, and
+//            the stacked row panels w_k), two operand panels P and Q as for
+//            itype 1, the lower triangles of L's diagonal blocks and their
+//            products (nt T x T tiles each), and two T x n blocks.
 struct GstLayout {
-    int64_t T, nt, m, solve, p, q, y, v, d, t1, g, lh, wf, ld, ldg, total;
+    int64_t T, nt, m, solve, p, q, y, v, d, t1, lh, wf, ld, ldg, total;
 };
 
 static GstLayout make_gst_layout(int itype, int64_t n, int64_t T_A, int64_t esize)
@@ -358,8 +358,11 @@ static GstLayout make_gst_layout(int itype, int64_t n, int64_t T_A, int64_t esiz
     } else {
         G.ldg = align_up(n, SYRK_LDW);
         const int64_t sq = align_up(G.ldg * G.ldg, al);
-        G.g = o;
-        o += sq;
+        const int64_t pw = G.ldg * 2 * align_up(G.T, SYRK_KP);
+        G.p = o;
+        o += align_up(pw, al);
+        G.q = o;
+        o += align_up(pw, al);
         G.lh = o;
         o += sq;
         G.wf = o;
@@ -628,6 +631,7 @@ struct Solver {
         const E *V = nullptr;
         int krange = SYRK_K_ALL;
         bool add = false;
+        int64_t ncols = 0;  // > 0: the whole m x ncols rectangle (rect_update)
     };
 
     template <int BM, int KB, int WM, int WN>
@@ -647,7 +651,10 @@ struct Solver {
         a.kp = (int)kp;
         a.tiles = (int)cdiv(m, BM);
         a.jt_end = (jt_end > 0 && jt_end < a.tiles) ? jt_end : 0;
-        if (a.jt_end > 0) {
+        a.ncols = (int)x.ncols;
+        if (a.ncols > 0) {
+            a.ntiles = a.tiles * (int)cdiv(x.ncols, BM);
+        } else if (a.jt_end > 0) {
             a.ntiles = 0;
             for (int J = 0; J < a.jt_end; ++J)
                 a.ntiles += a.tiles - J;
@@ -693,6 +700,30 @@ struct Solver {
                     return syrk_cfg<128, 16, 2, 4>(m, W, ldw, kp, C, ldc, jt(128), info, s, x);
                 return syrk_cfg<128, 8, 2, 4>(m, W, ldw, kp, C, ldc, jt(128), info, s, x);
             }
+        }
+    }
+
+    // C (m x ncols, ldc) -/+= W V^H over every tile, W and V in the padded
+    // panel layout (same ldw, rows up to the larger of m and ncols rounded to
+    // the tile); on the trailing-update kernel.
+    static int rect_update(int64_t m, int64_t ncols, const E *W, const E *Vc, int64_t ldw, int64_t kp, E *C,
+                           int64_t ldc, bool add, const int *info, hipStream_t s)
+    {
+        if (m <= 0 || ncols <= 0)
+            return 0;
+        Syr2 x;
+        x.V = Vc;
+        x.add = add;
+        x.ncols = ncols;
+        if constexpr (CPLX) {
+            return syrk_cfg<64, 16, 2, 2>(m, W, ldw, kp, C, ldc, 0, info, s, x);
+        } else {
+            if (cdiv(m, 128) * cdiv(ncols, 128) < 512)
+                return syrk_cfg<64, 16, 2, 2>(m, W, ldw, kp, C, ldc, 0, info, s, x);
+            if constexpr (sizeof(R) == 4)
+                return syrk_cfg<128, 16, 2, 4>(m, W, ldw, kp, C, ldc, 0, info, s, x);
+            else
+                return syrk_cfg<128, 16, 2, 4>(m, W, ldw, kp, C, ldc, 0, info, s, x);
         }
     }
 
@@ -1143,44 +1174,50 @@ struct Solver {
         return potrs_general(n, n, Lb, ldl, M, n, SL, info, sw, s, false, true);
     }
 
-    // Types 2 and 3 (C = L^H A L) by T-blocks, with no sequential sweep.  For
-    // block row k (p = kT columns before it) let a21 = A(k, 0:p),
-    // l21 = L(k, 0:p), a22 = A_kk, l22 = L_kk and
+    // D (ldw x halves*kh) <- zero-padded column panels [S0 | S1] (rows [0, m),
+    // tk columns each)
+    static int panel_pack(const E *S0, int64_t ld0, const E *S1, int64_t ld1, E *D, int64_t ldw, int64_t m,
+                          int64_t tk, int64_t kh, int halves, hipStream_t s)
+    {
+        SPD_VALIDATE(check_panel_pack<E>(S0, ld0, S1, ld1, D, ldw, m, tk, kh, halves, g_chk));
+        const int64_t blocks = std::min<int64_t>(cdiv(ldw * kh * halves, 256), 8192);
+        panel_pack_kernel<R, CPLX><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(S0, ld0, S1, ld1, D, ldw, m, tk, kh,
+                                                                               halves);
+        SPD_CHECK_LAUNCH("panel_pack_kernel");
+        return 0;
+    }
+
+    // Types 2 and 3 (C = L^H A L) by T-blocks.  For block row k (p = kT columns
+    // before it) let a21 = A(k, 0:p), l21 = L(k, 0:p), a22 = A_kk, l22 = L_kk
+    // and
     //   w_k = a21 L(0:p, 0:p) + a22 l21 / 2.
     // Then C(k, 0:p) receives l22^H (w_k + a22 l21 / 2), C_kk receives
     // l22^H a22 l22, and the leading p x p block receives w_k^H l21 + l21^H w_k.
-    // Summed over k the last terms are Wf^H Lsb + Lsb^H Wf, with Wf the w_k
-    // stacked as block rows (block strictly lower) and Lsb the block
-    // strictly-lower part of L; the first terms of all w_k are the one product
-    // Gsb L, Gsb the block strictly-lower part of A.
+    // The first terms of all w_k together are Gsb L (Gsb the block
+    // strictly-lower part of A), accumulated right-looking one depth block at
+    // a time; the leading-block terms are one rank-2k update per block row.
     static int gst23(int64_t n, E *M, const E *Lb, int64_t ldl, const GstLayout &G, const int *info, void *work,
                      hipStream_t s)
     {
-        const int64_t T = G.T, nt = G.nt, ldg = G.ldg, nfull = n / T;
-        E *Gb = (E *)work + G.g, *LH = (E *)work + G.lh, *Wf = (E *)work + G.wf;
+        const int64_t T = G.T, nt = G.nt, ldg = G.ldg, nfull = n / T, kh = align_up(T, SYRK_KP);
+        E *P = (E *)work + G.p, *Q = (E *)work + G.q, *LH = (E *)work + G.lh, *Wf = (E *)work + G.wf;
         E *Ld = (E *)work + G.ld, *T1 = (E *)work + G.t1, *Vb = (E *)work + G.v, *Xb = (E *)work + G.y;
         const int64_t sqb = std::min<int64_t>(cdiv(ldg * ldg, 256), 8192);
         SPD_VALIDATE(check_gst_diag_tril<E>(Lb, ldl, Ld, n, T, nt, g_chk));
         gst_diag_tril_kernel<R, CPLX><<<dim3((unsigned)std::min<int64_t>(cdiv(nt * T * T, 256), 8192)), dim3(256), 0,
                                         s>>>(Lb, ldl, Ld, n, T, nt);
         SPD_CHECK_LAUNCH("gst_diag_tril_kernel");
-        SPD_VALIDATE(check_gst_blocklower<E>(M, n, Gb, ldg, n, T, g_chk));
-        gst_blocklower_kernel<R, CPLX><<<dim3((unsigned)sqb), dim3(256), 0, s>>>(M, n, Gb, ldg, n, T);
-        SPD_CHECK_LAUNCH("gst_blocklower_kernel");
         SPD_VALIDATE(check_gst_lh<E>(Lb, ldl, LH, ldg, n, g_chk));
         gst_lh_kernel<R, CPLX><<<dim3((unsigned)sqb), dim3(256), 0, s>>>(Lb, ldl, LH, ldg, n, T, 0);
         SPD_CHECK_LAUNCH("gst_lh_kernel");
         SPD_TRY(zero2d<E>(Wf, ldg, ldg, ldg, s));
-        {
-            // Wf = Gsb L = Gsb (L^H)^H; row i of Gsb is zero from its block's
-            // first column on and column j of L above j, so the depth of tile
-            // (I, J) is [j0, i0 + BM)
-            ProfScope ps(PROF_SYRK, FMUL * (double)n * n * n / 3.0, s);
-            Syr2 x;
-            x.V = LH;
-            x.krange = SYRK_K_BAND;
-            x.add = true;
-            SPD_TRY(syrk(n, Gb, ldg, ldg, n, Wf, ldg, 0, info, s, x));
+        // Wf(r0:n, 0:r0) += A(r0:n, block kk) L(block kk, 0:r0), r0 = (kk+1)T
+        for (int64_t kk = 0; kk + 1 < nt; ++kk) {
+            const int64_t r0 = (kk + 1) * T, m = n - r0, ldw = align_up(std::max(m, r0), SYRK_LDW);
+            SPD_TRY(panel_pack(M + r0 + kk * T * n, n, nullptr, 0, P, ldw, m, T, kh, 1, s));
+            SPD_TRY(panel_pack(LH + kk * T * ldg, ldg, nullptr, 0, Q, ldw, r0, T, kh, 1, s));
+            ProfScope ps(PROF_SYRK, FMUL * 2.0 * (double)m * r0 * T, s);
+            SPD_TRY(rect_update(m, r0, P, Q, ldw, kh, Wf + r0, ldg, true, info, s));
         }
         // block rows k >= 1: V = a22 l21, w_k += V/2, X = w_k + V/2, C(k, 0:p) = l22^H X
         for (int64_t k = 1; k < nt; ++k) {
@@ -1253,24 +1290,24 @@ struct Solver {
             SPD_TRY(diag(0, nfull, T));
         if (nfull < nt)
             SPD_TRY(diag(nfull, 1, n - nfull * T));
-        // Wf^H in place (the padding stays zero), then Lsb^H into the Gsb buffer
+        // Wf^H in place: block column k of it is w_k^H (rows [0, kT))
         const int64_t tt = cdiv(n, 32), pairs = tt * (tt + 1) / 2;
         SPD_VALIDATE(check_conj_transpose<E>(Wf, ldg, n, (unsigned)pairs, info, g_chk));
         conj_transpose_kernel<R, CPLX><<<dim3((unsigned)pairs), dim3(256), 0, s>>>(Wf, ldg, n, info);
         SPD_CHECK_LAUNCH("conj_transpose_kernel");
-        SPD_VALIDATE(check_gst_lh<E>(Lb, ldl, Gb, ldg, n, g_chk));
-        gst_lh_kernel<R, CPLX><<<dim3((unsigned)sqb), dim3(256), 0, s>>>(Lb, ldl, Gb, ldg, n, T, 1);
-        SPD_CHECK_LAUNCH("gst_lh_kernel");
-        // lower triangle of C += Wf^H Lsb + Lsb^H Wf; row a of either operand
-        // is zero before a's next block, so tile row I needs depth [i0, n)
-        ProfScope ps(PROF_SYRK, FMUL * 2.0 * (double)n * n * n / 3.0, s);
-        Syr2 x1, x2;
-        x1.V = Gb;
-        x1.krange = x2.krange = SYRK_K_ROW;
-        x1.add = x2.add = true;
-        x2.V = Wf;
-        SPD_TRY(syrk(n, Wf, ldg, ldg, n, M, n, 0, info, s, x1));
-        return syrk(n, Gb, ldg, ldg, n, M, n, 0, info, s, x2);
+        // C(0:p, 0:p) += w_k^H l21 + l21^H w_k = P Q^H with P = [w_k^H | l21^H],
+        // Q = [l21^H | w_k^H] (l21^H is block column k of L^H, rows [0, p))
+        for (int64_t k = 1; k < nt; ++k) {
+            const int64_t p = k * T, tk = std::min(T, n - p), ldw = align_up(p, SYRK_LDW);
+            SPD_TRY(panel_pack(Wf + p * ldg, ldg, LH + p * ldg, ldg, P, ldw, p, tk, kh, 2, s));
+            SPD_TRY(panel_pack(LH + p * ldg, ldg, Wf + p * ldg, ldg, Q, ldw, p, tk, kh, 2, s));
+            ProfScope ps(PROF_SYRK, FMUL * 2.0 * (double)p * (p + 1) * tk, s);
+            Syr2 x;
+            x.V = Q;
+            x.add = true;
+            SPD_TRY(syrk(p, P, ldw, 2 * kh, 2 * tk, M, n, 0, info, s, x));
+        }
+        return 0;
     }
 
     // prefix (forward only): block row r of B has non-zero columns [0, r T)

@@ -171,7 +171,9 @@ static bool check_syrk(const SyrkArgs &p, dim3 grid, Checker &c)
         int I, J;
         syrk_tile(p, (int)b, I, J);
         const int i0 = I * BM, j0 = J * BM;
-        if (I >= p.tiles || J > I || (p.jt_end > 0 && J >= p.jt_end)) {
+        const bool rectm = p.ncols > 0;
+        if (rectm ? (I >= p.tiles || (int64_t)J * BM >= p.ncols || p.krange != SYRK_K_ALL)
+                  : (I >= p.tiles || J > I || (p.jt_end > 0 && J >= p.jt_end))) {
             c.err = "syrk_kernel: workgroup maps outside the lower tiles";
             return false;
         }
@@ -201,13 +203,13 @@ static bool check_syrk(const SyrkArgs &p, dim3 grid, Checker &c)
             const int wm = wave % WM, wn = wave / WM;
             const int li = lane & 15, lk = lane >> 4;
             const int ib = wm * TM, jb = wn * TN;
-            const bool whole = (I != J) && (i0 + BM <= p.m);
+            const bool whole = rectm ? (i0 + BM <= p.m && j0 + BM <= p.ncols) : ((I != J) && (i0 + BM <= p.m));
             E *Ct = (E *)p.C + i0 + (int64_t)j0 * p.ldc;
             for (int fi = 0; fi < FM; ++fi)
                 for (int fj = 0; fj < FN; ++fj)
                     for (int q = 0; q < 4; ++q) {
                         const int i = ib + fi * 16 + li, j = jb + fj * 16 + acc_row<R>(lk, q);
-                        if (whole || (i0 + i < p.m && i0 + i >= j0 + j)) {
+                        if (whole || (i0 + i < p.m && (rectm ? j0 + j < p.ncols : i0 + i >= j0 + j))) {
                             E *dst = Ct + (uint32_t)(i + (int64_t)j * p.ldc);
                             if (!c.access(dst, sizeof(E), false, kn, b, tid) ||
                                 !c.access(dst, sizeof(E), true, kn, b, tid))
@@ -506,19 +508,6 @@ static bool check_gst_pack(const E *Y, int64_t ldy, const E *V, int64_t ldv, con
 }
 
 template <typename E>
-static bool check_gst_blocklower(const E *A, int64_t lda, E *G, int64_t ldg, int64_t n, int64_t T, Checker &c)
-{
-    const char *kn = "gst_blocklower_kernel";
-    if (!check_region(kn, G, ldg, ldg, ldg, true, c))
-        return false;
-    for (int64_t j = 0; j < n; ++j)
-        for (int64_t i = (j / T + 1) * T; i < n; ++i)
-            if (!c.access(A + i + j * lda, sizeof(E), false, kn, 0, 0))
-                return false;
-    return true;
-}
-
-template <typename E>
 static bool check_lower_read(const char *kn, const E *L, int64_t ldl, int64_t n, Checker &c)
 {
     for (int64_t j = 0; j < n; ++j)
@@ -559,6 +548,19 @@ static bool check_gst_half(E *W, int64_t ldw, const E *V, E *X, int64_t ldv, int
     const char *kn = "gst_half_kernel";
     return check_region(kn, W, ldw, rows, p, false, c) && check_region(kn, W, ldw, rows, p, true, c) &&
            check_region(kn, V, ldv, rows, p, false, c) && check_region(kn, X, ldv, rows, p, true, c);
+}
+
+template <typename E>
+static bool check_panel_pack(const E *S0, int64_t ld0, const E *S1, int64_t ld1, E *D, int64_t ldw, int64_t m,
+                             int64_t tk, int64_t kh, int halves, Checker &c)
+{
+    const char *kn = "panel_pack_kernel";
+    if (m > ldw || tk > kh || halves < 1 || halves > 2) {
+        c.err = "panel_pack_kernel: panel larger than its buffer";
+        return false;
+    }
+    return check_region(kn, D, ldw, ldw, kh * halves, true, c) && check_region(kn, S0, ld0, m, tk, false, c) &&
+           (halves == 1 || check_region(kn, S1, ld1, m, tk, false, c));
 }
 
 }  // namespace spd

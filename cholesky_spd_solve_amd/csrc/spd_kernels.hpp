@@ -789,23 +789,23 @@ __global__ void __launch_bounds__(256) gst_pack_kernel(const void *Yv, int64_t l
     }
 }
 
-// G (ldg x ldg, zero padded) = the strictly block-lower part of the Hermitian
-// matrix whose lower triangle is stored in A: G(i, j) = A(i, j) when row i lies
-// in a later T-block than column j, else 0.
+// D (ldw x halves*kh) = [S0 | S1] as zero-padded column panels: columns
+// [0, tk) of half h hold rows [0, m) of S_h (ld ld_h), everything else is 0.
 template <typename R, bool CPLX>
-__global__ void __launch_bounds__(256) gst_blocklower_kernel(const void *Av, int64_t lda, void *Gv, int64_t ldg,
-                                                             int64_t n, int64_t T)
+__global__ void __launch_bounds__(256) panel_pack_kernel(const void *S0v, int64_t ld0, const void *S1v, int64_t ld1,
+                                                         void *Dv, int64_t ldw, int64_t m, int64_t tk, int64_t kh,
+                                                         int halves)
 {
     typedef typename Elem<R, CPLX>::type E;
-    const E *A = (const E *)Av;
-    E *G = (E *)Gv;
-    const int64_t total = ldg * ldg;
+    const E *S0 = (const E *)S0v, *S1 = (const E *)S1v;
+    E *D = (E *)Dv;
+    const int64_t total = ldw * kh * halves;
     for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
-        const int64_t i = e % ldg, j = e / ldg;
+        const int64_t i = e % ldw, c = e / ldw, h = c / kh, k = c % kh;
         R re = 0, im = 0;
-        if (i < n && j < n && i / T > j / T)
-            Elem<R, CPLX>::load(A + i + j * lda, re, im);
-        Elem<R, CPLX>::store(G + i + j * ldg, re, im);
+        if (i < m && k < tk)
+            Elem<R, CPLX>::load((h == 0 ? S0 + i + k * ld0 : S1 + i + k * ld1), re, im);
+        Elem<R, CPLX>::store(D + e, re, im);
     }
 }
 

@@ -50,6 +50,8 @@ struct SyrkArgs {
     int kp;         // columns of W (a multiple of KB)
     int tiles;      // tile rows = ceil(m / BM)
     int jt_end;     // 0: every lower tile; > 0: only tile columns J < jt_end
+    int ncols;      // 0: the lower triangle of the m x m C; > 0: every tile of the
+                    // m x ncols C (rows of W against rows of V, no triangle)
     int ntiles;     // number of tiles updated (workgroups)
     int krange;     // depth range of tile (I, J): SYRK_K_ALL [0, kp), SYRK_K_ROW [i0, kp),
                     // SYRK_K_BAND [j0, i0 + BM) (the operands are zero outside it)
@@ -77,13 +79,19 @@ __host__ __device__ inline void syrk_krange(const SyrkArgs &p, int i0, int j0, i
     }
 }
 
-// Tile (I, J) of workgroup b: the whole lower triangle in row order, or, with
+// Tile (I, J) of workgroup b: with ncols > 0 every tile of the rectangle in
+// column order; otherwise the whole lower triangle in row order, or, with
 // jt_end > 0, the first jt_end tile columns in column order (column J holds
 // tiles I = J .. tiles - 1).  Workgroup ids are first remapped so consecutive
 // tiles share an XCD.  Shared with the host-side launch validator.
 __host__ __device__ inline void syrk_tile(const SyrkArgs &p, int b, int &I, int &J)
 {
     int t = xcd_remap(b, p.ntiles);
+    if (p.ncols > 0) {  // rectangle, column by column
+        I = t % p.tiles;
+        J = t / p.tiles;
+        return;
+    }
     if (p.jt_end <= 0) {
         tri_index(t, I, J);
         return;
@@ -274,7 +282,9 @@ syrk_kernel(const SyrkArgs p)
     // fma(-1, acc, c) rounds exactly as c - acc
     const R sg = p.add ? R(1) : R(-1);
     E *__restrict__ Ct = (E *)p.C + i0 + (int64_t)j0 * p.ldc;
-    const bool whole = (I != J) && (i0 + BM <= p.m);  // every element of the tile is updated
+    const bool rectm = p.ncols > 0;
+    const bool whole = rectm ? (i0 + BM <= p.m && j0 + BM <= p.ncols)
+                             : ((I != J) && (i0 + BM <= p.m));  // every element of the tile is updated
 #pragma unroll
     for (int fi = 0; fi < FM; ++fi) {
         const int i = ib + fi * 16 + li;
@@ -303,7 +313,7 @@ syrk_kernel(const SyrkArgs p)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int j = jb + fj * 16 + acc_row<R>(lk, q);
-                    if (i0 + i < p.m && i0 + i >= j0 + j) {
+                    if (i0 + i < p.m && (rectm ? j0 + j < p.ncols : i0 + i >= j0 + j)) {
                         E *dst = Ct + (uint32_t)(i + (int64_t)j * p.ldc);
                         R xr, xi = 0;
                         Elem<R, CPLX>::load(dst, xr, xi);

@@ -89,11 +89,11 @@ def test_sygst_workspace_size(lib):
         solve = lib.spd_workspace_size(dt, n, n, T) // es
         pw = up(up(n, 128) * 2 * up(T, 32), al)
         assert f(dt, 1, n, T) == (sq + up(solve, al) + 2 * pw + 2 * up(n * T, al) + 2 * up(T * T, al)) * es
-        # itypes 2 and 3: M, three squares of order n up to 128, two sets of
-        # nt T x T tiles, two T x n blocks
+        # itypes 2 and 3: M, the panels P and Q, two squares of order n up to
+        # 128, two sets of nt T x T tiles, two T x n blocks
         nt = -(-n // T)
         sq128 = up(up(n, 128) ** 2, al)
-        ref = (sq + 3 * sq128 + 2 * up(nt * T * T, al) + 2 * up(T * n, al)) * es
+        ref = (sq + 2 * pw + 2 * sq128 + 2 * up(nt * T * T, al) + 2 * up(T * n, al)) * es
         assert f(dt, 2, n, T) == f(dt, 3, n, T) == ref
 
 
