@@ -362,8 +362,10 @@ def bench_sygst(args, cfg):
     avg = k_ms / max(k_launches, 1)
     ach = (k_flops / k_launches) / (avg * 1e-3) / 1e12 if k_launches else None
     roofline = {
-        "kernel": ("syrk_kernel as rank-2k update A22 -= Z L21^H + L21 Z^H" if itype == 1 else
-                   "syrk_kernel as products Wf = Gsb L and C += Wf^H Lsb + Lsb^H Wf"),
+        "kernel": ("syrk_kernel: potrf's trailing update and the reduction's rank-2k updates "
+                   "A22 -= Z L21^H + L21 Z^H" if itype == 1 else
+                   "syrk_kernel: potrf's trailing update and the reduction's products "
+                   "Wf += A_panel L_panel and C += w_k^H l21 + l21^H w_k"),
         "bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
         "frac": (ach / peak) if ach else None, "traffic": None, "launches": k_launches,
         "avg_launch_ms": avg, "flops_per_launch": k_flops / max(k_launches, 1),

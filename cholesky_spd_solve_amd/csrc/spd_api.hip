@@ -1169,8 +1169,10 @@ struct Solver {
             SPD_TRY(syrk(m, P, ldw, 2 * kh, 2 * tk, M + r0 + r0 * n, n, 0, info, s, x));
         }
         // C21 blocks: the forward substitution of the block strictly-lower part
-        if (rect_usable(ldl))
-            return potrs_blocks(n, n, Lb, ldl, M, n, SL, info, sw, s, false, true);
+        if (rect_usable(ldl)) {
+            E *lp[2] = {P, Q};  // the rank-2k panels are free now; each holds ldq x kq
+            return potrs_blocks(n, n, Lb, ldl, M, n, SL, info, sw, s, false, true, lp);
+        }
         return potrs_general(n, n, Lb, ldl, M, n, SL, info, sw, s, false, true);
     }
 
@@ -1390,9 +1392,19 @@ struct Solver {
     // block row r of B is non-zero in columns [0, r T) only and its other
     // columns (the diagonal block and the rest) are left alone; step k then
     // updates and solves only the columns block k's solution can reach.
+    //
+    // lp (forward only, nrhs >= n): two buffers of L.ldq x L.kq elements; each
+    // step's panel of L is packed into one of them, zero padded, and the block
+    // updates run on the trailing-update kernel's rectangular mode (wide
+    // right-hand sides).
     static int potrs_blocks(int64_t n, int64_t nrhs, const E *A, int64_t lda, E *B, int64_t ldb, const Layout &L,
-                            const int *info, void *work, hipStream_t s, bool backward, bool prefix = false)
+                            const int *info, void *work, hipStream_t s, bool backward, bool prefix = false,
+                            E *const *lp = nullptr)
     {
+        if (lp != nullptr && (backward || nrhs < n)) {
+            g_last_error = "packed-panel block update is for the forward substitution with nrhs >= n";
+            return SPD_ERR_HIP;
+        }
         if (prefix && backward) {
             g_last_error = "column-prefix substitution is forward only";
             return SPD_ERR_HIP;
@@ -1508,29 +1520,45 @@ struct Solver {
             SPD_TRY(apply_inv(Inv, k, T, B, ldb, c0, tk, nc, Tmp, trans, info, st));
             return copy_t(B + c0, ldb, Qb[q], L.ldq, Tmp, T, tk, nc, align_up(tk, RECT_KB), info, st);
         };
+        // B(rows r, r + h) -= L(same rows, block k) Y_k, Y_k transposed in Qb[qi]
+        auto update = [&](int64_t k, int64_t r, int64_t h, int q, hipStream_t st) -> int {
+            const int64_t c0 = k * T, tk = std::min(T, n - c0), kp = align_up(tk, RECT_KB);
+            if (lp != nullptr)  // panel packed at rows r0 = c0 + tk onwards
+                return rect_update(h, cols(k), lp[q] + (r - c0 - tk), Qb[q], L.ldq, L.kq, B + r, ldb, false, info,
+                                   st);
+            return rect<false>(A + r + c0 * lda, lda, Qb[q], L.ldq, B + r, ldb, h, cols(k), kp, tk, vec, info, st);
+        };
+        // the panel of L below block k, packed into lp[q] (on the chain stream,
+        // before the event the caller's stream waits on for step k)
+        auto pack_panel = [&](int64_t k, int q, hipStream_t st) -> int {
+            const int64_t c0 = k * T, r0 = c0 + std::min(T, n - c0);
+            if (lp == nullptr || r0 >= n)
+                return 0;
+            return panel_pack(A + r0 + c0 * lda, lda, nullptr, 0, lp[q], L.ldq, n - r0, std::min(T, n - c0), L.kq, 1,
+                              st);
+        };
         // ---- forward: L Y = B
         SPD_TRY(solve_block(0, false, qi, sl));
+        SPD_TRY(pack_panel(0, qi, sl));
         SPD_TRY(rec(la.ev_panel, sl));
         for (int64_t k = 0; k < nt; ++k) {
             const int64_t c0 = k * T, tk = std::min(T, n - c0), r0 = c0 + tk, m = n - r0;
-            const int64_t kp = align_up(tk, RECT_KB);
             SPD_TRY(wait(s, la.ev_panel));  // Y_k in Qb[qi]
             if (m <= 0)
                 break;
             const int64_t t1 = std::min(T, m);  // rows of block k+1
-            if (k > 0)
-                SPD_TRY(wait(sl, la.ev_rest));  // step k-1's update wrote block k+1 and read Qb[qi^1]
+            if (k > 0)  // step k-1's update wrote block k+1 and read Qb[qi^1] and lp[qi^1]
+                SPD_TRY(wait(sl, la.ev_rest));
             if (split && k + 1 < nfull) {
                 SPD_TRY(chain(k, k + 1, false, qi ^ 1, sl));
             } else {
-                SPD_TRY(rect<false>(A + r0 + c0 * lda, lda, Qb[qi], L.ldq, B + r0, ldb, t1, cols(k), kp, tk, vec,
-                                    info, sl));
+                SPD_TRY(update(k, r0, t1, qi, sl));
                 SPD_TRY(solve_block(k + 1, false, qi ^ 1, sl));
             }
+            SPD_TRY(pack_panel(k + 1, qi ^ 1, sl));
             SPD_TRY(rec(la.ev_panel, sl));
             if (m > t1)
-                SPD_TRY(rect<false>(A + (r0 + t1) + c0 * lda, lda, Qb[qi], L.ldq, B + r0 + t1, ldb, m - t1, cols(k),
-                                    kp, tk, vec, info, s));
+                SPD_TRY(update(k, r0 + t1, m - t1, qi, s));
             SPD_TRY(rec(la.ev_rest, s));
             qi ^= 1;
         }

@@ -56,8 +56,10 @@ def run(gpu, itype, dt, n, T_A, pad=0, seed=3):
         assert torch.all(torch.diagonal(A).imag == 0)  # C is Hermitian: real diagonal
 
 
-SHAPES = [("f64", 1, 8, 0), ("f64", 33, 32, 0), ("f64", 300, 64, 3), ("f64", 1000, 256, 0), ("f64", 777, 100, 5),
-          ("f32", 518, 128, 0), ("f32", 200, 64, 2), ("c128", 300, 100, 1), ("c64", 130, 64, 0)]
+# (1000, 128) and (1000, 256) also cover the ordering of the packed L panels
+# against the one-block lookahead of the final substitution (type 1)
+SHAPES = [("f64", 1, 8, 0), ("f64", 33, 32, 0), ("f64", 300, 64, 3), ("f64", 1000, 256, 0), ("f64", 1000, 128, 0),
+          ("f64", 777, 100, 5), ("f32", 518, 128, 0), ("f32", 200, 64, 2), ("c128", 300, 100, 1), ("c64", 130, 64, 0)]
 
 
 @pytest.mark.parametrize("itype", [1, 2, 3])
