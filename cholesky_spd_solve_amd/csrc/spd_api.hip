@@ -1504,7 +1504,10 @@ struct Solver {
                 return 0;
             }
         };
-        const bool ahead = lookahead_enabled() && nt >= 3;
+        // With packed panels (wide right-hand sides) every product fills the GPU
+        // by itself, and the next block's inverse product, run beside the
+        // update, would only get the CUs the update leaves: one stream.
+        const bool ahead = lookahead_enabled() && nt >= 3 && lp == nullptr;
         Lookahead la;
         hipStream_t sl = s;
         if (ahead) {
@@ -1546,6 +1549,13 @@ struct Solver {
             SPD_TRY(wait(s, la.ev_panel));  // Y_k in Qb[qi]
             if (m <= 0)
                 break;
+            if (lp != nullptr) {  // one stream: all rows below block k at once, then block k+1
+                SPD_TRY(update(k, r0, m, qi, s));
+                SPD_TRY(solve_block(k + 1, false, qi ^ 1, s));
+                SPD_TRY(pack_panel(k + 1, qi ^ 1, s));
+                qi ^= 1;
+                continue;
+            }
             const int64_t t1 = std::min(T, m);  // rows of block k+1
             if (k > 0)  // step k-1's update wrote block k+1 and read Qb[qi^1] and lp[qi^1]
                 SPD_TRY(wait(sl, la.ev_rest));
