@@ -1077,9 +1077,9 @@ struct Solver {
     // D (n x n, ldd) = the full Hermitian matrix whose lower triangle is in S
     static int herm_full(const E *S, int64_t lds, E *D, int64_t ldd, int64_t n, hipStream_t s)
     {
-        const int64_t blocks = std::min<int64_t>(cdiv(n * n, 256), 8192);
+        const int64_t tt = cdiv(n, 32), pairs = tt * (tt + 1) / 2;  // 32 x 32 tile pairs
         SPD_VALIDATE(check_expand<E>("herm_full_kernel", S, lds, D, ldd, n, true, g_chk));
-        herm_full_kernel<R, CPLX><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(S, lds, D, ldd, n);
+        herm_full_kernel<R, CPLX><<<dim3((unsigned)pairs), dim3(256), 0, s>>>(S, lds, D, ldd, n);
         SPD_CHECK_LAUNCH("herm_full_kernel");
         return 0;
     }
@@ -1204,13 +1204,13 @@ struct Solver {
         const int64_t T = G.T, nt = G.nt, ldg = G.ldg, nfull = n / T, kh = align_up(T, SYRK_KP);
         E *P = (E *)work + G.p, *Q = (E *)work + G.q, *LH = (E *)work + G.lh, *Wf = (E *)work + G.wf;
         E *Ld = (E *)work + G.ld, *T1 = (E *)work + G.t1, *Vb = (E *)work + G.v, *Xb = (E *)work + G.y;
-        const int64_t sqb = std::min<int64_t>(cdiv(ldg * ldg, 256), 8192);
         SPD_VALIDATE(check_gst_diag_tril<E>(Lb, ldl, Ld, n, T, nt, g_chk));
         gst_diag_tril_kernel<R, CPLX><<<dim3((unsigned)std::min<int64_t>(cdiv(nt * T * T, 256), 8192)), dim3(256), 0,
                                         s>>>(Lb, ldl, Ld, n, T, nt);
         SPD_CHECK_LAUNCH("gst_diag_tril_kernel");
         SPD_VALIDATE(check_gst_lh<E>(Lb, ldl, LH, ldg, n, g_chk));
-        gst_lh_kernel<R, CPLX><<<dim3((unsigned)sqb), dim3(256), 0, s>>>(Lb, ldl, LH, ldg, n, T, 0);
+        const int64_t tg = ldg / 32;  // 32 x 32 tile pairs of the padded square
+        gst_lh_kernel<R, CPLX><<<dim3((unsigned)(tg * (tg + 1) / 2)), dim3(256), 0, s>>>(Lb, ldl, LH, ldg, n, T, 0);
         SPD_CHECK_LAUNCH("gst_lh_kernel");
         SPD_TRY(zero2d<E>(Wf, ldg, ldg, ldg, s));
         // Wf(r0:n, 0:r0) += A(r0:n, block kk) L(block kk, 0:r0), r0 = (kk+1)T

@@ -521,8 +521,8 @@ template <typename E>
 static bool check_gst_lh(const E *L, int64_t ldl, E *X, int64_t ldx, int64_t n, Checker &c)
 {
     const char *kn = "gst_lh_kernel";
-    if (ldx < n) {
-        c.err = "gst_lh_kernel: leading dimension below n";
+    if (ldx < n || ldx % 32 != 0) {
+        c.err = "gst_lh_kernel: leading dimension below n or not whole 32 x 32 tiles";
         return false;
     }
     return check_region(kn, X, ldx, ldx, ldx, true, c) && check_lower_read(kn, L, ldl, n, c);

@@ -643,26 +643,38 @@ __global__ void __launch_bounds__(256) gp_loglik_kernel(const R *Y, int64_t ldy,
 // Reduction of the generalized eigenproblem (helpers).  M (n x n, ldm) gets
 // the full Hermitian matrix whose lower triangle is stored in A: M(i, j) =
 // A(i, j) for i >= j and conj(A(j, i)) above; only A's lower triangle is
-// read, and the imaginary part of the diagonal is taken as zero.
+// read, and the imaginary part of the diagonal is taken as zero.  One
+// workgroup (32 x 8 threads) per pair of 32 x 32 tiles (I, J), I >= J: tile
+// (I, J) of A is staged in LDS, written to M(I, J) and, conjugate-transposed,
+// to M(J, I), both down columns.
 template <typename R, bool CPLX>
 __global__ void __launch_bounds__(256) herm_full_kernel(const void *Av, int64_t lda, void *Mv, int64_t ldm, int64_t n)
 {
     typedef typename Elem<R, CPLX>::type E;
+    constexpr int TB = 32;
+    __shared__ R t[2][TB][TB + 1];  // t[.][c][r] = A(i0 + r, j0 + c)
     const E *A = (const E *)Av;
     E *M = (E *)Mv;
-    const int64_t total = n * n;
-    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
-        const int64_t i = e % n, j = e / n;
-        R re, im = 0;
-        if (i >= j) {
-            Elem<R, CPLX>::load(A + i + j * lda, re, im);
-            if (i == j)
-                im = 0;
-        } else {
-            Elem<R, CPLX>::load(A + j + i * lda, re, im);
-            im = -im;
+    int I, J;
+    tri_index((int)blockIdx.x, I, J);
+    const int64_t i0 = (int64_t)I * TB, j0 = (int64_t)J * TB;
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+    for (int c = ty; c < TB; c += 8) {
+        R re = 0, im = 0;
+        if (i0 + tx < n && j0 + c < n && (I != J || tx >= c))
+            Elem<R, CPLX>::load(A + (i0 + tx) + (j0 + c) * lda, re, im);
+        t[0][c][tx] = re;
+        t[1][c][tx] = (I == J && tx == c) ? R(0) : im;
+    }
+    __syncthreads();
+    for (int c = ty; c < TB; c += 8) {
+        if (i0 + tx < n && j0 + c < n) {  // M(I, J)
+            const bool low = I != J || tx >= c;
+            Elem<R, CPLX>::store(M + (i0 + tx) + (j0 + c) * ldm, low ? t[0][c][tx] : t[0][tx][c],
+                                 low ? t[1][c][tx] : -t[1][tx][c]);
         }
-        Elem<R, CPLX>::store(M + i + j * ldm, re, im);
+        if (I != J && j0 + tx < n && i0 + c < n)  // M(J, I)(r, c) = conj(A(I, J)(c, r))
+            Elem<R, CPLX>::store(M + (j0 + tx) + (i0 + c) * ldm, t[0][tx][c], -t[1][tx][c]);
     }
 }
 
@@ -812,23 +824,42 @@ __global__ void __launch_bounds__(256) panel_pack_kernel(const void *S0v, int64_
 // X (ldx x ldx, zero padded) = L^H restricted to the entries (i, j) with
 // j >= i (strict = 0: the whole upper triangle of L^H) or with column j in a
 // later T-block than row i (strict = 1); L's lower triangle is read, the
-// diagonal's imaginary part taken as zero.
+// diagonal's imaginary part taken as zero.  One workgroup per pair of 32 x 32
+// tiles (I, J), I >= J, of the ldx x ldx square: tile (I, J) of L is staged in
+// LDS and written conjugate-transposed to X(J, I); X(I, J) below the diagonal
+// gets zeros.
 template <typename R, bool CPLX>
 __global__ void __launch_bounds__(256) gst_lh_kernel(const void *Lv, int64_t ldl, void *Xv, int64_t ldx, int64_t n,
                                                      int64_t T, int strict)
 {
     typedef typename Elem<R, CPLX>::type E;
+    constexpr int TB = 32;
+    __shared__ R t[2][TB][TB + 1];  // t[.][c][r] = L(i0 + r, j0 + c)
     const E *L = (const E *)Lv;
     E *X = (E *)Xv;
-    const int64_t total = ldx * ldx;
-    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
-        const int64_t i = e % ldx, j = e / ldx;
+    int I, J;
+    tri_index((int)blockIdx.x, I, J);
+    const int64_t i0 = (int64_t)I * TB, j0 = (int64_t)J * TB;
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+    for (int c = ty; c < TB; c += 8) {
+        R re = 0, im = 0;
+        if (i0 + tx < n && j0 + c < n && (I != J || tx >= c))
+            Elem<R, CPLX>::load(L + (i0 + tx) + (j0 + c) * ldl, re, im);
+        t[0][c][tx] = re;
+        t[1][c][tx] = (I == J && tx == c) ? R(0) : im;
+    }
+    __syncthreads();
+    for (int c = ty; c < TB; c += 8) {
+        // X(J, I)(r, c): i = j0 + r, j = i0 + c, value conj(L(j, i)) = conj(t[r][c])
+        const int64_t i = j0 + tx, j = i0 + c;
         R re = 0, im = 0;
         if (i < n && j < n && (strict ? j / T > i / T : j >= i)) {
-            Elem<R, CPLX>::load(L + j + i * ldl, re, im);
-            im = (i == j) ? R(0) : -im;
+            re = t[0][tx][c];
+            im = -t[1][tx][c];
         }
         Elem<R, CPLX>::store(X + i + j * ldx, re, im);
+        if (I != J)  // strictly below the diagonal of X
+            Elem<R, CPLX>::store(X + (i0 + tx) + (j0 + c) * ldx, R(0), R(0));
     }
 }
 
