@@ -50,12 +50,13 @@ PEAK = {  # MI355X published dense peaks, TFLOP/s
     "c64": 157.3,
 }
 HBM_PEAK_GBS = 8000.0
-# HBM bytes per trailing-update launch at the default workload (fp64 N=32768,
-# T_A=512), from FETCH_SIZE and WRITE_SIZE counter passes scaled by a plain
-# copy's reading (profiles/counters_syrk_f64_n32768_t512.md).  Valid for the
-# trailing-update kernels as they were when the counters were taken; set to
-# None when they change.
-SYRK_TRAFFIC_BYTES = {("f64", 32768, 512): 4.408e9}
+# HBM bytes per trailing-update launch on the caller's stream at the default
+# workload (fp64 N=32768, T_A=512), from FETCH_SIZE and WRITE_SIZE counter
+# passes scaled by a plain copy's reading
+# (profiles/counters_syrk_f64_n32768_t512.md).  Valid for the trailing-update
+# kernels and schedule as they were when the counters were taken; emptied when
+# they change.
+SYRK_TRAFFIC_BYTES = {("f64", 32768, 512): 10.415e9}
 
 
 def parse():
@@ -167,8 +168,9 @@ def main():
         log(f"[bench] warmup {w + 1}/{args.warmup} done")
 
     # timed region: K steps; restores happen between steps, outside the events
-    spd.profile_enable(1 << spd.PROF_SYRK)
+    spd.profile_enable((1 << spd.PROF_SYRK) | (1 << spd.PROF_SYRK_AUX))
     spd.profile_read(spd.PROF_SYRK)
+    spd.profile_read(spd.PROF_SYRK_AUX)
     evs = []
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -181,6 +183,7 @@ def main():
     wall = time.perf_counter() - wall0
     spd.profile_enable(0)
     syrk_ms, syrk_launches, syrk_flops = spd.profile_read(spd.PROF_SYRK)
+    aux_ms, aux_launches, aux_flops = spd.profile_read(spd.PROF_SYRK_AUX)
 
     step_ms = [e[0].elapsed_time(e[3]) for e in evs]
     potrf_ms = [e[0].elapsed_time(e[1]) for e in evs]
@@ -223,8 +226,9 @@ def main():
     syrk_avg_ms = syrk_ms / max(syrk_launches, 1)
     syrk_achieved = (syrk_flops / syrk_launches) / (syrk_avg_ms * 1e-3) / 1e12 if syrk_launches else None
     peak = PEAK[dt]
+    aux_avg_ms = aux_ms / max(aux_launches, 1)
     roofline = {
-        "kernel": "syrk_kernel (trailing update A22 -= L21 L21^H, lower tiles)",
+        "kernel": "syrk_kernel (trailing update A22 -= L21 L21^H, lower tiles; launches on the caller's stream)",
         "bound": "mfma",
         "achieved": syrk_achieved,
         "peak": peak,
@@ -234,6 +238,12 @@ def main():
         "launches": syrk_launches,
         "avg_launch_ms": syrk_avg_ms,
         "flops_per_launch": syrk_flops / max(syrk_launches, 1),
+        # the same kernel's launches on the factorization's auxiliary stream
+        # (the next tile columns), timed while they share the GPU
+        "aux_stream": {"launches": aux_launches, "avg_launch_ms": aux_avg_ms,
+                       "flops_per_launch": aux_flops / max(aux_launches, 1),
+                       "achieved": (aux_flops / aux_launches) / (aux_avg_ms * 1e-3) / 1e12 if aux_launches else None,
+                       "flop_share": aux_flops / max(aux_flops + syrk_flops, 1.0)},
     }
 
     cpu = None

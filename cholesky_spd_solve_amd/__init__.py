@@ -35,7 +35,7 @@ SYMBOLS = ("spd_workspace_size", "spd_potrf", "spd_potrs", "spd_forward_solve", 
            "spd_sygst_workspace_size", "spd_sygst", "spd_last_error", "spd_profile_enable", "spd_profile_read",
            "spd_debug_validate")
 SPD_ERR_HIP, SPD_ERR_CHECK = 1, 2
-PROF_SYRK, PROF_PANEL, PROF_DIAG, PROF_SOLVE, PROF_UPDATE = 0, 1, 2, 3, 4
+PROF_SYRK, PROF_PANEL, PROF_DIAG, PROF_SOLVE, PROF_UPDATE, PROF_SYRK_AUX = 0, 1, 2, 3, 4, 5
 
 _lock = threading.Lock()
 _lib = None

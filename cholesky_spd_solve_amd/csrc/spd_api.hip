@@ -109,7 +109,7 @@ struct ProfScope {
     }
 };
 
-enum { PROF_SYRK = 0, PROF_PANEL = 1, PROF_DIAG = 2, PROF_SOLVE = 3, PROF_UPDATE = 4 };
+enum { PROF_SYRK = 0, PROF_PANEL = 1, PROF_DIAG = 2, PROF_SOLVE = 3, PROF_UPDATE = 4, PROF_SYRK_AUX = 5 };
 
 // ------------------------------------------------------------- helpers ----
 
@@ -265,8 +265,8 @@ static int set_info(int *info, hipStream_t s)
 
 // Workspace layout, in elements of the working type (each region 256-byte
 // aligned):  INV  nt * T * T   inverted diagonal tiles (tile t at t*T*T, ld T)
-//            W    2 x (n rounded up to 128) x (T rounded up to 32): the panels
-//                 L21 of two consecutive steps (potrf) / merge temporaries (both)
+//            W    4 x (n rounded up to 128) x (T rounded up to 32): the panels
+//                 L21 of four consecutive steps (potrf) / merge temporaries (both)
 //            TMP  max(T*T, T*n_rhs)   one block row of the right-hand side
 struct Layout {
     int64_t T, nt, inv, w, wsz, tmp, ctr, q, ldq, kq, qsz, gf, gb, part, total;  // offsets / sizes in elements
@@ -294,7 +294,7 @@ static Layout make_layout(int64_t n, int64_t n_rhs, int64_t T_A, int64_t esize)
     L.inv = 0;
     L.w = align_up(L.nt * L.T * L.T, al);
     L.wsz = align_up(align_up(n, SYRK_LDW) * align_up(L.T, SYRK_KP), al);
-    L.tmp = L.w + 2 * L.wsz;  // two panel buffers: step k's and step k+1's
+    L.tmp = L.w + 4 * L.wsz;  // four panel buffers: two steps in use, two being built
     // ctr: the fused leaf + panel launch's workgroup counter (one int)
     L.ctr = L.tmp + align_up(std::max(L.T * L.T, L.T * std::max<int64_t>(n_rhs, 1)), al);
     L.q = L.ctr + al;
@@ -378,6 +378,24 @@ static GstLayout make_gst_layout(int itype, int64_t n, int64_t T_A, int64_t esiz
     }
     G.total = o;
     return G;
+}
+
+// The two-step schedule of potrf (trailing updates of depth 2T) is used unless
+// the environment sets SPD_TWO_STEP=0; it pairs steps while at least
+// two_step_rows() rows remain beyond the pair (SPD_TWO_STEP_ROWS, default 8192).
+static bool two_step_enabled()
+{
+    static const bool on = [] {
+        const char *v = getenv("SPD_TWO_STEP");
+        return !(v != nullptr && v[0] == '0');
+    }();
+    return on;
+}
+
+static int64_t two_step_rows()  // read at every call (tests vary it)
+{
+    const char *v = getenv("SPD_TWO_STEP_ROWS");
+    return v != nullptr ? std::max<int64_t>(0, atoll(v)) : INT64_C(8192);
 }
 
 // The lookahead schedule is on unless the environment sets SPD_LOOKAHEAD=0
@@ -632,6 +650,9 @@ struct Solver {
         int krange = SYRK_K_ALL;
         bool add = false;
         int64_t ncols = 0;  // > 0: the whole m x ncols rectangle (rect_update)
+        const E *W2 = nullptr;  // second panel for depth [kp1, kp) (the two-step update)
+        int64_t kp1 = 0;
+        bool aux = false;  // potrf's auxiliary stream (timed as its own class)
     };
 
     template <int BM, int KB, int WM, int WN>
@@ -642,6 +663,9 @@ struct Solver {
         SyrkArgs a;
         a.W = W;
         a.V = x.V != nullptr ? x.V : W;
+        a.W2 = x.W2;
+        a.V2 = x.W2;  // the symmetric form only
+        a.kp1 = (int)x.kp1;
         a.krange = x.krange;
         a.add = x.add ? 1 : 0;
         a.ldw = ldw;
@@ -671,6 +695,13 @@ struct Solver {
 
     // kw: the panel's true width (kp is it rounded up), for the flop count;
     // cols > 0: only the first cols columns of C (a multiple of 128)
+    static Syr2 aux_update()
+    {
+        Syr2 x;
+        x.aux = true;
+        return x;
+    }
+
     // x: the rank-2k form (timed by its caller, not as the trailing update)
     static int syrk(int64_t m, const E *W, int64_t ldw, int64_t kp, int64_t kw, E *C, int64_t ldc, int64_t cols,
                     const int *info, hipStream_t s, const Syr2 &x = Syr2())
@@ -678,7 +709,12 @@ struct Solver {
         if (m <= 0)
             return 0;
         const int64_t w = cols > 0 ? std::min<int64_t>(m, cols) : m;  // columns of C updated
-        ProfScope ps(x.V == nullptr ? PROF_SYRK : -1, FMUL * (double)w * (2.0 * m - w + 1.0) * (double)kw, s);
+        if (x.W2 != nullptr && x.V != nullptr) {
+            g_last_error = "two-panel update is for the symmetric form";
+            return SPD_ERR_HIP;
+        }
+        ProfScope ps(x.V != nullptr ? -1 : x.aux ? PROF_SYRK_AUX : PROF_SYRK,
+                     FMUL * (double)w * (2.0 * m - w + 1.0) * (double)kw, s);
         auto jt = [&](int64_t bm) { return cols > 0 ? (int)(cols / bm) : 0; };
         if constexpr (CPLX) {
             return syrk_cfg<64, 16, 2, 2>(m, W, ldw, kp, C, ldc, jt(64), info, s, x);
@@ -815,8 +851,11 @@ struct Solver {
     // solve the panel into Wk with the zero-padded layout the trailing update
     // reads (leading dimension m rounded up to SYRK_LDW, width tk rounded up to
     // SYRK_KP) and copy it back into A.  All on stream s.
+    // ldw_fixed > 0: Wk's leading dimension (the two-step schedule keeps all
+    // panels at one leading dimension); rows [m, m rounded up to SYRK_LDW) are
+    // zeroed either way.
     static int diag_panel(int64_t n, E *A, int64_t lda, int64_t T, int64_t c0, E *Inv, E *Wk, int *info,
-                          int *ctr, hipStream_t s)
+                          int *ctr, hipStream_t s, int64_t ldw_fixed = 0)
     {
         const int64_t tk = std::min(T, n - c0);
         E *D = A + c0 + c0 * lda;
@@ -874,7 +913,7 @@ struct Solver {
         if (m <= 0)
             return 0;
         E *P = D + tk;  // m x tk panel
-        const int64_t ldw = align_up(m, SYRK_LDW), kp = align_up(tk, SYRK_KP);
+        const int64_t ldw = ldw_fixed > 0 ? ldw_fixed : align_up(m, SYRK_LDW), kp = align_up(tk, SYRK_KP);
         ProfScope ps(PROF_PANEL, FMUL * (double)m * tk * tk, s);
         bool done = false;
         if constexpr (!CPLX) {
@@ -913,7 +952,7 @@ struct Solver {
             g.small = true;  // lean tiles: this product shares the GPU with the trailing update
             SPD_TRY((gemm<R, CPLX>(NT, g, s)));
         }
-        SPD_TRY(zero2d<E>(Wk + m, ldw, ldw - m, kp, s));
+        SPD_TRY(zero2d<E>(Wk + m, ldw, align_up(m, SYRK_LDW) - m, kp, s));
         SPD_TRY(zero2d<E>(Wk + tk * ldw, ldw, m, kp - tk, s));
         SPD_TRY(copy2d<E>(P, lda, Wk, ldw, m, tk, info, s));
         return 0;
@@ -952,6 +991,8 @@ struct Solver {
             }
             return 0;
         }
+        if (two_step_enabled())
+            return potrf_pairs(n, A, lda, L, Inv, info, ctr, work, s);
         Lookahead la;
         SPD_TRY(la.begin(s));
         hipStream_t sl = la.look;
@@ -965,7 +1006,7 @@ struct Solver {
             if (k > 0)
                 SPD_TRY(la.wait(sl, la.ev_rest));  // update of step k-1 done
             // tile column k+1 of the trailing matrix, then diagonal tile and panel k+1
-            SPD_TRY(syrk(m, Wk, ldw, kp, T, A + (c0 + T) * (1 + lda), lda, T, info, sl));
+            SPD_TRY(syrk(m, Wk, ldw, kp, T, A + (c0 + T) * (1 + lda), lda, T, info, sl, aux_update()));
             SPD_TRY(diag_panel(n, A, lda, T, c0 + T, Inv, Wb[(k + 1) % 2], info, ctr, sl));
             SPD_TRY(la.record(la.ev_panel, sl));
             // the rest of the trailing matrix, beyond tile column k+1
@@ -974,6 +1015,78 @@ struct Solver {
             SPD_TRY(la.record(la.ev_rest, s));
         }
         SPD_TRY(la.wait(s, la.ev_panel));  // join: last diagonal tile
+        return 0;
+    }
+
+    // Two-step lookahead: while the trailing matrix is large, the update beyond
+    // the next two tile columns is applied every other step with both panels
+    // at once (depth 2T, which the trailing-update kernel runs at a higher rate
+    // than depth T).  For the pair of tiles (a, b = a+1), with panels W_a and
+    // W_b solved, the caller's stream applies [W_a | W_b] to the trailing
+    // matrix from tile a+4 on, while the auxiliary stream applies [W_a | W_b]
+    // to tile columns a+2 and a+3, factors tile a+2 and solves its panel,
+    // applies that panel to tile column a+3, and factors tile a+3 and solves
+    // its panel.  Once fewer than two_step_rows() rows would remain beyond the
+    // pair, the auxiliary stream's chain (two tiles) would be longer than the
+    // caller's update, and the schedule continues one step at a time as in
+    // potrf.  Panels live in four buffers of one leading dimension; panel k's
+    // row 0 is row (k+1)T of A.
+    static int potrf_pairs(int64_t n, E *A, int64_t lda, const Layout &L, E *Inv, int *info, int *ctr, void *work,
+                           hipStream_t s)
+    {
+        const int64_t T = L.T, nt = L.nt, ldw = align_up(n, SYRK_LDW), kp = align_up(T, SYRK_KP);
+        auto Wp = [&](int64_t k) { return (E *)work + L.w + (k % 4) * L.wsz; };
+        auto C = [&](int64_t k) { return A + k * T * (1 + lda); };  // trailing matrix from tile k
+        Lookahead la;
+        SPD_TRY(la.begin(s));
+        hipStream_t sl = la.look;
+        // tiles 0 and 1
+        SPD_TRY(diag_panel(n, A, lda, T, 0, Inv, Wp(0), info, ctr, sl, ldw));
+        SPD_TRY(syrk(n - T, Wp(0), ldw, kp, T, C(1), lda, T, info, sl, aux_update()));
+        SPD_TRY(diag_panel(n, A, lda, T, T, Inv, Wp(1), info, ctr, sl, ldw));
+        SPD_TRY(la.record(la.ev_panel, sl));
+        // pairs: panels a and a+1 solved, tile column a+1 updated by every panel
+        // before it, tiles from a+2 on by the panels before a
+        int64_t a = 0;
+        for (; a + 1 < nt && n - (a + 4) * T >= two_step_rows(); a += 2) {
+            const int64_t c = a + 2, d = a + 3, e = a + 4;
+            SPD_TRY(la.wait(s, la.ev_panel));  // panels a and b
+            if (a > 0)
+                SPD_TRY(la.wait(sl, la.ev_rest));  // the pair before has updated tile columns c and d
+            Syr2 x;
+            x.kp1 = kp;
+            // tile columns c and d by [W_a | W_b] (W_a's rows from tile c start at its row T)
+            x.W2 = Wp(a + 1);
+            x.aux = true;
+            SPD_TRY(syrk(n - c * T, Wp(a) + T, ldw, 2 * kp, 2 * T, C(c), lda, 2 * T, info, sl, x));
+            x.aux = false;
+            SPD_TRY(diag_panel(n, A, lda, T, c * T, Inv, Wp(c), info, ctr, sl, ldw));
+            SPD_TRY(syrk(n - d * T, Wp(c), ldw, kp, T, C(d), lda, T, info, sl, aux_update()));
+            SPD_TRY(diag_panel(n, A, lda, T, d * T, Inv, Wp(d), info, ctr, sl, ldw));
+            SPD_TRY(la.record(la.ev_panel, sl));
+            x.W2 = Wp(a + 1) + 2 * T;  // W_b's rows from tile e
+            SPD_TRY(syrk(n - e * T, Wp(a) + 3 * T, ldw, 2 * kp, 2 * T, C(e), lda, 0, info, s, x));
+            SPD_TRY(la.record(la.ev_rest, s));
+        }
+        // single steps from k = a: tile column a+1 and panel a+1 are done already,
+        // so step a only applies W_a to the tiles from a+2 on
+        SPD_TRY(la.wait(s, la.ev_panel));
+        if (a > 0)
+            SPD_TRY(la.wait(sl, la.ev_rest));
+        if ((a + 2) * T < n)
+            SPD_TRY(syrk(n - (a + 2) * T, Wp(a) + T, ldw, kp, T, C(a + 2), lda, 0, info, s));
+        SPD_TRY(la.record(la.ev_rest, s));
+        for (int64_t k = a + 1; k + 1 < nt; ++k) {
+            SPD_TRY(la.wait(s, la.ev_panel));  // panel k
+            SPD_TRY(la.wait(sl, la.ev_rest));  // the update of step k-1 reached tile column k+1
+            SPD_TRY(syrk(n - (k + 1) * T, Wp(k), ldw, kp, T, C(k + 1), lda, T, info, sl, aux_update()));
+            SPD_TRY(diag_panel(n, A, lda, T, (k + 1) * T, Inv, Wp(k + 1), info, ctr, sl, ldw));
+            SPD_TRY(la.record(la.ev_panel, sl));
+            if ((k + 2) * T < n)
+                SPD_TRY(syrk(n - (k + 2) * T, Wp(k) + T, ldw, kp, T, C(k + 2), lda, 0, info, s));
+            SPD_TRY(la.record(la.ev_rest, s));
+        }
+        SPD_TRY(la.wait(s, la.ev_panel));  // join: the last tile
         return 0;
     }
 
@@ -1884,7 +1997,7 @@ int spd_profile_enable(int mask)
 
 int spd_profile_read(int kernel_class, double *ms, int64_t *launches, double *flops)
 {
-    if (kernel_class < 0 || kernel_class > 4)
+    if (kernel_class < 0 || kernel_class > 5)
         return -1;
     std::vector<ProfRec> mine;
     {

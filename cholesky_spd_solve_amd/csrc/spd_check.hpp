@@ -181,7 +181,8 @@ static bool check_syrk(const SyrkArgs &p, dim3 grid, Checker &c)
         const E *Vc = (const E *)p.V;
         int kb, ke;
         syrk_krange<BM>(p, i0, j0, kb, ke);
-        if (kb < 0 || ke > p.kp || kb >= ke || kb % KB != 0 || ke % KB != 0) {
+        if (kb < 0 || ke > p.kp || kb >= ke || kb % KB != 0 || ke % KB != 0 ||
+            (p.kp1 > 0 && (p.kp1 % KB != 0 || p.kp1 >= p.kp || kb != 0))) {
             c.err = "syrk_kernel: depth range outside the panel or not whole slices";
             return false;
         }
@@ -195,8 +196,11 @@ static bool check_syrk(const SyrkArgs &p, dim3 grid, Checker &c)
                         c.err = "syrk_kernel: load outside its tile slice";
                         return false;
                     }
-                    if (!c.access(W + i0 + (int64_t)k0 * p.ldw + off, LD::V * sizeof(E), false, kn, b, tid) ||
-                        !c.access(Vc + j0 + (int64_t)k0 * p.ldw + off, LD::V * sizeof(E), false, kn, b, tid))
+                    const bool second = p.kp1 > 0 && k0 >= p.kp1;
+                    const E *Wp = second ? (const E *)p.W2 : W, *Vp = second ? (const E *)p.V2 : Vc;
+                    const int64_t kk0 = second ? k0 - p.kp1 : k0;
+                    if (!c.access(Wp + i0 + kk0 * p.ldw + off, LD::V * sizeof(E), false, kn, b, tid) ||
+                        !c.access(Vp + j0 + kk0 * p.ldw + off, LD::V * sizeof(E), false, kn, b, tid))
                         return false;
                 }
             const int lane = tid & 63, wave = tid >> 6;

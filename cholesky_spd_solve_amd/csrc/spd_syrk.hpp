@@ -43,6 +43,9 @@ namespace spd {
 struct SyrkArgs {
     const void *W;  // panel, column-major, leading dimension ldw (see above)
     const void *V;  // column operand, same layout (V == W: the symmetric update)
+    const void *W2; // kp1 > 0: depth [kp1, kp) comes from W2 and V2 (depth 0 at
+    const void *V2; // their column 0), same leading dimension: two panels side by side
+    int kp1;
     int64_t ldw;
     void *C;        // trailing matrix, column-major, leading dimension ldc
     int64_t ldc;
@@ -231,8 +234,13 @@ syrk_kernel(const SyrkArgs p)
     for (int k0 = kb; k0 < ke; k0 += KB) {
         const bool more = k0 + KB < ke;
         if (more) {
-            wa += step;
-            wb += step;
+            if (k0 + KB == p.kp1) {  // second panel pair
+                wa = (const E *)p.W2 + i0;
+                wb = (const E *)p.V2 + j0;
+            } else {
+                wa += step;
+                wb += step;
+            }
             load(wa, wb);
         }
         // Operand fragments are double-buffered in registers: those of k-step

@@ -207,7 +207,9 @@ int spd_debug_validate(int mode);
  * for one class, the summed kernel time in milliseconds, the number of
  * launches and their algorithmic flop count (real-equivalent flops: a complex
  * multiply-add counts 8), then forgets that class's events.
- * Classes: bit 0 = trailing update (A22 -= L21 L21^H), bit 1 = panel solve,
+ * Classes: bit 0 = trailing update (A22 -= L21 L21^H) on the caller's stream,
+ * bit 5 = the trailing update's launches on potrf's auxiliary stream (the
+ * next tile columns), bit 1 = panel solve,
  * bit 2 = diagonal-tile factorization and inversion, bit 3 = substitution
  * (each whole call) and spd_sygst's two triangular products (itypes 2 and 3,
  * each launch), bit 4 = the substitutions' block-update kernel (real

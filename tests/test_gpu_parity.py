@@ -326,3 +326,26 @@ def test_binding_rejects_bad_arguments(gpu):
         gpu.potrf(A, 0)  # T_A < 1
     with pytest.raises(ValueError):
         gpu.potrf(torch.empty(8, 8, device="cuda", dtype=torch.float64), 4)  # row-major storage
+
+
+@pytest.mark.parametrize("dt,n,nrhs,T_A", [("f64", 1000, 5, 128), ("f64", 1300, 3, 128), ("f32", 1024, 4, 128),
+                                           ("c128", 700, 3, 64), ("f64", 2048, 16, 256)])
+def test_two_step_schedule_parity(gpu, dt, n, nrhs, T_A, monkeypatch):
+    """The two-step factorization schedule (pairs of steps share one trailing
+    update of depth 2 T_A) pairs only while 8192 rows remain beyond a pair;
+    SPD_TWO_STEP_ROWS=0 makes it pair every step at these sizes, with odd and
+    even tile counts and a ragged last tile."""
+    monkeypatch.setenv("SPD_TWO_STEP_ROWS", "0")
+    A = spdgen.make_A(n, dt, 0.5, 21, device="cuda")
+    B = spdgen.make_B(n, nrhs, dt, 21, device="cuda")
+    A_np, B_np = wide(A), wide(B)
+    L = spdgen.to_colmajor(A)
+    info = gpu.potrf(L, T_A)
+    X = spdgen.to_colmajor(B)
+    gpu.potrs(L, X, T_A, info=info)
+    torch.cuda.synchronize()
+    assert int(info.item()) == 0
+    Lo, info_o = oracle.potrf(A_np)
+    assert info_o == 0
+    assert np.abs(np.tril(wide(L)) - Lo).max() <= L_TOL[dt] * np.abs(Lo).max()
+    assert rel_err_cols(X, oracle.potrs(Lo, B_np)) <= X_TOL[dt]

@@ -53,20 +53,20 @@ def test_workspace_size(lib):
     assert f(1, 10, -1, 64) == 0
     assert f(1, 10, 1, 0) == 0
     assert f(9, 10, 1, 4) == 0
-    # INV nt*T*T + two panels of (n rounded up to 128) x (T rounded up to 32)
+    # INV nt*T*T + four panels of (n rounded up to 128) x (T rounded up to 32)
     # + TMP max(T*T, T*nrhs) + a 256-byte counter; for nrhs > 0 also two
     # buffers for the transposed solved block, (nrhs rounded up to 128) x (T
     # rounded up to 32), two sets of nt*T*T chain products and 8 partial
     # T x nrhs blocks; each rounded up to 256 bytes
     n, nrhs, T = 32768, 128, 512
-    el = (n // T) * T * T + 2 * n * T + T * T
+    el = (n // T) * T * T + 4 * n * T + T * T
     solve = 2 * 128 * 512 + 2 * (n // T) * T * T + 8 * T * nrhs
     assert f(1, n, 0, T) == el * 8 + 256
     assert f(1, n, nrhs, T) == (el + solve) * 8 + 256
     assert f(3, n, nrhs, T) == (el + solve) * 16 + 256
     n, nrhs, T = 1000, 7, 100
     up = lambda a, b: -(-a // b) * b
-    el = up(10 * 100 * 100, 32) + 2 * up(1024 * 128, 32) + up(100 * 100, 32)
+    el = up(10 * 100 * 100, 32) + 4 * up(1024 * 128, 32) + up(100 * 100, 32)
     solve = up(2 * 128 * 128, 32) + 2 * up(10 * 100 * 100, 32) + up(8 * 100 * 7, 32)
     assert f(1, n, 0, T) == el * 8 + 256
     assert f(1, n, nrhs, T) == (el + solve) * 8 + 256
