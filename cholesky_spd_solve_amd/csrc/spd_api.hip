@@ -320,15 +320,16 @@ static Layout make_layout(int64_t n, int64_t n_rhs, int64_t T_A, int64_t esize)
 // region 256-byte aligned).  M (n x n, ld n) holds the full Hermitian A and
 // then the result.
 //   itype 1: the substitution workspace for n right-hand sides (its INV and W
-//            regions also serve the blocked sweep), the two rank-2k operand
-//            panels P and Q (n rounded up to 128 rows, 2 x (T rounded up to
-//            32) columns), Y and V (n x T, ld n), and two T x T tiles;
+//            regions also serve the blocked sweep), two sets of the rank-2k
+//            operand panels P and Q (n rounded up to 128 rows, 2 x (T rounded
+//            up to 32) columns; one step ahead), Y and V (n x T, ld n), and two
+//            T x T tiles;
 //   itypes 2, 3: two square matrices of order n rounded up to 128 (L^H, and
 //            the stacked row panels w_k), two operand panels P and Q as for
 //            itype 1, the lower triangles of L's diagonal blocks and their
 //            products (nt T x T tiles each), and two T x n blocks.
 struct GstLayout {
-    int64_t T, nt, m, solve, p, q, y, v, d, t1, lh, wf, ld, ldg, total;
+    int64_t T, nt, m, solve, p, q, p2, q2, y, v, d, t1, lh, wf, ld, ldg, total;
 };
 
 static GstLayout make_gst_layout(int itype, int64_t n, int64_t T_A, int64_t esize)
@@ -346,6 +347,10 @@ static GstLayout make_gst_layout(int itype, int64_t n, int64_t T_A, int64_t esiz
         G.p = o;
         o += align_up(pw, al);
         G.q = o;
+        o += align_up(pw, al);
+        G.p2 = o;
+        o += align_up(pw, al);
+        G.q2 = o;
         o += align_up(pw, al);
         G.y = o;
         o += align_up(n * G.T, al);
@@ -808,6 +813,9 @@ struct Solver {
             constexpr int KBL = sizeof(R) == 8 ? 16 : 32;  // slice depth of the 64-row tiles
             const bool big = m >= 16384;
             if (n > 64) {
+                if (m >= 24576)  // 64 x 64 tiles: twice the workgroups (measured 10-15 % faster here)
+                    return vec ? rect_cfg<64, 64, KBL, 2, 2, PT, true>(P, ldp, Q, ldq, C, ldc, m, n, kp, kvalid, info, s)
+                               : rect_cfg<64, 64, KBL, 2, 2, PT, false>(P, ldp, Q, ldq, C, ldc, m, n, kp, kvalid, info, s);
                 if (big)
                     return vec ? rect_cfg<64, 128, KBL, 2, 4, PT, true>(P, ldp, Q, ldq, C, ldc, m, n, kp, kvalid, info, s)
                                : rect_cfg<64, 128, KBL, 2, 4, PT, false>(P, ldp, Q, ldq, C, ldc, m, n, kp, kvalid, info, s);
@@ -1212,14 +1220,17 @@ struct Solver {
         const int64_t T = SL.T, nt = SL.nt, kh = align_up(T, SYRK_KP);
         E *sw = (E *)work + G.solve;
         E *Inv = sw + SL.inv;
-        E *P = (E *)work + G.p, *Q = (E *)work + G.q, *Y = (E *)work + G.y, *V = (E *)work + G.v;
+        E *P[2] = {(E *)work + G.p, (E *)work + G.p2}, *Q[2] = {(E *)work + G.q, (E *)work + G.q2};
+        E *Y = (E *)work + G.y, *V = (E *)work + G.v;
         E *D = (E *)work + G.d, *T1 = (E *)work + G.t1;
         SPD_TRY(all_inverses(n, Lb, ldl, T, nt, Inv, sw + SL.w, info, s));
-        for (int64_t k = 0; k < nt; ++k) {
+        // block k's diagonal C_kk (from its current lower triangle) and, below
+        // it, Y - L21 C_kk back into M and the rank-2k operands into P[q], Q[q]
+        auto prep = [&](int64_t k, int q, hipStream_t st) -> int {
             const int64_t c0 = k * T, tk = std::min(T, n - c0), r0 = c0 + tk, m = n - r0;
             E *Mkk = M + c0 + c0 * n;
             const E *Wk = Inv + k * T * T;
-            SPD_TRY(herm_full(Mkk, n, D, T, tk, s));  // its lower triangle is current
+            SPD_TRY(herm_full(Mkk, n, D, T, tk, st));
             Gemm g1;  // T1 = W11 A11
             g1.A = Wk;
             g1.lda = T;
@@ -1231,7 +1242,7 @@ struct Solver {
             g1.kmode = KM_END_BY_I;
             g1.info = info;
             g1.small = true;
-            SPD_TRY((gemm<R, CPLX>(NN, g1, s)));
+            SPD_TRY((gemm<R, CPLX>(NN, g1, st)));
             Gemm g2;  // C11 = T1 W11^H, the whole tile
             g2.A = T1;
             g2.lda = T;
@@ -1243,9 +1254,9 @@ struct Solver {
             g2.kmode = KM_END_BY_J;
             g2.info = info;
             g2.small = true;
-            SPD_TRY((gemm<R, CPLX>(NT, g2, s)));
+            SPD_TRY((gemm<R, CPLX>(NT, g2, st)));
             if (m <= 0)
-                break;
+                return 0;
             Gemm g3;  // Y = A21 W11^H
             g3.A = M + r0 + c0 * n;
             g3.lda = n;
@@ -1257,7 +1268,7 @@ struct Solver {
             g3.n = g3.k = tk;
             g3.kmode = KM_END_BY_J;
             g3.info = info;
-            SPD_TRY((gemm<R, CPLX>(NT, g3, s)));
+            SPD_TRY((gemm<R, CPLX>(NT, g3, st)));
             Gemm g4;  // V = L21 C11
             g4.A = Lb + r0 + c0 * ldl;
             g4.lda = ldl;
@@ -1268,22 +1279,62 @@ struct Solver {
             g4.m = m;
             g4.n = g4.k = tk;
             g4.info = info;
-            SPD_TRY((gemm<R, CPLX>(NN, g4, s)));
+            SPD_TRY((gemm<R, CPLX>(NN, g4, st)));
             const int64_t ldw = align_up(m, SYRK_LDW);
-            SPD_VALIDATE(check_gst_pack<E>(Y, n, V, n, Lb + r0 + c0 * ldl, ldl, P, Q, ldw, M + r0 + c0 * n, n, m, tk,
-                                           kh, g_chk));
+            SPD_VALIDATE(check_gst_pack<E>(Y, n, V, n, Lb + r0 + c0 * ldl, ldl, P[q], Q[q], ldw, M + r0 + c0 * n, n,
+                                           m, tk, kh, g_chk));
             const int64_t pb = std::min<int64_t>(cdiv(ldw * kh, 256), 8192);
-            gst_pack_kernel<R, CPLX><<<dim3((unsigned)pb), dim3(256), 0, s>>>(Y, n, V, n, Lb + r0 + c0 * ldl, ldl, P, Q,
-                                                                              ldw, M + r0 + c0 * n, n, m, tk, kh);
+            gst_pack_kernel<R, CPLX><<<dim3((unsigned)pb), dim3(256), 0, st>>>(
+                Y, n, V, n, Lb + r0 + c0 * ldl, ldl, P[q], Q[q], ldw, M + r0 + c0 * n, n, m, tk, kh);
             SPD_CHECK_LAUNCH("gst_pack_kernel");
-            ProfScope ps(PROF_SYRK, FMUL * 2.0 * (double)m * (m + 1) * tk, s);
-            Syr2 x;  // A22 -= P Q^H = Z L21^H + L21 Z^H
-            x.V = Q;
-            SPD_TRY(syrk(m, P, ldw, 2 * kh, 2 * tk, M + r0 + r0 * n, n, 0, info, s, x));
+            return 0;
+        };
+        // A22 -= P Q^H = Z L21^H + L21 Z^H over rows and columns from r (a
+        // multiple of T past the block's end; cols > 0: that many columns only)
+        auto update = [&](int64_t k, int q, int64_t r, int64_t cols, int cls, hipStream_t st) -> int {
+            const int64_t c0 = k * T, tk = std::min(T, n - c0), r0 = c0 + tk, m = n - r;
+            if (m <= 0)
+                return 0;
+            const int64_t w = cols > 0 ? std::min(cols, m) : m;
+            ProfScope ps(cls, FMUL * (double)w * (2.0 * m - w + 1.0) * 2.0 * tk, st);
+            Syr2 x;
+            x.V = Q[q] + (r - r0);
+            return syrk(m, P[q] + (r - r0), align_up(n - r0, SYRK_LDW), 2 * kh, 2 * tk, M + r + r * n, n, cols, info,
+                        st, x);
+        };
+        const bool ahead = lookahead_enabled() && T % syrk_bm() == 0 && nt >= 3;
+        if (!ahead) {
+            for (int64_t k = 0; k < nt; ++k) {
+                SPD_TRY(prep(k, 0, s));
+                SPD_TRY(update(k, 0, std::min(n, (k + 1) * T), 0, PROF_SYRK, s));
+            }
+        } else {
+            // one step ahead on the auxiliary stream, as in potrf: tile column
+            // k+1 by block k's operands, then block k+1's preparation into the
+            // other operand buffers; the caller's stream updates the rest
+            Lookahead la;
+            SPD_TRY(la.begin(s));
+            hipStream_t sl = la.look;
+            SPD_TRY(prep(0, 0, sl));
+            SPD_TRY(la.record(la.ev_panel, sl));
+            int q = 0;
+            for (int64_t k = 0; k + 1 < nt; ++k) {
+                const int64_t r0 = (k + 1) * T;
+                SPD_TRY(la.wait(s, la.ev_panel));  // operands of block k
+                if (k > 0)
+                    SPD_TRY(la.wait(sl, la.ev_rest));  // the update of step k-1 reached tile column k+1
+                SPD_TRY(update(k, q, r0, T, PROF_SYRK_AUX, sl));
+                SPD_TRY(prep(k + 1, q ^ 1, sl));
+                SPD_TRY(la.record(la.ev_panel, sl));
+                SPD_TRY(update(k, q, r0 + T, 0, PROF_SYRK, s));
+                SPD_TRY(la.record(la.ev_rest, s));
+                q ^= 1;
+            }
+            SPD_TRY(la.wait(s, la.ev_panel));  // join: the last block's C_kk
         }
         // C21 blocks: the forward substitution of the block strictly-lower part
         if (rect_usable(ldl)) {
-            E *lp[2] = {P, Q};  // the rank-2k panels are free now; each holds ldq x kq
+            E *lp[2] = {P[0], Q[0]};  // the rank-2k panels are free now; each holds ldq x kq
             return potrs_blocks(n, n, Lb, ldl, M, n, SL, info, sw, s, false, true, lp);
         }
         return potrs_general(n, n, Lb, ldl, M, n, SL, info, sw, s, false, true);

@@ -83,12 +83,12 @@ def test_sygst_workspace_size(lib):
         n, T = 1000, 128
         al = 256 // es
         sq = up(n * n, al)
-        # itype 1: M, the substitution workspace for n right-hand sides, the
-        # rank-2k panels P and Q ((n up to 128) x 2 (T up to 32)), Y and V
-        # (n x T), two T x T tiles
+        # itype 1: M, the substitution workspace for n right-hand sides, two
+        # sets of the rank-2k panels P and Q ((n up to 128) x 2 (T up to 32)),
+        # Y and V (n x T), two T x T tiles
         solve = lib.spd_workspace_size(dt, n, n, T) // es
         pw = up(up(n, 128) * 2 * up(T, 32), al)
-        assert f(dt, 1, n, T) == (sq + up(solve, al) + 2 * pw + 2 * up(n * T, al) + 2 * up(T * T, al)) * es
+        assert f(dt, 1, n, T) == (sq + up(solve, al) + 4 * pw + 2 * up(n * T, al) + 2 * up(T * T, al)) * es
         # itypes 2 and 3: M, the panels P and Q, two squares of order n up to
         # 128, two sets of nt T x T tiles, two T x n blocks
         nt = -(-n // T)
