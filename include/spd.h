@@ -136,9 +136,9 @@ int spd_gp_loglik(spd_dtype_t dt, int64_t n, int64_t n_rhs, const void *dA, int6
                   void *d_work, size_t work_bytes, void *stream);
 
 /* Bytes of device workspace spd_sygst needs; 0 for invalid arguments
- * (unknown dtype or itype, n <= 0, T_A < 1).  About n^2 elements plus the
- * substitution workspace for n right-hand sides (itype 1), or 3 n^2 elements
- * (itypes 2 and 3). */
+ * (unknown dtype or itype, n <= 0, T_A < 1).  About n^2 + 10 n T_A elements
+ * plus the substitution workspace for n right-hand sides (itype 1), or
+ * 3 n^2 + 8 n T_A elements (itypes 2 and 3), n rounded up to 128. */
 size_t spd_sygst_workspace_size(spd_dtype_t dt, int itype, int64_t n, int64_t T_A);
 
 /* Reduction of a Hermitian-definite generalized eigenproblem to standard form
