@@ -250,8 +250,9 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(A0, B0, n, nrhs, fmul, args.cpu_seconds, gp)
 
-    metric = ("GP marginal log-likelihood (potrf + forward substitution) TFLOP/s, fp64 N=32768, 1 MI355X" if gp
-              else "potrf+potrs TFLOP/s and % of MFMA peak, fp64 N=32768, 1 MI355X")
+    dname = {"f64": "fp64", "f32": "fp32", "c128": "complex128", "c64": "complex64"}[dt]
+    metric = (f"GP marginal log-likelihood (potrf + forward substitution) TFLOP/s, {dname} N={n}, 1 MI355X" if gp
+              else f"potrf+potrs TFLOP/s and % of MFMA peak, {dname} N={n}, 1 MI355X")
     workload = (f"{dt} Gaussian-process log-likelihood N={n}, {nrhs} residual columns, T_A={T}, "
                 f"A = G G^H/N + {cfg['delta']} I, seed {args.seed}" if gp else
                 f"{dt} SPD solve N={n} N_RHS={nrhs} T_A={T}, A = G G^H/N + {cfg['delta']} I, seed {args.seed}")
