@@ -387,7 +387,9 @@ static GstLayout make_gst_layout(int itype, int64_t n, int64_t T_A, int64_t esiz
 
 // The two-step schedule of potrf (trailing updates of depth 2T) is used unless
 // the environment sets SPD_TWO_STEP=0; it pairs steps while at least
-// two_step_rows() rows remain beyond the pair (SPD_TWO_STEP_ROWS, default 8192).
+// two_step_rows(T) rows remain beyond the pair (SPD_TWO_STEP_ROWS, default 40 T:
+// below that the auxiliary stream's two-tile chain, sharing the GPU with the
+// caller's update, outlasts it).
 static bool two_step_enabled()
 {
     static const bool on = [] {
@@ -397,10 +399,10 @@ static bool two_step_enabled()
     return on;
 }
 
-static int64_t two_step_rows()  // read at every call (tests vary it)
+static int64_t two_step_rows(int64_t T)  // read at every call (tests vary it)
 {
     const char *v = getenv("SPD_TWO_STEP_ROWS");
-    return v != nullptr ? std::max<int64_t>(0, atoll(v)) : INT64_C(8192);
+    return v != nullptr ? std::max<int64_t>(0, atoll(v)) : 40 * T;
 }
 
 // The lookahead schedule is on unless the environment sets SPD_LOOKAHEAD=0
@@ -1042,8 +1044,10 @@ struct Solver {
     // its panel.  Once fewer than two_step_rows() rows would remain beyond the
     // pair, the auxiliary stream's chain (two tiles) would be longer than the
     // caller's update, and the schedule continues one step at a time as in
-    // potrf.  Panels live in four buffers of one leading dimension; panel k's
-    // row 0 is row (k+1)T of A.
+    // potrf.  Step 0 is a single step whose auxiliary part solves tiles 1 and 2,
+    // so that the caller's first update starts after tile 0 alone.  Panels live
+    // in four buffers of one leading dimension; panel k's row 0 is row (k+1)T of
+    // A.
     static int potrf_pairs(int64_t n, E *A, int64_t lda, const Layout &L, E *Inv, int *info, int *ctr, void *work,
                            hipStream_t s)
     {
@@ -1053,19 +1057,28 @@ struct Solver {
         Lookahead la;
         SPD_TRY(la.begin(s));
         hipStream_t sl = la.look;
-        // tiles 0 and 1
+        // step 0 as a single step whose auxiliary part reaches two tiles ahead:
+        // tile columns 1 and 2 by W_0, tile 1, tile column 2 by W_1, tile 2;
+        // meanwhile the caller's stream applies W_0 from tile 3 on
         SPD_TRY(diag_panel(n, A, lda, T, 0, Inv, Wp(0), info, ctr, sl, ldw));
-        SPD_TRY(syrk(n - T, Wp(0), ldw, kp, T, C(1), lda, T, info, sl, aux_update()));
-        SPD_TRY(diag_panel(n, A, lda, T, T, Inv, Wp(1), info, ctr, sl, ldw));
         SPD_TRY(la.record(la.ev_panel, sl));
+        SPD_TRY(la.wait(s, la.ev_panel));  // panel 0
+        SPD_TRY(syrk(n - T, Wp(0), ldw, kp, T, C(1), lda, 2 * T, info, sl, aux_update()));
+        SPD_TRY(diag_panel(n, A, lda, T, T, Inv, Wp(1), info, ctr, sl, ldw));
+        SPD_TRY(syrk(n - 2 * T, Wp(1), ldw, kp, T, C(2), lda, T, info, sl, aux_update()));
+        SPD_TRY(diag_panel(n, A, lda, T, 2 * T, Inv, Wp(2), info, ctr, sl, ldw));
+        SPD_TRY(la.record(la.ev_panel, sl));
+        if (3 * T < n)
+            SPD_TRY(syrk(n - 3 * T, Wp(0) + 2 * T, ldw, kp, T, C(3), lda, 0, info, s));
+        SPD_TRY(la.record(la.ev_rest, s));
         // pairs: panels a and a+1 solved, tile column a+1 updated by every panel
         // before it, tiles from a+2 on by the panels before a
-        int64_t a = 0;
-        for (; a + 1 < nt && n - (a + 4) * T >= two_step_rows(); a += 2) {
+        const int64_t pair_rows = two_step_rows(T);
+        int64_t a = 1;
+        for (; a + 1 < nt && n - (a + 4) * T >= pair_rows; a += 2) {
             const int64_t c = a + 2, d = a + 3, e = a + 4;
             SPD_TRY(la.wait(s, la.ev_panel));  // panels a and b
-            if (a > 0)
-                SPD_TRY(la.wait(sl, la.ev_rest));  // the pair before has updated tile columns c and d
+            SPD_TRY(la.wait(sl, la.ev_rest));  // the update before has reached tile columns c and d
             Syr2 x;
             x.kp1 = kp;
             // tile columns c and d by [W_a | W_b] (W_a's rows from tile c start at its row T)
@@ -1084,8 +1097,7 @@ struct Solver {
         // single steps from k = a: tile column a+1 and panel a+1 are done already,
         // so step a only applies W_a to the tiles from a+2 on
         SPD_TRY(la.wait(s, la.ev_panel));
-        if (a > 0)
-            SPD_TRY(la.wait(sl, la.ev_rest));
+        SPD_TRY(la.wait(sl, la.ev_rest));
         if ((a + 2) * T < n)
             SPD_TRY(syrk(n - (a + 2) * T, Wp(a) + T, ldw, kp, T, C(a + 2), lda, 0, info, s));
         SPD_TRY(la.record(la.ev_rest, s));
