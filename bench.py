@@ -3,7 +3,9 @@
 
 One step = the whole solve path on one synthetic input: Cholesky
 factorization of A (in place), log det from the factor, and the blocked
-forward/back substitution of B (in place).  Inputs are generated once, with
+forward/back substitution of B (in place), by default as one spd_posv call
+(which overlaps the forward substitution with the factorization; --separate
+times spd_potrf, spd_logdet and spd_potrs instead).  Inputs are generated once, with
 a pristine copy kept in HBM; before every step A and B are restored from it
 by a device-to-device copy that is outside the step's timed events.
 
@@ -76,6 +78,9 @@ def parse():
                         "log-likelihood of the N_RHS residual columns (forward substitution + reduction); "
                         "sygst: potrf of B + reduction of the generalized eigenproblem (A, B) to standard form")
     p.add_argument("--itype", type=int, choices=(1, 2, 3), default=1, help="problem type of --workload sygst")
+    p.add_argument("--separate", action="store_true",
+                   help="solve workload: time spd_potrf, spd_logdet and spd_potrs as three calls instead of the "
+                        "one-call spd_posv")
     return p.parse_args()
 
 
@@ -145,8 +150,15 @@ def main():
         A.copy_(A0)
         B.copy_(B0)
 
+    fused = not gp and not args.separate
+
     def step(ev):
         ev[0].record(stream)
+        if fused:  # potrf, logdet and potrs in one call (spd_posv)
+            spd.posv(A, B, T, info=info, logdet_out=ldbuf if cfg["logdet"] else None, work=work)
+            for e in ev[1:]:
+                e.record(stream)
+            return
         spd.potrf(A, T, info=info, work=work)
         ev[1].record(stream)
         if cfg["logdet"] and not gp:
@@ -222,7 +234,7 @@ def main():
         log(f"[bench] backward error {check['backward_error']:.3e} (bound {check['bound_64_n_eps']:.3e})")
 
     value = flops / (ms * 1e-3) / 1e12
-    potrf_tf = flops_potrf / (float(np.mean(potrf_ms)) * 1e-3) / 1e12
+    potrf_tf = None if fused else flops_potrf / (float(np.mean(potrf_ms)) * 1e-3) / 1e12
     syrk_avg_ms = syrk_ms / max(syrk_launches, 1)
     syrk_achieved = (syrk_flops / syrk_launches) / (syrk_avg_ms * 1e-3) / 1e12 if syrk_launches else None
     peak = PEAK[dt]
@@ -272,8 +284,11 @@ def main():
         "config": {"workload": workload, "n": n, "n_rhs": nrhs, "T_A": T, "logdet": cfg["logdet"] or gp},
         "pct_of_peak": 100.0 * value / peak,
         "potrf_tflops": potrf_tf,
-        "potrf_pct_of_peak": 100.0 * potrf_tf / peak,
-        "phase_ms": ({"potrf": float(np.mean(potrf_ms)), "gp_loglik": float(np.mean(potrs_ms))} if gp else
+        "potrf_pct_of_peak": None if potrf_tf is None else 100.0 * potrf_tf / peak,
+        "entry_points": ("spd_posv (potrf + logdet + potrs in one call)" if fused else
+                         "spd_potrf, spd_gp_loglik" if gp else "spd_potrf, spd_logdet, spd_potrs"),
+        "phase_ms": ({"posv": ms} if fused else
+                     {"potrf": float(np.mean(potrf_ms)), "gp_loglik": float(np.mean(potrs_ms))} if gp else
                      {"potrf": float(np.mean(potrf_ms)), "logdet": float(np.mean(logdet_ms)),
                       "potrs": float(np.mean(potrs_ms))}),
         "wall_ms_per_step_incl_restore": 1e3 * wall / args.steps,

@@ -31,7 +31,8 @@ DTYPE_CODE = {
     torch.complex64: SPD_C64,
     torch.complex128: SPD_C128,
 }
-SYMBOLS = ("spd_workspace_size", "spd_potrf", "spd_potrs", "spd_forward_solve", "spd_gp_loglik", "spd_logdet",
+SYMBOLS = ("spd_workspace_size", "spd_potrf", "spd_potrs", "spd_posv", "spd_forward_solve", "spd_gp_loglik",
+           "spd_logdet",
            "spd_sygst_workspace_size", "spd_sygst", "spd_last_error", "spd_profile_enable", "spd_profile_read",
            "spd_debug_validate")
 SPD_ERR_HIP, SPD_ERR_CHECK = 1, 2
@@ -72,6 +73,8 @@ def load():
             lib.spd_potrf.restype = i32
             lib.spd_potrs.argtypes = [i32, i64, i64, vp, i64, vp, i64, i64, vp, vp, sz, vp]
             lib.spd_potrs.restype = i32
+            lib.spd_posv.argtypes = [i32, i64, i64, vp, i64, vp, i64, i64, vp, vp, vp, sz, vp]
+            lib.spd_posv.restype = i32
             lib.spd_forward_solve.argtypes = [i32, i64, i64, vp, i64, vp, i64, i64, vp, vp, sz, vp]
             lib.spd_forward_solve.restype = i32
             lib.spd_gp_loglik.argtypes = [i32, i64, i64, vp, i64, vp, i64, i64, vp, vp, vp, sz, vp]
@@ -180,6 +183,28 @@ def potrs(L: torch.Tensor, B: torch.Tensor, T_A: int, info: torch.Tensor | None 
                           work.numel(), ctypes.c_void_p(_stream(stream)))
     _check(rc, "spd_potrs")
     return B
+
+
+def posv(A: torch.Tensor, B: torch.Tensor, T_A: int, info: torch.Tensor | None = None,
+         logdet_out: torch.Tensor | None = None, work: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Factor A (in place, as potrf), write log det(A) into ``logdet_out``
+    (device float64, optional) and overwrite B with the solution, in one
+    call.  Returns the device int32 ``info``."""
+    lda = _colmajor(A, "A")
+    ldb = _colmajor(B, "B")
+    n, nrhs = B.shape
+    if A.shape != (n, n):
+        raise ValueError("A must be n x n with n = B.shape[0]")
+    if B.dtype != A.dtype:
+        raise TypeError("A and B must have the same dtype")
+    if info is None:
+        info = torch.empty(1, dtype=torch.int32, device=A.device)
+    if work is None:
+        work = workspace(A.dtype, n, nrhs, T_A, A.device)
+    rc = load().spd_posv(_code(A), n, nrhs, _ptr(A), lda, _ptr(B), ldb, int(T_A), _ptr(info), _ptr(logdet_out),
+                         _ptr(work), work.numel(), ctypes.c_void_p(_stream(stream)))
+    _check(rc, "spd_posv")
+    return info
 
 
 def forward_solve(L: torch.Tensor, B: torch.Tensor, T_A: int, info: torch.Tensor | None = None,

@@ -23,6 +23,7 @@
 #include <mutex>
 #include <string>
 #include <vector>
+#include <functional>
 
 #include "spd.h"
 #include "spd_gemm.hpp"
@@ -422,18 +423,18 @@ static bool lookahead_enabled()
 // ends.  Default priority, non-blocking with respect to the null stream.  In a
 // dry run (no HIP calls) both schedules run on the caller's stream.
 struct AuxStreams {
-    hipStream_t look = nullptr;
-    hipEvent_t ev_fork = nullptr, ev_panel = nullptr, ev_rest = nullptr;
+    hipStream_t look = nullptr, look2 = nullptr;
+    hipEvent_t ev_fork = nullptr, ev_panel = nullptr, ev_rest = nullptr, ev_fw = nullptr;
 };
 
 struct Lookahead {
-    hipStream_t look = nullptr;
-    hipEvent_t ev_fork = nullptr, ev_panel = nullptr, ev_rest = nullptr;
+    hipStream_t look = nullptr, look2 = nullptr;  // look2: the fused solve's forward substitution
+    hipEvent_t ev_fork = nullptr, ev_panel = nullptr, ev_rest = nullptr, ev_fw = nullptr;
 
     int begin(hipStream_t s)
     {
         if (g_validate == 2) {
-            look = s;
+            look = look2 = s;
             return 0;
         }
         static thread_local std::vector<std::pair<int, AuxStreams>> per_device;
@@ -447,21 +448,25 @@ struct Lookahead {
                 x = &pd.second;
         if (x == nullptr) {
             AuxStreams n;
-            if ((e = hipStreamCreateWithFlags(&n.look, hipStreamNonBlocking)) != hipSuccess)
+            if ((e = hipStreamCreateWithFlags(&n.look, hipStreamNonBlocking)) != hipSuccess ||
+                (e = hipStreamCreateWithFlags(&n.look2, hipStreamNonBlocking)) != hipSuccess)
                 return hip_fail(e, "hipStreamCreateWithFlags");
-            for (hipEvent_t *ev : {&n.ev_fork, &n.ev_panel, &n.ev_rest})
+            for (hipEvent_t *ev : {&n.ev_fork, &n.ev_panel, &n.ev_rest, &n.ev_fw})
                 if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess)
                     return hip_fail(e, "hipEventCreateWithFlags");
             per_device.emplace_back(dev, n);
             x = &per_device.back().second;
         }
         look = x->look;
+        look2 = x->look2;
         ev_fork = x->ev_fork;
         ev_panel = x->ev_panel;
         ev_rest = x->ev_rest;
-        // the auxiliary stream starts after everything already queued on s
+        ev_fw = x->ev_fw;
+        // the auxiliary streams start after everything already queued on s
         SPD_TRY_HIP(hipEventRecord(ev_fork, s), "hipEventRecord");
         SPD_TRY_HIP(hipStreamWaitEvent(look, ev_fork, 0), "hipStreamWaitEvent");
+        SPD_TRY_HIP(hipStreamWaitEvent(look2, ev_fork, 0), "hipStreamWaitEvent");
         return 0;
     }
     int record(hipEvent_t ev, hipStream_t st)
@@ -982,7 +987,20 @@ struct Solver {
     // to the rest of the trailing matrix.  Events order the two streams:
     // panel k is ready before stream s uses it, and the update of step k-1 has
     // finished before the auxiliary stream touches tile column k+1.
-    static int potrf(int64_t n, E *A, int64_t lda, int64_t T_A, int *info, void *work, hipStream_t s)
+    // Called as tiles of L become final (tiles [k0, k1)), on the host, right
+    // after the auxiliary stream's event for them is recorded; the fused
+    // solve enqueues its forward substitution steps from it.
+    typedef std::function<int(int64_t, int64_t)> PanelHook;
+
+    static bool two_step_schedule(int64_t T, int64_t nt)
+    {
+        return lookahead_enabled() && (T % syrk_bm() == 0) && nt >= 3 && two_step_enabled();
+    }
+
+    // hook (the two-step schedule only): every tile's inverse is kept (tile k
+    // at Inv + k T^2) and hook is called as tiles become final
+    static int potrf(int64_t n, E *A, int64_t lda, int64_t T_A, int *info, void *work, hipStream_t s,
+                     const PanelHook *hook = nullptr)
     {
         SPD_TRY(set_info(info, s));
         if (n == 0)
@@ -994,7 +1012,11 @@ struct Solver {
         if constexpr (!CPLX)
             SPD_TRY(set_info(ctr, s));
         E *Wb[2] = {(E *)work + L.w, (E *)work + L.w + L.wsz};
-        SPD_TRY(zero2d<E>(Inv, T, T, T, s));
+        SPD_TRY(zero2d<E>(Inv, T, T, hook != nullptr ? nt * T : T, s));
+        if (hook != nullptr && !two_step_schedule(T, nt)) {
+            g_last_error = "panel hook needs the two-step schedule";
+            return SPD_ERR_HIP;
+        }
         const bool lookahead = lookahead_enabled() && (T % syrk_bm() == 0) && nt >= 3;
         if (!lookahead) {
             for (int64_t c0 = 0; c0 < n; c0 += T) {
@@ -1007,7 +1029,7 @@ struct Solver {
             return 0;
         }
         if (two_step_enabled())
-            return potrf_pairs(n, A, lda, L, Inv, info, ctr, work, s);
+            return potrf_pairs(n, A, lda, L, Inv, info, ctr, work, s, hook);
         Lookahead la;
         SPD_TRY(la.begin(s));
         hipStream_t sl = la.look;
@@ -1048,26 +1070,33 @@ struct Solver {
     // so that the caller's first update starts after tile 0 alone.  Panels live
     // in four buffers of one leading dimension; panel k's row 0 is row (k+1)T of
     // A.
-    static int potrf_pairs(int64_t n, E *A, int64_t lda, const Layout &L, E *Inv, int *info, int *ctr, void *work,
-                           hipStream_t s)
+    static int potrf_pairs(int64_t n, E *A, int64_t lda, const Layout &L, E *Inv0, int *info, int *ctr, void *work,
+                           hipStream_t s, const PanelHook *hook = nullptr)
     {
         const int64_t T = L.T, nt = L.nt, ldw = align_up(n, SYRK_LDW), kp = align_up(T, SYRK_KP);
         auto Wp = [&](int64_t k) { return (E *)work + L.w + (k % 4) * L.wsz; };
         auto C = [&](int64_t k) { return A + k * T * (1 + lda); };  // trailing matrix from tile k
+        auto Iv = [&](int64_t k) { return hook != nullptr ? Inv0 + k * T * T : Inv0; };
+        auto diag_panel = [&](int64_t c0, E *Wk, hipStream_t st) {
+            return Solver::diag_panel(n, A, lda, T, c0, Iv(c0 / T), Wk, info, ctr, st, ldw);
+        };
+        auto done = [&](int64_t k0, int64_t k1) { return hook != nullptr ? (*hook)(std::min(k0, nt), std::min(k1, nt)) : 0; };
         Lookahead la;
         SPD_TRY(la.begin(s));
         hipStream_t sl = la.look;
         // step 0 as a single step whose auxiliary part reaches two tiles ahead:
         // tile columns 1 and 2 by W_0, tile 1, tile column 2 by W_1, tile 2;
         // meanwhile the caller's stream applies W_0 from tile 3 on
-        SPD_TRY(diag_panel(n, A, lda, T, 0, Inv, Wp(0), info, ctr, sl, ldw));
+        SPD_TRY(diag_panel(0, Wp(0), sl));
         SPD_TRY(la.record(la.ev_panel, sl));
+        SPD_TRY(done(0, 1));
         SPD_TRY(la.wait(s, la.ev_panel));  // panel 0
         SPD_TRY(syrk(n - T, Wp(0), ldw, kp, T, C(1), lda, 2 * T, info, sl, aux_update()));
-        SPD_TRY(diag_panel(n, A, lda, T, T, Inv, Wp(1), info, ctr, sl, ldw));
+        SPD_TRY(diag_panel(T, Wp(1), sl));
         SPD_TRY(syrk(n - 2 * T, Wp(1), ldw, kp, T, C(2), lda, T, info, sl, aux_update()));
-        SPD_TRY(diag_panel(n, A, lda, T, 2 * T, Inv, Wp(2), info, ctr, sl, ldw));
+        SPD_TRY(diag_panel(2 * T, Wp(2), sl));
         SPD_TRY(la.record(la.ev_panel, sl));
+        SPD_TRY(done(1, 3));
         if (3 * T < n)
             SPD_TRY(syrk(n - 3 * T, Wp(0) + 2 * T, ldw, kp, T, C(3), lda, 0, info, s));
         SPD_TRY(la.record(la.ev_rest, s));
@@ -1086,10 +1115,11 @@ struct Solver {
             x.aux = true;
             SPD_TRY(syrk(n - c * T, Wp(a) + T, ldw, 2 * kp, 2 * T, C(c), lda, 2 * T, info, sl, x));
             x.aux = false;
-            SPD_TRY(diag_panel(n, A, lda, T, c * T, Inv, Wp(c), info, ctr, sl, ldw));
+            SPD_TRY(diag_panel(c * T, Wp(c), sl));
             SPD_TRY(syrk(n - d * T, Wp(c), ldw, kp, T, C(d), lda, T, info, sl, aux_update()));
-            SPD_TRY(diag_panel(n, A, lda, T, d * T, Inv, Wp(d), info, ctr, sl, ldw));
+            SPD_TRY(diag_panel(d * T, Wp(d), sl));
             SPD_TRY(la.record(la.ev_panel, sl));
+            SPD_TRY(done(c, d + 1));
             x.W2 = Wp(a + 1) + 2 * T;  // W_b's rows from tile e
             SPD_TRY(syrk(n - e * T, Wp(a) + 3 * T, ldw, 2 * kp, 2 * T, C(e), lda, 0, info, s, x));
             SPD_TRY(la.record(la.ev_rest, s));
@@ -1105,8 +1135,9 @@ struct Solver {
             SPD_TRY(la.wait(s, la.ev_panel));  // panel k
             SPD_TRY(la.wait(sl, la.ev_rest));  // the update of step k-1 reached tile column k+1
             SPD_TRY(syrk(n - (k + 1) * T, Wp(k), ldw, kp, T, C(k + 1), lda, T, info, sl, aux_update()));
-            SPD_TRY(diag_panel(n, A, lda, T, (k + 1) * T, Inv, Wp(k + 1), info, ctr, sl, ldw));
+            SPD_TRY(diag_panel((k + 1) * T, Wp(k + 1), sl));
             SPD_TRY(la.record(la.ev_panel, sl));
+            SPD_TRY(done(k + 1, k + 2));
             if ((k + 2) * T < n)
                 SPD_TRY(syrk(n - (k + 2) * T, Wp(k) + T, ldw, kp, T, C(k + 2), lda, 0, info, s));
             SPD_TRY(la.record(la.ev_rest, s));
@@ -1184,6 +1215,68 @@ struct Solver {
             SPD_CHECK_LAUNCH("gp_loglik_kernel");
             return 0;
         }
+    }
+
+    // Fused solve: potrf, log det (optional) and potrs in one call.  With the
+    // two-step factorization schedule (real types, block-update kernel usable)
+    // the forward substitution runs on a second auxiliary stream, one block as
+    // soon as its tile of L is final (the factorization keeps every tile's
+    // inverse), so that it fills the factorization's chain-bound tail; the
+    // back substitution follows.  Otherwise the three calls in sequence.
+    static int posv(int64_t n, int64_t nrhs, E *A, int64_t lda, E *B, int64_t ldb, int64_t T_A, int *info,
+                    double *logdet_out, void *work, hipStream_t s)
+    {
+        const Layout L = make_layout(std::max<int64_t>(n, 1), nrhs, T_A, sizeof(E));
+        bool fused = !CPLX && n > 0 && nrhs > 0 && rect_usable(lda) && two_step_schedule(L.T, L.nt);
+        if (!fused) {
+            SPD_TRY(potrf(n, A, lda, T_A, info, work, s));
+            if (logdet_out != nullptr)
+                SPD_TRY(logdet(n, A, lda, info, logdet_out, s));
+            return potrs(n, nrhs, A, lda, B, ldb, T_A, info, work, s);
+        }
+        const int64_t T = L.T;
+        // The forward steps run beside the factorization, which uses INV, W and
+        // its counter (placed for n_rhs = 0, possibly inside this layout's
+        // TMP): they take their block row from PART and their transposed
+        // block from the first operand buffer, both beyond the factorization's
+        // regions.
+        E *Inv = (E *)work + L.inv;
+        E *Tmp = (E *)work + L.part;
+        E *Qf = (E *)work + L.q;
+        const bool vec = rect_vec(A, lda, T);
+        Lookahead la;  // the factorization's streams and events (shared per thread and device)
+        SPD_TRY(la.begin(s));
+        hipStream_t fs = la.look2;
+        auto step = [&](int64_t k) -> int {  // Y_k = inv(L_kk) B_k, then B below -= L_panel Y_k
+            const int64_t c0 = k * T, tk = std::min(T, n - c0), r0 = c0 + tk, kp = align_up(tk, RECT_KB);
+            SPD_TRY(apply_inv(Inv, k, T, B, ldb, c0, tk, nrhs, Tmp, false, info, fs));
+            SPD_TRY(copy_t(B + c0, ldb, Qf, L.ldq, Tmp, T, tk, nrhs, kp, info, fs));
+            if (r0 < n)
+                SPD_TRY(rect<false>(A + r0 + c0 * lda, lda, Qf, L.ldq, B + r0, ldb, n - r0, nrhs, kp, tk, vec, info,
+                                    fs));
+            return 0;
+        };
+        const PanelHook hook = [&](int64_t k0, int64_t k1) -> int {
+            if (k0 >= k1)
+                return 0;
+            SPD_TRY(la.wait(fs, la.ev_panel));  // tiles [k0, k1) of L are final
+            for (int64_t k = k0; k < k1; ++k)
+                SPD_TRY(step(k));
+            return 0;
+        };
+        {
+            ProfScope ps(PROF_SOLVE, FMUL * (double)n * n * nrhs, s);  // the factorization with the forward sweep
+            SPD_TRY(potrf(n, A, lda, T_A, info, work, s, &hook));
+            SPD_TRY(la.record(la.ev_fw, fs));
+            SPD_TRY(la.wait(s, la.ev_fw));
+        }
+        if (logdet_out != nullptr)
+            SPD_TRY(logdet(n, A, lda, info, logdet_out, s));
+        {
+            ProfScope ps(PROF_SOLVE, FMUL * (double)n * n * nrhs, s);
+            SPD_TRY(potrs_blocks(n, nrhs, A, lda, B, ldb, L, info, work, s, true, false, nullptr, false));
+        }
+        return nan_fill(n, nrhs, B, ldb, info, s);
     }
 
     // Reduction of the Hermitian-definite generalized eigenproblem to standard
@@ -1578,9 +1671,12 @@ struct Solver {
     // step's panel of L is packed into one of them, zero padded, and the block
     // updates run on the trailing-update kernel's rectangular mode (wide
     // right-hand sides).
+    //
+    // forward = false (the fused solve): only L^H X = B, with the tile
+    // inverses already in the workspace.
     static int potrs_blocks(int64_t n, int64_t nrhs, const E *A, int64_t lda, E *B, int64_t ldb, const Layout &L,
                             const int *info, void *work, hipStream_t s, bool backward, bool prefix = false,
-                            E *const *lp = nullptr)
+                            E *const *lp = nullptr, bool forward = true)
     {
         if (lp != nullptr && (backward || nrhs < n)) {
             g_last_error = "packed-panel block update is for the forward substitution with nrhs >= n";
@@ -1596,14 +1692,15 @@ struct Solver {
         E *Qb[2] = {(E *)work + L.q, (E *)work + L.q + L.qsz};
         E *GF = (E *)work + L.gf, *GB = (E *)work + L.gb, *Part = (E *)work + L.part;
         const bool vec = rect_vec(A, lda, T);
-        SPD_TRY(all_inverses(n, A, lda, T, nt, Inv, (E *)work + L.w, info, s));
+        if (forward)
+            SPD_TRY(all_inverses(n, A, lda, T, nt, Inv, (E *)work + L.w, info, s));
         SPD_TRY(zero2d<E>(Qb[0], L.ldq, L.ldq, 2 * L.kq, s));  // both buffers (adjacent, same ld)
         const int64_t nfull = n / T;  // whole blocks
         // split chain: depth split of each operand pair, sh parts of ks
         const int64_t sh = (T % 4 == 0 && T >= 64) ? 4 : (T % 2 == 0 && T >= 32) ? 2 : 1, ks = T / sh;
         const bool split = nfull >= 2 && !prefix;
         auto cols = [&](int64_t r) { return prefix ? std::min(nrhs, r * T) : nrhs; };  // columns of block row r
-        if (split) {
+        if (split && forward) {
             // GF_k = -inv(L_k+1,k+1) L_k+1,k for whole blocks k+1 (k = 0 .. nfull-2)
             Gemm g;
             g.A = Inv + T * T;
@@ -1722,6 +1819,7 @@ struct Solver {
                               st);
         };
         // ---- forward: L Y = B
+        if (forward) {
         SPD_TRY(solve_block(0, false, qi, sl));
         SPD_TRY(pack_panel(0, qi, sl));
         SPD_TRY(rec(la.ev_panel, sl));
@@ -1753,10 +1851,12 @@ struct Solver {
             SPD_TRY(rec(la.ev_rest, s));
             qi ^= 1;
         }
+        }
         if (!backward)
             return 0;
         // ---- backward: L^H X = Y, from the last block up
-        SPD_TRY(wait(sl, la.ev_rest));  // every forward update is done
+        if (forward)
+            SPD_TRY(wait(sl, la.ev_rest));  // every forward update is done
         qi ^= 1;
         SPD_TRY(solve_block(nt - 1, true, qi, sl));
         SPD_TRY(rec(la.ev_panel, sl));
@@ -2016,6 +2116,48 @@ int spd_sygst(spd_dtype_t dt, int itype, int64_t n, void *dA, int64_t lda, const
     case SPD_C128:
         return Solver<double, true>::gst(itype, n, (Elem<double, true>::type *)dA, lda,
                                          (const Elem<double, true>::type *)dL, ldl, T_A, d_info, d_work, s);
+    }
+    return -1;
+}
+
+int spd_posv(spd_dtype_t dt, int64_t n, int64_t n_rhs, void *dA, int64_t lda, void *dB, int64_t ldb, int64_t T_A,
+             int32_t *d_info, double *d_logdet, void *d_work, size_t work_bytes, void *stream)
+{
+    if (elem_size(dt) == 0) return -1;
+    if (n < 0 || n > INT32_MAX) return -2;
+    if (n_rhs < 0 || n_rhs > INT32_MAX) return -3;
+    if (dA == nullptr && n > 0) return -4;
+    if (lda < std::max<int64_t>(1, n)) return -5;
+    if (dB == nullptr && n > 0 && n_rhs > 0) return -6;
+    if (ldb < std::max<int64_t>(1, n)) return -7;
+    if (T_A < 1) return -8;
+    if (d_info == nullptr) return -9;
+    const size_t need = spd_workspace_size(dt, n, n_rhs, T_A);
+    if (d_work == nullptr && need > 0) return -11;
+    if (work_bytes < need) return -12;
+    if (g_validate) {
+        g_chk.begin();
+        g_chk.add(dA, matrix_bytes(dt, n, n, lda), true, "A");
+        g_chk.add(dB, matrix_bytes(dt, n, n_rhs, ldb), true, "B");
+        g_chk.add(d_info, 4, true, "info");
+        if (d_logdet != nullptr)
+            g_chk.add(d_logdet, sizeof(double), true, "logdet");
+        g_chk.add(d_work, work_bytes, true, "workspace");
+    }
+    hipStream_t s = (hipStream_t)stream;
+    switch (dt) {
+    case SPD_R32:
+        return Solver<float, false>::posv(n, n_rhs, (float *)dA, lda, (float *)dB, ldb, T_A, d_info, d_logdet, d_work,
+                                          s);
+    case SPD_R64:
+        return Solver<double, false>::posv(n, n_rhs, (double *)dA, lda, (double *)dB, ldb, T_A, d_info, d_logdet,
+                                           d_work, s);
+    case SPD_C64:
+        return Solver<float, true>::posv(n, n_rhs, (Elem<float, true>::type *)dA, lda, (Elem<float, true>::type *)dB,
+                                         ldb, T_A, d_info, d_logdet, d_work, s);
+    case SPD_C128:
+        return Solver<double, true>::posv(n, n_rhs, (Elem<double, true>::type *)dA, lda,
+                                          (Elem<double, true>::type *)dB, ldb, T_A, d_info, d_logdet, d_work, s);
     }
     return -1;
 }

@@ -26,10 +26,10 @@
  *   - All pointers named d_* or dA/dB are device pointers owned by the caller.
  *     The library allocates no device memory.  Its only state between calls is
  *     what spd_profile_* keeps while profiling is on and, for the lookahead
- *     schedule of spd_potrf, one auxiliary HIP stream (default priority,
- *     non-blocking) and three events per host thread and device, created on
- *     first use and kept until the process ends.  Calls from one host thread
- *     must not overlap on one device (they share that stream).
+ *     schedules, two auxiliary HIP streams (default priority, non-blocking)
+ *     and four events per host thread and device, created on first use and
+ *     kept until the process ends.  Calls from one host thread must not
+ *     overlap on one device (they share those streams).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *     the calls return without waiting for it.  spd_potrf may also run part of
  *     the factorization on its auxiliary stream, ordered with `stream` by
@@ -104,6 +104,25 @@ int spd_potrf(spd_dtype_t dt, int64_t n, void *dA, int64_t lda, int64_t T_A,
 int spd_potrs(spd_dtype_t dt, int64_t n, int64_t n_rhs, const void *dA, int64_t lda,
               void *dB, int64_t ldb, int64_t T_A, const int32_t *d_info,
               void *d_work, size_t work_bytes, void *stream);
+
+/* Solve A X = B in one call: the factorization of spd_potrf, log det(A) as
+ * spd_logdet (when d_logdet is not NULL) and the substitutions of spd_potrs
+ * (JAXMg paper, "Software design": potrs factors A and solves, optionally
+ * returning log det(A)).  The results are those of the three calls; with the
+ * default factorization schedule (real types) the forward substitution runs
+ * on a second auxiliary stream (default priority, non-blocking, created once
+ * per host thread and device like the first), one block as soon as its tile
+ * of L is final, so that it overlaps the factorization.
+ *   dA, lda   as spd_potrf: overwritten by L
+ *   dB, ldb   as spd_potrs: n x n_rhs, overwritten by X (NaN if d_info != 0)
+ *   d_info    device int32, written (as spd_potrf)
+ *   d_logdet  device double or NULL (NaN if d_info != 0)
+ *   d_work    workspace of >= spd_workspace_size(dt, n, n_rhs, T_A) bytes
+ * Argument numbers: dt=1 n=2 n_rhs=3 dA=4 lda=5 dB=6 ldb=7 T_A=8 d_info=9
+ * d_logdet=10 d_work=11 work_bytes=12. */
+int spd_posv(spd_dtype_t dt, int64_t n, int64_t n_rhs, void *dA, int64_t lda, void *dB,
+             int64_t ldb, int64_t T_A, int32_t *d_info, double *d_logdet, void *d_work,
+             size_t work_bytes, void *stream);
 
 /* Forward substitution only: overwrite B with Y = L^-1 B, from the factor of
  * spd_potrf (JAXMg paper, "Software design": the first of potrs' two

@@ -121,3 +121,17 @@ def test_dry_run_sygst(lib, itype, dt, n, T):
     for lda, ldl in ((n, n), (n + 3, n + 5)):
         rc = lib.spd_sygst(code, itype, n, vp(A), lda, vp(Lb), ldl, T, vp(info), vp(work), wbytes, None)
         assert rc == 0, (rc, lib.spd_last_error())
+
+
+@pytest.mark.parametrize("dt,n,nrhs,T", SHAPES + [("f64", 2000, 7, 128), ("f64", 1300, 130, 128)])
+def test_dry_run_posv(lib, dt, n, nrhs, T):
+    """The fused solve (the factorization with the forward substitution on a
+    second stream where the two-step schedule applies, the three calls
+    otherwise), with and without log det."""
+    code, es = CODE[dt], ES[CODE[dt]]
+    vp = ctypes.c_void_p
+    A, B, info, ld, work = BASE, 2 * BASE, 3 * BASE, 3 * BASE + 4096, 4 * BASE
+    wbytes = lib.spd_workspace_size(code, n, nrhs, T)
+    for logdet in (vp(ld), None):
+        rc = lib.spd_posv(code, n, nrhs, vp(A), n, vp(B), n, T, vp(info), logdet, vp(work), wbytes, None)
+        assert rc == 0, (rc, lib.spd_last_error())

@@ -349,3 +349,72 @@ def test_two_step_schedule_parity(gpu, dt, n, nrhs, T_A, monkeypatch):
     assert info_o == 0
     assert np.abs(np.tril(wide(L)) - Lo).max() <= L_TOL[dt] * np.abs(Lo).max()
     assert rel_err_cols(X, oracle.potrs(Lo, B_np)) <= X_TOL[dt]
+
+
+
+def posv_check(gpu, dt, n, nrhs, T_A, seed=31, lda_pad=0):
+    A = spdgen.make_A(n, dt, 0.5, seed, lda=n + lda_pad, device="cuda")
+    B = spdgen.make_B(n, nrhs, dt, seed, device="cuda")
+    A_np, B_np = wide(A), wide(B)
+    ld = torch.zeros(1, dtype=torch.float64, device="cuda")
+    info = gpu.posv(A, B, T_A, logdet_out=ld)
+    torch.cuda.synchronize()
+    assert int(info.item()) == 0
+    Lo, info_o = oracle.potrf(A_np)
+    assert info_o == 0
+    assert np.abs(np.tril(wide(A)) - Lo).max() <= L_TOL[dt] * np.abs(Lo).max()
+    err = rel_err_cols(B, oracle.potrs(Lo, B_np))
+    assert err <= X_TOL[dt], err
+    if dt in ("f64", "c128"):
+        assert logdet_rel(float(ld.item()), oracle.logdet(Lo)) <= LOGDET_TOL
+    return err
+
+
+@pytest.mark.parametrize("dt,n,nrhs,T_A,pad", [("f64", 1000, 5, 128, 0), ("f64", 1300, 33, 128, 3),
+                                               ("f64", 2048, 16, 256, 0), ("f32", 1024, 4, 128, 0),
+                                               ("c128", 700, 3, 64, 0), ("f64", 300, 2, 100, 0),
+                                               ("f64", 600, 130, 128, 0)])
+def test_posv_parity(gpu, dt, n, nrhs, T_A, pad):
+    """spd_posv against the oracle: the fused path (real, T_A a multiple of
+    128, three or more tiles) and the fallback to the three calls."""
+    posv_check(gpu, dt, n, nrhs, T_A, lda_pad=pad)
+
+
+@pytest.mark.parametrize("dt,n,nrhs,T_A", [("f64", 1300, 9, 128), ("f64", 1024, 3, 128)])
+def test_posv_paired_steps(gpu, dt, n, nrhs, T_A, monkeypatch):
+    """With every step paired, the forward substitution follows the tiles as
+    the pairs finish them."""
+    monkeypatch.setenv("SPD_TWO_STEP_ROWS", "0")
+    posv_check(gpu, dt, n, nrhs, T_A)
+
+
+def test_posv_failed_factorization(gpu):
+    n, T_A = 1000, 128
+    A = spdgen.make_A(n, "f64", 0.5, 5, device="cuda")
+    A[700, 700] = -1.0
+    B = spdgen.make_B(n, 3, "f64", 5, device="cuda")
+    ld = torch.zeros(1, dtype=torch.float64, device="cuda")
+    info = gpu.posv(A, B, T_A, logdet_out=ld)
+    torch.cuda.synchronize()
+    assert int(info.item()) == 701
+    assert torch.isnan(B).all() and math.isnan(float(ld.item()))
+
+
+def test_posv_full_size(gpu):
+    """N = 32768 fp64, T_A = 512, 128 right-hand sides (the benchmark's
+    workload): backward error of X within 64 N eps and log det against the
+    factor's diagonal."""
+    n, nrhs, T_A = 32768, 128, 512
+    A0 = spdgen.make_A(n, "f64", 0.05, 0, device="cuda")
+    B0 = spdgen.make_B(n, nrhs, "f64", 0, device="cuda")
+    A = spdgen.to_colmajor(A0)
+    B = spdgen.to_colmajor(B0)
+    ld = torch.zeros(1, dtype=torch.float64, device="cuda")
+    info = gpu.posv(A, B, T_A, logdet_out=ld)
+    torch.cuda.synchronize()
+    assert int(info.item()) == 0
+    eta = backward_error(A0, B, B0)
+    assert eta <= 64 * n * EPS["f64"], eta
+    d = torch.diagonal(A).to(torch.float64)
+    ref = float(2.0 * torch.log(d).sum().item())
+    assert abs(float(ld.item()) - ref) <= 1e-11 * abs(ref)

@@ -129,6 +129,14 @@ def test_argument_validation_returns_before_gpu_work(lib):
     assert gp(1, 4, 2, dummy, 3, dummy, 4, 2, info, out, dummy, 1 << 20, None) == -5
     assert gp(1, 4, 2, dummy, 4, dummy, 4, 2, info, None, dummy, 1 << 20, None) == -10
     assert gp(1, 4, 2, dummy, 4, dummy, 4, 2, info, out, dummy, 8, None) == -12
+    pv = lib.spd_posv
+    assert pv(7, 4, 2, dummy, 4, dummy, 4, 2, info, None, dummy, 1 << 20, None) == -1
+    assert pv(1, 4, -1, dummy, 4, dummy, 4, 2, info, None, dummy, 1 << 20, None) == -3
+    assert pv(1, 4, 2, dummy, 3, dummy, 4, 2, info, None, dummy, 1 << 20, None) == -5
+    assert pv(1, 4, 2, dummy, 4, dummy, 3, 2, info, None, dummy, 1 << 20, None) == -7
+    assert pv(1, 4, 2, dummy, 4, dummy, 4, 0, info, None, dummy, 1 << 20, None) == -8
+    assert pv(1, 4, 2, dummy, 4, dummy, 4, 2, None, None, dummy, 1 << 20, None) == -9
+    assert pv(1, 4, 2, dummy, 4, dummy, 4, 2, info, None, dummy, 8, None) == -12
     gst = lib.spd_sygst
     assert gst(7, 1, 4, dummy, 4, dummy, 4, 2, info, dummy, 1 << 20, None) == -1
     assert gst(1, 0, 4, dummy, 4, dummy, 4, 2, info, dummy, 1 << 20, None) == -2
