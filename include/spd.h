@@ -27,7 +27,7 @@
  *     The library allocates no device memory.  Its only state between calls is
  *     what spd_profile_* keeps while profiling is on and, for the lookahead
  *     schedules, two auxiliary HIP streams (default priority, non-blocking)
- *     and four events per host thread and device, created on first use and
+ *     and five events per host thread and device, created on first use and
  *     kept until the process ends.  Calls from one host thread must not
  *     overlap on one device (they share those streams).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
