@@ -417,6 +417,25 @@ def bench_sygst(args, cfg):
     return 0 if (check is None or check["ok"]) else 1
 
 
+def sample_size(run, n, target_s):
+    """Order of the leading block the CPU oracle takes about ``target_s``
+    seconds on: a small block fits the host caches and runs faster per flop
+    than a large one, so a first estimate from a 1024 block is refined by a
+    run at about a quarter of the target before the cubic scaling is trusted."""
+    def scale(m0, t0, goal):
+        m = int(m0 * (goal / max(t0, 1e-3)) ** (1.0 / 3.0))
+        return max(256, min(n, (m // 256) * 256))
+
+    m0 = min(n, 1024)
+    t0 = run(m0)
+    m1 = scale(m0, t0, target_s / 4.0)
+    t1 = run(m1) if m1 > m0 else t0
+    m1 = max(m1, m0)
+    m = scale(m1, t1, target_s)
+    log(f"[bench] cpu oracle: {m0} took {t0:.2f} s, {m1} took {t1:.2f} s; sample size {m}")
+    return m
+
+
 def cpu_baseline_sygst(B0, H0, n, itype, fmul, target_s):
     """The CPU oracle on the leading principal blocks of B and A: potrf, then
     the reduction by its definition; same flop formula as the GPU value."""
@@ -430,11 +449,7 @@ def cpu_baseline_sygst(B0, H0, n, itype, fmul, target_s):
         oracle.sygst(itype, a, l)
         return time.perf_counter() - t
 
-    m0 = min(n, 1024)
-    t0 = run(m0)
-    m = int(m0 * (target_s / max(t0, 1e-3)) ** (1.0 / 3.0))
-    m = max(256, min(n, (m // 256) * 256))
-    log(f"[bench] cpu oracle: {m0} took {t0:.2f} s; sample size {m}")
+    m = sample_size(lambda k: run(k), n, target_s)
     t = run(m)
     fl = fmul * (m**3 / 3.0 + float(m) ** 3)
     return {"value": fl / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
@@ -464,11 +479,7 @@ def cpu_baseline(A0, B0, n, nrhs, fmul, target_s, gp=False):
         oracle.logdet(l)
         return time.perf_counter() - t, info
 
-    m0 = min(n, 1024)
-    t0, _ = run(m0)
-    m = int(m0 * (target_s / max(t0, 1e-3)) ** (1.0 / 3.0))
-    m = max(256, min(n, (m // 256) * 256))
-    log(f"[bench] cpu oracle: {m0} took {t0:.2f} s; sample size {m}")
+    m = sample_size(lambda k: run(k)[0], n, target_s)
     t, info = run(m)
     fl = fmul * (m**3 / 3.0 + (1.0 if gp else 2.0) * m * m * nrhs)
     what = "Gaussian-process log-likelihood by its definition" if gp else "potrf + potrs + logdet"
