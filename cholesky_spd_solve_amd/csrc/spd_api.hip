@@ -668,7 +668,7 @@ struct Solver {
         bool aux = false;  // potrf's auxiliary stream (timed as its own class)
     };
 
-    template <int BM, int KB, int WM, int WN>
+    template <int BM, int KB, int WM, int WN, bool BIGLD = false>
     static int syrk_cfg(int64_t m, const E *W, int64_t ldw, int64_t kp, E *C, int64_t ldc, int jt_end,
                         const int *info, hipStream_t s, const Syr2 &x = Syr2())
     {
@@ -700,8 +700,8 @@ struct Solver {
         }
         a.info = info;
         const dim3 grid((unsigned)a.ntiles), block(64 * WM * WN);
-        SPD_VALIDATE((check_syrk<R, CPLX, BM, KB, WM, WN>(a, grid, g_chk)));
-        syrk_kernel<R, CPLX, BM, KB, WM, WN><<<grid, block, 0, s>>>(a);
+        SPD_VALIDATE((check_syrk<R, CPLX, BM, KB, WM, WN, BIGLD>(a, grid, g_chk)));
+        syrk_kernel<R, CPLX, BM, KB, WM, WN, BIGLD><<<grid, block, 0, s>>>(a);
         SPD_CHECK_LAUNCH("syrk_kernel");
         return 0;
     }
@@ -729,6 +729,8 @@ struct Solver {
         ProfScope ps(x.V != nullptr ? -1 : x.aux ? PROF_SYRK_AUX : PROF_SYRK,
                      FMUL * (double)w * (2.0 * m - w + 1.0) * (double)kw, s);
         auto jt = [&](int64_t bm) { return cols > 0 ? (int)(cols / bm) : 0; };
+        if (ldc >= SYRK_LD32)  // 64-bit offsets into C; one 64-row tile shape for every such case
+            return syrk_cfg<64, 16, 2, 2, true>(m, W, ldw, kp, C, ldc, jt(64), info, s, x);
         if constexpr (CPLX) {
             // 8 waves on 64 x 64 complex tiles: 3-6 % above 4 waves (c128, T = 256)
             return syrk_cfg<64, 16, 2, 4>(m, W, ldw, kp, C, ldc, jt(64), info, s, x);
@@ -769,6 +771,8 @@ struct Solver {
         x.V = Vc;
         x.add = add;
         x.ncols = ncols;
+        if (ldc >= SYRK_LD32)  // 64-bit offsets into C
+            return syrk_cfg<64, 16, 2, 2, true>(m, W, ldw, kp, C, ldc, 0, info, s, x);
         if constexpr (CPLX) {
             return syrk_cfg<64, 16, 2, 2>(m, W, ldw, kp, C, ldc, 0, info, s, x);
         } else {

@@ -152,9 +152,10 @@ static bool check_gemm(const GemmArgs &p, dim3 grid, Checker &c)
 
 // Replay of syrk_kernel (spd_syrk.hpp): whole-tile vector loads of both row
 // blocks of W for every slice, and the epilogue's read-modify-write of C.
-template <typename R, bool CPLX, int BM, int KB, int WM, int WN>
+template <typename R, bool CPLX, int BM, int KB, int WM, int WN, bool BIGLD>
 static bool check_syrk(const SyrkArgs &p, dim3 grid, Checker &c)
 {
+    typedef typename SyrkOff<BIGLD>::type Off;
     typedef typename Elem<R, CPLX>::type E;
     constexpr int NT = 64 * WM * WN;
     constexpr int TM = BM / WM, TN = BM / WN;
@@ -214,7 +215,12 @@ static bool check_syrk(const SyrkArgs &p, dim3 grid, Checker &c)
                     for (int q = 0; q < 4; ++q) {
                         const int i = ib + fi * 16 + li, j = jb + fj * 16 + acc_row<R>(lk, q);
                         if (whole || (i0 + i < p.m && (rectm ? j0 + j < p.ncols : i0 + i >= j0 + j))) {
-                            E *dst = Ct + (uint32_t)(i + (int64_t)j * p.ldc);
+                            const int64_t full = i + (int64_t)j * p.ldc;
+                            if ((int64_t)(Off)full != full) {
+                                c.err = "syrk_kernel: offset into C does not fit its type";
+                                return false;
+                            }
+                            E *dst = Ct + (Off)full;
                             if (!c.access(dst, sizeof(E), false, kn, b, tid) ||
                                 !c.access(dst, sizeof(E), true, kn, b, tid))
                                 return false;

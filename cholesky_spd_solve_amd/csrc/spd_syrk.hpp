@@ -126,10 +126,17 @@ struct SyrkLoad {
     }
 };
 
-template <typename R, bool CPLX, int BM, int KB, int WM, int WN>
+// Offsets into C within a tile: 32-bit while BM columns of C span fewer than
+// 2^32 elements, 64-bit beyond (BIGLD).
+template <bool BIGLD> struct SyrkOff { typedef uint32_t type; };
+template <> struct SyrkOff<true> { typedef int64_t type; };
+constexpr int64_t SYRK_LD32 = INT64_C(1) << 24;  // leading dimensions below this use 32-bit offsets
+
+template <typename R, bool CPLX, int BM, int KB, int WM, int WN, bool BIGLD = false>
 __global__ void __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)))
 syrk_kernel(const SyrkArgs p)
 {
+    typedef typename SyrkOff<BIGLD>::type Off;
     typedef typename Elem<R, CPLX>::type E;
     typedef typename AccT<R>::type V4;
     typedef SyrkLoad<R, CPLX, BM, KB, 64 * WM * WN> LD;
@@ -304,14 +311,14 @@ syrk_kernel(const SyrkArgs p)
                 for (int q = 0; q < 4; ++q) {
                     const int j = jb + fj * 16 + acc_row<R>(lk, q);
                     ci[fj][q] = 0;
-                    Elem<R, CPLX>::load(Ct + (uint32_t)(i + (int64_t)j * p.ldc), cr[fj][q], ci[fj][q]);
+                    Elem<R, CPLX>::load(Ct + (Off)(i + (int64_t)j * p.ldc), cr[fj][q], ci[fj][q]);
                 }
 #pragma unroll
             for (int fj = 0; fj < FN; ++fj)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int j = jb + fj * 16 + acc_row<R>(lk, q);
-                    Elem<R, CPLX>::store(Ct + (uint32_t)(i + (int64_t)j * p.ldc),
+                    Elem<R, CPLX>::store(Ct + (Off)(i + (int64_t)j * p.ldc),
                                          fma_r(sg, acc[0][fi][fj][q], cr[fj][q]),
                                          CPLX ? fma_r(sg, acc[NP - 1][fi][fj][q], ci[fj][q]) : R(0));
                 }
@@ -322,7 +329,7 @@ syrk_kernel(const SyrkArgs p)
                 for (int q = 0; q < 4; ++q) {
                     const int j = jb + fj * 16 + acc_row<R>(lk, q);
                     if (i0 + i < p.m && (rectm ? j0 + j < p.ncols : i0 + i >= j0 + j)) {
-                        E *dst = Ct + (uint32_t)(i + (int64_t)j * p.ldc);
+                        E *dst = Ct + (Off)(i + (int64_t)j * p.ldc);
                         R xr, xi = 0;
                         Elem<R, CPLX>::load(dst, xr, xi);
                         Elem<R, CPLX>::store(dst, fma_r(sg, acc[0][fi][fj][q], xr),

@@ -91,6 +91,14 @@ def test_dry_run_real_general_path(lib):
     dry_solve(lib, 1, 65, 3, 32, lda=(1 << 24) + 8)
 
 
+@pytest.mark.parametrize("dt", ["f64", "f32", "c128", "c64"])
+def test_dry_run_huge_leading_dimension(lib, dt):
+    """Leading dimensions whose 64 or 128 columns span more than 2^32
+    elements: the trailing update must address C with 64-bit offsets (the
+    replay checks that every offset fits the kernel's offset type)."""
+    dry_solve(lib, CODE[dt], 300, 5, 64, lda=1 << 27, ldb=(1 << 27) + 3)
+
+
 def test_dry_run_detects_a_short_workspace(lib):
     """The validator itself: a workspace one byte too small for the kernels
     (but passed as large enough) must be caught."""

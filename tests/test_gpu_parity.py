@@ -418,3 +418,10 @@ def test_posv_full_size(gpu):
     d = torch.diagonal(A).to(torch.float64)
     ref = float(2.0 * torch.log(d).sum().item())
     assert abs(float(ld.item()) - ref) <= 1e-11 * abs(ref)
+
+
+def test_huge_leading_dimension(gpu):
+    """A leading dimension of 7e7 elements: 64 columns of A span more than
+    2^32 elements, so the trailing update must address A with 64-bit offsets
+    (45 GB of device storage, 160 x 160 of it used)."""
+    posv_check(gpu, "f32", 160, 3, 64, lda_pad=70_000_000 - 160)
