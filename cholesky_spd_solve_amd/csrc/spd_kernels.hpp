@@ -61,16 +61,19 @@ __host__ __device__ inline bool leaf_geom(const LeafArgs &p, int g, int64_t &c0,
 // factor = 0: the leaf already holds L; only inv(L) is produced.
 //
 // Thread (r, g) = (tid % 64, tid / 64) owns row r of the leaf and of its
-// inverse, columns g, g + 4, g + 8, ...: every column step is a few LDS
-// read-modify-writes per thread with no index division, and the values of
-// column j a wave needs are the same for all its lanes (LDS broadcasts).
+// inverse, columns g, g + G, g + 2G, ...: every column step is at most
+// LEAF / G LDS read-modify-writes per thread with no index division, and the
+// values of column j a wave needs are the same for all its lanes (LDS
+// broadcasts).  G = 16 waves (1024 threads): the column steps are sequential,
+// so their length, not the thread count, sets the leaf's time.
+constexpr int LEAF_G = 16;
 template <typename R, bool CPLX>
-__global__ void __launch_bounds__(256) leaf_kernel(const LeafArgs p)
+__global__ void __launch_bounds__(64 * LEAF_G) leaf_kernel(const LeafArgs p)
 {
     typedef typename Elem<R, CPLX>::type E;
     constexpr int NP = CPLX ? 2 : 1;
     constexpr int LD = LEAF + 1;
-    constexpr int G = 4;           // column phases (waves)
+    constexpr int G = LEAF_G;      // column phases (waves)
     __shared__ R S[NP][LEAF][LD];  // S[.][c][r] = L(r, c)
     __shared__ R X[NP][LEAF][LD];  // X[.][c][r] = inv(L)(r, c)
     __shared__ R dg[LEAF];
