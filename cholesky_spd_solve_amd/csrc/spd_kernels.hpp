@@ -77,6 +77,9 @@ __global__ void __launch_bounds__(64 * LEAF_G) leaf_kernel(const LeafArgs p)
     __shared__ R S[NP][LEAF][LD];  // S[.][c][r] = L(r, c)
     __shared__ R X[NP][LEAF][LD];  // X[.][c][r] = inv(L)(r, c)
     __shared__ R dg[LEAF];
+    __shared__ R rs[LEAF];   // 1 / L(j, j)
+    __shared__ R piv[2];     // 1 / L(j, j) of column j in slot j % 2
+    __shared__ int pbad[2];  // its pivot failed
 
     int64_t c0, ioff;
     int lb;
@@ -113,41 +116,53 @@ __global__ void __launch_bounds__(64 * LEAF_G) leaf_kernel(const LeafArgs p)
     }
     __syncthreads();
 
-    for (int j = 0; j < lb; ++j) {
-        R ljj;
+    // Pivot of column j, computed by one thread as soon as S(j, j) is final:
+    // 1/L(j, j), L(j, j) and whether the pivot failed (not > 0, NaN included),
+    // in slot j % 2.  Column j's pivot is computed during the update of step
+    // j - 1 by the thread that updates S(j, j), so its dependent chain (square
+    // root and division) runs beside the other threads' updates.
+    //
+    // Column j of L and row j of inv(L) are kept unscaled in S and X: every
+    // reader multiplies by 1/L(j, j) as it reads (rounding exactly as a scaled
+    // copy would), and the scaling is applied once more when they are stored.
+    // No step writes what another thread reads in the same step (the update
+    // of step j reads column j of S and row j of X and writes columns > j and
+    // rows > j), so one barrier per step suffices.
+    auto pivot = [&](int j) {
+        const R d = S[0][j][j];
+        R ljj = d;
+        int bad = 0;
         if (p.factor) {
-            const R d = S[0][j][j];
-            if (!(d > R(0))) {  // uniform: every thread read the same pivot
-                if (tid == 0)
-                    atomicCAS(p.info, 0, (int)(p.col0 + c0 + j + 1));
-                return;
-            }
-            ljj = sqrt(d);
-        } else {
-            ljj = S[0][j][j];
+            bad = !(d > R(0));
+            ljj = bad ? R(1) : sqrt(d);
         }
-        const R rinv = R(1) / ljj;
-        // column j of L below the diagonal (phase 0), row j of inv(L) (phase 1)
-        if (g == 0 && p.factor && r > j && r < lb) {
-            S[0][j][r] *= rinv;
-            if constexpr (CPLX) S[NP - 1][j][r] *= rinv;
+        const R ri = R(1) / ljj;
+        piv[j & 1] = ri;
+        pbad[j & 1] = bad;
+        rs[j] = ri;
+        dg[j] = ljj;
+    };
+    if (tid == 0 && lb > 0)
+        pivot(0);
+    __syncthreads();
+
+    for (int j = 0; j < lb; ++j) {
+        if (pbad[j & 1]) {  // uniform: every thread reads the same flag
+            if (tid == 0)
+                atomicCAS(p.info, 0, (int)(p.col0 + c0 + j + 1));
+            return;
         }
-        if (g == 1 && r <= j) {
-            X[0][r][j] *= rinv;
-            if constexpr (CPLX) X[NP - 1][r][j] *= rinv;
-        }
-        if (p.factor && tid == 0)
-            dg[j] = ljj;
-        __syncthreads();
+        const R rinv = piv[j & 1];
+        const R cs = p.factor ? rinv : R(1);  // scale of column j of S (given L: none)
         if (r > j && r < lb) {
-            const R ar = S[0][j][r];
-            const R ai = CPLX ? S[NP - 1][j][r] : R(0);
+            const R ar = S[0][j][r] * cs;
+            const R ai = CPLX ? S[NP - 1][j][r] * cs : R(0);
             if (p.factor) {
                 // trailing lower triangle: S(r, c) -= L(r, j) conj(L(c, j)), j < c <= r
                 for (int c = j + 1 + g; c <= r; c += G) {
-                    const R br = S[0][j][c];
+                    const R br = S[0][j][c] * cs;
                     if constexpr (CPLX) {
-                        const R bi = S[1][j][c];
+                        const R bi = S[1][j][c] * cs;
                         S[0][c][r] -= ar * br + ai * bi;
                         S[1][c][r] -= ai * br - ar * bi;
                     } else {
@@ -155,11 +170,14 @@ __global__ void __launch_bounds__(64 * LEAF_G) leaf_kernel(const LeafArgs p)
                     }
                 }
             }
+            // S(j + 1, j + 1) is final: thread (j + 1, 0) updated it above
+            if (r == j + 1 && g == 0)
+                pivot(j + 1);
             // rows below j of inv(L): X(r, c) -= L(r, j) X(j, c), c <= j < r
             for (int c = g; c <= j; c += G) {
-                const R xr = X[0][c][j];
+                const R xr = X[0][c][j] * rinv;
                 if constexpr (CPLX) {
-                    const R xi = X[1][c][j];
+                    const R xi = X[1][c][j] * rinv;
                     X[0][c][r] -= ar * xr - ai * xi;
                     X[1][c][r] -= ar * xi + ai * xr;
                 } else {
@@ -177,10 +195,12 @@ __global__ void __launch_bounds__(64 * LEAF_G) leaf_kernel(const LeafArgs p)
             if (r == c)
                 Elem<R, CPLX>::store(A + r + (int64_t)c * p.lda, dg[c], R(0));
             else
-                Elem<R, CPLX>::store(A + r + (int64_t)c * p.lda, S[0][c][r], CPLX ? S[NP - 1][c][r] : R(0));
+                Elem<R, CPLX>::store(A + r + (int64_t)c * p.lda, S[0][c][r] * rs[c],
+                                     CPLX ? S[NP - 1][c][r] * rs[c] : R(0));
         }
         if (r >= c)
-            Elem<R, CPLX>::store(Inv + r + (int64_t)c * p.ldi, X[0][c][r], CPLX ? X[NP - 1][c][r] : R(0));
+            Elem<R, CPLX>::store(Inv + r + (int64_t)c * p.ldi, X[0][c][r] * rs[r],
+                                 CPLX ? X[NP - 1][c][r] * rs[r] : R(0));
         else
             Elem<R, CPLX>::store(Inv + r + (int64_t)c * p.ldi, R(0), R(0));
     }
