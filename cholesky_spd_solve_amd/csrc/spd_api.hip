@@ -513,10 +513,10 @@ struct Solver {
         p.ctr = nullptr;
         SPD_VALIDATE((check_leaf<R, CPLX>(p, (unsigned)grid, g_chk)));
         if constexpr (CPLX)
-            leaf_kernel<R, CPLX><<<dim3((unsigned)grid), dim3(64 * LEAF_G), 0, s>>>(p);
+            leaf16c_kernel<R><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p);
         else
             leaf16_kernel<R><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p);
-        SPD_CHECK_LAUNCH("leaf_kernel");
+        SPD_CHECK_LAUNCH("leaf16_kernel");
         return 0;
     }
 

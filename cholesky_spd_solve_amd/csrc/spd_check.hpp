@@ -321,7 +321,7 @@ template <typename R, bool CPLX>
 static bool check_leaf(const LeafArgs &p, unsigned grid, Checker &c, bool panel = false)
 {
     typedef typename Elem<R, CPLX>::type E;
-    const char *kn = panel ? "leaf16_kernel (leaf + panel)" : "leaf_kernel";
+    const char *kn = panel ? "leaf16_kernel (leaf + panel)" : "leaf16_kernel";
     if (p.info != nullptr && !c.access(p.info, 4, p.factor != 0, kn, 0, 0))
         return false;
     if (panel && (p.ctr == nullptr || !c.access(p.ctr, 4, true, kn, 0, 0))) {

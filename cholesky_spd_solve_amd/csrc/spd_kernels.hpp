@@ -47,168 +47,18 @@ __host__ __device__ inline bool leaf_geom(const LeafArgs &p, int g, int64_t &c0,
     return true;
 }
 
-// One workgroup per leaf.  Leaf w lies in tile t = w / lpt at leaf slot
-// b = w % lpt: columns c = t*T + b*LEAF ... of the matrix.
+// ---------------------------------------------------------------------------
+// Leaf kernels: one workgroup per leaf.  Leaf w lies in tile t = w / lpt at
+// leaf slot b = w % lpt: columns c = t*T + b*LEAF ... of the matrix.
 //
-// factor = 1: right-looking unblocked Cholesky of the leaf's lower triangle in
-// LDS (pivot from the real part of the diagonal; a pivot that is not > 0,
-// including NaN, stops the factorization and records info), then L is written
-// back over the lower triangle (diagonal imaginary parts set to 0) and inv(L)
-// is written to the inverse storage with explicit zeros above the diagonal.
-// The inverse is built alongside: L X = I is solved row by row, row j of X
-// being final once column j of L is, and then removed from the rows below.
-//
+// factor = 1: Cholesky factorization of the leaf's lower triangle (pivots from
+// the real part of the diagonal; a pivot that is not > 0, NaN included,
+// records info and the leaf is not written back), then L is written back
+// over the lower triangle (diagonal imaginary parts 0) and inv(L) to the
+// inverse storage with explicit zeros above the diagonal.
 // factor = 0: the leaf already holds L; only inv(L) is produced.
 //
-// Thread (r, g) = (tid % 64, tid / 64) owns row r of the leaf and of its
-// inverse, columns g, g + G, g + 2G, ...: every column step is at most
-// LEAF / G LDS read-modify-writes per thread with no index division, and the
-// values of column j a wave needs are the same for all its lanes (LDS
-// broadcasts).  G = 16 waves (1024 threads): the column steps are sequential,
-// so their length, not the thread count, sets the leaf's time.
-constexpr int LEAF_G = 16;
-template <typename R, bool CPLX>
-__global__ void __launch_bounds__(64 * LEAF_G) leaf_kernel(const LeafArgs p)
-{
-    typedef typename Elem<R, CPLX>::type E;
-    constexpr int NP = CPLX ? 2 : 1;
-    constexpr int LD = LEAF + 1;
-    constexpr int G = LEAF_G;      // column phases (waves)
-    __shared__ R S[NP][LEAF][LD];  // S[.][c][r] = L(r, c)
-    __shared__ R X[NP][LEAF][LD];  // X[.][c][r] = inv(L)(r, c)
-    __shared__ R dg[LEAF];
-    __shared__ R rs[LEAF];   // 1 / L(j, j)
-    __shared__ R piv[2];     // 1 / L(j, j) of column j in slot j % 2
-    __shared__ int pbad[2];  // its pivot failed
-
-    int64_t c0, ioff;
-    int lb;
-    if (!leaf_geom(p, (int)blockIdx.x, c0, lb, ioff))
-        return;
-    E *A = (E *)p.A + c0 + c0 * p.lda;
-    E *Inv = (E *)p.Inv + ioff;
-    const int tid = threadIdx.x;
-    const int r = tid & (LEAF - 1), g = tid / LEAF;
-
-    // all loads in flight together, the status word alongside them
-    R vr[LEAF / G], vi[LEAF / G];
-#pragma unroll
-    for (int k = 0; k < LEAF / G; ++k) {
-        const int c = g + G * k;
-        vr[k] = 0;
-        vi[k] = 0;
-        if (r < lb && c < lb && r >= c)
-            Elem<R, CPLX>::load(A + r + (int64_t)c * p.lda, vr[k], vi[k]);
-        if (r == c)
-            vi[k] = 0;
-    }
-    if (p.info != nullptr && *p.info != 0)
-        return;
-#pragma unroll
-    for (int k = 0; k < LEAF / G; ++k) {
-        const int c = g + G * k;
-        if (c < lb) {
-            S[0][c][r] = vr[k];
-            if constexpr (CPLX) S[NP - 1][c][r] = vi[k];
-            X[0][c][r] = (r == c) ? R(1) : R(0);
-            if constexpr (CPLX) X[NP - 1][c][r] = 0;
-        }
-    }
-    __syncthreads();
-
-    // Pivot of column j, computed by one thread as soon as S(j, j) is final:
-    // 1/L(j, j), L(j, j) and whether the pivot failed (not > 0, NaN included),
-    // in slot j % 2.  Column j's pivot is computed during the update of step
-    // j - 1 by the thread that updates S(j, j), so its dependent chain (square
-    // root and division) runs beside the other threads' updates.
-    //
-    // Column j of L and row j of inv(L) are kept unscaled in S and X: every
-    // reader multiplies by 1/L(j, j) as it reads (rounding exactly as a scaled
-    // copy would), and the scaling is applied once more when they are stored.
-    // No step writes what another thread reads in the same step (the update
-    // of step j reads column j of S and row j of X and writes columns > j and
-    // rows > j), so one barrier per step suffices.
-    auto pivot = [&](int j) {
-        const R d = S[0][j][j];
-        R ljj = d;
-        int bad = 0;
-        if (p.factor) {
-            bad = !(d > R(0));
-            ljj = bad ? R(1) : sqrt(d);
-        }
-        const R ri = R(1) / ljj;
-        piv[j & 1] = ri;
-        pbad[j & 1] = bad;
-        rs[j] = ri;
-        dg[j] = ljj;
-    };
-    if (tid == 0 && lb > 0)
-        pivot(0);
-    __syncthreads();
-
-    for (int j = 0; j < lb; ++j) {
-        if (pbad[j & 1]) {  // uniform: every thread reads the same flag
-            if (tid == 0)
-                atomicCAS(p.info, 0, (int)(p.col0 + c0 + j + 1));
-            return;
-        }
-        const R rinv = piv[j & 1];
-        const R cs = p.factor ? rinv : R(1);  // scale of column j of S (given L: none)
-        if (r > j && r < lb) {
-            const R ar = S[0][j][r] * cs;
-            const R ai = CPLX ? S[NP - 1][j][r] * cs : R(0);
-            if (p.factor) {
-                // trailing lower triangle: S(r, c) -= L(r, j) conj(L(c, j)), j < c <= r
-                for (int c = j + 1 + g; c <= r; c += G) {
-                    const R br = S[0][j][c] * cs;
-                    if constexpr (CPLX) {
-                        const R bi = S[1][j][c] * cs;
-                        S[0][c][r] -= ar * br + ai * bi;
-                        S[1][c][r] -= ai * br - ar * bi;
-                    } else {
-                        S[0][c][r] -= ar * br;
-                    }
-                }
-            }
-            // S(j + 1, j + 1) is final: thread (j + 1, 0) updated it above
-            if (r == j + 1 && g == 0)
-                pivot(j + 1);
-            // rows below j of inv(L): X(r, c) -= L(r, j) X(j, c), c <= j < r
-            for (int c = g; c <= j; c += G) {
-                const R xr = X[0][c][j] * rinv;
-                if constexpr (CPLX) {
-                    const R xi = X[1][c][j] * rinv;
-                    X[0][c][r] -= ar * xr - ai * xi;
-                    X[1][c][r] -= ar * xi + ai * xr;
-                } else {
-                    X[0][c][r] -= ar * xr;
-                }
-            }
-        }
-        __syncthreads();
-    }
-
-    for (int c = g; c < lb; c += G) {
-        if (r >= lb)
-            continue;
-        if (p.factor && r >= c) {
-            if (r == c)
-                Elem<R, CPLX>::store(A + r + (int64_t)c * p.lda, dg[c], R(0));
-            else
-                Elem<R, CPLX>::store(A + r + (int64_t)c * p.lda, S[0][c][r] * rs[c],
-                                     CPLX ? S[NP - 1][c][r] * rs[c] : R(0));
-        }
-        if (r >= c)
-            Elem<R, CPLX>::store(Inv + r + (int64_t)c * p.ldi, X[0][c][r] * rs[r],
-                                 CPLX ? X[NP - 1][c][r] * rs[r] : R(0));
-        else
-            Elem<R, CPLX>::store(Inv + r + (int64_t)c * p.ldi, R(0), R(0));
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Blocked leaf for real types: the same result as leaf_kernel (L and inv(L)
-// of a LEAF x LEAF diagonal block) with 16 x 16 sub-blocks.
+// Blocked leaf for real types, with 16 x 16 sub-blocks:
 //
 //   for b = 0..3:  factor and invert the diagonal block (b, b)        (one wave)
 //                  L(i, b) = A(i, b) inv(L(b, b))^T         i > b      (MFMA)
@@ -594,6 +444,267 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) l
             if (p.factor && r >= c)
                 A[r + (int64_t)c * p.lda] = sv[k];
             Inv[r + (int64_t)c * p.ldi] = (r >= c) ? xv[k] : R(0);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Blocked leaf for complex types: leaf16_kernel's scheme with real and
+// imaginary parts in separate LDS planes.
+//
+//   for b = 0..3:  factor and invert the diagonal block (b, b)        (one wave)
+//                  L(i, b) = A(i, b) inv(L(b, b))^H         i > b      (MFMA)
+//                  A(i, j) -= L(i, b) L(j, b)^H        b < j <= i      (MFMA)
+//   inv(L)(i, b) = -inv(L(i, i)) sum_{b<=k<i} L(i, k) inv(L)(k, b)
+//
+// In the diagonal block sweep lane c holds row c of the Hermitian block and
+// column c of the inverse.  Step j: the pivot is the real part of lane j's
+// a[j]; every lane scales its a[j] by 1/L(j, j), which leaves L(c, j) in
+// lane c; then A(c, r) -= L(c, j) conj(L(r, j)) and x[r] -= L(r, j) x[j] for
+// r > j, with L(r, j) read from lane r.  Every complex 16 x 16 x 16 product is
+// sixteen v_mfma_*_16x16x4 (four per complex multiply-add).
+
+// acc += A op(B) for complex 16 x 16 blocks in LDS planes (real, imaginary):
+// A(r, k) = pa*[k * ak + r * ar], B(k, c) = pb*[k * bk + c * bc], op(B) =
+// conj(B) when CB.  Lane layout as mma16.
+template <typename R, bool CB>
+__device__ __forceinline__ void mma16c(const R *par, const R *pai, int ak, int ar, const R *pbr, const R *pbi, int bk,
+                                       int bc, typename AccT<R>::type &cr, typename AccT<R>::type &ci)
+{
+    const int lane = threadIdx.x & 63, li = lane & 15, lk = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int k = 4 * s + lk;
+        const R a0 = par[k * ak + li * ar], a1 = pai[k * ak + li * ar];
+        const R b0 = pbr[k * bk + li * bc];
+        const R b1 = CB ? -pbi[k * bk + li * bc] : pbi[k * bk + li * bc];
+        cr = mfma16(b0, a0, cr);
+        cr = mfma16(-b1, a1, cr);
+        ci = mfma16(b1, a0, ci);
+        ci = mfma16(b0, a1, ci);
+    }
+}
+
+// Column J of the complex sweep (pivot scale s, ljj already known), then the
+// columns after it; the pivot is diag16_pivot's on the real parts.
+template <typename R, bool FACTOR, int J>
+__device__ __forceinline__ void diag16c_step(R *ar, R *ai, R *xr, R *xi, int c, R s, R ljj, int &bad)
+{
+    if constexpr (J < LB16) {
+        if constexpr (FACTOR) {
+            ar[J] = (c == J) ? ljj : ar[J] * s;
+            ai[J] = (c == J) ? R(0) : ai[J] * s;
+        }
+        xr[J] *= s;
+        xi[J] *= s;
+        R s1 = R(0), l1 = R(0);
+        if constexpr (J + 1 < LB16) {
+            const R lr = row_value<J + 1>(ar[J]), lq = row_value<J + 1>(ai[J]);  // L(J + 1, J)
+            if constexpr (FACTOR) {  // a[J + 1] -= a[J] conj(l)
+                ar[J + 1] -= ar[J] * lr + ai[J] * lq;
+                ai[J + 1] -= ai[J] * lr - ar[J] * lq;
+            }
+            const R tr = xr[J + 1] - (lr * xr[J] - lq * xi[J]);  // x[J + 1] -= l x[J]
+            xi[J + 1] -= lr * xi[J] + lq * xr[J];
+            xr[J + 1] = tr;
+            diag16_pivot<R, FACTOR, J + 1>(ar, s1, l1, bad);
+        }
+        R br[LB16], bi[LB16];
+        diag16_bcast<R, J, J + 2>(ar, br);
+        diag16_bcast<R, J, J + 2>(ai, bi);
+#pragma unroll
+        for (int r = J + 2; r < LB16; ++r)
+            asm volatile("" : "+v"(br[r]), "+v"(bi[r]));
+#pragma unroll
+        for (int r = J + 2; r < LB16; ++r) {
+            if constexpr (FACTOR) {  // a[r] -= a[J] conj(L(r, J))
+                ar[r] -= ar[J] * br[r] + ai[J] * bi[r];
+                ai[r] -= ai[J] * br[r] - ar[J] * bi[r];
+            }
+            const R tr = xr[r] - (br[r] * xr[J] - bi[r] * xi[J]);  // x[r] -= L(r, J) x[J]
+            xi[r] -= br[r] * xi[J] + bi[r] * xr[J];
+            xr[r] = tr;
+        }
+#pragma unroll
+        for (int r = J + 2; r < LB16; ++r)
+            asm volatile("" : "+v"(ar[r]), "+v"(ai[r]), "+v"(xr[r]), "+v"(xi[r]));
+        diag16c_step<R, FACTOR, J + 1>(ar, ai, xr, xi, c, s1, l1, bad);
+    }
+}
+
+// Factor (FACTOR) and invert, or only invert, the complex 16 x 16 diagonal
+// block at (o, o) of S0 + i S1 (S*[c][r] = element (r, c), lower triangle);
+// L goes back to S (zeros above the diagonal, real diagonal), inv(L) to X.
+// One wave, as diag16.
+template <typename R, bool FACTOR>
+__device__ void diag16c(R (*S0)[LDL], R (*S1)[LDL], R (*X0)[LDL], R (*X1)[LDL], int o, int lb, int gcol, int *info,
+                        int *failed)
+{
+    const int lane = threadIdx.x & 63, c = lane & 15;
+    R ar[LB16], ai[LB16], xr[LB16], xi[LB16];
+#pragma unroll
+    for (int r = 0; r < LB16; ++r) {  // row c: A(c, r), the upper part as conj(A(r, c))
+        ar[r] = (r <= c) ? S0[o + r][o + c] : S0[o + c][o + r];
+        ai[r] = (r <= c) ? S1[o + r][o + c] : -S1[o + c][o + r];
+        xr[r] = (r == c) ? R(1) : R(0);
+        xi[r] = R(0);
+    }
+    int bad = -1;
+    R s0, l0;
+    diag16_pivot<R, FACTOR, 0>(ar, s0, l0, bad);
+    diag16c_step<R, FACTOR, 0>(ar, ai, xr, xi, c, s0, l0, bad);
+    if (FACTOR && bad >= 0 && lane == 0 && o + bad < lb) {
+        if (info != nullptr)
+            atomicCAS(info, 0, gcol + o + bad + 1);
+        *failed = 1;
+    }
+    if (lane < LB16) {
+#pragma unroll
+        for (int r = 0; r < LB16; ++r) {
+            if constexpr (FACTOR) {  // row c of L
+                S0[o + r][o + c] = (r <= c) ? ar[r] : R(0);
+                S1[o + r][o + c] = (r <= c) ? ai[r] : R(0);
+            }
+            X0[o + c][o + r] = (r >= c) ? xr[r] : R(0);  // column c of inv(L)
+            X1[o + c][o + r] = (r >= c) ? xi[r] : R(0);
+        }
+    }
+}
+
+template <typename R>
+__global__ void __launch_bounds__(256) leaf16c_kernel(const LeafArgs p)
+{
+    typedef typename AccT<R>::type V4;
+    typedef typename Elem<R, true>::type E;
+    constexpr int NB = LEAF / LB16;
+    __shared__ R S[2][LEAF][LDL];           // S[.][c][r] = L(r, c)
+    __shared__ R X[2][LEAF][LDL];           // X[.][c][r] = inv(L)(r, c)
+    __shared__ R Tm[4][2][LB16][LB16 + 1];  // per-wave 16 x 16 scratch
+    __shared__ int failed;
+
+    int64_t c0, ioff;
+    int lb;
+    if (!leaf_geom(p, (int)blockIdx.x, c0, lb, ioff))
+        return;
+    E *A = (E *)p.A + c0 + c0 * p.lda;
+    E *Inv = (E *)p.Inv + ioff;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int li = lane & 15, lk = lane >> 4;
+    const int r = tid & (LEAF - 1), g = tid / LEAF;
+
+    // all loads in flight together, the status word alongside them; the
+    // diagonal's imaginary part is taken as 0 and padding beyond lb is the
+    // identity
+    R vr[LEAF / 4], vi[LEAF / 4];
+#pragma unroll
+    for (int k = 0; k < LEAF / 4; ++k) {
+        const int c = g + 4 * k;
+        vr[k] = (r == c) ? R(1) : R(0);
+        vi[k] = R(0);
+        if (r < lb && c < lb && r >= c)
+            Elem<R, true>::load(A + r + (int64_t)c * p.lda, vr[k], vi[k]);
+        if (r == c)
+            vi[k] = R(0);
+    }
+    if (p.info != nullptr && *p.info != 0)
+        return;
+#pragma unroll
+    for (int k = 0; k < LEAF / 4; ++k) {
+        S[0][g + 4 * k][r] = vr[k];
+        S[1][g + 4 * k][r] = vi[k];
+        X[0][g + 4 * k][r] = R(0);
+        X[1][g + 4 * k][r] = R(0);
+    }
+    if (tid == 0)
+        failed = 0;
+    __syncthreads();
+
+    // store the 16 x 16 accumulator blocks (lane layout of mma16) at (ro, co)
+    // of M, scaled by sg
+    auto put = [&](R (*M)[LEAF][LDL], int ro, int co, const V4 &cr, const V4 &ci, R sg) {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+            const int rr = li, cc = acc_row<R>(lk, qq);
+            M[0][co + cc][ro + rr] = sg * cr[qq];
+            M[1][co + cc][ro + rr] = sg * ci[qq];
+        }
+    };
+
+    for (int b = 0; b < NB; ++b) {
+        const int o = b * LB16;
+        if (wave == 0) {
+            if (p.factor)
+                diag16c<R, true>(S[0], S[1], X[0], X[1], o, lb, p.col0 + (int)c0, p.info, &failed);
+            else
+                diag16c<R, false>(S[0], S[1], X[0], X[1], o, lb, p.col0 + (int)c0, p.info, &failed);
+        }
+        __syncthreads();
+        if (p.factor) {
+            // L(i, b) = A(i, b) inv(L(b, b))^H, one block per wave
+            const int i = b + 1 + wave;
+            if (i < NB) {
+                V4 cr = {0, 0, 0, 0}, ci = {0, 0, 0, 0};
+                mma16c<R, true>(&S[0][o][i * LB16], &S[1][o][i * LB16], LDL, 1, &X[0][o][o], &X[1][o][o], LDL, 1,
+                                cr, ci);
+                put(S, i * LB16, o, cr, ci, R(1));
+            }
+            __syncthreads();
+            // A(i, j) -= L(i, b) L(j, b)^H, b < j <= i
+            for (int t = wave; t < (NB - 1 - b) * (NB - b) / 2; t += 4) {
+                int ti, tj;
+                tri_index(t, ti, tj);
+                const int i2 = b + 1 + ti, j2 = b + 1 + tj;
+                V4 cr = {0, 0, 0, 0}, ci = {0, 0, 0, 0};
+                mma16c<R, true>(&S[0][o][i2 * LB16], &S[1][o][i2 * LB16], LDL, 1, &S[0][o][j2 * LB16],
+                                &S[1][o][j2 * LB16], LDL, 1, cr, ci);
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    const int rr = li, cc = acc_row<R>(lk, qq);
+                    if (i2 != j2 || rr >= cc) {
+                        S[0][j2 * LB16 + cc][i2 * LB16 + rr] -= cr[qq];
+                        S[1][j2 * LB16 + cc][i2 * LB16 + rr] -= ci[qq];
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    // inverse off-diagonal blocks, by distance d = i - b
+    for (int d = 1; d < NB; ++d) {
+        const int b = wave, i = b + d;
+        if (i < NB) {
+            V4 cr = {0, 0, 0, 0}, ci = {0, 0, 0, 0};
+            for (int k = b; k < i; ++k)  // T = sum_k L(i, k) X(k, b)
+                mma16c<R, false>(&S[0][k * LB16][i * LB16], &S[1][k * LB16][i * LB16], LDL, 1,
+                                 &X[0][b * LB16][k * LB16], &X[1][b * LB16][k * LB16], 1, LDL, cr, ci);
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {  // Tm[.][c][r] = T(r, c)
+                Tm[wave][0][acc_row<R>(lk, qq)][li] = cr[qq];
+                Tm[wave][1][acc_row<R>(lk, qq)][li] = ci[qq];
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's LDS stores done before reading them back
+            __builtin_amdgcn_wave_barrier();
+            V4 c2r = {0, 0, 0, 0}, c2i = {0, 0, 0, 0};  // X(i, b) = -inv(L(i, i)) T
+            mma16c<R, false>(&X[0][i * LB16][i * LB16], &X[1][i * LB16][i * LB16], LDL, 1, &Tm[wave][0][0][0],
+                             &Tm[wave][1][0][0], 1, LB16 + 1, c2r, c2i);
+            put(X, i * LB16, b * LB16, c2r, c2i, R(-1));
+        }
+        __syncthreads();
+    }
+
+    if (failed)
+        return;
+#pragma unroll
+    for (int k = 0; k < LEAF / 4; ++k) {
+        const int c = g + 4 * k;
+        if (r < lb && c < lb) {
+            if (p.factor && r >= c)
+                Elem<R, true>::store(A + r + (int64_t)c * p.lda, S[0][c][r], r == c ? R(0) : S[1][c][r]);
+            if (r >= c)
+                Elem<R, true>::store(Inv + r + (int64_t)c * p.ldi, X[0][c][r], X[1][c][r]);
+            else
+                Elem<R, true>::store(Inv + r + (int64_t)c * p.ldi, R(0), R(0));
         }
     }
 }
