@@ -463,21 +463,24 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) l
 // lane c; then A(c, r) -= L(c, j) conj(L(r, j)) and x[r] -= L(r, j) x[j] for
 // r > j, with L(r, j) read from lane r.  Every complex 16 x 16 x 16 product is
 // sixteen v_mfma_*_16x16x4 (four per complex multiply-add).
+//
+// LDS: one array S per plane holds L in its lower triangle (S[c][r] =
+// L(r, c), r >= c) and the strict lower triangle of inv(L) in its upper one
+// (S[r][c] = inv(L)(r, c), r > c); inv(L)'s diagonal is kept apart.  That is
+// 85 KB in all, so a leaf fits on a CU beside one trailing-update workgroup.
 
-// acc += A op(B) for complex 16 x 16 blocks in LDS planes (real, imaginary):
-// A(r, k) = pa*[k * ak + r * ar], B(k, c) = pb*[k * bk + c * bc], op(B) =
-// conj(B) when CB.  Lane layout as mma16.
-template <typename R, bool CB>
-__device__ __forceinline__ void mma16c(const R *par, const R *pai, int ak, int ar, const R *pbr, const R *pbi, int bk,
-                                       int bc, typename AccT<R>::type &cr, typename AccT<R>::type &ci)
+// acc += A B for complex 16 x 16 blocks whose elements come from fa(r, k, re,
+// im) and fb(k, c, re, im).  Lane layout as mma16.
+template <typename R, typename FA, typename FB>
+__device__ __forceinline__ void mma16c(FA fa, FB fb, typename AccT<R>::type &cr, typename AccT<R>::type &ci)
 {
     const int lane = threadIdx.x & 63, li = lane & 15, lk = lane >> 4;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         const int k = 4 * s + lk;
-        const R a0 = par[k * ak + li * ar], a1 = pai[k * ak + li * ar];
-        const R b0 = pbr[k * bk + li * bc];
-        const R b1 = CB ? -pbi[k * bk + li * bc] : pbi[k * bk + li * bc];
+        R a0, a1, b0, b1;
+        fa(li, k, a0, a1);
+        fb(k, li, b0, b1);
         cr = mfma16(b0, a0, cr);
         cr = mfma16(-b1, a1, cr);
         ci = mfma16(b1, a0, ci);
@@ -534,11 +537,10 @@ __device__ __forceinline__ void diag16c_step(R *ar, R *ai, R *xr, R *xi, int c, 
 
 // Factor (FACTOR) and invert, or only invert, the complex 16 x 16 diagonal
 // block at (o, o) of S0 + i S1 (S*[c][r] = element (r, c), lower triangle);
-// L goes back to S (zeros above the diagonal, real diagonal), inv(L) to X.
-// One wave, as diag16.
+// L goes back to S's lower triangle (real diagonal), inv(L) to S's upper
+// triangle and Xd (its diagonal).  One wave, as diag16.
 template <typename R, bool FACTOR>
-__device__ void diag16c(R (*S0)[LDL], R (*S1)[LDL], R (*X0)[LDL], R (*X1)[LDL], int o, int lb, int gcol, int *info,
-                        int *failed)
+__device__ void diag16c(R (*S0)[LDL], R (*S1)[LDL], R *Xd0, R *Xd1, int o, int lb, int gcol, int *info, int *failed)
 {
     const int lane = threadIdx.x & 63, c = lane & 15;
     R ar[LB16], ai[LB16], xr[LB16], xi[LB16];
@@ -561,13 +563,18 @@ __device__ void diag16c(R (*S0)[LDL], R (*S1)[LDL], R (*X0)[LDL], R (*X1)[LDL], 
     if (lane < LB16) {
 #pragma unroll
         for (int r = 0; r < LB16; ++r) {
-            if constexpr (FACTOR) {  // row c of L
-                S0[o + r][o + c] = (r <= c) ? ar[r] : R(0);
-                S1[o + r][o + c] = (r <= c) ? ai[r] : R(0);
+            if (r <= c) {  // row c of L
+                if constexpr (FACTOR) {
+                    S0[o + r][o + c] = ar[r];
+                    S1[o + r][o + c] = ai[r];
+                }
+            } else {  // column c of inv(L) below its diagonal
+                S0[o + r][o + c] = xr[r];
+                S1[o + r][o + c] = xi[r];
             }
-            X0[o + c][o + r] = (r >= c) ? xr[r] : R(0);  // column c of inv(L)
-            X1[o + c][o + r] = (r >= c) ? xi[r] : R(0);
         }
+        Xd0[o + c] = xr[c];
+        Xd1[o + c] = xi[c];
     }
 }
 
@@ -577,8 +584,8 @@ __global__ void __launch_bounds__(256) leaf16c_kernel(const LeafArgs p)
     typedef typename AccT<R>::type V4;
     typedef typename Elem<R, true>::type E;
     constexpr int NB = LEAF / LB16;
-    __shared__ R S[2][LEAF][LDL];           // S[.][c][r] = L(r, c)
-    __shared__ R X[2][LEAF][LDL];           // X[.][c][r] = inv(L)(r, c)
+    __shared__ R S[2][LEAF][LDL];           // L below the diagonal, inv(L) above (see above)
+    __shared__ R Xd[2][LEAF];               // diagonal of inv(L)
     __shared__ R Tm[4][2][LB16][LB16 + 1];  // per-wave 16 x 16 scratch
     __shared__ int failed;
 
@@ -612,21 +619,30 @@ __global__ void __launch_bounds__(256) leaf16c_kernel(const LeafArgs p)
     for (int k = 0; k < LEAF / 4; ++k) {
         S[0][g + 4 * k][r] = vr[k];
         S[1][g + 4 * k][r] = vi[k];
-        X[0][g + 4 * k][r] = R(0);
-        X[1][g + 4 * k][r] = R(0);
     }
     if (tid == 0)
         failed = 0;
     __syncthreads();
 
-    // store the 16 x 16 accumulator blocks (lane layout of mma16) at (ro, co)
-    // of M, scaled by sg
-    auto put = [&](R (*M)[LEAF][LDL], int ro, int co, const V4 &cr, const V4 &ci, R sg) {
+    // operand fetchers: element (row, col) of L (lower triangle), of inv(L)
+    // (zero above its diagonal) and of conj(inv(L))^T
+    auto lget = [&](int row, int col, R &re, R &im) {
+        re = S[0][col][row];
+        im = S[1][col][row];
+    };
+    auto xget = [&](int row, int col, R &re, R &im) {
+        re = row > col ? S[0][row][col] : row == col ? Xd[0][row] : R(0);
+        im = row > col ? S[1][row][col] : row == col ? Xd[1][row] : R(0);
+    };
+    // store the 16 x 16 accumulator blocks (lane layout of mma16) as rows ro..,
+    // columns co.. of L (lower part) or, below its diagonal, of inv(L), scaled by sg
+    auto put = [&](bool inv, int ro, int co, const V4 &cr, const V4 &ci, R sg) {
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
-            const int rr = li, cc = acc_row<R>(lk, qq);
-            M[0][co + cc][ro + rr] = sg * cr[qq];
-            M[1][co + cc][ro + rr] = sg * ci[qq];
+            const int rr = ro + li, cc = co + acc_row<R>(lk, qq);
+            const int i0 = inv ? rr : cc, i1 = inv ? cc : rr;
+            S[0][i0][i1] = sg * cr[qq];
+            S[1][i0][i1] = sg * ci[qq];
         }
     };
 
@@ -634,19 +650,24 @@ __global__ void __launch_bounds__(256) leaf16c_kernel(const LeafArgs p)
         const int o = b * LB16;
         if (wave == 0) {
             if (p.factor)
-                diag16c<R, true>(S[0], S[1], X[0], X[1], o, lb, p.col0 + (int)c0, p.info, &failed);
+                diag16c<R, true>(S[0], S[1], Xd[0], Xd[1], o, lb, p.col0 + (int)c0, p.info, &failed);
             else
-                diag16c<R, false>(S[0], S[1], X[0], X[1], o, lb, p.col0 + (int)c0, p.info, &failed);
+                diag16c<R, false>(S[0], S[1], Xd[0], Xd[1], o, lb, p.col0 + (int)c0, p.info, &failed);
         }
         __syncthreads();
         if (p.factor) {
             // L(i, b) = A(i, b) inv(L(b, b))^H, one block per wave
+            // (each wave reads and then writes only its own block of column b)
             const int i = b + 1 + wave;
             if (i < NB) {
                 V4 cr = {0, 0, 0, 0}, ci = {0, 0, 0, 0};
-                mma16c<R, true>(&S[0][o][i * LB16], &S[1][o][i * LB16], LDL, 1, &X[0][o][o], &X[1][o][o], LDL, 1,
-                                cr, ci);
-                put(S, i * LB16, o, cr, ci, R(1));
+                mma16c<R>([&](int rr, int k, R &re, R &im) { lget(i * LB16 + rr, o + k, re, im); },
+                          [&](int k, int cc, R &re, R &im) {
+                              xget(o + cc, o + k, re, im);
+                              im = -im;
+                          },
+                          cr, ci);
+                put(false, i * LB16, o, cr, ci, R(1));
             }
             __syncthreads();
             // A(i, j) -= L(i, b) L(j, b)^H, b < j <= i
@@ -654,15 +675,19 @@ __global__ void __launch_bounds__(256) leaf16c_kernel(const LeafArgs p)
                 int ti, tj;
                 tri_index(t, ti, tj);
                 const int i2 = b + 1 + ti, j2 = b + 1 + tj;
-                V4 cr = {0, 0, 0, 0}, ci = {0, 0, 0, 0};
-                mma16c<R, true>(&S[0][o][i2 * LB16], &S[1][o][i2 * LB16], LDL, 1, &S[0][o][j2 * LB16],
-                                &S[1][o][j2 * LB16], LDL, 1, cr, ci);
+                V4 dr = {0, 0, 0, 0}, di = {0, 0, 0, 0};
+                mma16c<R>([&](int rr, int k, R &re, R &im) { lget(i2 * LB16 + rr, o + k, re, im); },
+                          [&](int k, int cc, R &re, R &im) {
+                              lget(j2 * LB16 + cc, o + k, re, im);
+                              im = -im;
+                          },
+                          dr, di);
 #pragma unroll
                 for (int qq = 0; qq < 4; ++qq) {
                     const int rr = li, cc = acc_row<R>(lk, qq);
                     if (i2 != j2 || rr >= cc) {
-                        S[0][j2 * LB16 + cc][i2 * LB16 + rr] -= cr[qq];
-                        S[1][j2 * LB16 + cc][i2 * LB16 + rr] -= ci[qq];
+                        S[0][j2 * LB16 + cc][i2 * LB16 + rr] -= dr[qq];
+                        S[1][j2 * LB16 + cc][i2 * LB16 + rr] -= di[qq];
                     }
                 }
             }
@@ -676,8 +701,9 @@ __global__ void __launch_bounds__(256) leaf16c_kernel(const LeafArgs p)
         if (i < NB) {
             V4 cr = {0, 0, 0, 0}, ci = {0, 0, 0, 0};
             for (int k = b; k < i; ++k)  // T = sum_k L(i, k) X(k, b)
-                mma16c<R, false>(&S[0][k * LB16][i * LB16], &S[1][k * LB16][i * LB16], LDL, 1,
-                                 &X[0][b * LB16][k * LB16], &X[1][b * LB16][k * LB16], 1, LDL, cr, ci);
+                mma16c<R>([&](int rr, int kk, R &re, R &im) { lget(i * LB16 + rr, k * LB16 + kk, re, im); },
+                          [&](int kk, int cc, R &re, R &im) { xget(k * LB16 + kk, b * LB16 + cc, re, im); }, cr,
+                          ci);
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {  // Tm[.][c][r] = T(r, c)
                 Tm[wave][0][acc_row<R>(lk, qq)][li] = cr[qq];
@@ -686,9 +712,13 @@ __global__ void __launch_bounds__(256) leaf16c_kernel(const LeafArgs p)
             __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's LDS stores done before reading them back
             __builtin_amdgcn_wave_barrier();
             V4 c2r = {0, 0, 0, 0}, c2i = {0, 0, 0, 0};  // X(i, b) = -inv(L(i, i)) T
-            mma16c<R, false>(&X[0][i * LB16][i * LB16], &X[1][i * LB16][i * LB16], LDL, 1, &Tm[wave][0][0][0],
-                             &Tm[wave][1][0][0], 1, LB16 + 1, c2r, c2i);
-            put(X, i * LB16, b * LB16, c2r, c2i, R(-1));
+            mma16c<R>([&](int rr, int kk, R &re, R &im) { xget(i * LB16 + rr, i * LB16 + kk, re, im); },
+                      [&](int kk, int cc, R &re, R &im) {
+                          re = Tm[wave][0][cc][kk];
+                          im = Tm[wave][1][cc][kk];
+                      },
+                      c2r, c2i);
+            put(true, i * LB16, b * LB16, c2r, c2i, R(-1));
         }
         __syncthreads();
     }
@@ -701,10 +731,9 @@ __global__ void __launch_bounds__(256) leaf16c_kernel(const LeafArgs p)
         if (r < lb && c < lb) {
             if (p.factor && r >= c)
                 Elem<R, true>::store(A + r + (int64_t)c * p.lda, S[0][c][r], r == c ? R(0) : S[1][c][r]);
-            if (r >= c)
-                Elem<R, true>::store(Inv + r + (int64_t)c * p.ldi, X[0][c][r], X[1][c][r]);
-            else
-                Elem<R, true>::store(Inv + r + (int64_t)c * p.ldi, R(0), R(0));
+            R xr = R(0), xi = R(0);
+            xget(r, c, xr, xi);
+            Elem<R, true>::store(Inv + r + (int64_t)c * p.ldi, xr, xi);
         }
     }
 }
