@@ -275,6 +275,23 @@ def test_info_negative_pivot(gpu, j):
     assert torch.isnan(X).all()
 
 
+@pytest.mark.parametrize("dt,j", [("c128", 0), ("c128", 21), ("c128", 64), ("c128", 150), ("c128", 299),
+                                  ("c64", 37), ("c64", 200)])
+def test_info_negative_pivot_complex(gpu, dt, j):
+    """A negative pivot anywhere in a complex leaf (inside a 16 x 16 diagonal
+    block, on a block boundary, in a later tile) stops the factorization at
+    the oracle's column."""
+    n, T = 300, 64
+    A = spdgen.make_A(n, dt, 0.5, 5, device="cuda")
+    A[j, j] = -1.0
+    _, info_o = oracle.potrf(wide(A))
+    L, X = cm_copy(A), cm_copy(spdgen.make_B(n, 2, dt, 5, device="cuda"))
+    info, ld = gpu_solve(gpu, L, X, T)
+    assert info == info_o == j + 1
+    assert math.isnan(ld)
+    assert torch.isnan(torch.view_as_real(X)).all()
+
+
 def test_info_nan_and_zero(gpu):
     n = 100
     A = spdgen.make_A(n, "c128", 0.5, 4, device="cuda")
