@@ -520,35 +520,34 @@ struct Solver {
         return 0;
     }
 
-    // Real types: factor and invert the lb x lb leaf at D and solve the prows
-    // rows below it, P <- P inv(L_leaf)^T in place, in one launch.
+    // Factor and invert the lb x lb leaf at D and solve the prows rows below
+    // it, P <- P inv(L_leaf)^H in place, in one launch (ctr: the workgroup
+    // counter, 0 between launches).
     static int leaf_panel(E *D, int64_t lda, int64_t lb, int64_t prows, E *Inv, int64_t ldi, int *info, int *ctr,
                           int64_t col0, hipStream_t s)
     {
-        if constexpr (CPLX) {
-            g_last_error = "fused leaf and panel launch is for real types";
-            return SPD_ERR_HIP;
-        } else {
-            LeafArgs p;
-            p.A = D;
-            p.lda = lda;
-            p.Inv = Inv;
-            p.ldi = ldi;
-            p.sInv = 0;
-            p.n = (int)lb;
-            p.T = (int)lb;
-            p.lpt = 1;
-            p.factor = 1;
-            p.info = info;
-            p.col0 = (int)col0;
-            p.prows = (int)prows;
-            p.ctr = ctr;
-            const int64_t grid = 1 + cdiv(prows, LEAF);
-            SPD_VALIDATE((check_leaf<R, CPLX>(p, (unsigned)grid, g_chk, true)));
+        LeafArgs p;
+        p.A = D;
+        p.lda = lda;
+        p.Inv = Inv;
+        p.ldi = ldi;
+        p.sInv = 0;
+        p.n = (int)lb;
+        p.T = (int)lb;
+        p.lpt = 1;
+        p.factor = 1;
+        p.info = info;
+        p.col0 = (int)col0;
+        p.prows = (int)prows;
+        p.ctr = ctr;
+        const int64_t grid = 1 + cdiv(prows, LEAF);
+        SPD_VALIDATE((check_leaf<R, CPLX>(p, (unsigned)grid, g_chk, true)));
+        if constexpr (CPLX)
+            leaf16c_kernel<R, true><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p);
+        else
             leaf16_kernel<R, true><<<dim3((unsigned)grid), dim3(256), 0, s>>>(p);
-            SPD_CHECK_LAUNCH("leaf16_kernel (leaf + panel)");
-            return 0;
-        }
+        SPD_CHECK_LAUNCH("leaf16_kernel (leaf + panel)");
+        return 0;
     }
 
     // Complete inv(L_tt) from its inverted leaves for `ntiles` tiles of size tk
@@ -886,31 +885,10 @@ struct Solver {
                 E *Db = D + b0 + b0 * lda;
                 const int64_t r = tk - b0 - lb;
                 E *P = Db + lb;  // r x lb below the leaf
-                if constexpr (!CPLX) {
-                    // the leaf and P <- P inv(Lb)^T in one launch
-                    SPD_TRY(leaf_panel(Db, lda, lb, std::max<int64_t>(r, 0), Inv + b0 * (1 + T), T, info, ctr, c0 + b0,
-                                       s));
-                    if (r <= 0)
-                        continue;
-                } else {
-                    SPD_TRY(leaves(Db, lda, lb, lb, Inv + b0 * (1 + T), T, 0, 1, true, info, c0 + b0, s));
-                    if (r <= 0)
-                        continue;
-                    Gemm g;  // P <- P inv(Lb)^H, in place (one tile column)
-                    g.A = P;
-                    g.lda = lda;
-                    g.B = Inv + b0 * (1 + T);
-                    g.ldb = T;
-                    g.C = P;
-                    g.ldc = lda;
-                    g.m = r;
-                    g.n = lb;
-                    g.k = lb;
-                    g.kmode = KM_END_BY_J;
-                    g.info = info;
-                    g.inplace = true;
-                    SPD_TRY((gemm<R, CPLX>(NT, g, s)));
-                }
+                // the leaf and P <- P inv(Lb)^H in one launch
+                SPD_TRY(leaf_panel(Db, lda, lb, std::max<int64_t>(r, 0), Inv + b0 * (1 + T), T, info, ctr, c0 + b0, s));
+                if (r <= 0)
+                    continue;
                 Gemm u;  // rest of the tile: lower part of D22 -= P P^H
                 u.A = P;
                 u.lda = lda;
@@ -1009,8 +987,7 @@ struct Solver {
         const int64_t T = L.T, nt = L.nt;
         E *Inv = (E *)work + L.inv;  // inverse of the current diagonal tile, ld T
         int *ctr = (int *)((E *)work + L.ctr);
-        if constexpr (!CPLX)
-            SPD_TRY(set_info(ctr, s));
+        SPD_TRY(set_info(ctr, s));
         E *Wb[2] = {(E *)work + L.w, (E *)work + L.w + L.wsz};
         SPD_TRY(zero2d<E>(Inv, T, T, hook != nullptr ? nt * T : T, s));
         if (hook != nullptr && !two_step_schedule(T, nt)) {

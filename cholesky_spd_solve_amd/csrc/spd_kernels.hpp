@@ -488,6 +488,23 @@ __device__ __forceinline__ void mma16c(FA fa, FB fb, typename AccT<R>::type &cr,
     }
 }
 
+// As mma16c with A's operands already in registers: a*[s] = A(li, 4 s + lk).
+template <typename R, typename FB>
+__device__ __forceinline__ void mma16c_ra(const R (&ar)[4], const R (&ai)[4], FB fb, typename AccT<R>::type &cr,
+                                          typename AccT<R>::type &ci)
+{
+    const int lane = threadIdx.x & 63, li = lane & 15, lk = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        R b0, b1;
+        fb(4 * s + lk, li, b0, b1);
+        cr = mfma16(b0, ar[s], cr);
+        cr = mfma16(-b1, ai[s], cr);
+        ci = mfma16(b1, ar[s], ci);
+        ci = mfma16(b0, ai[s], ci);
+    }
+}
+
 // Column J of the complex sweep (pivot scale s, ljj already known), then the
 // columns after it; the pivot is diag16_pivot's on the real parts.
 template <typename R, bool FACTOR, int J>
@@ -540,7 +557,8 @@ __device__ __forceinline__ void diag16c_step(R *ar, R *ai, R *xr, R *xi, int c, 
 // L goes back to S's lower triangle (real diagonal), inv(L) to S's upper
 // triangle and Xd (its diagonal).  One wave, as diag16.
 template <typename R, bool FACTOR>
-__device__ void diag16c(R (*S0)[LDL], R (*S1)[LDL], R *Xd0, R *Xd1, int o, int lb, int gcol, int *info, int *failed)
+__device__ __forceinline__ void diag16c(R (*S0)[LDL], R (*S1)[LDL], R *Xd0, R *Xd1, int o, int lb, int gcol, int *info,
+                                        int *failed)
 {
     const int lane = threadIdx.x & 63, c = lane & 15;
     R ar[LB16], ai[LB16], xr[LB16], xi[LB16];
@@ -578,7 +596,14 @@ __device__ void diag16c(R (*S0)[LDL], R (*S1)[LDL], R *Xd0, R *Xd1, int o, int l
     }
 }
 
-template <typename R>
+// PANEL: one launch factors a single leaf and solves the p.prows panel rows
+// below it, L(i, leaf) = A(i, leaf) inv(L_leaf)^H, as leaf16_kernel's PANEL
+// mode: every workgroup factors and inverts the leaf in its own LDS (the same
+// bits), workgroup w >= 1 multiplies rows [64(w-1), 64w) of the panel in place,
+// reading them straight into the matrix-core operand registers (no LDS), and
+// the last workgroup to count itself out on p.ctr stores L and inv(L) and
+// resets the counter.  Only workgroup 0 records info.
+template <typename R, bool PANEL = false>
 __global__ void __launch_bounds__(256) leaf16c_kernel(const LeafArgs p)
 {
     typedef typename AccT<R>::type V4;
@@ -591,13 +616,15 @@ __global__ void __launch_bounds__(256) leaf16c_kernel(const LeafArgs p)
 
     int64_t c0, ioff;
     int lb;
-    if (!leaf_geom(p, (int)blockIdx.x, c0, lb, ioff))
+    const int w = PANEL ? (int)blockIdx.x : 0;  // panel block of this workgroup (0: none)
+    if (!leaf_geom(p, PANEL ? 0 : (int)blockIdx.x, c0, lb, ioff))
         return;
     E *A = (E *)p.A + c0 + c0 * p.lda;
     E *Inv = (E *)p.Inv + ioff;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int li = lane & 15, lk = lane >> 4;
     const int r = tid & (LEAF - 1), g = tid / LEAF;
+    int *const info = (w == 0) ? p.info : nullptr;
 
     // all loads in flight together, the status word alongside them; the
     // diagonal's imaginary part is taken as 0 and padding beyond lb is the
@@ -650,9 +677,9 @@ __global__ void __launch_bounds__(256) leaf16c_kernel(const LeafArgs p)
         const int o = b * LB16;
         if (wave == 0) {
             if (p.factor)
-                diag16c<R, true>(S[0], S[1], Xd[0], Xd[1], o, lb, p.col0 + (int)c0, p.info, &failed);
+                diag16c<R, true>(S[0], S[1], Xd[0], Xd[1], o, lb, p.col0 + (int)c0, info, &failed);
             else
-                diag16c<R, false>(S[0], S[1], Xd[0], Xd[1], o, lb, p.col0 + (int)c0, p.info, &failed);
+                diag16c<R, false>(S[0], S[1], Xd[0], Xd[1], o, lb, p.col0 + (int)c0, info, &failed);
         }
         __syncthreads();
         if (p.factor) {
@@ -725,6 +752,59 @@ __global__ void __launch_bounds__(256) leaf16c_kernel(const LeafArgs p)
 
     if (failed)
         return;
+    if constexpr (PANEL) {
+        if (w > 0) {
+            // wave v owns panel rows 16v .. 16v + 15 of this block:
+            // P(v, j) = sum_{k <= j} B(v, k) conj(inv(L)(j, k)) over 16 x 16 blocks,
+            // B read from global in the operand layout of mma16c (lane (li, lk)
+            // holds B(16v + li, 16 bk + 4 s + lk) in br[bk][s] + i bi[bk][s])
+            E *const Pb = A + lb + (int64_t)(w - 1) * LEAF;  // rows lb + 64(w-1) .. of the leaf's columns
+            const int prow = p.prows - (w - 1) * LEAF;       // its rows that exist
+            const int row = wave * LB16 + li;
+            R br[NB][4], bi[NB][4];
+#pragma unroll
+            for (int bk = 0; bk < NB; ++bk)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int k = bk * LB16 + 4 * q + lk;
+                    br[bk][q] = R(0);
+                    bi[bk][q] = R(0);
+                    if (row < prow && k < lb)
+                        Elem<R, true>::load(Pb + row + (int64_t)k * p.lda, br[bk][q], bi[bk][q]);
+                }
+            // every block of the row is read before any is overwritten (the
+            // rows belong to this wave alone)
+#pragma unroll
+            for (int bj = 0; bj < NB; ++bj) {
+                V4 cr = {0, 0, 0, 0}, ci = {0, 0, 0, 0};
+#pragma unroll
+                for (int bk = 0; bk <= bj; ++bk)
+                    mma16c_ra<R>(br[bk], bi[bk],
+                                 [&](int kk, int cc, R &re, R &im) {
+                                     xget(bj * LB16 + cc, bk * LB16 + kk, re, im);
+                                     im = -im;
+                                 },
+                                 cr, ci);
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    const int cc = bj * LB16 + acc_row<R>(lk, qq);
+                    if (row < prow && cc < lb)
+                        Elem<R, true>::store(Pb + row + (int64_t)cc * p.lda, cr[qq], ci[qq]);
+                }
+            }
+        }
+        // count out; the last workgroup stores the leaf
+        __shared__ int last;
+        __syncthreads();
+        if (tid == 0) {
+            last = atomicAdd(p.ctr, 1) == (int)gridDim.x - 1;
+            if (last)
+                atomicExch(p.ctr, 0);
+        }
+        __syncthreads();
+        if (!last)
+            return;
+    }
 #pragma unroll
     for (int k = 0; k < LEAF / 4; ++k) {
         const int c = g + 4 * k;
