@@ -132,7 +132,6 @@ struct Gemm {
     bool beta = false;
     const int *info = nullptr;
     bool small = false;    // prefer the small tile shape
-    bool inplace = false;  // C aliases A: one workgroup must own whole rows (n <= BN)
 };
 
 template <typename R, bool CPLX, int BM, int BN, int KB, int WM, int WN, bool AT, bool BT>
@@ -188,16 +187,6 @@ static int gemm(Lay lay, const Gemm &g, hipStream_t s)
         return 0;
     if (g.k <= 0 && g.beta)
         return 0;
-    if (g.inplace) {
-        // C aliases A: a workgroup reads rows [i0, i0 + BM) of A for every k and
-        // writes the same rows of C only after its last read, so it must cover
-        // all n columns itself.
-        if (g.n > 64 || g.A != g.C) {
-            g_last_error = "in-place product needs n <= 64 and C == A";
-            return SPD_ERR_HIP;
-        }
-        return launch_gemm_cfg<R, CPLX, 64, 64, 16, 2, 2>(lay, g, s);
-    }
     if constexpr (!CPLX) {
         // large products: 128x128 tiles; small ones: 64x64, or 32x32 when even
         // 64x64 tiles would leave most CUs idle (latency-bound chains)
