@@ -413,12 +413,12 @@ static bool lookahead_enabled()
 // dry run (no HIP calls) both schedules run on the caller's stream.
 struct AuxStreams {
     hipStream_t look = nullptr, look2 = nullptr;
-    hipEvent_t ev_fork = nullptr, ev_panel = nullptr, ev_rest = nullptr, ev_fw = nullptr, ev_col = nullptr;
+    hipEvent_t ev_fork = nullptr, ev_panel = nullptr, ev_rest = nullptr, ev_fw = nullptr;
 };
 
 struct Lookahead {
     hipStream_t look = nullptr, look2 = nullptr;  // look2: the fused solve's forward substitution
-    hipEvent_t ev_fork = nullptr, ev_panel = nullptr, ev_rest = nullptr, ev_fw = nullptr, ev_col = nullptr;
+    hipEvent_t ev_fork = nullptr, ev_panel = nullptr, ev_rest = nullptr, ev_fw = nullptr;
 
     int begin(hipStream_t s)
     {
@@ -440,7 +440,7 @@ struct Lookahead {
             if ((e = hipStreamCreateWithFlags(&n.look, hipStreamNonBlocking)) != hipSuccess ||
                 (e = hipStreamCreateWithFlags(&n.look2, hipStreamNonBlocking)) != hipSuccess)
                 return hip_fail(e, "hipStreamCreateWithFlags");
-            for (hipEvent_t *ev : {&n.ev_fork, &n.ev_panel, &n.ev_rest, &n.ev_fw, &n.ev_col})
+            for (hipEvent_t *ev : {&n.ev_fork, &n.ev_panel, &n.ev_rest, &n.ev_fw})
                 if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess)
                     return hip_fail(e, "hipEventCreateWithFlags");
             per_device.emplace_back(dev, n);
@@ -452,7 +452,6 @@ struct Lookahead {
         ev_panel = x->ev_panel;
         ev_rest = x->ev_rest;
         ev_fw = x->ev_fw;
-        ev_col = x->ev_col;
         // the auxiliary streams start after everything already queued on s
         SPD_TRY_HIP(hipEventRecord(ev_fork, s), "hipEventRecord");
         SPD_TRY_HIP(hipStreamWaitEvent(look, ev_fork, 0), "hipStreamWaitEvent");
@@ -1035,11 +1034,7 @@ struct Solver {
     // potrf.  Step 0 is a single step whose auxiliary part solves tiles 1 and 2,
     // so that the caller's first update starts after tile 0 alone.  Panels live
     // in four buffers of one leading dimension; panel k's row 0 is row (k+1)T of
-    // A.  In the single steps with fewer than 32 T rows beyond the next tile
-    // column, the auxiliary stream's chain is the longer of the two; there the
-    // caller's update also waits for the auxiliary stream's update of tile
-    // column k+1, which then has the GPU to itself (measured 0.35 ms less per
-    // solve at N = 32768, T = 512).
+    // A.
     static int potrf_pairs(int64_t n, E *A, int64_t lda, const Layout &L, E *Inv0, int *info, int *ctr, void *work,
                            hipStream_t s, const PanelHook *hook = nullptr)
     {
@@ -1105,14 +1100,9 @@ struct Solver {
             SPD_TRY(la.wait(s, la.ev_panel));  // panel k
             SPD_TRY(la.wait(sl, la.ev_rest));  // the update of step k-1 reached tile column k+1
             SPD_TRY(syrk(n - (k + 1) * T, Wp(k), ldw, kp, T, C(k + 1), lda, T, info, sl, aux_update()));
-            const bool tail = n - (k + 2) * T < 32 * T;
-            if (tail)
-                SPD_TRY(la.record(la.ev_col, sl));
             SPD_TRY(diag_panel((k + 1) * T, Wp(k + 1), sl));
             SPD_TRY(la.record(la.ev_panel, sl));
             SPD_TRY(done(k + 1, k + 2));
-            if (tail)
-                SPD_TRY(la.wait(s, la.ev_col));
             if ((k + 2) * T < n)
                 SPD_TRY(syrk(n - (k + 2) * T, Wp(k) + T, ldw, kp, T, C(k + 2), lda, 0, info, s));
             SPD_TRY(la.record(la.ev_rest, s));
