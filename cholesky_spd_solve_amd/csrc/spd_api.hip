@@ -1192,7 +1192,10 @@ struct Solver {
                     double *logdet_out, void *work, hipStream_t s)
     {
         const Layout L = make_layout(std::max<int64_t>(n, 1), nrhs, T_A, sizeof(E));
-        bool fused = !CPLX && n > 0 && nrhs > 0 && rect_usable(lda) && two_step_schedule(L.T, L.nt);
+        // real types take the block-update kernel for the substitutions, complex
+        // types (and very large leading dimensions) the general product
+        const bool blocks = !CPLX && rect_usable(lda);
+        bool fused = n > 0 && nrhs > 0 && two_step_schedule(L.T, L.nt);
         if (!fused) {
             SPD_TRY(potrf(n, A, lda, T_A, info, work, s));
             if (logdet_out != nullptr)
@@ -1215,6 +1218,26 @@ struct Solver {
         auto step = [&](int64_t k) -> int {  // Y_k = inv(L_kk) B_k, then B below -= L_panel Y_k
             const int64_t c0 = k * T, tk = std::min(T, n - c0), r0 = c0 + tk, kp = align_up(tk, RECT_KB);
             SPD_TRY(apply_inv(Inv, k, T, B, ldb, c0, tk, nrhs, Tmp, false, info, fs));
+            if (!blocks) {
+                SPD_TRY(copy2d<E>(B + c0, ldb, Tmp, T, tk, nrhs, info, fs));
+                if (r0 < n) {
+                    Gemm u;  // B_below -= L_panel Y_k
+                    u.A = A + r0 + c0 * lda;
+                    u.lda = lda;
+                    u.B = B + c0;
+                    u.ldb = ldb;
+                    u.C = B + r0;
+                    u.ldc = ldb;
+                    u.m = n - r0;
+                    u.n = nrhs;
+                    u.k = tk;
+                    u.neg = true;
+                    u.beta = true;
+                    u.info = info;
+                    SPD_TRY((gemm<R, CPLX>(NN, u, fs)));
+                }
+                return 0;
+            }
             SPD_TRY(copy_t(B + c0, ldb, Qf, L.ldq, Tmp, T, tk, nrhs, kp, info, fs));
             if (r0 < n)
                 SPD_TRY(rect<false>(A + r0 + c0 * lda, lda, Qf, L.ldq, B + r0, ldb, n - r0, nrhs, kp, tk, vec, info,
@@ -1239,7 +1262,10 @@ struct Solver {
             SPD_TRY(logdet(n, A, lda, info, logdet_out, s));
         {
             ProfScope ps(PROF_SOLVE, FMUL * (double)n * n * nrhs, s);
-            SPD_TRY(potrs_blocks(n, nrhs, A, lda, B, ldb, L, info, work, s, true, false, nullptr, false));
+            if (blocks)
+                SPD_TRY(potrs_blocks(n, nrhs, A, lda, B, ldb, L, info, work, s, true, false, nullptr, false));
+            else
+                SPD_TRY(potrs_general(n, nrhs, A, lda, B, ldb, L, info, work, s, true, false, false));
         }
         return nan_fill(n, nrhs, B, ldb, info, s);
     }
@@ -1553,15 +1579,19 @@ struct Solver {
 
     // prefix (forward only): block row r of B has non-zero columns [0, r T)
     // only and the rest of it is left alone (see potrs_blocks).
+    // forward = false (the fused solve): only L^H X = B, with the tile
+    // inverses already in the workspace.
     static int potrs_general(int64_t n, int64_t nrhs, const E *A, int64_t lda, E *B, int64_t ldb, const Layout &L,
-                             const int *info, void *work, hipStream_t s, bool backward, bool prefix = false)
+                             const int *info, void *work, hipStream_t s, bool backward, bool prefix = false,
+                             bool forward = true)
     {
         const int64_t T = L.T, nt = L.nt;
         E *Inv = (E *)work + L.inv;
         E *Tmp = (E *)work + L.tmp;  // T x nrhs, ld T
-        SPD_TRY(all_inverses(n, A, lda, T, nt, Inv, (E *)work + L.w, info, s));
+        if (forward)
+            SPD_TRY(all_inverses(n, A, lda, T, nt, Inv, (E *)work + L.w, info, s));
         // forward: L Y = B
-        for (int64_t k = 0; k < nt; ++k) {
+        for (int64_t k = 0; forward && k < nt; ++k) {
             const int64_t c0 = k * T, tk = std::min(T, n - c0), m = n - c0 - tk;
             const int64_t nc = prefix ? std::min(nrhs, c0) : nrhs;  // columns of block row k
             if (nc <= 0)

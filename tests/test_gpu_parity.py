@@ -389,11 +389,14 @@ def posv_check(gpu, dt, n, nrhs, T_A, seed=31, lda_pad=0):
 
 @pytest.mark.parametrize("dt,n,nrhs,T_A,pad", [("f64", 1000, 5, 128, 0), ("f64", 1300, 33, 128, 3),
                                                ("f64", 2048, 16, 256, 0), ("f32", 1024, 4, 128, 0),
-                                               ("c128", 700, 3, 64, 0), ("f64", 300, 2, 100, 0),
+                                               ("c128", 700, 3, 64, 0), ("c128", 1300, 17, 256, 5),
+                                               ("c64", 1000, 5, 128, 3), ("f64", 300, 2, 100, 0),
                                                ("f64", 600, 130, 128, 0)])
 def test_posv_parity(gpu, dt, n, nrhs, T_A, pad):
-    """spd_posv against the oracle: the fused path (real, T_A a multiple of
-    128, three or more tiles) and the fallback to the three calls."""
+    """spd_posv against the oracle: the fused path (T_A a multiple of the
+    trailing-update tile, three or more tiles; block-update substitutions for
+    real types, the general product for complex ones) and the fallback to the
+    three calls."""
     posv_check(gpu, dt, n, nrhs, T_A, lda_pad=pad)
 
 
