@@ -109,7 +109,7 @@ int spd_potrs(spd_dtype_t dt, int64_t n, int64_t n_rhs, const void *dA, int64_t 
  * spd_logdet (when d_logdet is not NULL) and the substitutions of spd_potrs
  * (JAXMg paper, "Software design": potrs factors A and solves, optionally
  * returning log det(A)).  The results are those of the three calls; with the
- * default factorization schedule (real types) the forward substitution runs
+ * default factorization schedule (any dtype) the forward substitution runs
  * on a second auxiliary stream (default priority, non-blocking, created once
  * per host thread and device like the first), one block as soon as its tile
  * of L is final, so that it overlaps the factorization.
