@@ -377,7 +377,7 @@ static GstLayout make_gst_layout(int itype, int64_t n, int64_t T_A, int64_t esiz
 
 // The two-step schedule of potrf (trailing updates of depth 2T) is used unless
 // the environment sets SPD_TWO_STEP=0; it pairs steps while at least
-// two_step_rows(T) rows remain beyond the pair (SPD_TWO_STEP_ROWS, default 40 T:
+// two_step_rows(T) rows remain beyond the pair (SPD_TWO_STEP_ROWS, default 32 T:
 // below that the auxiliary stream's two-tile chain, sharing the GPU with the
 // caller's update, outlasts it).
 static bool two_step_enabled()
@@ -392,7 +392,7 @@ static bool two_step_enabled()
 static int64_t two_step_rows(int64_t T)  // read at every call (tests vary it)
 {
     const char *v = getenv("SPD_TWO_STEP_ROWS");
-    return v != nullptr ? std::max<int64_t>(0, atoll(v)) : 40 * T;
+    return v != nullptr ? std::max<int64_t>(0, atoll(v)) : 32 * T;
 }
 
 // The lookahead schedule is on unless the environment sets SPD_LOOKAHEAD=0

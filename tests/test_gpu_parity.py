@@ -349,7 +349,7 @@ def test_binding_rejects_bad_arguments(gpu):
                                            ("c128", 700, 3, 64), ("f64", 2048, 16, 256)])
 def test_two_step_schedule_parity(gpu, dt, n, nrhs, T_A, monkeypatch):
     """The two-step factorization schedule (pairs of steps share one trailing
-    update of depth 2 T_A) pairs only while 40 T_A rows remain beyond a pair;
+    update of depth 2 T_A) pairs only while 32 T_A rows remain beyond a pair;
     SPD_TWO_STEP_ROWS=0 makes it pair every step at these sizes, with odd and
     even tile counts and a ragged last tile."""
     monkeypatch.setenv("SPD_TWO_STEP_ROWS", "0")
