@@ -50,14 +50,18 @@ def _load():
             i64, vp = ctypes.c_int64, ctypes.c_void_p
             lib.oracle_num_threads.restype = ctypes.c_int
             for suf in ("d", "z"):
+                f = getattr(lib, "oracle_potrf_cols_" + suf)
+                f.argtypes, f.restype = [i64, vp, vp, i64, i64], ctypes.c_int
+            for suf in ("d", "z", "s"):
                 f = getattr(lib, "oracle_potrf_" + suf)
                 f.argtypes, f.restype = [i64, vp, vp], ctypes.c_int
                 f = getattr(lib, "oracle_potrs_" + suf)
                 f.argtypes, f.restype = [i64, i64, vp, vp], None
                 f = getattr(lib, "oracle_logdet_" + suf)
                 f.argtypes, f.restype = [i64, vp], ctypes.c_double
-                f = getattr(lib, "oracle_fwd_" + suf)
-                f.argtypes, f.restype = [i64, i64, vp, vp], None
+                if suf != "s":
+                    f = getattr(lib, "oracle_fwd_" + suf)
+                    f.argtypes, f.restype = [i64, i64, vp, vp], None
             _lib = lib
     return _lib
 
@@ -93,6 +97,52 @@ def potrf(a):
     f = _load().oracle_potrf_z if np.iscomplexobj(a) else _load().oracle_potrf_d
     info = f(n, _p(a), _p(l))
     return l, int(info)
+
+
+class Factorization:
+    """The factorization of :func:`potrf` taken a range of columns at a time
+    (the same arithmetic, so the same bits): ``advance(j1)`` computes columns
+    up to ``j1``, and ``done`` is true once all ``n`` are there or a pivot
+    failed.  For large orders, where one call runs for minutes, this lets a
+    caller report progress between ranges.  ``a`` is read as potrf reads it
+    (lower triangle; real part of the diagonal)."""
+
+    def __init__(self, a):
+        self.a = _wide(a)
+        self.n = self.a.shape[0]
+        if self.a.shape != (self.n, self.n):
+            raise ValueError("a must be square")
+        self.l = np.zeros_like(self.a)
+        self.next = 0
+        self.info = 0
+
+    @property
+    def done(self) -> bool:
+        return self.info != 0 or self.next >= self.n
+
+    def advance(self, j1: int) -> int:
+        j1 = min(int(j1), self.n)
+        if self.done or j1 <= self.next:
+            return self.info
+        f = _load().oracle_potrf_cols_z if np.iscomplexobj(self.a) else _load().oracle_potrf_cols_d
+        self.info = int(f(self.n, _p(self.a), _p(self.l), self.next, j1))
+        self.next = j1
+        return self.info
+
+    @staticmethod
+    def equal_work_bounds(n: int, parts: int):
+        """Column boundaries splitting the factorization of order n into
+        ``parts`` ranges of about equal work (column j costs about (n - j) j
+        multiply-adds)."""
+        total = n**3 / 6.0
+        bounds, j = [], 0
+        for p in range(1, parts):
+            goal = total * p / parts
+            while j < n and (n * j * j / 2.0 - j**3 / 3.0) < goal:
+                j += 1
+            bounds.append(j)
+        bounds.append(n)
+        return bounds
 
 
 def potrs(l, b):
@@ -210,3 +260,48 @@ def solve(a, b, want_logdet: bool = False):
     if want_logdet:
         return x, logdet(l), info
     return x, info
+
+
+# ------------------------------------------------------ single precision ---
+# The same routines with every operation in IEEE single precision, for the CPU
+# baseline of float32 workloads in their own working precision.  Parity is
+# always checked against the double-precision routines above.
+
+def _single(x) -> np.ndarray:
+    x = np.asarray(x)
+    if np.iscomplexobj(x):
+        raise ValueError("the single-precision oracle is real only")
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
+def potrf_single(a):
+    """:func:`potrf` in single precision: returns (L float32, info)."""
+    a = _single(a)
+    n = a.shape[0]
+    if a.shape != (n, n):
+        raise ValueError("a must be square")
+    l = np.zeros_like(a)
+    if n == 0:
+        return l, 0
+    return l, int(_load().oracle_potrf_s(n, _p(a), _p(l)))
+
+
+def potrs_single(l, b):
+    """:func:`potrs` in single precision."""
+    l = _single(l)
+    n = l.shape[0]
+    b = np.asarray(b)
+    vec = b.ndim == 1
+    b2 = b.reshape(n, 1) if vec else b
+    bt = np.array(b2.T, dtype=np.float32, order="C", copy=True)
+    if n > 0 and bt.shape[0] > 0:
+        _load().oracle_potrs_s(n, bt.shape[0], _p(l), _p(bt))
+    x = bt.T.copy()
+    return x.reshape(b.shape) if vec else x
+
+
+def logdet_single(l) -> float:
+    """2 * sum_i log L_ii of a single-precision factor, summed in double."""
+    l = _single(l)
+    n = l.shape[0]
+    return 0.0 if n == 0 else float(_load().oracle_logdet_s(n, _p(l)))

@@ -41,10 +41,12 @@ int oracle_num_threads(void) { return omp_get_max_threads(); }
 
 /* ---------------------------------------------------------------- real --- */
 
-int oracle_potrf_d(int64_t n, const double *a, double *l)
+/* Columns [j0, j1) of L, with the columns before j0 already in l (rows of l
+ * beyond what is computed are zero).  oracle_potrf_d is this over [0, n);
+ * taking the columns in several calls gives the same bits. */
+int oracle_potrf_cols_d(int64_t n, const double *a, double *l, int64_t j0, int64_t j1)
 {
-    memset(l, 0, sizeof(double) * (size_t)(n * n));
-    for (int64_t j = 0; j < n; ++j) {
+    for (int64_t j = j0; j < j1; ++j) {
         const double *lj = l + j * n;
         double d = a[j * n + j];
         for (int64_t k = 0; k < j; ++k)
@@ -63,6 +65,12 @@ int oracle_potrf_d(int64_t n, const double *a, double *l)
         }
     }
     return 0;
+}
+
+int oracle_potrf_d(int64_t n, const double *a, double *l)
+{
+    memset(l, 0, sizeof(double) * (size_t)(n * n));
+    return oracle_potrf_cols_d(n, a, l, 0, n);
 }
 
 /* Forward substitution L y = b (row by row), then back substitution
@@ -116,10 +124,10 @@ double oracle_logdet_d(int64_t n, const double *l)
 
 /* ------------------------------------------------------------- complex --- */
 
-int oracle_potrf_z(int64_t n, const double complex *a, double complex *l)
+/* Columns [j0, j1) of L, as oracle_potrf_cols_d. */
+int oracle_potrf_cols_z(int64_t n, const double complex *a, double complex *l, int64_t j0, int64_t j1)
 {
-    memset(l, 0, sizeof(double complex) * (size_t)(n * n));
-    for (int64_t j = 0; j < n; ++j) {
+    for (int64_t j = j0; j < j1; ++j) {
         const double complex *lj = l + j * n;
         double d = creal(a[j * n + j]);
         for (int64_t k = 0; k < j; ++k)
@@ -139,6 +147,12 @@ int oracle_potrf_z(int64_t n, const double complex *a, double complex *l)
         }
     }
     return 0;
+}
+
+int oracle_potrf_z(int64_t n, const double complex *a, double complex *l)
+{
+    memset(l, 0, sizeof(double complex) * (size_t)(n * n));
+    return oracle_potrf_cols_z(n, a, l, 0, n);
 }
 
 /* L y = b, then L^H x = y; b is overwritten by x. */
@@ -188,5 +202,66 @@ double oracle_logdet_z(int64_t n, const double complex *l)
     double s = 0.0;
     for (int64_t i = 0; i < n; ++i)
         s += log(creal(l[i * n + i]));
+    return 2.0 * s;
+}
+
+/* ------------------------------------------------------ single (float) --- */
+/* The same three routines with every product and sum in IEEE single
+ * precision (the working precision of a float32 solve); log det is summed in
+ * double from the single-precision diagonal.  They time the CPU baseline of
+ * float32 workloads in their own precision; parity is always checked against
+ * the double-precision routines above. */
+
+int oracle_potrf_s(int64_t n, const float *a, float *l)
+{
+    memset(l, 0, sizeof(float) * (size_t)(n * n));
+    for (int64_t j = 0; j < n; ++j) {
+        const float *lj = l + j * n;
+        float d = a[j * n + j];
+        for (int64_t k = 0; k < j; ++k)
+            d -= lj[k] * lj[k];
+        if (!(d > 0.0f))
+            return (int)(j + 1);
+        const float ljj = sqrtf(d);
+        l[j * n + j] = ljj;
+#pragma omp parallel for schedule(static)
+        for (int64_t i = j + 1; i < n; ++i) {
+            const float *li = l + i * n;
+            float s = a[i * n + j];
+            for (int64_t k = 0; k < j; ++k)
+                s -= li[k] * lj[k];
+            l[i * n + j] = s / ljj;
+        }
+    }
+    return 0;
+}
+
+void oracle_potrs_s(int64_t n, int64_t nrhs, const float *l, float *b)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t c = 0; c < nrhs; ++c) {
+        float *y = b + c * n;
+        for (int64_t i = 0; i < n; ++i) {
+            const float *li = l + i * n;
+            float s = y[i];
+            for (int64_t k = 0; k < i; ++k)
+                s -= li[k] * y[k];
+            y[i] = s / li[i];
+        }
+        for (int64_t i = n - 1; i >= 0; --i) {
+            const float *li = l + i * n;
+            const float xi = y[i] / li[i];
+            y[i] = xi;
+            for (int64_t k = 0; k < i; ++k)
+                y[k] -= li[k] * xi;
+        }
+    }
+}
+
+double oracle_logdet_s(int64_t n, const float *l)
+{
+    double s = 0.0;
+    for (int64_t i = 0; i < n; ++i)
+        s += log((double)l[i * n + i]);
     return 2.0 * s;
 }

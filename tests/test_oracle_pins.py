@@ -543,3 +543,107 @@ def test_sygst_exact_integer_brute_force(itype):
     assert all(v.denominator == 1 and abs(v) < 2**50 for row in ref for v in row)
     C = oracle.sygst(itype, A.astype(np.float64), L)
     np.testing.assert_array_equal(C, np.array([[float(v) for v in row] for row in ref]))
+
+
+# ------------------------------------------- factorization by column ranges ---
+
+@pytest.mark.parametrize("cplx", [False, True])
+def test_factorization_by_ranges_recovers_integer_factor(cplx):
+    """Taken a range of columns at a time, the factorization still recovers
+    a hand-built integer factor bit for bit, and equals potrf's bits on a
+    random input for any split."""
+    rng = np.random.default_rng(11)
+    L = int_lower(30, rng, cplx)
+    f = oracle.Factorization(exact_gram(L))
+    for j1 in (1, 7, 8, 29, 30):
+        assert f.advance(j1) == 0
+    assert f.done
+    np.testing.assert_array_equal(f.l, L.astype(f.l.dtype))
+    A = random_spd(257, 12, cplx)
+    Lo, _ = oracle.potrf(A)
+    for parts in (1, 3, 8):
+        g = oracle.Factorization(A)
+        for j1 in oracle.Factorization.equal_work_bounds(257, parts):
+            g.advance(j1)
+        assert g.done and g.info == 0
+        np.testing.assert_array_equal(g.l, Lo)
+
+
+def test_factorization_by_ranges_stops_at_the_failing_pivot():
+    """A non-positive leading minor inside the second range stops the
+    factorization there with the 1-based column, as potrf does."""
+    rng = np.random.default_rng(13)
+    L = int_lower(20, rng)
+    A = exact_gram(L)
+    A[12, 12] = -1.0
+    f = oracle.Factorization(A)
+    assert f.advance(10) == 0 and not f.done
+    assert f.advance(20) == 13 and f.done
+    assert oracle.potrf(A)[1] == 13
+
+
+def test_equal_work_bounds():
+    """Boundaries are increasing, end at n, and split the n^3/6 multiply-adds
+    into parts within one column's work of each other."""
+    n, parts = 4096, 8
+    b = oracle.Factorization.equal_work_bounds(n, parts)
+    assert len(b) == parts and b[-1] == n and all(x < y for x, y in zip(b, b[1:]))
+    work = lambda j: n * j * j / 2.0 - j**3 / 3.0  # noqa: E731
+    edges = [0] + b
+    shares = [work(y) - work(x) for x, y in zip(edges, edges[1:])]
+    assert max(shares) - min(shares) <= 2 * n * n / 4
+
+
+# ------------------------------------------------------ single precision ---
+
+EPS32 = float(np.finfo(np.float32).eps)
+
+
+@pytest.mark.parametrize("n,seed", [(1, 0), (8, 2), (17, 3)])
+def test_single_recovers_integer_factor_exactly(n, seed):
+    """Single precision: every partial sum of the integer Gram matrix stays
+    below 2^24 and every sqrt is of a perfect square, so L comes back bit for
+    bit."""
+    L = int_lower(n, np.random.default_rng(seed))
+    A = exact_gram(L)
+    assert np.abs(A).max() < 2**24
+    Lo, info = oracle.potrf_single(A)
+    assert info == 0 and Lo.dtype == np.float32
+    np.testing.assert_array_equal(Lo, L.astype(np.float32))
+
+
+def test_single_pascal_and_closed_forms():
+    n = 12  # the largest Pascal entry C(22, 11) < 2^24
+    P = np.array([[math.comb(i + j, i) for j in range(n)] for i in range(n)], dtype=np.float32)
+    Lx = np.array([[math.comb(i, j) for j in range(n)] for i in range(n)], dtype=np.float32)
+    Lo, info = oracle.potrf_single(P)
+    assert info == 0
+    np.testing.assert_array_equal(Lo, Lx)
+    assert oracle.logdet_single(Lo) == 0.0
+    L1, info = oracle.potrf_single(np.array([[16.0]], dtype=np.float32))
+    assert info == 0 and L1[0, 0] == 4.0
+    assert oracle.potrs_single(L1, np.array([[8.0]], dtype=np.float32))[0, 0] == 0.5
+    A = np.eye(5, dtype=np.float32)
+    A[3, 3] = -2.0
+    assert oracle.potrf_single(A)[1] == 4
+
+
+@pytest.mark.parametrize("n,seed", [(64, 0), (500, 1)])
+def test_single_vs_lapack_spotrf(n, seed):
+    """Single-precision LAPACK (SciPy's cholesky / cho_solve on float32
+    input: spotrf / spotrs) agrees within single-precision rounding, and the
+    normwise backward error of x stays inside 64 n eps(float32)."""
+    A = random_spd(n, seed, False, delta=0.5).astype(np.float32)
+    b = np.random.default_rng(seed + 3).standard_normal((n, 3)).astype(np.float32)
+    L, info = oracle.potrf_single(A)
+    assert info == 0 and L.dtype == np.float32
+    Lref = scipy.linalg.cholesky(A, lower=True)
+    assert Lref.dtype == np.float32
+    assert np.abs(L - Lref).max() <= 64 * n * EPS32 * np.abs(Lref).max()
+    x = oracle.potrs_single(L, b)
+    xref = scipy.linalg.cho_solve((Lref, True), b)
+    assert np.linalg.norm(x - xref) <= 1e-3 * np.linalg.norm(xref)
+    eta = rigal_gaches(A.astype(np.float64), x.astype(np.float64), b.astype(np.float64))
+    assert eta.max() <= 64 * n * EPS32
+    _, ld = np.linalg.slogdet(A.astype(np.float64))
+    assert abs(oracle.logdet_single(L) - ld) <= 1e-3 * max(1.0, abs(ld))
