@@ -34,9 +34,12 @@ DTYPE_CODE = {
 SYMBOLS = ("spd_workspace_size", "spd_potrf", "spd_potrs", "spd_posv", "spd_forward_solve", "spd_gp_loglik",
            "spd_logdet",
            "spd_sygst_workspace_size", "spd_sygst", "spd_last_error", "spd_profile_enable", "spd_profile_read",
-           "spd_debug_validate")
+           "spd_debug_validate", "spd_set_option", "spd_get_option", "spd_release")
 SPD_ERR_HIP, SPD_ERR_CHECK = 1, 2
 PROF_SYRK, PROF_PANEL, PROF_DIAG, PROF_SOLVE, PROF_UPDATE, PROF_SYRK_AUX = 0, 1, 2, 3, 4, 5
+# schedule / tile-shape options (spd_set_option)
+OPT_LOOKAHEAD, OPT_TWO_STEP, OPT_PAIR_ROWS, OPT_SYRK_DEEP_ROWS, OPT_RECT_TALL_ROWS = 1, 2, 3, 4, 5
+OPT_DEFAULT = -(1 << 63)
 
 _lock = threading.Lock()
 _lib = None
@@ -94,6 +97,12 @@ def load():
             lib.spd_profile_read.restype = i32
             lib.spd_debug_validate.argtypes = [i32]
             lib.spd_debug_validate.restype = i32
+            lib.spd_set_option.argtypes = [i32, i64]
+            lib.spd_set_option.restype = i32
+            lib.spd_get_option.argtypes = [i32]
+            lib.spd_get_option.restype = i64
+            lib.spd_release.argtypes = []
+            lib.spd_release.restype = i32
             _lib = lib
     return _lib
 
@@ -307,6 +316,42 @@ def debug_validate(mode: int) -> None:
     """Launch validation: 0 off, 1 replay every launch's addresses on the host
     before enqueueing it, 2 replay only (dry run, no GPU work)."""
     _check(load().spd_debug_validate(int(mode)), "spd_debug_validate")
+
+
+def set_option(opt: int, value: int) -> None:
+    """Set a schedule / tile-shape option (OPT_*; OPT_DEFAULT restores the
+    default).  Options select among schedules and tile shapes that compute
+    the same result; they are process-wide."""
+    _check(load().spd_set_option(int(opt), int(value)), "spd_set_option")
+
+
+def get_option(opt: int) -> int:
+    return int(load().spd_get_option(int(opt)))
+
+
+class options:
+    """Context manager: set options for a block, restore the previous values
+    after it, e.g. ``with options({OPT_PAIR_ROWS: 0}): ...``."""
+
+    def __init__(self, values: dict):
+        self.values = dict(values)
+        self.saved = {}
+
+    def __enter__(self):
+        for k, v in self.values.items():
+            self.saved[k] = get_option(k)
+            set_option(k, v)
+        return self
+
+    def __exit__(self, *exc):
+        for k, v in self.saved.items():
+            set_option(k, v)
+        return False
+
+
+def release() -> None:
+    """Wait for and destroy this thread's auxiliary streams and events."""
+    _check(load().spd_release(), "spd_release")
 
 
 def profile_enable(mask: int) -> None:

@@ -20,6 +20,7 @@
 
 #include <algorithm>
 #include <cstdlib>
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -375,46 +376,92 @@ static GstLayout make_gst_layout(int itype, int64_t n, int64_t T_A, int64_t esiz
     return G;
 }
 
+// Schedule and tile-shape options (spd_set_option).  They are process-wide
+// atomics; every entry point copies them into g_opt when it is called, so one
+// call sees one consistent set whatever other threads change meanwhile.  They
+// select among schedules and tile shapes that compute the same factorization
+// and solve; results agree with each other within rounding.
+enum { OPT_LOOKAHEAD, OPT_TWO_STEP, OPT_PAIR_ROWS, OPT_SYRK_DEEP_ROWS, OPT_RECT_TALL_ROWS, OPT_COUNT };
+static const int64_t k_opt_default[OPT_COUNT] = {1, 1, -1, -1, 16384};
+static std::atomic<int64_t> g_opt_store[OPT_COUNT] = {{1}, {1}, {-1}, {-1}, {16384}};
+struct Options {
+    int64_t v[OPT_COUNT];
+};
+static thread_local Options g_opt = {{1, 1, -1, -1, 16384}};
+
+static void snapshot_options()
+{
+    for (int i = 0; i < OPT_COUNT; ++i)
+        g_opt.v[i] = g_opt_store[i].load(std::memory_order_relaxed);
+}
+
 // The two-step schedule of potrf (trailing updates of depth 2T) is used unless
-// the environment sets SPD_TWO_STEP=0; it pairs steps while at least
-// two_step_rows(T) rows remain beyond the pair (SPD_TWO_STEP_ROWS, default 32 T:
-// below that the auxiliary stream's two-tile chain, sharing the GPU with the
-// caller's update, outlasts it).
-static bool two_step_enabled()
+// SPD_OPT_TWO_STEP is 0; it pairs steps while at least two_step_rows(T) rows
+// remain beyond the pair (SPD_OPT_PAIR_ROWS; by default 32 T: below that the
+// auxiliary stream's two-tile chain, sharing the GPU with the caller's update,
+// outlasts it).
+static bool two_step_enabled() { return g_opt.v[OPT_TWO_STEP] != 0; }
+
+static int64_t two_step_rows(int64_t T)
 {
-    static const bool on = [] {
-        const char *v = getenv("SPD_TWO_STEP");
-        return !(v != nullptr && v[0] == '0');
-    }();
-    return on;
+    const int64_t v = g_opt.v[OPT_PAIR_ROWS];
+    return v >= 0 ? v : 32 * T;
 }
 
-static int64_t two_step_rows(int64_t T)  // read at every call (tests vary it)
+// The lookahead schedule is on unless SPD_OPT_LOOKAHEAD is 0 (the sequential
+// schedule does the same work without overlap; it is there to measure each
+// kernel on its own).
+static bool lookahead_enabled() { return g_opt.v[OPT_LOOKAHEAD] != 0; }
+
+// Trailing-update orders from which 128-row tiles take the deeper slices
+// (fp64: 16 instead of 8; fp32: 32 instead of 16).
+static int64_t syrk_deep_rows(int64_t esize)
 {
-    const char *v = getenv("SPD_TWO_STEP_ROWS");
-    return v != nullptr ? std::max<int64_t>(0, atoll(v)) : 32 * T;
+    const int64_t v = g_opt.v[OPT_SYRK_DEEP_ROWS];
+    return v >= 0 ? v : (esize == 8 ? 24576 : 12288);
 }
 
-// The lookahead schedule is on unless the environment sets SPD_LOOKAHEAD=0
-// (the sequential schedule does the same work without overlap; it is there
-// to measure each kernel on its own).
-static bool lookahead_enabled()
-{
-    static const bool on = [] {
-        const char *v = getenv("SPD_LOOKAHEAD");
-        return !(v != nullptr && v[0] == '0');
-    }();
-    return on;
-}
+// Block-update heights from which the substitutions (and the factorization's
+// panel product) take 64-row tiles.
+static int64_t rect_tall_rows() { return g_opt.v[OPT_RECT_TALL_ROWS]; }
 
-// The auxiliary stream and events of the lookahead schedule: one set per
-// host thread and device, created on first use and kept until the process
-// ends.  Default priority, non-blocking with respect to the null stream.  In a
-// dry run (no HIP calls) both schedules run on the caller's stream.
+// The auxiliary streams and events of the lookahead schedules: one set per
+// host thread and device, created on first use and kept until spd_release is
+// called on that thread (or the process ends).  Default priority, non-blocking
+// with respect to the null stream.  In a dry run (no HIP calls) every schedule
+// runs on the caller's stream.
 struct AuxStreams {
     hipStream_t look = nullptr, look2 = nullptr;
     hipEvent_t ev_fork = nullptr, ev_panel = nullptr, ev_rest = nullptr, ev_fw = nullptr;
 };
+static thread_local std::vector<std::pair<int, AuxStreams>> g_aux;
+
+// Wait for and destroy the calling thread's auxiliary streams and events.
+static int release_aux()
+{
+    int rc = 0;
+    for (auto &pd : g_aux) {
+        AuxStreams &x = pd.second;
+        for (hipStream_t st : {x.look, x.look2}) {
+            if (st == nullptr)
+                continue;
+            hipError_t e = hipStreamSynchronize(st);
+            if (e == hipSuccess)
+                e = hipStreamDestroy(st);
+            if (e != hipSuccess && rc == 0)
+                rc = hip_fail(e, "spd_release");
+        }
+        for (hipEvent_t ev : {x.ev_fork, x.ev_panel, x.ev_rest, x.ev_fw}) {
+            if (ev == nullptr)
+                continue;
+            hipError_t e = hipEventDestroy(ev);
+            if (e != hipSuccess && rc == 0)
+                rc = hip_fail(e, "spd_release");
+        }
+    }
+    g_aux.clear();
+    return rc;
+}
 
 struct Lookahead {
     hipStream_t look = nullptr, look2 = nullptr;  // look2: the fused solve's forward substitution
@@ -426,25 +473,36 @@ struct Lookahead {
             look = look2 = s;
             return 0;
         }
-        static thread_local std::vector<std::pair<int, AuxStreams>> per_device;
         int dev = 0;
         hipError_t e = hipGetDevice(&dev);
         if (e != hipSuccess)
             return hip_fail(e, "hipGetDevice");
         AuxStreams *x = nullptr;
-        for (auto &pd : per_device)
+        for (auto &pd : g_aux)
             if (pd.first == dev)
                 x = &pd.second;
         if (x == nullptr) {
             AuxStreams n;
+            auto undo = [&n] {
+                for (hipStream_t st : {n.look, n.look2})
+                    if (st != nullptr)
+                        (void)hipStreamDestroy(st);
+                for (hipEvent_t ev : {n.ev_fork, n.ev_panel, n.ev_rest, n.ev_fw})
+                    if (ev != nullptr)
+                        (void)hipEventDestroy(ev);
+            };
             if ((e = hipStreamCreateWithFlags(&n.look, hipStreamNonBlocking)) != hipSuccess ||
-                (e = hipStreamCreateWithFlags(&n.look2, hipStreamNonBlocking)) != hipSuccess)
+                (e = hipStreamCreateWithFlags(&n.look2, hipStreamNonBlocking)) != hipSuccess) {
+                undo();
                 return hip_fail(e, "hipStreamCreateWithFlags");
+            }
             for (hipEvent_t *ev : {&n.ev_fork, &n.ev_panel, &n.ev_rest, &n.ev_fw})
-                if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess)
+                if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess) {
+                    undo();
                     return hip_fail(e, "hipEventCreateWithFlags");
-            per_device.emplace_back(dev, n);
-            x = &per_device.back().second;
+                }
+            g_aux.emplace_back(dev, n);
+            x = &g_aux.back().second;
         }
         look = x->look;
         look2 = x->look2;
@@ -733,13 +791,13 @@ struct Solver {
             if constexpr (sizeof(R) == 4) {
                 // fp32: 32-deep slices for large orders (72 % of the fp32 peak
                 // against 61 % at m = 15872), 16-deep below
-                if (m >= 12288)
+                if (m >= syrk_deep_rows(4))
                     return syrk_cfg<128, 32, 2, 4>(m, W, ldw, kp, C, ldc, jt(128), info, s, x);
                 return syrk_cfg<128, 16, 2, 4>(m, W, ldw, kp, C, ldc, jt(128), info, s, x);
             } else {
                 // slice depth: 16 for the large early steps, 8 below (more
                 // workgroups in flight per byte of LDS; measured better for m < ~24k)
-                if (m >= 24576)
+                if (m >= syrk_deep_rows(8))
                     return syrk_cfg<128, 16, 2, 4>(m, W, ldw, kp, C, ldc, jt(128), info, s, x);
                 return syrk_cfg<128, 8, 2, 4>(m, W, ldw, kp, C, ldc, jt(128), info, s, x);
             }
@@ -818,7 +876,7 @@ struct Solver {
             // workgroup's 512-deep product is a fixed latency, so more, smaller
             // tiles finish sooner)
             constexpr int KBL = sizeof(R) == 8 ? 16 : 32;  // slice depth of the 64-row tiles
-            if (m >= 16384)
+            if (m >= rect_tall_rows())
                 return vec ? rect_cfg<64, 64, KBL, 2, 2, PT, true>(P, ldp, Q, ldq, C, ldc, m, n, kp, kvalid, info, s)
                            : rect_cfg<64, 64, KBL, 2, 2, PT, false>(P, ldp, Q, ldq, C, ldc, m, n, kp, kvalid, info, s);
             if (n > 64)
@@ -909,7 +967,7 @@ struct Solver {
                 // product, which matters in the late steps where this product is
                 // on the critical path
                 const bool vec = rect_vec(A, lda, T);
-                if (m >= 16384)
+                if (m >= rect_tall_rows())
                     SPD_TRY((vec ? rect_cfg<64, 128, (sizeof(R) == 8 ? 16 : 32), 2, 4, false, true, true>(
                                        P, lda, Inv, T, Wk, ldw, m, tk, tk, tk, info, s)
                                  : rect_cfg<64, 128, (sizeof(R) == 8 ? 16 : 32), 2, 4, false, false, true>(
@@ -1949,6 +2007,7 @@ int spd_potrf(spd_dtype_t dt, int64_t n, void *dA, int64_t lda, int64_t T_A, int
         g_chk.add(d_info, 4, true, "info");
         g_chk.add(d_work, work_bytes, true, "workspace");
     }
+    snapshot_options();
     hipStream_t s = (hipStream_t)stream;
     switch (dt) {
     case SPD_R32: return Solver<float, false>::potrf(n, (float *)dA, lda, T_A, d_info, d_work, s);
@@ -1982,6 +2041,7 @@ int spd_potrs(spd_dtype_t dt, int64_t n, int64_t n_rhs, const void *dA, int64_t 
         g_chk.add(d_info, 4, false, "info");
         g_chk.add(d_work, work_bytes, true, "workspace");
     }
+    snapshot_options();
     hipStream_t s = (hipStream_t)stream;
     switch (dt) {
     case SPD_R32:
@@ -2020,6 +2080,7 @@ int spd_forward_solve(spd_dtype_t dt, int64_t n, int64_t n_rhs, const void *dA, 
         g_chk.add(d_info, 4, false, "info");
         g_chk.add(d_work, work_bytes, true, "workspace");
     }
+    snapshot_options();
     hipStream_t s = (hipStream_t)stream;
     switch (dt) {
     case SPD_R32:
@@ -2061,6 +2122,7 @@ int spd_gp_loglik(spd_dtype_t dt, int64_t n, int64_t n_rhs, const void *dA, int6
         g_chk.add(d_out, (size_t)n_rhs * sizeof(double), true, "out");
         g_chk.add(d_work, work_bytes, true, "workspace");
     }
+    snapshot_options();
     hipStream_t s = (hipStream_t)stream;
     if (dt == SPD_R32)
         return Solver<float, false>::gp_loglik(n, n_rhs, (const float *)dA, lda, (float *)dR, ldr, T_A, d_info, d_out,
@@ -2098,6 +2160,7 @@ int spd_sygst(spd_dtype_t dt, int itype, int64_t n, void *dA, int64_t lda, const
         g_chk.add(d_info, 4, false, "info");
         g_chk.add(d_work, work_bytes, true, "workspace");
     }
+    snapshot_options();
     hipStream_t s = (hipStream_t)stream;
     switch (dt) {
     case SPD_R32:
@@ -2139,6 +2202,7 @@ int spd_posv(spd_dtype_t dt, int64_t n, int64_t n_rhs, void *dA, int64_t lda, vo
             g_chk.add(d_logdet, sizeof(double), true, "logdet");
         g_chk.add(d_work, work_bytes, true, "workspace");
     }
+    snapshot_options();
     hipStream_t s = (hipStream_t)stream;
     switch (dt) {
     case SPD_R32:
@@ -2171,6 +2235,7 @@ int spd_logdet(spd_dtype_t dt, int64_t n, const void *dA, int64_t lda, const int
         g_chk.add(d_info, 4, false, "info");
         g_chk.add(d_logdet, sizeof(double), true, "logdet");
     }
+    snapshot_options();
     hipStream_t s = (hipStream_t)stream;
     switch (dt) {
     case SPD_R32: return Solver<float, false>::logdet(n, (const float *)dA, lda, d_info, d_logdet, s);
@@ -2184,6 +2249,43 @@ int spd_logdet(spd_dtype_t dt, int64_t n, const void *dA, int64_t lda, const int
 }
 
 const char *spd_last_error(void) { return g_last_error.c_str(); }
+
+int spd_set_option(spd_option_t opt, int64_t value)
+{
+    const int i = (int)opt - 1;
+    if (i < 0 || i >= OPT_COUNT)
+        return -1;
+    if (value == SPD_OPT_DEFAULT)
+        value = k_opt_default[i];
+    switch (i) {
+    case OPT_LOOKAHEAD:
+    case OPT_TWO_STEP:
+        if (value != 0 && value != 1)
+            return -2;
+        break;
+    case OPT_PAIR_ROWS:
+    case OPT_SYRK_DEEP_ROWS:
+        if (value < -1)
+            return -2;
+        break;
+    default:
+        if (value < 0)
+            return -2;
+        break;
+    }
+    g_opt_store[i].store(value, std::memory_order_relaxed);
+    return 0;
+}
+
+int64_t spd_get_option(spd_option_t opt)
+{
+    const int i = (int)opt - 1;
+    if (i < 0 || i >= OPT_COUNT)
+        return INT64_MIN;
+    return g_opt_store[i].load(std::memory_order_relaxed);
+}
+
+int spd_release(void) { return release_aux(); }
 
 int spd_debug_validate(int mode)
 {

@@ -25,10 +25,11 @@
  *     A with L (real positive diagonal); potrs overwrites B with X.
  *   - All pointers named d_* or dA/dB are device pointers owned by the caller.
  *     The library allocates no device memory.  Its only state between calls is
- *     what spd_profile_* keeps while profiling is on and, for the lookahead
- *     schedules, two auxiliary HIP streams (default priority, non-blocking)
- *     and five events per host thread and device, created on first use and
- *     kept until the process ends.  Calls from one host thread must not
+ *     the options of spd_set_option, what spd_profile_* keeps while profiling
+ *     is on and, for the lookahead schedules, two auxiliary HIP streams
+ *     (default priority, non-blocking) and four events per host thread and
+ *     device, created on first use and kept until spd_release is called on
+ *     that thread (or the process ends).  Calls from one host thread must not
  *     overlap on one device (they share those streams).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *     the calls return without waiting for it.  spd_potrf may also run part of
@@ -203,6 +204,52 @@ int spd_logdet(spd_dtype_t dt, int64_t n, const void *dA, int64_t lda,
 /* Text of the last error (HIP or launch validation) seen by this library in
  * the calling thread. */
 const char *spd_last_error(void);
+
+/* Schedule and tile-shape options.  None of them changes what is computed:
+ * every setting gives the same factorization, log-determinant and solution
+ * within rounding (the bits may differ between settings, and are the same
+ * from run to run for one setting).  They exist to measure the schedules
+ * against each other and to let tests reach every kernel variant at sizes a
+ * plain CPU reference can check.  Options are process-wide; each entry point
+ * reads all of them once when it is called, so a call sees one consistent set.
+ *   SPD_OPT_LOOKAHEAD        1 (default): the factorization and the
+ *                            substitutions run one step ahead on an auxiliary
+ *                            stream; 0: everything in order on `stream`
+ *   SPD_OPT_TWO_STEP         1 (default): under lookahead, pairs of steps share
+ *                            one trailing update of depth 2 T_A while the
+ *                            trailing matrix is large; 0: one step at a time
+ *                            (spd_posv then runs its three parts in sequence)
+ *   SPD_OPT_PAIR_ROWS        steps are paired while at least this many rows
+ *                            remain beyond the pair; -1 (default): 32 T_A
+ *   SPD_OPT_SYRK_DEEP_ROWS   trailing updates of at least this order on
+ *                            128-row tiles take the deeper operand slices;
+ *                            -1 (default): 24576 (fp64), 12288 (fp32)
+ *   SPD_OPT_RECT_TALL_ROWS   block updates of the substitutions and the
+ *                            panel products of at least this many rows take
+ *                            64-row tiles, fewer rows 32-row tiles (default
+ *                            16384)
+ * spd_set_option returns 0, -1 for an unknown option, -2 for a value out of
+ * range (LOOKAHEAD and TWO_STEP take 0 or 1, PAIR_ROWS and SYRK_DEEP_ROWS
+ * >= -1, RECT_TALL_ROWS >= 0); SPD_OPT_DEFAULT restores an option's default.
+ * spd_get_option returns the current value (INT64_MIN for an unknown
+ * option). */
+typedef enum {
+    SPD_OPT_LOOKAHEAD = 1,
+    SPD_OPT_TWO_STEP = 2,
+    SPD_OPT_PAIR_ROWS = 3,
+    SPD_OPT_SYRK_DEEP_ROWS = 4,
+    SPD_OPT_RECT_TALL_ROWS = 5
+} spd_option_t;
+#define SPD_OPT_DEFAULT INT64_MIN
+int spd_set_option(spd_option_t opt, int64_t value);
+int64_t spd_get_option(spd_option_t opt);
+
+/* Wait for the work on the calling thread's auxiliary streams (on every
+ * device it used) to finish, then destroy those streams and their events.
+ * The next call that needs them creates them again.  Returns 0, or
+ * SPD_ERR_HIP (spd_last_error() says which call failed; the thread's set is
+ * forgotten either way). */
+int spd_release(void);
 
 /* Launch validation, a debugging aid for callers and tests.
  *   mode 0  off (default)

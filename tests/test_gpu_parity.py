@@ -1,13 +1,11 @@
 """GPU parity: the HIP library (through its C ABI) against the CPU oracle.
 
-Small and medium sizes are compared element by element with the oracle run on
-the very same input bytes.  The three large workloads (fp32 N=16384,
-complex128 N=8192, fp64 N=32768) are too big for the unblocked oracle, so there
-the oracle computes sampled outputs (the leading 2*T_A columns of L and the
-same columns of sampled rows, which depend only on the leading principal
-block plus those rows) and the rest is checked through properties that hold
-at any size: the normwise backward error of X, the factorization residual at
-sampled entries, and log det recomputed from the factor's diagonal.
+Small and medium sizes, with ragged tiles in all four dtypes, and the two
+small benchmark workloads are compared element by element with the oracle run
+on the very same input bytes; so are the invariants (bitwise determinism,
+power-of-two scaling, untouched upper triangle and padding, info on failed
+pivots).  The three large workloads are in test_gpu_workloads.py, every kernel
+variant they use at oracle-sized orders in test_gpu_variants.py.
 """
 from __future__ import annotations
 
@@ -19,7 +17,7 @@ import torch
 
 import oracle
 import spdgen
-from helpers import (EPS, L_TOL, LOGDET_TOL, TORCH, X_TOL, backward_error, logdet_rel, rel_err_cols, wide)
+from helpers import EPS, L_TOL, LOGDET_TOL, X_TOL, backward_error, logdet_rel, rel_err_cols, wide
 
 pytestmark = pytest.mark.gpu
 
@@ -103,86 +101,6 @@ def test_config2_full(gpu):
     """fp64 N=4096, N_RHS=16, T_A=256, delta=0.1: element-by-element."""
     A, B, c = spdgen.make_config(2, 0, device="cuda")
     check_against_oracle(gpu, c["dtype"], c["n"], c["nrhs"], c["T_A"], A=A, B=B)
-
-
-# ----------------------------------------------------- large workloads ---
-
-def sampled_parity(spd, k: int, seed: int = 0):
-    A, B, c = spdgen.make_config(k, seed, device="cuda")
-    dt, n, nrhs, T = c["dtype"], c["n"], c["nrhs"], c["T_A"]
-    L = cm_copy(A)
-    X = cm_copy(B)
-    info, ld = gpu_solve(spd, L, X, T, want_logdet=True)
-    assert info == 0
-
-    # (1) sampled outputs the oracle computes exactly: columns [0, K) of L on
-    # the rows [0, K) and on sampled rows R.  Cholesky of the principal block
-    # on S = [0, K) + R has these entries (its first K columns only involve
-    # A[S, :K] and earlier columns).
-    K = min(n, 2 * T)
-    rng = np.random.default_rng(1000 + k)
-    tail = np.arange(max(K, n - 5), n)
-    R = np.unique(np.concatenate([rng.choice(np.arange(K, n), 96, replace=False), tail]))
-    S = np.concatenate([np.arange(K), R])
-    St = torch.from_numpy(S).cuda()
-    A_sub = wide(A[St][:, St])
-    Lo, info_o = oracle.potrf(A_sub)
-    assert info_o == 0
-    Lg_sub = wide(L[St][:, :K])
-    Lg_sub = np.where(np.arange(len(S))[:, None] >= np.arange(K)[None, :], Lg_sub, 0)
-    err_L = np.abs(Lg_sub - Lo[:, :K]).max() / np.abs(Lo[:, :K]).max()
-    assert err_L <= L_TOL[dt], err_L
-    d = wide(torch.diagonal(L)).real
-    pre = 2.0 * np.sum(np.log(d[:K]))
-    pre_o = oracle.logdet(Lo[:K, :K])
-    tol_ld = LOGDET_TOL if dt in ("f64", "c128") else 1e-4
-    assert logdet_rel(pre, pre_o) <= tol_ld
-
-    # (2) log det: the device reduction against the factor's own diagonal
-    full = 2.0 * math.fsum(np.log(d))
-    assert logdet_rel(ld, full) <= 1e-13
-
-    # (3) normwise backward error of X (residual in double on the GPU)
-    eta = backward_error(A, X, B)
-    assert eta <= 64 * n * EPS[dt], eta
-
-    # (4) factorization residual at sampled entries (i >= j):
-    #     |A_ij - sum_k L_ik conj(L_jk)| <= 64 n eps sum_k |L_ik||L_jk|
-    ii = rng.integers(0, n, 200)
-    jj = (rng.random(200) * (ii + 1)).astype(np.int64)
-    Lr_i = wide(L[torch.from_numpy(ii).cuda()])
-    Lr_j = wide(L[torch.from_numpy(jj).cuda()])
-    Aw = wide(A[torch.from_numpy(ii).cuda(), torch.from_numpy(jj).cuda()])
-    worst = 0.0
-    for t in range(len(ii)):
-        i, j = ii[t], jj[t]
-        li, lj = Lr_i[t, : j + 1], Lr_j[t, : j + 1]
-        r = abs(Aw[t] - np.sum(li * np.conj(lj)))
-        bound = 64 * n * EPS[dt] * np.sum(np.abs(li) * np.abs(lj))
-        worst = max(worst, r / bound)
-    assert worst <= 1.0, worst
-
-    # (5) independent library cross-check (torch / rocSOLVER Cholesky)
-    Ld = torch.linalg.cholesky(A)
-    Xr = torch.cholesky_solve(B, Ld)
-    err_x = rel_err_cols(X, Xr)
-    assert err_x <= X_TOL[dt], err_x
-    ldr = 2.0 * float(torch.log(torch.diagonal(Ld).real.double()).sum().item())
-    assert logdet_rel(ld, ldr) <= tol_ld
-    print(f"config {k}: L[:, :{K}] {err_L:.2e} eta {eta:.2e} residual/bound {worst:.2e} "
-          f"x vs library {err_x:.2e} logdet {ld:.10g}")
-
-
-def test_config3_sampled(gpu):
-    sampled_parity(gpu, 3)
-
-
-def test_config4_sampled(gpu):
-    sampled_parity(gpu, 4)
-
-
-def test_config5_sampled(gpu):
-    sampled_parity(gpu, 5)
 
 
 # ------------------------------------------------------- invariants -------
@@ -347,12 +265,16 @@ def test_binding_rejects_bad_arguments(gpu):
 
 @pytest.mark.parametrize("dt,n,nrhs,T_A", [("f64", 1000, 5, 128), ("f64", 1300, 3, 128), ("f32", 1024, 4, 128),
                                            ("c128", 700, 3, 64), ("f64", 2048, 16, 256)])
-def test_two_step_schedule_parity(gpu, dt, n, nrhs, T_A, monkeypatch):
+def test_two_step_schedule_parity(gpu, dt, n, nrhs, T_A):
     """The two-step factorization schedule (pairs of steps share one trailing
     update of depth 2 T_A) pairs only while 32 T_A rows remain beyond a pair;
-    SPD_TWO_STEP_ROWS=0 makes it pair every step at these sizes, with odd and
+    SPD_OPT_PAIR_ROWS = 0 makes it pair every step at these sizes, with odd and
     even tile counts and a ragged last tile."""
-    monkeypatch.setenv("SPD_TWO_STEP_ROWS", "0")
+    with gpu.options({gpu.OPT_PAIR_ROWS: 0}):
+        _two_step_case(gpu, dt, n, nrhs, T_A)
+
+
+def _two_step_case(gpu, dt, n, nrhs, T_A):
     A = spdgen.make_A(n, dt, 0.5, 21, device="cuda")
     B = spdgen.make_B(n, nrhs, dt, 21, device="cuda")
     A_np, B_np = wide(A), wide(B)
@@ -401,11 +323,11 @@ def test_posv_parity(gpu, dt, n, nrhs, T_A, pad):
 
 
 @pytest.mark.parametrize("dt,n,nrhs,T_A", [("f64", 1300, 9, 128), ("f64", 1024, 3, 128)])
-def test_posv_paired_steps(gpu, dt, n, nrhs, T_A, monkeypatch):
+def test_posv_paired_steps(gpu, dt, n, nrhs, T_A):
     """With every step paired, the forward substitution follows the tiles as
     the pairs finish them."""
-    monkeypatch.setenv("SPD_TWO_STEP_ROWS", "0")
-    posv_check(gpu, dt, n, nrhs, T_A)
+    with gpu.options({gpu.OPT_PAIR_ROWS: 0}):
+        posv_check(gpu, dt, n, nrhs, T_A)
 
 
 def test_posv_failed_factorization(gpu):
@@ -418,26 +340,6 @@ def test_posv_failed_factorization(gpu):
     torch.cuda.synchronize()
     assert int(info.item()) == 701
     assert torch.isnan(B).all() and math.isnan(float(ld.item()))
-
-
-def test_posv_full_size(gpu):
-    """N = 32768 fp64, T_A = 512, 128 right-hand sides (the benchmark's
-    workload): backward error of X within 64 N eps and log det against the
-    factor's diagonal."""
-    n, nrhs, T_A = 32768, 128, 512
-    A0 = spdgen.make_A(n, "f64", 0.05, 0, device="cuda")
-    B0 = spdgen.make_B(n, nrhs, "f64", 0, device="cuda")
-    A = spdgen.to_colmajor(A0)
-    B = spdgen.to_colmajor(B0)
-    ld = torch.zeros(1, dtype=torch.float64, device="cuda")
-    info = gpu.posv(A, B, T_A, logdet_out=ld)
-    torch.cuda.synchronize()
-    assert int(info.item()) == 0
-    eta = backward_error(A0, B, B0)
-    assert eta <= 64 * n * EPS["f64"], eta
-    d = torch.diagonal(A).to(torch.float64)
-    ref = float(2.0 * torch.log(d).sum().item())
-    assert abs(float(ld.item()) - ref) <= 1e-11 * abs(ref)
 
 
 def test_huge_leading_dimension(gpu):

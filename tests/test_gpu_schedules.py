@@ -1,37 +1,29 @@
 """GPU parity of the alternative factorization schedules.
 
-The library reads SPD_LOOKAHEAD (0: the sequential schedule, every kernel on
-the caller's stream) and SPD_TWO_STEP (0: one-step lookahead instead of the
-paired-step schedule) once per process, so each setting runs in a child
-process: potrf, log det and potrs through the one-call entry point (which
-falls back to the three calls when its fused path is off) on small real and
-complex inputs, checked against the oracle on the same bytes.
+SPD_OPT_LOOKAHEAD = 0 selects the sequential schedule (every kernel on the
+caller's stream) and SPD_OPT_TWO_STEP = 0 the one-step lookahead instead of
+the paired-step schedule.  Under each, potrf, log det and potrs run through
+the one-call entry point (which falls back to the three calls when its fused
+path is off) on small real and complex inputs, checked against the oracle on
+the same bytes; and the auxiliary streams can be released and made again.
 """
 from __future__ import annotations
 
-import os
-import subprocess
-import sys
-
-import pytest
-
-pytestmark = pytest.mark.gpu
-
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-
-CHILD = r"""
-import sys
-sys.path[:0] = [{root!r}, {tests!r}]
 import numpy as np
+import pytest
 import torch
-import cholesky_spd_solve_amd as spd
+
 import oracle
 import spdgen
 from helpers import L_TOL, LOGDET_TOL, X_TOL, logdet_rel, rel_err_cols, wide
 
-for dt, n, nrhs, T in [("f64", 1000, 5, 128), ("f64", 1300, 7, 256), ("f64", 2100, 3, 128),
-                       ("f32", 1024, 4, 128), ("c128", 700, 3, 64)]:
-    print("case", dt, n, nrhs, T, flush=True)
+pytestmark = pytest.mark.gpu
+
+CASES = [("f64", 1000, 5, 128), ("f64", 1300, 7, 256), ("f64", 2100, 3, 128), ("f32", 1024, 4, 128),
+         ("c128", 700, 3, 64)]
+
+
+def run_case(spd, dt, n, nrhs, T):
     A = spdgen.make_A(n, dt, 0.5, 7, device="cuda")
     B = spdgen.make_B(n, nrhs, dt, 7, device="cuda")
     A_np, B_np = wide(A), wide(B)
@@ -46,13 +38,21 @@ for dt, n, nrhs, T in [("f64", 1000, 5, 128), ("f64", 1300, 7, 256), ("f64", 210
     assert rel_err_cols(X, oracle.potrs(Lo, B_np)) <= X_TOL[dt], (dt, n)
     if dt in ("f64", "c128"):
         assert logdet_rel(float(ld.item()), oracle.logdet(Lo)) <= LOGDET_TOL, (dt, n)
-print("ok", flush=True)
-"""
 
 
-@pytest.mark.parametrize("env", [{"SPD_LOOKAHEAD": "0"}, {"SPD_TWO_STEP": "0"}], ids=["sequential", "one-step"])
-def test_schedule_parity(gpu, env):
-    code = CHILD.format(root=ROOT, tests=os.path.join(ROOT, "tests"))
-    r = subprocess.run([sys.executable, "-c", code], env=dict(os.environ, **env), capture_output=True, text=True,
-                       timeout=240)
-    assert r.returncode == 0 and r.stdout.rstrip().endswith("ok"), r.stdout[-2000:] + r.stderr[-2000:]
+@pytest.mark.parametrize("opt", ["sequential", "one-step"])
+@pytest.mark.parametrize("dt,n,nrhs,T", CASES)
+def test_schedule_parity(gpu, opt, dt, n, nrhs, T):
+    values = {gpu.OPT_LOOKAHEAD: 0} if opt == "sequential" else {gpu.OPT_TWO_STEP: 0}
+    with gpu.options(values):
+        run_case(gpu, dt, n, nrhs, T)
+
+
+def test_release_and_recreate_streams(gpu):
+    """spd_release waits for and destroys the auxiliary streams; the next call
+    makes them again and still matches the oracle."""
+    run_case(gpu, "f64", 1300, 7, 256)
+    gpu.release()
+    gpu.release()  # nothing left: a no-op
+    run_case(gpu, "f64", 1300, 7, 256)
+    gpu.release()

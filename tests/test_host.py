@@ -158,6 +158,33 @@ def test_profile_class_validation(lib):
         spd.profile_read(9)
 
 
+def test_options_validate_and_restore(lib):
+    """spd_set_option checks its option number and value range; the
+    default marker restores each option's default."""
+    import cholesky_spd_solve_amd as spd
+    defaults = {spd.OPT_LOOKAHEAD: 1, spd.OPT_TWO_STEP: 1, spd.OPT_PAIR_ROWS: -1, spd.OPT_SYRK_DEEP_ROWS: -1,
+                spd.OPT_RECT_TALL_ROWS: 16384}
+    for k, v in defaults.items():
+        assert spd.get_option(k) == v
+    assert lib.spd_set_option(0, 1) == -1
+    assert lib.spd_set_option(6, 1) == -1
+    assert lib.spd_get_option(6) == -(1 << 63)
+    assert lib.spd_set_option(spd.OPT_LOOKAHEAD, 2) == -2
+    assert lib.spd_set_option(spd.OPT_TWO_STEP, -1) == -2
+    assert lib.spd_set_option(spd.OPT_PAIR_ROWS, -2) == -2
+    assert lib.spd_set_option(spd.OPT_RECT_TALL_ROWS, -1) == -2
+    with spd.options({spd.OPT_PAIR_ROWS: 0, spd.OPT_LOOKAHEAD: 0, spd.OPT_RECT_TALL_ROWS: 7}):
+        assert spd.get_option(spd.OPT_PAIR_ROWS) == 0
+        assert spd.get_option(spd.OPT_LOOKAHEAD) == 0
+        assert spd.get_option(spd.OPT_RECT_TALL_ROWS) == 7
+    for k, v in defaults.items():
+        assert spd.get_option(k) == v
+    spd.set_option(spd.OPT_SYRK_DEEP_ROWS, 5)
+    spd.set_option(spd.OPT_SYRK_DEEP_ROWS, spd.OPT_DEFAULT)
+    assert spd.get_option(spd.OPT_SYRK_DEEP_ROWS) == -1
+    assert lib.spd_release() == 0  # nothing created on this thread: nothing to do
+
+
 # ------------------------------------------------------------ generator ---
 
 @pytest.mark.parametrize("dt", ["f64", "f32", "c128", "c64"])
