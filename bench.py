@@ -58,7 +58,7 @@ HBM_PEAK_GBS = 8000.0
 # (profiles/counters_syrk_f64_n32768_t512.md).  Valid for the trailing-update
 # kernels and schedule as they were when the counters were taken; emptied when
 # they change.
-SYRK_TRAFFIC_BYTES = {("f64", 32768, 512): 8.931e9}
+SYRK_TRAFFIC_BYTES = {("f64", 32768, 512, "posv"): 8.931e9}
 
 
 def parse():
@@ -78,6 +78,10 @@ def parse():
                         "log-likelihood of the N_RHS residual columns (forward substitution + reduction); "
                         "sygst: potrf of B + reduction of the generalized eigenproblem (A, B) to standard form")
     p.add_argument("--itype", type=int, choices=(1, 2, 3), default=1, help="problem type of --workload sygst")
+    p.add_argument("--no-phases", action="store_true",
+                   help="skip the three-call loop that gives potrf's own rate and the phase times")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the other workloads (1-4 and complex64 N=8192) reported beside workload 5")
     p.add_argument("--separate", action="store_true",
                    help="solve workload: time spd_potrf, spd_logdet and spd_potrs as three calls instead of the "
                         "one-call spd_posv")
@@ -138,72 +142,20 @@ def main():
     A0, B0, _ = spdgen.make_config(args.config, args.seed, device="cuda")
     torch.cuda.synchronize()
     log(f"[bench] inputs ready in {time.time() - t0:.1f} s")
-    A = spdgen.to_colmajor(A0)
-    B = spdgen.to_colmajor(B0)
-    work = spd.workspace(A.dtype, n, nrhs, T)
-    info = torch.zeros(1, dtype=torch.int32, device="cuda")
-    ldbuf = torch.zeros(1, dtype=torch.float64, device="cuda")
-    gpout = torch.zeros(nrhs, dtype=torch.float64, device="cuda")
-    stream = torch.cuda.current_stream()
+    bufs = SolveBuffers(spd, A0, B0, T)
+    peak = PEAK[dt]
 
-    def restore():
-        A.copy_(A0)
-        B.copy_(B0)
-
-    fused = not gp and not args.separate
-
-    def step(ev):
-        ev[0].record(stream)
-        if fused:  # potrf, logdet and potrs in one call (spd_posv)
-            spd.posv(A, B, T, info=info, logdet_out=ldbuf if cfg["logdet"] else None, work=work)
-            for e in ev[1:]:
-                e.record(stream)
-            return
-        spd.potrf(A, T, info=info, work=work)
-        ev[1].record(stream)
-        if cfg["logdet"] and not gp:
-            spd.logdet(A, info, out=ldbuf)
-        ev[2].record(stream)
-        if gp:
-            spd.gp_loglik(A, B, T, info=info, work=work, out=gpout)
-        else:
-            spd.potrs(A, B, T, info=info, work=work)
-        ev[3].record(stream)
-
-    def events():
-        return [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-
-    for w in range(args.warmup):
-        restore()
-        step(events())
-        torch.cuda.synchronize()
-        log(f"[bench] warmup {w + 1}/{args.warmup} done")
-
-    # timed region: K steps; restores happen between steps, outside the events
-    spd.profile_enable((1 << spd.PROF_SYRK) | (1 << spd.PROF_SYRK_AUX))
-    spd.profile_read(spd.PROF_SYRK)
-    spd.profile_read(spd.PROF_SYRK_AUX)
-    evs = []
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    for k in range(args.steps):
-        restore()
-        ev = events()
-        step(ev)
-        evs.append(ev)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    spd.profile_enable(0)
-    syrk_ms, syrk_launches, syrk_flops = spd.profile_read(spd.PROF_SYRK)
-    aux_ms, aux_launches, aux_flops = spd.profile_read(spd.PROF_SYRK_AUX)
-
-    step_ms = [e[0].elapsed_time(e[3]) for e in evs]
-    potrf_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    logdet_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    potrs_ms = [e[2].elapsed_time(e[3]) for e in evs]
-    ms = float(np.mean(step_ms))
-    status = int(info.item())
-    log(f"[bench] steps: {', '.join(f'{x:.2f}' for x in step_ms)} ms; info={status}")
+    mode = "gp" if gp else "three" if args.separate else "posv"
+    three = None
+    if mode == "posv" and not args.no_phases:
+        # the three calls on the same inputs, for the factorization's own rate
+        # and the per-phase times (timed before the headline loop, whose
+        # output the check below reads)
+        three = solve_loop(spd, bufs, cfg, "three", args.steps, min(args.warmup, 2), False, "three calls")
+    r = solve_loop(spd, bufs, cfg, mode, args.steps, args.warmup, True, mode)
+    ms = float(np.mean(r["step_ms"]))
+    status = r["info"]
+    A, B = bufs.A, bufs.B
 
     check = None
     if not args.no_check and gp:
@@ -211,33 +163,35 @@ def main():
         # computed factor, in double on the GPU
         Lw = torch.tril(A).to(torch.float64)
         Yw, Rw = B.to(torch.float64), B0.to(torch.float64)
-        r = Rw - Lw @ Yw
-        eta = (r.abs().amax(dim=0) / (Lw.abs().sum(dim=1).max() * Yw.abs().amax(dim=0) + Rw.abs().amax(dim=0))).max()
+        rr = Rw - Lw @ Yw
+        eta = (rr.abs().amax(dim=0) / (Lw.abs().sum(dim=1).max() * Yw.abs().amax(dim=0) + Rw.abs().amax(dim=0))).max()
         eps = 2.0**-52 if dt == "f64" else 2.0**-23
+        gpout = bufs.gpout
         finite = bool(torch.isfinite(gpout).all().item())
         check = {"forward_backward_error": float(eta.item()), "bound_64_n_eps": 64 * n * eps,
                  "loglik_first": float(gpout[0].item()), "ok": bool(eta.item() <= 64 * n * eps and status == 0
                                                                    and finite)}
-        del Lw, Yw, Rw, r
+        del Lw, Yw, Rw, rr
         log(f"[bench] forward-substitution backward error {check['forward_backward_error']:.3e} "
             f"(bound {check['bound_64_n_eps']:.3e}); loglik[0] = {check['loglik_first']:.6f}")
     elif not args.no_check:
-        # normwise backward error of the last step's X, residual in double on the GPU
-        wd = torch.complex128 if cplx else torch.float64
-        Aw, Xw, Bw = A0.to(wd), B.to(wd), B0.to(wd)
-        r = Bw - Aw @ Xw
-        eta = (r.abs().amax(dim=0) / (Aw.abs().sum(dim=1).max() * Xw.abs().amax(dim=0) + Bw.abs().amax(dim=0))).max()
-        eps = 2.0**-52 if dt in ("f64", "c128") else 2.0**-23
-        check = {"backward_error": float(eta.item()), "bound_64_n_eps": 64 * n * eps,
-                 "ok": bool(eta.item() <= 64 * n * eps and status == 0)}
-        del Aw, Xw, Bw, r
+        check = backward_check(A0, B, B0, dt, n, status)
         log(f"[bench] backward error {check['backward_error']:.3e} (bound {check['bound_64_n_eps']:.3e})")
 
     value = flops / (ms * 1e-3) / 1e12
-    potrf_tf = None if fused else flops_potrf / (float(np.mean(potrf_ms)) * 1e-3) / 1e12
+    phases = three if three is not None else r if mode != "posv" else None
+    potrf_tf = None
+    phase_ms = {"posv": ms} if mode == "posv" else {}
+    if phases is not None:
+        potrf_ms = float(np.mean(phases["potrf_ms"]))
+        potrf_tf = flops_potrf / (potrf_ms * 1e-3) / 1e12
+        phase_ms.update({"potrf": potrf_ms, "logdet": float(np.mean(phases["logdet_ms"])),
+                         ("gp_loglik" if gp else "potrs"): float(np.mean(phases["potrs_ms"])),
+                         "three_calls": float(np.mean(phases["step_ms"]))})
+    syrk_ms, syrk_launches, syrk_flops = r["syrk"]
+    aux_ms, aux_launches, aux_flops = r["aux"]
     syrk_avg_ms = syrk_ms / max(syrk_launches, 1)
     syrk_achieved = (syrk_flops / syrk_launches) / (syrk_avg_ms * 1e-3) / 1e12 if syrk_launches else None
-    peak = PEAK[dt]
     aux_avg_ms = aux_ms / max(aux_launches, 1)
     roofline = {
         "kernel": "syrk_kernel (trailing update A22 -= L21 L21^H, lower tiles; launches on the caller's stream)",
@@ -246,7 +200,7 @@ def main():
         "peak": peak,
         "unit": "TFLOP/s",
         "frac": (syrk_achieved / peak) if syrk_achieved else None,
-        "traffic": SYRK_TRAFFIC_BYTES.get((dt, n, T)) if not gp else None,
+        "traffic": SYRK_TRAFFIC_BYTES.get((dt, n, T, mode)) if not gp else None,
         "launches": syrk_launches,
         "avg_launch_ms": syrk_avg_ms,
         "flops_per_launch": syrk_flops / max(syrk_launches, 1),
@@ -257,6 +211,12 @@ def main():
                        "achieved": (aux_flops / aux_launches) / (aux_avg_ms * 1e-3) / 1e12 if aux_launches else None,
                        "flop_share": aux_flops / max(aux_flops + syrk_flops, 1.0)},
     }
+
+    others = None
+    if not gp and args.config == 5 and not args.no_configs:
+        del bufs, A, B
+        torch.cuda.empty_cache()
+        others = other_configs(spd, args, cpu=not args.no_cpu_baseline)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -285,19 +245,183 @@ def main():
         "pct_of_peak": 100.0 * value / peak,
         "potrf_tflops": potrf_tf,
         "potrf_pct_of_peak": None if potrf_tf is None else 100.0 * potrf_tf / peak,
-        "entry_points": ("spd_posv (potrf + logdet + potrs in one call)" if fused else
+        "entry_points": ("spd_posv (potrf + logdet + potrs in one call); phases from spd_potrf, spd_logdet, "
+                         "spd_potrs timed on the same inputs" if mode == "posv" else
                          "spd_potrf, spd_gp_loglik" if gp else "spd_potrf, spd_logdet, spd_potrs"),
-        "phase_ms": ({"posv": ms} if fused else
-                     {"potrf": float(np.mean(potrf_ms)), "gp_loglik": float(np.mean(potrs_ms))} if gp else
-                     {"potrf": float(np.mean(potrf_ms)), "logdet": float(np.mean(logdet_ms)),
-                      "potrs": float(np.mean(potrs_ms))}),
-        "wall_ms_per_step_incl_restore": 1e3 * wall / args.steps,
+        "phase_ms": phase_ms,
+        "wall_ms_per_step_incl_restore": r["wall_ms"],
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "configs": others,
         "check": check,
     }
     print(json.dumps(out), flush=True)
-    return 0 if (check is None or check["ok"]) else 1
+    ok = check is None or check["ok"]
+    if others is not None:
+        ok = ok and all(v.get("check_ok", True) for v in others.values())
+    return 0 if ok else 1
+
+
+class SolveBuffers:
+    """Working copies of A and B (restored from the pristine A0, B0 before
+    every step, outside the timed events), the workspace and small outputs."""
+
+    def __init__(self, spd, A0, B0, T):
+        import torch
+        import spdgen
+        n, nrhs = B0.shape
+        self.A0, self.B0 = A0, B0
+        self.A = spdgen.to_colmajor(A0)
+        self.B = spdgen.to_colmajor(B0)
+        self.work = spd.workspace(self.A.dtype, n, nrhs, T)
+        self.info = torch.zeros(1, dtype=torch.int32, device="cuda")
+        self.ldbuf = torch.zeros(1, dtype=torch.float64, device="cuda")
+        self.gpout = torch.zeros(nrhs, dtype=torch.float64, device="cuda")
+
+    def restore(self):
+        self.A.copy_(self.A0)
+        self.B.copy_(self.B0)
+
+
+def solve_loop(spd, bufs, cfg, mode, steps, warmup, profile, tag):
+    """Warm up, then time ``steps`` steps of ``mode``: "posv" (one call),
+    "three" (spd_potrf, spd_logdet, spd_potrs) or "gp" (spd_potrf,
+    spd_gp_loglik).  Each step is bracketed by HIP events on the caller's
+    stream, with the phase boundaries of the multi-call modes; with
+    ``profile`` the trailing-update launches are timed by the library's own
+    events on the streams they run on."""
+    import numpy as np
+    import torch
+
+    T = cfg["T_A"]
+    stream = torch.cuda.current_stream()
+    A, B = bufs.A, bufs.B
+    want_ld = cfg["logdet"]
+
+    def step(ev):
+        ev[0].record(stream)
+        if mode == "posv":
+            spd.posv(A, B, T, info=bufs.info, logdet_out=bufs.ldbuf if want_ld else None, work=bufs.work)
+            for e in ev[1:]:
+                e.record(stream)
+            return
+        spd.potrf(A, T, info=bufs.info, work=bufs.work)
+        ev[1].record(stream)
+        if want_ld and mode != "gp":
+            spd.logdet(A, bufs.info, out=bufs.ldbuf)
+        ev[2].record(stream)
+        if mode == "gp":
+            spd.gp_loglik(A, B, T, info=bufs.info, work=bufs.work, out=bufs.gpout)
+        else:
+            spd.potrs(A, B, T, info=bufs.info, work=bufs.work)
+        ev[3].record(stream)
+
+    def events():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+    for w in range(warmup):
+        bufs.restore()
+        step(events())
+        torch.cuda.synchronize()
+        log(f"[bench] {tag}: warmup {w + 1}/{warmup} done")
+    if profile:
+        spd.profile_enable((1 << spd.PROF_SYRK) | (1 << spd.PROF_SYRK_AUX))
+        spd.profile_read(spd.PROF_SYRK)
+        spd.profile_read(spd.PROF_SYRK_AUX)
+    evs = []
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for _ in range(steps):
+        bufs.restore()
+        ev = events()
+        step(ev)
+        evs.append(ev)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    syrk = aux = (0.0, 0, 0.0)
+    if profile:
+        spd.profile_enable(0)
+        syrk = spd.profile_read(spd.PROF_SYRK)
+        aux = spd.profile_read(spd.PROF_SYRK_AUX)
+    out = {
+        "step_ms": [e[0].elapsed_time(e[3]) for e in evs],
+        "potrf_ms": [e[0].elapsed_time(e[1]) for e in evs],
+        "logdet_ms": [e[1].elapsed_time(e[2]) for e in evs],
+        "potrs_ms": [e[2].elapsed_time(e[3]) for e in evs],
+        "wall_ms": 1e3 * wall / max(steps, 1),
+        "syrk": syrk,
+        "aux": aux,
+        "info": int(bufs.info.item()),
+    }
+    log(f"[bench] {tag}: steps {', '.join(f'{x:.2f}' for x in out['step_ms'])} ms; "
+        f"mean {np.mean(out['step_ms']):.3f} ms; info={out['info']}")
+    return out
+
+
+def backward_check(A0, X, B0, dt, n, status):
+    """Normwise backward error of X (residual in double on the GPU)."""
+    import torch
+    wd = torch.complex128 if A0.is_complex() else torch.float64
+    Aw, Xw, Bw = A0.to(wd), X.to(wd), B0.to(wd)
+    rr = Bw - Aw @ Xw
+    eta = (rr.abs().amax(dim=0) / (Aw.abs().sum(dim=1).max() * Xw.abs().amax(dim=0) + Bw.abs().amax(dim=0))).max()
+    eps = 2.0**-52 if dt in ("f64", "c128") else 2.0**-23
+    return {"backward_error": float(eta.item()), "bound_64_n_eps": 64 * n * eps,
+            "ok": bool(eta.item() <= 64 * n * eps and status == 0)}
+
+
+# The other workloads reported beside the headline one: the four smaller
+# benchmark configurations, and complex64 at the complex128 workload's shape.
+EXTRA_WORKLOADS = {"c64_n8192": dict(dtype="c64", n=8192, nrhs=32, T_A=256, delta=0.5, logdet=True)}
+
+
+def other_configs(spd, args, cpu):
+    """ms per solve (one call and three calls), TFLOP/s and % of the matrix
+    peak for workloads 1-4 and complex64 N = 8192, each on its own inputs,
+    plus, for the fp32 workload, the single-precision oracle on a bounded
+    sample as its own-precision CPU baseline."""
+    import numpy as np
+    import torch
+
+    import spdgen
+
+    out = {}
+    items = [(str(k), dict(spdgen.CONFIGS[k]), k) for k in (1, 2, 3, 4)]
+    items += [(name, dict(c), None) for name, c in EXTRA_WORKLOADS.items()]
+    for name, c, k in items:
+        dt, n, nrhs, T = c["dtype"], c["n"], c["nrhs"], c["T_A"]
+        fmul = 4.0 if dt in ("c64", "c128") else 1.0
+        t0 = time.time()
+        if k is not None:
+            A0, B0, _ = spdgen.make_config(k, args.seed, device="cuda")
+        else:
+            A0 = spdgen.make_A(n, dt, c["delta"], args.seed, device="cuda")
+            B0 = spdgen.make_B(n, nrhs, dt, args.seed, device="cuda")
+        torch.cuda.synchronize()
+        log(f"[bench] workload {name}: {dt} N={n} N_RHS={nrhs} T_A={T}, inputs in {time.time() - t0:.1f} s")
+        bufs = SolveBuffers(spd, A0, B0, T)
+        steps = max(args.steps, 10)
+        three = solve_loop(spd, bufs, c, "three", steps, 2, False, f"{name} three calls")
+        one = solve_loop(spd, bufs, c, "posv", steps, 2, False, f"{name} posv")
+        chk = backward_check(A0, bufs.B, B0, dt, n, one["info"])
+        flops_potrf = fmul * n**3 / 3.0
+        flops = flops_potrf + fmul * 2.0 * n * n * nrhs
+        ms = float(np.mean(one["step_ms"]))
+        potrf_ms = float(np.mean(three["potrf_ms"]))
+        peak = PEAK[dt]
+        rec = {"workload": f"{dt} N={n} N_RHS={nrhs} T_A={T} delta={c['delta']}" + ("" if k else " (extra)"),
+               "ms": ms, "tflops": flops / (ms * 1e-3) / 1e12, "pct_of_peak": 100.0 * flops / (ms * 1e-3) / 1e12 / peak,
+               "peak": peak, "three_calls_ms": float(np.mean(three["step_ms"])), "potrf_ms": potrf_ms,
+               "potrf_tflops": flops_potrf / (potrf_ms * 1e-3) / 1e12,
+               "potrf_pct_of_peak": 100.0 * flops_potrf / (potrf_ms * 1e-3) / 1e12 / peak,
+               "logdet_ms": float(np.mean(three["logdet_ms"])), "potrs_ms": float(np.mean(three["potrs_ms"])),
+               "backward_error": chk["backward_error"], "check_ok": chk["ok"]}
+        if cpu and dt == "f32":
+            rec["cpu_baseline"] = cpu_baseline(A0, B0, n, nrhs, fmul, args.cpu_seconds / 2, single=True)
+        out[name] = rec
+        del bufs, A0, B0
+        torch.cuda.empty_cache()
+    return out
 
 
 def bench_sygst(args, cfg):
@@ -457,14 +581,38 @@ def cpu_baseline_sygst(B0, H0, n, itype, fmul, target_s):
                       f"definition), {t:.2f} s", "seconds": t}
 
 
-def cpu_baseline(A0, B0, n, nrhs, fmul, target_s, gp=False):
+def host_cpu():
+    """CPU model, socket count and logical CPUs of this host (from
+    /proc/cpuinfo), and the CPUs this process may run on."""
+    model, sockets, logical = None, set(), 0
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                key, _, val = line.partition(":")
+                key, val = key.strip(), val.strip()
+                if key == "model name" and model is None:
+                    model = val
+                elif key == "physical id":
+                    sockets.add(val)
+                elif key == "processor":
+                    logical += 1
+    except OSError:
+        pass
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        allowed = os.cpu_count()
+    return {"model": model, "sockets": len(sockets) or None, "logical_cpus": logical or None,
+            "cpus_allowed": allowed}
+
+
+def cpu_baseline(A0, B0, n, nrhs, fmul, target_s, gp=False, single=False):
     """The CPU oracle, as it stands, on the leading principal block of the same
     matrix (and the matching rows of B): a bounded sample sized for about
     ``target_s`` seconds, scaled to TFLOP/s with the same flop formula.  For
     the likelihood workload the oracle's own definition (a full solve and
-    log det) is what runs."""
-    import numpy as np
-
+    log det) is what runs; with ``single`` the oracle's single-precision
+    routines (the fp32 workload in its own precision)."""
     import oracle
 
     def run(m):
@@ -474,6 +622,11 @@ def cpu_baseline(A0, B0, n, nrhs, fmul, target_s, gp=False):
         if gp:
             _, info = oracle.gp_loglik(a, b)
             return time.perf_counter() - t, info
+        if single:
+            l, info = oracle.potrf_single(a)
+            oracle.potrs_single(l, b)
+            oracle.logdet_single(l)
+            return time.perf_counter() - t, info
         l, info = oracle.potrf(a)
         oracle.potrs(l, b)
         oracle.logdet(l)
@@ -482,11 +635,11 @@ def cpu_baseline(A0, B0, n, nrhs, fmul, target_s, gp=False):
     m = sample_size(lambda k: run(k)[0], n, target_s)
     t, info = run(m)
     fl = fmul * (m**3 / 3.0 + (1.0 if gp else 2.0) * m * m * nrhs)
-    what = "Gaussian-process log-likelihood by its definition" if gp else "potrf + potrs + logdet"
+    what = ("GP log-likelihood by its definition" if gp else
+            "potrf+potrs+logdet, float32 oracle" if single else "potrf+potrs+logdet, float64 oracle")
     return {"value": fl / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"leading {m} x {m} principal block of the same A with the first {m} rows of all "
-                      f"{nrhs} right-hand sides ({what}), {t:.2f} s",
-            "seconds": t}
+            "sample": f"leading {m}^2 block of A, first {m} rows of B ({what}), {t:.1f} s",
+            "seconds": t, "sample_n": m, "cpu": host_cpu()}
 
 
 if __name__ == "__main__":
