@@ -121,10 +121,15 @@ constexpr int LDL = LEAF + 1;    // LDS row length of the leaf arrays
 
 // 1/sqrt(d) for finite d > 0 (and sqrt(d) in sq), without branches.  With
 // d = f 2^e (f in [1/2, 1)) and k = floor(e / 2), m = d 4^-k lies in [1/2, 2):
-// the hardware reciprocal square root estimate of m is refined by coupled
-// Newton steps on g -> sqrt(m) and h -> 1/(2 sqrt(m)) (each step squares the
-// relative error), and the powers of two are put back exactly.  The result is
-// within a few units in the last place.
+// the hardware reciprocal square root estimate y of m is refined by
+// Goldschmidt's square-root iteration (R. E. Goldschmidt, "Applications of
+// division by convergence", MIT, 1964; in the coupled form of P. Markstein,
+// "Software division and square root using Goldschmidt's algorithms", RNC 6,
+// 2004): g = m y -> sqrt(m) and h = y / 2 -> 1 / (2 sqrt(m)) are updated
+// together by r = 1/2 - g h, g += g r, h += h r, each step squaring the
+// relative error; the powers of two are then put back exactly.  Both results
+// are within 2 units in the last place (checked against correctly rounded
+// values over the whole exponent range by the factorization's tests).
 __device__ __forceinline__ double rsqrt_refined(double d, double &sq)
 {
     const int k = __builtin_amdgcn_frexp_exp(d) >> 1;
