@@ -34,8 +34,9 @@ DTYPE_CODE = {
 SYMBOLS = ("spd_workspace_size", "spd_potrf", "spd_potrs", "spd_posv", "spd_forward_solve", "spd_gp_loglik",
            "spd_logdet",
            "spd_sygst_workspace_size", "spd_sygst", "spd_last_error", "spd_profile_enable", "spd_profile_read",
-           "spd_debug_validate", "spd_set_option", "spd_get_option", "spd_release")
-SPD_ERR_HIP, SPD_ERR_CHECK = 1, 2
+           "spd_debug_validate", "spd_set_option", "spd_get_option", "spd_release", "spd_posv_noalloc")
+SPD_ERR_HIP, SPD_ERR_CHECK, SPD_ERR_SCRATCH = 1, 2, 3
+NOALLOC_SCRATCH_BYTES = 64 << 20  # spd_posv_noalloc's fixed per-device buffer
 PROF_SYRK, PROF_PANEL, PROF_DIAG, PROF_SOLVE, PROF_UPDATE, PROF_SYRK_AUX = 0, 1, 2, 3, 4, 5
 # schedule / tile-shape options (spd_set_option)
 OPT_LOOKAHEAD, OPT_TWO_STEP, OPT_PAIR_ROWS, OPT_SYRK_DEEP_ROWS, OPT_RECT_TALL_ROWS = 1, 2, 3, 4, 5
@@ -78,6 +79,8 @@ def load():
             lib.spd_potrs.restype = i32
             lib.spd_posv.argtypes = [i32, i64, i64, vp, i64, vp, i64, i64, vp, vp, vp, sz, vp]
             lib.spd_posv.restype = i32
+            lib.spd_posv_noalloc.argtypes = [i32, i64, i64, vp, i64, vp, i64, i64, vp, vp, vp]
+            lib.spd_posv_noalloc.restype = i32
             lib.spd_forward_solve.argtypes = [i32, i64, i64, vp, i64, vp, i64, i64, vp, vp, sz, vp]
             lib.spd_forward_solve.restype = i32
             lib.spd_gp_loglik.argtypes = [i32, i64, i64, vp, i64, vp, i64, i64, vp, vp, vp, sz, vp]
@@ -113,7 +116,8 @@ def _check(rc: int, what: str):
     if rc < 0:
         raise ValueError(f"{what}: argument {-rc} is invalid")
     msg = load().spd_last_error().decode(errors="replace")
-    kind = "launch validation failed" if rc == SPD_ERR_CHECK else "HIP error"
+    kind = ("launch validation failed" if rc == SPD_ERR_CHECK else
+            "scratch buffer too small" if rc == SPD_ERR_SCRATCH else "HIP error")
     raise SpdError(f"{what}: {kind}: {msg}")
 
 
@@ -213,6 +217,25 @@ def posv(A: torch.Tensor, B: torch.Tensor, T_A: int, info: torch.Tensor | None =
     rc = load().spd_posv(_code(A), n, nrhs, _ptr(A), lda, _ptr(B), ldb, int(T_A), _ptr(info), _ptr(logdet_out),
                          _ptr(work), work.numel(), ctypes.c_void_p(_stream(stream)))
     _check(rc, "spd_posv")
+    return info
+
+
+def posv_noalloc(A: torch.Tensor, B: torch.Tensor, T_A: int, info: torch.Tensor, logdet_out=None,
+                 stream=None) -> torch.Tensor:
+    """posv with no workspace argument: the library's fixed per-device
+    scratch buffer serves as workspace and nothing is allocated (``info`` and
+    ``logdet_out`` are the caller's).  Raises SpdError when the sizes need
+    more than NOALLOC_SCRATCH_BYTES of workspace."""
+    lda = _colmajor(A, "A")
+    ldb = _colmajor(B, "B")
+    n, nrhs = B.shape
+    if A.shape != (n, n):
+        raise ValueError("A must be n x n with n = B.shape[0]")
+    if B.dtype != A.dtype:
+        raise TypeError("A and B must have the same dtype")
+    rc = load().spd_posv_noalloc(_code(A), n, nrhs, _ptr(A), lda, _ptr(B), ldb, int(T_A), _ptr(info),
+                                 _ptr(logdet_out), ctypes.c_void_p(_stream(stream)))
+    _check(rc, "spd_posv_noalloc")
     return info
 
 

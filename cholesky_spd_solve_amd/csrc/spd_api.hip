@@ -1975,6 +1975,50 @@ static size_t matrix_bytes(int dt, int64_t m, int64_t n, int64_t ld)
     return (size_t)(((n - 1) * ld + m) * elem_size(dt));
 }
 
+// ------------------------------------------------ fixed scratch buffer ---
+// spd_posv_noalloc takes its workspace from this array instead of from the
+// caller.  Each device the library runs on holds its own copy from the time
+// the library's code is loaded there until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it only names a stand-in):
+// the device address of each device's copy comes from hipGetSymbolAddress,
+// taken once per device with that device current, and only that address is
+// used.
+static __device__ __align__(256) unsigned char scratch[SPD_NOALLOC_SCRATCH_BYTES];
+
+static std::mutex g_scratch_mu;
+static std::vector<std::pair<int, void *>> g_scratch_addr;  // (device, address of its copy)
+
+// Address of the current device's copy of `scratch` (a fixed stand-in in a
+// dry run, which makes no HIP calls and dereferences nothing).
+static int scratch_address(void **out)
+{
+    if (g_validate == 2) {
+        *out = (void *)(uintptr_t)(UINT64_C(0x7e0000000000));
+        return 0;
+    }
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    for (auto &d : g_scratch_addr)
+        if (d.first == dev) {
+            *out = d.second;
+            return 0;
+        }
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr || (uintptr_t)p % 256 != 0) {
+        g_last_error = "hipGetSymbolAddress(scratch): unexpected address";
+        return SPD_ERR_HIP;
+    }
+    g_scratch_addr.emplace_back(dev, p);
+    *out = p;
+    return 0;
+}
+
 }  // namespace spd
 
 using namespace spd;
@@ -2217,6 +2261,55 @@ int spd_posv(spd_dtype_t dt, int64_t n, int64_t n_rhs, void *dA, int64_t lda, vo
     case SPD_C128:
         return Solver<double, true>::posv(n, n_rhs, (Elem<double, true>::type *)dA, lda,
                                           (Elem<double, true>::type *)dB, ldb, T_A, d_info, d_logdet, d_work, s);
+    }
+    return -1;
+}
+
+int spd_posv_noalloc(spd_dtype_t dt, int64_t n, int64_t n_rhs, void *dA, int64_t lda, void *dB, int64_t ldb,
+                     int64_t T_A, int32_t *d_info, double *d_logdet, void *stream)
+{
+    if (elem_size(dt) == 0) return -1;
+    if (n < 0 || n > INT32_MAX) return -2;
+    if (n_rhs < 0 || n_rhs > INT32_MAX) return -3;
+    if (dA == nullptr && n > 0) return -4;
+    if (lda < std::max<int64_t>(1, n)) return -5;
+    if (dB == nullptr && n > 0 && n_rhs > 0) return -6;
+    if (ldb < std::max<int64_t>(1, n)) return -7;
+    if (T_A < 1) return -8;
+    if (d_info == nullptr) return -9;
+    const size_t need = spd_workspace_size(dt, n, n_rhs, T_A);
+    if (need > (size_t)SPD_NOALLOC_SCRATCH_BYTES) {
+        g_last_error = "spd_posv_noalloc: these sizes need " + std::to_string(need) +
+                       " bytes of workspace; the fixed scratch buffer holds " +
+                       std::to_string((size_t)SPD_NOALLOC_SCRATCH_BYTES);
+        return SPD_ERR_SCRATCH;
+    }
+    void *ws = nullptr;
+    SPD_TRY(scratch_address(&ws));
+    if (g_validate) {
+        g_chk.begin();
+        g_chk.add(dA, matrix_bytes(dt, n, n, lda), true, "A");
+        g_chk.add(dB, matrix_bytes(dt, n, n_rhs, ldb), true, "B");
+        g_chk.add(d_info, 4, true, "info");
+        if (d_logdet != nullptr)
+            g_chk.add(d_logdet, sizeof(double), true, "logdet");
+        g_chk.add(ws, SPD_NOALLOC_SCRATCH_BYTES, true, "scratch");
+    }
+    snapshot_options();
+    g_opt.v[OPT_LOOKAHEAD] = 0;  // every kernel in order on `stream`: no auxiliary streams or events
+    hipStream_t s = (hipStream_t)stream;
+    switch (dt) {
+    case SPD_R32:
+        return Solver<float, false>::posv(n, n_rhs, (float *)dA, lda, (float *)dB, ldb, T_A, d_info, d_logdet, ws, s);
+    case SPD_R64:
+        return Solver<double, false>::posv(n, n_rhs, (double *)dA, lda, (double *)dB, ldb, T_A, d_info, d_logdet, ws,
+                                           s);
+    case SPD_C64:
+        return Solver<float, true>::posv(n, n_rhs, (Elem<float, true>::type *)dA, lda, (Elem<float, true>::type *)dB,
+                                         ldb, T_A, d_info, d_logdet, ws, s);
+    case SPD_C128:
+        return Solver<double, true>::posv(n, n_rhs, (Elem<double, true>::type *)dA, lda,
+                                          (Elem<double, true>::type *)dB, ldb, T_A, d_info, d_logdet, ws, s);
     }
     return -1;
 }

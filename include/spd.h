@@ -64,6 +64,10 @@ typedef enum {
 
 #define SPD_ERR_HIP 1
 #define SPD_ERR_CHECK 2
+#define SPD_ERR_SCRATCH 3
+
+/* Size of the fixed device scratch buffer of spd_posv_noalloc (per device). */
+#define SPD_NOALLOC_SCRATCH_BYTES (64 << 20)
 
 /* Bytes of device workspace that spd_potrf and spd_potrs need for these
  * sizes (one workspace serves both).  Returns 0 for invalid arguments
@@ -124,6 +128,32 @@ int spd_potrs(spd_dtype_t dt, int64_t n, int64_t n_rhs, const void *dA, int64_t 
 int spd_posv(spd_dtype_t dt, int64_t n, int64_t n_rhs, void *dA, int64_t lda, void *dB,
              int64_t ldb, int64_t T_A, int32_t *d_info, double *d_logdet, void *d_work,
              size_t work_bytes, void *stream);
+
+/* spd_posv for callers that cannot allocate device memory or pass a
+ * workspace: code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, results and argument
+ * numbers as spd_posv without d_work and work_bytes (dt=1 n=2 n_rhs=3 dA=4
+ * lda=5 dB=6 ldb=7 T_A=8 d_info=9 d_logdet=10).
+ *   - The workspace is a fixed buffer of SPD_NOALLOC_SCRATCH_BYTES bytes
+ *     compiled into the library: each device the library runs on holds its
+ *     own copy until the process ends.  Sizes whose
+ *     spd_workspace_size(dt, n, n_rhs, T_A) exceeds it are rejected with
+ *     SPD_ERR_SCRATCH (spd_last_error() gives both sizes) and nothing is
+ *     enqueued; 64 MiB covers, e.g., fp64 n = 4096 with T_A = 256 and up to
+ *     128 right-hand sides.
+ *   - The call allocates nothing (no hipMalloc, no library routine that
+ *     allocates) and creates no stream or event: every kernel runs in order
+ *     on `stream` (the sequential schedule), on the current device, whose
+ *     copy of the buffer it uses.  The first call on a device looks up that
+ *     copy's address once.
+ *   - Every call on one device shares that device's buffer, which keeps the
+ *     previous call's contents; the call initialises what it needs.  Calls
+ *     that overlap on one device (on different streams, or from different
+ *     host threads) race on the buffer and must be ordered by the caller.
+ * Returns 0, -i for an invalid argument, SPD_ERR_SCRATCH, SPD_ERR_HIP or
+ * SPD_ERR_CHECK as the other entry points. */
+int spd_posv_noalloc(spd_dtype_t dt, int64_t n, int64_t n_rhs, void *dA, int64_t lda, void *dB,
+                     int64_t ldb, int64_t T_A, int32_t *d_info, double *d_logdet, void *stream);
 
 /* Forward substitution only: overwrite B with Y = L^-1 B, from the factor of
  * spd_potrf (JAXMg paper, "Software design": the first of potrs' two

@@ -143,3 +143,26 @@ def test_dry_run_posv(lib, dt, n, nrhs, T):
     for logdet in (vp(ld), None):
         rc = lib.spd_posv(code, n, nrhs, vp(A), n, vp(B), n, T, vp(info), logdet, vp(work), wbytes, None)
         assert rc == 0, (rc, lib.spd_last_error())
+
+
+@pytest.mark.parametrize("dt,n,nrhs,T", [("f64", 2048, 16, 256), ("f64", 1000, 5, 128), ("c128", 700, 3, 64),
+                                         ("f32", 65, 2, 64), ("c64", 300, 4, 100)])
+def test_dry_run_posv_noalloc(lib, dt, n, nrhs, T):
+    """The fixed-scratch solve replays in bounds of the scratch buffer (a
+    stand-in address in a dry run), with and without log det."""
+    code = CODE[dt]
+    vp = ctypes.c_void_p
+    A, B, info, ld = BASE, 2 * BASE, 3 * BASE, 3 * BASE + 4096
+    for logdet in (vp(ld), None):
+        rc = lib.spd_posv_noalloc(code, n, nrhs, vp(A), n, vp(B), n, T, vp(info), logdet, None)
+        assert rc == 0, (rc, lib.spd_last_error())
+
+
+def test_dry_run_posv_noalloc_rejects_large_sizes(lib):
+    vp = ctypes.c_void_p
+    n, nrhs, T = 16384, 64, 512
+    assert lib.spd_workspace_size(0, n, nrhs, T) > (64 << 20)
+    rc = lib.spd_posv_noalloc(0, n, nrhs, vp(BASE), n, vp(2 * BASE), n, T, vp(3 * BASE), None, None)
+    assert rc == 3
+    assert b"bytes of workspace" in lib.spd_last_error()
+    assert lib.spd_posv_noalloc(0, 4, 1, vp(BASE), 3, vp(2 * BASE), 4, 2, vp(3 * BASE), None, None) == -5
