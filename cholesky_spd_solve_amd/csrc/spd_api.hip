@@ -418,7 +418,7 @@ static bool lookahead_enabled() { return g_opt.v[OPT_LOOKAHEAD] != 0; }
 static int64_t syrk_deep_rows(int64_t esize)
 {
     const int64_t v = g_opt.v[OPT_SYRK_DEEP_ROWS];
-    return v >= 0 ? v : (esize == 8 ? 24576 : 12288);
+    return v >= 0 ? v : (esize == 8 ? 24576 : 8192);
 }
 
 // Block-update heights from which the substitutions (and the factorization's
@@ -713,7 +713,7 @@ struct Solver {
         bool aux = false;  // potrf's auxiliary stream (timed as its own class)
     };
 
-    template <int BM, int KB, int WM, int WN, bool BIGLD = false>
+    template <int BM, int KB, int WM, int WN, bool BIGLD = false, bool PK = false>
     static int syrk_cfg(int64_t m, const E *W, int64_t ldw, int64_t kp, E *C, int64_t ldc, int jt_end,
                         const int *info, hipStream_t s, const Syr2 &x = Syr2())
     {
@@ -744,9 +744,10 @@ struct Solver {
             a.ntiles = a.tiles * (a.tiles + 1) / 2;
         }
         a.info = info;
+        a.vecc = ((uintptr_t)C % 16 == 0 && (ldc * (int64_t)sizeof(E)) % 16 == 0) ? 1 : 0;
         const dim3 grid((unsigned)a.ntiles), block(64 * WM * WN);
-        SPD_VALIDATE((check_syrk<R, CPLX, BM, KB, WM, WN, BIGLD>(a, grid, g_chk)));
-        syrk_kernel<R, CPLX, BM, KB, WM, WN, BIGLD><<<grid, block, 0, s>>>(a);
+        SPD_VALIDATE((check_syrk<R, CPLX, BM, KB, WM, WN, BIGLD, PK>(a, grid, g_chk)));
+        syrk_kernel<R, CPLX, BM, KB, WM, WN, BIGLD, PK><<<grid, block, 0, s>>>(a);
         SPD_CHECK_LAUNCH("syrk_kernel");
         return 0;
     }
@@ -784,15 +785,21 @@ struct Solver {
             // tiles: one 128 x 128 x T tile is a fixed ~55 us of a CU's
             // matrix-core time, so a small update finishes sooner on four times
             // as many workgroups with a quarter of the work each.
+            // Packed rows (two or four adjacent rows per lane, 16-byte LDS
+            // operand reads and C vectors; the same bits) where they measured
+            // faster alone: fp64 64-row tiles 3-4.5 % (m = 2048-4096, depth
+            // 512), fp32 32-deep 128-row tiles 1-2 % at depth 512; fp64
+            // 128-row tiles within 1 %, fp32 16-deep and 64-row tiles 3-5 %
+            // slower, so those keep the plain layout.
             const int64_t t128 = cdiv(m, 128);
             const int64_t n128 = cols > 0 ? std::min<int64_t>(cols / 128, t128) * t128 : t128 * (t128 + 1) / 2;
             if (n128 < 512)
-                return syrk_cfg<64, 16, 2, 2>(m, W, ldw, kp, C, ldc, jt(64), info, s, x);
+                return syrk_cfg<64, 16, 2, 2, false, sizeof(R) == 8>(m, W, ldw, kp, C, ldc, jt(64), info, s, x);
             if constexpr (sizeof(R) == 4) {
                 // fp32: 32-deep slices for large orders (72 % of the fp32 peak
                 // against 61 % at m = 15872), 16-deep below
                 if (m >= syrk_deep_rows(4))
-                    return syrk_cfg<128, 32, 2, 4>(m, W, ldw, kp, C, ldc, jt(128), info, s, x);
+                    return syrk_cfg<128, 32, 2, 4, false, true>(m, W, ldw, kp, C, ldc, jt(128), info, s, x);
                 return syrk_cfg<128, 16, 2, 4>(m, W, ldw, kp, C, ldc, jt(128), info, s, x);
             } else {
                 // slice depth: 16 for the large early steps, 8 below (more

@@ -152,7 +152,7 @@ static bool check_gemm(const GemmArgs &p, dim3 grid, Checker &c)
 
 // Replay of syrk_kernel (spd_syrk.hpp): whole-tile vector loads of both row
 // blocks of W for every slice, and the epilogue's read-modify-write of C.
-template <typename R, bool CPLX, int BM, int KB, int WM, int WN, bool BIGLD>
+template <typename R, bool CPLX, int BM, int KB, int WM, int WN, bool BIGLD, bool PK = false>
 static bool check_syrk(const SyrkArgs &p, dim3 grid, Checker &c)
 {
     typedef typename SyrkOff<BIGLD>::type Off;
@@ -210,10 +210,15 @@ static bool check_syrk(const SyrkArgs &p, dim3 grid, Checker &c)
             const int ib = wm * TM, jb = wn * TN;
             const bool whole = rectm ? (i0 + BM <= p.m && j0 + BM <= p.ncols) : ((I != J) && (i0 + BM <= p.m));
             E *Ct = (E *)p.C + i0 + (int64_t)j0 * p.ldc;
+            constexpr int RA = SyrkPack<R, PK, FM>::value, RB = SyrkPack<R, PK, FN>::value;
+            // whole tiles with 16-byte access to C: RA adjacent rows per vector
+            const bool vec = RA > 1 && whole && p.vecc;
             for (int fi = 0; fi < FM; ++fi)
                 for (int fj = 0; fj < FN; ++fj)
                     for (int q = 0; q < 4; ++q) {
-                        const int i = ib + fi * 16 + li, j = jb + fj * 16 + acc_row<R>(lk, q);
+                        const int i = ib + pk_index<RA>(fi, li), j = jb + pk_index<RB>(fj, acc_row<R>(lk, q));
+                        if (vec && fi % RA != 0)
+                            continue;  // inside the vector of fragment fi - fi % RA
                         if (whole || (i0 + i < p.m && (rectm ? j0 + j < p.ncols : i0 + i >= j0 + j))) {
                             const int64_t full = i + (int64_t)j * p.ldc;
                             if ((int64_t)(Off)full != full) {
@@ -221,8 +226,12 @@ static bool check_syrk(const SyrkArgs &p, dim3 grid, Checker &c)
                                 return false;
                             }
                             E *dst = Ct + (Off)full;
-                            if (!c.access(dst, sizeof(E), false, kn, b, tid) ||
-                                !c.access(dst, sizeof(E), true, kn, b, tid))
+                            const size_t bytes = vec ? RA * sizeof(E) : sizeof(E);
+                            if (vec && (uintptr_t)dst % 16 != 0) {
+                                c.err = "syrk_kernel: unaligned vector access to C";
+                                return false;
+                            }
+                            if (!c.access(dst, bytes, false, kn, b, tid) || !c.access(dst, bytes, true, kn, b, tid))
                                 return false;
                         }
                     }

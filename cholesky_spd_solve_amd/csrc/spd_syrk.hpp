@@ -59,6 +59,9 @@ struct SyrkArgs {
     int krange;     // depth range of tile (I, J): SYRK_K_ALL [0, kp), SYRK_K_ROW [i0, kp),
                     // SYRK_K_BAND [j0, i0 + BM) (the operands are zero outside it)
     int add;        // 1: C += W V^H instead of C -= W V^H
+    int vecc;       // 1: C is 16-byte aligned with a leading dimension that keeps
+                    // every column so (the packed-row kernel then moves whole
+                    // tiles of C with 16-byte vectors)
     const int *info;  // if non-null and *info != 0 the kernel does nothing
 };
 
@@ -132,8 +135,31 @@ template <bool BIGLD> struct SyrkOff { typedef uint32_t type; };
 template <> struct SyrkOff<true> { typedef int64_t type; };
 constexpr int64_t SYRK_LD32 = INT64_C(1) << 24;  // leading dimensions below this use 32-bit offsets
 
-template <typename R, bool CPLX, int BM, int KB, int WM, int WN, bool BIGLD = false>
-__global__ void __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)))
+// Packed rows.  Within a wave's TM x TN block of C, fragment f (of 16 rows,
+// or of 16 columns) and lane index l (0..15) address row (column)
+//     pk_index<RP>(f, l) = (f / RP) * 16 RP + RP l + f % RP,
+// so the RP fragments f = RP g .. RP g + RP - 1 of one lane hold RP adjacent
+// rows: one 16-byte LDS read gives a lane its operands for all of them, and
+// the epilogue moves RP adjacent elements of a column of C per vector.
+// RP = 1 is the plain layout (row 16 f + l).  Only which lane holds which row
+// changes, not what is summed or in which order, so the results are the same
+// bits for every RP.  Shared with the host-side launch validator.
+template <int RP>
+__host__ __device__ inline int pk_index(int f, int l)
+{
+    return (f / RP) * 16 * RP + RP * l + f % RP;
+}
+
+// Rows per 16-byte operand read: RP adjacent rows of W fill one vector, up to
+// the number of fragments.
+template <typename R, bool PK, int F>
+struct SyrkPack {
+    static constexpr int V = (int)(16 / sizeof(R));
+    static constexpr int value = !PK ? 1 : (V < F ? V : F);
+};
+
+template <typename R, bool CPLX, int BM, int KB, int WM, int WN, bool BIGLD = false, bool PK = false>
+__global__ void __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(PK ? 4 : 2)))
 syrk_kernel(const SyrkArgs p)
 {
     typedef typename SyrkOff<BIGLD>::type Off;
@@ -147,9 +173,12 @@ syrk_kernel(const SyrkArgs p)
     constexpr int V = LD::V, L = LD::L;
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
     static_assert(KB % 4 == 0, "KB must be a multiple of 4");
+    static_assert(!(PK && CPLX), "packed rows are for real types");
+    constexpr int RA = SyrkPack<R, PK, FM>::value, RB = SyrkPack<R, PK, FN>::value;
+    static_assert(FM % RA == 0 && FN % RB == 0, "fragments do not pack");
 
-    __shared__ R As[2][NP][KB][BM];  // As[.][.][k][r] = W(i0 + r, k0 + k)
-    __shared__ R Bs[2][NP][KB][BM];  // Bs[.][.][k][r] = conj(W(j0 + r, k0 + k))
+    __shared__ __align__(16) R As[2][NP][KB][BM];  // As[.][.][k][r] = W(i0 + r, k0 + k)
+    __shared__ __align__(16) R Bs[2][NP][KB][BM];  // Bs[.][.][k][r] = conj(W(j0 + r, k0 + k))
 
     int I, J;
     syrk_tile(p, (int)blockIdx.x, I, J);
@@ -255,14 +284,33 @@ syrk_kernel(const SyrkArgs p)
         // are issued, so the LDS latency hides behind them.
         R fa[2][NP][FM], fb[2][NP][FN];
         auto frag = [&](int kr, R (&a)[NP][FM], R (&b)[NP][FN]) {
+            if constexpr (RA > 1 || RB > 1) {
+                typedef R va __attribute__((ext_vector_type(RA)));
+                typedef R vb __attribute__((ext_vector_type(RB)));
 #pragma unroll
-            for (int c = 0; c < NP; ++c) {
+                for (int g = 0; g < FM / RA; ++g) {
+                    const va x = *(const va *)&As[cur][0][kr][ib + pk_index<RA>(g * RA, li)];
 #pragma unroll
-                for (int fi = 0; fi < FM; ++fi)
-                    a[c][fi] = As[cur][c][kr][ib + fi * 16 + li];
+                    for (int u = 0; u < RA; ++u)
+                        a[0][g * RA + u] = x[u];
+                }
 #pragma unroll
-                for (int fj = 0; fj < FN; ++fj)
-                    b[c][fj] = Bs[cur][c][kr][jb + fj * 16 + li];
+                for (int g = 0; g < FN / RB; ++g) {
+                    const vb y = *(const vb *)&Bs[cur][0][kr][jb + pk_index<RB>(g * RB, li)];
+#pragma unroll
+                    for (int u = 0; u < RB; ++u)
+                        b[0][g * RB + u] = y[u];
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < NP; ++c) {
+#pragma unroll
+                    for (int fi = 0; fi < FM; ++fi)
+                        a[c][fi] = As[cur][c][kr][ib + fi * 16 + li];
+#pragma unroll
+                    for (int fj = 0; fj < FN; ++fj)
+                        b[c][fj] = Bs[cur][c][kr][jb + fj * 16 + li];
+                }
             }
         };
         frag(lk, fa[0], fb[0]);
@@ -300,16 +348,45 @@ syrk_kernel(const SyrkArgs p)
     const bool rectm = p.ncols > 0;
     const bool whole = rectm ? (i0 + BM <= p.m && j0 + BM <= p.ncols)
                              : ((I != J) && (i0 + BM <= p.m));  // every element of the tile is updated
+    if constexpr (RA > 1) {
+        if (whole && p.vecc) {
+            // RA adjacent rows of one column of C per 16-byte vector
+            typedef R va __attribute__((ext_vector_type(RA)));
+#pragma unroll
+            for (int g = 0; g < FM / RA; ++g) {
+                const int i = ib + pk_index<RA>(g * RA, li);
+#pragma unroll
+                for (int fj = 0; fj < FN; ++fj) {
+                    va cv[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int j = jb + pk_index<RB>(fj, acc_row<R>(lk, q));
+                        cv[q] = *(const va *)(Ct + (Off)(i + (int64_t)j * p.ldc));
+                    }
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int j = jb + pk_index<RB>(fj, acc_row<R>(lk, q));
+                        va o;
+#pragma unroll
+                        for (int u = 0; u < RA; ++u)
+                            o[u] = fma_r(sg, acc[0][g * RA + u][fj][q], cv[q][u]);
+                        *(va *)(Ct + (Off)(i + (int64_t)j * p.ldc)) = o;
+                    }
+                }
+            }
+            return;
+        }
+    }
 #pragma unroll
     for (int fi = 0; fi < FM; ++fi) {
-        const int i = ib + fi * 16 + li;
+        const int i = ib + pk_index<RA>(fi, li);
         R cr[FN][4], ci[FN][4];
         if (whole) {
 #pragma unroll
             for (int fj = 0; fj < FN; ++fj)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int j = jb + fj * 16 + acc_row<R>(lk, q);
+                    const int j = jb + pk_index<RB>(fj, acc_row<R>(lk, q));
                     ci[fj][q] = 0;
                     Elem<R, CPLX>::load(Ct + (Off)(i + (int64_t)j * p.ldc), cr[fj][q], ci[fj][q]);
                 }
@@ -317,7 +394,7 @@ syrk_kernel(const SyrkArgs p)
             for (int fj = 0; fj < FN; ++fj)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int j = jb + fj * 16 + acc_row<R>(lk, q);
+                    const int j = jb + pk_index<RB>(fj, acc_row<R>(lk, q));
                     Elem<R, CPLX>::store(Ct + (Off)(i + (int64_t)j * p.ldc),
                                          fma_r(sg, acc[0][fi][fj][q], cr[fj][q]),
                                          CPLX ? fma_r(sg, acc[NP - 1][fi][fj][q], ci[fj][q]) : R(0));
@@ -327,7 +404,7 @@ syrk_kernel(const SyrkArgs p)
             for (int fj = 0; fj < FN; ++fj)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int j = jb + fj * 16 + acc_row<R>(lk, q);
+                    const int j = jb + pk_index<RB>(fj, acc_row<R>(lk, q));
                     if (i0 + i < p.m && (rectm ? j0 + j < p.ncols : i0 + i >= j0 + j)) {
                         E *dst = Ct + (Off)(i + (int64_t)j * p.ldc);
                         R xr, xi = 0;
