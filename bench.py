@@ -58,7 +58,7 @@ HBM_PEAK_GBS = 8000.0
 # (profiles/counters_syrk_f64_n32768_t512.md).  Valid for the trailing-update
 # kernels and schedule as they were when the counters were taken; emptied when
 # they change.
-SYRK_TRAFFIC_BYTES = {("f64", 32768, 512, "posv"): 8.931e9}
+SYRK_TRAFFIC_BYTES = {("f64", 32768, 512, "posv"): 8.926e9}
 
 
 def parse():
@@ -211,6 +211,19 @@ def main():
                        "achieved": (aux_flops / aux_launches) / (aux_avg_ms * 1e-3) / 1e12 if aux_launches else None,
                        "flop_share": aux_flops / max(aux_flops + syrk_flops, 1.0)},
     }
+
+    if mode == "posv" and not args.no_phases:
+        # the same trailing-update kernel with nothing beside it: the
+        # sequential schedule (every launch in order on the caller's stream),
+        # its launches timed by the same events
+        with spd.options({spd.OPT_LOOKAHEAD: 0}):
+            seq = solve_loop(spd, bufs, cfg, "three", 2, 1, True, "sequential schedule")
+        s_ms, s_launches, s_flops = seq["syrk"]
+        s_avg = s_ms / max(s_launches, 1)
+        s_ach = (s_flops / s_launches) / (s_avg * 1e-3) / 1e12 if s_launches else None
+        roofline["alone"] = {"schedule": "sequential (SPD_OPT_LOOKAHEAD = 0): no launch shares the GPU",
+                             "achieved": s_ach, "frac": (s_ach / peak) if s_ach else None, "launches": s_launches,
+                             "avg_launch_ms": s_avg, "potrf_ms": float(np.mean(seq["potrf_ms"]))}
 
     others = None
     if not gp and args.config == 5 and not args.no_configs:
