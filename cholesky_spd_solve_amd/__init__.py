@@ -361,9 +361,14 @@ class options:
         self.saved = {}
 
     def __enter__(self):
-        for k, v in self.values.items():
-            self.saved[k] = get_option(k)
-            set_option(k, v)
+        try:
+            for k, v in self.values.items():
+                prev = get_option(k)
+                set_option(k, v)
+                self.saved[k] = prev
+        except BaseException:
+            self.__exit__()
+            raise
         return self
 
     def __exit__(self, *exc):

@@ -179,6 +179,12 @@ def test_options_validate_and_restore(lib):
         assert spd.get_option(spd.OPT_RECT_TALL_ROWS) == 7
     for k, v in defaults.items():
         assert spd.get_option(k) == v
+    # a rejected value inside the block leaves every option as it was
+    with pytest.raises(ValueError, match="argument 2"):
+        with spd.options({spd.OPT_PAIR_ROWS: 0, spd.OPT_LOOKAHEAD: 5}):
+            pass
+    for k, v in defaults.items():
+        assert spd.get_option(k) == v
     spd.set_option(spd.OPT_SYRK_DEEP_ROWS, 5)
     spd.set_option(spd.OPT_SYRK_DEEP_ROWS, spd.OPT_DEFAULT)
     assert spd.get_option(spd.OPT_SYRK_DEEP_ROWS) == -1
