@@ -142,10 +142,11 @@ int spd_posv(spd_dtype_t dt, int64_t n, int64_t n_rhs, void *dA, int64_t lda, vo
  *     enqueued; 64 MiB covers, e.g., fp64 n = 4096 with T_A = 256 and up to
  *     128 right-hand sides.
  *   - The call allocates nothing (no hipMalloc, no library routine that
- *     allocates) and creates no stream or event: every kernel runs in order
- *     on `stream` (the sequential schedule), on the current device, whose
- *     copy of the buffer it uses.  The first call on a device looks up that
- *     copy's address once.
+ *     allocates) and creates no stream or event (while spd_profile_enable's
+ *     kernel timing is off; that timing records events): every kernel runs in
+ *     order on `stream` (the sequential schedule), on the current device,
+ *     whose copy of the buffer it uses.  The first call on a device looks up
+ *     that copy's address once.
  *   - Every call on one device shares that device's buffer, which keeps the
  *     previous call's contents; the call initialises what it needs.  Calls
  *     that overlap on one device (on different streams, or from different
