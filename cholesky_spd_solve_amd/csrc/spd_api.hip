@@ -31,6 +31,7 @@
 #include "spd_kernels.hpp"
 #include "spd_rect.hpp"
 #include "spd_syrk.hpp"
+#include "spd_tile.hpp"
 #include "spd_check.hpp"
 
 namespace spd {
@@ -260,7 +261,7 @@ static int set_info(int *info, hipStream_t s)
 //                 L21 of four consecutive steps (potrf) / merge temporaries (both)
 //            TMP  max(T*T, T*n_rhs)   one block row of the right-hand side
 struct Layout {
-    int64_t T, nt, inv, w, wsz, tmp, ctr, q, ldq, kq, qsz, gf, gb, part, total;  // offsets / sizes in elements
+    int64_t T, nt, inv, w, wsz, tmp, ctr, flags, q, ldq, kq, qsz, gf, gb, part, total;  // offsets / sizes in elements
 };
 
 // The trailing-update panel W is stored with its leading dimension rounded up
@@ -276,6 +277,10 @@ constexpr int64_t RECT_KB = 32;    // multiple of every block-update slice depth
 // products (two operand pairs, each split along its depth).
 constexpr int64_t CHAIN_SPLITS = 8;
 
+// The one-launch diagonal tile's flags start 256 bytes after the leaf + panel
+// counter (Layout::flags)
+static int *tile_flags(int *ctr) { return ctr + 256 / sizeof(int); }
+
 static Layout make_layout(int64_t n, int64_t n_rhs, int64_t T_A, int64_t esize)
 {
     Layout L;
@@ -286,9 +291,11 @@ static Layout make_layout(int64_t n, int64_t n_rhs, int64_t T_A, int64_t esize)
     L.w = align_up(L.nt * L.T * L.T, al);
     L.wsz = align_up(align_up(n, SYRK_LDW) * align_up(L.T, SYRK_KP), al);
     L.tmp = L.w + 4 * L.wsz;  // four panel buffers: two steps in use, two being built
-    // ctr: the fused leaf + panel launch's workgroup counter (one int)
+    // ctr: the fused leaf + panel launch's workgroup counter (one int);
+    // flags: the one-launch diagonal tile's block flags and counter
     L.ctr = L.tmp + align_up(std::max(L.T * L.T, L.T * std::max<int64_t>(n_rhs, 1)), al);
-    L.q = L.ctr + al;
+    L.flags = L.ctr + al;
+    L.q = L.flags + align_up(cdiv(4 * (int64_t)tile_flag_ints((int)cdiv(L.T, LEAF)), esize), al);
     L.ldq = align_up(n_rhs, RECT_LDQ);
     L.kq = align_up(L.T, RECT_KB);
     L.qsz = L.ldq * L.kq;  // two buffers, adjacent
@@ -381,13 +388,22 @@ static GstLayout make_gst_layout(int itype, int64_t n, int64_t T_A, int64_t esiz
 // call sees one consistent set whatever other threads change meanwhile.  They
 // select among schedules and tile shapes that compute the same factorization
 // and solve; results agree with each other within rounding.
-enum { OPT_LOOKAHEAD, OPT_TWO_STEP, OPT_PAIR_ROWS, OPT_SYRK_DEEP_ROWS, OPT_RECT_TALL_ROWS, OPT_COUNT };
-static const int64_t k_opt_default[OPT_COUNT] = {1, 1, -1, -1, 16384};
-static std::atomic<int64_t> g_opt_store[OPT_COUNT] = {{1}, {1}, {-1}, {-1}, {16384}};
+enum {
+    OPT_LOOKAHEAD,
+    OPT_TWO_STEP,
+    OPT_PAIR_ROWS,
+    OPT_SYRK_DEEP_ROWS,
+    OPT_RECT_TALL_ROWS,
+    OPT_TILE_LAUNCH,
+    OPT_TILE_WAIT_US,
+    OPT_COUNT
+};
+static const int64_t k_opt_default[OPT_COUNT] = {1, 1, -1, -1, 16384, 1, 2000000};
+static std::atomic<int64_t> g_opt_store[OPT_COUNT] = {{1}, {1}, {-1}, {-1}, {16384}, {1}, {2000000}};
 struct Options {
     int64_t v[OPT_COUNT];
 };
-static thread_local Options g_opt = {{1, 1, -1, -1, 16384}};
+static thread_local Options g_opt = {{1, 1, -1, -1, 16384, 1, 2000000}};
 
 static void snapshot_options()
 {
@@ -424,6 +440,13 @@ static int64_t syrk_deep_rows(int64_t esize)
 // Block-update heights from which the substitutions (and the factorization's
 // panel product) take 64-row tiles.
 static int64_t rect_tall_rows() { return g_opt.v[OPT_RECT_TALL_ROWS]; }
+
+// Each diagonal tile of a real factorization is factored and inverted in one
+// launch (tile_kernel) unless SPD_OPT_TILE_LAUNCH is 0 (then by the leaf,
+// in-tile update and inverse-merge launches); SPD_OPT_TILE_WAIT_US bounds each
+// of that kernel's waits for another workgroup's block.
+static bool tile_launch_enabled() { return g_opt.v[OPT_TILE_LAUNCH] != 0; }
+static int64_t tile_wait_ticks() { return g_opt.v[OPT_TILE_WAIT_US] * 100; }  // 100 MHz wall clock
 
 // The auxiliary streams and events of the lookahead schedules: one set per
 // host thread and device, created on first use and kept until spd_release is
@@ -697,6 +720,34 @@ struct Solver {
         return 0;
     }
 
+    // Factor the tk x tk diagonal tile at D and write inv(L_kk) to Inv (ld
+    // ldi) in one launch (tile_kernel; real types)
+    static int tile_launch(E *D, int64_t lda, int64_t tk, E *Inv, int64_t ldi, int *info, int *flags, int64_t col0,
+                           hipStream_t s)
+    {
+        if constexpr (CPLX) {
+            g_last_error = "the one-launch diagonal tile takes real types";
+            return SPD_ERR_HIP;
+        } else {
+            TileArgs p;
+            p.D = D;
+            p.lda = lda;
+            p.Inv = Inv;
+            p.ldi = ldi;
+            p.tk = (int)tk;
+            p.nb = (int)cdiv(tk, LEAF);
+            p.flags = flags;
+            p.info = info;
+            p.col0 = (int)col0;
+            p.limit = tile_wait_ticks();
+            const unsigned grid = (unsigned)tile_groups(p.nb);
+            SPD_VALIDATE((check_tile<R>(p, grid, g_chk)));
+            tile_kernel<R><<<dim3(grid), dim3(256), 0, s>>>(p);
+            SPD_CHECK_LAUNCH("tile_kernel");
+            return 0;
+        }
+    }
+
     static constexpr int64_t syrk_bm() { return CPLX ? 64 : 128; }
 
     // Lower triangle of C (m x m, ldc) -= W W^H with W as laid out above; with
@@ -931,7 +982,10 @@ struct Solver {
     {
         const int64_t tk = std::min(T, n - c0);
         E *D = A + c0 + c0 * lda;
-        {
+        if (!CPLX && tile_launch_enabled()) {
+            ProfScope ps(PROF_DIAG, FMUL * 2.0 * (double)tk * tk * tk / 3.0, s);
+            SPD_TRY(tile_launch(D, lda, tk, Inv, T, info, tile_flags(ctr), c0, s));
+        } else {
             ProfScope ps(PROF_DIAG, FMUL * 2.0 * (double)tk * tk * tk / 3.0, s);
             for (int64_t b0 = 0; b0 < tk; b0 += LEAF) {
                 const int64_t lb = std::min<int64_t>(LEAF, tk - b0);
@@ -1041,6 +1095,7 @@ struct Solver {
         E *Inv = (E *)work + L.inv;  // inverse of the current diagonal tile, ld T
         int *ctr = (int *)((E *)work + L.ctr);
         SPD_TRY(set_info(ctr, s));
+        SPD_TRY(zero2d<int>(tile_flags(ctr), 1, tile_flag_ints((int)cdiv(T, LEAF)), 1, s));
         E *Wb[2] = {(E *)work + L.w, (E *)work + L.w + L.wsz};
         SPD_TRY(zero2d<E>(Inv, T, T, hook != nullptr ? nt * T : T, s));
         if (hook != nullptr && !two_step_schedule(T, nt)) {
@@ -2360,6 +2415,7 @@ int spd_set_option(spd_option_t opt, int64_t value)
     switch (i) {
     case OPT_LOOKAHEAD:
     case OPT_TWO_STEP:
+    case OPT_TILE_LAUNCH:
         if (value != 0 && value != 1)
             return -2;
         break;

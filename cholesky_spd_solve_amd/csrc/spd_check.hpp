@@ -27,6 +27,7 @@
 #include "spd_kernels.hpp"
 #include "spd_rect.hpp"
 #include "spd_syrk.hpp"
+#include "spd_tile.hpp"
 
 namespace spd {
 
@@ -365,6 +366,121 @@ static bool check_leaf(const LeafArgs &p, unsigned grid, Checker &c, bool panel 
                     if (!c.access(Pb + r + (int64_t)col * p.lda, sizeof(E), false, kn, g, 0) ||
                         !c.access(Pb + r + (int64_t)col * p.lda, sizeof(E), true, kn, g, 0))
                         return false;
+        }
+    }
+    return true;
+}
+
+// Replay of tile_kernel (spd_tile.hpp).  Per role, the column segments of
+// the blocks it reads and writes (each segment one contiguous access), the
+// flags it waits for and raises, and the order: every flag a workgroup waits
+// for must be raised by exactly one workgroup of a smaller id (so that waits
+// only ever point back to workgroups dispatched before them).
+template <typename R>
+static bool check_tile(const TileArgs &p, unsigned grid, Checker &c)
+{
+    const char *kn = "tile_kernel";
+    const int nb = p.nb;
+    if (nb < 1 || nb * LEAF < p.tk || (nb - 1) * LEAF >= p.tk || grid != (unsigned)tile_groups(nb)) {
+        c.err = "tile_kernel: block count does not match the tile order";
+        return false;
+    }
+    if (p.info != nullptr && !c.access(p.info, 4, true, kn, 0, 0))
+        return false;
+    const int nflags = tile_flag_ints(nb);
+    if (!c.access(p.flags, 4 * (size_t)nflags, true, kn, 0, 0))
+        return false;
+    // producer of every flag: L blocks at i nb + j, inverse blocks at nb^2 + i nb + b
+    std::vector<int> prod(2 * nb * nb, -1);
+    auto raise = [&](int f, int g) {
+        if (prod[f] >= 0) {
+            c.err = "tile_kernel: a flag is raised by two workgroups";
+            return false;
+        }
+        prod[f] = g;
+        return true;
+    };
+    for (unsigned g = 0; g < grid; ++g) {
+        int i, j;
+        const int kind = tile_role(nb, (int)g, i, j);
+        if (kind == TILE_D) {
+            if (j > 0 && !raise(i * nb + j - 1, (int)g))
+                return false;
+            if (!raise(i * nb + i, (int)g))
+                return false;
+        } else if (kind == TILE_O) {
+            if (!raise(i * nb + j, (int)g))
+                return false;
+        } else if (kind == TILE_X) {
+            if (!raise(nb * nb + i * nb + j, (int)g))
+                return false;
+        } else {
+            c.err = "tile_kernel: a workgroup without a role";
+            return false;
+        }
+    }
+    const R *A = (const R *)p.D, *Iv = (const R *)p.Inv;
+    auto nrows = [&](int b) { return std::min(LEAF, p.tk - b * LEAF); };
+    // columns [0, nc) of block (bi, bj) of M (ld), rows [0, nr) (lower: rows >= column)
+    auto blk = [&](const R *M, int64_t ld, int bi, int bj, int nr, int nc, bool lower, bool write, unsigned g) {
+        for (int col = 0; col < nc; ++col) {
+            const int r0 = lower ? col : 0;
+            if (r0 >= nr)
+                continue;
+            const R *e = M + (int64_t)bi * LEAF + r0 + ((int64_t)bj * LEAF + col) * ld;
+            if (!c.access(e, sizeof(R) * (size_t)(nr - r0), write, kn, g, 0))
+                return false;
+        }
+        return true;
+    };
+    auto waits = [&](unsigned g, int f) {
+        if (f < 0 || f >= 2 * nb * nb || prod[f] < 0 || prod[f] >= (int)g) {
+            char buf[160];
+            snprintf(buf, sizeof buf, "tile_kernel: workgroup %u waits for flag %d, raised by workgroup %d", g, f,
+                     (f >= 0 && f < 2 * nb * nb) ? prod[f] : -2);
+            c.err = buf;
+            return false;
+        }
+        return true;
+    };
+    for (unsigned g = 0; g < grid; ++g) {
+        int i, j;
+        const int kind = tile_role(nb, (int)g, i, j);
+        const int nr = nrows(i);
+        if (kind == TILE_D) {
+            if (!blk(A, p.lda, j, j, nr, nr, true, false, g) || !blk(A, p.lda, j, j, nr, nr, true, true, g) ||
+                !blk(Iv, p.ldi, j, j, nr, nr, false, true, g))
+                return false;
+            if (j > 0) {
+                if (!blk(A, p.lda, j, j - 1, nr, LEAF, false, false, g) ||
+                    !blk(A, p.lda, j, j - 1, nr, LEAF, false, true, g) || !waits(g, (j - 1) * nb + j - 1) ||
+                    !blk(Iv, p.ldi, j - 1, j - 1, LEAF, LEAF, true, false, g))
+                    return false;
+            }
+            for (int l = 0; l + 1 < j; ++l)
+                if (!waits(g, j * nb + l) || !waits(g, (j - 1) * nb + l) ||
+                    !blk(A, p.lda, j, l, nr, LEAF, false, false, g) ||
+                    !blk(A, p.lda, j - 1, l, LEAF, LEAF, false, false, g))
+                    return false;
+        } else if (kind == TILE_O) {
+            if (!blk(A, p.lda, i, j, nr, LEAF, false, false, g) || !blk(A, p.lda, i, j, nr, LEAF, false, true, g) ||
+                !waits(g, j * nb + j) || !blk(Iv, p.ldi, j, j, LEAF, LEAF, true, false, g))
+                return false;
+            for (int l = 0; l < j; ++l)
+                if (!waits(g, i * nb + l) || !waits(g, j * nb + l) ||
+                    !blk(A, p.lda, i, l, nr, LEAF, false, false, g) ||
+                    !blk(A, p.lda, j, l, LEAF, LEAF, false, false, g))
+                    return false;
+        } else {
+            const int b = j;
+            if (!waits(g, i * nb + i) || !blk(Iv, p.ldi, i, i, nr, nr, true, false, g) ||
+                !blk(Iv, p.ldi, i, b, nr, LEAF, false, true, g))
+                return false;
+            for (int k = b; k < i; ++k)
+                if (!waits(g, i * nb + k) || !waits(g, k == b ? b * nb + b : nb * nb + k * nb + b) ||
+                    !blk(A, p.lda, i, k, nr, LEAF, false, false, g) ||
+                    !blk(Iv, p.ldi, k, b, LEAF, LEAF, k == b, false, g))
+                    return false;
         }
     }
     return true;

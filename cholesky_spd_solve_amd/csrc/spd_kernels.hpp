@@ -269,6 +269,91 @@ __device__ void diag16(R (*S)[LDL], R (*X)[LDL], int o, int lb, int gcol, int *i
     }
 }
 
+// Factor (factor) and invert, or only invert, the 64 x 64 block held in S
+// (S[c][r] = element (r, c); lower triangle read; identity beyond lb): L
+// goes back to S (zeros above the diagonal), inv(L) to X, which must hold
+// zeros on entry.  All 256 threads of the workgroup take part (wave 0 sweeps
+// the 16 x 16 diagonal blocks, the four waves share the 16 x 16 products);
+// the block is in S and X and *failed is 0 before the call (with a barrier
+// after the stores), and the results are there after it.  A pivot that is
+// not > 0 records info at column gcol + its index (columns < lb only) and
+// sets *failed.
+template <typename R>
+__device__ __forceinline__ void leaf_lds(R (*S)[LDL], R (*X)[LDL], R (*Tm)[LB16][LB16 + 1], bool factor, int lb,
+                                         int gcol, int *info, int *failed)
+{
+    typedef typename AccT<R>::type V4;
+    constexpr int NB = LEAF / LB16;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int li = lane & 15, lk = lane >> 4;
+    // store the 16 x 16 accumulator block (lane layout of mma16) at (ro, co)
+    // of M, scaled by sg; lower part only when low
+    auto put = [&](R (*M)[LDL], int ro, int co, const V4 &acc, R sg, bool low) {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+            const int rr = li, cc = acc_row<R>(lk, qq);
+            if (!low || rr >= cc)
+                M[co + cc][ro + rr] = sg * acc[qq];
+        }
+    };
+
+    for (int b = 0; b < NB; ++b) {
+        const int o = b * LB16;
+        if (wave == 0) {
+            if (factor)
+                diag16<R, true>(S, X, o, lb, gcol, info, failed);
+            else
+                diag16<R, false>(S, X, o, lb, gcol, info, failed);
+        }
+        __syncthreads();
+        if (factor) {
+            // L(i, b) = A(i, b) inv(L(b, b))^T, one block per wave
+            const int i = b + 1 + wave;
+            if (i < NB) {
+                V4 acc = {0, 0, 0, 0};
+                acc = mma16<R>(&S[o][i * LB16], LDL, 1, &X[o][o], LDL, 1, acc);
+                put(S, i * LB16, o, acc, R(1), false);
+            }
+            __syncthreads();
+            // A(i, j) -= L(i, b) L(j, b)^T, b < j <= i
+            for (int t = wave; t < (NB - 1 - b) * (NB - b) / 2; t += 4) {
+                int ti, tj;
+                tri_index(t, ti, tj);
+                const int i2 = b + 1 + ti, j2 = b + 1 + tj;
+                V4 acc = {0, 0, 0, 0};
+                acc = mma16<R>(&S[o][i2 * LB16], LDL, 1, &S[o][j2 * LB16], LDL, 1, acc);
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    const int rr = li, cc = acc_row<R>(lk, qq);
+                    if (i2 != j2 || rr >= cc)
+                        S[j2 * LB16 + cc][i2 * LB16 + rr] -= acc[qq];
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    // inverse off-diagonal blocks, by distance d = i - b
+    for (int d = 1; d < NB; ++d) {
+        const int b = wave, i = b + d;
+        if (i < NB) {
+            V4 acc = {0, 0, 0, 0};
+            for (int k = b; k < i; ++k)  // T = sum_k L(i, k) X(k, b)
+                acc = mma16<R>(&S[k * LB16][i * LB16], LDL, 1, &X[b * LB16][k * LB16], 1, LDL, acc);
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq)
+                Tm[wave][acc_row<R>(lk, qq)][li] = acc[qq];  // Tm[c][r] = T(r, c)
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's LDS stores done before reading them back
+            __builtin_amdgcn_wave_barrier();
+            V4 acc2 = {0, 0, 0, 0};  // X(i, b) = -inv(L(i, i)) T
+            acc2 = mma16<R>(&X[i * LB16][i * LB16], LDL, 1, &Tm[wave][0][0], 1, LB16 + 1, acc2);
+            put(X, i * LB16, b * LB16, acc2, R(-1), false);
+        }
+        __syncthreads();
+    }
+
+}
+
 // At most 256 registers per lane, so that a leaf fits in the registers one
 // finishing trailing-update workgroup gives back.
 //
@@ -331,71 +416,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) l
         failed = 0;
     __syncthreads();
 
-    // store the 16 x 16 accumulator block (lane layout of mma16) at (ro, co)
-    // of M, scaled by sg; lower part only when low
-    auto put = [&](R (*M)[LDL], int ro, int co, const V4 &acc, R sg, bool low) {
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-            const int rr = li, cc = acc_row<R>(lk, qq);
-            if (!low || rr >= cc)
-                M[co + cc][ro + rr] = sg * acc[qq];
-        }
-    };
-
-    for (int b = 0; b < NB; ++b) {
-        const int o = b * LB16;
-        if (wave == 0) {
-            if (p.factor)
-                diag16<R, true>(S, X, o, lb, p.col0 + (int)c0, info, &failed);
-            else
-                diag16<R, false>(S, X, o, lb, p.col0 + (int)c0, info, &failed);
-        }
-        __syncthreads();
-        if (p.factor) {
-            // L(i, b) = A(i, b) inv(L(b, b))^T, one block per wave
-            const int i = b + 1 + wave;
-            if (i < NB) {
-                V4 acc = {0, 0, 0, 0};
-                acc = mma16<R>(&S[o][i * LB16], LDL, 1, &X[o][o], LDL, 1, acc);
-                put(S, i * LB16, o, acc, R(1), false);
-            }
-            __syncthreads();
-            // A(i, j) -= L(i, b) L(j, b)^T, b < j <= i
-            for (int t = wave; t < (NB - 1 - b) * (NB - b) / 2; t += 4) {
-                int ti, tj;
-                tri_index(t, ti, tj);
-                const int i2 = b + 1 + ti, j2 = b + 1 + tj;
-                V4 acc = {0, 0, 0, 0};
-                acc = mma16<R>(&S[o][i2 * LB16], LDL, 1, &S[o][j2 * LB16], LDL, 1, acc);
-#pragma unroll
-                for (int qq = 0; qq < 4; ++qq) {
-                    const int rr = li, cc = acc_row<R>(lk, qq);
-                    if (i2 != j2 || rr >= cc)
-                        S[j2 * LB16 + cc][i2 * LB16 + rr] -= acc[qq];
-                }
-            }
-            __syncthreads();
-        }
-    }
-
-    // inverse off-diagonal blocks, by distance d = i - b
-    for (int d = 1; d < NB; ++d) {
-        const int b = wave, i = b + d;
-        if (i < NB) {
-            V4 acc = {0, 0, 0, 0};
-            for (int k = b; k < i; ++k)  // T = sum_k L(i, k) X(k, b)
-                acc = mma16<R>(&S[k * LB16][i * LB16], LDL, 1, &X[b * LB16][k * LB16], 1, LDL, acc);
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq)
-                Tm[wave][acc_row<R>(lk, qq)][li] = acc[qq];  // Tm[c][r] = T(r, c)
-            __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's LDS stores done before reading them back
-            __builtin_amdgcn_wave_barrier();
-            V4 acc2 = {0, 0, 0, 0};  // X(i, b) = -inv(L(i, i)) T
-            acc2 = mma16<R>(&X[i * LB16][i * LB16], LDL, 1, &Tm[wave][0][0], 1, LB16 + 1, acc2);
-            put(X, i * LB16, b * LB16, acc2, R(-1), false);
-        }
-        __syncthreads();
-    }
+    leaf_lds<R>(S, X, Tm, p.factor != 0, lb, p.col0 + (int)c0, info, &failed);
 
     if (failed)
         return;

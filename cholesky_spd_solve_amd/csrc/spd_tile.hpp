@@ -1,0 +1,399 @@
+// The diagonal tile of the blocked Cholesky factorization in one launch, real
+// types: A_kk = L_kk L_kk^T and inv(L_kk) (JAXMg paper, "Software design":
+// step 1 of each tile of potrf, and the tile inverses that the panel solve and
+// the substitutions apply).
+//
+// The tile (order tk <= T) is cut into nb = ceil(tk / 64) block rows and
+// columns.  Every 64 x 64 block of the lower triangle of L, and every block
+// below the diagonal of inv(L_kk), is computed by a workgroup of its own
+// (left-looking, so each block is written once):
+//
+//   D_j  (diagonal role, block row j):
+//        S    = A_j,j-1 - sum_{l < j-1} L_jl L_j-1,l^T
+//        L_j,j-1 = S inv(L_j-1,j-1)^T                     (published first)
+//        A'   = A_jj - sum_{l < j} L_jl L_jl^T
+//        L_jj, inv(L_jj) from A' inside LDS (the 64 x 64 leaf of the
+//        multi-kernel path, the same arithmetic)
+//   O_ij (i >= j + 2):
+//        L_ij = (A_ij - sum_{l < j} L_il L_jl^T) inv(L_jj)^T
+//   X_ib (i > b):
+//        inv(L)_ib = -inv(L_ii) sum_{b <= k < i} L_ik inv(L)_kb
+//
+// Each block has a ready flag in the workspace.  A workgroup waits for the
+// flags of the blocks it reads (its thread 0 polls with agent-scope loads,
+// then an acquire fence) and raises its own after its stores (release fence,
+// then an agent-scope store).  Workgroup ids are assigned in the order
+// D_0, O_2..nb-1,0, D_1, O_3..,1, ..., D_nb-1, then X_ib by (i, b): every
+// block a workgroup waits for belongs to a smaller id.  Workgroups are
+// dispatched in id order, so a waiting workgroup never holds back the one it
+// waits for; every wait is also bounded in time (a wait that runs out raises
+// an abort word that ends every other wait, and sets info to -1), so each
+// wave of the launch exits.  Each workgroup counts itself out at the end and
+// the last one clears the flags, so they are zero between launches.
+#pragma once
+
+#include "spd_kernels.hpp"
+
+namespace spd {
+
+struct TileArgs {
+    void *D;        // the diagonal tile: its first element, column-major, lda
+    int64_t lda;
+    void *Inv;      // inv(L_kk): first element, leading dimension ldi; blocks
+    int64_t ldi;    // below and on the diagonal written, the rest left as is
+    int tk;         // order of the tile
+    int nb;         // block rows = ceil(tk / 64)
+    int *flags;     // tile_flag_ints(nb) ints, zero between launches
+    int *info;      // first failing global column + 1 (kept if already set);
+                    // -1 if a wait ran out of time
+    int col0;       // global column of the tile's first column
+    int64_t limit;  // longest wait, in ticks of the 100 MHz wall clock
+};
+
+enum { TILE_D = 0, TILE_O = 1, TILE_X = 2 };
+
+__host__ __device__ inline int tile_groups(int nb) { return nb * nb - nb + 1; }
+// flags: L blocks (nb x nb), inverse blocks (nb x nb), the abort word and the
+// workgroup counter
+__host__ __device__ inline int tile_flag_ints(int nb) { return 2 * nb * nb + 2; }
+
+// Role of workgroup g: kind and block (i, j); -1 past the last role.
+__host__ __device__ inline int tile_role(int nb, int g, int &i, int &j)
+{
+    for (int c = 0; c < nb; ++c) {
+        if (g == 0) {
+            i = c;
+            j = c;
+            return TILE_D;
+        }
+        --g;
+        const int no = nb - c - 2 > 0 ? nb - c - 2 : 0;
+        if (g < no) {
+            i = c + 2 + g;
+            j = c;
+            return TILE_O;
+        }
+        g -= no;
+    }
+    for (int r = 1; r < nb; ++r) {
+        if (g < r) {
+            i = r;
+            j = g;
+            return TILE_X;
+        }
+        g -= r;
+    }
+    i = j = -1;
+    return -1;
+}
+
+// Thread 0 polls the flags (f2 may be null) until both are raised, the abort
+// word is raised, or the time limit passes (then it raises the abort word and
+// records info = -1 unless info is set); then the workgroup proceeds.
+__device__ inline void tile_wait(const int *f1, const int *f2, int *abort_word, int64_t limit, int *info)
+{
+    if (threadIdx.x == 0) {
+        // the poll count bounds the wait as well, should the clock not run
+        // (one poll takes well over 16 ticks: three agent-scope loads)
+        const int64_t t0 = (int64_t)wall_clock64(), max_polls = limit / 16 + 64;
+        for (int64_t polls = 0;; ++polls) {
+            if (__hip_atomic_load(f1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0 &&
+                (f2 == nullptr || __hip_atomic_load(f2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0))
+                break;
+            if (__hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+                break;
+            if ((int64_t)wall_clock64() - t0 > limit || polls > max_polls) {
+                __hip_atomic_store(abort_word, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (info != nullptr)
+                    atomicCAS(info, 0, -1);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+}
+
+// Every wave's stores are made visible at agent scope, then thread 0 raises
+// the flag.
+__device__ inline void tile_signal(int *flag)
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (threadIdx.x == 0)
+        __hip_atomic_store(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A 64 x 64 block in flight between global memory and LDS: thread (r, g) =
+// (tid % 64, tid / 64) holds elements (r, g + 4k), k < 16.
+template <typename R>
+struct TileBlk {
+    R v[LEAF / 4];
+
+    // src(r, c) for r < nr, c < nc, zero elsewhere; lower: zero above the
+    // diagonal as well
+    __device__ __forceinline__ void load(const R *src, int64_t ld, int nr, int nc, bool lower)
+    {
+        const int r = threadIdx.x & 63, g = threadIdx.x >> 6;
+#pragma unroll
+        for (int k = 0; k < LEAF / 4; ++k) {
+            const int c = g + 4 * k;
+            v[k] = R(0);
+            if (r < nr && c < nc && (!lower || r >= c))
+                v[k] = src[r + (int64_t)c * ld];
+        }
+    }
+    __device__ __forceinline__ void put(R (*M)[LDL]) const
+    {
+        const int r = threadIdx.x & 63, g = threadIdx.x >> 6;
+#pragma unroll
+        for (int k = 0; k < LEAF / 4; ++k)
+            M[g + 4 * k][r] = v[k];
+    }
+};
+
+// This wave's 32 x 32 quadrant of a 64 x 64 block as 2 x 2 accumulators of
+// 16 x 16 (wave w: rows 32 (w % 2) .., columns 32 (w / 2) ..); accumulator
+// (a, b) element q of lane (li, lk) is (32 (w % 2) + 16 a + li,
+// 32 (w / 2) + 16 b + acc_row(lk, q)).
+template <typename R>
+struct TileQuad {
+    typedef typename AccT<R>::type V4;
+    V4 t[2][2];
+
+    __device__ __forceinline__ static int row(int a) { return 32 * ((threadIdx.x >> 6) & 1) + 16 * a + (threadIdx.x & 15); }
+    __device__ __forceinline__ static int col(int b, int q)
+    {
+        return 32 * (threadIdx.x >> 7) + 16 * b + acc_row<R>((threadIdx.x & 63) >> 4, q);
+    }
+    __device__ __forceinline__ void zero()
+    {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+                t[a][b] = V4{0, 0, 0, 0};
+    }
+    // -src(r, c) for r < nr, c < nc; diag: zero above the diagonal and -1 on
+    // the diagonal beyond nr (the identity padding of a short last block)
+    __device__ __forceinline__ void load_neg(const R *src, int64_t ld, int nr, int nc, bool diag)
+    {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int r = row(a), c = col(b, q);
+                    R x = (diag && r == c) ? R(-1) : R(0);
+                    if (r < nr && c < nc && (!diag || r >= c))
+                        x = -src[r + (int64_t)c * ld];
+                    t[a][b][q] = x;
+                }
+    }
+    __device__ __forceinline__ void to_lds(R (*M)[LDL], R sg) const
+    {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    M[col(b, q)][row(a)] = sg * t[a][b][q];
+    }
+    __device__ __forceinline__ void store(R *dst, int64_t ld, int nr, R sg) const
+    {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int r = row(a), c = col(b, q);
+                    if (r < nr)
+                        dst[r + (int64_t)c * ld] = sg * t[a][b][q];
+                }
+    }
+};
+
+// Depth ranges of a 16 x 16 product tile at (ro, co) (multiples of 16)
+enum {
+    TK_FULL = 0,     // [0, 64)
+    TK_TO_COL = 1,   // [0, co + 16): right operand X^T with X lower triangular
+    TK_FROM_COL = 2, // [co, 64): right operand lower triangular
+    TK_TO_ROW = 3,   // [0, ro + 16): left operand lower triangular
+};
+
+// Q += P B on the quadrant, P(r, k) = pa[k ak + r ar], B(k, c) = pb[k bk + c bc]
+// (both 64 x 64 in LDS); lower: only the tiles on or below the diagonal.
+template <typename R>
+__device__ __forceinline__ void tile_mma(TileQuad<R> &Q, const R *pa, int ak, int ar, const R *pb, int bk, int bc,
+                                         int kmode, bool lower)
+{
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int ro = 32 * (wave & 1) + 16 * a, co = 32 * (wave >> 1) + 16 * b;
+            if (lower && co > ro)
+                continue;
+            int k0 = 0, k1 = LEAF;
+            if (kmode == TK_TO_COL)
+                k1 = co + 16;
+            else if (kmode == TK_FROM_COL)
+                k0 = co;
+            else if (kmode == TK_TO_ROW)
+                k1 = ro + 16;
+            for (int k = k0; k < k1; k += 16)
+                Q.t[a][b] = mma16<R>(pa + k * ak + ro * ar, ak, ar, pb + k * bk + co * bc, bk, bc, Q.t[a][b]);
+        }
+}
+
+template <typename R>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) tile_kernel(const TileArgs p)
+{
+    __shared__ R S[LEAF][LDL];
+    __shared__ R X[LEAF][LDL];
+    __shared__ R Tm[4][LB16][LB16 + 1];
+    __shared__ int failed, last;
+
+    const int tid = threadIdx.x, nb = p.nb;
+    int bi, bj;
+    const int kind = tile_role(nb, (int)blockIdx.x, bi, bj);
+    R *const A = (R *)p.D;
+    R *const Iv = (R *)p.Inv;
+    int *const abort_word = p.flags + 2 * nb * nb;
+    int *const ctr = abort_word + 1;
+    auto nrows = [&](int b) { return (p.tk - b * LEAF) < LEAF ? p.tk - b * LEAF : LEAF; };
+    auto Ab = [&](int i, int j) { return A + (int64_t)i * LEAF + (int64_t)j * LEAF * p.lda; };
+    auto Xb = [&](int i, int j) { return Iv + (int64_t)i * LEAF + (int64_t)j * LEAF * p.ldi; };
+    auto fL = [&](int i, int j) { return p.flags + i * nb + j; };
+    auto fX = [&](int i, int j) { return p.flags + nb * nb + i * nb + j; };
+    auto wait = [&](const int *f1, const int *f2) { tile_wait(f1, f2, abort_word, p.limit, p.info); };
+    TileBlk<R> u, w;
+
+    if (kind == TILE_D) {
+        const int j = bi, nr = nrows(j);
+        TileQuad<R> Fd, Fs;
+        Fd.load_neg(Ab(j, j), p.lda, nr, nr, true);
+        if (j > 0)
+            Fs.load_neg(Ab(j, j - 1), p.lda, nr, LEAF, false);
+        for (int l = 0; l + 1 < j; ++l) {
+            wait(fL(j, l), fL(j - 1, l));
+            u.load(Ab(j, l), p.lda, nr, LEAF, false);
+            w.load(Ab(j - 1, l), p.lda, LEAF, LEAF, false);
+            u.put(S);
+            w.put(X);
+            __syncthreads();
+            tile_mma<R>(Fs, &S[0][0], LDL, 1, &X[0][0], LDL, 1, TK_FULL, false);
+            tile_mma<R>(Fd, &S[0][0], LDL, 1, &S[0][0], LDL, 1, TK_FULL, true);
+            __syncthreads();
+        }
+        if (j > 0) {
+            // L_j,j-1 = (A_j,j-1 - ...) inv(L_j-1,j-1)^T
+            wait(fL(j - 1, j - 1), nullptr);
+            w.load(Xb(j - 1, j - 1), p.ldi, LEAF, LEAF, true);
+            Fs.to_lds(S, R(-1));
+            w.put(X);
+            __syncthreads();
+            TileQuad<R> G;
+            G.zero();
+            tile_mma<R>(G, &S[0][0], LDL, 1, &X[0][0], LDL, 1, TK_TO_COL, false);
+            __syncthreads();
+            G.store(Ab(j, j - 1), p.lda, nr, R(1));
+            G.to_lds(S, R(1));
+            tile_signal(fL(j, j - 1));
+            tile_mma<R>(Fd, &S[0][0], LDL, 1, &S[0][0], LDL, 1, TK_FULL, true);
+            __syncthreads();
+        }
+        Fd.to_lds(S, R(-1));
+#pragma unroll
+        for (int k = 0; k < LEAF / 4; ++k)
+            X[(tid >> 6) + 4 * k][tid & 63] = R(0);
+        if (tid == 0)
+            failed = 0;
+        __syncthreads();
+        leaf_lds<R>(S, X, Tm, true, nr, p.col0 + j * LEAF, p.info, &failed);
+        {
+            const int r = tid & 63, g = tid >> 6;
+            R *const Ad = Ab(j, j);
+            R *const Xd = Xb(j, j);
+#pragma unroll
+            for (int k = 0; k < LEAF / 4; ++k) {
+                const int c = g + 4 * k;
+                if (r < nr && c < nr) {
+                    if (r >= c)
+                        Ad[r + (int64_t)c * p.lda] = S[c][r];
+                    Xd[r + (int64_t)c * p.ldi] = (r >= c) ? X[c][r] : R(0);
+                }
+            }
+        }
+        tile_signal(fL(j, j));
+    } else if (kind == TILE_O) {
+        const int i = bi, j = bj, nr = nrows(i);
+        TileQuad<R> F;
+        F.load_neg(Ab(i, j), p.lda, nr, LEAF, false);
+        for (int l = 0; l < j; ++l) {
+            wait(fL(i, l), fL(j, l));
+            u.load(Ab(i, l), p.lda, nr, LEAF, false);
+            w.load(Ab(j, l), p.lda, LEAF, LEAF, false);
+            u.put(S);
+            w.put(X);
+            __syncthreads();
+            tile_mma<R>(F, &S[0][0], LDL, 1, &X[0][0], LDL, 1, TK_FULL, false);
+            __syncthreads();
+        }
+        wait(fL(j, j), nullptr);
+        w.load(Xb(j, j), p.ldi, LEAF, LEAF, true);
+        F.to_lds(S, R(-1));
+        w.put(X);
+        __syncthreads();
+        TileQuad<R> G;
+        G.zero();
+        tile_mma<R>(G, &S[0][0], LDL, 1, &X[0][0], LDL, 1, TK_TO_COL, false);
+        G.store(Ab(i, j), p.lda, nr, R(1));
+        tile_signal(fL(i, j));
+    } else if (kind == TILE_X) {
+        const int i = bi, b = bj, nr = nrows(i);
+        TileQuad<R> G;
+        G.zero();
+        for (int k = b; k < i; ++k) {
+            wait(fL(i, k), k == b ? fL(b, b) : fX(k, b));
+            u.load(Ab(i, k), p.lda, nr, LEAF, false);
+            w.load(Xb(k, b), p.ldi, LEAF, LEAF, k == b);
+            u.put(S);
+            w.put(X);
+            __syncthreads();
+            // G += L_ik inv(L)_kb: B(k, c) = X[c][k]
+            tile_mma<R>(G, &S[0][0], LDL, 1, &X[0][0], 1, LDL, k == b ? TK_FROM_COL : TK_FULL, false);
+            __syncthreads();
+        }
+        wait(fL(i, i), nullptr);
+        w.load(Xb(i, i), p.ldi, nr, nr, true);
+        G.to_lds(S, R(1));
+        w.put(X);
+        __syncthreads();
+        // H = inv(L_ii) G: P(r, k) = X[k][r], B(k, c) = S[c][k]
+        TileQuad<R> H;
+        H.zero();
+        tile_mma<R>(H, &X[0][0], LDL, 1, &S[0][0], 1, LDL, TK_TO_ROW, false);
+        H.store(Xb(i, b), p.ldi, nr, R(-1));
+        tile_signal(fX(i, b));
+    }
+
+    // count out; the last workgroup clears the flags for the next launch
+    __syncthreads();
+    if (tid == 0)
+        last = atomicAdd(ctr, 1) == (int)gridDim.x - 1;
+    __syncthreads();
+    if (last) {
+        for (int e = tid; e < 2 * nb * nb + 1; e += blockDim.x)
+            p.flags[e] = 0;
+        if (tid == 0)
+            *ctr = 0;
+    }
+}
+
+}  // namespace spd

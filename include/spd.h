@@ -87,7 +87,8 @@ size_t spd_workspace_size(spd_dtype_t dt, int64_t n, int64_t n_rhs, int64_t T_A)
  *             the leading minor of order j is not positive definite (the pivot
  *             of column j-1 is <= 0 or NaN); then the factorization stopped
  *             there and the contents of the lower triangle from column j-1 on
- *             are unspecified
+ *             are unspecified; -1 if a wait of the one-launch diagonal tile
+ *             ran out of time (SPD_OPT_TILE_WAIT_US; the factor is unusable)
  *   d_work    device workspace of work_bytes >= spd_workspace_size(dt, n, 0, T_A)
  *             bytes (may be NULL when that size is 0)
  *   stream    hipStream_t
@@ -259,9 +260,22 @@ const char *spd_last_error(void);
  *                            panel products of at least this many rows take
  *                            64-row tiles, fewer rows 32-row tiles (default
  *                            16384)
+ *   SPD_OPT_TILE_LAUNCH      1 (default): each diagonal tile of a real
+ *                            factorization is factored and inverted in one
+ *                            launch whose workgroups hand 64 x 64 blocks to
+ *                            each other through flags in the workspace; 0: by
+ *                            a sequence of leaf, in-tile update and
+ *                            inverse-merge launches (complex types always)
+ *   SPD_OPT_TILE_WAIT_US     longest wait of that launch for another
+ *                            workgroup's block, in microseconds (default
+ *                            2000000).  A wait that runs out ends the
+ *                            launch's other waits as well and sets info to -1
+ *                            (the factor is then not usable); it exists so
+ *                            that no wave can wait forever.
  * spd_set_option returns 0, -1 for an unknown option, -2 for a value out of
- * range (LOOKAHEAD and TWO_STEP take 0 or 1, PAIR_ROWS and SYRK_DEEP_ROWS
- * >= -1, RECT_TALL_ROWS >= 0); SPD_OPT_DEFAULT restores an option's default.
+ * range (LOOKAHEAD, TWO_STEP and TILE_LAUNCH take 0 or 1, PAIR_ROWS and
+ * SYRK_DEEP_ROWS >= -1, RECT_TALL_ROWS and TILE_WAIT_US >= 0);
+ * SPD_OPT_DEFAULT restores an option's default.
  * spd_get_option returns the current value (INT64_MIN for an unknown
  * option). */
 typedef enum {
@@ -269,7 +283,9 @@ typedef enum {
     SPD_OPT_TWO_STEP = 2,
     SPD_OPT_PAIR_ROWS = 3,
     SPD_OPT_SYRK_DEEP_ROWS = 4,
-    SPD_OPT_RECT_TALL_ROWS = 5
+    SPD_OPT_RECT_TALL_ROWS = 5,
+    SPD_OPT_TILE_LAUNCH = 6,
+    SPD_OPT_TILE_WAIT_US = 7
 } spd_option_t;
 #define SPD_OPT_DEFAULT INT64_MIN
 int spd_set_option(spd_option_t opt, int64_t value);

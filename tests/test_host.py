@@ -54,22 +54,24 @@ def test_workspace_size(lib):
     assert f(1, 10, 1, 0) == 0
     assert f(9, 10, 1, 4) == 0
     # INV nt*T*T + four panels of (n rounded up to 128) x (T rounded up to 32)
-    # + TMP max(T*T, T*nrhs) + a 256-byte counter; for nrhs > 0 also two
+    # + TMP max(T*T, T*nrhs) + a 256-byte counter + the one-launch diagonal
+    # tile's 2 nb^2 + 2 int flags (nb = ceil(T / 64)) rounded up to 256 bytes
+    # (768 bytes at T = 512, 256 at T = 100); for nrhs > 0 also two
     # buffers for the transposed solved block, (nrhs rounded up to 128) x (T
     # rounded up to 32), two sets of nt*T*T chain products and 8 partial
     # T x nrhs blocks; each rounded up to 256 bytes
     n, nrhs, T = 32768, 128, 512
     el = (n // T) * T * T + 4 * n * T + T * T
     solve = 2 * 128 * 512 + 2 * (n // T) * T * T + 8 * T * nrhs
-    assert f(1, n, 0, T) == el * 8 + 256
-    assert f(1, n, nrhs, T) == (el + solve) * 8 + 256
-    assert f(3, n, nrhs, T) == (el + solve) * 16 + 256
+    assert f(1, n, 0, T) == el * 8 + 256 + 768
+    assert f(1, n, nrhs, T) == (el + solve) * 8 + 256 + 768
+    assert f(3, n, nrhs, T) == (el + solve) * 16 + 256 + 768
     n, nrhs, T = 1000, 7, 100
     up = lambda a, b: -(-a // b) * b
     el = up(10 * 100 * 100, 32) + 4 * up(1024 * 128, 32) + up(100 * 100, 32)
     solve = up(2 * 128 * 128, 32) + 2 * up(10 * 100 * 100, 32) + up(8 * 100 * 7, 32)
-    assert f(1, n, 0, T) == el * 8 + 256
-    assert f(1, n, nrhs, T) == (el + solve) * 8 + 256
+    assert f(1, n, 0, T) == el * 8 + 256 + 256
+    assert f(1, n, nrhs, T) == (el + solve) * 8 + 256 + 256
     # T_A > n is clamped to n
     assert f(1, 100, 1, 1000) == f(1, 100, 1, 100)
 
@@ -163,16 +165,18 @@ def test_options_validate_and_restore(lib):
     default marker restores each option's default."""
     import cholesky_spd_solve_amd as spd
     defaults = {spd.OPT_LOOKAHEAD: 1, spd.OPT_TWO_STEP: 1, spd.OPT_PAIR_ROWS: -1, spd.OPT_SYRK_DEEP_ROWS: -1,
-                spd.OPT_RECT_TALL_ROWS: 16384}
+                spd.OPT_RECT_TALL_ROWS: 16384, spd.OPT_TILE_LAUNCH: 1, spd.OPT_TILE_WAIT_US: 2000000}
     for k, v in defaults.items():
         assert spd.get_option(k) == v
     assert lib.spd_set_option(0, 1) == -1
-    assert lib.spd_set_option(6, 1) == -1
-    assert lib.spd_get_option(6) == -(1 << 63)
+    assert lib.spd_set_option(8, 1) == -1
+    assert lib.spd_get_option(8) == -(1 << 63)
     assert lib.spd_set_option(spd.OPT_LOOKAHEAD, 2) == -2
     assert lib.spd_set_option(spd.OPT_TWO_STEP, -1) == -2
     assert lib.spd_set_option(spd.OPT_PAIR_ROWS, -2) == -2
     assert lib.spd_set_option(spd.OPT_RECT_TALL_ROWS, -1) == -2
+    assert lib.spd_set_option(spd.OPT_TILE_LAUNCH, 2) == -2
+    assert lib.spd_set_option(spd.OPT_TILE_WAIT_US, -1) == -2
     with spd.options({spd.OPT_PAIR_ROWS: 0, spd.OPT_LOOKAHEAD: 0, spd.OPT_RECT_TALL_ROWS: 7}):
         assert spd.get_option(spd.OPT_PAIR_ROWS) == 0
         assert spd.get_option(spd.OPT_LOOKAHEAD) == 0
