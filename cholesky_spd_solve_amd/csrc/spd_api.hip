@@ -441,8 +441,8 @@ static int64_t syrk_deep_rows(int64_t esize)
 // panel product) take 64-row tiles.
 static int64_t rect_tall_rows() { return g_opt.v[OPT_RECT_TALL_ROWS]; }
 
-// Each diagonal tile of a real factorization is factored and inverted in one
-// launch (tile_kernel) unless SPD_OPT_TILE_LAUNCH is 0 (then by the leaf,
+// Each diagonal tile of the factorization is factored and inverted in one
+// launch (tile_kernel, tile_kernel_c) unless SPD_OPT_TILE_LAUNCH is 0 (then by the leaf,
 // in-tile update and inverse-merge launches); SPD_OPT_TILE_WAIT_US bounds each
 // of that kernel's waits for another workgroup's block.
 static bool tile_launch_enabled() { return g_opt.v[OPT_TILE_LAUNCH] != 0; }
@@ -721,14 +721,11 @@ struct Solver {
     }
 
     // Factor the tk x tk diagonal tile at D and write inv(L_kk) to Inv (ld
-    // ldi) in one launch (tile_kernel; real types)
+    // ldi) in one launch (tile_kernel, tile_kernel_c)
     static int tile_launch(E *D, int64_t lda, int64_t tk, E *Inv, int64_t ldi, int *info, int *flags, int64_t col0,
                            hipStream_t s)
     {
-        if constexpr (CPLX) {
-            g_last_error = "the one-launch diagonal tile takes real types";
-            return SPD_ERR_HIP;
-        } else {
+        {
             TileArgs p;
             p.D = D;
             p.lda = lda;
@@ -741,8 +738,11 @@ struct Solver {
             p.col0 = (int)col0;
             p.limit = tile_wait_ticks();
             const unsigned grid = (unsigned)tile_groups(p.nb);
-            SPD_VALIDATE((check_tile<R>(p, grid, g_chk)));
-            tile_kernel<R><<<dim3(grid), dim3(256), 0, s>>>(p);
+            SPD_VALIDATE((check_tile<R, CPLX>(p, grid, g_chk)));
+            if constexpr (CPLX)
+                tile_kernel_c<R><<<dim3(grid), dim3(256), 0, s>>>(p);
+            else
+                tile_kernel<R><<<dim3(grid), dim3(256), 0, s>>>(p);
             SPD_CHECK_LAUNCH("tile_kernel");
             return 0;
         }
@@ -982,7 +982,7 @@ struct Solver {
     {
         const int64_t tk = std::min(T, n - c0);
         E *D = A + c0 + c0 * lda;
-        if (!CPLX && tile_launch_enabled()) {
+        if (tile_launch_enabled()) {
             ProfScope ps(PROF_DIAG, FMUL * 2.0 * (double)tk * tk * tk / 3.0, s);
             SPD_TRY(tile_launch(D, lda, tk, Inv, T, info, tile_flags(ctr), c0, s));
         } else {

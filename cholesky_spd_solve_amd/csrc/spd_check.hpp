@@ -371,15 +371,17 @@ static bool check_leaf(const LeafArgs &p, unsigned grid, Checker &c, bool panel 
     return true;
 }
 
-// Replay of tile_kernel (spd_tile.hpp).  Per role, the column segments of
-// the blocks it reads and writes (each segment one contiguous access), the
+// Replay of tile_kernel / tile_kernel_c (spd_tile.hpp).  Per role, the
+// column segments of the blocks it reads (the diagonal blocks of the inverse
+// as whole squares) and writes (each segment one contiguous access), the
 // flags it waits for and raises, and the order: every flag a workgroup waits
 // for must be raised by exactly one workgroup of a smaller id (so that waits
 // only ever point back to workgroups dispatched before them).
-template <typename R>
+template <typename R, bool CPLX>
 static bool check_tile(const TileArgs &p, unsigned grid, Checker &c)
 {
-    const char *kn = "tile_kernel";
+    typedef typename Elem<R, CPLX>::type E;
+    const char *kn = CPLX ? "tile_kernel_c" : "tile_kernel";
     const int nb = p.nb;
     if (nb < 1 || nb * LEAF < p.tk || (nb - 1) * LEAF >= p.tk || grid != (unsigned)tile_groups(nb)) {
         c.err = "tile_kernel: block count does not match the tile order";
@@ -419,16 +421,16 @@ static bool check_tile(const TileArgs &p, unsigned grid, Checker &c)
             return false;
         }
     }
-    const R *A = (const R *)p.D, *Iv = (const R *)p.Inv;
+    const E *A = (const E *)p.D, *Iv = (const E *)p.Inv;
     auto nrows = [&](int b) { return std::min(LEAF, p.tk - b * LEAF); };
     // columns [0, nc) of block (bi, bj) of M (ld), rows [0, nr) (lower: rows >= column)
-    auto blk = [&](const R *M, int64_t ld, int bi, int bj, int nr, int nc, bool lower, bool write, unsigned g) {
+    auto blk = [&](const E *M, int64_t ld, int bi, int bj, int nr, int nc, bool lower, bool write, unsigned g) {
         for (int col = 0; col < nc; ++col) {
             const int r0 = lower ? col : 0;
             if (r0 >= nr)
                 continue;
-            const R *e = M + (int64_t)bi * LEAF + r0 + ((int64_t)bj * LEAF + col) * ld;
-            if (!c.access(e, sizeof(R) * (size_t)(nr - r0), write, kn, g, 0))
+            const E *e = M + (int64_t)bi * LEAF + r0 + ((int64_t)bj * LEAF + col) * ld;
+            if (!c.access(e, sizeof(E) * (size_t)(nr - r0), write, kn, g, 0))
                 return false;
         }
         return true;
@@ -454,7 +456,7 @@ static bool check_tile(const TileArgs &p, unsigned grid, Checker &c)
             if (j > 0) {
                 if (!blk(A, p.lda, j, j - 1, nr, LEAF, false, false, g) ||
                     !blk(A, p.lda, j, j - 1, nr, LEAF, false, true, g) || !waits(g, (j - 1) * nb + j - 1) ||
-                    !blk(Iv, p.ldi, j - 1, j - 1, LEAF, LEAF, true, false, g))
+                    !blk(Iv, p.ldi, j - 1, j - 1, LEAF, LEAF, false, false, g))
                     return false;
             }
             for (int l = 0; l + 1 < j; ++l)
@@ -464,7 +466,7 @@ static bool check_tile(const TileArgs &p, unsigned grid, Checker &c)
                     return false;
         } else if (kind == TILE_O) {
             if (!blk(A, p.lda, i, j, nr, LEAF, false, false, g) || !blk(A, p.lda, i, j, nr, LEAF, false, true, g) ||
-                !waits(g, j * nb + j) || !blk(Iv, p.ldi, j, j, LEAF, LEAF, true, false, g))
+                !waits(g, j * nb + j) || !blk(Iv, p.ldi, j, j, LEAF, LEAF, false, false, g))
                 return false;
             for (int l = 0; l < j; ++l)
                 if (!waits(g, i * nb + l) || !waits(g, j * nb + l) ||
@@ -473,13 +475,13 @@ static bool check_tile(const TileArgs &p, unsigned grid, Checker &c)
                     return false;
         } else {
             const int b = j;
-            if (!waits(g, i * nb + i) || !blk(Iv, p.ldi, i, i, nr, nr, true, false, g) ||
+            if (!waits(g, i * nb + i) || !blk(Iv, p.ldi, i, i, nr, nr, false, false, g) ||
                 !blk(Iv, p.ldi, i, b, nr, LEAF, false, true, g))
                 return false;
             for (int k = b; k < i; ++k)
                 if (!waits(g, i * nb + k) || !waits(g, k == b ? b * nb + b : nb * nb + k * nb + b) ||
                     !blk(A, p.lda, i, k, nr, LEAF, false, false, g) ||
-                    !blk(Iv, p.ldi, k, b, LEAF, LEAF, k == b, false, g))
+                    !blk(Iv, p.ldi, k, b, LEAF, LEAF, false, false, g))
                     return false;
         }
     }

@@ -622,61 +622,31 @@ __device__ __forceinline__ void diag16c(R (*S0)[LDL], R (*S1)[LDL], R *Xd0, R *X
     }
 }
 
-// PANEL: one launch factors a single leaf and solves the p.prows panel rows
-// below it, L(i, leaf) = A(i, leaf) inv(L_leaf)^H, as leaf16_kernel's PANEL
-// mode: every workgroup factors and inverts the leaf in its own LDS (the same
-// bits), workgroup w >= 1 multiplies rows [64(w-1), 64w) of the panel in place,
-// reading them straight into the matrix-core operand registers (no LDS), and
-// the last workgroup to count itself out on p.ctr stores L and inv(L) and
-// resets the counter.  Only workgroup 0 records info.
-template <typename R, bool PANEL = false>
-__global__ void __launch_bounds__(256) leaf16c_kernel(const LeafArgs p)
+// Element (row, col) of inv(L) kept by the complex leaf (strict lower part in
+// the upper triangle of S, the diagonal in Xd, zero above the diagonal).
+template <typename R>
+__device__ __forceinline__ void leafc_xget(const R (*S)[LEAF][LDL], const R (*Xd)[LEAF], int row, int col, R &re, R &im)
+{
+    re = row > col ? S[0][row][col] : row == col ? Xd[0][row] : R(0);
+    im = row > col ? S[1][row][col] : row == col ? Xd[1][row] : R(0);
+}
+
+// Factor (factor) and invert, or only invert, the complex 64 x 64 block held
+// in the planes S[0] + i S[1] (S*[c][r] = element (r, c); lower triangle
+// read, real diagonal; identity beyond lb): L goes to S's lower triangle,
+// inv(L) below its diagonal to S's upper triangle (transposed) and its
+// diagonal to Xd.  All 256 threads take part; the block is in S and *failed
+// is 0 before the call (with a barrier after the stores), and the results are
+// there after it.  A pivot that is not > 0 records info at column gcol + its
+// index (columns < lb only) and sets *failed.
+template <typename R>
+__device__ __forceinline__ void leafc_lds(R (*S)[LEAF][LDL], R (*Xd)[LEAF], R (*Tm)[2][LB16][LB16 + 1], bool factor,
+                                          int lb, int gcol, int *info, int *failed)
 {
     typedef typename AccT<R>::type V4;
-    typedef typename Elem<R, true>::type E;
     constexpr int NB = LEAF / LB16;
-    __shared__ R S[2][LEAF][LDL];           // L below the diagonal, inv(L) above (see above)
-    __shared__ R Xd[2][LEAF];               // diagonal of inv(L)
-    __shared__ R Tm[4][2][LB16][LB16 + 1];  // per-wave 16 x 16 scratch
-    __shared__ int failed;
-
-    int64_t c0, ioff;
-    int lb;
-    const int w = PANEL ? (int)blockIdx.x : 0;  // panel block of this workgroup (0: none)
-    if (!leaf_geom(p, PANEL ? 0 : (int)blockIdx.x, c0, lb, ioff))
-        return;
-    E *A = (E *)p.A + c0 + c0 * p.lda;
-    E *Inv = (E *)p.Inv + ioff;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int li = lane & 15, lk = lane >> 4;
-    const int r = tid & (LEAF - 1), g = tid / LEAF;
-    int *const info = (w == 0) ? p.info : nullptr;
-
-    // all loads in flight together, the status word alongside them; the
-    // diagonal's imaginary part is taken as 0 and padding beyond lb is the
-    // identity
-    R vr[LEAF / 4], vi[LEAF / 4];
-#pragma unroll
-    for (int k = 0; k < LEAF / 4; ++k) {
-        const int c = g + 4 * k;
-        vr[k] = (r == c) ? R(1) : R(0);
-        vi[k] = R(0);
-        if (r < lb && c < lb && r >= c)
-            Elem<R, true>::load(A + r + (int64_t)c * p.lda, vr[k], vi[k]);
-        if (r == c)
-            vi[k] = R(0);
-    }
-    if (p.info != nullptr && *p.info != 0)
-        return;
-#pragma unroll
-    for (int k = 0; k < LEAF / 4; ++k) {
-        S[0][g + 4 * k][r] = vr[k];
-        S[1][g + 4 * k][r] = vi[k];
-    }
-    if (tid == 0)
-        failed = 0;
-    __syncthreads();
-
     // operand fetchers: element (row, col) of L (lower triangle), of inv(L)
     // (zero above its diagonal) and of conj(inv(L))^T
     auto lget = [&](int row, int col, R &re, R &im) {
@@ -702,13 +672,13 @@ __global__ void __launch_bounds__(256) leaf16c_kernel(const LeafArgs p)
     for (int b = 0; b < NB; ++b) {
         const int o = b * LB16;
         if (wave == 0) {
-            if (p.factor)
-                diag16c<R, true>(S[0], S[1], Xd[0], Xd[1], o, lb, p.col0 + (int)c0, info, &failed);
+            if (factor)
+                diag16c<R, true>(S[0], S[1], Xd[0], Xd[1], o, lb, gcol, info, failed);
             else
-                diag16c<R, false>(S[0], S[1], Xd[0], Xd[1], o, lb, p.col0 + (int)c0, info, &failed);
+                diag16c<R, false>(S[0], S[1], Xd[0], Xd[1], o, lb, gcol, info, failed);
         }
         __syncthreads();
-        if (p.factor) {
+        if (factor) {
             // L(i, b) = A(i, b) inv(L(b, b))^H, one block per wave
             // (each wave reads and then writes only its own block of column b)
             const int i = b + 1 + wave;
@@ -775,6 +745,66 @@ __global__ void __launch_bounds__(256) leaf16c_kernel(const LeafArgs p)
         }
         __syncthreads();
     }
+
+}
+
+// PANEL: one launch factors a single leaf and solves the p.prows panel rows
+// below it, L(i, leaf) = A(i, leaf) inv(L_leaf)^H, as leaf16_kernel's PANEL
+// mode: every workgroup factors and inverts the leaf in its own LDS (the same
+// bits), workgroup w >= 1 multiplies rows [64(w-1), 64w) of the panel in place,
+// reading them straight into the matrix-core operand registers (no LDS), and
+// the last workgroup to count itself out on p.ctr stores L and inv(L) and
+// resets the counter.  Only workgroup 0 records info.
+template <typename R, bool PANEL = false>
+__global__ void __launch_bounds__(256) leaf16c_kernel(const LeafArgs p)
+{
+    typedef typename AccT<R>::type V4;
+    typedef typename Elem<R, true>::type E;
+    constexpr int NB = LEAF / LB16;
+    __shared__ R S[2][LEAF][LDL];           // L below the diagonal, inv(L) above (see above)
+    __shared__ R Xd[2][LEAF];               // diagonal of inv(L)
+    __shared__ R Tm[4][2][LB16][LB16 + 1];  // per-wave 16 x 16 scratch
+    __shared__ int failed;
+
+    int64_t c0, ioff;
+    int lb;
+    const int w = PANEL ? (int)blockIdx.x : 0;  // panel block of this workgroup (0: none)
+    if (!leaf_geom(p, PANEL ? 0 : (int)blockIdx.x, c0, lb, ioff))
+        return;
+    E *A = (E *)p.A + c0 + c0 * p.lda;
+    E *Inv = (E *)p.Inv + ioff;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int li = lane & 15, lk = lane >> 4;
+    const int r = tid & (LEAF - 1), g = tid / LEAF;
+    int *const info = (w == 0) ? p.info : nullptr;
+
+    // all loads in flight together, the status word alongside them; the
+    // diagonal's imaginary part is taken as 0 and padding beyond lb is the
+    // identity
+    R vr[LEAF / 4], vi[LEAF / 4];
+#pragma unroll
+    for (int k = 0; k < LEAF / 4; ++k) {
+        const int c = g + 4 * k;
+        vr[k] = (r == c) ? R(1) : R(0);
+        vi[k] = R(0);
+        if (r < lb && c < lb && r >= c)
+            Elem<R, true>::load(A + r + (int64_t)c * p.lda, vr[k], vi[k]);
+        if (r == c)
+            vi[k] = R(0);
+    }
+    if (p.info != nullptr && *p.info != 0)
+        return;
+#pragma unroll
+    for (int k = 0; k < LEAF / 4; ++k) {
+        S[0][g + 4 * k][r] = vr[k];
+        S[1][g + 4 * k][r] = vi[k];
+    }
+    if (tid == 0)
+        failed = 0;
+    __syncthreads();
+
+    leafc_lds<R>(S, Xd, Tm, p.factor != 0, lb, p.col0 + (int)c0, info, &failed);
+    auto xget = [&](int row, int col, R &re, R &im) { leafc_xget<R>(S, Xd, row, col, re, im); };
 
     if (failed)
         return;

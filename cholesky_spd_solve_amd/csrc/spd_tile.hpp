@@ -396,4 +396,318 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) t
     }
 }
 
+// ---------------------------------------------------------------------------
+// Complex types: the same roles, flags and order, with conjugate transposes
+// (L_ij = (A_ij - sum_l L_il L_jl^H) inv(L_jj)^H, the leaf as the complex
+// multi-kernel leaf).  The blocks other workgroups publish are read straight
+// from global memory into the matrix-core operand registers; LDS holds only
+// what a workgroup hands between its own waves (its updated block before the
+// solve product, L_j,j-1 before the diagonal update) and the leaf.
+
+template <typename R>
+struct TileQuadC {
+    typedef typename AccT<R>::type V4;
+    typedef typename Elem<R, true>::type E;
+    V4 re[2][2], im[2][2];
+
+    __device__ __forceinline__ void zero()
+    {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                re[a][b] = V4{0, 0, 0, 0};
+                im[a][b] = V4{0, 0, 0, 0};
+            }
+    }
+    // -src(r, c) for r < nr, c < nc; diag: zero above the diagonal, a real
+    // diagonal, and -1 on the diagonal beyond nr
+    __device__ __forceinline__ void load_neg(const E *src, int64_t ld, int nr, int nc, bool diag)
+    {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int r = TileQuad<R>::row(a), c = TileQuad<R>::col(b, q);
+                    R x = (diag && r == c) ? R(-1) : R(0), y = R(0);
+                    if (r < nr && c < nc && (!diag || r >= c)) {
+                        Elem<R, true>::load(src + r + (int64_t)c * ld, x, y);
+                        x = -x;
+                        y = (diag && r == c) ? R(0) : -y;
+                    }
+                    re[a][b][q] = x;
+                    im[a][b][q] = y;
+                }
+    }
+    // planes S[0] + i S[1] (S*[c][r] = element (r, c)) = sg * this; realdiag:
+    // the diagonal's imaginary part is stored as 0
+    __device__ __forceinline__ void to_lds(R (*S)[LEAF][LDL], R sg, bool realdiag) const
+    {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int r = TileQuad<R>::row(a), c = TileQuad<R>::col(b, q);
+                    S[0][c][r] = sg * re[a][b][q];
+                    S[1][c][r] = (realdiag && r == c) ? R(0) : sg * im[a][b][q];
+                }
+    }
+    __device__ __forceinline__ void store(E *dst, int64_t ld, int nr, R sg) const
+    {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int r = TileQuad<R>::row(a), c = TileQuad<R>::col(b, q);
+                    if (r < nr)
+                        Elem<R, true>::store(dst + r + (int64_t)c * ld, sg * re[a][b][q], sg * im[a][b][q]);
+                }
+    }
+};
+
+// Q += P B on the quadrant for complex 64 x 64 operands given by fa(r, k, re,
+// im) = P(r, k) and fb(k, c, re, im) = B(k, c); kmode and lower as tile_mma.
+// Each 16-deep step first fetches the operands of all four 16 x 16 tiles (in
+// the lane layout of mma16: lane (li, lk) takes P(row + li, k + 4 s + lk) and
+// B(k + 4 s + lk, col + li)), then issues their products.
+template <typename R, typename FA, typename FB>
+__device__ __forceinline__ void tile_mma_c(TileQuadC<R> &Q, FA fa, FB fb, int kmode, bool lower)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, lk = lane >> 4;
+    const int rb = 32 * (wave & 1), cb = 32 * (wave >> 1);
+    int k0[2][2], k1[2][2], kmin = LEAF, kmax = 0;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int ro = rb + 16 * a, co = cb + 16 * b;
+            int x0 = 0, x1 = LEAF;
+            if (kmode == TK_TO_COL)
+                x1 = co + 16;
+            else if (kmode == TK_FROM_COL)
+                x0 = co;
+            else if (kmode == TK_TO_ROW)
+                x1 = ro + 16;
+            if (lower && co > ro)
+                x1 = x0;  // no product for tiles above the diagonal
+            k0[a][b] = x0;
+            k1[a][b] = x1;
+            if (x0 < x1) {
+                kmin = x0 < kmin ? x0 : kmin;
+                kmax = x1 > kmax ? x1 : kmax;
+            }
+        }
+    for (int k = kmin; k < kmax; k += 16) {
+        R ar[2][4], ai[2][4], br[2][4], bi[2][4];
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                fa(rb + 16 * a + li, k + 4 * s + lk, ar[a][s], ai[a][s]);
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                fb(k + 4 * s + lk, cb + 16 * b + li, br[b][s], bi[b][s]);
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                if (k < k0[a][b] || k >= k1[a][b])
+                    continue;
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    Q.re[a][b] = mfma16(br[b][s], ar[a][s], Q.re[a][b]);
+                    Q.re[a][b] = mfma16(-bi[b][s], ai[a][s], Q.re[a][b]);
+                    Q.im[a][b] = mfma16(bi[b][s], ar[a][s], Q.im[a][b]);
+                    Q.im[a][b] = mfma16(br[b][s], ai[a][s], Q.im[a][b]);
+                }
+            }
+    }
+}
+
+template <typename R>
+__global__ void __launch_bounds__(256) tile_kernel_c(const TileArgs p)
+{
+    typedef typename Elem<R, true>::type E;
+    __shared__ R S[2][LEAF][LDL];           // planes of the exchanged block, then of the leaf
+    __shared__ R Xd[2][LEAF];               // diagonal of the leaf's inverse
+    __shared__ R Tm[4][2][LB16][LB16 + 1];  // the leaf's per-wave scratch
+    __shared__ int failed, last;
+
+    const int tid = threadIdx.x, nb = p.nb;
+    int bi, bj;
+    const int kind = tile_role(nb, (int)blockIdx.x, bi, bj);
+    E *const A = (E *)p.D;
+    E *const Iv = (E *)p.Inv;
+    int *const abort_word = p.flags + 2 * nb * nb;
+    int *const ctr = abort_word + 1;
+    auto nrows = [&](int b) { return (p.tk - b * LEAF) < LEAF ? p.tk - b * LEAF : LEAF; };
+    auto Ab = [&](int i, int j) { return A + (int64_t)i * LEAF + (int64_t)j * LEAF * p.lda; };
+    auto Xb = [&](int i, int j) { return Iv + (int64_t)i * LEAF + (int64_t)j * LEAF * p.ldi; };
+    auto fL = [&](int i, int j) { return p.flags + i * nb + j; };
+    auto fX = [&](int i, int j) { return p.flags + nb * nb + i * nb + j; };
+    auto wait = [&](const int *f1, const int *f2) { tile_wait(f1, f2, abort_word, p.limit, p.info); };
+    // operand fetchers: M(r, k) of a global block with nr rows, its conjugate
+    // transpose conj(M(c, k)) at (k, c), and the LDS planes
+    auto gget = [&](const E *M, int64_t ld, int nr, int r, int k, R &x, R &y) {
+        x = R(0);
+        y = R(0);
+        if (r < nr)
+            Elem<R, true>::load(M + r + (int64_t)k * ld, x, y);
+    };
+    auto sget = [&](int r, int k, R &x, R &y) {
+        x = S[0][k][r];
+        y = S[1][k][r];
+    };
+
+    if (kind == TILE_D) {
+        const int j = bi, nr = nrows(j);
+        TileQuadC<R> Fd, Fs;
+        Fd.load_neg(Ab(j, j), p.lda, nr, nr, true);
+        if (j > 0)
+            Fs.load_neg(Ab(j, j - 1), p.lda, nr, LEAF, false);
+        for (int l = 0; l + 1 < j; ++l) {
+            wait(fL(j, l), fL(j - 1, l));
+            const E *U = Ab(j, l), *V = Ab(j - 1, l);
+            tile_mma_c<R>(
+                Fs, [&](int r, int k, R &x, R &y) { gget(U, p.lda, nr, r, k, x, y); },
+                [&](int k, int c, R &x, R &y) {
+                    gget(V, p.lda, LEAF, c, k, x, y);
+                    y = -y;
+                },
+                TK_FULL, false);
+            tile_mma_c<R>(
+                Fd, [&](int r, int k, R &x, R &y) { gget(U, p.lda, nr, r, k, x, y); },
+                [&](int k, int c, R &x, R &y) {
+                    gget(U, p.lda, nr, c, k, x, y);
+                    y = -y;
+                },
+                TK_FULL, true);
+        }
+        if (j > 0) {
+            // L_j,j-1 = (A_j,j-1 - ...) inv(L_j-1,j-1)^H
+            wait(fL(j - 1, j - 1), nullptr);
+            Fs.to_lds(S, R(-1), false);
+            __syncthreads();
+            const E *Xp = Xb(j - 1, j - 1);
+            TileQuadC<R> G;
+            G.zero();
+            tile_mma_c<R>(G, sget,
+                          [&](int k, int c, R &x, R &y) {
+                              gget(Xp, p.ldi, LEAF, c, k, x, y);
+                              y = -y;
+                          },
+                          TK_TO_COL, false);
+            __syncthreads();
+            G.store(Ab(j, j - 1), p.lda, nr, R(1));
+            G.to_lds(S, R(1), false);
+            tile_signal(fL(j, j - 1));
+            tile_mma_c<R>(Fd, sget,
+                          [&](int k, int c, R &x, R &y) {
+                              sget(c, k, x, y);
+                              y = -y;
+                          },
+                          TK_FULL, true);
+            __syncthreads();
+        }
+        Fd.to_lds(S, R(-1), true);
+        if (tid == 0)
+            failed = 0;
+        __syncthreads();
+        leafc_lds<R>(S, Xd, Tm, true, nr, p.col0 + j * LEAF, p.info, &failed);
+        {
+            const int r = tid & 63, g = tid >> 6;
+            E *const Ad = Ab(j, j);
+            E *const Xdst = Xb(j, j);
+#pragma unroll
+            for (int k = 0; k < LEAF / 4; ++k) {
+                const int c = g + 4 * k;
+                if (r < nr && c < nr) {
+                    if (r >= c)
+                        Elem<R, true>::store(Ad + r + (int64_t)c * p.lda, S[0][c][r], r == c ? R(0) : S[1][c][r]);
+                    R x, y;
+                    leafc_xget<R>(S, Xd, r, c, x, y);
+                    Elem<R, true>::store(Xdst + r + (int64_t)c * p.ldi, x, y);
+                }
+            }
+        }
+        tile_signal(fL(j, j));
+    } else if (kind == TILE_O) {
+        const int i = bi, j = bj, nr = nrows(i);
+        TileQuadC<R> F;
+        F.load_neg(Ab(i, j), p.lda, nr, LEAF, false);
+        for (int l = 0; l < j; ++l) {
+            wait(fL(i, l), fL(j, l));
+            const E *U = Ab(i, l), *V = Ab(j, l);
+            tile_mma_c<R>(
+                F, [&](int r, int k, R &x, R &y) { gget(U, p.lda, nr, r, k, x, y); },
+                [&](int k, int c, R &x, R &y) {
+                    gget(V, p.lda, LEAF, c, k, x, y);
+                    y = -y;
+                },
+                TK_FULL, false);
+        }
+        wait(fL(j, j), nullptr);
+        F.to_lds(S, R(-1), false);
+        __syncthreads();
+        const E *Xj = Xb(j, j);
+        TileQuadC<R> G;
+        G.zero();
+        tile_mma_c<R>(G, sget,
+                      [&](int k, int c, R &x, R &y) {
+                          gget(Xj, p.ldi, LEAF, c, k, x, y);
+                          y = -y;
+                      },
+                      TK_TO_COL, false);
+        G.store(Ab(i, j), p.lda, nr, R(1));
+        tile_signal(fL(i, j));
+    } else if (kind == TILE_X) {
+        const int i = bi, b = bj, nr = nrows(i);
+        TileQuadC<R> G;
+        G.zero();
+        for (int k = b; k < i; ++k) {
+            wait(fL(i, k), k == b ? fL(b, b) : fX(k, b));
+            const E *U = Ab(i, k), *V = Xb(k, b);
+            // G += L_ik inv(L)_kb
+            tile_mma_c<R>(
+                G, [&](int r, int kk, R &x, R &y) { gget(U, p.lda, nr, r, kk, x, y); },
+                [&](int kk, int c, R &x, R &y) { gget(V + (int64_t)c * p.ldi, p.ldi, LEAF, kk, 0, x, y); },
+                k == b ? TK_FROM_COL : TK_FULL, false);
+        }
+        wait(fL(i, i), nullptr);
+        G.to_lds(S, R(1), false);
+        __syncthreads();
+        // H = inv(L_ii) G
+        const E *Xi = Xb(i, i);
+        TileQuadC<R> H;
+        H.zero();
+        tile_mma_c<R>(H,
+                      [&](int r, int kk, R &x, R &y) {
+                          // rows and columns past a short last block are zero
+                          gget(Xi, p.ldi, kk < nr ? nr : 0, r, kk, x, y);
+                      },
+                      [&](int kk, int c, R &x, R &y) { sget(kk, c, x, y); }, TK_TO_ROW, false);
+        H.store(Xb(i, b), p.ldi, nr, R(-1));
+        tile_signal(fX(i, b));
+    }
+
+    __syncthreads();
+    if (tid == 0)
+        last = atomicAdd(ctr, 1) == (int)gridDim.x - 1;
+    __syncthreads();
+    if (last) {
+        for (int e = tid; e < 2 * nb * nb + 1; e += blockDim.x)
+            p.flags[e] = 0;
+        if (tid == 0)
+            *ctr = 0;
+    }
+}
+
 }  // namespace spd
