@@ -396,14 +396,15 @@ enum {
     OPT_RECT_TALL_ROWS,
     OPT_TILE_LAUNCH,
     OPT_TILE_WAIT_US,
+    OPT_COLUMN_FIRST_ROWS,
     OPT_COUNT
 };
-static const int64_t k_opt_default[OPT_COUNT] = {1, 1, -1, -1, 16384, 1, 2000000};
-static std::atomic<int64_t> g_opt_store[OPT_COUNT] = {{1}, {1}, {-1}, {-1}, {16384}, {1}, {2000000}};
+static const int64_t k_opt_default[OPT_COUNT] = {1, 1, -1, -1, 16384, 1, 2000000, 8192};
+static std::atomic<int64_t> g_opt_store[OPT_COUNT] = {{1}, {1}, {-1}, {-1}, {16384}, {1}, {2000000}, {8192}};
 struct Options {
     int64_t v[OPT_COUNT];
 };
-static thread_local Options g_opt = {{1, 1, -1, -1, 16384, 1, 2000000}};
+static thread_local Options g_opt = {{1, 1, -1, -1, 16384, 1, 2000000, 8192}};
 
 static void snapshot_options()
 {
@@ -448,6 +449,14 @@ static int64_t rect_tall_rows() { return g_opt.v[OPT_RECT_TALL_ROWS]; }
 static bool tile_launch_enabled() { return g_opt.v[OPT_TILE_LAUNCH] != 0; }
 static int64_t tile_wait_ticks() { return g_opt.v[OPT_TILE_WAIT_US] * 100; }  // 100 MHz wall clock
 
+// Lookahead steps taken one at a time: while fewer than column_first_rows()
+// rows remain beyond the next tile (SPD_OPT_COLUMN_FIRST_ROWS), the caller's
+// trailing update waits until the auxiliary stream has updated the next tile
+// column.  There the diagonal-tile chain outlasts the caller's update; left to
+// run beside that update, the column update shares every CU with it and
+// delays the tile that waits for it.
+static int64_t column_first_rows() { return g_opt.v[OPT_COLUMN_FIRST_ROWS]; }
+
 // The auxiliary streams and events of the lookahead schedules: one set per
 // host thread and device, created on first use and kept until spd_release is
 // called on that thread (or the process ends).  Default priority, non-blocking
@@ -455,7 +464,7 @@ static int64_t tile_wait_ticks() { return g_opt.v[OPT_TILE_WAIT_US] * 100; }  //
 // runs on the caller's stream.
 struct AuxStreams {
     hipStream_t look = nullptr, look2 = nullptr;
-    hipEvent_t ev_fork = nullptr, ev_panel = nullptr, ev_rest = nullptr, ev_fw = nullptr;
+    hipEvent_t ev_fork = nullptr, ev_panel = nullptr, ev_rest = nullptr, ev_fw = nullptr, ev_col = nullptr;
 };
 static thread_local std::vector<std::pair<int, AuxStreams>> g_aux;
 
@@ -474,7 +483,7 @@ static int release_aux()
             if (e != hipSuccess && rc == 0)
                 rc = hip_fail(e, "spd_release");
         }
-        for (hipEvent_t ev : {x.ev_fork, x.ev_panel, x.ev_rest, x.ev_fw}) {
+        for (hipEvent_t ev : {x.ev_fork, x.ev_panel, x.ev_rest, x.ev_fw, x.ev_col}) {
             if (ev == nullptr)
                 continue;
             hipError_t e = hipEventDestroy(ev);
@@ -488,7 +497,7 @@ static int release_aux()
 
 struct Lookahead {
     hipStream_t look = nullptr, look2 = nullptr;  // look2: the fused solve's forward substitution
-    hipEvent_t ev_fork = nullptr, ev_panel = nullptr, ev_rest = nullptr, ev_fw = nullptr;
+    hipEvent_t ev_fork = nullptr, ev_panel = nullptr, ev_rest = nullptr, ev_fw = nullptr, ev_col = nullptr;
 
     int begin(hipStream_t s)
     {
@@ -510,7 +519,7 @@ struct Lookahead {
                 for (hipStream_t st : {n.look, n.look2})
                     if (st != nullptr)
                         (void)hipStreamDestroy(st);
-                for (hipEvent_t ev : {n.ev_fork, n.ev_panel, n.ev_rest, n.ev_fw})
+                for (hipEvent_t ev : {n.ev_fork, n.ev_panel, n.ev_rest, n.ev_fw, n.ev_col})
                     if (ev != nullptr)
                         (void)hipEventDestroy(ev);
             };
@@ -519,7 +528,7 @@ struct Lookahead {
                 undo();
                 return hip_fail(e, "hipStreamCreateWithFlags");
             }
-            for (hipEvent_t *ev : {&n.ev_fork, &n.ev_panel, &n.ev_rest, &n.ev_fw})
+            for (hipEvent_t *ev : {&n.ev_fork, &n.ev_panel, &n.ev_rest, &n.ev_fw, &n.ev_col})
                 if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess) {
                     undo();
                     return hip_fail(e, "hipEventCreateWithFlags");
@@ -533,6 +542,7 @@ struct Lookahead {
         ev_panel = x->ev_panel;
         ev_rest = x->ev_rest;
         ev_fw = x->ev_fw;
+        ev_col = x->ev_col;
         // the auxiliary streams start after everything already queued on s
         SPD_TRY_HIP(hipEventRecord(ev_fork, s), "hipEventRecord");
         SPD_TRY_HIP(hipStreamWaitEvent(look, ev_fork, 0), "hipStreamWaitEvent");
@@ -1129,6 +1139,10 @@ struct Solver {
                 SPD_TRY(la.wait(sl, la.ev_rest));  // update of step k-1 done
             // tile column k+1 of the trailing matrix, then diagonal tile and panel k+1
             SPD_TRY(syrk(m, Wk, ldw, kp, T, A + (c0 + T) * (1 + lda), lda, T, info, sl, aux_update()));
+            if (m - T < column_first_rows()) {
+                SPD_TRY(la.record(la.ev_col, sl));
+                SPD_TRY(la.wait(s, la.ev_col));
+            }
             SPD_TRY(diag_panel(n, A, lda, T, c0 + T, Inv, Wb[(k + 1) % 2], info, ctr, sl));
             SPD_TRY(la.record(la.ev_panel, sl));
             // the rest of the trailing matrix, beyond tile column k+1
@@ -1220,6 +1234,10 @@ struct Solver {
             SPD_TRY(la.wait(s, la.ev_panel));  // panel k
             SPD_TRY(la.wait(sl, la.ev_rest));  // the update of step k-1 reached tile column k+1
             SPD_TRY(syrk(n - (k + 1) * T, Wp(k), ldw, kp, T, C(k + 1), lda, T, info, sl, aux_update()));
+            if (n - (k + 2) * T < column_first_rows()) {
+                SPD_TRY(la.record(la.ev_col, sl));
+                SPD_TRY(la.wait(s, la.ev_col));
+            }
             SPD_TRY(diag_panel((k + 1) * T, Wp(k + 1), sl));
             SPD_TRY(la.record(la.ev_panel, sl));
             SPD_TRY(done(k + 1, k + 2));

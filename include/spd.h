@@ -272,9 +272,15 @@ const char *spd_last_error(void);
  *                            launch's other waits as well and sets info to -1
  *                            (the factor is then not usable); it exists so
  *                            that no wave can wait forever.
+ *   SPD_OPT_COLUMN_FIRST_ROWS  under lookahead, in the steps taken one at a
+ *                            time, the trailing update on `stream` waits for
+ *                            the auxiliary stream's update of the next tile
+ *                            column while fewer than this many rows remain
+ *                            beyond the next tile (default 8192; 0: never)
  * spd_set_option returns 0, -1 for an unknown option, -2 for a value out of
  * range (LOOKAHEAD, TWO_STEP and TILE_LAUNCH take 0 or 1, PAIR_ROWS and
- * SYRK_DEEP_ROWS >= -1, RECT_TALL_ROWS and TILE_WAIT_US >= 0);
+ * SYRK_DEEP_ROWS >= -1, RECT_TALL_ROWS, TILE_WAIT_US and COLUMN_FIRST_ROWS
+ * >= 0);
  * SPD_OPT_DEFAULT restores an option's default.
  * spd_get_option returns the current value (INT64_MIN for an unknown
  * option). */
@@ -285,7 +291,8 @@ typedef enum {
     SPD_OPT_SYRK_DEEP_ROWS = 4,
     SPD_OPT_RECT_TALL_ROWS = 5,
     SPD_OPT_TILE_LAUNCH = 6,
-    SPD_OPT_TILE_WAIT_US = 7
+    SPD_OPT_TILE_WAIT_US = 7,
+    SPD_OPT_COLUMN_FIRST_ROWS = 8
 } spd_option_t;
 #define SPD_OPT_DEFAULT INT64_MIN
 int spd_set_option(spd_option_t opt, int64_t value);

@@ -2,7 +2,9 @@
 
 SPD_OPT_LOOKAHEAD = 0 selects the sequential schedule (every kernel on the
 caller's stream) and SPD_OPT_TWO_STEP = 0 the one-step lookahead instead of
-the paired-step schedule.  Under each, potrf, log det and potrs run through
+the paired-step schedule; SPD_OPT_COLUMN_FIRST_ROWS moves the point from which
+the caller's update waits for the next tile column (never, or in every single
+step; with SPD_OPT_PAIR_ROWS past N every step is single).  Under each, potrf, log det and potrs run through
 the one-call entry point (which falls back to the three calls when its fused
 path is off) on small real and complex inputs, checked against the oracle on
 the same bytes; and the auxiliary streams can be released and made again.
@@ -40,10 +42,19 @@ def run_case(spd, dt, n, nrhs, T):
         assert logdet_rel(float(ld.item()), oracle.logdet(Lo)) <= LOGDET_TOL, (dt, n)
 
 
-@pytest.mark.parametrize("opt", ["sequential", "one-step"])
+SCHEDULES = {
+    "sequential": lambda g: {g.OPT_LOOKAHEAD: 0},
+    "one-step": lambda g: {g.OPT_TWO_STEP: 0},
+    "one-step, column first everywhere": lambda g: {g.OPT_TWO_STEP: 0, g.OPT_COLUMN_FIRST_ROWS: 1 << 40},
+    "column first never": lambda g: {g.OPT_COLUMN_FIRST_ROWS: 0},
+    "column first everywhere": lambda g: {g.OPT_COLUMN_FIRST_ROWS: 1 << 40, g.OPT_PAIR_ROWS: 1 << 40},
+}
+
+
+@pytest.mark.parametrize("opt", list(SCHEDULES))
 @pytest.mark.parametrize("dt,n,nrhs,T", CASES)
 def test_schedule_parity(gpu, opt, dt, n, nrhs, T):
-    values = {gpu.OPT_LOOKAHEAD: 0} if opt == "sequential" else {gpu.OPT_TWO_STEP: 0}
+    values = SCHEDULES[opt](gpu)
     with gpu.options(values):
         run_case(gpu, dt, n, nrhs, T)
 
