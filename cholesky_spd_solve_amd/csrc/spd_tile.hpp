@@ -10,10 +10,11 @@
 //
 //   D_j  (diagonal role, block row j):
 //        S    = A_j,j-1 - sum_{l < j-1} L_jl L_j-1,l^T
-//        L_j,j-1 = S inv(L_j-1,j-1)^T                     (published first)
+//        L_j,j-1 = S inv(L_j-1,j-1)^T          (published before the leaf)
 //        A'   = A_jj - sum_{l < j} L_jl L_jl^T
 //        L_jj, inv(L_jj) from A' inside LDS (the 64 x 64 leaf of the
-//        multi-kernel path, the same arithmetic)
+//        multi-kernel path, the same arithmetic); inv(L_jj) is published
+//        before L_jj is stored (no role of the launch reads L_jj)
 //   O_ij (i >= j + 2):
 //        L_ij = (A_ij - sum_{l < j} L_il L_jl^T) inv(L_jj)^T
 //   X_ib (i > b):
@@ -304,7 +305,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) t
             __syncthreads();
             G.store(Ab(j, j - 1), p.lda, nr, R(1));
             G.to_lds(S, R(1));
-            tile_signal(fL(j, j - 1));
+            __syncthreads();
             tile_mma<R>(Fd, &S[0][0], LDL, 1, &S[0][0], LDL, 1, TK_FULL, true);
             __syncthreads();
         }
@@ -314,23 +315,35 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) t
             X[(tid >> 6) + 4 * k][tid & 63] = R(0);
         if (tid == 0)
             failed = 0;
-        __syncthreads();
+        // L_j,j-1 is published only now, when its stores have long completed
+        // (nothing needs it before the next diagonal block); the barrier of
+        // the signal also serves the leaf
+        if (j > 0)
+            tile_signal(fL(j, j - 1));
+        else
+            __syncthreads();
         leaf_lds<R>(S, X, Tm, true, nr, p.col0 + j * LEAF, p.info, &failed);
+        // inv(L_jj) first: the other roles wait for it, and none reads L_jj
+        const int r = tid & 63, g = tid >> 6;
         {
-            const int r = tid & 63, g = tid >> 6;
-            R *const Ad = Ab(j, j);
             R *const Xd = Xb(j, j);
 #pragma unroll
             for (int k = 0; k < LEAF / 4; ++k) {
                 const int c = g + 4 * k;
-                if (r < nr && c < nr) {
-                    if (r >= c)
-                        Ad[r + (int64_t)c * p.lda] = S[c][r];
+                if (r < nr && c < nr)
                     Xd[r + (int64_t)c * p.ldi] = (r >= c) ? X[c][r] : R(0);
-                }
             }
         }
         tile_signal(fL(j, j));
+        {
+            R *const Ad = Ab(j, j);
+#pragma unroll
+            for (int k = 0; k < LEAF / 4; ++k) {
+                const int c = g + 4 * k;
+                if (r < nr && c < nr && r >= c)
+                    Ad[r + (int64_t)c * p.lda] = S[c][r];
+            }
+        }
     } else if (kind == TILE_O) {
         const int i = bi, j = bj, nr = nrows(i);
         TileQuad<R> F;
@@ -608,7 +621,7 @@ __global__ void __launch_bounds__(256) tile_kernel_c(const TileArgs p)
             __syncthreads();
             G.store(Ab(j, j - 1), p.lda, nr, R(1));
             G.to_lds(S, R(1), false);
-            tile_signal(fL(j, j - 1));
+            __syncthreads();
             tile_mma_c<R>(Fd, sget,
                           [&](int k, int c, R &x, R &y) {
                               sget(c, k, x, y);
@@ -620,18 +633,20 @@ __global__ void __launch_bounds__(256) tile_kernel_c(const TileArgs p)
         Fd.to_lds(S, R(-1), true);
         if (tid == 0)
             failed = 0;
-        __syncthreads();
+        // L_j,j-1 published now (see tile_kernel); the barrier serves the leaf
+        if (j > 0)
+            tile_signal(fL(j, j - 1));
+        else
+            __syncthreads();
         leafc_lds<R>(S, Xd, Tm, true, nr, p.col0 + j * LEAF, p.info, &failed);
+        // inv(L_jj) first: the other roles wait for it, and none reads L_jj
+        const int r = tid & 63, g = tid >> 6;
         {
-            const int r = tid & 63, g = tid >> 6;
-            E *const Ad = Ab(j, j);
             E *const Xdst = Xb(j, j);
 #pragma unroll
             for (int k = 0; k < LEAF / 4; ++k) {
                 const int c = g + 4 * k;
                 if (r < nr && c < nr) {
-                    if (r >= c)
-                        Elem<R, true>::store(Ad + r + (int64_t)c * p.lda, S[0][c][r], r == c ? R(0) : S[1][c][r]);
                     R x, y;
                     leafc_xget<R>(S, Xd, r, c, x, y);
                     Elem<R, true>::store(Xdst + r + (int64_t)c * p.ldi, x, y);
@@ -639,6 +654,15 @@ __global__ void __launch_bounds__(256) tile_kernel_c(const TileArgs p)
             }
         }
         tile_signal(fL(j, j));
+        {
+            E *const Ad = Ab(j, j);
+#pragma unroll
+            for (int k = 0; k < LEAF / 4; ++k) {
+                const int c = g + 4 * k;
+                if (r < nr && c < nr && r >= c)
+                    Elem<R, true>::store(Ad + r + (int64_t)c * p.lda, S[0][c][r], r == c ? R(0) : S[1][c][r]);
+            }
+        }
     } else if (kind == TILE_O) {
         const int i = bi, j = bj, nr = nrows(i);
         TileQuadC<R> F;
