@@ -397,14 +397,15 @@ enum {
     OPT_TILE_LAUNCH,
     OPT_TILE_WAIT_US,
     OPT_COLUMN_FIRST_ROWS,
+    OPT_TILE_HOLD_ROWS,
     OPT_COUNT
 };
-static const int64_t k_opt_default[OPT_COUNT] = {1, 1, -1, -1, 16384, 1, 2000000, 8192};
-static std::atomic<int64_t> g_opt_store[OPT_COUNT] = {{1}, {1}, {-1}, {-1}, {16384}, {1}, {2000000}, {8192}};
+static const int64_t k_opt_default[OPT_COUNT] = {1, 1, -1, -1, 16384, 1, 2000000, 8192, 8192};
+static std::atomic<int64_t> g_opt_store[OPT_COUNT] = {{1}, {1}, {-1}, {-1}, {16384}, {1}, {2000000}, {8192}, {8192}};
 struct Options {
     int64_t v[OPT_COUNT];
 };
-static thread_local Options g_opt = {{1, 1, -1, -1, 16384, 1, 2000000, 8192}};
+static thread_local Options g_opt = {{1, 1, -1, -1, 16384, 1, 2000000, 8192, 8192}};
 
 static void snapshot_options()
 {
@@ -456,6 +457,13 @@ static int64_t tile_wait_ticks() { return g_opt.v[OPT_TILE_WAIT_US] * 100; }  //
 // run beside that update, the column update shares every CU with it and
 // delays the tile that waits for it.
 static int64_t column_first_rows() { return g_opt.v[OPT_COLUMN_FIRST_ROWS]; }
+
+// A real diagonal tile with fewer than tile_hold_rows() rows below it
+// (SPD_OPT_TILE_HOLD_ROWS) is launched so that each workgroup has a CU to
+// itself: idle waves hold registers (see tile_kernel) and the launch asks for
+// the CU's whole LDS.  There the chain is the longer path, and the tile's
+// leaves sharing SIMDs with the trailing update run two to three times slower.
+static int64_t tile_hold_rows() { return g_opt.v[OPT_TILE_HOLD_ROWS]; }
 
 // The auxiliary streams and events of the lookahead schedules: one set per
 // host thread and device, created on first use and kept until spd_release is
@@ -733,7 +741,7 @@ struct Solver {
     // Factor the tk x tk diagonal tile at D and write inv(L_kk) to Inv (ld
     // ldi) in one launch (tile_kernel, tile_kernel_c)
     static int tile_launch(E *D, int64_t lda, int64_t tk, E *Inv, int64_t ldi, int *info, int *flags, int64_t col0,
-                           hipStream_t s)
+                           int64_t rows_below, hipStream_t s)
     {
         {
             TileArgs p;
@@ -747,12 +755,32 @@ struct Solver {
             p.info = info;
             p.col0 = (int)col0;
             p.limit = tile_wait_ticks();
+            p.hold = (!CPLX && rows_below < tile_hold_rows()) ? 1 : 0;
             const unsigned grid = (unsigned)tile_groups(p.nb);
             SPD_VALIDATE((check_tile<R, CPLX>(p, grid, g_chk)));
-            if constexpr (CPLX)
+            if constexpr (CPLX) {
                 tile_kernel_c<R><<<dim3(grid), dim3(256), 0, s>>>(p);
-            else
-                tile_kernel<R><<<dim3(grid), dim3(256), 0, s>>>(p);
+            } else {
+                // holding: the idle waves take the registers, and group memory
+                // up to the CU's whole LDS (not used) keeps every other
+                // workgroup off the CU
+                size_t dyn = 0;
+                if (p.hold) {
+                    int dev = 0, lds = 0;
+                    hipFuncAttributes fa;
+                    SPD_TRY_HIP(hipGetDevice(&dev), "hipGetDevice");
+                    SPD_TRY_HIP(hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev),
+                                "hipDeviceGetAttribute");
+                    SPD_TRY_HIP(hipFuncGetAttributes(&fa, (const void *)tile_kernel<R>), "hipFuncGetAttributes");
+                    if ((size_t)lds > fa.sharedSizeBytes) {
+                        dyn = (size_t)lds - fa.sharedSizeBytes;
+                        SPD_TRY_HIP(hipFuncSetAttribute((const void *)tile_kernel<R>,
+                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn),
+                                    "hipFuncSetAttribute");
+                    }
+                }
+                tile_kernel<R><<<dim3(grid), dim3(p.hold ? 512 : 256), dyn, s>>>(p);
+            }
             SPD_CHECK_LAUNCH("tile_kernel");
             return 0;
         }
@@ -994,7 +1022,7 @@ struct Solver {
         E *D = A + c0 + c0 * lda;
         if (tile_launch_enabled()) {
             ProfScope ps(PROF_DIAG, FMUL * 2.0 * (double)tk * tk * tk / 3.0, s);
-            SPD_TRY(tile_launch(D, lda, tk, Inv, T, info, tile_flags(ctr), c0, s));
+            SPD_TRY(tile_launch(D, lda, tk, Inv, T, info, tile_flags(ctr), c0, n - c0 - tk, s));
         } else {
             ProfScope ps(PROF_DIAG, FMUL * 2.0 * (double)tk * tk * tk / 3.0, s);
             for (int64_t b0 = 0; b0 < tk; b0 += LEAF) {

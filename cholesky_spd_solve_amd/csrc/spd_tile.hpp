@@ -49,6 +49,7 @@ struct TileArgs {
                     // -1 if a wait ran out of time
     int col0;       // global column of the tile's first column
     int64_t limit;  // longest wait, in ticks of the 100 MHz wall clock
+    int hold;       // real types: 1 to launch 512 threads per workgroup (see tile_kernel)
 };
 
 enum { TILE_D = 0, TILE_O = 1, TILE_X = 2 };
@@ -252,14 +253,28 @@ __device__ __forceinline__ void tile_mma(TileQuad<R> &Q, const R *pa, int ak, in
         }
 }
 
+// Launched with 256 threads, or with 512 (TileArgs::hold): then waves 4-7 do
+// no work and only meet every barrier of waves 0-3 until those are done.  They
+// hold registers, so that no wave of another kernel (the trailing update)
+// shares a SIMD with this workgroup's working waves: the leaf's sweeps, one
+// wave's long chain of vector instructions, then run at their own pace
+// instead of sharing the multiply pipeline with matrix-core waves.
 template <typename R>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) tile_kernel(const TileArgs p)
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) tile_kernel(const TileArgs p)
 {
     __shared__ R S[LEAF][LDL];
     __shared__ R X[LEAF][LDL];
     __shared__ R Tm[4][LB16][LB16 + 1];
-    __shared__ int failed, last;
+    __shared__ int failed, last, done;
 
+    if (threadIdx.x == 0)
+        done = 0;
+    if (threadIdx.x >= 256) {
+        do
+            __syncthreads();
+        while (!done);
+        return;
+    }
     const int tid = threadIdx.x, nb = p.nb;
     int bi, bj;
     const int kind = tile_role(nb, (int)blockIdx.x, bi, bj);
@@ -402,11 +417,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) t
         last = atomicAdd(ctr, 1) == (int)gridDim.x - 1;
     __syncthreads();
     if (last) {
-        for (int e = tid; e < 2 * nb * nb + 1; e += blockDim.x)
+        for (int e = tid; e < 2 * nb * nb + 1; e += 256)
             p.flags[e] = 0;
         if (tid == 0)
             *ctr = 0;
     }
+    if (tid == 0)
+        done = 1;  // the idle waves leave after this barrier
+    __syncthreads();
 }
 
 // ---------------------------------------------------------------------------

@@ -277,10 +277,16 @@ const char *spd_last_error(void);
  *                            the auxiliary stream's update of the next tile
  *                            column while fewer than this many rows remain
  *                            beyond the next tile (default 8192; 0: never)
+ *   SPD_OPT_TILE_HOLD_ROWS   a real diagonal tile with fewer than this many
+ *                            rows below it is factored by workgroups that keep
+ *                            a CU each to themselves (twice the threads, half
+ *                            of them idle, and all of the CU's group memory),
+ *                            so that no other kernel's waves share the working
+ *                            waves' SIMDs (default 8192; 0: never)
  * spd_set_option returns 0, -1 for an unknown option, -2 for a value out of
  * range (LOOKAHEAD, TWO_STEP and TILE_LAUNCH take 0 or 1, PAIR_ROWS and
- * SYRK_DEEP_ROWS >= -1, RECT_TALL_ROWS, TILE_WAIT_US and COLUMN_FIRST_ROWS
- * >= 0);
+ * SYRK_DEEP_ROWS >= -1, RECT_TALL_ROWS, TILE_WAIT_US, COLUMN_FIRST_ROWS and
+ * TILE_HOLD_ROWS >= 0);
  * SPD_OPT_DEFAULT restores an option's default.
  * spd_get_option returns the current value (INT64_MIN for an unknown
  * option). */
@@ -292,7 +298,8 @@ typedef enum {
     SPD_OPT_RECT_TALL_ROWS = 5,
     SPD_OPT_TILE_LAUNCH = 6,
     SPD_OPT_TILE_WAIT_US = 7,
-    SPD_OPT_COLUMN_FIRST_ROWS = 8
+    SPD_OPT_COLUMN_FIRST_ROWS = 8,
+    SPD_OPT_TILE_HOLD_ROWS = 9
 } spd_option_t;
 #define SPD_OPT_DEFAULT INT64_MIN
 int spd_set_option(spd_option_t opt, int64_t value);

@@ -5,8 +5,9 @@ launch whose workgroups own 64 x 64 blocks and wait for each other's blocks
 through flags.  These tests compare it with the oracle on tiles of one to
 sixteen blocks, with short last blocks and short last tiles, through the
 one-call solve (which applies the tile inverses it builds) and the three
-calls; they check the previous launch sequence (SPD_OPT_TILE_LAUNCH = 0) the
-same way, a failing pivot in every block position of a tile, and the bounded
+calls, launched both with and without CU-holding workgroups
+(SPD_OPT_TILE_HOLD_ROWS); they check the previous launch sequence
+(SPD_OPT_TILE_LAUNCH = 0) the same way, a failing pivot in every block position of a tile, and the bounded
 wait: with a zero time limit the launch gives up at once, reports info = -1
 and clears its flags, so the next call on the same workspace is exact again.
 """
@@ -62,12 +63,14 @@ def check(dt, n, A, B, res):
         assert logdet_rel(ld, oracle.logdet(Lo)) <= LOGDET_TOL, (dt, n)
 
 
-@pytest.mark.parametrize("launch", [1, 0])
+@pytest.mark.parametrize("launch,hold", [(1, 8192), (1, 0), (0, 8192)])
 @pytest.mark.parametrize("dt,n,nrhs,T", CASES)
-def test_tile_parity(gpu, launch, dt, n, nrhs, T):
+def test_tile_parity(gpu, launch, hold, dt, n, nrhs, T):
+    """hold 8192 (the default): every tile of these sizes is launched with
+    CU-holding workgroups (real types); hold 0: never."""
     A = spdgen.make_A(n, dt, 0.5, 11, device="cuda")
     B = spdgen.make_B(n, nrhs, dt, 11, device="cuda")
-    with gpu.options({gpu.OPT_TILE_LAUNCH: launch}):
+    with gpu.options({gpu.OPT_TILE_LAUNCH: launch, gpu.OPT_TILE_HOLD_ROWS: hold}):
         check(dt, n, A, B, solve_one_call(gpu, A, B, T))
         check(dt, n, A, B, solve_three_calls(gpu, A, B, T))
 

@@ -166,12 +166,12 @@ def test_options_validate_and_restore(lib):
     import cholesky_spd_solve_amd as spd
     defaults = {spd.OPT_LOOKAHEAD: 1, spd.OPT_TWO_STEP: 1, spd.OPT_PAIR_ROWS: -1, spd.OPT_SYRK_DEEP_ROWS: -1,
                 spd.OPT_RECT_TALL_ROWS: 16384, spd.OPT_TILE_LAUNCH: 1, spd.OPT_TILE_WAIT_US: 2000000,
-                spd.OPT_COLUMN_FIRST_ROWS: 8192}
+                spd.OPT_COLUMN_FIRST_ROWS: 8192, spd.OPT_TILE_HOLD_ROWS: 8192}
     for k, v in defaults.items():
         assert spd.get_option(k) == v
     assert lib.spd_set_option(0, 1) == -1
-    assert lib.spd_set_option(9, 1) == -1
-    assert lib.spd_get_option(9) == -(1 << 63)
+    assert lib.spd_set_option(10, 1) == -1
+    assert lib.spd_get_option(10) == -(1 << 63)
     assert lib.spd_set_option(spd.OPT_LOOKAHEAD, 2) == -2
     assert lib.spd_set_option(spd.OPT_TWO_STEP, -1) == -2
     assert lib.spd_set_option(spd.OPT_PAIR_ROWS, -2) == -2
@@ -179,6 +179,7 @@ def test_options_validate_and_restore(lib):
     assert lib.spd_set_option(spd.OPT_TILE_LAUNCH, 2) == -2
     assert lib.spd_set_option(spd.OPT_TILE_WAIT_US, -1) == -2
     assert lib.spd_set_option(spd.OPT_COLUMN_FIRST_ROWS, -1) == -2
+    assert lib.spd_set_option(spd.OPT_TILE_HOLD_ROWS, -1) == -2
     with spd.options({spd.OPT_PAIR_ROWS: 0, spd.OPT_LOOKAHEAD: 0, spd.OPT_RECT_TALL_ROWS: 7}):
         assert spd.get_option(spd.OPT_PAIR_ROWS) == 0
         assert spd.get_option(spd.OPT_LOOKAHEAD) == 0
