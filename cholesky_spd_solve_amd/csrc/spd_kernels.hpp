@@ -483,12 +483,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) l
 //                  A(i, j) -= L(i, b) L(j, b)^H        b < j <= i      (MFMA)
 //   inv(L)(i, b) = -inv(L(i, i)) sum_{b<=k<i} L(i, k) inv(L)(k, b)
 //
-// In the diagonal block sweep lane c holds row c of the Hermitian block and
-// column c of the inverse.  Step j: the pivot is the real part of lane j's
-// a[j]; every lane scales its a[j] by 1/L(j, j), which leaves L(c, j) in
-// lane c; then A(c, r) -= L(c, j) conj(L(r, j)) and x[r] -= L(r, j) x[j] for
-// r > j, with L(r, j) read from lane r.  Every complex 16 x 16 x 16 product is
-// sixteen v_mfma_*_16x16x4 (four per complex multiply-add).
+// The diagonal block sweep gives each of the wave's four rows of 16 lanes one
+// real plane: lane 16 g + c holds the real (g = 0) and imaginary (g = 1)
+// parts of row c of the Hermitian block, and those of column c of the
+// inverse (g = 2, 3).  Step j: the pivot is row 0's lane j; every lane
+// scales its entry j by 1/L(j, j), which leaves L(c, j) in lane c of rows 0
+// and 1; then A(c, r) -= L(c, j) conj(L(r, j)) and x[r] -= L(r, j) x[j] for
+// r > j are one real update y[r] -= P Re L(r, j) + Q Im L(r, j) in every
+// lane, with P its own entry j and Q the partner plane's (signed).  Every
+// complex 16 x 16 x 16 product is sixteen v_mfma_*_16x16x4 (four per complex
+// multiply-add).
 //
 // LDS: one array S per plane holds L in its lower triangle (S[c][r] =
 // L(r, c), r >= c) and the strict lower triangle of inv(L) in its upper one
@@ -531,94 +535,181 @@ __device__ __forceinline__ void mma16c_ra(const R (&ar)[4], const R (&ai)[4], FB
     }
 }
 
-// Column J of the complex sweep (pivot scale s, ljj already known), then the
-// columns after it; the pivot is diag16_pivot's on the real parts.
+// Exchanges between the four rows of 16 lanes (gfx950 permlane swaps):
+// row_pairs gives e = [v0, v0, v2, v2] and o = [v1, v1, v3, v3] (row by
+// row), low_half [x0, x1, x0, x1]; lane_value the value of lane N.
+__device__ __forceinline__ double f64_of(unsigned lo, unsigned hi)
+{
+    return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+}
+__device__ __forceinline__ void row_pairs(double v, double &e, double &o)
+{
+    const unsigned long long b = __builtin_bit_cast(unsigned long long, v);
+    const auto l = __builtin_amdgcn_permlane16_swap((unsigned)b, (unsigned)b, false, false);
+    const auto h = __builtin_amdgcn_permlane16_swap((unsigned)(b >> 32), (unsigned)(b >> 32), false, false);
+    e = f64_of(l[0], h[0]);
+    o = f64_of(l[1], h[1]);
+}
+__device__ __forceinline__ void row_pairs(float v, float &e, float &o)
+{
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    const auto l = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    e = __builtin_bit_cast(float, (unsigned)l[0]);
+    o = __builtin_bit_cast(float, (unsigned)l[1]);
+}
+__device__ __forceinline__ double low_half(double x)
+{
+    const unsigned long long b = __builtin_bit_cast(unsigned long long, x);
+    const auto l = __builtin_amdgcn_permlane32_swap((unsigned)b, (unsigned)b, false, false);
+    const auto h = __builtin_amdgcn_permlane32_swap((unsigned)(b >> 32), (unsigned)(b >> 32), false, false);
+    return f64_of(l[0], h[0]);
+}
+__device__ __forceinline__ float low_half(float x)
+{
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto l = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (unsigned)l[0]);
+}
+template <int N>
+__device__ __forceinline__ double lane_value(double x)
+{
+    const unsigned long long b = __builtin_bit_cast(unsigned long long, x);
+    return f64_of((unsigned)__builtin_amdgcn_readlane((int)(unsigned)b, N),
+                  (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(b >> 32), N));
+}
+template <int N>
+__device__ __forceinline__ float lane_value(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), N));
+}
+
+// y += ur(lane N) m + ui(lane N) q, lane N of this lane's row read by the
+// multiply-adds themselves (DPP row_newbcast on the first source; the
+// compiler does not fold a broadcast into a 64-bit multiply-add by itself).
+// FIRST: ur and ui were just written by other VALU instructions, and a DPP
+// read of a VGPR must come at least two cycles after its write.
+template <int N, bool FIRST>
+__device__ __forceinline__ void fmac_pair(double &y, double ur, double ui, double m, double q)
+{
+    if constexpr (FIRST)
+        asm("s_nop 1\n\tv_fmac_f64_dpp %0, %1, %2 row_newbcast:%5 row_mask:0xf bank_mask:0xf\n\t"
+            "v_fmac_f64_dpp %0, %3, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf"
+            : "+v"(y)
+            : "v"(ur), "v"(m), "v"(ui), "v"(q), "n"(N));
+    else
+        asm("v_fmac_f64_dpp %0, %1, %2 row_newbcast:%5 row_mask:0xf bank_mask:0xf\n\t"
+            "v_fmac_f64_dpp %0, %3, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf"
+            : "+v"(y)
+            : "v"(ur), "v"(m), "v"(ui), "v"(q), "n"(N));
+}
+template <int N, bool FIRST>
+__device__ __forceinline__ void fmac_pair(float &y, float ur, float ui, float m, float q)
+{
+    if constexpr (FIRST)
+        asm("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:%5 row_mask:0xf bank_mask:0xf\n\t"
+            "v_fmac_f32_dpp %0, %3, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf"
+            : "+v"(y)
+            : "v"(ur), "v"(m), "v"(ui), "v"(q), "n"(N));
+    else
+        asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%5 row_mask:0xf bank_mask:0xf\n\t"
+            "v_fmac_f32_dpp %0, %3, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf"
+            : "+v"(y)
+            : "v"(ur), "v"(m), "v"(ui), "v"(q), "n"(N));
+}
+// y[r] += L_re(r, J) m + L_im(r, J) q for r = N .. 15 (ur, ui: rows 0 and
+// 1 of column J in every row)
+template <typename R, int N, bool FIRST>
+__device__ __forceinline__ void diag16c_update(R *y, R ur, R ui, R m, R q)
+{
+    if constexpr (N < LB16) {
+        fmac_pair<N, FIRST>(y[N], ur, ui, m, q);
+        diag16c_update<R, N + 1, false>(y, ur, ui, m, q);
+    }
+}
+
+// Scale of pivot column J from its value d = Re A(J, J) (uniform), as
+// diag16_pivot.
 template <typename R, bool FACTOR, int J>
-__device__ __forceinline__ void diag16c_step(R *ar, R *ai, R *xr, R *xi, int c, R s, R ljj, int &bad)
+__device__ __forceinline__ void diag16c_pivot(R d, R &s, R &ljj, int &bad)
+{
+    if constexpr (FACTOR) {
+        const bool ok = d > R(0);
+        bad = (!ok && bad < 0) ? J : bad;
+        d = ok ? d : R(1);
+        s = rsqrt_refined(d, ljj);
+    } else {
+        ljj = d;
+        s = R(1) / d;
+    }
+}
+
+// Column J of the complex sweep (pivot scale s, ljj already known), then the
+// columns after it.  y, c, g as in diag16c; sg = -1 in rows 1 and 2.  The
+// column is scaled (rows 0 and 1 only when FACTOR: otherwise they hold the
+// given L), L(r, J) = row 0's and row 1's y[J] in lane r is copied into
+// every row, then y[r] -= P Re L(r, J) + Q Im L(r, J) for r > J, row J + 1
+// first so that the next pivot's chain overlaps the other rows.
+template <typename R, bool FACTOR, int J>
+__device__ __forceinline__ void diag16c_step(R *y, int c, int g, R sg, R s, R ljj, int &bad)
 {
     if constexpr (J < LB16) {
-        if constexpr (FACTOR) {
-            ar[J] = (c == J) ? ljj : ar[J] * s;
-            ai[J] = (c == J) ? R(0) : ai[J] * s;
+        if constexpr (FACTOR)
+            y[J] = (g < 2 && c == J) ? (g == 0 ? ljj : R(0)) : y[J] * s;
+        else
+            y[J] = (g < 2) ? y[J] : y[J] * s;
+        R e, od;
+        row_pairs(y[J], e, od);
+        R P = y[J], Q = sg * ((g & 1) ? e : od);  // Q: the partner plane's entry J
+        if constexpr (!FACTOR) {
+            P = (g < 2) ? R(0) : P;
+            Q = (g < 2) ? R(0) : Q;
         }
-        xr[J] *= s;
-        xi[J] *= s;
+        const R ur = low_half(e), ui = low_half(od);
         R s1 = R(0), l1 = R(0);
         if constexpr (J + 1 < LB16) {
-            const R lr = row_value<J + 1>(ar[J]), lq = row_value<J + 1>(ai[J]);  // L(J + 1, J)
-            if constexpr (FACTOR) {  // a[J + 1] -= a[J] conj(l)
-                ar[J + 1] -= ar[J] * lr + ai[J] * lq;
-                ai[J + 1] -= ai[J] * lr - ar[J] * lq;
-            }
-            const R tr = xr[J + 1] - (lr * xr[J] - lq * xi[J]);  // x[J + 1] -= l x[J]
-            xi[J + 1] -= lr * xi[J] + lq * xr[J];
-            xr[J + 1] = tr;
-            diag16_pivot<R, FACTOR, J + 1>(ar, s1, l1, bad);
+            y[J + 1] = __builtin_fma(-Q, row_value<J + 1>(ui), __builtin_fma(-P, row_value<J + 1>(ur), y[J + 1]));
+            diag16c_pivot<R, FACTOR, J + 1>(lane_value<J + 1>(y[J + 1]), s1, l1, bad);
         }
-        R br[LB16], bi[LB16];
-        diag16_bcast<R, J, J + 2>(ar, br);
-        diag16_bcast<R, J, J + 2>(ai, bi);
-#pragma unroll
-        for (int r = J + 2; r < LB16; ++r)
-            asm volatile("" : "+v"(br[r]), "+v"(bi[r]));
-#pragma unroll
-        for (int r = J + 2; r < LB16; ++r) {
-            if constexpr (FACTOR) {  // a[r] -= a[J] conj(L(r, J))
-                ar[r] -= ar[J] * br[r] + ai[J] * bi[r];
-                ai[r] -= ai[J] * br[r] - ar[J] * bi[r];
-            }
-            const R tr = xr[r] - (br[r] * xr[J] - bi[r] * xi[J]);  // x[r] -= L(r, J) x[J]
-            xi[r] -= br[r] * xi[J] + bi[r] * xr[J];
-            xr[r] = tr;
-        }
-#pragma unroll
-        for (int r = J + 2; r < LB16; ++r)
-            asm volatile("" : "+v"(ar[r]), "+v"(ai[r]), "+v"(xr[r]), "+v"(xi[r]));
-        diag16c_step<R, FACTOR, J + 1>(ar, ai, xr, xi, c, s1, l1, bad);
+        if constexpr (J + 2 < LB16)
+            diag16c_update<R, J + 2, true>(y, ur, ui, -P, -Q);
+        diag16c_step<R, FACTOR, J + 1>(y, c, g, sg, s1, l1, bad);
     }
 }
 
 // Factor (FACTOR) and invert, or only invert, the complex 16 x 16 diagonal
 // block at (o, o) of S0 + i S1 (S*[c][r] = element (r, c), lower triangle);
 // L goes back to S's lower triangle (real diagonal), inv(L) to S's upper
-// triangle and Xd (its diagonal).  One wave, as diag16.
+// triangle and Xd (its diagonal).  One wave: lane 16 g + c keeps y[r] = Re
+// A(c, r), Im A(c, r), Re inv(L)(r, c), Im inv(L)(r, c) for g = 0 .. 3.
 template <typename R, bool FACTOR>
 __device__ __forceinline__ void diag16c(R (*S0)[LDL], R (*S1)[LDL], R *Xd0, R *Xd1, int o, int lb, int gcol, int *info,
                                         int *failed)
 {
-    const int lane = threadIdx.x & 63, c = lane & 15;
-    R ar[LB16], ai[LB16], xr[LB16], xi[LB16];
+    const int lane = threadIdx.x & 63, c = lane & 15, g = lane >> 4;
+    R(*const Sp)[LDL] = (g & 1) ? S1 : S0;
+    R y[LB16];
 #pragma unroll
-    for (int r = 0; r < LB16; ++r) {  // row c: A(c, r), the upper part as conj(A(r, c))
-        ar[r] = (r <= c) ? S0[o + r][o + c] : S0[o + c][o + r];
-        ai[r] = (r <= c) ? S1[o + r][o + c] : -S1[o + c][o + r];
-        xr[r] = (r == c) ? R(1) : R(0);
-        xi[r] = R(0);
+    for (int r = 0; r < LB16; ++r) {  // row c of A, the upper part as conj(A(r, c)); e_c
+        const R v = (r <= c) ? Sp[o + r][o + c] : Sp[o + c][o + r];
+        y[r] = g == 0 ? v : g == 1 ? ((r <= c) ? v : -v) : (g == 2 && r == c) ? R(1) : R(0);
     }
+    const R sg = (g == 1 || g == 2) ? R(-1) : R(1);
     int bad = -1;
     R s0, l0;
-    diag16_pivot<R, FACTOR, 0>(ar, s0, l0, bad);
-    diag16c_step<R, FACTOR, 0>(ar, ai, xr, xi, c, s0, l0, bad);
+    diag16c_pivot<R, FACTOR, 0>(lane_value<0>(y[0]), s0, l0, bad);
+    diag16c_step<R, FACTOR, 0>(y, c, g, sg, s0, l0, bad);
     if (FACTOR && bad >= 0 && lane == 0 && o + bad < lb) {
         if (info != nullptr)
             atomicCAS(info, 0, gcol + o + bad + 1);
         *failed = 1;
     }
-    if (lane < LB16) {
+    R *const Xp = (g & 1) ? Xd1 : Xd0;
 #pragma unroll
-        for (int r = 0; r < LB16; ++r) {
-            if (r <= c) {  // row c of L
-                if constexpr (FACTOR) {
-                    S0[o + r][o + c] = ar[r];
-                    S1[o + r][o + c] = ai[r];
-                }
-            } else {  // column c of inv(L) below its diagonal
-                S0[o + r][o + c] = xr[r];
-                S1[o + r][o + c] = xi[r];
-            }
-        }
-        Xd0[o + c] = xr[c];
-        Xd1[o + c] = xi[c];
+    for (int r = 0; r < LB16; ++r) {
+        if (g < 2 ? (FACTOR && r <= c) : r > c)  // row c of L; column c of inv(L) below its diagonal
+            Sp[o + r][o + c] = y[r];
+        if (g >= 2 && r == c)
+            Xp[o + c] = y[r];
     }
 }
 
