@@ -760,6 +760,35 @@ __device__ __forceinline__ void leafc_lds(R (*S)[LEAF][LDL], R (*Xd)[LEAF], R (*
         }
     };
 
+    // T += sum_{k0 <= k < k1} L(i, k) X(k, b)
+    auto tsum = [&](int i, int b, int k0, int k1, V4 &cr, V4 &ci) {
+        for (int k = k0; k < k1; ++k)
+            mma16c<R>([&](int rr, int kk, R &re, R &im) { lget(i * LB16 + rr, k * LB16 + kk, re, im); },
+                      [&](int kk, int cc, R &re, R &im) { xget(k * LB16 + kk, b * LB16 + cc, re, im); }, cr, ci);
+    };
+    // X(i, b) = -inv(L(i, i)) T, T through this wave's scratch
+    auto finish = [&](int i, int b, const V4 &cr, const V4 &ci) {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {  // Tm[.][c][r] = T(r, c)
+            Tm[wave][0][acc_row<R>(lk, qq)][li] = cr[qq];
+            Tm[wave][1][acc_row<R>(lk, qq)][li] = ci[qq];
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's LDS stores done before reading them back
+        __builtin_amdgcn_wave_barrier();
+        V4 c2r = {0, 0, 0, 0}, c2i = {0, 0, 0, 0};
+        mma16c<R>([&](int rr, int kk, R &re, R &im) { xget(i * LB16 + rr, i * LB16 + kk, re, im); },
+                  [&](int kk, int cc, R &re, R &im) {
+                      re = Tm[wave][0][cc][kk];
+                      im = Tm[wave][1][cc][kk];
+                  },
+                  c2r, c2i);
+        put(true, i * LB16, b * LB16, c2r, c2i, R(-1));
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+    };
+    static_assert(NB == 4, "the inverse schedule below is written for four sub-blocks");
+    V4 t31r = {0, 0, 0, 0}, t31i = {0, 0, 0, 0}, t30r = {0, 0, 0, 0}, t30i = {0, 0, 0, 0};
+
     for (int b = 0; b < NB; ++b) {
         const int o = b * LB16;
         if (wave == 0) {
@@ -767,6 +796,22 @@ __device__ __forceinline__ void leafc_lds(R (*S)[LEAF][LDL], R (*Xd)[LEAF], R (*
                 diag16c<R, true>(S[0], S[1], Xd[0], Xd[1], o, lb, gcol, info, failed);
             else
                 diag16c<R, false>(S[0], S[1], Xd[0], Xd[1], o, lb, gcol, info, failed);
+        } else if (b == 2 && wave == 1) {
+            // beside the sweeps, the inverse blocks whose inputs are final
+            V4 tr = {0, 0, 0, 0}, ti = {0, 0, 0, 0};
+            tsum(1, 0, 0, 1, tr, ti);
+            finish(1, 0, tr, ti);
+        } else if (b == 3 && wave == 1) {
+            V4 tr = {0, 0, 0, 0}, ti = {0, 0, 0, 0};
+            tsum(2, 1, 1, 2, tr, ti);
+            finish(2, 1, tr, ti);
+            tsum(3, 1, 1, 3, t31r, t31i);
+        } else if (b == 3 && wave == 2) {
+            V4 tr = {0, 0, 0, 0}, ti = {0, 0, 0, 0};
+            tsum(2, 0, 0, 2, tr, ti);
+            finish(2, 0, tr, ti);
+        } else if (b == 3 && wave == 3) {
+            tsum(3, 0, 0, 2, t30r, t30i);
         }
         __syncthreads();
         if (factor) {
@@ -809,34 +854,20 @@ __device__ __forceinline__ void leafc_lds(R (*S)[LEAF][LDL], R (*Xd)[LEAF], R (*
         }
     }
 
-    // inverse off-diagonal blocks, by distance d = i - b
-    for (int d = 1; d < NB; ++d) {
-        const int b = wave, i = b + d;
-        if (i < NB) {
-            V4 cr = {0, 0, 0, 0}, ci = {0, 0, 0, 0};
-            for (int k = b; k < i; ++k)  // T = sum_k L(i, k) X(k, b)
-                mma16c<R>([&](int rr, int kk, R &re, R &im) { lget(i * LB16 + rr, k * LB16 + kk, re, im); },
-                          [&](int kk, int cc, R &re, R &im) { xget(k * LB16 + kk, b * LB16 + cc, re, im); }, cr,
-                          ci);
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {  // Tm[.][c][r] = T(r, c)
-                Tm[wave][0][acc_row<R>(lk, qq)][li] = cr[qq];
-                Tm[wave][1][acc_row<R>(lk, qq)][li] = ci[qq];
-            }
-            __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's LDS stores done before reading them back
-            __builtin_amdgcn_wave_barrier();
-            V4 c2r = {0, 0, 0, 0}, c2i = {0, 0, 0, 0};  // X(i, b) = -inv(L(i, i)) T
-            mma16c<R>([&](int rr, int kk, R &re, R &im) { xget(i * LB16 + rr, i * LB16 + kk, re, im); },
-                      [&](int kk, int cc, R &re, R &im) {
-                          re = Tm[wave][0][cc][kk];
-                          im = Tm[wave][1][cc][kk];
-                      },
-                      c2r, c2i);
-            put(true, i * LB16, b * LB16, c2r, c2i, R(-1));
-        }
-        __syncthreads();
+    // the last block row of the inverse: X(3, b) = -inv(L(3, 3)) sum_k L(3, k) X(k, b)
+    // (rows 1 and 2 and the partial sums above were formed beside the sweeps,
+    // each sum in the order of k)
+    if (wave == 0) {
+        V4 tr = {0, 0, 0, 0}, ti = {0, 0, 0, 0};
+        tsum(3, 2, 2, 3, tr, ti);
+        finish(3, 2, tr, ti);
+    } else if (wave == 1) {
+        finish(3, 1, t31r, t31i);
+    } else if (wave == 3) {
+        tsum(3, 0, 2, 3, t30r, t30i);
+        finish(3, 0, t30r, t30i);
     }
-
+    __syncthreads();
 }
 
 // PANEL: one launch factors a single leaf and solves the p.prows panel rows
