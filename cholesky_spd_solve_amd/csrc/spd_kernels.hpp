@@ -297,6 +297,34 @@ __device__ __forceinline__ void leaf_lds(R (*S)[LDL], R (*X)[LDL], R (*Tm)[LB16]
         }
     };
 
+    // acc += sum_{k0 <= k < k1} L(i, k) X(k, b)
+    auto tsum = [&](int i, int b, int k0, int k1, V4 &acc) {
+        for (int k = k0; k < k1; ++k)
+            acc = mma16<R>(&S[k * LB16][i * LB16], LDL, 1, &X[b * LB16][k * LB16], 1, LDL, acc);
+    };
+    // T to this wave's scratch (Tm[c][r] = T(r, c)), and back
+    auto stage = [&](const V4 &acc) {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+            Tm[wave][acc_row<R>(lk, qq)][li] = acc[qq];
+    };
+    auto unstage = [&](V4 &acc) {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+            acc[qq] = Tm[wave][acc_row<R>(lk, qq)][li];
+    };
+    // X(i, b) = -inv(L(i, i)) T, T staged
+    auto apply = [&](int i, int b) {
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's LDS stores done before reading them back
+        __builtin_amdgcn_wave_barrier();
+        V4 acc2 = {0, 0, 0, 0};
+        acc2 = mma16<R>(&X[i * LB16][i * LB16], LDL, 1, &Tm[wave][0][0], 1, LB16 + 1, acc2);
+        put(X, i * LB16, b * LB16, acc2, R(-1), false);
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+    };
+    static_assert(NB == 4, "the inverse schedule below is written for four sub-blocks");
+
     for (int b = 0; b < NB; ++b) {
         const int o = b * LB16;
         if (wave == 0) {
@@ -304,6 +332,30 @@ __device__ __forceinline__ void leaf_lds(R (*S)[LDL], R (*X)[LDL], R (*Tm)[LB16]
                 diag16<R, true>(S, X, o, lb, gcol, info, failed);
             else
                 diag16<R, false>(S, X, o, lb, gcol, info, failed);
+        } else if (b == 2 && wave == 1) {
+            // beside the sweeps, the inverse blocks whose inputs are final
+            // (partial sums of the last block row wait in the wave's scratch)
+            V4 t = {0, 0, 0, 0};
+            tsum(1, 0, 0, 1, t);
+            stage(t);
+            apply(1, 0);
+        } else if (b == 3 && wave == 1) {
+            V4 t = {0, 0, 0, 0};
+            tsum(2, 1, 1, 2, t);
+            stage(t);
+            apply(2, 1);
+            V4 t31 = {0, 0, 0, 0};
+            tsum(3, 1, 1, 3, t31);
+            stage(t31);
+        } else if (b == 3 && wave == 2) {
+            V4 t = {0, 0, 0, 0};
+            tsum(2, 0, 0, 2, t);
+            stage(t);
+            apply(2, 0);
+        } else if (b == 3 && wave == 3) {
+            V4 t30 = {0, 0, 0, 0};
+            tsum(3, 0, 0, 2, t30);
+            stage(t30);
         }
         __syncthreads();
         if (factor) {
@@ -333,24 +385,24 @@ __device__ __forceinline__ void leaf_lds(R (*S)[LDL], R (*X)[LDL], R (*Tm)[LB16]
         }
     }
 
-    // inverse off-diagonal blocks, by distance d = i - b
-    for (int d = 1; d < NB; ++d) {
-        const int b = wave, i = b + d;
-        if (i < NB) {
-            V4 acc = {0, 0, 0, 0};
-            for (int k = b; k < i; ++k)  // T = sum_k L(i, k) X(k, b)
-                acc = mma16<R>(&S[k * LB16][i * LB16], LDL, 1, &X[b * LB16][k * LB16], 1, LDL, acc);
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq)
-                Tm[wave][acc_row<R>(lk, qq)][li] = acc[qq];  // Tm[c][r] = T(r, c)
-            __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's LDS stores done before reading them back
-            __builtin_amdgcn_wave_barrier();
-            V4 acc2 = {0, 0, 0, 0};  // X(i, b) = -inv(L(i, i)) T
-            acc2 = mma16<R>(&X[i * LB16][i * LB16], LDL, 1, &Tm[wave][0][0], 1, LB16 + 1, acc2);
-            put(X, i * LB16, b * LB16, acc2, R(-1), false);
-        }
-        __syncthreads();
+    // the last block row of the inverse: X(3, b) = -inv(L(3, 3)) sum_k L(3, k) X(k, b)
+    // (rows 1 and 2 and the partial sums above were formed beside the sweeps,
+    // each sum in the order of k)
+    if (wave == 0) {
+        V4 t = {0, 0, 0, 0};
+        tsum(3, 2, 2, 3, t);
+        stage(t);
+        apply(3, 2);
+    } else if (wave == 1) {
+        apply(3, 1);
+    } else if (wave == 3) {
+        V4 t = {0, 0, 0, 0};
+        unstage(t);
+        tsum(3, 0, 2, 3, t);
+        stage(t);
+        apply(3, 0);
     }
+    __syncthreads();
 
 }
 
@@ -766,13 +818,23 @@ __device__ __forceinline__ void leafc_lds(R (*S)[LEAF][LDL], R (*Xd)[LEAF], R (*
             mma16c<R>([&](int rr, int kk, R &re, R &im) { lget(i * LB16 + rr, k * LB16 + kk, re, im); },
                       [&](int kk, int cc, R &re, R &im) { xget(k * LB16 + kk, b * LB16 + cc, re, im); }, cr, ci);
     };
-    // X(i, b) = -inv(L(i, i)) T, T through this wave's scratch
-    auto finish = [&](int i, int b, const V4 &cr, const V4 &ci) {
+    // T to this wave's scratch (Tm[.][c][r] = T(r, c)), and back
+    auto stage = [&](const V4 &cr, const V4 &ci) {
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {  // Tm[.][c][r] = T(r, c)
+        for (int qq = 0; qq < 4; ++qq) {
             Tm[wave][0][acc_row<R>(lk, qq)][li] = cr[qq];
             Tm[wave][1][acc_row<R>(lk, qq)][li] = ci[qq];
         }
+    };
+    auto unstage = [&](V4 &cr, V4 &ci) {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+            cr[qq] = Tm[wave][0][acc_row<R>(lk, qq)][li];
+            ci[qq] = Tm[wave][1][acc_row<R>(lk, qq)][li];
+        }
+    };
+    // X(i, b) = -inv(L(i, i)) T, T staged
+    auto apply = [&](int i, int b) {
         __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's LDS stores done before reading them back
         __builtin_amdgcn_wave_barrier();
         V4 c2r = {0, 0, 0, 0}, c2i = {0, 0, 0, 0};
@@ -787,7 +849,6 @@ __device__ __forceinline__ void leafc_lds(R (*S)[LEAF][LDL], R (*Xd)[LEAF], R (*
         __builtin_amdgcn_wave_barrier();
     };
     static_assert(NB == 4, "the inverse schedule below is written for four sub-blocks");
-    V4 t31r = {0, 0, 0, 0}, t31i = {0, 0, 0, 0}, t30r = {0, 0, 0, 0}, t30i = {0, 0, 0, 0};
 
     for (int b = 0; b < NB; ++b) {
         const int o = b * LB16;
@@ -798,20 +859,28 @@ __device__ __forceinline__ void leafc_lds(R (*S)[LEAF][LDL], R (*Xd)[LEAF], R (*
                 diag16c<R, false>(S[0], S[1], Xd[0], Xd[1], o, lb, gcol, info, failed);
         } else if (b == 2 && wave == 1) {
             // beside the sweeps, the inverse blocks whose inputs are final
+            // (partial sums of the last block row wait in the wave's scratch)
             V4 tr = {0, 0, 0, 0}, ti = {0, 0, 0, 0};
             tsum(1, 0, 0, 1, tr, ti);
-            finish(1, 0, tr, ti);
+            stage(tr, ti);
+            apply(1, 0);
         } else if (b == 3 && wave == 1) {
             V4 tr = {0, 0, 0, 0}, ti = {0, 0, 0, 0};
             tsum(2, 1, 1, 2, tr, ti);
-            finish(2, 1, tr, ti);
-            tsum(3, 1, 1, 3, t31r, t31i);
+            stage(tr, ti);
+            apply(2, 1);
+            V4 ur = {0, 0, 0, 0}, ui = {0, 0, 0, 0};
+            tsum(3, 1, 1, 3, ur, ui);
+            stage(ur, ui);
         } else if (b == 3 && wave == 2) {
             V4 tr = {0, 0, 0, 0}, ti = {0, 0, 0, 0};
             tsum(2, 0, 0, 2, tr, ti);
-            finish(2, 0, tr, ti);
+            stage(tr, ti);
+            apply(2, 0);
         } else if (b == 3 && wave == 3) {
-            tsum(3, 0, 0, 2, t30r, t30i);
+            V4 tr = {0, 0, 0, 0}, ti = {0, 0, 0, 0};
+            tsum(3, 0, 0, 2, tr, ti);
+            stage(tr, ti);
         }
         __syncthreads();
         if (factor) {
@@ -860,12 +929,16 @@ __device__ __forceinline__ void leafc_lds(R (*S)[LEAF][LDL], R (*Xd)[LEAF], R (*
     if (wave == 0) {
         V4 tr = {0, 0, 0, 0}, ti = {0, 0, 0, 0};
         tsum(3, 2, 2, 3, tr, ti);
-        finish(3, 2, tr, ti);
+        stage(tr, ti);
+        apply(3, 2);
     } else if (wave == 1) {
-        finish(3, 1, t31r, t31i);
+        apply(3, 1);
     } else if (wave == 3) {
-        tsum(3, 0, 2, 3, t30r, t30i);
-        finish(3, 0, t30r, t30i);
+        V4 tr = {0, 0, 0, 0}, ti = {0, 0, 0, 0};
+        unstage(tr, ti);
+        tsum(3, 0, 2, 3, tr, ti);
+        stage(tr, ti);
+        apply(3, 0);
     }
     __syncthreads();
 }
