@@ -32,6 +32,7 @@
 #include "spd_rect.hpp"
 #include "spd_syrk.hpp"
 #include "spd_tile.hpp"
+#include "spd_subst.hpp"
 #include "spd_check.hpp"
 
 namespace spd {
@@ -261,8 +262,12 @@ static int set_info(int *info, hipStream_t s)
 //                 L21 of four consecutive steps (potrf) / merge temporaries (both)
 //            TMP  max(T*T, T*n_rhs)   one block row of the right-hand side
 struct Layout {
-    int64_t T, nt, inv, w, wsz, tmp, ctr, flags, q, ldq, kq, qsz, gf, gb, part, total;  // offsets / sizes in elements
+    int64_t T, nt, inv, w, wsz, tmp, ctr, flags, q, ldq, kq, qsz, gf, gb, part, z, ldz, sflags,
+        total;  // offsets / sizes in elements
 };
+
+// Right-hand-side columns of a piece of the one-launch back substitution
+static int64_t subst_tc(int64_t n_rhs) { return n_rhs <= 32 ? 32 : 64; }
 
 // The trailing-update panel W is stored with its leading dimension rounded up
 // to SYRK_LDW rows and its width to SYRK_KP columns, the padding zeroed, so the
@@ -306,9 +311,17 @@ static Layout make_layout(int64_t n, int64_t n_rhs, int64_t T_A, int64_t esize)
         L.gf = L.q + align_up(2 * L.qsz, al);
         L.gb = L.gf + align_up(L.nt * L.T * L.T, al);
         L.part = L.gb + align_up(L.nt * L.T * L.T, al);
-        L.total = L.part + align_up(CHAIN_SPLITS * L.T * n_rhs, al);
+        // the one-launch back substitution's buffer of one tile row (T x n_rhs,
+        // leading dimension T) and its flags
+        const int64_t tc = subst_tc(n_rhs);
+        L.ldz = L.T;
+        L.z = L.part + align_up(CHAIN_SPLITS * L.T * n_rhs, al);
+        L.sflags = L.z + align_up(L.T * n_rhs, al);
+        const int64_t nfl = subst_flag_ints((int)L.nt, (int)cdiv(L.T, SUB_TR), (int)cdiv(n_rhs, tc));
+        L.total = L.sflags + align_up(cdiv(4 * nfl, esize), al);
     } else {
-        L.gf = L.gb = L.part = L.q;
+        L.gf = L.gb = L.part = L.z = L.sflags = L.q;
+        L.ldz = 0;
         L.total = L.q;
     }
     return L;
@@ -398,14 +411,16 @@ enum {
     OPT_TILE_WAIT_US,
     OPT_COLUMN_FIRST_ROWS,
     OPT_TILE_HOLD_ROWS,
+    OPT_SUBST_LAUNCH,
     OPT_COUNT
 };
-static const int64_t k_opt_default[OPT_COUNT] = {1, 1, -1, -1, 16384, 1, 2000000, 8192, 8192};
-static std::atomic<int64_t> g_opt_store[OPT_COUNT] = {{1}, {1}, {-1}, {-1}, {16384}, {1}, {2000000}, {8192}, {8192}};
+static const int64_t k_opt_default[OPT_COUNT] = {1, 1, -1, -1, 16384, 1, 2000000, 8192, 8192, 2097152};
+static std::atomic<int64_t> g_opt_store[OPT_COUNT] = {{1},     {1},       {-1},   {-1},   {16384},
+                                                      {1},     {2000000}, {8192}, {8192}, {2097152}};
 struct Options {
     int64_t v[OPT_COUNT];
 };
-static thread_local Options g_opt = {{1, 1, -1, -1, 16384, 1, 2000000, 8192, 8192}};
+static thread_local Options g_opt = {{1, 1, -1, -1, 16384, 1, 2000000, 8192, 8192, 2097152}};
 
 static void snapshot_options()
 {
@@ -464,6 +479,19 @@ static int64_t column_first_rows() { return g_opt.v[OPT_COLUMN_FIRST_ROWS]; }
 // the CU's whole LDS.  There the chain is the longer path, and the tile's
 // leaves sharing SIMDs with the trailing update run two to three times slower.
 static int64_t tile_hold_rows() { return g_opt.v[OPT_TILE_HOLD_ROWS]; }
+
+// The back substitution runs in one launch (subst_kernel) while n n_rhs
+// (four times that for complex types) is at most SPD_OPT_SUBST_LAUNCH, else
+// (and always when it is 0) by block steps on the stream and one auxiliary
+// stream.  The one launch removes the block steps' launch and event latency,
+// which is what bounds small and medium solves; at n = 32768, n_rhs = 128 its
+// block products (a 32-row piece at a time, one chunk of loads in flight)
+// are slower than the block steps' large updates.  Its waits are bounded by
+// SPD_OPT_TILE_WAIT_US.
+static bool subst_launch_enabled(int64_t n, int64_t nrhs, bool cplx)
+{
+    return (double)n * (double)nrhs * (cplx ? 4.0 : 1.0) <= (double)g_opt.v[OPT_SUBST_LAUNCH];
+}
 
 // The auxiliary streams and events of the lookahead schedules: one set per
 // host thread and device, created on first use and kept until spd_release is
@@ -1312,6 +1340,47 @@ struct Solver {
         return 0;
     }
 
+    // The back substitution L^H X = Y in one launch (subst_kernel), with the
+    // inverse of every diagonal tile in the workspace's INV region; Z and the
+    // flags in the workspace (the flags zeroed first).  status (may be null)
+    // becomes -1 if a wait of the launch runs out; X is then NaN.
+    template <int TC>
+    static int back_subst_tc(int64_t n, int64_t nrhs, const E *A, int64_t lda, E *B, int64_t ldb, const Layout &L,
+                             const int *info, int *status, void *work, hipStream_t s)
+    {
+        SubstArgs p;
+        p.A = A;
+        p.lda = lda;
+        p.Inv = (const E *)work + L.inv;
+        p.B = B;
+        p.ldb = ldb;
+        p.Z = (E *)work + L.z;
+        p.ldz = L.ldz;
+        p.n = (int)n;
+        p.nrhs = (int)nrhs;
+        p.T = (int)L.T;
+        p.nt = (int)L.nt;
+        p.nr = (int)cdiv(L.T, SUB_TR);
+        p.nc = (int)cdiv(nrhs, TC);
+        p.flags = (int *)((E *)work + L.sflags);
+        p.info = info;
+        p.status = status;
+        p.limit = tile_wait_ticks();
+        SPD_TRY(zero2d<int>(p.flags, 1, subst_flag_ints(p.nt, p.nr, p.nc), 1, s));
+        const unsigned grid = (unsigned)subst_groups(p);
+        SPD_VALIDATE((check_subst<R, CPLX, TC>(p, grid, g_chk)));
+        subst_kernel<R, CPLX, TC><<<dim3(grid), dim3(SUB_THREADS), 0, s>>>(p);
+        SPD_CHECK_LAUNCH("subst_kernel");
+        return 0;
+    }
+    static int back_subst(int64_t n, int64_t nrhs, const E *A, int64_t lda, E *B, int64_t ldb, const Layout &L,
+                          const int *info, int *status, void *work, hipStream_t s)
+    {
+        if (subst_tc(nrhs) == 32)
+            return back_subst_tc<32>(n, nrhs, A, lda, B, ldb, L, info, status, work, s);
+        return back_subst_tc<64>(n, nrhs, A, lda, B, ldb, L, info, status, work, s);
+    }
+
     // backward = false: the forward substitution L Y = B only
     static int potrs(int64_t n, int64_t nrhs, const E *A, int64_t lda, E *B, int64_t ldb, int64_t T_A,
                      const int *info, void *work, hipStream_t s, bool backward = true)
@@ -1321,10 +1390,15 @@ struct Solver {
         const Layout L = make_layout(n, nrhs, T_A, sizeof(E));
         {
             ProfScope ps(PROF_SOLVE, FMUL * (backward ? 2.0 : 1.0) * (double)n * n * nrhs, s);
+            // the back substitution in one launch: the sweeps below only solve
+            // L Y = B (and build the tile inverses)
+            const bool one = backward && subst_launch_enabled(n, nrhs, CPLX);
             if (rect_usable(lda))
-                SPD_TRY(potrs_blocks(n, nrhs, A, lda, B, ldb, L, info, work, s, backward));
+                SPD_TRY(potrs_blocks(n, nrhs, A, lda, B, ldb, L, info, work, s, backward && !one));
             else
-                SPD_TRY(potrs_general(n, nrhs, A, lda, B, ldb, L, info, work, s, backward));
+                SPD_TRY(potrs_general(n, nrhs, A, lda, B, ldb, L, info, work, s, backward && !one));
+            if (one)  // d_info is read-only here: a wait that runs out shows as NaN in X
+                SPD_TRY(back_subst(n, nrhs, A, lda, B, ldb, L, info, nullptr, work, s));
         }
         return nan_fill(n, nrhs, B, ldb, info, s);
     }
@@ -1428,7 +1502,9 @@ struct Solver {
             SPD_TRY(logdet(n, A, lda, info, logdet_out, s));
         {
             ProfScope ps(PROF_SOLVE, FMUL * (double)n * n * nrhs, s);
-            if (blocks)
+            if (subst_launch_enabled(n, nrhs, CPLX))
+                SPD_TRY(back_subst(n, nrhs, A, lda, B, ldb, L, info, info, work, s));
+            else if (blocks)
                 SPD_TRY(potrs_blocks(n, nrhs, A, lda, B, ldb, L, info, work, s, true, false, nullptr, false));
             else
                 SPD_TRY(potrs_general(n, nrhs, A, lda, B, ldb, L, info, work, s, true, false, false));

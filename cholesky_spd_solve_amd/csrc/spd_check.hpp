@@ -26,6 +26,7 @@
 #include "spd_gemm.hpp"
 #include "spd_kernels.hpp"
 #include "spd_rect.hpp"
+#include "spd_subst.hpp"
 #include "spd_syrk.hpp"
 #include "spd_tile.hpp"
 
@@ -486,6 +487,104 @@ static bool check_tile(const TileArgs &p, unsigned grid, Checker &c)
         }
     }
     return true;
+}
+
+// Replay of subst_kernel (spd_subst.hpp): the role of every workgroup, the
+// column segments each one reads and writes (the operand loads are masked to
+// them), and that every flag or counter a role waits for is raised by roles
+// with smaller ids only (the counter of (i, ct) by exactly the row pieces of
+// tile row i).
+template <typename R, bool CPLX, int TC>
+static bool check_subst(const SubstArgs &p, unsigned grid, Checker &c)
+{
+    typedef typename Elem<R, CPLX>::type E;
+    const char *kn = "subst_kernel";
+    if (p.nt < 1 || p.T < 1 || p.n < 1 || p.nrhs < 1 || (int64_t)(p.nt - 1) * p.T >= p.n ||
+        (int64_t)p.nt * p.T < p.n || p.nr != (p.T + SUB_TR - 1) / SUB_TR || p.nc != (p.nrhs + TC - 1) / TC ||
+        p.ldz < p.T || p.ldb < p.n || p.lda < p.n || grid != (unsigned)subst_groups(p)) {
+        c.err = "subst_kernel: launch shape does not match the problem";
+        return false;
+    }
+    if (p.info != nullptr && !c.access(p.info, 4, false, kn, 0, 0))
+        return false;
+    if (p.status != nullptr && !c.access(p.status, 4, true, kn, 0, 0))
+        return false;
+    if (!c.access(p.flags, 4 * (size_t)subst_flag_ints(p.nt, p.nr, p.nc), true, kn, 0, 0))
+        return false;
+    const int nfz = p.nt * p.nr * p.nc;
+    std::vector<int> zprod(nfz, -1), xcount(p.nt * p.nc, 0), xlast(p.nt * p.nc, -1);
+    for (unsigned g = 0; g < grid; ++g) {
+        int i, rt, ct;
+        const int kind = subst_role(p, (int)g, i, rt, ct);
+        if (i < 0 || i >= p.nt || rt < 0 || rt >= subst_rows(p, i) || ct < 0 || ct >= p.nc) {
+            c.err = "subst_kernel: a workgroup without a role";
+            return false;
+        }
+        if (kind == SUB_R) {
+            int &z = zprod[(i * p.nr + rt) * p.nc + ct];
+            if (z >= 0) {
+                c.err = "subst_kernel: a piece of Z is written by two workgroups";
+                return false;
+            }
+            z = (int)g;
+        } else {
+            ++xcount[i * p.nc + ct];
+            xlast[i * p.nc + ct] = (int)g;
+        }
+    }
+    for (int i = 0; i < p.nt; ++i)
+        for (int ct = 0; ct < p.nc; ++ct)
+            if (xcount[i * p.nc + ct] != subst_rows(p, i)) {
+                c.err = "subst_kernel: a counter does not count every row piece";
+                return false;
+            }
+    const E *A = (const E *)p.A, *Iv = (const E *)p.Inv;
+    const E *B = (const E *)p.B, *Z = (const E *)p.Z;
+    auto rows = [&](int ti) { return std::min(p.T, p.n - ti * p.T); };
+    // rows [r0, r0 + nr) of columns [c0, c0 + nc) of M (ld)
+    auto seg = [&](const E *M, int64_t ld, int64_t r0, int nr, int64_t c0, int nc, bool write, unsigned g) {
+        for (int col = 0; col < nc && nr > 0; ++col)
+            if (!c.access(M + r0 + (c0 + col) * ld, sizeof(E) * (size_t)nr, write, kn, g, 0))
+                return false;
+        return true;
+    };
+    auto after = [&](unsigned g, int producer) {
+        if (producer < 0 || producer >= (int)g) {
+            char buf[128];
+            snprintf(buf, sizeof buf, "subst_kernel: workgroup %u waits for workgroup %d", g, producer);
+            c.err = buf;
+            return false;
+        }
+        return true;
+    };
+    for (unsigned g = 0; g < grid; ++g) {
+        int i, rt, ct;
+        const int kind = subst_role(p, (int)g, i, rt, ct);
+        const int tki = rows(i), r0 = rt * SUB_TR, c0 = ct * TC;
+        const int nrow = std::min(SUB_TR, tki - r0), ncol = std::min(TC, p.nrhs - c0);
+        const int64_t row0 = (int64_t)i * p.T;
+        if (kind == SUB_R) {
+            if (!seg(B, p.ldb, row0 + r0, nrow, c0, ncol, false, g) ||
+                !seg(Z, p.ldz, r0, nrow, c0, ncol, true, g))
+                return false;
+            for (int j = p.nt - 1; j > i; --j) {
+                const int64_t rj = (int64_t)j * p.T;
+                if (!after(g, xlast[j * p.nc + ct]) || !seg(A, p.lda, rj, rows(j), row0 + r0, nrow, false, g) ||
+                    !seg(B, p.ldb, rj, rows(j), c0, ncol, false, g))
+                    return false;
+            }
+        } else {
+            for (int r = rt; r < subst_rows(p, i); ++r)
+                if (!after(g, zprod[(i * p.nr + r) * p.nc + ct]))
+                    return false;
+            if (!seg(Iv + (int64_t)i * p.T * p.T, p.T, r0, tki - r0, r0, nrow, false, g) ||
+                !seg(Z, p.ldz, r0, tki - r0, c0, ncol, false, g) ||
+                !seg(B, p.ldb, row0 + r0, nrow, c0, ncol, true, g))
+                return false;
+        }
+    }
+    // a wait that runs out: the last workgroup fills X with NaN
+    return seg(B, p.ldb, 0, p.n, 0, p.nrhs, true, 0);
 }
 
 // dst(0:m, 0:n) written, src(0:m, 0:n) read (either may be null)

@@ -1,0 +1,396 @@
+// The back substitution L^H X = Y of the solve in one launch (JAXMg paper,
+// "Software design": the triangular solves of potrs after the factorization;
+// here by tile rows of T_A from the last one up):
+//
+//   X_i = inv(L_ii)^H (Y_i - sum_{j > i} L_ji^H X_j)
+//
+// with the inverse of every diagonal tile already built (the factorization
+// keeps them).  Tile row i is cut into row pieces of SUB_TR rows and column
+// pieces of TC right-hand sides; each piece (rt, ct) has two roles:
+//
+//   R(i, rt, ct): Z = Y_i(rt, ct) - sum_{j > i} L_ji(:, rt)^H X_j(:, ct), a
+//                 term as soon as X_j(:, ct) is complete, in decreasing j;
+//                 Z goes to a workspace buffer (T rows, one per tile row in
+//                 turn);
+//   C(i, rt, ct): X_i(rt, ct) = sum_{r >= rt} inv(L_ii)^H(rt, r) Z(r, ct),
+//                 once the pieces r >= rt of Z are there; X goes into B.
+//
+// A counter per (i, ct) counts the C roles done (X_i(:, ct) is complete when
+// it reaches the tile row's number of row pieces); a flag per R role marks
+// its piece of Z.  Workgroup ids run over the tile rows from the last: the R
+// roles of tile row i, then its C roles.  Every role waits only for roles
+// with smaller ids, which are dispatched before it, so no waiting workgroup
+// holds back one it waits for.  Every wait is bounded in time as in the
+// one-launch diagonal tile (a wait that runs out raises an abort word that
+// ends the others and sets info to -1), and the last workgroup to finish
+// clears the flags, which are zero between launches (and, if a wait ran out,
+// fills X with NaN).
+//
+// The single Z buffer is safe: R(i, rt, ct) writes its piece only after
+// X_{i+1}(:, ct) is complete, that is after every C role of tile row i + 1
+// that reads column piece ct of Z has finished.
+#pragma once
+
+#include "spd_kernels.hpp"
+
+namespace spd {
+
+constexpr int SUB_TR = 32;        // rows of a piece
+constexpr int SUB_THREADS = 512;  // threads of a workgroup: two halves of 256
+enum { SUB_R = 0, SUB_C = 1 };
+
+struct SubstArgs {
+    const void *A;    // L: first element, column-major, lda; lower triangle read
+    int64_t lda;
+    const void *Inv;  // inv(L_kk) at Inv + k T T, leading dimension T; its 64 x 64
+                      // blocks on and below the diagonal are read (those on the
+                      // diagonal as whole squares, zero above the diagonal)
+    void *B;          // Y on entry, X on exit; ldb
+    int64_t ldb;
+    void *Z;          // T x nrhs buffer, leading dimension ldz >= T
+    int64_t ldz;
+    int n, nrhs, T, nt;
+    int nr;           // row pieces of a whole tile row: ceil(T / SUB_TR)
+    int nc;           // column pieces: ceil(nrhs / TC)
+    int *flags;       // subst_flag_ints(nt, nr, nc) ints, zero between launches
+    const int *info;  // nothing is done when non-zero on entry (may be null)
+    int *status;      // set to -1 if a wait ran out (may be null); X is then NaN
+    int64_t limit;    // longest wait, in wall-clock ticks (100 MHz)
+};
+
+__host__ __device__ inline int subst_flag_ints(int nt, int nr, int nc) { return nt * nr * nc + nt * nc + 2; }
+
+// row pieces of tile row i
+__host__ __device__ inline int subst_rows(const SubstArgs &p, int i)
+{
+    const int tk = (p.n - i * p.T) < p.T ? p.n - i * p.T : p.T;
+    return (tk + SUB_TR - 1) / SUB_TR;
+}
+
+__host__ __device__ inline int subst_groups(const SubstArgs &p)
+{
+    return 2 * p.nc * (p.nr * (p.nt - 1) + subst_rows(p, p.nt - 1));
+}
+
+// Role of workgroup g: kind, tile row i, row piece rt, column piece ct.
+__host__ __device__ inline int subst_role(const SubstArgs &p, int g, int &i, int &rt, int &ct)
+{
+    const int nrl = subst_rows(p, p.nt - 1), first = 2 * nrl * p.nc;
+    int per, rem;
+    if (g < first) {
+        i = p.nt - 1;
+        per = nrl;
+        rem = g;
+    } else {
+        const int q = g - first, blk = 2 * p.nr * p.nc;
+        i = p.nt - 2 - q / blk;
+        per = p.nr;
+        rem = q % blk;
+    }
+    const int kind = rem < per * p.nc ? SUB_R : SUB_C;
+    const int idx = rem % (per * p.nc);
+    rt = idx / p.nc;
+    ct = idx % p.nc;
+    return kind;
+}
+
+// Thread 0 polls *f until it reaches target (or the abort word is raised, or
+// the time limit passes: then it raises the abort word and sets info = -1
+// unless info is set); then the workgroup proceeds.
+__device__ inline void subst_wait(const int *f, int target, int *abort_word, int64_t limit, int *info)
+{
+    if (threadIdx.x == 0) {
+        const int64_t t0 = (int64_t)wall_clock64(), max_polls = limit / 16 + 64;
+        for (int64_t polls = 0;; ++polls) {
+            if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target)
+                break;
+            if (__hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+                break;
+            if ((int64_t)wall_clock64() - t0 > limit || polls > max_polls) {
+                __hip_atomic_store(abort_word, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (info != nullptr)
+                    atomicCAS(info, 0, -1);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+}
+
+// Every wave's stores are made visible at agent scope, then thread 0 adds 1
+// to the counter (or raises the flag).
+__device__ inline void subst_signal(int *f)
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (threadIdx.x == 0)
+        __hip_atomic_fetch_add(f, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The SUB_TR x TC piece a half workgroup (256 threads, h = tid / 256)
+// accumulates: wave w of the half holds rows 16 (w % 2) .. + 16 and columns
+// (TC / 2) (w / 2) .. + TC / 2 as FN 16 x 16 accumulators (real and
+// imaginary planes for complex types); accumulator b element q of lane
+// (li, lk) is (16 (w % 2) + li, (TC / 2) (w / 2) + 16 b + acc_row(lk, q)).
+template <typename R, bool CPLX, int TC>
+struct SubstAcc {
+    typedef typename AccT<R>::type V4;
+    typedef typename Elem<R, CPLX>::type E;
+    static constexpr int FN = TC / 32;
+    static constexpr int NP = CPLX ? 2 : 1;
+    V4 t[NP][FN];
+
+    __device__ __forceinline__ static int row() { return 16 * ((threadIdx.x >> 6) & 1) + (threadIdx.x & 15); }
+    __device__ __forceinline__ static int col(int b, int q)
+    {
+        return (TC / 2) * ((threadIdx.x >> 7) & 1) + 16 * b + acc_row<R>((threadIdx.x & 63) >> 4, q);
+    }
+    __device__ __forceinline__ void zero()
+    {
+#pragma unroll
+        for (int c = 0; c < NP; ++c)
+#pragma unroll
+            for (int b = 0; b < FN; ++b)
+                t[c][b] = V4{0, 0, 0, 0};
+    }
+    // -src(r, c) for r < nr, c < nc (zero elsewhere)
+    __device__ __forceinline__ void load_neg(const E *src, int64_t ld, int nr, int nc)
+    {
+#pragma unroll
+        for (int b = 0; b < FN; ++b)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = row(), c = col(b, q);
+                R x = R(0), y = R(0);
+                if (r < nr && c < nc)
+                    Elem<R, CPLX>::load(src + r + (int64_t)c * ld, x, y);
+                t[0][b][q] = -x;
+                if constexpr (CPLX)
+                    t[NP - 1][b][q] = -y;
+            }
+    }
+    // dst(r, c) = sg * this for r < nr, c < nc
+    __device__ __forceinline__ void store(E *dst, int64_t ld, int nr, int nc, R sg) const
+    {
+#pragma unroll
+        for (int b = 0; b < FN; ++b)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = row(), c = col(b, q);
+                if (r < nr && c < nc)
+                    Elem<R, CPLX>::store(dst + r + (int64_t)c * ld, sg * t[0][b][q], sg * t[NP - 1][b][q]);
+            }
+    }
+    // the second half's accumulators are added to the first's through M
+    // (at least NP SUB_TR TC elements); both halves call it
+    __device__ __forceinline__ void fold(R *M)
+    {
+        const int slot = threadIdx.x & 255;
+        if (threadIdx.x >= 256) {
+#pragma unroll
+            for (int c = 0; c < NP; ++c)
+#pragma unroll
+                for (int b = 0; b < FN; ++b)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        M[((c * FN + b) * 4 + q) * 256 + slot] = t[c][b][q];
+        }
+        __syncthreads();
+        if (threadIdx.x < 256) {
+#pragma unroll
+            for (int c = 0; c < NP; ++c)
+#pragma unroll
+                for (int b = 0; b < FN; ++b)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        t[c][b][q] += M[((c * FN + b) * 4 + q) * 256 + slot];
+        }
+        __syncthreads();
+    }
+};
+
+// Each half's LDS: one chunk of both operands
+template <typename R, bool CPLX, int TC, int KC>
+struct SubstStage {
+    static constexpr int NP = CPLX ? 2 : 1;
+    R As[NP][SUB_TR][KC + 1];  // As[.][r][k] = conj(M(k0 + k, r))
+    R Bs[NP][TC][KC + 1];      // Bs[.][c][k] = Q(k0 + k, c)
+};
+
+// acc += M^H Q: M(k, r) = m[k + r ldm] for k < K, r < nr and Q(k, c) =
+// q[k + c ldq] for k < K, c < nc (zero elsewhere).  The depth goes in steps
+// of 2 KC: half h of the workgroup takes [2 KC s + h KC, + KC) into its own
+// stage and accumulators, and the loads of its next chunk are in flight
+// while its matrix-core waves work on the current one.
+template <typename R, bool CPLX, int TC, int KC>
+__device__ __forceinline__ void subst_mma(SubstAcc<R, CPLX, TC> &acc, const typename Elem<R, CPLX>::type *m,
+                                          int64_t ldm, int K, int nr, const typename Elem<R, CPLX>::type *q,
+                                          int64_t ldq, int nc, SubstStage<R, CPLX, TC, KC> *st)
+{
+    constexpr int NP = CPLX ? 2 : 1;
+    constexpr int LA = SUB_TR * KC / 256, LB = TC * KC / 256;
+    static_assert((SUB_TR * KC) % 256 == 0 && (TC * KC) % 256 == 0, "chunk loads must divide evenly");
+    const int h = threadIdx.x >> 8, tid = threadIdx.x & 255, wave = tid >> 6;
+    const int ro = 16 * (wave & 1), co = (TC / 2) * (wave >> 1);
+    SubstStage<R, CPLX, TC, KC> &S = st[h];
+    R ra[NP][LA], rb[NP][LB];
+    auto fetch = [&](int k0) {
+#pragma unroll
+        for (int u = 0; u < LA; ++u) {
+            const int e = tid + 256 * u, k = e % KC, r = e / KC;
+            R x = R(0), y = R(0);
+            if (k0 + k < K && r < nr)
+                Elem<R, CPLX>::load(m + (k0 + k) + (int64_t)r * ldm, x, y);
+            ra[0][u] = x;
+            if constexpr (CPLX)
+                ra[NP - 1][u] = -y;
+        }
+#pragma unroll
+        for (int u = 0; u < LB; ++u) {
+            const int e = tid + 256 * u, k = e % KC, c = e / KC;
+            R x = R(0), y = R(0);
+            if (k0 + k < K && c < nc)
+                Elem<R, CPLX>::load(q + (k0 + k) + (int64_t)c * ldq, x, y);
+            rb[0][u] = x;
+            if constexpr (CPLX)
+                rb[NP - 1][u] = y;
+        }
+    };
+    const int steps = (K + 2 * KC - 1) / (2 * KC);
+    fetch(h * KC);
+    for (int s = 0; s < steps; ++s) {
+        __syncthreads();  // the previous chunk's products are done with the LDS
+#pragma unroll
+        for (int pl = 0; pl < NP; ++pl) {
+#pragma unroll
+            for (int u = 0; u < LA; ++u) {
+                const int e = tid + 256 * u;
+                S.As[pl][e / KC][e % KC] = ra[pl][u];
+            }
+#pragma unroll
+            for (int u = 0; u < LB; ++u) {
+                const int e = tid + 256 * u;
+                S.Bs[pl][e / KC][e % KC] = rb[pl][u];
+            }
+        }
+        __syncthreads();
+        if (s + 1 < steps)
+            fetch(2 * KC * (s + 1) + h * KC);
+        // two 16-deep steps at a time: their operand reads in flight together,
+        // without holding a whole chunk's operands in registers
+#pragma unroll 2
+        for (int k = 0; k < KC; k += 16) {
+#pragma unroll
+            for (int b = 0; b < acc.FN; ++b) {
+                if constexpr (!CPLX) {
+                    acc.t[0][b] = mma16<R>(&S.As[0][ro][k], 1, KC + 1, &S.Bs[0][co + 16 * b][k], 1, KC + 1, acc.t[0][b]);
+                } else {
+                    mma16c<R>(
+                        [&](int rr, int kk, R &re, R &im) {
+                            re = S.As[0][ro + rr][k + kk];
+                            im = S.As[1][ro + rr][k + kk];
+                        },
+                        [&](int kk, int cc, R &re, R &im) {
+                            re = S.Bs[0][co + 16 * b + cc][k + kk];
+                            im = S.Bs[1][co + 16 * b + cc][k + kk];
+                        },
+                        acc.t[0][b], acc.t[1][b]);
+                }
+            }
+        }
+    }
+}
+
+// SUB_THREADS threads: two halves of 256 share each product (subst_mma).
+template <typename R, bool CPLX, int TC>
+__global__ void __launch_bounds__(SUB_THREADS) subst_kernel(const SubstArgs p)
+{
+    typedef typename Elem<R, CPLX>::type E;
+    constexpr int KC = CPLX ? 32 : 64;
+    typedef SubstStage<R, CPLX, TC, KC> Stage;
+    static_assert(sizeof(Stage) >= sizeof(R) * (CPLX ? 2 : 1) * SUB_TR * TC, "the fold needs one stage");
+    __shared__ Stage st[2];
+    __shared__ int skip, last;
+
+    int i, rt, ct;
+    const int kind = subst_role(p, (int)blockIdx.x, i, rt, ct);
+    const int tid = threadIdx.x;
+    const int frows = p.nt * p.nr * p.nc;
+    int *const abort_word = p.flags + frows + p.nt * p.nc;
+    int *const ctr = abort_word + 1;
+    auto fZ = [&](int ti, int r, int c) { return p.flags + (ti * p.nr + r) * p.nc + c; };
+    auto fX = [&](int ti, int c) { return p.flags + frows + ti * p.nc + c; };
+    auto tile_rows = [&](int ti) { return (p.n - ti * p.T) < p.T ? p.n - ti * p.T : p.T; };
+    const E *const A = (const E *)p.A;
+    E *const B = (E *)p.B;
+    E *const Z = (E *)p.Z;
+    const int tki = tile_rows(i), r0 = rt * SUB_TR, c0 = ct * TC;
+    const int nrow = (tki - r0) < SUB_TR ? tki - r0 : SUB_TR;
+    const int ncol = (p.nrhs - c0) < TC ? p.nrhs - c0 : TC;
+    const int64_t row0 = (int64_t)i * p.T;  // first row of tile row i
+    const bool first = tid < 256;          // the half that holds the result
+
+    if (tid == 0)
+        skip = (p.info != nullptr && *(volatile const int *)p.info != 0) ? 1 : 0;
+    __syncthreads();
+    if (!skip) {
+        SubstAcc<R, CPLX, TC> acc;
+        if (kind == SUB_R) {
+            if (first)
+                acc.load_neg(B + row0 + r0 + (int64_t)c0 * p.ldb, p.ldb, nrow, ncol);
+            else
+                acc.zero();
+            for (int j = p.nt - 1; j > i; --j) {
+                subst_wait(fX(j, ct), subst_rows(p, j), abort_word, p.limit, p.status);
+                const int64_t rj = (int64_t)j * p.T;
+                // -Z += L(rows of j, columns of the piece)^H X_j(:, ct)
+                subst_mma<R, CPLX, TC, KC>(acc, A + rj + (row0 + r0) * p.lda, p.lda, tile_rows(j), nrow,
+                                           B + rj + (int64_t)c0 * p.ldb, p.ldb, ncol, st);
+            }
+            __syncthreads();
+            acc.fold(&st[0].As[0][0][0]);
+            if (first)
+                acc.store(Z + r0 + (int64_t)c0 * p.ldz, p.ldz, nrow, ncol, R(-1));
+            subst_signal(fZ(i, rt, ct));
+        } else {
+            const int nri = subst_rows(p, i);
+            for (int r = rt; r < nri; ++r)
+                subst_wait(fZ(i, r, ct), 1, abort_word, p.limit, p.status);
+            acc.zero();
+            // X = inv(L_ii)(rows r0.., columns of the piece)^H Z(r0.., ct)
+            const E *const Iv = (const E *)p.Inv + (int64_t)i * p.T * p.T;
+            subst_mma<R, CPLX, TC, KC>(acc, Iv + r0 + (int64_t)r0 * p.T, p.T, tki - r0, nrow,
+                                       Z + r0 + (int64_t)c0 * p.ldz, p.ldz, ncol, st);
+            __syncthreads();
+            acc.fold(&st[0].As[0][0][0]);
+            if (first)
+                acc.store(B + row0 + r0 + (int64_t)c0 * p.ldb, p.ldb, nrow, ncol, R(1));
+            subst_signal(fX(i, ct));
+        }
+    }
+
+    // count out (the stores above visible first, for the NaN fill below)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (tid == 0)
+        last = atomicAdd(ctr, 1) == (int)gridDim.x - 1;
+    __syncthreads();
+    if (last) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        const bool aborted = *(volatile int *)abort_word != 0;
+        const int nf = subst_flag_ints(p.nt, p.nr, p.nc) - 1;  // all but the counter
+        for (int e = tid; e < nf; e += blockDim.x)
+            p.flags[e] = 0;
+        if (tid == 0)
+            *ctr = 0;
+        if (aborted) {
+            const R nan = __builtin_nan("");
+            for (int64_t e = tid; e < (int64_t)p.n * p.nrhs; e += blockDim.x)
+                Elem<R, CPLX>::store(B + e % p.n + (e / p.n) * p.ldb, nan, nan);
+        }
+    }
+}
+
+}  // namespace spd

@@ -283,10 +283,18 @@ const char *spd_last_error(void);
  *                            of them idle, and all of the CU's group memory),
  *                            so that no other kernel's waves share the working
  *                            waves' SIMDs (default 8192; 0: never)
+ *   SPD_OPT_SUBST_LAUNCH     the back substitution L^H X = Y runs in one
+ *                            launch whose workgroups hand solved pieces of X
+ *                            to each other through flags in the workspace
+ *                            (waits bounded as for TILE_LAUNCH) while
+ *                            n * n_rhs (4 n * n_rhs for complex types) is at
+ *                            most this value (default 2097152), otherwise by
+ *                            block steps on `stream` and an auxiliary stream
+ *                            (0: always by block steps)
  * spd_set_option returns 0, -1 for an unknown option, -2 for a value out of
  * range (LOOKAHEAD, TWO_STEP and TILE_LAUNCH take 0 or 1, PAIR_ROWS and
- * SYRK_DEEP_ROWS >= -1, RECT_TALL_ROWS, TILE_WAIT_US, COLUMN_FIRST_ROWS and
- * TILE_HOLD_ROWS >= 0);
+ * SYRK_DEEP_ROWS >= -1, RECT_TALL_ROWS, TILE_WAIT_US, COLUMN_FIRST_ROWS,
+ * TILE_HOLD_ROWS and SUBST_LAUNCH >= 0);
  * SPD_OPT_DEFAULT restores an option's default.
  * spd_get_option returns the current value (INT64_MIN for an unknown
  * option). */
@@ -299,7 +307,8 @@ typedef enum {
     SPD_OPT_TILE_LAUNCH = 6,
     SPD_OPT_TILE_WAIT_US = 7,
     SPD_OPT_COLUMN_FIRST_ROWS = 8,
-    SPD_OPT_TILE_HOLD_ROWS = 9
+    SPD_OPT_TILE_HOLD_ROWS = 9,
+    SPD_OPT_SUBST_LAUNCH = 10
 } spd_option_t;
 #define SPD_OPT_DEFAULT INT64_MIN
 int spd_set_option(spd_option_t opt, int64_t value);

@@ -66,6 +66,14 @@ def test_dry_run_in_bounds(lib, dt, n, nrhs, T):
     dry_solve(lib, CODE[dt], n, nrhs, T)
 
 
+@pytest.mark.parametrize("dt,n,nrhs,T", SHAPES[::3])
+def test_dry_run_block_step_back_substitution(lib, dt, n, nrhs, T):
+    """The back substitution by block steps (SPD_OPT_SUBST_LAUNCH = 0), which
+    these sizes otherwise do in one launch."""
+    with spd.options({spd.OPT_SUBST_LAUNCH: 0}):
+        dry_solve(lib, CODE[dt], n, nrhs, T)
+
+
 @pytest.mark.parametrize("dt,n,nrhs,T", [("f64", 333, 6, 64), ("c128", 333, 6, 64), ("f32", 300, 9, 128),
                                          ("f64", 1024, 16, 256)])
 def test_dry_run_padded_and_unaligned(lib, dt, n, nrhs, T):

@@ -58,20 +58,25 @@ def test_workspace_size(lib):
     # tile's 2 nb^2 + 2 int flags (nb = ceil(T / 64)) rounded up to 256 bytes
     # (768 bytes at T = 512, 256 at T = 100); for nrhs > 0 also two
     # buffers for the transposed solved block, (nrhs rounded up to 128) x (T
-    # rounded up to 32), two sets of nt*T*T chain products and 8 partial
-    # T x nrhs blocks; each rounded up to 256 bytes
+    # rounded up to 32), two sets of nt*T*T chain products, 8 partial
+    # T x nrhs blocks, the one-launch back substitution's T x nrhs block and
+    # its nt*nr*nc + nt*nc + 2 int flags (nr = ceil(T / 32) row pieces, nc =
+    # ceil(nrhs / 64) column pieces, 32 wide when nrhs <= 32); each rounded up
+    # to 256 bytes
     n, nrhs, T = 32768, 128, 512
-    el = (n // T) * T * T + 4 * n * T + T * T
-    solve = 2 * 128 * 512 + 2 * (n // T) * T * T + 8 * T * nrhs
-    assert f(1, n, 0, T) == el * 8 + 256 + 768
-    assert f(1, n, nrhs, T) == (el + solve) * 8 + 256 + 768
-    assert f(3, n, nrhs, T) == (el + solve) * 16 + 256 + 768
-    n, nrhs, T = 1000, 7, 100
     up = lambda a, b: -(-a // b) * b
+    el = (n // T) * T * T + 4 * n * T + T * T
+    solve = 2 * 128 * 512 + 2 * (n // T) * T * T + 8 * T * nrhs + T * nrhs
+    sflags = up(4 * (64 * 16 * 2 + 64 * 2 + 2), 256)
+    assert f(1, n, 0, T) == el * 8 + 256 + 768
+    assert f(1, n, nrhs, T) == (el + solve) * 8 + 256 + 768 + sflags
+    assert f(3, n, nrhs, T) == (el + solve) * 16 + 256 + 768 + sflags
+    n, nrhs, T = 1000, 7, 100
     el = up(10 * 100 * 100, 32) + 4 * up(1024 * 128, 32) + up(100 * 100, 32)
-    solve = up(2 * 128 * 128, 32) + 2 * up(10 * 100 * 100, 32) + up(8 * 100 * 7, 32)
+    solve = up(2 * 128 * 128, 32) + 2 * up(10 * 100 * 100, 32) + up(8 * 100 * 7, 32) + up(100 * 7, 32)
+    sflags = up(4 * (10 * 4 * 1 + 10 * 1 + 2), 256)
     assert f(1, n, 0, T) == el * 8 + 256 + 256
-    assert f(1, n, nrhs, T) == (el + solve) * 8 + 256 + 256
+    assert f(1, n, nrhs, T) == (el + solve) * 8 + 256 + 256 + sflags
     # T_A > n is clamped to n
     assert f(1, 100, 1, 1000) == f(1, 100, 1, 100)
 
@@ -166,12 +171,12 @@ def test_options_validate_and_restore(lib):
     import cholesky_spd_solve_amd as spd
     defaults = {spd.OPT_LOOKAHEAD: 1, spd.OPT_TWO_STEP: 1, spd.OPT_PAIR_ROWS: -1, spd.OPT_SYRK_DEEP_ROWS: -1,
                 spd.OPT_RECT_TALL_ROWS: 16384, spd.OPT_TILE_LAUNCH: 1, spd.OPT_TILE_WAIT_US: 2000000,
-                spd.OPT_COLUMN_FIRST_ROWS: 8192, spd.OPT_TILE_HOLD_ROWS: 8192}
+                spd.OPT_COLUMN_FIRST_ROWS: 8192, spd.OPT_TILE_HOLD_ROWS: 8192, spd.OPT_SUBST_LAUNCH: 2097152}
     for k, v in defaults.items():
         assert spd.get_option(k) == v
     assert lib.spd_set_option(0, 1) == -1
-    assert lib.spd_set_option(10, 1) == -1
-    assert lib.spd_get_option(10) == -(1 << 63)
+    assert lib.spd_set_option(11, 1) == -1
+    assert lib.spd_get_option(11) == -(1 << 63)
     assert lib.spd_set_option(spd.OPT_LOOKAHEAD, 2) == -2
     assert lib.spd_set_option(spd.OPT_TWO_STEP, -1) == -2
     assert lib.spd_set_option(spd.OPT_PAIR_ROWS, -2) == -2
@@ -180,6 +185,7 @@ def test_options_validate_and_restore(lib):
     assert lib.spd_set_option(spd.OPT_TILE_WAIT_US, -1) == -2
     assert lib.spd_set_option(spd.OPT_COLUMN_FIRST_ROWS, -1) == -2
     assert lib.spd_set_option(spd.OPT_TILE_HOLD_ROWS, -1) == -2
+    assert lib.spd_set_option(spd.OPT_SUBST_LAUNCH, -1) == -2
     with spd.options({spd.OPT_PAIR_ROWS: 0, spd.OPT_LOOKAHEAD: 0, spd.OPT_RECT_TALL_ROWS: 7}):
         assert spd.get_option(spd.OPT_PAIR_ROWS) == 0
         assert spd.get_option(spd.OPT_LOOKAHEAD) == 0
