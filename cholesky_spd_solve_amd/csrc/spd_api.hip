@@ -317,7 +317,7 @@ static Layout make_layout(int64_t n, int64_t n_rhs, int64_t T_A, int64_t esize)
         L.ldz = L.T;
         L.z = L.part + align_up(CHAIN_SPLITS * L.T * n_rhs, al);
         L.sflags = L.z + align_up(L.T * n_rhs, al);
-        const int64_t nfl = subst_flag_ints((int)L.nt, (int)cdiv(L.T, SUB_TR), (int)cdiv(n_rhs, tc));
+        const int64_t nfl = subst_flag_ints((int)L.nt, (int)cdiv(n_rhs, tc));
         L.total = L.sflags + align_up(cdiv(4 * nfl, esize), al);
     } else {
         L.gf = L.gb = L.part = L.z = L.sflags = L.q;
@@ -1366,7 +1366,7 @@ struct Solver {
         p.info = info;
         p.status = status;
         p.limit = tile_wait_ticks();
-        SPD_TRY(zero2d<int>(p.flags, 1, subst_flag_ints(p.nt, p.nr, p.nc), 1, s));
+        SPD_TRY(zero2d<int>(p.flags, 1, subst_flag_ints(p.nt, p.nc), 1, s));
         const unsigned grid = (unsigned)subst_groups(p);
         SPD_VALIDATE((check_subst<R, CPLX, TC>(p, grid, g_chk)));
         subst_kernel<R, CPLX, TC><<<dim3(grid), dim3(SUB_THREADS), 0, s>>>(p);

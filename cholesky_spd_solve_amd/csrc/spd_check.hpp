@@ -491,8 +491,8 @@ static bool check_tile(const TileArgs &p, unsigned grid, Checker &c)
 
 // Replay of subst_kernel (spd_subst.hpp): the role of every workgroup, the
 // column segments each one reads and writes (the operand loads are masked to
-// them), and that every flag or counter a role waits for is raised by roles
-// with smaller ids only (the counter of (i, ct) by exactly the row pieces of
+// them), and that every counter a role waits for is advanced by roles with
+// smaller ids only (each counter of (i, ct) by exactly the row pieces of
 // tile row i).
 template <typename R, bool CPLX, int TC>
 static bool check_subst(const SubstArgs &p, unsigned grid, Checker &c)
@@ -509,10 +509,13 @@ static bool check_subst(const SubstArgs &p, unsigned grid, Checker &c)
         return false;
     if (p.status != nullptr && !c.access(p.status, 4, true, kn, 0, 0))
         return false;
-    if (!c.access(p.flags, 4 * (size_t)subst_flag_ints(p.nt, p.nr, p.nc), true, kn, 0, 0))
+    if (!c.access(p.flags, 4 * (size_t)subst_flag_ints(p.nt, p.nc), true, kn, 0, 0))
         return false;
-    const int nfz = p.nt * p.nr * p.nc;
-    std::vector<int> zprod(nfz, -1), xcount(p.nt * p.nc, 0), xlast(p.nt * p.nc, -1);
+    // per (i, ct): roles counted by the Z counter and by the X counter, and
+    // the largest id among them
+    std::vector<int> zcount(p.nt * p.nc, 0), zlast(p.nt * p.nc, -1), xcount(p.nt * p.nc, 0),
+        xlast(p.nt * p.nc, -1);
+    std::vector<char> seen((size_t)p.nt * p.nr * p.nc * 2, 0);
     for (unsigned g = 0; g < grid; ++g) {
         int i, rt, ct;
         const int kind = subst_role(p, (int)g, i, rt, ct);
@@ -520,21 +523,19 @@ static bool check_subst(const SubstArgs &p, unsigned grid, Checker &c)
             c.err = "subst_kernel: a workgroup without a role";
             return false;
         }
-        if (kind == SUB_R) {
-            int &z = zprod[(i * p.nr + rt) * p.nc + ct];
-            if (z >= 0) {
-                c.err = "subst_kernel: a piece of Z is written by two workgroups";
-                return false;
-            }
-            z = (int)g;
-        } else {
-            ++xcount[i * p.nc + ct];
-            xlast[i * p.nc + ct] = (int)g;
+        char &once = seen[((size_t)(i * p.nr + rt) * p.nc + ct) * 2 + kind];
+        if (once) {
+            c.err = "subst_kernel: two workgroups take the same role";
+            return false;
         }
+        once = 1;
+        std::vector<int> &cnt = kind == SUB_R ? zcount : xcount, &lst = kind == SUB_R ? zlast : xlast;
+        ++cnt[i * p.nc + ct];
+        lst[i * p.nc + ct] = std::max(lst[i * p.nc + ct], (int)g);
     }
     for (int i = 0; i < p.nt; ++i)
         for (int ct = 0; ct < p.nc; ++ct)
-            if (xcount[i * p.nc + ct] != subst_rows(p, i)) {
+            if (zcount[i * p.nc + ct] != subst_rows(p, i) || xcount[i * p.nc + ct] != subst_rows(p, i)) {
                 c.err = "subst_kernel: a counter does not count every row piece";
                 return false;
             }
@@ -574,9 +575,8 @@ static bool check_subst(const SubstArgs &p, unsigned grid, Checker &c)
                     return false;
             }
         } else {
-            for (int r = rt; r < subst_rows(p, i); ++r)
-                if (!after(g, zprod[(i * p.nr + r) * p.nc + ct]))
-                    return false;
+            if (!after(g, zlast[i * p.nc + ct]))
+                return false;
             if (!seg(Iv + (int64_t)i * p.T * p.T, p.T, r0, tki - r0, r0, nrow, false, g) ||
                 !seg(Z, p.ldz, r0, tki - r0, c0, ncol, false, g) ||
                 !seg(B, p.ldb, row0 + r0, nrow, c0, ncol, true, g))

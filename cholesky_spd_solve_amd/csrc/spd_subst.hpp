@@ -13,11 +13,11 @@
 //                 Z goes to a workspace buffer (T rows, one per tile row in
 //                 turn);
 //   C(i, rt, ct): X_i(rt, ct) = sum_{r >= rt} inv(L_ii)^H(rt, r) Z(r, ct),
-//                 once the pieces r >= rt of Z are there; X goes into B.
+//                 once Z(:, ct) is complete; X goes into B.
 //
-// A counter per (i, ct) counts the C roles done (X_i(:, ct) is complete when
-// it reaches the tile row's number of row pieces); a flag per R role marks
-// its piece of Z.  Workgroup ids run over the tile rows from the last: the R
+// Two counters per (i, ct) count the R roles and the C roles done: Z(:, ct)
+// and X_i(:, ct) are complete when they reach the tile row's number of row
+// pieces (one wait each, however many pieces).  Workgroup ids run over the tile rows from the last: the R
 // roles of tile row i, then its C roles.  Every role waits only for roles
 // with smaller ids, which are dispatched before it, so no waiting workgroup
 // holds back one it waits for.  Every wait is bounded in time as in the
@@ -52,13 +52,15 @@ struct SubstArgs {
     int n, nrhs, T, nt;
     int nr;           // row pieces of a whole tile row: ceil(T / SUB_TR)
     int nc;           // column pieces: ceil(nrhs / TC)
-    int *flags;       // subst_flag_ints(nt, nr, nc) ints, zero between launches
+    int *flags;       // subst_flag_ints(nt, nc) ints, zero between launches
     const int *info;  // nothing is done when non-zero on entry (may be null)
     int *status;      // set to -1 if a wait ran out (may be null); X is then NaN
     int64_t limit;    // longest wait, in wall-clock ticks (100 MHz)
 };
 
-__host__ __device__ inline int subst_flag_ints(int nt, int nr, int nc) { return nt * nr * nc + nt * nc + 2; }
+// counters of Z(:, ct) and of X_i(:, ct) per (i, ct), the abort word and the
+// count of workgroups done
+__host__ __device__ inline int subst_flag_ints(int nt, int nc) { return 2 * nt * nc + 2; }
 
 // row pieces of tile row i
 __host__ __device__ inline int subst_rows(const SubstArgs &p, int i)
@@ -184,7 +186,8 @@ struct SubstAcc {
             }
     }
     // the second half's accumulators are added to the first's through M
-    // (at least NP SUB_TR TC elements); both halves call it
+    // (at least NP SUB_TR TC elements of LDS no thread still reads); both
+    // halves call it
     __device__ __forceinline__ void fold(R *M)
     {
         const int slot = threadIdx.x & 255;
@@ -211,30 +214,60 @@ struct SubstAcc {
     }
 };
 
-// Each half's LDS: one chunk of both operands
+// Each half's LDS: one chunk of both operands.  Within every 16-deep block
+// of a row, depth 4 s + g sits at position 4 g + s, so that the four operands
+// lane (i, g) gives the four 16x16x4 products of that block (depths 4 s + g,
+// s = 0 .. 3) are adjacent and arrive in 16-byte reads; rows are padded by
+// 16 bytes (aligned, and spread over the banks).
 template <typename R, bool CPLX, int TC, int KC>
 struct SubstStage {
     static constexpr int NP = CPLX ? 2 : 1;
-    R As[NP][SUB_TR][KC + 1];  // As[.][r][k] = conj(M(k0 + k, r))
-    R Bs[NP][TC][KC + 1];      // Bs[.][c][k] = Q(k0 + k, c)
+    static constexpr int LDR = KC + 16 / (int)sizeof(R);
+    R As[NP][SUB_TR][LDR];  // As[.][r][pos(k)] = conj(M(k0 + k, r))
+    R Bs[NP][TC][LDR];      // Bs[.][c][pos(k)] = Q(k0 + k, c)
+    __device__ __forceinline__ static int pos(int k) { return (k & ~15) + 4 * (k & 3) + ((k >> 2) & 3); }
 };
+
+// v[s] = p[s], s < 4, in 16-byte reads (p 16-byte aligned)
+__device__ __forceinline__ void lds4(const float *p, float (&v)[4])
+{
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    const f4 x = *(const f4 *)p;
+    v[0] = x[0];
+    v[1] = x[1];
+    v[2] = x[2];
+    v[3] = x[3];
+}
+__device__ __forceinline__ void lds4(const double *p, double (&v)[4])
+{
+    typedef double d2 __attribute__((ext_vector_type(2)));
+    const d2 x = *(const d2 *)p, y = *(const d2 *)(p + 2);
+    v[0] = x[0];
+    v[1] = x[1];
+    v[2] = y[0];
+    v[3] = y[1];
+}
 
 // acc += M^H Q: M(k, r) = m[k + r ldm] for k < K, r < nr and Q(k, c) =
 // q[k + c ldq] for k < K, c < nc (zero elsewhere).  The depth goes in steps
 // of 2 KC: half h of the workgroup takes [2 KC s + h KC, + KC) into its own
 // stage and accumulators, and the loads of its next chunk are in flight
-// while its matrix-core waves work on the current one.
+// while its matrix-core waves work on the current one.  Each 16x16x4 product
+// takes the operands mma16 (mma16c) would, in the same order.
 template <typename R, bool CPLX, int TC, int KC>
 __device__ __forceinline__ void subst_mma(SubstAcc<R, CPLX, TC> &acc, const typename Elem<R, CPLX>::type *m,
                                           int64_t ldm, int K, int nr, const typename Elem<R, CPLX>::type *q,
                                           int64_t ldq, int nc, SubstStage<R, CPLX, TC, KC> *st)
 {
+    typedef SubstStage<R, CPLX, TC, KC> Stage;
     constexpr int NP = CPLX ? 2 : 1;
     constexpr int LA = SUB_TR * KC / 256, LB = TC * KC / 256;
     static_assert((SUB_TR * KC) % 256 == 0 && (TC * KC) % 256 == 0, "chunk loads must divide evenly");
+    static_assert(KC % 16 == 0, "chunks are whole 16-deep blocks");
     const int h = threadIdx.x >> 8, tid = threadIdx.x & 255, wave = tid >> 6;
+    const int li = tid & 15, lk = (tid >> 4) & 3;
     const int ro = 16 * (wave & 1), co = (TC / 2) * (wave >> 1);
-    SubstStage<R, CPLX, TC, KC> &S = st[h];
+    Stage &S = st[h];
     R ra[NP][LA], rb[NP][LB];
     auto fetch = [&](int k0) {
 #pragma unroll
@@ -267,38 +300,40 @@ __device__ __forceinline__ void subst_mma(SubstAcc<R, CPLX, TC> &acc, const type
 #pragma unroll
             for (int u = 0; u < LA; ++u) {
                 const int e = tid + 256 * u;
-                S.As[pl][e / KC][e % KC] = ra[pl][u];
+                S.As[pl][e / KC][Stage::pos(e % KC)] = ra[pl][u];
             }
 #pragma unroll
             for (int u = 0; u < LB; ++u) {
                 const int e = tid + 256 * u;
-                S.Bs[pl][e / KC][e % KC] = rb[pl][u];
+                S.Bs[pl][e / KC][Stage::pos(e % KC)] = rb[pl][u];
             }
         }
         __syncthreads();
         if (s + 1 < steps)
             fetch(2 * KC * (s + 1) + h * KC);
-        // two 16-deep steps at a time: their operand reads in flight together,
-        // without holding a whole chunk's operands in registers
 #pragma unroll 2
         for (int k = 0; k < KC; k += 16) {
+            R a[NP][4], bv[NP][acc.FN][4];
 #pragma unroll
-            for (int b = 0; b < acc.FN; ++b) {
-                if constexpr (!CPLX) {
-                    acc.t[0][b] = mma16<R>(&S.As[0][ro][k], 1, KC + 1, &S.Bs[0][co + 16 * b][k], 1, KC + 1, acc.t[0][b]);
-                } else {
-                    mma16c<R>(
-                        [&](int rr, int kk, R &re, R &im) {
-                            re = S.As[0][ro + rr][k + kk];
-                            im = S.As[1][ro + rr][k + kk];
-                        },
-                        [&](int kk, int cc, R &re, R &im) {
-                            re = S.Bs[0][co + 16 * b + cc][k + kk];
-                            im = S.Bs[1][co + 16 * b + cc][k + kk];
-                        },
-                        acc.t[0][b], acc.t[1][b]);
-                }
+            for (int pl = 0; pl < NP; ++pl) {
+                lds4(&S.As[pl][ro + li][k + 4 * lk], a[pl]);
+#pragma unroll
+                for (int b = 0; b < acc.FN; ++b)
+                    lds4(&S.Bs[pl][co + 16 * b + li][k + 4 * lk], bv[pl][b]);
             }
+#pragma unroll
+            for (int b = 0; b < acc.FN; ++b)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    if constexpr (!CPLX) {
+                        acc.t[0][b] = mfma16(bv[0][b][u], a[0][u], acc.t[0][b]);
+                    } else {
+                        acc.t[0][b] = mfma16(bv[0][b][u], a[0][u], acc.t[0][b]);
+                        acc.t[0][b] = mfma16(-bv[1][b][u], a[1][u], acc.t[0][b]);
+                        acc.t[1][b] = mfma16(bv[1][b][u], a[0][u], acc.t[1][b]);
+                        acc.t[1][b] = mfma16(bv[0][b][u], a[1][u], acc.t[1][b]);
+                    }
+                }
         }
     }
 }
@@ -308,19 +343,19 @@ template <typename R, bool CPLX, int TC>
 __global__ void __launch_bounds__(SUB_THREADS) subst_kernel(const SubstArgs p)
 {
     typedef typename Elem<R, CPLX>::type E;
-    constexpr int KC = CPLX ? 32 : 64;
+    constexpr int KC = CPLX ? (TC == 64 ? 16 : 32) : 64;  // chunk depth: the staging registers of two chunks fit
     typedef SubstStage<R, CPLX, TC, KC> Stage;
-    static_assert(sizeof(Stage) >= sizeof(R) * (CPLX ? 2 : 1) * SUB_TR * TC, "the fold needs one stage");
+    static_assert(2 * sizeof(Stage) >= sizeof(R) * (CPLX ? 2 : 1) * SUB_TR * TC, "the fold needs both stages");
     __shared__ Stage st[2];
     __shared__ int skip, last;
 
     int i, rt, ct;
     const int kind = subst_role(p, (int)blockIdx.x, i, rt, ct);
     const int tid = threadIdx.x;
-    const int frows = p.nt * p.nr * p.nc;
-    int *const abort_word = p.flags + frows + p.nt * p.nc;
+    const int frows = p.nt * p.nc;
+    int *const abort_word = p.flags + 2 * frows;
     int *const ctr = abort_word + 1;
-    auto fZ = [&](int ti, int r, int c) { return p.flags + (ti * p.nr + r) * p.nc + c; };
+    auto fZ = [&](int ti, int c) { return p.flags + ti * p.nc + c; };
     auto fX = [&](int ti, int c) { return p.flags + frows + ti * p.nc + c; };
     auto tile_rows = [&](int ti) { return (p.n - ti * p.T) < p.T ? p.n - ti * p.T : p.T; };
     const E *const A = (const E *)p.A;
@@ -350,21 +385,19 @@ __global__ void __launch_bounds__(SUB_THREADS) subst_kernel(const SubstArgs p)
                                            B + rj + (int64_t)c0 * p.ldb, p.ldb, ncol, st);
             }
             __syncthreads();
-            acc.fold(&st[0].As[0][0][0]);
+            acc.fold((R *)st);
             if (first)
                 acc.store(Z + r0 + (int64_t)c0 * p.ldz, p.ldz, nrow, ncol, R(-1));
-            subst_signal(fZ(i, rt, ct));
+            subst_signal(fZ(i, ct));
         } else {
-            const int nri = subst_rows(p, i);
-            for (int r = rt; r < nri; ++r)
-                subst_wait(fZ(i, r, ct), 1, abort_word, p.limit, p.status);
+            subst_wait(fZ(i, ct), subst_rows(p, i), abort_word, p.limit, p.status);
             acc.zero();
             // X = inv(L_ii)(rows r0.., columns of the piece)^H Z(r0.., ct)
             const E *const Iv = (const E *)p.Inv + (int64_t)i * p.T * p.T;
             subst_mma<R, CPLX, TC, KC>(acc, Iv + r0 + (int64_t)r0 * p.T, p.T, tki - r0, nrow,
                                        Z + r0 + (int64_t)c0 * p.ldz, p.ldz, ncol, st);
             __syncthreads();
-            acc.fold(&st[0].As[0][0][0]);
+            acc.fold((R *)st);
             if (first)
                 acc.store(B + row0 + r0 + (int64_t)c0 * p.ldb, p.ldb, nrow, ncol, R(1));
             subst_signal(fX(i, ct));
@@ -380,7 +413,7 @@ __global__ void __launch_bounds__(SUB_THREADS) subst_kernel(const SubstArgs p)
     if (last) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         const bool aborted = *(volatile int *)abort_word != 0;
-        const int nf = subst_flag_ints(p.nt, p.nr, p.nc) - 1;  // all but the counter
+        const int nf = subst_flag_ints(p.nt, p.nc) - 1;  // all but the count of workgroups done
         for (int e = tid; e < nf; e += blockDim.x)
             p.flags[e] = 0;
         if (tid == 0)

@@ -60,21 +60,20 @@ def test_workspace_size(lib):
     # buffers for the transposed solved block, (nrhs rounded up to 128) x (T
     # rounded up to 32), two sets of nt*T*T chain products, 8 partial
     # T x nrhs blocks, the one-launch back substitution's T x nrhs block and
-    # its nt*nr*nc + nt*nc + 2 int flags (nr = ceil(T / 32) row pieces, nc =
-    # ceil(nrhs / 64) column pieces, 32 wide when nrhs <= 32); each rounded up
-    # to 256 bytes
+    # its 2*nt*nc + 2 int counters (nc = ceil(nrhs / 64) column pieces, 32 wide
+    # when nrhs <= 32); each rounded up to 256 bytes
     n, nrhs, T = 32768, 128, 512
     up = lambda a, b: -(-a // b) * b
     el = (n // T) * T * T + 4 * n * T + T * T
     solve = 2 * 128 * 512 + 2 * (n // T) * T * T + 8 * T * nrhs + T * nrhs
-    sflags = up(4 * (64 * 16 * 2 + 64 * 2 + 2), 256)
+    sflags = up(4 * (2 * 64 * 2 + 2), 256)
     assert f(1, n, 0, T) == el * 8 + 256 + 768
     assert f(1, n, nrhs, T) == (el + solve) * 8 + 256 + 768 + sflags
     assert f(3, n, nrhs, T) == (el + solve) * 16 + 256 + 768 + sflags
     n, nrhs, T = 1000, 7, 100
     el = up(10 * 100 * 100, 32) + 4 * up(1024 * 128, 32) + up(100 * 100, 32)
     solve = up(2 * 128 * 128, 32) + 2 * up(10 * 100 * 100, 32) + up(8 * 100 * 7, 32) + up(100 * 7, 32)
-    sflags = up(4 * (10 * 4 * 1 + 10 * 1 + 2), 256)
+    sflags = up(4 * (2 * 10 * 1 + 2), 256)
     assert f(1, n, 0, T) == el * 8 + 256 + 256
     assert f(1, n, nrhs, T) == (el + solve) * 8 + 256 + 256 + sflags
     # T_A > n is clamped to n
