@@ -272,8 +272,9 @@ static bool check_rect(const RectArgs &p, dim3 grid, Checker &c)
         const bool prows = i0 + BM <= p.m;
         const R *P = (const R *)p.P + (PT ? (int64_t)i0 * p.ldp : (int64_t)i0);
         const R *Q = (const R *)p.Q + j0;
+        const int kend = rect_slices<BN, KB, STORE>(p, j0) * KB;
         for (int tid = 0; tid < NT; ++tid) {
-            for (int k0 = 0; k0 < p.kp; k0 += KB) {
+            for (int k0 = 0; k0 < kend; k0 += KB) {
                 const R *pa = P + (PT ? (int64_t)k0 : (int64_t)k0 * p.ldp);
                 const R *qb = Q + (int64_t)k0 * p.ldq;
                 const bool fast = prows && k0 + KB <= p.kvalid;

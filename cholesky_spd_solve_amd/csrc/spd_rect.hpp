@@ -84,6 +84,20 @@ struct RectLoad {
 // DEPTH: slices of P and Q in flight from memory (1: the next one; 2: the
 // next two, in two register sets, for more bytes in flight per CU).
 // STORE: C = P Q^T (C is not read) instead of C -= P Q^T.
+// Slices of depth KB a workgroup whose tile starts at column j0 multiplies.
+// STORE (the factorization's panel W = P inv(L_kk)^T, Q = inv(L_kk) lower
+// triangular): Q(j, k) = 0 for k > j, so columns [j0, j0 + BN) need depth
+// j0 + BN only; otherwise the whole depth kp.
+template <int BN, int KB, bool STORE>
+__host__ __device__ inline int rect_slices(const RectArgs &p, int j0)
+{
+    const int all = p.kp / KB;
+    if (!STORE)
+        return all;
+    const int need = (j0 + BN + KB - 1) / KB;
+    return need < all ? need : all;
+}
+
 template <typename R, int BM, int BN, int KB, int WM, int WN, bool PT, bool VEC, int DEPTH = 1, bool STORE = false>
 __global__ void __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)))
 rect_kernel(const RectArgs p)
@@ -189,7 +203,7 @@ rect_kernel(const RectArgs p)
         for (int fj = 0; fj < FN; ++fj)
             acc[fi][fj] = V4{0, 0, 0, 0};
 
-    const int nsl = p.kp / KB;
+    const int nsl = rect_slices<BN, KB, STORE>(p, j0);
     load(rga[0], rgb[0], pa, qb, 0);
     if (DEPTH == 2 && nsl > 1)
         load(rga[DEPTH - 1], rgb[DEPTH - 1], pa + pstep, qb + qstep, KB);
