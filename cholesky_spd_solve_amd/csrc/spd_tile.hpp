@@ -435,131 +435,130 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) t
 // what a workgroup hands between its own waves (its updated block before the
 // solve product, L_j,j-1 before the diagonal update) and the leaf.
 
+// This wave's four 16 x 16 tiles of a complex 64 x 64 block: tile t covers
+// columns 16 t .. and rows 16 ((w - t) mod 4) .. (w = wave), one tile in every
+// block row and block column, so that the products whose depth depends on
+// the tile's row or column (triangular operands, the lower triangle only)
+// share out evenly over the four waves.  Element q of lane (li, lk) in tile
+// t is (16 ((w - t) mod 4) + li, 16 t + acc_row(lk, q)).
 template <typename R>
 struct TileQuadC {
     typedef typename AccT<R>::type V4;
     typedef typename Elem<R, true>::type E;
-    V4 re[2][2], im[2][2];
+    V4 re[4], im[4];
+
+    __device__ __forceinline__ static int rblk(int t) { return ((int)(threadIdx.x >> 6) - t) & 3; }
+    __device__ __forceinline__ static int row(int t) { return 16 * rblk(t) + (threadIdx.x & 15); }
+    __device__ __forceinline__ static int col(int t, int q) { return 16 * t + acc_row<R>((threadIdx.x & 63) >> 4, q); }
 
     __device__ __forceinline__ void zero()
     {
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                re[a][b] = V4{0, 0, 0, 0};
-                im[a][b] = V4{0, 0, 0, 0};
-            }
+        for (int t = 0; t < 4; ++t) {
+            re[t] = V4{0, 0, 0, 0};
+            im[t] = V4{0, 0, 0, 0};
+        }
     }
     // -src(r, c) for r < nr, c < nc; diag: zero above the diagonal, a real
     // diagonal, and -1 on the diagonal beyond nr
     __device__ __forceinline__ void load_neg(const E *src, int64_t ld, int nr, int nc, bool diag)
     {
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int r = TileQuad<R>::row(a), c = TileQuad<R>::col(b, q);
-                    R x = (diag && r == c) ? R(-1) : R(0), y = R(0);
-                    if (r < nr && c < nc && (!diag || r >= c)) {
-                        Elem<R, true>::load(src + r + (int64_t)c * ld, x, y);
-                        x = -x;
-                        y = (diag && r == c) ? R(0) : -y;
-                    }
-                    re[a][b][q] = x;
-                    im[a][b][q] = y;
+            for (int q = 0; q < 4; ++q) {
+                const int r = row(t), c = col(t, q);
+                R x = (diag && r == c) ? R(-1) : R(0), y = R(0);
+                if (r < nr && c < nc && (!diag || r >= c)) {
+                    Elem<R, true>::load(src + r + (int64_t)c * ld, x, y);
+                    x = -x;
+                    y = (diag && r == c) ? R(0) : -y;
                 }
+                re[t][q] = x;
+                im[t][q] = y;
+            }
     }
     // planes S[0] + i S[1] (S*[c][r] = element (r, c)) = sg * this; realdiag:
     // the diagonal's imaginary part is stored as 0
     __device__ __forceinline__ void to_lds(R (*S)[LEAF][LDL], R sg, bool realdiag) const
     {
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int r = TileQuad<R>::row(a), c = TileQuad<R>::col(b, q);
-                    S[0][c][r] = sg * re[a][b][q];
-                    S[1][c][r] = (realdiag && r == c) ? R(0) : sg * im[a][b][q];
-                }
+            for (int q = 0; q < 4; ++q) {
+                const int r = row(t), c = col(t, q);
+                S[0][c][r] = sg * re[t][q];
+                S[1][c][r] = (realdiag && r == c) ? R(0) : sg * im[t][q];
+            }
     }
     __device__ __forceinline__ void store(E *dst, int64_t ld, int nr, R sg) const
     {
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int r = TileQuad<R>::row(a), c = TileQuad<R>::col(b, q);
-                    if (r < nr)
-                        Elem<R, true>::store(dst + r + (int64_t)c * ld, sg * re[a][b][q], sg * im[a][b][q]);
-                }
+            for (int q = 0; q < 4; ++q) {
+                const int r = row(t), c = col(t, q);
+                if (r < nr)
+                    Elem<R, true>::store(dst + r + (int64_t)c * ld, sg * re[t][q], sg * im[t][q]);
+            }
     }
 };
 
-// Q += P B on the quadrant for complex 64 x 64 operands given by fa(r, k, re,
-// im) = P(r, k) and fb(k, c, re, im) = B(k, c); kmode and lower as tile_mma.
-// Each 16-deep step first fetches the operands of all four 16 x 16 tiles (in
-// the lane layout of mma16: lane (li, lk) takes P(row + li, k + 4 s + lk) and
-// B(k + 4 s + lk, col + li)), then issues their products.
+// Q += P B on this wave's tiles for complex 64 x 64 operands given by fa(r,
+// k, re, im) = P(r, k) and fb(k, c, re, im) = B(k, c); kmode and lower as
+// tile_mma.  Each 16-deep step first fetches the operands of all the wave's
+// tiles that take it (in the lane layout of mma16: lane (li, lk) takes
+// P(row + li, k + 4 s + lk) and B(k + 4 s + lk, col + li)), then issues their
+// products.
 template <typename R, typename FA, typename FB>
 __device__ __forceinline__ void tile_mma_c(TileQuadC<R> &Q, FA fa, FB fb, int kmode, bool lower)
 {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, lk = lane >> 4;
-    const int rb = 32 * (wave & 1), cb = 32 * (wave >> 1);
-    int k0[2][2], k1[2][2], kmin = LEAF, kmax = 0;
+    const int lane = threadIdx.x & 63, li = lane & 15, lk = lane >> 4;
+    int k0[4], k1[4], kmin = LEAF, kmax = 0;
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int t = 0; t < 4; ++t) {
+        const int ro = 16 * TileQuadC<R>::rblk(t), co = 16 * t;
+        int x0 = 0, x1 = LEAF;
+        if (kmode == TK_TO_COL)
+            x1 = co + 16;
+        else if (kmode == TK_FROM_COL)
+            x0 = co;
+        else if (kmode == TK_TO_ROW)
+            x1 = ro + 16;
+        if (lower && co > ro)
+            x1 = x0;  // no product for tiles above the diagonal
+        k0[t] = x0;
+        k1[t] = x1;
+        if (x0 < x1) {
+            kmin = x0 < kmin ? x0 : kmin;
+            kmax = x1 > kmax ? x1 : kmax;
+        }
+    }
+    for (int k = kmin; k < kmax; k += 16) {
+        R ar[4][4], ai[4][4], br[4][4], bi[4][4];
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const int ro = rb + 16 * a, co = cb + 16 * b;
-            int x0 = 0, x1 = LEAF;
-            if (kmode == TK_TO_COL)
-                x1 = co + 16;
-            else if (kmode == TK_FROM_COL)
-                x0 = co;
-            else if (kmode == TK_TO_ROW)
-                x1 = ro + 16;
-            if (lower && co > ro)
-                x1 = x0;  // no product for tiles above the diagonal
-            k0[a][b] = x0;
-            k1[a][b] = x1;
-            if (x0 < x1) {
-                kmin = x0 < kmin ? x0 : kmin;
-                kmax = x1 > kmax ? x1 : kmax;
+        for (int t = 0; t < 4; ++t) {
+            if (k < k0[t] || k >= k1[t])
+                continue;
+            const int ro = 16 * TileQuadC<R>::rblk(t), co = 16 * t;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                fa(ro + li, k + 4 * s + lk, ar[t][s], ai[t][s]);
+                fb(k + 4 * s + lk, co + li, br[t][s], bi[t][s]);
             }
         }
-    for (int k = kmin; k < kmax; k += 16) {
-        R ar[2][4], ai[2][4], br[2][4], bi[2][4];
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+        for (int t = 0; t < 4; ++t) {
+            if (k < k0[t] || k >= k1[t])
+                continue;
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-                fa(rb + 16 * a + li, k + 4 * s + lk, ar[a][s], ai[a][s]);
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                fb(k + 4 * s + lk, cb + 16 * b + li, br[b][s], bi[b][s]);
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                if (k < k0[a][b] || k >= k1[a][b])
-                    continue;
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    Q.re[a][b] = mfma16(br[b][s], ar[a][s], Q.re[a][b]);
-                    Q.re[a][b] = mfma16(-bi[b][s], ai[a][s], Q.re[a][b]);
-                    Q.im[a][b] = mfma16(bi[b][s], ar[a][s], Q.im[a][b]);
-                    Q.im[a][b] = mfma16(br[b][s], ai[a][s], Q.im[a][b]);
-                }
+            for (int s = 0; s < 4; ++s) {
+                Q.re[t] = mfma16(br[t][s], ar[t][s], Q.re[t]);
+                Q.re[t] = mfma16(-bi[t][s], ai[t][s], Q.re[t]);
+                Q.im[t] = mfma16(bi[t][s], ar[t][s], Q.im[t]);
+                Q.im[t] = mfma16(br[t][s], ai[t][s], Q.im[t]);
             }
+        }
     }
 }
 
