@@ -155,67 +155,59 @@ struct TileBlk {
     }
 };
 
-// This wave's 32 x 32 quadrant of a 64 x 64 block as 2 x 2 accumulators of
-// 16 x 16 (wave w: rows 32 (w % 2) .., columns 32 (w / 2) ..); accumulator
-// (a, b) element q of lane (li, lk) is (32 (w % 2) + 16 a + li,
-// 32 (w / 2) + 16 b + acc_row(lk, q)).
+// This wave's four 16 x 16 tiles of a 64 x 64 block: tile t covers columns
+// 16 t .. and rows 16 ((w - t) mod 4) .. (w = wave), one tile in every block
+// row and block column, so that the products whose depth depends on the
+// tile's row or column (triangular operands, the lower triangle only) share
+// out evenly over the four waves.  Element q of lane (li, lk) in tile t is
+// (16 ((w - t) mod 4) + li, 16 t + acc_row(lk, q)).
 template <typename R>
 struct TileQuad {
     typedef typename AccT<R>::type V4;
-    V4 t[2][2];
+    V4 t[4];
 
-    __device__ __forceinline__ static int row(int a) { return 32 * ((threadIdx.x >> 6) & 1) + 16 * a + (threadIdx.x & 15); }
-    __device__ __forceinline__ static int col(int b, int q)
-    {
-        return 32 * (threadIdx.x >> 7) + 16 * b + acc_row<R>((threadIdx.x & 63) >> 4, q);
-    }
+    __device__ __forceinline__ static int rblk(int u) { return ((int)(threadIdx.x >> 6) - u) & 3; }
+    __device__ __forceinline__ static int row(int u) { return 16 * rblk(u) + (threadIdx.x & 15); }
+    __device__ __forceinline__ static int col(int u, int q) { return 16 * u + acc_row<R>((threadIdx.x & 63) >> 4, q); }
     __device__ __forceinline__ void zero()
     {
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-                t[a][b] = V4{0, 0, 0, 0};
+        for (int u = 0; u < 4; ++u)
+            t[u] = V4{0, 0, 0, 0};
     }
     // -src(r, c) for r < nr, c < nc; diag: zero above the diagonal and -1 on
     // the diagonal beyond nr (the identity padding of a short last block)
     __device__ __forceinline__ void load_neg(const R *src, int64_t ld, int nr, int nc, bool diag)
     {
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int r = row(a), c = col(b, q);
-                    R x = (diag && r == c) ? R(-1) : R(0);
-                    if (r < nr && c < nc && (!diag || r >= c))
-                        x = -src[r + (int64_t)c * ld];
-                    t[a][b][q] = x;
-                }
+            for (int q = 0; q < 4; ++q) {
+                const int r = row(u), c = col(u, q);
+                R x = (diag && r == c) ? R(-1) : R(0);
+                if (r < nr && c < nc && (!diag || r >= c))
+                    x = -src[r + (int64_t)c * ld];
+                t[u][q] = x;
+            }
     }
     __device__ __forceinline__ void to_lds(R (*M)[LDL], R sg) const
     {
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    M[col(b, q)][row(a)] = sg * t[a][b][q];
+            for (int q = 0; q < 4; ++q)
+                M[col(u, q)][row(u)] = sg * t[u][q];
     }
     __device__ __forceinline__ void store(R *dst, int64_t ld, int nr, R sg) const
     {
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int r = row(a), c = col(b, q);
-                    if (r < nr)
-                        dst[r + (int64_t)c * ld] = sg * t[a][b][q];
-                }
+            for (int q = 0; q < 4; ++q) {
+                const int r = row(u), c = col(u, q);
+                if (r < nr)
+                    dst[r + (int64_t)c * ld] = sg * t[u][q];
+            }
     }
 };
 
@@ -227,30 +219,28 @@ enum {
     TK_TO_ROW = 3,   // [0, ro + 16): left operand lower triangular
 };
 
-// Q += P B on the quadrant, P(r, k) = pa[k ak + r ar], B(k, c) = pb[k bk + c bc]
-// (both 64 x 64 in LDS); lower: only the tiles on or below the diagonal.
+// Q += P B on this wave's tiles, P(r, k) = pa[k ak + r ar], B(k, c) =
+// pb[k bk + c bc] (both 64 x 64 in LDS); lower: only the tiles on or below
+// the diagonal.
 template <typename R>
 __device__ __forceinline__ void tile_mma(TileQuad<R> &Q, const R *pa, int ak, int ar, const R *pb, int bk, int bc,
                                          int kmode, bool lower)
 {
-    const int wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const int ro = 32 * (wave & 1) + 16 * a, co = 32 * (wave >> 1) + 16 * b;
-            if (lower && co > ro)
-                continue;
-            int k0 = 0, k1 = LEAF;
-            if (kmode == TK_TO_COL)
-                k1 = co + 16;
-            else if (kmode == TK_FROM_COL)
-                k0 = co;
-            else if (kmode == TK_TO_ROW)
-                k1 = ro + 16;
-            for (int k = k0; k < k1; k += 16)
-                Q.t[a][b] = mma16<R>(pa + k * ak + ro * ar, ak, ar, pb + k * bk + co * bc, bk, bc, Q.t[a][b]);
-        }
+    for (int u = 0; u < 4; ++u) {
+        const int ro = 16 * TileQuad<R>::rblk(u), co = 16 * u;
+        if (lower && co > ro)
+            continue;
+        int k0 = 0, k1 = LEAF;
+        if (kmode == TK_TO_COL)
+            k1 = co + 16;
+        else if (kmode == TK_FROM_COL)
+            k0 = co;
+        else if (kmode == TK_TO_ROW)
+            k1 = ro + 16;
+        for (int k = k0; k < k1; k += 16)
+            Q.t[u] = mma16<R>(pa + k * ak + ro * ar, ak, ar, pb + k * bk + co * bc, bk, bc, Q.t[u]);
+    }
 }
 
 // Launched with 256 threads, or with 512 (TileArgs::hold): then waves 4-7 do
