@@ -412,15 +412,16 @@ enum {
     OPT_COLUMN_FIRST_ROWS,
     OPT_TILE_HOLD_ROWS,
     OPT_SUBST_LAUNCH,
+    OPT_TILE_UPDATE_ROWS,
     OPT_COUNT
 };
-static const int64_t k_opt_default[OPT_COUNT] = {1, 1, -1, -1, 16384, 1, 2000000, 8192, 8192, 2097152};
-static std::atomic<int64_t> g_opt_store[OPT_COUNT] = {{1},     {1},       {-1},   {-1},   {16384},
-                                                      {1},     {2000000}, {8192}, {8192}, {2097152}};
+static const int64_t k_opt_default[OPT_COUNT] = {1, 1, -1, -1, 16384, 1, 2000000, 8192, 8192, 2097152, -1};
+static std::atomic<int64_t> g_opt_store[OPT_COUNT] = {{1},       {1},    {-1},   {-1},      {16384}, {1},
+                                                      {2000000}, {8192}, {8192}, {2097152}, {-1}};
 struct Options {
     int64_t v[OPT_COUNT];
 };
-static thread_local Options g_opt = {{1, 1, -1, -1, 16384, 1, 2000000, 8192, 8192, 2097152}};
+static thread_local Options g_opt = {{1, 1, -1, -1, 16384, 1, 2000000, 8192, 8192, 2097152, -1}};
 
 static void snapshot_options()
 {
@@ -479,6 +480,20 @@ static int64_t column_first_rows() { return g_opt.v[OPT_COLUMN_FIRST_ROWS]; }
 // the CU's whole LDS.  There the chain is the longer path, and the tile's
 // leaves sharing SIMDs with the trailing update run two to three times slower.
 static int64_t tile_hold_rows() { return g_opt.v[OPT_TILE_HOLD_ROWS]; }
+
+// In the steps taken one at a time (two-step schedule), while fewer than
+// tile_update_rows() rows remain beyond the next tile
+// (SPD_OPT_TILE_UPDATE_ROWS), the next diagonal tile takes its last trailing
+// update inside its own launch (one-launch tile only) and the caller's update
+// covers the rest of its tile column; the panel product waits for that.  It
+// pays only while that update is short next to the tile: by default 2048 rows
+// for real types and never for complex ones (measured: fp64 N = 4096 2.79 ->
+// 2.73 ms, fp32 N = 16384 within 0.2 %, complex128 N = 8192 1 % slower).
+static int64_t tile_update_rows(bool cplx)
+{
+    const int64_t v = g_opt.v[OPT_TILE_UPDATE_ROWS];
+    return v >= 0 ? v : (cplx ? 0 : 2048);
+}
 
 // The back substitution runs in one launch (subst_kernel) while n n_rhs
 // (four times that for complex types) is at most SPD_OPT_SUBST_LAUNCH, else
@@ -769,10 +784,13 @@ struct Solver {
     // Factor the tk x tk diagonal tile at D and write inv(L_kk) to Inv (ld
     // ldi) in one launch (tile_kernel, tile_kernel_c)
     static int tile_launch(E *D, int64_t lda, int64_t tk, E *Inv, int64_t ldi, int *info, int *flags, int64_t col0,
-                           int64_t rows_below, hipStream_t s)
+                           int64_t rows_below, hipStream_t s, const E *W = nullptr, int64_t ldw = 0, int64_t wk = 0)
     {
         {
             TileArgs p;
+            p.W = W;
+            p.ldw = ldw;
+            p.wk = W != nullptr ? (int)wk : 0;
             p.D = D;
             p.lda = lda;
             p.Inv = Inv;
@@ -828,6 +846,8 @@ struct Solver {
         const E *W2 = nullptr;  // second panel for depth [kp1, kp) (the two-step update)
         int64_t kp1 = 0;
         bool aux = false;  // potrf's auxiliary stream (timed as its own class)
+        int64_t skip = 0;  // the lower triangle without its leading skip x skip block
+                           // (a multiple of the tile order)
     };
 
     template <int BM, int KB, int WM, int WN, bool BIGLD = false, bool PK = false>
@@ -860,6 +880,20 @@ struct Solver {
         } else {
             a.ntiles = a.tiles * (a.tiles + 1) / 2;
         }
+        a.tskip = 0;
+        if (x.skip >= m)
+            return 0;  // all of C is the block left to the next tile
+        if (x.skip > 0) {
+            const int sk = (int)(x.skip / BM);
+            if (a.ncols > 0 || a.jt_end > 0 || (int64_t)sk * BM != x.skip) {
+                g_last_error = "trailing update: the skipped block must be whole lower-triangle tiles";
+                return SPD_ERR_HIP;
+            }
+            a.tskip = sk * (sk + 1) / 2;
+            a.ntiles -= a.tskip;
+            if (a.ntiles <= 0)
+                return 0;
+        }
         a.info = info;
         a.vecc = ((uintptr_t)C % 16 == 0 && (ldc * (int64_t)sizeof(E)) % 16 == 0) ? 1 : 0;
         const dim3 grid((unsigned)a.ntiles), block(64 * WM * WN);
@@ -889,8 +923,9 @@ struct Solver {
             g_last_error = "two-panel update is for the symmetric form";
             return SPD_ERR_HIP;
         }
+        const double sk = (double)std::min(x.skip, m);  // the leading block left to the next tile
         ProfScope ps(x.V != nullptr ? -1 : x.aux ? PROF_SYRK_AUX : PROF_SYRK,
-                     FMUL * (double)w * (2.0 * m - w + 1.0) * (double)kw, s);
+                     FMUL * ((double)w * (2.0 * m - w + 1.0) - sk * (sk + 1.0)) * (double)kw, s);
         auto jt = [&](int64_t bm) { return cols > 0 ? (int)(cols / bm) : 0; };
         if (ldc >= SYRK_LD32)  // 64-bit offsets into C; one 64-row tile shape for every such case
             return syrk_cfg<64, 16, 2, 2, true>(m, W, ldw, kp, C, ldc, jt(64), info, s, x);
@@ -1043,14 +1078,25 @@ struct Solver {
     // ldw_fixed > 0: Wk's leading dimension (the two-step schedule keeps all
     // panels at one leading dimension); rows [m, m rounded up to SYRK_LDW) are
     // zeroed either way.
+    // Wprev (ld ldw_fixed), wk > 0: the tile first takes the last trailing
+    // update A_kk -= Wprev_k Wprev_k^H itself (one-launch tile only), Wprev_k
+    // the previous panel's rows of this tile; then before_panel (if given)
+    // runs between the tile and the panel product (the caller makes s wait
+    // for the update of the rest of the tile column there).
     static int diag_panel(int64_t n, E *A, int64_t lda, int64_t T, int64_t c0, E *Inv, E *Wk, int *info,
-                          int *ctr, hipStream_t s, int64_t ldw_fixed = 0)
+                          int *ctr, hipStream_t s, int64_t ldw_fixed = 0, const E *Wprev = nullptr,
+                          int64_t wk = 0, const std::function<int()> *before_panel = nullptr)
     {
         const int64_t tk = std::min(T, n - c0);
         E *D = A + c0 + c0 * lda;
+        if (Wprev != nullptr && (!tile_launch_enabled() || ldw_fixed <= 0)) {
+            g_last_error = "the tile's own trailing update needs the one-launch tile";
+            return SPD_ERR_HIP;
+        }
         if (tile_launch_enabled()) {
             ProfScope ps(PROF_DIAG, FMUL * 2.0 * (double)tk * tk * tk / 3.0, s);
-            SPD_TRY(tile_launch(D, lda, tk, Inv, T, info, tile_flags(ctr), c0, n - c0 - tk, s));
+            SPD_TRY(tile_launch(D, lda, tk, Inv, T, info, tile_flags(ctr), c0, n - c0 - tk, s, Wprev, ldw_fixed,
+                                wk));
         } else {
             ProfScope ps(PROF_DIAG, FMUL * 2.0 * (double)tk * tk * tk / 3.0, s);
             for (int64_t b0 = 0; b0 < tk; b0 += LEAF) {
@@ -1080,6 +1126,8 @@ struct Solver {
             }
             SPD_TRY(merge_inverses(D, lda, 0, Inv, T, 0, 1, tk, Wk, info, s));
         }
+        if (before_panel != nullptr)
+            SPD_TRY((*before_panel)());
         const int64_t m = n - c0 - tk;
         if (m <= 0)
             return 0;
@@ -1232,8 +1280,9 @@ struct Solver {
         auto Wp = [&](int64_t k) { return (E *)work + L.w + (k % 4) * L.wsz; };
         auto C = [&](int64_t k) { return A + k * T * (1 + lda); };  // trailing matrix from tile k
         auto Iv = [&](int64_t k) { return hook != nullptr ? Inv0 + k * T * T : Inv0; };
-        auto diag_panel = [&](int64_t c0, E *Wk, hipStream_t st) {
-            return Solver::diag_panel(n, A, lda, T, c0, Iv(c0 / T), Wk, info, ctr, st, ldw);
+        auto diag_panel = [&](int64_t c0, E *Wk, hipStream_t st, const E *Wprev = nullptr,
+                              const std::function<int()> *before_panel = nullptr) {
+            return Solver::diag_panel(n, A, lda, T, c0, Iv(c0 / T), Wk, info, ctr, st, ldw, Wprev, T, before_panel);
         };
         auto done = [&](int64_t k0, int64_t k1) { return hook != nullptr ? (*hook)(std::min(k0, nt), std::min(k1, nt)) : 0; };
         Lookahead la;
@@ -1287,6 +1336,24 @@ struct Solver {
             SPD_TRY(syrk(n - (a + 2) * T, Wp(a) + T, ldw, kp, T, C(a + 2), lda, 0, info, s));
         SPD_TRY(la.record(la.ev_rest, s));
         for (int64_t k = a + 1; k + 1 < nt; ++k) {
+            if (tile_launch_enabled() && n - (k + 2) * T < tile_update_rows(CPLX)) {
+                // Tile k+1 takes its update by W_k inside its own launch, beside
+                // the caller's update of everything else from tile column k+1
+                // on; panel k+1 waits for that update (the rest of its column).
+                SPD_TRY(la.wait(sl, la.ev_rest));  // the update of step k-1 reached tile k+1
+                const std::function<int()> rest = [&]() -> int {
+                    SPD_TRY(la.wait(s, la.ev_panel));  // panel k
+                    Syr2 x;
+                    x.skip = T;
+                    SPD_TRY(syrk(n - (k + 1) * T, Wp(k), ldw, kp, T, C(k + 1), lda, 0, info, s, x));
+                    SPD_TRY(la.record(la.ev_rest, s));
+                    return la.wait(sl, la.ev_rest);
+                };
+                SPD_TRY(diag_panel((k + 1) * T, Wp(k + 1), sl, Wp(k), &rest));
+                SPD_TRY(la.record(la.ev_panel, sl));
+                SPD_TRY(done(k + 1, k + 2));
+                continue;
+            }
             SPD_TRY(la.wait(s, la.ev_panel));  // panel k
             SPD_TRY(la.wait(sl, la.ev_rest));  // the update of step k-1 reached tile column k+1
             SPD_TRY(syrk(n - (k + 1) * T, Wp(k), ldw, kp, T, C(k + 1), lda, T, info, sl, aux_update()));
@@ -2543,6 +2610,7 @@ int spd_set_option(spd_option_t opt, int64_t value)
         break;
     case OPT_PAIR_ROWS:
     case OPT_SYRK_DEEP_ROWS:
+    case OPT_TILE_UPDATE_ROWS:
         if (value < -1)
             return -2;
         break;

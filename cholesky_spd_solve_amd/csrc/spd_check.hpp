@@ -447,10 +447,26 @@ static bool check_tile(const TileArgs &p, unsigned grid, Checker &c)
         }
         return true;
     };
+    // the tile's own trailing update: rows [0, nr) of block b of W, columns [0, wk)
+    const E *Wp = (const E *)p.W;
+    auto wblk = [&](int b, int nr, unsigned g) {
+        for (int col = 0; col < p.wk; ++col)
+            if (!c.access(Wp + (int64_t)b * LEAF + (int64_t)col * p.ldw, sizeof(E) * (size_t)nr, false, kn, g, 0))
+                return false;
+        return true;
+    };
+    if (p.wk > 0 && (Wp == nullptr || p.ldw < p.tk)) {
+        c.err = "tile_kernel: the previous panel does not cover the tile";
+        return false;
+    }
     for (unsigned g = 0; g < grid; ++g) {
         int i, j;
         const int kind = tile_role(nb, (int)g, i, j);
         const int nr = nrows(i);
+        if (p.wk > 0 && kind == TILE_D && (!wblk(j, nr, g) || (j > 0 && !wblk(j - 1, LEAF, g))))
+            return false;
+        if (p.wk > 0 && kind == TILE_O && (!wblk(i, nr, g) || !wblk(j, LEAF, g)))
+            return false;
         if (kind == TILE_D) {
             if (!blk(A, p.lda, j, j, nr, nr, true, false, g) || !blk(A, p.lda, j, j, nr, nr, true, true, g) ||
                 !blk(Iv, p.ldi, j, j, nr, nr, false, true, g))

@@ -53,6 +53,9 @@ struct SyrkArgs {
     int kp;         // columns of W (a multiple of KB)
     int tiles;      // tile rows = ceil(m / BM)
     int jt_end;     // 0: every lower tile; > 0: only tile columns J < jt_end
+    int tskip;      // lower triangle (jt_end = ncols = 0): the first tskip tiles of the row
+                    // order are left alone (tskip = s (s + 1) / 2 leaves the leading
+                    // s x s tiles, the diagonal tile the next launch updates itself)
     int ncols;      // 0: the lower triangle of the m x m C; > 0: every tile of the
                     // m x ncols C (rows of W against rows of V, no triangle)
     int ntiles;     // number of tiles updated (workgroups)
@@ -86,7 +89,8 @@ __host__ __device__ inline void syrk_krange(const SyrkArgs &p, int i0, int j0, i
 }
 
 // Tile (I, J) of workgroup b: with ncols > 0 every tile of the rectangle in
-// column order; otherwise the whole lower triangle in row order, or, with
+// column order; otherwise the whole lower triangle in row order (past its
+// first tskip tiles), or, with
 // jt_end > 0, the first jt_end tile columns in column order (column J holds
 // tiles I = J .. tiles - 1).  Workgroup ids are first remapped so consecutive
 // tiles share an XCD.  Shared with the host-side launch validator.
@@ -99,7 +103,7 @@ __host__ __device__ inline void syrk_tile(const SyrkArgs &p, int b, int &I, int 
         return;
     }
     if (p.jt_end <= 0) {
-        tri_index(t, I, J);
+        tri_index(t + p.tskip, I, J);
         return;
     }
     J = 0;

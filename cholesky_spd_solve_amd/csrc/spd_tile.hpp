@@ -20,6 +20,11 @@
 //   X_ib (i > b):
 //        inv(L)_ib = -inv(L_ii) sum_{b <= k < i} L_ik inv(L)_kb
 //
+// With wk > 0 the tile first takes the last update of the trailing matrix
+// itself: every L block role starts from A_ij - W_i W_j^T, with W (ldw) the
+// previous panel's rows of this tile (wk columns), so that the launch need
+// not wait for a separate update of the tile.
+//
 // Each block has a ready flag in the workspace.  A workgroup waits for the
 // flags of the blocks it reads (its thread 0 polls with agent-scope loads,
 // then an acquire fence) and raises its own after its stores (release fence,
@@ -50,6 +55,9 @@ struct TileArgs {
     int col0;       // global column of the tile's first column
     int64_t limit;  // longest wait, in ticks of the 100 MHz wall clock
     int hold;       // real types: 1 to launch 512 threads per workgroup (see tile_kernel)
+    const void *W;  // wk > 0: A_ij -= W_i W_j^H first, W (ldw) the previous
+    int64_t ldw;    // panel's rows of this tile, wk columns (a multiple of 64
+    int wk;         // or the panel's zero-padded width)
 };
 
 enum { TILE_D = 0, TILE_O = 1, TILE_X = 2 };
@@ -280,12 +288,29 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) t
     auto wait = [&](const int *f1, const int *f2) { tile_wait(f1, f2, abort_word, p.limit, p.info); };
     TileBlk<R> u, w;
 
+    // W_i (rows of block i of the previous panel), columns [c, c + 64)
+    const R *const Wp = (const R *)p.W;
+    auto Wb = [&](int i, int c) { return Wp + (int64_t)i * LEAF + (int64_t)c * p.ldw; };
+
     if (kind == TILE_D) {
         const int j = bi, nr = nrows(j);
         TileQuad<R> Fd, Fs;
         Fd.load_neg(Ab(j, j), p.lda, nr, nr, true);
         if (j > 0)
             Fs.load_neg(Ab(j, j - 1), p.lda, nr, LEAF, false);
+        for (int c = 0; c < p.wk; c += LEAF) {  // the tile's last trailing update
+            u.load(Wb(j, c), p.ldw, nr, p.wk - c, false);
+            if (j > 0)
+                w.load(Wb(j - 1, c), p.ldw, LEAF, p.wk - c, false);
+            u.put(S);
+            if (j > 0)
+                w.put(X);
+            __syncthreads();
+            if (j > 0)
+                tile_mma<R>(Fs, &S[0][0], LDL, 1, &X[0][0], LDL, 1, TK_FULL, false);
+            tile_mma<R>(Fd, &S[0][0], LDL, 1, &S[0][0], LDL, 1, TK_FULL, true);
+            __syncthreads();
+        }
         for (int l = 0; l + 1 < j; ++l) {
             wait(fL(j, l), fL(j - 1, l));
             u.load(Ab(j, l), p.lda, nr, LEAF, false);
@@ -353,6 +378,15 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) t
         const int i = bi, j = bj, nr = nrows(i);
         TileQuad<R> F;
         F.load_neg(Ab(i, j), p.lda, nr, LEAF, false);
+        for (int c = 0; c < p.wk; c += LEAF) {  // the tile's last trailing update
+            u.load(Wb(i, c), p.ldw, nr, p.wk - c, false);
+            w.load(Wb(j, c), p.ldw, LEAF, p.wk - c, false);
+            u.put(S);
+            w.put(X);
+            __syncthreads();
+            tile_mma<R>(F, &S[0][0], LDL, 1, &X[0][0], LDL, 1, TK_FULL, false);
+            __syncthreads();
+        }
         for (int l = 0; l < j; ++l) {
             wait(fL(i, l), fL(j, l));
             u.load(Ab(i, l), p.lda, nr, LEAF, false);
@@ -587,12 +621,33 @@ __global__ void __launch_bounds__(256) tile_kernel_c(const TileArgs p)
         y = S[1][k][r];
     };
 
+    // W_i (rows of block i of the previous panel), columns [c, c + 64)
+    const E *const Wp = (const E *)p.W;
+    auto Wb = [&](int i, int c) { return Wp + (int64_t)i * LEAF + (int64_t)c * p.ldw; };
+    // the tile's last trailing update: F += W_i W_j^H over the panel's columns
+    auto pre = [&](TileQuadC<R> &F, int i, int j, int nr, int nc, bool lower) {
+        for (int c = 0; c < p.wk; c += LEAF) {
+            const E *U = Wb(i, c), *V = Wb(j, c);
+            const int kw = p.wk - c;
+            tile_mma_c<R>(
+                F, [&](int r, int k, R &x, R &y) { gget(U, p.ldw, k < kw ? nr : 0, r, k, x, y); },
+                [&](int k, int cc, R &x, R &y) {
+                    gget(V, p.ldw, k < kw ? nc : 0, cc, k, x, y);
+                    y = -y;
+                },
+                TK_FULL, lower);
+        }
+    };
+
     if (kind == TILE_D) {
         const int j = bi, nr = nrows(j);
         TileQuadC<R> Fd, Fs;
         Fd.load_neg(Ab(j, j), p.lda, nr, nr, true);
         if (j > 0)
             Fs.load_neg(Ab(j, j - 1), p.lda, nr, LEAF, false);
+        if (j > 0)
+            pre(Fs, j, j - 1, nr, LEAF, false);
+        pre(Fd, j, j, nr, nr, true);
         for (int l = 0; l + 1 < j; ++l) {
             wait(fL(j, l), fL(j - 1, l));
             const E *U = Ab(j, l), *V = Ab(j - 1, l);
@@ -674,6 +729,7 @@ __global__ void __launch_bounds__(256) tile_kernel_c(const TileArgs p)
         const int i = bi, j = bj, nr = nrows(i);
         TileQuadC<R> F;
         F.load_neg(Ab(i, j), p.lda, nr, LEAF, false);
+        pre(F, i, j, nr, LEAF, false);
         for (int l = 0; l < j; ++l) {
             wait(fL(i, l), fL(j, l));
             const E *U = Ab(i, l), *V = Ab(j, l);

@@ -291,10 +291,17 @@ const char *spd_last_error(void);
  *                            most this value (default 2097152), otherwise by
  *                            block steps on `stream` and an auxiliary stream
  *                            (0: always by block steps)
+ *   SPD_OPT_TILE_UPDATE_ROWS in the steps taken one at a time, while fewer
+ *                            than this many rows remain beyond the next tile,
+ *                            that tile takes its last trailing update inside
+ *                            its own launch (TILE_LAUNCH = 1 only) and the
+ *                            update on `stream` covers the rest of its tile
+ *                            column; -1 (default): 2048 for real types, 0
+ *                            (never) for complex ones
  * spd_set_option returns 0, -1 for an unknown option, -2 for a value out of
- * range (LOOKAHEAD, TWO_STEP and TILE_LAUNCH take 0 or 1, PAIR_ROWS and
- * SYRK_DEEP_ROWS >= -1, RECT_TALL_ROWS, TILE_WAIT_US, COLUMN_FIRST_ROWS,
- * TILE_HOLD_ROWS and SUBST_LAUNCH >= 0);
+ * range (LOOKAHEAD, TWO_STEP and TILE_LAUNCH take 0 or 1, PAIR_ROWS,
+ * SYRK_DEEP_ROWS and TILE_UPDATE_ROWS >= -1, RECT_TALL_ROWS, TILE_WAIT_US,
+ * COLUMN_FIRST_ROWS, TILE_HOLD_ROWS and SUBST_LAUNCH >= 0);
  * SPD_OPT_DEFAULT restores an option's default.
  * spd_get_option returns the current value (INT64_MIN for an unknown
  * option). */
@@ -308,7 +315,8 @@ typedef enum {
     SPD_OPT_TILE_WAIT_US = 7,
     SPD_OPT_COLUMN_FIRST_ROWS = 8,
     SPD_OPT_TILE_HOLD_ROWS = 9,
-    SPD_OPT_SUBST_LAUNCH = 10
+    SPD_OPT_SUBST_LAUNCH = 10,
+    SPD_OPT_TILE_UPDATE_ROWS = 11
 } spd_option_t;
 #define SPD_OPT_DEFAULT INT64_MIN
 int spd_set_option(spd_option_t opt, int64_t value);

@@ -4,7 +4,10 @@ SPD_OPT_LOOKAHEAD = 0 selects the sequential schedule (every kernel on the
 caller's stream) and SPD_OPT_TWO_STEP = 0 the one-step lookahead instead of
 the paired-step schedule; SPD_OPT_COLUMN_FIRST_ROWS moves the point from which
 the caller's update waits for the next tile column (never, or in every single
-step; with SPD_OPT_PAIR_ROWS past N every step is single).  Under each, potrf, log det and potrs run through
+step; with SPD_OPT_PAIR_ROWS past N every step is single), and
+SPD_OPT_TILE_UPDATE_ROWS the steps whose diagonal tile takes its own last
+update (none, or every single step; with SPD_OPT_TILE_LAUNCH = 0 the tile is
+the launch sequence, which never does).  Under each, potrf, log det and potrs run through
 the one-call entry point (which falls back to the three calls when its fused
 path is off) on small real and complex inputs, checked against the oracle on
 the same bytes; and the auxiliary streams can be released and made again.
@@ -48,6 +51,9 @@ SCHEDULES = {
     "one-step, column first everywhere": lambda g: {g.OPT_TWO_STEP: 0, g.OPT_COLUMN_FIRST_ROWS: 1 << 40},
     "column first never": lambda g: {g.OPT_COLUMN_FIRST_ROWS: 0},
     "column first everywhere": lambda g: {g.OPT_COLUMN_FIRST_ROWS: 1 << 40, g.OPT_PAIR_ROWS: 1 << 40},
+    "tile's own update never": lambda g: {g.OPT_TILE_UPDATE_ROWS: 0},
+    "tile's own update everywhere": lambda g: {g.OPT_TILE_UPDATE_ROWS: 1 << 40, g.OPT_PAIR_ROWS: 1 << 40},
+    "tile's own update, launch sequence": lambda g: {g.OPT_TILE_LAUNCH: 0},
 }
 
 

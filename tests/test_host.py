@@ -170,12 +170,12 @@ def test_options_validate_and_restore(lib):
     import cholesky_spd_solve_amd as spd
     defaults = {spd.OPT_LOOKAHEAD: 1, spd.OPT_TWO_STEP: 1, spd.OPT_PAIR_ROWS: -1, spd.OPT_SYRK_DEEP_ROWS: -1,
                 spd.OPT_RECT_TALL_ROWS: 16384, spd.OPT_TILE_LAUNCH: 1, spd.OPT_TILE_WAIT_US: 2000000,
-                spd.OPT_COLUMN_FIRST_ROWS: 8192, spd.OPT_TILE_HOLD_ROWS: 8192, spd.OPT_SUBST_LAUNCH: 2097152}
+                spd.OPT_COLUMN_FIRST_ROWS: 8192, spd.OPT_TILE_HOLD_ROWS: 8192, spd.OPT_SUBST_LAUNCH: 2097152, spd.OPT_TILE_UPDATE_ROWS: -1}
     for k, v in defaults.items():
         assert spd.get_option(k) == v
     assert lib.spd_set_option(0, 1) == -1
-    assert lib.spd_set_option(11, 1) == -1
-    assert lib.spd_get_option(11) == -(1 << 63)
+    assert lib.spd_set_option(12, 1) == -1
+    assert lib.spd_get_option(12) == -(1 << 63)
     assert lib.spd_set_option(spd.OPT_LOOKAHEAD, 2) == -2
     assert lib.spd_set_option(spd.OPT_TWO_STEP, -1) == -2
     assert lib.spd_set_option(spd.OPT_PAIR_ROWS, -2) == -2
@@ -185,6 +185,7 @@ def test_options_validate_and_restore(lib):
     assert lib.spd_set_option(spd.OPT_COLUMN_FIRST_ROWS, -1) == -2
     assert lib.spd_set_option(spd.OPT_TILE_HOLD_ROWS, -1) == -2
     assert lib.spd_set_option(spd.OPT_SUBST_LAUNCH, -1) == -2
+    assert lib.spd_set_option(spd.OPT_TILE_UPDATE_ROWS, -2) == -2
     with spd.options({spd.OPT_PAIR_ROWS: 0, spd.OPT_LOOKAHEAD: 0, spd.OPT_RECT_TALL_ROWS: 7}):
         assert spd.get_option(spd.OPT_PAIR_ROWS) == 0
         assert spd.get_option(spd.OPT_LOOKAHEAD) == 0
