@@ -311,12 +311,12 @@ static Layout make_layout(int64_t n, int64_t n_rhs, int64_t T_A, int64_t esize)
         L.gf = L.q + align_up(2 * L.qsz, al);
         L.gb = L.gf + align_up(L.nt * L.T * L.T, al);
         L.part = L.gb + align_up(L.nt * L.T * L.T, al);
-        // the one-launch back substitution's buffer of one tile row (T x n_rhs,
-        // leading dimension T) and its flags
+        // the one-launch back substitution's two buffers of one tile row (T x
+        // n_rhs each, leading dimension T, adjacent) and its flags
         const int64_t tc = subst_tc(n_rhs);
         L.ldz = L.T;
         L.z = L.part + align_up(CHAIN_SPLITS * L.T * n_rhs, al);
-        L.sflags = L.z + align_up(L.T * n_rhs, al);
+        L.sflags = L.z + align_up(2 * L.T * n_rhs, al);
         const int64_t nfl = subst_flag_ints((int)L.nt, (int)cdiv(n_rhs, tc));
         L.total = L.sflags + align_up(cdiv(4 * nfl, esize), al);
     } else {
@@ -1407,8 +1407,42 @@ struct Solver {
         return 0;
     }
 
+    // GB_k = -L_k,k-1 inv(L_k-1,k-1) into GB + k T T (leading dimension T, the
+    // rows of tile k) for the whole tiles k = 1 .. n / T - 1 in one batched
+    // product and, with ragged, for a short last tile in a second one.
+    static int back_chain_products(int64_t n, const E *A, int64_t lda, int64_t T, const E *Inv, E *GB,
+                                   bool ragged, const int *info, hipStream_t s)
+    {
+        const int64_t nfull = n / T, tail = n - nfull * T;
+        auto product = [&](int64_t k, int64_t m, int batch) {
+            Gemm h;
+            h.A = A + k * T + (k - 1) * T * lda;
+            h.lda = lda;
+            h.sA_out = T * (1 + lda);
+            h.B = Inv + (k - 1) * T * T;
+            h.ldb = T;
+            h.sB_out = T * T;
+            h.C = GB + k * T * T;
+            h.ldc = T;
+            h.sC_out = T * T;
+            h.batch = batch;
+            h.m = m;
+            h.n = h.k = T;
+            h.kmode = KM_BEG_BY_J;
+            h.neg = true;
+            h.info = info;
+            return gemm<R, CPLX>(NN, h, s);
+        };
+        if (nfull >= 2)
+            SPD_TRY(product(1, T, (int)(nfull - 1)));
+        if (ragged && tail > 0 && nfull >= 1)
+            SPD_TRY(product(nfull, tail, 1));
+        return 0;
+    }
+
     // The back substitution L^H X = Y in one launch (subst_kernel), with the
-    // inverse of every diagonal tile in the workspace's INV region; Z and the
+    // inverse of every diagonal tile in the workspace's INV region and the
+    // products G_i = GB_{i+1} formed first (back_chain_products); Z and the
     // flags in the workspace (the flags zeroed first).  status (may be null)
     // becomes -1 if a wait of the launch runs out; X is then NaN.
     template <int TC>
@@ -1416,9 +1450,12 @@ struct Solver {
                              const int *info, int *status, void *work, hipStream_t s)
     {
         SubstArgs p;
+        E *const GB = (E *)work + L.gb;
+        SPD_TRY(back_chain_products(n, A, lda, L.T, (const E *)work + L.inv, GB, true, info, s));
         p.A = A;
         p.lda = lda;
         p.Inv = (const E *)work + L.inv;
+        p.G = GB;
         p.B = B;
         p.ldb = ldb;
         p.Z = (E *)work + L.z;
@@ -2023,25 +2060,8 @@ struct Solver {
             g.info = info;
             SPD_TRY((gemm<R, CPLX>(NN, g, s)));
         }
-        if (split && backward) {
-            // GB_k = -L_k,k-1 inv(L_k-1,k-1) for whole blocks k (k = 1 .. nfull-1)
-            Gemm h;
-            h.A = A + T;
-            h.lda = lda;
-            h.sA_out = T * (1 + lda);
-            h.B = Inv;
-            h.ldb = T;
-            h.sB_out = T * T;
-            h.C = GB + T * T;
-            h.ldc = T;
-            h.sC_out = T * T;
-            h.batch = (int)(nfull - 1);
-            h.m = h.n = h.k = T;
-            h.kmode = KM_BEG_BY_J;
-            h.neg = true;
-            h.info = info;
-            SPD_TRY((gemm<R, CPLX>(NN, h, s)));
-        }
+        if (split && backward)  // GB_k for whole blocks k (k = 1 .. nfull-1)
+            SPD_TRY(back_chain_products(n, A, lda, T, Inv, GB, false, info, s));
         // Next block (index kn, rows [cn, cn + T)) in one split product:
         //   forward:  Y_kn = GF_k Y_k + inv(L_kn,kn) B_kn          (kn = k + 1)
         //   backward: X_kn = inv(L_kn,kn)^T B_kn + GB_k^T X_k      (kn = k - 1)

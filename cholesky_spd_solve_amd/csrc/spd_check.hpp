@@ -556,7 +556,7 @@ static bool check_subst(const SubstArgs &p, unsigned grid, Checker &c)
                 c.err = "subst_kernel: a counter does not count every row piece";
                 return false;
             }
-    const E *A = (const E *)p.A, *Iv = (const E *)p.Inv;
+    const E *A = (const E *)p.A, *Iv = (const E *)p.Inv, *G = (const E *)p.G;
     const E *B = (const E *)p.B, *Z = (const E *)p.Z;
     auto rows = [&](int ti) { return std::min(p.T, p.n - ti * p.T); };
     // rows [r0, r0 + nr) of columns [c0, c0 + nc) of M (ld)
@@ -581,11 +581,13 @@ static bool check_subst(const SubstArgs &p, unsigned grid, Checker &c)
         const int tki = rows(i), r0 = rt * SUB_TR, c0 = ct * TC;
         const int nrow = std::min(SUB_TR, tki - r0), ncol = std::min(TC, p.nrhs - c0);
         const int64_t row0 = (int64_t)i * p.T;
+        const E *Zi = Z + (i & 1) * p.ldz * p.nrhs;
         if (kind == SUB_R) {
             if (!seg(B, p.ldb, row0 + r0, nrow, c0, ncol, false, g) ||
-                !seg(Z, p.ldz, r0, nrow, c0, ncol, true, g))
+                !seg(Zi, p.ldz, r0, nrow, c0, ncol, true, g))
                 return false;
-            for (int j = p.nt - 1; j > i; --j) {
+            // the last term (j = i + 2) is also the wait that frees buffer i % 2
+            for (int j = p.nt - 1; j > i + 1; --j) {
                 const int64_t rj = (int64_t)j * p.T;
                 if (!after(g, xlast[j * p.nc + ct]) || !seg(A, p.lda, rj, rows(j), row0 + r0, nrow, false, g) ||
                     !seg(B, p.ldb, rj, rows(j), c0, ncol, false, g))
@@ -595,8 +597,13 @@ static bool check_subst(const SubstArgs &p, unsigned grid, Checker &c)
             if (!after(g, zlast[i * p.nc + ct]))
                 return false;
             if (!seg(Iv + (int64_t)i * p.T * p.T, p.T, r0, tki - r0, r0, nrow, false, g) ||
-                !seg(Z, p.ldz, r0, tki - r0, c0, ncol, false, g) ||
+                !seg(Zi, p.ldz, r0, tki - r0, c0, ncol, false, g) ||
                 !seg(B, p.ldb, row0 + r0, nrow, c0, ncol, true, g))
+                return false;
+            if (i + 1 < p.nt &&
+                (!after(g, xlast[(i + 1) * p.nc + ct]) ||
+                 !seg(G + (int64_t)(i + 1) * p.T * p.T, p.T, 0, rows(i + 1), r0, nrow, false, g) ||
+                 !seg(B, p.ldb, row0 + p.T, rows(i + 1), c0, ncol, false, g)))
                 return false;
         }
     }

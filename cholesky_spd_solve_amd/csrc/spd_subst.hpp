@@ -3,19 +3,25 @@
 // here by tile rows of T_A from the last one up):
 //
 //   X_i = inv(L_ii)^H (Y_i - sum_{j > i} L_ji^H X_j)
+//       = inv(L_ii)^H Z_i + G_i^H X_{i+1},
+//   Z_i = Y_i - sum_{j > i+1} L_ji^H X_j,   G_i = -L_{i+1,i} inv(L_ii),
 //
 // with the inverse of every diagonal tile already built (the factorization
-// keeps them).  Tile row i is cut into row pieces of SUB_TR rows and column
-// pieces of TC right-hand sides; each piece (rt, ct) has two roles:
+// keeps them) and G_i formed before the launch.  Split this way, the step
+// from X_{i+1} to X_i is one product: Z_i and inv(L_ii)^H Z_i only need
+// X_{i+2} and are formed while X_{i+1} is still being solved.  Tile row i is
+// cut into row pieces of SUB_TR rows and column pieces of TC right-hand
+// sides; each piece (rt, ct) has two roles:
 //
-//   R(i, rt, ct): Z = Y_i(rt, ct) - sum_{j > i} L_ji(:, rt)^H X_j(:, ct), a
-//                 term as soon as X_j(:, ct) is complete, in decreasing j;
-//                 Z goes to a workspace buffer (T rows, one per tile row in
-//                 turn);
-//   C(i, rt, ct): X_i(rt, ct) = sum_{r >= rt} inv(L_ii)^H(rt, r) Z(r, ct),
-//                 once Z(:, ct) is complete; X goes into B.
+//   R(i, rt, ct): Z_i(rt, ct) = Y_i(rt, ct) - sum_{j > i+1} L_ji(:, rt)^H
+//                 X_j(:, ct), a term as soon as X_j(:, ct) is complete, in
+//                 decreasing j, into a workspace buffer (T rows; tile rows
+//                 of even and odd index take one buffer each);
+//   C(i, rt, ct): X_i(rt, ct) = sum_{r >= rt} inv(L_ii)^H(rt, r) Z_i(r, ct)
+//                 once Z_i(:, ct) is complete, then + G_i(:, rt)^H
+//                 X_{i+1}(:, ct) once that is complete; X goes into B.
 //
-// Two counters per (i, ct) count the R roles and the C roles done: Z(:, ct)
+// Two counters per (i, ct) count the R roles and the C roles done: Z_i(:, ct)
 // and X_i(:, ct) are complete when they reach the tile row's number of row
 // pieces (one wait each, however many pieces).  Workgroup ids run over the tile rows from the last: the R
 // roles of tile row i, then its C roles.  Every role waits only for roles
@@ -26,9 +32,11 @@
 // clears the flags, which are zero between launches (and, if a wait ran out,
 // fills X with NaN).
 //
-// The single Z buffer is safe: R(i, rt, ct) writes its piece only after
-// X_{i+1}(:, ct) is complete, that is after every C role of tile row i + 1
-// that reads column piece ct of Z has finished.
+// Two Z buffers suffice: R(i, rt, ct) writes its piece of buffer i % 2 only
+// after X_{i+2}(:, ct) is complete, that is after every C role of tile row
+// i + 2 (the previous user of that buffer) has read column piece ct of it;
+// R roles of the last two tile rows have no terms and are the first users
+// of their buffers.
 #pragma once
 
 #include "spd_kernels.hpp"
@@ -37,6 +45,13 @@ namespace spd {
 
 constexpr int SUB_TR = 32;        // rows of a piece
 constexpr int SUB_THREADS = 512;  // threads of a workgroup: two halves of 256
+// Each counter and word has a 128-byte line of its own: the waiting
+// workgroups poll them at agent scope, and polls and updates of different
+// counters then go to different lines.
+constexpr int SUB_FLAG_STRIDE = 32;
+// A waiting workgroup sleeps about 64 SUB_POLL_SLEEP clocks between polls
+// and looks at the abort word every fourth poll.
+constexpr int SUB_POLL_SLEEP = 4;
 enum { SUB_R = 0, SUB_C = 1 };
 
 struct SubstArgs {
@@ -47,8 +62,10 @@ struct SubstArgs {
                       // diagonal as whole squares, zero above the diagonal)
     void *B;          // Y on entry, X on exit; ldb
     int64_t ldb;
-    void *Z;          // T x nrhs buffer, leading dimension ldz >= T
-    int64_t ldz;
+    const void *G;    // G_i = -L_{i+1,i} inv(L_ii) at G + (i + 1) T T, leading
+                      // dimension T, the rows of tile i + 1 (i < nt - 1)
+    void *Z;          // two T x nrhs buffers, leading dimension ldz >= T, the
+    int64_t ldz;      // second ldz * nrhs elements after the first
     int n, nrhs, T, nt;
     int nr;           // row pieces of a whole tile row: ceil(T / SUB_TR)
     int nc;           // column pieces: ceil(nrhs / TC)
@@ -60,7 +77,7 @@ struct SubstArgs {
 
 // counters of Z(:, ct) and of X_i(:, ct) per (i, ct), the abort word and the
 // count of workgroups done
-__host__ __device__ inline int subst_flag_ints(int nt, int nc) { return 2 * nt * nc + 2; }
+__host__ __device__ inline int subst_flag_ints(int nt, int nc) { return (2 * nt * nc + 2) * SUB_FLAG_STRIDE; }
 
 // row pieces of tile row i
 __host__ __device__ inline int subst_rows(const SubstArgs &p, int i)
@@ -106,7 +123,7 @@ __device__ inline void subst_wait(const int *f, int target, int *abort_word, int
         for (int64_t polls = 0;; ++polls) {
             if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target)
                 break;
-            if (__hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+            if ((polls & 3) == 3 && __hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
                 break;
             if ((int64_t)wall_clock64() - t0 > limit || polls > max_polls) {
                 __hip_atomic_store(abort_word, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -114,7 +131,7 @@ __device__ inline void subst_wait(const int *f, int target, int *abort_word, int
                     atomicCAS(info, 0, -1);
                 break;
             }
-            __builtin_amdgcn_s_sleep(1);
+            __builtin_amdgcn_s_sleep(SUB_POLL_SLEEP);
         }
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
@@ -340,10 +357,10 @@ __device__ __forceinline__ void subst_mma(SubstAcc<R, CPLX, TC> &acc, const type
 
 // SUB_THREADS threads: two halves of 256 share each product (subst_mma).
 template <typename R, bool CPLX, int TC>
-__global__ void __launch_bounds__(SUB_THREADS) subst_kernel(const SubstArgs p)
+__global__ void __launch_bounds__(SUB_THREADS) __attribute__((amdgpu_waves_per_eu(4))) subst_kernel(const SubstArgs p)
 {
     typedef typename Elem<R, CPLX>::type E;
-    constexpr int KC = CPLX ? (TC == 64 ? 16 : 32) : 64;  // chunk depth: the staging registers of two chunks fit
+    constexpr int KC = CPLX ? (TC == 64 ? 16 : 32) : (sizeof(R) == 4 && TC == 64 ? 32 : 64);  // chunk depth: the staging registers of two chunks fit
     typedef SubstStage<R, CPLX, TC, KC> Stage;
     static_assert(2 * sizeof(Stage) >= sizeof(R) * (CPLX ? 2 : 1) * SUB_TR * TC, "the fold needs both stages");
     __shared__ Stage st[2];
@@ -353,14 +370,14 @@ __global__ void __launch_bounds__(SUB_THREADS) subst_kernel(const SubstArgs p)
     const int kind = subst_role(p, (int)blockIdx.x, i, rt, ct);
     const int tid = threadIdx.x;
     const int frows = p.nt * p.nc;
-    int *const abort_word = p.flags + 2 * frows;
-    int *const ctr = abort_word + 1;
-    auto fZ = [&](int ti, int c) { return p.flags + ti * p.nc + c; };
-    auto fX = [&](int ti, int c) { return p.flags + frows + ti * p.nc + c; };
+    int *const abort_word = p.flags + 2 * frows * SUB_FLAG_STRIDE;
+    int *const ctr = abort_word + SUB_FLAG_STRIDE;
+    auto fZ = [&](int ti, int c) { return p.flags + (ti * p.nc + c) * SUB_FLAG_STRIDE; };
+    auto fX = [&](int ti, int c) { return p.flags + (frows + ti * p.nc + c) * SUB_FLAG_STRIDE; };
     auto tile_rows = [&](int ti) { return (p.n - ti * p.T) < p.T ? p.n - ti * p.T : p.T; };
     const E *const A = (const E *)p.A;
     E *const B = (E *)p.B;
-    E *const Z = (E *)p.Z;
+    E *const Zi = (E *)p.Z + (i & 1) * p.ldz * p.nrhs;  // tile row i's Z buffer
     const int tki = tile_rows(i), r0 = rt * SUB_TR, c0 = ct * TC;
     const int nrow = (tki - r0) < SUB_TR ? tki - r0 : SUB_TR;
     const int ncol = (p.nrhs - c0) < TC ? p.nrhs - c0 : TC;
@@ -377,7 +394,7 @@ __global__ void __launch_bounds__(SUB_THREADS) subst_kernel(const SubstArgs p)
                 acc.load_neg(B + row0 + r0 + (int64_t)c0 * p.ldb, p.ldb, nrow, ncol);
             else
                 acc.zero();
-            for (int j = p.nt - 1; j > i; --j) {
+            for (int j = p.nt - 1; j > i + 1; --j) {
                 subst_wait(fX(j, ct), subst_rows(p, j), abort_word, p.limit, p.status);
                 const int64_t rj = (int64_t)j * p.T;
                 // -Z += L(rows of j, columns of the piece)^H X_j(:, ct)
@@ -387,15 +404,22 @@ __global__ void __launch_bounds__(SUB_THREADS) subst_kernel(const SubstArgs p)
             __syncthreads();
             acc.fold((R *)st);
             if (first)
-                acc.store(Z + r0 + (int64_t)c0 * p.ldz, p.ldz, nrow, ncol, R(-1));
+                acc.store(Zi + r0 + (int64_t)c0 * p.ldz, p.ldz, nrow, ncol, R(-1));
             subst_signal(fZ(i, ct));
         } else {
             subst_wait(fZ(i, ct), subst_rows(p, i), abort_word, p.limit, p.status);
             acc.zero();
-            // X = inv(L_ii)(rows r0.., columns of the piece)^H Z(r0.., ct)
+            // X = inv(L_ii)(rows r0.., columns of the piece)^H Z_i(r0.., ct)
             const E *const Iv = (const E *)p.Inv + (int64_t)i * p.T * p.T;
             subst_mma<R, CPLX, TC, KC>(acc, Iv + r0 + (int64_t)r0 * p.T, p.T, tki - r0, nrow,
-                                       Z + r0 + (int64_t)c0 * p.ldz, p.ldz, ncol, st);
+                                       Zi + r0 + (int64_t)c0 * p.ldz, p.ldz, ncol, st);
+            if (i + 1 < p.nt) {
+                // + G_i(:, columns of the piece)^H X_{i+1}(:, ct)
+                subst_wait(fX(i + 1, ct), subst_rows(p, i + 1), abort_word, p.limit, p.status);
+                const E *const Gi = (const E *)p.G + (int64_t)(i + 1) * p.T * p.T;
+                subst_mma<R, CPLX, TC, KC>(acc, Gi + (int64_t)r0 * p.T, p.T, tile_rows(i + 1), nrow,
+                                           B + row0 + p.T + (int64_t)c0 * p.ldb, p.ldb, ncol, st);
+            }
             __syncthreads();
             acc.fold((R *)st);
             if (first)
@@ -413,7 +437,7 @@ __global__ void __launch_bounds__(SUB_THREADS) subst_kernel(const SubstArgs p)
     if (last) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         const bool aborted = *(volatile int *)abort_word != 0;
-        const int nf = subst_flag_ints(p.nt, p.nc) - 1;  // all but the count of workgroups done
+        const int nf = (2 * frows + 1) * SUB_FLAG_STRIDE;  // all lines but the count of workgroups done
         for (int e = tid; e < nf; e += blockDim.x)
             p.flags[e] = 0;
         if (tid == 0)

@@ -59,21 +59,21 @@ def test_workspace_size(lib):
     # (768 bytes at T = 512, 256 at T = 100); for nrhs > 0 also two
     # buffers for the transposed solved block, (nrhs rounded up to 128) x (T
     # rounded up to 32), two sets of nt*T*T chain products, 8 partial
-    # T x nrhs blocks, the one-launch back substitution's T x nrhs block and
-    # its 2*nt*nc + 2 int counters (nc = ceil(nrhs / 64) column pieces, 32 wide
-    # when nrhs <= 32); each rounded up to 256 bytes
+    # T x nrhs blocks, the one-launch back substitution's two T x nrhs blocks
+    # and its 2*nt*nc + 2 counters of 128 bytes each (nc = ceil(nrhs / 64)
+    # column pieces, 32 wide when nrhs <= 32); each rounded up to 256 bytes
     n, nrhs, T = 32768, 128, 512
     up = lambda a, b: -(-a // b) * b
     el = (n // T) * T * T + 4 * n * T + T * T
-    solve = 2 * 128 * 512 + 2 * (n // T) * T * T + 8 * T * nrhs + T * nrhs
-    sflags = up(4 * (2 * 64 * 2 + 2), 256)
+    solve = 2 * 128 * 512 + 2 * (n // T) * T * T + 8 * T * nrhs + 2 * T * nrhs
+    sflags = up(4 * 32 * (2 * 64 * 2 + 2), 256)
     assert f(1, n, 0, T) == el * 8 + 256 + 768
     assert f(1, n, nrhs, T) == (el + solve) * 8 + 256 + 768 + sflags
     assert f(3, n, nrhs, T) == (el + solve) * 16 + 256 + 768 + sflags
     n, nrhs, T = 1000, 7, 100
     el = up(10 * 100 * 100, 32) + 4 * up(1024 * 128, 32) + up(100 * 100, 32)
-    solve = up(2 * 128 * 128, 32) + 2 * up(10 * 100 * 100, 32) + up(8 * 100 * 7, 32) + up(100 * 7, 32)
-    sflags = up(4 * (2 * 10 * 1 + 2), 256)
+    solve = up(2 * 128 * 128, 32) + 2 * up(10 * 100 * 100, 32) + up(8 * 100 * 7, 32) + up(2 * 100 * 7, 32)
+    sflags = up(4 * 32 * (2 * 10 * 1 + 2), 256)
     assert f(1, n, 0, T) == el * 8 + 256 + 256
     assert f(1, n, nrhs, T) == (el + solve) * 8 + 256 + 256 + sflags
     # T_A > n is clamped to n
