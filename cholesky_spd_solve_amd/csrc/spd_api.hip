@@ -1407,31 +1407,39 @@ struct Solver {
         return 0;
     }
 
-    // GB_k = -L_k,k-1 inv(L_k-1,k-1) into GB + k T T (leading dimension T, the
-    // rows of tile k) for the whole tiles k = 1 .. n / T - 1 in one batched
-    // product and, with ragged, for a short last tile in a second one.
+    // GB_k = -L_k,k-1 inv(L_k-1,k-1) into GB + k T T (leading dimension T) for
+    // the batch tiles k, k + 1, ..., each of m rows (m = min(T, n - k T) for
+    // one tile alone).
+    static int back_chain_product(int64_t k, int64_t m, int batch, const E *A, int64_t lda, int64_t T,
+                                  const E *Inv, E *GB, const int *info, hipStream_t s)
+    {
+        Gemm h;
+        h.A = A + k * T + (k - 1) * T * lda;
+        h.lda = lda;
+        h.sA_out = T * (1 + lda);
+        h.B = Inv + (k - 1) * T * T;
+        h.ldb = T;
+        h.sB_out = T * T;
+        h.C = GB + k * T * T;
+        h.ldc = T;
+        h.sC_out = T * T;
+        h.batch = batch;
+        h.m = m;
+        h.n = h.k = T;
+        h.kmode = KM_BEG_BY_J;
+        h.neg = true;
+        h.info = info;
+        return gemm<R, CPLX>(NN, h, s);
+    }
+
+    // GB_k for the whole tiles k = 1 .. n / T - 1 in one batched product and,
+    // with ragged, for a short last tile in a second one.
     static int back_chain_products(int64_t n, const E *A, int64_t lda, int64_t T, const E *Inv, E *GB,
                                    bool ragged, const int *info, hipStream_t s)
     {
         const int64_t nfull = n / T, tail = n - nfull * T;
         auto product = [&](int64_t k, int64_t m, int batch) {
-            Gemm h;
-            h.A = A + k * T + (k - 1) * T * lda;
-            h.lda = lda;
-            h.sA_out = T * (1 + lda);
-            h.B = Inv + (k - 1) * T * T;
-            h.ldb = T;
-            h.sB_out = T * T;
-            h.C = GB + k * T * T;
-            h.ldc = T;
-            h.sC_out = T * T;
-            h.batch = batch;
-            h.m = m;
-            h.n = h.k = T;
-            h.kmode = KM_BEG_BY_J;
-            h.neg = true;
-            h.info = info;
-            return gemm<R, CPLX>(NN, h, s);
+            return back_chain_product(k, m, batch, A, lda, T, Inv, GB, info, s);
         };
         if (nfull >= 2)
             SPD_TRY(product(1, T, (int)(nfull - 1)));
@@ -1447,11 +1455,12 @@ struct Solver {
     // becomes -1 if a wait of the launch runs out; X is then NaN.
     template <int TC>
     static int back_subst_tc(int64_t n, int64_t nrhs, const E *A, int64_t lda, E *B, int64_t ldb, const Layout &L,
-                             const int *info, int *status, void *work, hipStream_t s)
+                             const int *info, int *status, void *work, hipStream_t s, bool have_g)
     {
         SubstArgs p;
         E *const GB = (E *)work + L.gb;
-        SPD_TRY(back_chain_products(n, A, lda, L.T, (const E *)work + L.inv, GB, true, info, s));
+        if (!have_g)
+            SPD_TRY(back_chain_products(n, A, lda, L.T, (const E *)work + L.inv, GB, true, info, s));
         p.A = A;
         p.lda = lda;
         p.Inv = (const E *)work + L.inv;
@@ -1477,12 +1486,13 @@ struct Solver {
         SPD_CHECK_LAUNCH("subst_kernel");
         return 0;
     }
+    // have_g: the products G_i are already in the workspace's GB region
     static int back_subst(int64_t n, int64_t nrhs, const E *A, int64_t lda, E *B, int64_t ldb, const Layout &L,
-                          const int *info, int *status, void *work, hipStream_t s)
+                          const int *info, int *status, void *work, hipStream_t s, bool have_g = false)
     {
         if (subst_tc(nrhs) == 32)
-            return back_subst_tc<32>(n, nrhs, A, lda, B, ldb, L, info, status, work, s);
-        return back_subst_tc<64>(n, nrhs, A, lda, B, ldb, L, info, status, work, s);
+            return back_subst_tc<32>(n, nrhs, A, lda, B, ldb, L, info, status, work, s, have_g);
+        return back_subst_tc<64>(n, nrhs, A, lda, B, ldb, L, info, status, work, s, have_g);
     }
 
     // backward = false: the forward substitution L Y = B only
@@ -1559,8 +1569,15 @@ struct Solver {
         Lookahead la;  // the factorization's streams and events (shared per thread and device)
         SPD_TRY(la.begin(s));
         hipStream_t fs = la.look2;
+        // the one-launch back substitution's products G_k = GB_{k+1} (in GB,
+        // beyond the factorization's regions too), one per tile as its tile
+        // column of L becomes final
+        const bool one = subst_launch_enabled(n, nrhs, CPLX);
         auto step = [&](int64_t k) -> int {  // Y_k = inv(L_kk) B_k, then B below -= L_panel Y_k
             const int64_t c0 = k * T, tk = std::min(T, n - c0), r0 = c0 + tk, kp = align_up(tk, RECT_KB);
+            if (one && r0 < n)
+                SPD_TRY(back_chain_product(k + 1, std::min(T, n - r0), 1, A, lda, T, Inv, (E *)work + L.gb, info,
+                                           fs));
             SPD_TRY(apply_inv(Inv, k, T, B, ldb, c0, tk, nrhs, Tmp, false, info, fs));
             if (!blocks) {
                 SPD_TRY(copy2d<E>(B + c0, ldb, Tmp, T, tk, nrhs, info, fs));
@@ -1606,8 +1623,8 @@ struct Solver {
             SPD_TRY(logdet(n, A, lda, info, logdet_out, s));
         {
             ProfScope ps(PROF_SOLVE, FMUL * (double)n * n * nrhs, s);
-            if (subst_launch_enabled(n, nrhs, CPLX))
-                SPD_TRY(back_subst(n, nrhs, A, lda, B, ldb, L, info, info, work, s));
+            if (one)
+                SPD_TRY(back_subst(n, nrhs, A, lda, B, ldb, L, info, info, work, s, true));
             else if (blocks)
                 SPD_TRY(potrs_blocks(n, nrhs, A, lda, B, ldb, L, info, work, s, true, false, nullptr, false));
             else
