@@ -506,11 +506,12 @@ static bool check_tile(const TileArgs &p, unsigned grid, Checker &c)
     return true;
 }
 
-// Replay of subst_kernel (spd_subst.hpp): the role of every workgroup, the
+// Replay of subst_kernel (spd_subst.hpp): the piece of every workgroup, the
 // column segments each one reads and writes (the operand loads are masked to
-// them), and that every counter a role waits for is advanced by roles with
-// smaller ids only (each counter of (i, ct) by exactly the row pieces of
-// tile row i).
+// them), and that every counter a workgroup waits for is advanced only by
+// workgroups of its own or later tile rows (each counter of (i, ct) by
+// exactly the row pieces of tile row i), with the tile rows in id order from
+// the last.
 template <typename R, bool CPLX, int TC>
 static bool check_subst(const SubstArgs &p, unsigned grid, Checker &c)
 {
@@ -528,34 +529,38 @@ static bool check_subst(const SubstArgs &p, unsigned grid, Checker &c)
         return false;
     if (!c.access(p.flags, 4 * (size_t)subst_flag_ints(p.nt, p.nc), true, kn, 0, 0))
         return false;
-    // per (i, ct): roles counted by the Z counter and by the X counter, and
-    // the largest id among them
-    std::vector<int> zcount(p.nt * p.nc, 0), zlast(p.nt * p.nc, -1), xcount(p.nt * p.nc, 0),
-        xlast(p.nt * p.nc, -1);
-    std::vector<char> seen((size_t)p.nt * p.nr * p.nc * 2, 0);
+    // per (i, ct): pieces counted by the counters; per tile row: the ids it
+    // spans
+    std::vector<int> count(p.nt * p.nc, 0), row_lo(p.nt, INT32_MAX), row_hi(p.nt, -1);
+    std::vector<char> seen((size_t)p.nt * p.nr * p.nc, 0);
     for (unsigned g = 0; g < grid; ++g) {
         int i, rt, ct;
-        const int kind = subst_role(p, (int)g, i, rt, ct);
+        subst_piece(p, (int)g, i, rt, ct);
         if (i < 0 || i >= p.nt || rt < 0 || rt >= subst_rows(p, i) || ct < 0 || ct >= p.nc) {
-            c.err = "subst_kernel: a workgroup without a role";
+            c.err = "subst_kernel: a workgroup without a piece";
             return false;
         }
-        char &once = seen[((size_t)(i * p.nr + rt) * p.nc + ct) * 2 + kind];
+        char &once = seen[(size_t)(i * p.nr + rt) * p.nc + ct];
         if (once) {
-            c.err = "subst_kernel: two workgroups take the same role";
+            c.err = "subst_kernel: two workgroups take the same piece";
             return false;
         }
         once = 1;
-        std::vector<int> &cnt = kind == SUB_R ? zcount : xcount, &lst = kind == SUB_R ? zlast : xlast;
-        ++cnt[i * p.nc + ct];
-        lst[i * p.nc + ct] = std::max(lst[i * p.nc + ct], (int)g);
+        ++count[i * p.nc + ct];
+        row_lo[i] = std::min(row_lo[i], (int)g);
+        row_hi[i] = std::max(row_hi[i], (int)g);
     }
-    for (int i = 0; i < p.nt; ++i)
+    for (int i = 0; i < p.nt; ++i) {
+        if (i + 1 < p.nt && row_lo[i] <= row_hi[i + 1]) {
+            c.err = "subst_kernel: tile rows are not in id order from the last";
+            return false;
+        }
         for (int ct = 0; ct < p.nc; ++ct)
-            if (zcount[i * p.nc + ct] != subst_rows(p, i) || xcount[i * p.nc + ct] != subst_rows(p, i)) {
+            if (count[i * p.nc + ct] != subst_rows(p, i)) {
                 c.err = "subst_kernel: a counter does not count every row piece";
                 return false;
             }
+    }
     const E *A = (const E *)p.A, *Iv = (const E *)p.Inv, *G = (const E *)p.G;
     const E *B = (const E *)p.B, *Z = (const E *)p.Z;
     auto rows = [&](int ti) { return std::min(p.T, p.n - ti * p.T); };
@@ -566,10 +571,12 @@ static bool check_subst(const SubstArgs &p, unsigned grid, Checker &c)
                 return false;
         return true;
     };
-    auto after = [&](unsigned g, int producer) {
-        if (producer < 0 || producer >= (int)g) {
+    // a counter of tile row j awaited by workgroup g of tile row i: j > i, or
+    // j = i for the Z counter (the R parts of row i wait for later rows only)
+    auto from = [&](unsigned g, int i, int j, bool same_row_ok) {
+        if (j < i || (j == i && !same_row_ok)) {
             char buf[128];
-            snprintf(buf, sizeof buf, "subst_kernel: workgroup %u waits for workgroup %d", g, producer);
+            snprintf(buf, sizeof buf, "subst_kernel: workgroup %u (tile row %d) waits for tile row %d", g, i, j);
             c.err = buf;
             return false;
         }
@@ -577,35 +584,30 @@ static bool check_subst(const SubstArgs &p, unsigned grid, Checker &c)
     };
     for (unsigned g = 0; g < grid; ++g) {
         int i, rt, ct;
-        const int kind = subst_role(p, (int)g, i, rt, ct);
+        subst_piece(p, (int)g, i, rt, ct);
         const int tki = rows(i), r0 = rt * SUB_TR, c0 = ct * TC;
         const int nrow = std::min(SUB_TR, tki - r0), ncol = std::min(TC, p.nrhs - c0);
         const int64_t row0 = (int64_t)i * p.T;
         const E *Zi = Z + (i & 1) * p.ldz * p.nrhs;
-        if (kind == SUB_R) {
-            if (!seg(B, p.ldb, row0 + r0, nrow, c0, ncol, false, g) ||
-                !seg(Zi, p.ldz, r0, nrow, c0, ncol, true, g))
-                return false;
-            // the last term (j = i + 2) is also the wait that frees buffer i % 2
-            for (int j = p.nt - 1; j > i + 1; --j) {
-                const int64_t rj = (int64_t)j * p.T;
-                if (!after(g, xlast[j * p.nc + ct]) || !seg(A, p.lda, rj, rows(j), row0 + r0, nrow, false, g) ||
-                    !seg(B, p.ldb, rj, rows(j), c0, ncol, false, g))
-                    return false;
-            }
-        } else {
-            if (!after(g, zlast[i * p.nc + ct]))
-                return false;
-            if (!seg(Iv + (int64_t)i * p.T * p.T, p.T, r0, tki - r0, r0, nrow, false, g) ||
-                !seg(Zi, p.ldz, r0, tki - r0, c0, ncol, false, g) ||
-                !seg(B, p.ldb, row0 + r0, nrow, c0, ncol, true, g))
-                return false;
-            if (i + 1 < p.nt &&
-                (!after(g, xlast[(i + 1) * p.nc + ct]) ||
-                 !seg(G + (int64_t)(i + 1) * p.T * p.T, p.T, 0, rows(i + 1), r0, nrow, false, g) ||
-                 !seg(B, p.ldb, row0 + p.T, rows(i + 1), c0, ncol, false, g)))
+        // R part
+        if (!seg(B, p.ldb, row0 + r0, nrow, c0, ncol, false, g) || !seg(Zi, p.ldz, r0, nrow, c0, ncol, true, g))
+            return false;
+        // the last term (j = i + 2) is also the wait that frees buffer i % 2
+        for (int j = p.nt - 1; j > i + 1; --j) {
+            const int64_t rj = (int64_t)j * p.T;
+            if (!from(g, i, j, false) || !seg(A, p.lda, rj, rows(j), row0 + r0, nrow, false, g) ||
+                !seg(B, p.ldb, rj, rows(j), c0, ncol, false, g))
                 return false;
         }
+        // C part
+        if (!from(g, i, i, true) || !seg(Iv + (int64_t)i * p.T * p.T, p.T, r0, tki - r0, r0, nrow, false, g) ||
+            !seg(Zi, p.ldz, r0, tki - r0, c0, ncol, false, g) || !seg(B, p.ldb, row0 + r0, nrow, c0, ncol, true, g))
+            return false;
+        if (i + 1 < p.nt &&
+            (!from(g, i, i + 1, false) ||
+             !seg(G + (int64_t)(i + 1) * p.T * p.T, p.T, 0, rows(i + 1), r0, nrow, false, g) ||
+             !seg(B, p.ldb, row0 + p.T, rows(i + 1), c0, ncol, false, g)))
+            return false;
     }
     // a wait that runs out: the last workgroup fills X with NaN
     return seg(B, p.ldb, 0, p.n, 0, p.nrhs, true, 0);

@@ -11,32 +11,35 @@
 // from X_{i+1} to X_i is one product: Z_i and inv(L_ii)^H Z_i only need
 // X_{i+2} and are formed while X_{i+1} is still being solved.  Tile row i is
 // cut into row pieces of SUB_TR rows and column pieces of TC right-hand
-// sides; each piece (rt, ct) has two roles:
+// sides; the workgroup of piece (i, rt, ct) takes two parts in turn:
 //
-//   R(i, rt, ct): Z_i(rt, ct) = Y_i(rt, ct) - sum_{j > i+1} L_ji(:, rt)^H
-//                 X_j(:, ct), a term as soon as X_j(:, ct) is complete, in
-//                 decreasing j, into a workspace buffer (T rows; tile rows
-//                 of even and odd index take one buffer each);
-//   C(i, rt, ct): X_i(rt, ct) = sum_{r >= rt} inv(L_ii)^H(rt, r) Z_i(r, ct)
-//                 once Z_i(:, ct) is complete, then + G_i(:, rt)^H
-//                 X_{i+1}(:, ct) once that is complete; X goes into B.
+//   R: Z_i(rt, ct) = Y_i(rt, ct) - sum_{j > i+1} L_ji(:, rt)^H X_j(:, ct),
+//      a term as soon as X_j(:, ct) is complete, in decreasing j, into a
+//      workspace buffer (T rows; tile rows of even and odd index take one
+//      buffer each);
+//   C: X_i(rt, ct) = sum_{r >= rt} inv(L_ii)^H(rt, r) Z_i(r, ct) once
+//      Z_i(:, ct) is complete, then + G_i(:, rt)^H X_{i+1}(:, ct) once that
+//      is complete; X goes into B.
 //
-// Two counters per (i, ct) count the R roles and the C roles done: Z_i(:, ct)
+// Two counters per (i, ct) count the R parts and the C parts done: Z_i(:, ct)
 // and X_i(:, ct) are complete when they reach the tile row's number of row
-// pieces (one wait each, however many pieces).  Workgroup ids run over the tile rows from the last: the R
-// roles of tile row i, then its C roles.  Every role waits only for roles
-// with smaller ids, which are dispatched before it, so no waiting workgroup
-// holds back one it waits for.  Every wait is bounded in time as in the
+// pieces (one wait each, however many pieces).  Workgroup ids run over the
+// tile rows from the last.  A workgroup waits only for workgroups of its own
+// tile row (their R parts, which wait for nothing of that row) and of later
+// ones; workgroups are dispatched in id order, so by the time one of tile
+// row i waits, every workgroup of the later rows and of row i has been
+// dispatched or will be as the later rows finish, and no wait can hold back
+// the one it waits for.  Every wait is bounded in time as in the
 // one-launch diagonal tile (a wait that runs out raises an abort word that
 // ends the others and sets info to -1), and the last workgroup to finish
 // clears the flags, which are zero between launches (and, if a wait ran out,
 // fills X with NaN).
 //
-// Two Z buffers suffice: R(i, rt, ct) writes its piece of buffer i % 2 only
-// after X_{i+2}(:, ct) is complete, that is after every C role of tile row
-// i + 2 (the previous user of that buffer) has read column piece ct of it;
-// R roles of the last two tile rows have no terms and are the first users
-// of their buffers.
+// Two Z buffers suffice: the R part of piece (i, rt, ct) writes its piece of
+// buffer i % 2 only after X_{i+2}(:, ct) is complete, that is after every C
+// part of tile row i + 2 (the previous user of that buffer) has read column
+// piece ct of it; the R parts of the last two tile rows have no terms and
+// are the first users of their buffers.
 #pragma once
 
 #include "spd_kernels.hpp"
@@ -52,7 +55,6 @@ constexpr int SUB_FLAG_STRIDE = 32;
 // A waiting workgroup sleeps about 64 SUB_POLL_SLEEP clocks between polls
 // and looks at the abort word every fourth poll.
 constexpr int SUB_POLL_SLEEP = 4;
-enum { SUB_R = 0, SUB_C = 1 };
 
 struct SubstArgs {
     const void *A;    // L: first element, column-major, lda; lower triangle read
@@ -88,29 +90,24 @@ __host__ __device__ inline int subst_rows(const SubstArgs &p, int i)
 
 __host__ __device__ inline int subst_groups(const SubstArgs &p)
 {
-    return 2 * p.nc * (p.nr * (p.nt - 1) + subst_rows(p, p.nt - 1));
+    return p.nc * (p.nr * (p.nt - 1) + subst_rows(p, p.nt - 1));
 }
 
-// Role of workgroup g: kind, tile row i, row piece rt, column piece ct.
-__host__ __device__ inline int subst_role(const SubstArgs &p, int g, int &i, int &rt, int &ct)
+// Piece of workgroup g: tile row i, row piece rt, column piece ct.
+__host__ __device__ inline void subst_piece(const SubstArgs &p, int g, int &i, int &rt, int &ct)
 {
-    const int nrl = subst_rows(p, p.nt - 1), first = 2 * nrl * p.nc;
-    int per, rem;
+    const int first = subst_rows(p, p.nt - 1) * p.nc;
+    int idx;
     if (g < first) {
         i = p.nt - 1;
-        per = nrl;
-        rem = g;
+        idx = g;
     } else {
-        const int q = g - first, blk = 2 * p.nr * p.nc;
+        const int q = g - first, blk = p.nr * p.nc;
         i = p.nt - 2 - q / blk;
-        per = p.nr;
-        rem = q % blk;
+        idx = q % blk;
     }
-    const int kind = rem < per * p.nc ? SUB_R : SUB_C;
-    const int idx = rem % (per * p.nc);
     rt = idx / p.nc;
     ct = idx % p.nc;
-    return kind;
 }
 
 // Thread 0 polls *f until it reaches target (or the abort word is raised, or
@@ -367,7 +364,7 @@ __global__ void __launch_bounds__(SUB_THREADS) __attribute__((amdgpu_waves_per_e
     __shared__ int skip, last;
 
     int i, rt, ct;
-    const int kind = subst_role(p, (int)blockIdx.x, i, rt, ct);
+    subst_piece(p, (int)blockIdx.x, i, rt, ct);
     const int tid = threadIdx.x;
     const int frows = p.nt * p.nc;
     int *const abort_word = p.flags + 2 * frows * SUB_FLAG_STRIDE;
@@ -389,7 +386,7 @@ __global__ void __launch_bounds__(SUB_THREADS) __attribute__((amdgpu_waves_per_e
     __syncthreads();
     if (!skip) {
         SubstAcc<R, CPLX, TC> acc;
-        if (kind == SUB_R) {
+        {  // R
             if (first)
                 acc.load_neg(B + row0 + r0 + (int64_t)c0 * p.ldb, p.ldb, nrow, ncol);
             else
@@ -406,7 +403,8 @@ __global__ void __launch_bounds__(SUB_THREADS) __attribute__((amdgpu_waves_per_e
             if (first)
                 acc.store(Zi + r0 + (int64_t)c0 * p.ldz, p.ldz, nrow, ncol, R(-1));
             subst_signal(fZ(i, ct));
-        } else {
+        }
+        {  // C
             subst_wait(fZ(i, ct), subst_rows(p, i), abort_word, p.limit, p.status);
             acc.zero();
             // X = inv(L_ii)(rows r0.., columns of the piece)^H Z_i(r0.., ct)
