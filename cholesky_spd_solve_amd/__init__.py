@@ -41,7 +41,7 @@ PROF_SYRK, PROF_PANEL, PROF_DIAG, PROF_SOLVE, PROF_UPDATE, PROF_SYRK_AUX = 0, 1,
 # schedule / tile-shape options (spd_set_option)
 OPT_LOOKAHEAD, OPT_TWO_STEP, OPT_PAIR_ROWS, OPT_SYRK_DEEP_ROWS, OPT_RECT_TALL_ROWS = 1, 2, 3, 4, 5
 OPT_TILE_LAUNCH, OPT_TILE_WAIT_US, OPT_COLUMN_FIRST_ROWS, OPT_TILE_HOLD_ROWS = 6, 7, 8, 9
-OPT_SUBST_LAUNCH, OPT_TILE_UPDATE_ROWS = 10, 11
+OPT_SUBST_LAUNCH, OPT_TILE_UPDATE_ROWS, OPT_TRIPLE_ROWS = 10, 11, 12
 OPT_DEFAULT = -(1 << 63)
 
 _lock = threading.Lock()

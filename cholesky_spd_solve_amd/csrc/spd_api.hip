@@ -262,7 +262,7 @@ static int set_info(int *info, hipStream_t s)
 //                 L21 of four consecutive steps (potrf) / merge temporaries (both)
 //            TMP  max(T*T, T*n_rhs)   one block row of the right-hand side
 struct Layout {
-    int64_t T, nt, inv, w, wsz, tmp, ctr, flags, q, ldq, kq, qsz, gf, gb, part, z, ldz, sflags,
+    int64_t T, nt, inv, w, wsz, npanels, tmp, ctr, flags, q, ldq, kq, qsz, gf, gb, part, z, ldz, sflags,
         total;  // offsets / sizes in elements
 };
 
@@ -282,6 +282,10 @@ constexpr int64_t RECT_KB = 32;    // multiple of every block-update slice depth
 // products (two operand pairs, each split along its depth).
 constexpr int64_t CHAIN_SPLITS = 8;
 
+// Orders of at least this many tiles keep six trailing-update panel buffers
+// (three steps in use, three being built) instead of four.
+constexpr int64_t TRIPLE_MIN_TILES = 40;
+
 // The one-launch diagonal tile's flags start 256 bytes after the leaf + panel
 // counter (Layout::flags)
 static int *tile_flags(int *ctr) { return ctr + 256 / sizeof(int); }
@@ -295,7 +299,10 @@ static Layout make_layout(int64_t n, int64_t n_rhs, int64_t T_A, int64_t esize)
     L.inv = 0;
     L.w = align_up(L.nt * L.T * L.T, al);
     L.wsz = align_up(align_up(n, SYRK_LDW) * align_up(L.T, SYRK_KP), al);
-    L.tmp = L.w + 4 * L.wsz;  // four panel buffers: two steps in use, two being built
+    // panel buffers: the steps in use and those being built (two and two, or
+    // three and three for large orders)
+    L.npanels = L.nt >= TRIPLE_MIN_TILES ? 6 : 4;
+    L.tmp = L.w + L.npanels * L.wsz;
     // ctr: the fused leaf + panel launch's workgroup counter (one int);
     // flags: the one-launch diagonal tile's block flags and counter
     L.ctr = L.tmp + align_up(std::max(L.T * L.T, L.T * std::max<int64_t>(n_rhs, 1)), al);
@@ -413,15 +420,16 @@ enum {
     OPT_TILE_HOLD_ROWS,
     OPT_SUBST_LAUNCH,
     OPT_TILE_UPDATE_ROWS,
+    OPT_TRIPLE_ROWS,
     OPT_COUNT
 };
-static const int64_t k_opt_default[OPT_COUNT] = {1, 1, -1, -1, 16384, 1, 2000000, 8192, 8192, 2097152, -1};
+static const int64_t k_opt_default[OPT_COUNT] = {1, 1, -1, -1, 16384, 1, 2000000, 8192, 8192, 2097152, -1, -1};
 static std::atomic<int64_t> g_opt_store[OPT_COUNT] = {{1},       {1},    {-1},   {-1},      {16384}, {1},
-                                                      {2000000}, {8192}, {8192}, {2097152}, {-1}};
+                                                      {2000000}, {8192}, {8192}, {2097152}, {-1},    {-1}};
 struct Options {
     int64_t v[OPT_COUNT];
 };
-static thread_local Options g_opt = {{1, 1, -1, -1, 16384, 1, 2000000, 8192, 8192, 2097152, -1}};
+static thread_local Options g_opt = {{1, 1, -1, -1, 16384, 1, 2000000, 8192, 8192, 2097152, -1, -1}};
 
 static void snapshot_options()
 {
@@ -439,6 +447,16 @@ static bool two_step_enabled() { return g_opt.v[OPT_TWO_STEP] != 0; }
 static int64_t two_step_rows(int64_t T)
 {
     const int64_t v = g_opt.v[OPT_PAIR_ROWS];
+    return v >= 0 ? v : 32 * T;
+}
+
+// Orders of at least TRIPLE_MIN_TILES tiles keep six panel buffers instead of
+// four, and there the schedule takes steps in threes (trailing updates of
+// depth 3T) while at least three_step_rows(T) rows remain beyond the three
+// (SPD_OPT_TRIPLE_ROWS; 0: never).
+static int64_t three_step_rows(int64_t T)
+{
+    const int64_t v = g_opt.v[OPT_TRIPLE_ROWS];
     return v >= 0 ? v : 32 * T;
 }
 
@@ -1258,26 +1276,47 @@ struct Solver {
         return 0;
     }
 
-    // Two-step lookahead: while the trailing matrix is large, the update beyond
-    // the next two tile columns is applied every other step with both panels
-    // at once (depth 2T, which the trailing-update kernel runs at a higher rate
-    // than depth T).  For the pair of tiles (a, b = a+1), with panels W_a and
-    // W_b solved, the caller's stream applies [W_a | W_b] to the trailing
-    // matrix from tile a+4 on, while the auxiliary stream applies [W_a | W_b]
-    // to tile columns a+2 and a+3, factors tile a+2 and solves its panel,
-    // applies that panel to tile column a+3, and factors tile a+3 and solves
-    // its panel.  Once fewer than two_step_rows() rows would remain beyond the
-    // pair, the auxiliary stream's chain (two tiles) would be longer than the
-    // caller's update, and the schedule continues one step at a time as in
-    // potrf.  Step 0 is a single step whose auxiliary part solves tiles 1 and 2,
-    // so that the caller's first update starts after tile 0 alone.  Panels live
-    // in four buffers of one leading dimension; panel k's row 0 is row (k+1)T of
-    // A.
+    // Multi-step lookahead: while the trailing matrix is large, the update
+    // beyond the next tiles is applied once per group of steps with all of the
+    // group's panels at once (depth gT, g = 2 or 3), which the trailing-update
+    // kernel runs at a higher rate than depth T.  In state S(a, g) the panels
+    // W_a .. W_{a+g-1} are solved, tile columns a+1 .. a+g-1 have every update
+    // and the tiles from a+g on have the updates by the panels before a.  One
+    // group step S(a, g) -> S(a+g, h): the auxiliary stream applies
+    // [W_a | .. | W_{a+g-1}] to tile columns a+g .. a+g+h-1 and then factors
+    // those h tiles one after the other (each tile's panel applied to the
+    // group's later tile columns before the next tile), while the caller's
+    // stream applies [W_a | .. | W_{a+g-1}] to the trailing matrix from tile
+    // a+g+h on.  Groups of three while three_step_rows() rows remain beyond
+    // the new group (orders with six panel buffers), of two while
+    // two_step_rows() do; below that the auxiliary stream's chain (two or three
+    // tiles) would outlast the caller's update, and the schedule continues one
+    // step at a time as in potrf.  The first step, from tile 0 alone, already
+    // solves two or three tiles, so that the caller's first update starts after
+    // tile 0.  Panel k lives in buffer k mod npanels; every buffer's row r
+    // holds row r + T of A (panel k's first row, row (k+1)T, is its row kT),
+    // and the buffers are adjacent, so the panels of a group read from one
+    // row of A on are one operand of depth gT (two, where the group wraps
+    // from the last buffer to the first).
     static int potrf_pairs(int64_t n, E *A, int64_t lda, const Layout &L, E *Inv0, int *info, int *ctr, void *work,
                            hipStream_t s, const PanelHook *hook = nullptr)
     {
         const int64_t T = L.T, nt = L.nt, ldw = align_up(n, SYRK_LDW), kp = align_up(T, SYRK_KP);
-        auto Wp = [&](int64_t k) { return (E *)work + L.w + (k % 4) * L.wsz; };
+        const int64_t NB = L.npanels;
+        E *const W0 = (E *)work + L.w;
+        auto Wp = [&](int64_t k) { return W0 + (k % NB) * L.wsz + k * T; };
+        // [W_a | .. | W_{a+g-1}] from row r of A on; x gets the second operand
+        // if the group wraps past the last buffer
+        auto group = [&](int64_t a, int64_t g, int64_t r, Syr2 &x) -> const E * {
+            const int64_t b = a % NB;
+            x.W2 = nullptr;
+            x.kp1 = 0;
+            if (b + g > NB) {
+                x.W2 = W0 + (r - T);
+                x.kp1 = (NB - b) * kp;
+            }
+            return W0 + b * L.wsz + (r - T);
+        };
         auto C = [&](int64_t k) { return A + k * T * (1 + lda); };  // trailing matrix from tile k
         auto Iv = [&](int64_t k) { return hook != nullptr ? Inv0 + k * T * T : Inv0; };
         auto diag_panel = [&](int64_t c0, E *Wk, hipStream_t st, const E *Wprev = nullptr,
@@ -1288,54 +1327,63 @@ struct Solver {
         Lookahead la;
         SPD_TRY(la.begin(s));
         hipStream_t sl = la.look;
-        // step 0 as a single step whose auxiliary part reaches two tiles ahead:
-        // tile columns 1 and 2 by W_0, tile 1, tile column 2 by W_1, tile 2;
-        // meanwhile the caller's stream applies W_0 from tile 3 on
+        // S(a, g) -> S(a+g, h)
+        auto group_step = [&](int64_t a, int64_t g, int64_t h) -> int {
+            const int64_t c = a + g, e = c + h;
+            SPD_TRY(la.wait(s, la.ev_panel));  // panels a .. c-1
+            if (a > 0)
+                SPD_TRY(la.wait(sl, la.ev_rest));  // the caller's update before has reached tile column c
+            Syr2 x;
+            x.aux = true;
+            const E *Wc = group(a, g, c * T, x);
+            SPD_TRY(syrk(n - c * T, Wc, ldw, g * kp, g * T, C(c), lda, h * T, info, sl, x));
+            for (int64_t t = c; t < e; ++t) {
+                SPD_TRY(diag_panel(t * T, Wp(t), sl));
+                if (t + 1 < e)
+                    SPD_TRY(syrk(n - (t + 1) * T, Wp(t), ldw, kp, T, C(t + 1), lda, (e - 1 - t) * T, info, sl,
+                                 aux_update()));
+            }
+            SPD_TRY(la.record(la.ev_panel, sl));
+            SPD_TRY(done(c, e));
+            if (e * T < n) {
+                Syr2 y;
+                const E *We = group(a, g, e * T, y);
+                SPD_TRY(syrk(n - e * T, We, ldw, g * kp, g * T, C(e), lda, 0, info, s, y));
+            }
+            SPD_TRY(la.record(la.ev_rest, s));
+            return 0;
+        };
+        // the size of the next group from S(a, g)
+        const int64_t triple_rows = NB >= 6 ? three_step_rows(T) : 0, pair_rows = two_step_rows(T);
+        auto next_group = [&](int64_t a, int64_t g) -> int64_t {
+            const int64_t c = a + g;
+            if (triple_rows > 0 && c + 3 <= nt && n - (c + 3) * T >= triple_rows)
+                return 3;
+            if (c + 2 <= nt && (a == 0 || n - (c + 2) * T >= pair_rows))
+                return 2;
+            return 1;
+        };
         SPD_TRY(diag_panel(0, Wp(0), sl));
         SPD_TRY(la.record(la.ev_panel, sl));
         SPD_TRY(done(0, 1));
-        SPD_TRY(la.wait(s, la.ev_panel));  // panel 0
-        SPD_TRY(syrk(n - T, Wp(0), ldw, kp, T, C(1), lda, 2 * T, info, sl, aux_update()));
-        SPD_TRY(diag_panel(T, Wp(1), sl));
-        SPD_TRY(syrk(n - 2 * T, Wp(1), ldw, kp, T, C(2), lda, T, info, sl, aux_update()));
-        SPD_TRY(diag_panel(2 * T, Wp(2), sl));
-        SPD_TRY(la.record(la.ev_panel, sl));
-        SPD_TRY(done(1, 3));
-        if (3 * T < n)
-            SPD_TRY(syrk(n - 3 * T, Wp(0) + 2 * T, ldw, kp, T, C(3), lda, 0, info, s));
-        SPD_TRY(la.record(la.ev_rest, s));
-        // pairs: panels a and a+1 solved, tile column a+1 updated by every panel
-        // before it, tiles from a+2 on by the panels before a
-        const int64_t pair_rows = two_step_rows(T);
-        int64_t a = 1;
-        for (; a + 1 < nt && n - (a + 4) * T >= pair_rows; a += 2) {
-            const int64_t c = a + 2, d = a + 3, e = a + 4;
-            SPD_TRY(la.wait(s, la.ev_panel));  // panels a and b
-            SPD_TRY(la.wait(sl, la.ev_rest));  // the update before has reached tile columns c and d
-            Syr2 x;
-            x.kp1 = kp;
-            // tile columns c and d by [W_a | W_b] (W_a's rows from tile c start at its row T)
-            x.W2 = Wp(a + 1);
-            x.aux = true;
-            SPD_TRY(syrk(n - c * T, Wp(a) + T, ldw, 2 * kp, 2 * T, C(c), lda, 2 * T, info, sl, x));
-            x.aux = false;
-            SPD_TRY(diag_panel(c * T, Wp(c), sl));
-            SPD_TRY(syrk(n - d * T, Wp(c), ldw, kp, T, C(d), lda, T, info, sl, aux_update()));
-            SPD_TRY(diag_panel(d * T, Wp(d), sl));
-            SPD_TRY(la.record(la.ev_panel, sl));
-            SPD_TRY(done(c, d + 1));
-            x.W2 = Wp(a + 1) + 2 * T;  // W_b's rows from tile e
-            SPD_TRY(syrk(n - e * T, Wp(a) + 3 * T, ldw, 2 * kp, 2 * T, C(e), lda, 0, info, s, x));
-            SPD_TRY(la.record(la.ev_rest, s));
+        int64_t a = 0, g = 1;
+        for (;;) {
+            if (a + g >= nt)
+                break;
+            const int64_t h = next_group(a, g);
+            if (g == 1 && h == 1 && a > 0)
+                break;  // single steps from k = a on
+            SPD_TRY(group_step(a, g, h));
+            a += g;
+            g = h;
         }
-        // single steps from k = a: tile column a+1 and panel a+1 are done already,
-        // so step a only applies W_a to the tiles from a+2 on
-        SPD_TRY(la.wait(s, la.ev_panel));
-        SPD_TRY(la.wait(sl, la.ev_rest));
-        if ((a + 2) * T < n)
-            SPD_TRY(syrk(n - (a + 2) * T, Wp(a) + T, ldw, kp, T, C(a + 2), lda, 0, info, s));
-        SPD_TRY(la.record(la.ev_rest, s));
-        for (int64_t k = a + 1; k + 1 < nt; ++k) {
+        if (a + g >= nt) {
+            SPD_TRY(la.wait(s, la.ev_panel));  // join: the last tile
+            return 0;
+        }
+        // single steps from k = a (S(a, 1): panel a solved, the tiles from a+1
+        // on updated by the panels before a)
+        for (int64_t k = a; k + 1 < nt; ++k) {
             if (tile_launch_enabled() && n - (k + 2) * T < tile_update_rows(CPLX)) {
                 // Tile k+1 takes its update by W_k inside its own launch, beside
                 // the caller's update of everything else from tile column k+1
@@ -2648,6 +2696,7 @@ int spd_set_option(spd_option_t opt, int64_t value)
     case OPT_PAIR_ROWS:
     case OPT_SYRK_DEEP_ROWS:
     case OPT_TILE_UPDATE_ROWS:
+    case OPT_TRIPLE_ROWS:
         if (value < -1)
             return -2;
         break;

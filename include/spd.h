@@ -247,9 +247,10 @@ const char *spd_last_error(void);
  *   SPD_OPT_LOOKAHEAD        1 (default): the factorization and the
  *                            substitutions run one step ahead on an auxiliary
  *                            stream; 0: everything in order on `stream`
- *   SPD_OPT_TWO_STEP         1 (default): under lookahead, pairs of steps share
- *                            one trailing update of depth 2 T_A while the
- *                            trailing matrix is large; 0: one step at a time
+ *   SPD_OPT_TWO_STEP         1 (default): under lookahead, groups of steps
+ *                            (pairs, threes: TRIPLE_ROWS) share one trailing
+ *                            update of depth 2 or 3 T_A while the trailing
+ *                            matrix is large; 0: one step at a time
  *                            (spd_posv then runs its three parts in sequence)
  *   SPD_OPT_PAIR_ROWS        steps are paired while at least this many rows
  *                            remain beyond the pair; -1 (default): 32 T_A
@@ -298,9 +299,16 @@ const char *spd_last_error(void);
  *                            update on `stream` covers the rest of its tile
  *                            column; -1 (default): 2048 for real types, 0
  *                            (never) for complex ones
+ *   SPD_OPT_TRIPLE_ROWS      orders of at least 40 tiles (whose workspace
+ *                            holds six trailing-update panels) take the
+ *                            factorization's steps in threes, one trailing
+ *                            update of depth 3 T_A per three steps, while at
+ *                            least this many rows remain beyond the three;
+ *                            then in pairs (PAIR_ROWS) and one at a time; -1
+ *                            (default): 32 T_A; 0: never
  * spd_set_option returns 0, -1 for an unknown option, -2 for a value out of
  * range (LOOKAHEAD, TWO_STEP and TILE_LAUNCH take 0 or 1, PAIR_ROWS,
- * SYRK_DEEP_ROWS and TILE_UPDATE_ROWS >= -1, RECT_TALL_ROWS, TILE_WAIT_US,
+ * SYRK_DEEP_ROWS, TILE_UPDATE_ROWS and TRIPLE_ROWS >= -1, RECT_TALL_ROWS, TILE_WAIT_US,
  * COLUMN_FIRST_ROWS, TILE_HOLD_ROWS and SUBST_LAUNCH >= 0);
  * SPD_OPT_DEFAULT restores an option's default.
  * spd_get_option returns the current value (INT64_MIN for an unknown
@@ -316,7 +324,8 @@ typedef enum {
     SPD_OPT_COLUMN_FIRST_ROWS = 8,
     SPD_OPT_TILE_HOLD_ROWS = 9,
     SPD_OPT_SUBST_LAUNCH = 10,
-    SPD_OPT_TILE_UPDATE_ROWS = 11
+    SPD_OPT_TILE_UPDATE_ROWS = 11,
+    SPD_OPT_TRIPLE_ROWS = 12
 } spd_option_t;
 #define SPD_OPT_DEFAULT INT64_MIN
 int spd_set_option(spd_option_t opt, int64_t value);

@@ -174,3 +174,21 @@ def test_dry_run_posv_noalloc_rejects_large_sizes(lib):
     assert rc == 3
     assert b"bytes of workspace" in lib.spd_last_error()
     assert lib.spd_posv_noalloc(0, 4, 1, vp(BASE), 3, vp(2 * BASE), 4, 2, vp(3 * BASE), None, None) == -5
+
+
+@pytest.mark.parametrize("triple_rows,pair_rows", [(-1, -1), (1, 0), (1, -1), (0, 0)])
+@pytest.mark.parametrize("dt,n,nrhs,T", [("f64", 6001, 3, 128), ("f32", 5120, 2, 128)])
+def test_dry_run_step_groups(lib, dt, n, nrhs, T, triple_rows, pair_rows):
+    """Orders of 40 tiles and more keep six trailing-update panels and take
+    the factorization's steps in threes while the trailing matrix is large;
+    every mix of threes, pairs and single steps (a ragged last tile, the
+    groups wrapping around the six buffers) replays in bounds, through the
+    three calls and the fused solve."""
+    code = CODE[dt]
+    with spd.options({spd.OPT_TRIPLE_ROWS: triple_rows, spd.OPT_PAIR_ROWS: pair_rows}):
+        dry_solve(lib, code, n, nrhs, T)
+        vp = ctypes.c_void_p
+        A, B, info, ld, work = BASE, 2 * BASE, 3 * BASE, 3 * BASE + 4096, 4 * BASE
+        wbytes = lib.spd_workspace_size(code, n, nrhs, T)
+        rc = lib.spd_posv(code, n, nrhs, vp(A), n, vp(B), n, T, vp(info), vp(ld), vp(work), wbytes, None)
+        assert rc == 0, (rc, lib.spd_last_error())

@@ -53,7 +53,7 @@ def test_workspace_size(lib):
     assert f(1, 10, -1, 64) == 0
     assert f(1, 10, 1, 0) == 0
     assert f(9, 10, 1, 4) == 0
-    # INV nt*T*T + four panels of (n rounded up to 128) x (T rounded up to 32)
+    # INV nt*T*T + four panels (six from 40 tiles on) of (n rounded up to 128) x (T rounded up to 32)
     # + TMP max(T*T, T*nrhs) + a 256-byte counter + the one-launch diagonal
     # tile's 2 nb^2 + 2 int flags (nb = ceil(T / 64)) rounded up to 256 bytes
     # (768 bytes at T = 512, 256 at T = 100); for nrhs > 0 also two
@@ -64,7 +64,7 @@ def test_workspace_size(lib):
     # column pieces, 32 wide when nrhs <= 32); each rounded up to 256 bytes
     n, nrhs, T = 32768, 128, 512
     up = lambda a, b: -(-a // b) * b
-    el = (n // T) * T * T + 4 * n * T + T * T
+    el = (n // T) * T * T + 6 * n * T + T * T  # 64 tiles: six panel buffers
     solve = 2 * 128 * 512 + 2 * (n // T) * T * T + 8 * T * nrhs + 2 * T * nrhs
     sflags = up(4 * 32 * (2 * 64 * 2 + 2), 256)
     assert f(1, n, 0, T) == el * 8 + 256 + 768
@@ -170,12 +170,13 @@ def test_options_validate_and_restore(lib):
     import cholesky_spd_solve_amd as spd
     defaults = {spd.OPT_LOOKAHEAD: 1, spd.OPT_TWO_STEP: 1, spd.OPT_PAIR_ROWS: -1, spd.OPT_SYRK_DEEP_ROWS: -1,
                 spd.OPT_RECT_TALL_ROWS: 16384, spd.OPT_TILE_LAUNCH: 1, spd.OPT_TILE_WAIT_US: 2000000,
-                spd.OPT_COLUMN_FIRST_ROWS: 8192, spd.OPT_TILE_HOLD_ROWS: 8192, spd.OPT_SUBST_LAUNCH: 2097152, spd.OPT_TILE_UPDATE_ROWS: -1}
+                spd.OPT_COLUMN_FIRST_ROWS: 8192, spd.OPT_TILE_HOLD_ROWS: 8192, spd.OPT_SUBST_LAUNCH: 2097152, spd.OPT_TILE_UPDATE_ROWS: -1,
+                spd.OPT_TRIPLE_ROWS: -1}
     for k, v in defaults.items():
         assert spd.get_option(k) == v
     assert lib.spd_set_option(0, 1) == -1
-    assert lib.spd_set_option(12, 1) == -1
-    assert lib.spd_get_option(12) == -(1 << 63)
+    assert lib.spd_set_option(13, 1) == -1
+    assert lib.spd_get_option(13) == -(1 << 63)
     assert lib.spd_set_option(spd.OPT_LOOKAHEAD, 2) == -2
     assert lib.spd_set_option(spd.OPT_TWO_STEP, -1) == -2
     assert lib.spd_set_option(spd.OPT_PAIR_ROWS, -2) == -2
@@ -186,6 +187,7 @@ def test_options_validate_and_restore(lib):
     assert lib.spd_set_option(spd.OPT_TILE_HOLD_ROWS, -1) == -2
     assert lib.spd_set_option(spd.OPT_SUBST_LAUNCH, -1) == -2
     assert lib.spd_set_option(spd.OPT_TILE_UPDATE_ROWS, -2) == -2
+    assert lib.spd_set_option(spd.OPT_TRIPLE_ROWS, -2) == -2
     with spd.options({spd.OPT_PAIR_ROWS: 0, spd.OPT_LOOKAHEAD: 0, spd.OPT_RECT_TALL_ROWS: 7}):
         assert spd.get_option(spd.OPT_PAIR_ROWS) == 0
         assert spd.get_option(spd.OPT_LOOKAHEAD) == 0
