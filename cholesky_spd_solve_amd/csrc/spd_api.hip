@@ -466,11 +466,12 @@ static int64_t three_step_rows(int64_t T)
 static bool lookahead_enabled() { return g_opt.v[OPT_LOOKAHEAD] != 0; }
 
 // Trailing-update orders from which 128-row tiles take the deeper slices
-// (fp64: 16 instead of 8; fp32: 32 instead of 16).
+// (fp64: 16 instead of 8, by default never since the early updates are taken
+// at depth 3T; fp32: 32 instead of 16).
 static int64_t syrk_deep_rows(int64_t esize)
 {
     const int64_t v = g_opt.v[OPT_SYRK_DEEP_ROWS];
-    return v >= 0 ? v : (esize == 8 ? 24576 : 8192);
+    return v >= 0 ? v : (esize == 8 ? INT64_MAX : 8192);
 }
 
 // Block-update heights from which the substitutions (and the factorization's
@@ -972,8 +973,8 @@ struct Solver {
                     return syrk_cfg<128, 32, 2, 4, false, true>(m, W, ldw, kp, C, ldc, jt(128), info, s, x);
                 return syrk_cfg<128, 16, 2, 4>(m, W, ldw, kp, C, ldc, jt(128), info, s, x);
             } else {
-                // slice depth: 16 for the large early steps, 8 below (more
-                // workgroups in flight per byte of LDS; measured better for m < ~24k)
+                // slice depth 8 (more workgroups in flight per byte of LDS);
+                // 16 from syrk_deep_rows(8) on, which the option can set
                 if (m >= syrk_deep_rows(8))
                     return syrk_cfg<128, 16, 2, 4>(m, W, ldw, kp, C, ldc, jt(128), info, s, x);
                 return syrk_cfg<128, 8, 2, 4>(m, W, ldw, kp, C, ldc, jt(128), info, s, x);

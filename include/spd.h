@@ -256,7 +256,7 @@ const char *spd_last_error(void);
  *                            remain beyond the pair; -1 (default): 32 T_A
  *   SPD_OPT_SYRK_DEEP_ROWS   trailing updates of at least this order on
  *                            128-row tiles take the deeper operand slices;
- *                            -1 (default): 24576 (fp64), 8192 (fp32)
+ *                            -1 (default): never (fp64), 8192 (fp32)
  *   SPD_OPT_RECT_TALL_ROWS   block updates of the substitutions and the
  *                            panel products of at least this many rows take
  *                            64-row tiles, fewer rows 32-row tiles (default
