@@ -1618,13 +1618,13 @@ struct Solver {
         Lookahead la;  // the factorization's streams and events (shared per thread and device)
         SPD_TRY(la.begin(s));
         hipStream_t fs = la.look2;
-        // the one-launch back substitution's products G_k = GB_{k+1} (in GB,
-        // beyond the factorization's regions too), one per tile as its tile
-        // column of L becomes final
+        // the back substitution's chain products G_k = GB_{k+1} (in GB, beyond
+        // the factorization's regions too), one per tile as its tile column of
+        // L becomes final (for the one launch and for the block steps)
         const bool one = subst_launch_enabled(n, nrhs, CPLX);
         auto step = [&](int64_t k) -> int {  // Y_k = inv(L_kk) B_k, then B below -= L_panel Y_k
             const int64_t c0 = k * T, tk = std::min(T, n - c0), r0 = c0 + tk, kp = align_up(tk, RECT_KB);
-            if (one && r0 < n)
+            if ((one || blocks) && r0 < n)
                 SPD_TRY(back_chain_product(k + 1, std::min(T, n - r0), 1, A, lda, T, Inv, (E *)work + L.gb, info,
                                            fs));
             SPD_TRY(apply_inv(Inv, k, T, B, ldb, c0, tk, nrhs, Tmp, false, info, fs));
@@ -2080,7 +2080,7 @@ struct Solver {
     // right-hand sides).
     //
     // forward = false (the fused solve): only L^H X = B, with the tile
-    // inverses already in the workspace.
+    // inverses and the chain products GB_k already in the workspace.
     static int potrs_blocks(int64_t n, int64_t nrhs, const E *A, int64_t lda, E *B, int64_t ldb, const Layout &L,
                             const int *info, void *work, hipStream_t s, bool backward, bool prefix = false,
                             E *const *lp = nullptr, bool forward = true)
@@ -2126,7 +2126,7 @@ struct Solver {
             g.info = info;
             SPD_TRY((gemm<R, CPLX>(NN, g, s)));
         }
-        if (split && backward)  // GB_k for whole blocks k (k = 1 .. nfull-1)
+        if (split && backward && forward)  // GB_k for whole blocks k (k = 1 .. nfull-1)
             SPD_TRY(back_chain_products(n, A, lda, T, Inv, GB, false, info, s));
         // Next block (index kn, rows [cn, cn + T)) in one split product:
         //   forward:  Y_kn = GF_k Y_k + inv(L_kn,kn) B_kn          (kn = k + 1)
