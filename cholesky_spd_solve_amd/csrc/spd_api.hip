@@ -935,8 +935,8 @@ struct Solver {
     static int syrk(int64_t m, const E *W, int64_t ldw, int64_t kp, int64_t kw, E *C, int64_t ldc, int64_t cols,
                     const int *info, hipStream_t s, const Syr2 &x = Syr2())
     {
-        if (m <= 0)
-            return 0;
+        if (m <= 0 || x.skip >= m)
+            return 0;  // nothing to update (no launch, nothing timed)
         const int64_t w = cols > 0 ? std::min<int64_t>(m, cols) : m;  // columns of C updated
         if (x.W2 != nullptr && x.V != nullptr) {
             g_last_error = "two-panel update is for the symmetric form";
