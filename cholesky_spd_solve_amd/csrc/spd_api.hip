@@ -437,11 +437,11 @@ static void snapshot_options()
         g_opt.v[i] = g_opt_store[i].load(std::memory_order_relaxed);
 }
 
-// The two-step schedule of potrf (trailing updates of depth 2T) is used unless
-// SPD_OPT_TWO_STEP is 0; it pairs steps while at least two_step_rows(T) rows
-// remain beyond the pair (SPD_OPT_PAIR_ROWS; by default 32 T: below that the
-// auxiliary stream's two-tile chain, sharing the GPU with the caller's update,
-// outlasts it).
+// The multi-step schedule of potrf (trailing updates of depth 2T or 3T, see
+// potrf_pairs) is used unless SPD_OPT_TWO_STEP is 0; it pairs steps while at
+// least two_step_rows(T) rows remain beyond the pair (SPD_OPT_PAIR_ROWS; by
+// default 32 T: below that the auxiliary stream's two-tile chain, sharing the
+// GPU with the caller's update, outlasts it).
 static bool two_step_enabled() { return g_opt.v[OPT_TWO_STEP] != 0; }
 
 static int64_t two_step_rows(int64_t T)
@@ -862,7 +862,8 @@ struct Solver {
         int krange = SYRK_K_ALL;
         bool add = false;
         int64_t ncols = 0;  // > 0: the whole m x ncols rectangle (rect_update)
-        const E *W2 = nullptr;  // second panel for depth [kp1, kp) (the two-step update)
+        const E *W2 = nullptr;  // second operand for depth [kp1, kp) (a group of panels that
+                                // wraps from the last panel buffer to the first)
         int64_t kp1 = 0;
         bool aux = false;  // potrf's auxiliary stream (timed as its own class)
         int64_t skip = 0;  // the lower triangle without its leading skip x skip block
@@ -1586,8 +1587,8 @@ struct Solver {
     }
 
     // Fused solve: potrf, log det (optional) and potrs in one call.  With the
-    // two-step factorization schedule (real types, block-update kernel usable)
-    // the forward substitution runs on a second auxiliary stream, one block as
+    // multi-step factorization schedule (any type) the forward substitution
+    // runs on a second auxiliary stream, one block as
     // soon as its tile of L is final (the factorization keeps every tile's
     // inverse), so that it fills the factorization's chain-bound tail; the
     // back substitution follows.  Otherwise the three calls in sequence.
