@@ -64,8 +64,10 @@ enum { TILE_D = 0, TILE_O = 1, TILE_X = 2 };
 
 __host__ __device__ inline int tile_groups(int nb) { return nb * nb - nb + 1; }
 // flags: L blocks (nb x nb), inverse blocks (nb x nb), the abort word and the
-// workgroup counter
-__host__ __device__ inline int tile_flag_ints(int nb) { return 2 * nb * nb + 2; }
+// workgroup counter, each on a 128-byte line of its own (TILE_FLAG_STRIDE
+// ints), so that polls and raises of different flags go to different lines
+constexpr int TILE_FLAG_STRIDE = 32;
+__host__ __device__ inline int tile_flag_ints(int nb) { return (2 * nb * nb + 2) * TILE_FLAG_STRIDE; }
 
 // Role of workgroup g: kind and block (i, j); -1 past the last role.
 __host__ __device__ inline int tile_role(int nb, int g, int &i, int &j)
@@ -98,19 +100,20 @@ __host__ __device__ inline int tile_role(int nb, int g, int &i, int &j)
 }
 
 // Thread 0 polls the flags (f2 may be null) until both are raised, the abort
-// word is raised, or the time limit passes (then it raises the abort word and
-// records info = -1 unless info is set); then the workgroup proceeds.
+// word (looked at every fourth poll) is raised, or the time limit passes (then
+// it raises the abort word and records info = -1 unless info is set); then the
+// workgroup proceeds.
 __device__ inline void tile_wait(const int *f1, const int *f2, int *abort_word, int64_t limit, int *info)
 {
     if (threadIdx.x == 0) {
         // the poll count bounds the wait as well, should the clock not run
-        // (one poll takes well over 16 ticks: three agent-scope loads)
+        // (one poll takes well over 16 ticks: two or three agent-scope loads)
         const int64_t t0 = (int64_t)wall_clock64(), max_polls = limit / 16 + 64;
         for (int64_t polls = 0;; ++polls) {
             if (__hip_atomic_load(f1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0 &&
                 (f2 == nullptr || __hip_atomic_load(f2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0))
                 break;
-            if (__hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+            if ((polls & 3) == 3 && __hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
                 break;
             if ((int64_t)wall_clock64() - t0 > limit || polls > max_polls) {
                 __hip_atomic_store(abort_word, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -278,13 +281,13 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) t
     const int kind = tile_role(nb, (int)blockIdx.x, bi, bj);
     R *const A = (R *)p.D;
     R *const Iv = (R *)p.Inv;
-    int *const abort_word = p.flags + 2 * nb * nb;
-    int *const ctr = abort_word + 1;
+    int *const abort_word = p.flags + 2 * nb * nb * TILE_FLAG_STRIDE;
+    int *const ctr = abort_word + TILE_FLAG_STRIDE;
     auto nrows = [&](int b) { return (p.tk - b * LEAF) < LEAF ? p.tk - b * LEAF : LEAF; };
     auto Ab = [&](int i, int j) { return A + (int64_t)i * LEAF + (int64_t)j * LEAF * p.lda; };
     auto Xb = [&](int i, int j) { return Iv + (int64_t)i * LEAF + (int64_t)j * LEAF * p.ldi; };
-    auto fL = [&](int i, int j) { return p.flags + i * nb + j; };
-    auto fX = [&](int i, int j) { return p.flags + nb * nb + i * nb + j; };
+    auto fL = [&](int i, int j) { return p.flags + (i * nb + j) * TILE_FLAG_STRIDE; };
+    auto fX = [&](int i, int j) { return p.flags + (nb * nb + i * nb + j) * TILE_FLAG_STRIDE; };
     auto wait = [&](const int *f1, const int *f2) { tile_wait(f1, f2, abort_word, p.limit, p.info); };
     TileBlk<R> u, w;
 
@@ -441,7 +444,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) t
         last = atomicAdd(ctr, 1) == (int)gridDim.x - 1;
     __syncthreads();
     if (last) {
-        for (int e = tid; e < 2 * nb * nb + 1; e += 256)
+        for (int e = tid; e < (2 * nb * nb + 1) * TILE_FLAG_STRIDE; e += 256)
             p.flags[e] = 0;
         if (tid == 0)
             *ctr = 0;
@@ -600,13 +603,13 @@ __global__ void __launch_bounds__(256) tile_kernel_c(const TileArgs p)
     const int kind = tile_role(nb, (int)blockIdx.x, bi, bj);
     E *const A = (E *)p.D;
     E *const Iv = (E *)p.Inv;
-    int *const abort_word = p.flags + 2 * nb * nb;
-    int *const ctr = abort_word + 1;
+    int *const abort_word = p.flags + 2 * nb * nb * TILE_FLAG_STRIDE;
+    int *const ctr = abort_word + TILE_FLAG_STRIDE;
     auto nrows = [&](int b) { return (p.tk - b * LEAF) < LEAF ? p.tk - b * LEAF : LEAF; };
     auto Ab = [&](int i, int j) { return A + (int64_t)i * LEAF + (int64_t)j * LEAF * p.lda; };
     auto Xb = [&](int i, int j) { return Iv + (int64_t)i * LEAF + (int64_t)j * LEAF * p.ldi; };
-    auto fL = [&](int i, int j) { return p.flags + i * nb + j; };
-    auto fX = [&](int i, int j) { return p.flags + nb * nb + i * nb + j; };
+    auto fL = [&](int i, int j) { return p.flags + (i * nb + j) * TILE_FLAG_STRIDE; };
+    auto fX = [&](int i, int j) { return p.flags + (nb * nb + i * nb + j) * TILE_FLAG_STRIDE; };
     auto wait = [&](const int *f1, const int *f2) { tile_wait(f1, f2, abort_word, p.limit, p.info); };
     // operand fetchers: M(r, k) of a global block with nr rows, its conjugate
     // transpose conj(M(c, k)) at (k, c), and the LDS planes
@@ -790,7 +793,7 @@ __global__ void __launch_bounds__(256) tile_kernel_c(const TileArgs p)
         last = atomicAdd(ctr, 1) == (int)gridDim.x - 1;
     __syncthreads();
     if (last) {
-        for (int e = tid; e < 2 * nb * nb + 1; e += blockDim.x)
+        for (int e = tid; e < (2 * nb * nb + 1) * TILE_FLAG_STRIDE; e += blockDim.x)
             p.flags[e] = 0;
         if (tid == 0)
             *ctr = 0;

@@ -55,8 +55,8 @@ def test_workspace_size(lib):
     assert f(9, 10, 1, 4) == 0
     # INV nt*T*T + four panels (six from 40 tiles on) of (n rounded up to 128) x (T rounded up to 32)
     # + TMP max(T*T, T*nrhs) + a 256-byte counter + the one-launch diagonal
-    # tile's 2 nb^2 + 2 int flags (nb = ceil(T / 64)) rounded up to 256 bytes
-    # (768 bytes at T = 512, 256 at T = 100); for nrhs > 0 also two
+    # tile's 2 nb^2 + 2 flags of 128 bytes each (nb = ceil(T / 64)) rounded up
+    # to 256 bytes (16640 bytes at T = 512, 1280 at T = 100); for nrhs > 0 also two
     # buffers for the transposed solved block, (nrhs rounded up to 128) x (T
     # rounded up to 32), two sets of nt*T*T chain products, 8 partial
     # T x nrhs blocks, the one-launch back substitution's two T x nrhs blocks
@@ -67,15 +67,15 @@ def test_workspace_size(lib):
     el = (n // T) * T * T + 6 * n * T + T * T  # 64 tiles: six panel buffers
     solve = 2 * 128 * 512 + 2 * (n // T) * T * T + 8 * T * nrhs + 2 * T * nrhs
     sflags = up(4 * 32 * (2 * 64 * 2 + 2), 256)
-    assert f(1, n, 0, T) == el * 8 + 256 + 768
-    assert f(1, n, nrhs, T) == (el + solve) * 8 + 256 + 768 + sflags
-    assert f(3, n, nrhs, T) == (el + solve) * 16 + 256 + 768 + sflags
+    assert f(1, n, 0, T) == el * 8 + 256 + 16640
+    assert f(1, n, nrhs, T) == (el + solve) * 8 + 256 + 16640 + sflags
+    assert f(3, n, nrhs, T) == (el + solve) * 16 + 256 + 16640 + sflags
     n, nrhs, T = 1000, 7, 100
     el = up(10 * 100 * 100, 32) + 4 * up(1024 * 128, 32) + up(100 * 100, 32)
     solve = up(2 * 128 * 128, 32) + 2 * up(10 * 100 * 100, 32) + up(8 * 100 * 7, 32) + up(2 * 100 * 7, 32)
     sflags = up(4 * 32 * (2 * 10 * 1 + 2), 256)
-    assert f(1, n, 0, T) == el * 8 + 256 + 256
-    assert f(1, n, nrhs, T) == (el + solve) * 8 + 256 + 256 + sflags
+    assert f(1, n, 0, T) == el * 8 + 256 + 1280
+    assert f(1, n, nrhs, T) == (el + solve) * 8 + 256 + 1280 + sflags
     # T_A > n is clamped to n
     assert f(1, 100, 1, 1000) == f(1, 100, 1, 100)
 
