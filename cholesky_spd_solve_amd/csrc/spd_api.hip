@@ -258,8 +258,9 @@ static int set_info(int *info, hipStream_t s)
 
 // Workspace layout, in elements of the working type (each region 256-byte
 // aligned):  INV  nt * T * T   inverted diagonal tiles (tile t at t*T*T, ld T)
-//            W    4 x (n rounded up to 128) x (T rounded up to 32): the panels
-//                 L21 of four consecutive steps (potrf) / merge temporaries (both)
+//            W    npanels (4, or 6 from TRIPLE_MIN_TILES tiles on) x (n rounded
+//                 up to 128) x (T rounded up to 32): the panels L21 of as many
+//                 consecutive steps (potrf) / merge temporaries (both)
 //            TMP  max(T*T, T*n_rhs)   one block row of the right-hand side
 struct Layout {
     int64_t T, nt, inv, w, wsz, npanels, tmp, ctr, flags, q, ldq, kq, qsz, gf, gb, part, z, ldz, sflags,
